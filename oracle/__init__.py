@@ -1,0 +1,24 @@
+"""Oracle for the fused LoRA linear layer: plain, slow, float64 CPU code.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import it.  The HIP library never calls it, and the two
+share no code.
+"""
+from .lora_oracle import (  # noqa: F401
+    lora_forward,
+    lora_backward,
+    lora_panel,
+    rope_angles,
+    rope_rotate,
+    qk_rope_forward,
+    qk_rope_backward,
+    round_f32,
+    round_bf16,
+    nf4_unpack,
+    nf4_dequant,
+    nf4_encode,
+    nf4_lora_forward,
+    nf4_lora_backward,
+    merged_weight,
+    rel_err,
+)

@@ -1,0 +1,230 @@
+"""Oracle for the fused LoRA linear layer (float64, numpy, CPU).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the HIP library.  It shares no code
+with the GPU path.
+
+Every function is the plain definition written out; numpy's float64 matmul is
+the only library primitive used.  Page citations name the page title and the
+section or equation on it:
+
+  [P1] "UnSloth加速微调体验：在LoRA基础上再提速3倍的秘密"
+       - section 算子融合 (operator fusion), equation y = Wx + ΔWx = Wx + BAx
+         with B ∈ R^{d×r}, A ∈ R^{r×k};
+       - section 反向传播优化 (backward optimisation): gradients of A and B,
+         intermediates Ax, BAx recomputed rather than stored;
+       - section RoPE缓存集成 (RoPE cache): cos/sin as one contiguous cache,
+         the rotation applied inside the q/k projection.
+  [P2] "微调太慢？试试Unsloth：实测训练速度翻倍，显存占用减半", section 5.1:
+       for inference the LoRA weights are merged into the main weight.
+  [P3] "Unsloth教程：本地微调大模型速度提升数倍，显存节省60%", section
+       显存优化策略, 4-bit QLoRA paragraph: base weight in NormalFloat4, only
+       the LoRA adapters train (no dW).
+  [P5] "Unsloth自动化优化：无需手动调参的实现原理", section 3.2: the fused
+       kernel is equivalent to A@B added to the original weight; section 5:
+       NF4 is the default 4-bit format, and fusion changes the order of the
+       gradient arithmetic, so results are equal up to rounding only.
+
+Readings where the pages are silent or garbled (each also listed in the design
+notes):
+  * scale s = alpha / r multiplies the low-rank branch ([P1] prints no scale);
+  * the gradient formulas printed in [P1] 反向传播优化 are dimensionally
+    inconsistent; the chain rule of Y = X W^T + s (X A^T) B^T gives
+    dX = G W + s (G B) A,  dB = s G^T (X A^T),  dA = s (G B)^T X;
+  * RoPE pairs element i with i + D/2 inside each head of width D
+    ("rotate-half"), angle pos * theta^(-2i/D), theta = 5e5;
+  * NF4: blocks of 64 consecutive elements of row-major W [d_out, d_in];
+    element 2j in the high nibble of byte j; value = bf16(f32(table[c] * absmax)).
+
+Layout: row-major, one token per row.  X [M, d_in], W [d_out, d_in],
+A [r, d_in], B [d_out, r], Y and dY [M, d_out].
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    if hasattr(a, "detach"):  # torch tensor: widen exactly
+        import torch
+
+        return a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# forward, backward ([P1] 算子融合, 反向传播优化)
+# ---------------------------------------------------------------------------
+
+def lora_panel(X, A) -> np.ndarray:
+    """P = X A^T [M, r]: the rank-r projection A x of every token ([P1] 算子融合)."""
+    return _f64(X) @ _f64(A).T
+
+
+def lora_forward(X, W, A, B, s: float) -> np.ndarray:
+    """Y = X W^T + s (X A^T) B^T: per token y = W x + s B (A x) ([P1] 算子融合, eq. y = Wx + BAx)."""
+    X, W, A, B = map(_f64, (X, W, A, B))
+    P = X @ A.T
+    return X @ W.T + s * (P @ B.T)
+
+
+def lora_backward(X, W, A, B, s: float, G):
+    """(dX, dA, dB) for upstream gradient G = dL/dY; no dW (W is frozen, [P3] QLoRA paragraph).
+
+    Chain rule of Y = X W^T + s P B^T with P = X A^T (recomputed, [P1] 反向传播优化):
+      dX = G W + s (G B) A
+      dB = s G^T P
+      dA = s (G B)^T X
+    """
+    X, W, A, B, G = map(_f64, (X, W, A, B, G))
+    P = X @ A.T
+    Q = G @ B
+    dX = G @ W + s * (Q @ A)
+    dB = s * (G.T @ P)
+    dA = s * (Q.T @ X)
+    return dX, dA, dB
+
+
+def merged_weight(W, A, B, s: float) -> np.ndarray:
+    """W' = W + s B A: the LoRA branch folded into the base weight ([P2] 5.1, [P5] 3.2)."""
+    return _f64(W) + s * (_f64(B) @ _f64(A))
+
+
+# ---------------------------------------------------------------------------
+# RoPE epilogue ([P1] RoPE缓存集成)
+# ---------------------------------------------------------------------------
+
+def rope_angles(pos, head_dim: int, theta: float) -> np.ndarray:
+    """Angle pos[t] * theta^(-2i/D) for t < M, i < D/2, in float64 ([M, D/2])."""
+    pos = np.asarray(pos, dtype=np.float64)
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv_freq = theta ** (-(2.0 * i) / head_dim)
+    return pos[:, None] * inv_freq[None, :]
+
+
+def rope_rotate(Z, pos, head_dim: int, theta: float, inverse: bool = False) -> np.ndarray:
+    """Rotate each pair (i, i + D/2) of every width-D head of each row by +angle
+    (or by -angle when inverse=True, which is the transpose of the rotation)."""
+    Z = _f64(Z)
+    M, d = Z.shape
+    if d % head_dim:
+        raise ValueError("d_out must be a multiple of head_dim")
+    half = head_dim // 2
+    a = rope_angles(pos, head_dim, theta)
+    c = np.cos(a)[:, None, :]
+    s = np.sin(a)[:, None, :]
+    if inverse:
+        s = -s
+    Zh = Z.reshape(M, d // head_dim, head_dim)
+    z1, z2 = Zh[..., :half], Zh[..., half:]
+    out = np.concatenate([z1 * c - z2 * s, z2 * c + z1 * s], axis=-1)
+    return out.reshape(M, d)
+
+
+def qk_rope_forward(X, W, A, B, s, pos, head_dim=128, theta=500000.0) -> np.ndarray:
+    """Y = RoPE(X W^T + s (X A^T) B^T): q/k projection with the rotation applied to its output."""
+    return rope_rotate(lora_forward(X, W, A, B, s), pos, head_dim, theta)
+
+
+def qk_rope_backward(X, W, A, B, s, pos, dY, head_dim=128, theta=500000.0):
+    """Backward of qk_rope_forward: G = R(-angle) dY, then the LoRA backward with G."""
+    G = rope_rotate(dY, pos, head_dim, theta, inverse=True)
+    return lora_backward(X, W, A, B, s, G)
+
+
+# ---------------------------------------------------------------------------
+# rounding and NF4 ([P3] QLoRA paragraph, [P5] section 5)
+# ---------------------------------------------------------------------------
+
+def round_f32(x) -> np.ndarray:
+    """Round float64 values to the nearest fp32 (ties to even), returned as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round fp32-representable values to bfloat16, nearest with ties to even.
+
+    bfloat16 keeps the top 16 bits of an fp32 word; the dropped low 16 bits
+    decide the rounding.  NaN stays NaN.
+    """
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    low = u & 0xFFFF
+    hi = u >> 16
+    up = (low > 0x8000) | ((low == 0x8000) & ((hi & 1) == 1))
+    hi = hi + up.astype(np.uint64)
+    out = (hi << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isnan(f), np.nan, out)
+
+
+def nf4_unpack(codes, n_elems: int) -> np.ndarray:
+    """4-bit codes of n_elems elements; element 2j is the high nibble of byte j."""
+    b = np.asarray(codes.cpu() if hasattr(codes, "cpu") else codes, dtype=np.uint8)
+    out = np.empty(n_elems, dtype=np.int64)
+    out[0::2] = b[: n_elems // 2] >> 4
+    out[1::2] = b[: n_elems // 2] & 0xF
+    return out
+
+
+def nf4_dequant(codes, absmax, table, d_out: int, d_in: int, blocksize: int = 64) -> np.ndarray:
+    """W [d_out, d_in] from NF4 codes: W[e] = bf16(f32(table[c_e] * absmax[e // blocksize])).
+
+    The float64 product of two fp32 values is exact, so rounding it once to
+    fp32 equals an fp32 multiply with round-to-nearest-even.
+    """
+    n = d_out * d_in
+    c = nf4_unpack(codes, n)
+    tab = _f64(table)
+    am = _f64(absmax)
+    e = np.arange(n)
+    w = round_bf16(round_f32(tab[c] * am[e // blocksize]))
+    return w.reshape(d_out, d_in)
+
+
+def nf4_encode(W, table, blocksize: int = 64):
+    """Quantise W [d_out, d_in] to (packed codes uint8, absmax fp32); used by tests.
+
+    absmax = max |w| of each block (fp32); each w / absmax goes to the nearest
+    table value, ties to the lower code; an all-zero block gets absmax 0 and
+    the code of 0.0.
+    """
+    W = _f64(W).reshape(-1)
+    tab = _f64(table)
+    n = W.size
+    blocks = W.reshape(-1, blocksize)
+    am = round_f32(np.abs(blocks).max(axis=1))
+    safe = np.where(am > 0, am, 1.0)
+    norm = blocks / safe[:, None]
+    dist = np.abs(norm[..., None] - tab[None, None, :])
+    codes = np.argmin(dist, axis=-1)  # first minimum = lower code on ties
+    zero_code = int(np.argmin(np.abs(tab)))
+    codes[am == 0] = zero_code
+    codes = codes.reshape(n)
+    packed = ((codes[0::2] << 4) | codes[1::2]).astype(np.uint8)
+    return packed, am.astype(np.float32)
+
+
+def nf4_lora_forward(X, codes, absmax, table, A, B, s, d_out, d_in, blocksize=64):
+    """Forward with the NF4-dequantised frozen base weight."""
+    W = nf4_dequant(codes, absmax, table, d_out, d_in, blocksize)
+    return lora_forward(X, W, A, B, s)
+
+
+def nf4_lora_backward(X, codes, absmax, table, A, B, s, dY, d_out, d_in, blocksize=64):
+    """Backward with the NF4-dequantised frozen base weight; never forms dW."""
+    W = nf4_dequant(codes, absmax, table, d_out, d_in, blocksize)
+    return lora_backward(X, W, A, B, s, dY)
+
+
+# ---------------------------------------------------------------------------
+# comparison
+# ---------------------------------------------------------------------------
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / max |ref| (0 when both are all zero)."""
+    got, ref = _f64(got), _f64(ref)
+    den = np.abs(ref).max() if ref.size else 0.0
+    num = np.abs(got - ref).max() if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else float("inf")
+    return float(num / den)

@@ -1,0 +1,335 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+None of these re-type the oracle's matrix formulas: they use hand-worked
+values, brute-force scalar sums on tiny inputs, exact integer arithmetic,
+finite differences, invariants of the rotation group, and library routines on
+special cases.  CPU only.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+RNG = np.random.default_rng(3407)
+
+
+def _rand(*shape):
+    return RNG.standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_2x2():
+    # X = [1 2], W = I, A = [1 1] (r = 1), B = [1; 2], s = 2.
+    # A x = 3, B A x = [3, 6], y = W x + s B A x = [1, 2] + [6, 12] = [7, 14].
+    X = np.array([[1.0, 2.0]])
+    W = np.eye(2)
+    A = np.array([[1.0, 1.0]])
+    B = np.array([[1.0], [2.0]])
+    Y = O.lora_forward(X, W, A, B, 2.0)
+    assert Y.tolist() == [[7.0, 14.0]]
+    # dY = [1 1]: dY B = 3; dX = dY W + s (dY B) A = [1,1] + 6 [1,1] = [7, 7];
+    # dB = s dY^T (X A^T) = 2 [1;1] 3 = [6; 6]; dA = s (dY B)^T X = 6 [1, 2].
+    dX, dA, dB = O.lora_backward(X, W, A, B, 2.0, np.array([[1.0, 1.0]]))
+    assert dX.tolist() == [[7.0, 7.0]]
+    assert dA.tolist() == [[6.0, 12.0]]
+    assert dB.tolist() == [[6.0], [6.0]]
+
+
+def _brute_forward(X, W, A, B, s):
+    """y_t[i] = sum_j W[i][j] x_t[j] + s sum_q B[i][q] sum_j A[q][j] x_t[j], exact."""
+    M, k = len(X), len(X[0])
+    d, r = len(W), len(A)
+    Y = []
+    for t in range(M):
+        ax = [sum(Fraction(A[q][j]) * Fraction(X[t][j]) for j in range(k)) for q in range(r)]
+        row = []
+        for i in range(d):
+            base = sum(Fraction(W[i][j]) * Fraction(X[t][j]) for j in range(k))
+            low = sum(Fraction(B[i][q]) * ax[q] for q in range(r))
+            row.append(base + Fraction(s) * low)
+        Y.append(row)
+    return Y
+
+
+def _brute_backward(X, W, A, B, s, G):
+    """Scalar-sum gradients of L = sum_t sum_i G[t][i] y_t[i], exact."""
+    M, k = len(X), len(X[0])
+    d, r = len(W), len(A)
+    F = Fraction
+    ax = [[sum(F(A[q][j]) * F(X[t][j]) for j in range(k)) for q in range(r)] for t in range(M)]
+    gb = [[sum(F(G[t][i]) * F(B[i][q]) for i in range(d)) for q in range(r)] for t in range(M)]
+    dX = [[sum(F(G[t][i]) * F(W[i][j]) for i in range(d)) + F(s) * sum(gb[t][q] * F(A[q][j]) for q in range(r))
+           for j in range(k)] for t in range(M)]
+    dB = [[F(s) * sum(F(G[t][i]) * ax[t][q] for t in range(M)) for q in range(r)] for i in range(d)]
+    dA = [[F(s) * sum(gb[t][q] * F(X[t][j]) for t in range(M)) for j in range(k)] for q in range(r)]
+    return dX, dA, dB
+
+
+def _small_ints(shape, lo=-3, hi=3):
+    return RNG.integers(lo, hi + 1, size=shape).astype(np.float64)
+
+
+@pytest.mark.parametrize("M,k,d,r", [(3, 5, 4, 2), (1, 8, 8, 1), (4, 3, 7, 3)])
+def test_integer_brute_force_exact(M, k, d, r):
+    X, W, A, B, G = (_small_ints(s) for s in [(M, k), (d, k), (r, k), (d, r), (M, d)])
+    s = 2.0
+    Y = O.lora_forward(X, W, A, B, s)
+    assert Y.tolist() == [[float(v) for v in row] for row in _brute_forward(X.tolist(), W.tolist(), A.tolist(), B.tolist(), s)]
+    dX, dA, dB = O.lora_backward(X, W, A, B, s, G)
+    bX, bA, bB = _brute_backward(X.tolist(), W.tolist(), A.tolist(), B.tolist(), s, G.tolist())
+    assert dX.tolist() == [[float(v) for v in row] for row in bX]
+    assert dA.tolist() == [[float(v) for v in row] for row in bA]
+    assert dB.tolist() == [[float(v) for v in row] for row in bB]
+
+
+def test_brute_force_float_shapes():
+    X, W, A, B = _rand(2, 6), _rand(5, 6), _rand(3, 6), _rand(5, 3)
+    ref = np.array([[float(v) for v in row] for row in _brute_forward(X.tolist(), W.tolist(), A.tolist(), B.tolist(), 0.25)])
+    assert np.abs(O.lora_forward(X, W, A, B, 0.25) - ref).max() < 1e-12
+
+
+def test_special_cases_B_zero_and_A_zero():
+    X, W, A, B, G = _rand(4, 6), _rand(5, 6), _rand(2, 6), _rand(5, 2), _rand(4, 5)
+    base = np.array([[sum(W[i, j] * X[t, j] for j in range(6)) for i in range(5)] for t in range(4)])
+    # B = 0: y = W x, dA = 0 exactly
+    Y = O.lora_forward(X, W, A, np.zeros_like(B), 0.5)
+    assert np.abs(Y - base).max() < 1e-12
+    dX, dA, dB = O.lora_backward(X, W, A, np.zeros_like(B), 0.5, G)
+    assert np.all(dA == 0.0)
+    # A = 0: y = W x, dB = 0 exactly
+    Y = O.lora_forward(X, W, np.zeros_like(A), B, 0.5)
+    assert np.abs(Y - base).max() < 1e-12
+    dX, dA, dB = O.lora_backward(X, W, np.zeros_like(A), B, 0.5, G)
+    assert np.all(dB == 0.0)
+
+
+def test_merged_weight_equals_unmerged():
+    # Folding the branch into the weight gives the same output (P2 5.1, P5 3.2).
+    X, W, A, B = _rand(7, 9), _rand(6, 9), _rand(4, 9), _rand(6, 4)
+    s = 4.0
+    Wm = O.merged_weight(W, A, B, s)
+    merged = np.array([[sum(Wm[i, j] * X[t, j] for j in range(9)) for i in range(6)] for t in range(7)])
+    unmerged = O.lora_forward(X, W, A, B, s)
+    assert np.abs(merged - unmerged).max() / np.abs(unmerged).max() < 1e-12
+
+
+def test_scale_enters_linearly():
+    X, W, A, B = _rand(3, 5), _rand(4, 5), _rand(2, 5), _rand(4, 2)
+    y0 = O.lora_forward(X, W, A, B, 0.0)
+    y1 = O.lora_forward(X, W, A, B, 1.0)
+    y3 = O.lora_forward(X, W, A, B, 3.0)
+    assert np.abs((y3 - y0) - 3.0 * (y1 - y0)).max() < 1e-12
+
+
+def test_parameter_count_4096_r16():
+    # A in R^{r x k}, B in R^{d x r}: 4096 x 4096 with r = 16 trains 2*4096*16 = 131072 values.
+    d = k = 4096
+    r = 16
+    assert r * k + d * r == 131072
+
+
+# ---------------------------------------------------------------------------
+# backward: finite differences and invariants
+# ---------------------------------------------------------------------------
+
+def _loss(X, W, A, B, s, G):
+    return float(np.sum(G * O.lora_forward(X, W, A, B, s)))
+
+
+def _fd(f, P, h=1e-3):
+    g = np.zeros_like(P)
+    for idx in np.ndindex(P.shape):
+        old = P[idx]
+        P[idx] = old + h
+        fp = f()
+        P[idx] = old - h
+        fm = f()
+        P[idx] = old
+        g[idx] = (fp - fm) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("s", [2.0, 0.25])
+def test_backward_matches_finite_differences(s):
+    M, k, d, r = 3, 5, 4, 2
+    X, W, A, B, G = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r), _rand(M, d)
+    dX, dA, dB = O.lora_backward(X, W, A, B, s, G)
+    f = lambda: _loss(X, W, A, B, s, G)  # noqa: E731
+    # L is linear in each of X, A, B separately: central differences are exact up to rounding.
+    assert np.abs(_fd(f, X) - dX).max() < 1e-9
+    assert np.abs(_fd(f, A) - dA).max() < 1e-9
+    assert np.abs(_fd(f, B) - dB).max() < 1e-9
+
+
+def test_backward_inner_product_identities():
+    # Y is homogeneous of degree 1 in X, in A and in B, so
+    #   <dX, X> = <G, Y>,  <dA, A> = <dB, B> = <G, Y - X W^T>.
+    M, k, d, r = 6, 7, 5, 3
+    X, W, A, B, G = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r), _rand(M, d)
+    s = 0.5
+    Y = O.lora_forward(X, W, A, B, s)
+    dX, dA, dB = O.lora_backward(X, W, A, B, s, G)
+    lora_part = Y - O.lora_forward(X, W, A, np.zeros_like(B), s)
+    assert abs(np.sum(dX * X) - np.sum(G * Y)) < 1e-10
+    assert abs(np.sum(dA * A) - np.sum(G * lora_part)) < 1e-10
+    assert abs(np.sum(dB * B) - np.sum(G * lora_part)) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# RoPE (P1 RoPE缓存集成; pairing and base are readings)
+# ---------------------------------------------------------------------------
+
+def test_rope_hand_values_rotate_half():
+    # head_dim 4: pairs are (0, 2) and (1, 3); frequency 0 is 1, frequency 1 is theta^(-2/4).
+    Z = np.array([[1.0, 0.0, 0.0, 0.0], [0.0, 1.0, 0.0, 0.0]])
+    pos = np.array([1, 2])
+    Y = O.rope_rotate(Z, pos, 4, 10000.0)
+    assert np.allclose(Y[0], [math.cos(1.0), 0.0, math.sin(1.0), 0.0], atol=1e-15)
+    a = 2 * 10000.0 ** -0.5
+    assert np.allclose(Y[1], [0.0, math.cos(a), 0.0, math.sin(a)], atol=1e-15)
+
+
+def test_rope_angles_closed_form():
+    a = O.rope_angles(np.array([0, 1, 7, 8191]), 128, 500000.0)
+    assert np.all(a[:, 0] == np.array([0, 1, 7, 8191], dtype=np.float64))  # theta^0 = 1
+    assert a[2, 63] == pytest.approx(7 * math.pow(500000.0, -126.0 / 128.0), rel=1e-15)
+    assert a[3, 1] == pytest.approx(8191 * math.pow(500000.0, -2.0 / 128.0), rel=1e-15)
+
+
+def test_rope_identity_norm_inverse_composition():
+    Z = _rand(5, 256)
+    zero = np.zeros(5, dtype=np.int64)
+    assert np.array_equal(O.rope_rotate(Z, zero, 128, 5e5), Z)
+    pos = np.array([0, 1, 100, 2047, 8191])
+    Y = O.rope_rotate(Z, pos, 128, 5e5)
+    zn = Z.reshape(5, 2, 2, 64)
+    yn = Y.reshape(5, 2, 2, 64)
+    assert np.abs((zn ** 2).sum(2) - (yn ** 2).sum(2)).max() < 1e-12  # per-pair norm
+    assert np.abs(O.rope_rotate(Y, pos, 128, 5e5, inverse=True) - Z).max() < 1e-12
+    p2 = np.array([3, 4, 5, 6, 7])
+    both = O.rope_rotate(O.rope_rotate(Z, pos, 128, 5e5), p2, 128, 5e5)
+    assert np.abs(both - O.rope_rotate(Z, pos + p2, 128, 5e5)).max() < 1e-10
+
+
+def test_rope_relative_position():
+    q, k = _rand(1, 128), _rand(1, 128)
+    for m, n in [(3, 10), (100, 40), (0, 2047)]:
+        lhs = np.sum(O.rope_rotate(q, [m], 128, 5e5) * O.rope_rotate(k, [n], 128, 5e5))
+        rhs = np.sum(q * O.rope_rotate(k, [n - m], 128, 5e5))
+        assert abs(lhs - rhs) < 1e-10
+
+
+def test_rope_backward_matches_finite_differences():
+    M, k, d, r = 2, 4, 8, 2
+    X, W, A, B, dY = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r), _rand(M, d)
+    pos = np.array([3, 11])
+    s = 0.5
+    dX, dA, dB = O.qk_rope_backward(X, W, A, B, s, pos, dY, head_dim=4, theta=10.0)
+    f = lambda: float(np.sum(dY * O.qk_rope_forward(X, W, A, B, s, pos, head_dim=4, theta=10.0)))  # noqa: E731
+    assert np.abs(_fd(f, X) - dX).max() < 1e-9
+    assert np.abs(_fd(f, A) - dA).max() < 1e-9
+    assert np.abs(_fd(f, B) - dB).max() < 1e-9
+
+
+# ---------------------------------------------------------------------------
+# rounding and NF4
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_ties_and_library_agreement():
+    import torch
+
+    one = 1.0
+    assert O.round_bf16([one + 2 ** -8])[0] == 1.0                 # tie, even stays
+    assert O.round_bf16([one + 3 * 2 ** -8])[0] == 1.0 + 2 ** -6    # tie, rounds to even above
+    assert O.round_bf16([one + 2 ** -8 + 2 ** -20])[0] == 1.0 + 2 ** -7
+    assert O.round_bf16([-(one + 3 * 2 ** -8)])[0] == -(1.0 + 2 ** -6)
+    x = np.concatenate([RNG.standard_normal(20000) * 10.0 ** RNG.integers(-6, 6, 20000),
+                        np.array([0.0, -0.0, 65504.0, 1e-40])]).astype(np.float32)
+    lib = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(x), lib)
+
+
+def test_nf4_table_matches_normal_quantile_construction():
+    from scipy.stats import norm
+
+    from synth import nf4_table
+
+    t = nf4_table().astype(np.float64)
+    assert len(t) == 16 and np.all(np.diff(t) > 0)
+    assert t[0] == -1.0 and t[7] == 0.0 and t[15] == 1.0
+    assert np.sum(t < 0) == 7 and np.sum(t > 0) == 8
+    # Quantiles of N(0,1): 8 positive levels and 7 negative ones, from
+    # offset delta = (1 - 1/(2*15) + 1 - 1/(2*16)) / 2 towards the median, plus zero.
+    delta = 0.5 * ((1 - 1 / 30) + (1 - 1 / 32))
+    pos = norm.ppf(np.linspace(delta, 0.5, 9)[:-1])
+    neg = -norm.ppf(np.linspace(delta, 0.5, 8)[:-1])
+    v = np.sort(np.concatenate([pos, [0.0], neg]))
+    v /= v.max()
+    assert np.abs(v - t).max() < 5e-7
+
+
+def test_nf4_unpack_order_high_nibble_first():
+    codes = O.nf4_unpack(np.array([0xAB, 0x0F], dtype=np.uint8), 4)
+    assert codes.tolist() == [10, 11, 0, 15]
+
+
+def test_nf4_dequant_hand_and_fp32_multiply():
+    from synth import nf4_table
+
+    t = nf4_table()
+    # byte 0xF0: element 0 is code 15 (+1), element 1 is code 0 (-1); absmax 0.5
+    w = O.nf4_dequant(np.array([0xF0] * 32, dtype=np.uint8), np.array([0.5], np.float32), t, 1, 64)
+    assert w[0, 0] == 0.5 and w[0, 1] == -0.5
+    # general case: fp32 multiply (numpy float32) then bf16 rounding
+    codes = RNG.integers(0, 256, 64 * 8, dtype=np.uint8)
+    am = (np.abs(RNG.standard_normal(16)) * 0.03).astype(np.float32)
+    w = O.nf4_dequant(codes, am, t, 8, 128)
+    c = O.nf4_unpack(codes, 1024)
+    prod32 = (t[c] * np.repeat(am, 64)).astype(np.float32)  # fp32 * fp32 in fp32
+    assert prod32.dtype == np.float32
+    import torch
+    ref = torch.from_numpy(prod32).to(torch.bfloat16).to(torch.float64).numpy().reshape(8, 128)
+    assert np.array_equal(w, ref)
+
+
+def test_nf4_round_trip_all_codes():
+    from synth import nf4_table
+
+    t = nf4_table()
+    codes = np.arange(16)
+    packed = ((codes[0::2] << 4) | codes[1::2]).astype(np.uint8)
+    packed = np.tile(packed, 8)  # one block of 64
+    w = O.nf4_dequant(packed, np.array([1.0], np.float32), t, 1, 64)
+    # with absmax 1 the decode is the table (rounded to bf16); -1, 0, +1 are exact
+    assert w[0, 0] == -1.0 and w[0, 7] == 0.0 and w[0, 15] == 1.0
+    assert np.abs(w[0, :16] - t).max() < 2 ** -8
+    re, am = O.nf4_encode(w, t)
+    assert am[0] == 1.0
+    assert np.array_equal(O.nf4_unpack(re, 64), np.tile(codes, 4))
+
+
+def test_nf4_encode_zero_block_and_ties():
+    from synth import nf4_table
+
+    t = nf4_table()
+    packed, am = O.nf4_encode(np.zeros((1, 64)), t)
+    assert am[0] == 0.0
+    assert np.all(O.nf4_unpack(packed, 64) == 7)
+    # a value exactly midway between codes 7 (0.0) and 8 goes to the lower code
+    mid = float(t[8]) / 2
+    w = np.zeros((1, 64))
+    w[0, 0] = 1.0  # sets absmax = 1
+    w[0, 1] = mid
+    packed, am = O.nf4_encode(w, t)
+    assert O.nf4_unpack(packed, 64)[1] == 7
+
+
+def test_rel_err():
+    assert O.rel_err(np.array([1.0, 2.0]), np.array([1.0, 4.0])) == 0.5
+    assert O.rel_err(np.zeros(3), np.zeros(3)) == 0.0
