@@ -1,0 +1,203 @@
+/*
+ * lora_linear.h - C ABI of the MI355X (gfx950) fused LoRA linear layer.
+ *
+ * The layer (page "UnSloth加速微调体验：在LoRA基础上再提速3倍的秘密", section
+ * 算子融合, equation y = Wx + ΔWx = Wx + BAx, with B in R^{d x r} and
+ * A in R^{r x k}) computes, for every token x (one row of X):
+ *
+ *     y = W x + s * B (A x),        s = alpha / r (the caller passes s)
+ *
+ * with the base weight W frozen.  Row-major, one token per row:
+ *
+ *     X  [M, d_in]     W  [d_out, d_in]     A [r, d_in]     B [d_out, r]
+ *     Y  [M, d_out]    dY [M, d_out]        dX [M, d_in]
+ *     dA [r, d_in] fp32                     dB [d_out, r] fp32
+ *
+ * Backward (section 反向传播优化 of the same page; its printed gradient formulas
+ * are garbled, these follow the chain rule):
+ *
+ *     dX = dY W + s (dY B) A,   dB = s dY^T (X A^T),   dA = s (dY B)^T X
+ *
+ * X A^T is recomputed, never stored by the forward.  No dW is ever formed:
+ * only the adapters train (page "Unsloth教程：本地微调大模型速度提升数倍，显存
+ * 节省60%", section 显存优化策略, 4-bit QLoRA paragraph).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers are DEVICE pointers (caller-owned, e.g. torch allocations) unless
+ *    an argument says "host".  The library never allocates or frees device
+ *    memory; scratch space comes from the caller's workspace `ws` of
+ *    `ws_bytes` bytes, sized by lora_workspace_bytes().  The workspace holds
+ *    nothing between calls.
+ *  - bf16 tensors are passed as their 16-bit patterns.  Accumulation is fp32.
+ *    dA and dB are always fp32 and are OVERWRITTEN (not accumulated into).
+ *  - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
+ *    work on it and never synchronise.  The library is re-entrant; calls that
+ *    share a workspace must be ordered by the caller.
+ *  - Every pointer must be 16-byte aligned; d_in and d_out must be multiples
+ *    of 8; 1 <= r <= 256; M >= 0 (M = 0 gives empty Y/dX and zero dA, dB; the
+ *    pointers to the M-row tensors X, Y, dY, dX and positions may then be NULL).
+ *  - Validation happens before any HIP call: on error nothing is launched and
+ *    no output is touched.  A failed launch returns LORA_ERR_DEVICE.  No
+ *    exception crosses the ABI and nothing is printed.
+ *  - A shape the kernels do not support returns LORA_ERR_SHAPE; there is no
+ *    slower fallback path.
+ */
+#ifndef LORA_LINEAR_H
+#define LORA_LINEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_ABI_VERSION 1
+
+/* element types of X, W, A, B, Y, dY, dX */
+enum { LORA_F32 = 0, LORA_BF16 = 1 };
+
+/* return codes */
+enum {
+  LORA_OK = 0,
+  LORA_ERR_NULL = -1,      /* a required pointer is NULL */
+  LORA_ERR_SHAPE = -2,     /* a size is out of range or breaks a divisibility rule */
+  LORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
+  LORA_ERR_DTYPE = -4,     /* unknown dtype, or a dtype the entry point does not take */
+  LORA_ERR_WORKSPACE = -5, /* ws_bytes < lora_workspace_bytes(...) or ws NULL when needed */
+  LORA_ERR_DEVICE = -6     /* current device is not gfx950, or a launch failed */
+};
+
+/* operation ids for lora_workspace_bytes */
+enum {
+  LORA_OP_FWD = 0,
+  LORA_OP_BWD = 1,
+  LORA_OP_ROPE_FWD = 2,
+  LORA_OP_ROPE_BWD = 3,
+  LORA_OP_NF4_FWD = 4,
+  LORA_OP_NF4_BWD = 5
+};
+
+/* Library version; equals LORA_ABI_VERSION of the header it was built from. */
+int lora_abi_version(void);
+
+/* Static description of a return code ("ok", "null pointer", ...). */
+const char* lora_strerror(int code);
+
+/*
+ * Bytes of workspace that entry point `op` needs for these sizes (0 if none).
+ * Pure host arithmetic; no device query.  Returns 0 for invalid arguments
+ * (the entry point itself then reports the error).
+ */
+size_t lora_workspace_bytes(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r);
+
+/*
+ * Forward: Y = X W^T + s (X A^T) B^T.
+ * Page "UnSloth加速微调体验…", section 算子融合: W x and the low-rank update are
+ * produced by one fused pass; the rank-r panel s X A^T is added into the same
+ * fp32 accumulator as X W^T, so no intermediate of size [M, d_out] exists.
+ * dtype: LORA_F32 or LORA_BF16 (X, W, A, B, Y all of that type).
+ */
+int lora_linear_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                    const void* X, const void* W, const void* A, const void* B, void* Y,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward: dX = dY W + s (dY B) A (skipped when dX is NULL),
+ *           dB = s dY^T (X A^T),  dA = s (dY B)^T X  (fp32, overwritten).
+ * Page "UnSloth加速微调体验…", section 反向传播优化: X A^T is recomputed here
+ * instead of being kept from the forward.  No dW.
+ */
+int lora_linear_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                    const void* X, const void* W, const void* A, const void* B, const void* dY,
+                    void* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Fill the RoPE cache: cos_cache[p * head_dim/2 + i] = cos(p * theta^(-2i/head_dim)),
+ * sin_cache likewise, for p < max_pos and i < head_dim/2, computed in fp64 and
+ * rounded to fp32.  Page "UnSloth加速微调体验…", section RoPE缓存集成: the cos/sin
+ * values live in one contiguous block and a position selects a row by a
+ * pointer offset.  Both arrays are device fp32 [max_pos, head_dim/2].
+ */
+int lora_rope_cache(int64_t max_pos, int head_dim, double theta, float* cos_cache,
+                    float* sin_cache, void* stream);
+
+/*
+ * q/k projection with the RoPE rotation as the forward epilogue
+ * (section RoPE缓存集成: the rotation is applied while q_proj(x) + lora_q(x) is
+ * produced).  Within every head of width head_dim (must be 128, and d_out a
+ * multiple of it), element i pairs with i + 64 and rotates by the angle whose
+ * cos/sin sit in row positions[t] of the caches (rotate-half pairing):
+ *     y_i = z_i cos - z_{i+64} sin,   y_{i+64} = z_{i+64} cos + z_i sin,
+ * where z is the fused LoRA output.  positions: device int32 [M], each in
+ * [0, max_pos) (the caller guarantees it; it is not checked on the device).
+ */
+int lora_qk_rope_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                     const void* X, const void* W, const void* A, const void* B, int head_dim,
+                     const int32_t* positions, const float* cos_cache, const float* sin_cache,
+                     int64_t max_pos, void* Y, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of lora_qk_rope_fwd: the inverse rotation (the transpose, angle
+ * negated) is applied to dY, then the LoRA backward runs on the result.
+ * Outputs as lora_linear_bwd.
+ */
+int lora_qk_rope_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                     const void* X, const void* W, const void* A, const void* B, int head_dim,
+                     const int32_t* positions, const float* cos_cache, const float* sin_cache,
+                     int64_t max_pos, const void* dY, void* dX, float* dA, float* dB, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/*
+ * Forward with an NF4 base weight (QLoRA; page "Unsloth教程…", section 显存优化策略;
+ * page "Unsloth自动化优化：无需手动调参的实现原理", section 5: NF4 is the default).
+ * W_nf4: device uint8 [d_out * d_in / 2], element e = i*d_in + j of W in byte
+ * e/2, high nibble for even e.  absmax: device fp32 [d_out * d_in / blocksize],
+ * one per block of `blocksize` consecutive elements.  table16: HOST pointer to
+ * the 16 fp32 code values (copied into the launch).  The weight used is
+ *     W[e] = bf16_rne(fp32_rne(table16[code_e] * absmax[e / blocksize])),
+ * formed inside the GEMM's load stage, never written to memory.
+ * blocksize must be 64 and d_in a multiple of 64.  X, A, B, Y are bf16.
+ */
+int nf4_lora_linear_fwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                        const void* X, const uint8_t* W_nf4, const float* absmax, int blocksize,
+                        const float* table16, const void* A, const void* B, void* Y, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Backward with the NF4 base weight; outputs as lora_linear_bwd.  Never forms dW. */
+int nf4_lora_linear_bwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                        const void* X, const uint8_t* W_nf4, const float* absmax, int blocksize,
+                        const float* table16, const void* A, const void* B, const void* dY,
+                        void* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Dequantise n NF4 elements to bf16 bit patterns with the same device routine
+ * the NF4 GEMMs use in their load stage (exposed so it can be checked bit for
+ * bit).  n must be a multiple of blocksize (64).  table16 is a HOST pointer.
+ */
+int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_t n,
+                const float* table16, uint16_t* out_bf16, void* stream);
+
+/*
+ * Launch profiling (measurement hook, not part of the layer's arithmetic).
+ * Between lora_profile_begin and lora_profile_end every kernel the library
+ * launches is bracketed by two HIP events on its stream, and the launch's
+ * algorithmic FLOP and minimum HBM bytes are recorded with its kind.  At most
+ * max_launches launches are recorded (later ones are not).  Query after the
+ * stream has been synchronised.  Kinds are numbered 0 .. lora_profile_kinds()-1.
+ *   lora_profile_begin: LORA_ERR_SHAPE if max_launches < 1; LORA_ERR_DEVICE if
+ *     event creation fails.
+ *   lora_profile_query: totals over the recorded launches of `kind`:
+ *     summed event time in ms, launch count, summed FLOP, summed bytes.
+ */
+int lora_profile_begin(int max_launches);
+int lora_profile_end(void);
+int lora_profile_kinds(void);
+const char* lora_profile_kind_name(int kind);
+int lora_profile_query(int kind, double* total_ms, int* count, double* total_flop, double* total_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_LINEAR_H */

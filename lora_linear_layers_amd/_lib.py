@@ -1,0 +1,141 @@
+"""ctypes binding of liblora_linear.so (the C ABI in include/lora_linear.h).
+
+Argument marshalling only: torch tensors in, device pointers and the current
+HIP stream out to the library, return codes turned into exceptions.  Every
+step of the computation runs in the library's kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblora_linear.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD = range(6)
+
+_lib = None
+
+_i64, _f32, _vp, _sz, _int, _dbl = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
+                                    ctypes.c_int, ctypes.c_double)
+_fp = ctypes.POINTER(ctypes.c_float)
+
+_SIGS = {
+    "lora_abi_version": ([], _int),
+    "lora_strerror": ([_int], ctypes.c_char_p),
+    "lora_workspace_bytes": ([_int, _int, _i64, _i64, _i64, _i64], _sz),
+    "lora_linear_fwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "lora_linear_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                         _vp], _int),
+    "lora_rope_cache": ([_i64, _int, _dbl, _vp, _vp, _vp], _int),
+    "lora_qk_rope_fwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _i64, _vp,
+                          _vp, _sz, _vp], _int),
+    "lora_qk_rope_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _i64, _vp,
+                          _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "nf4_lora_linear_fwd": ([_i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _int, _fp, _vp, _vp, _vp, _vp, _sz, _vp],
+                            _int),
+    "nf4_lora_linear_bwd": ([_i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _int, _fp, _vp, _vp, _vp, _vp, _vp, _vp,
+                             _vp, _sz, _vp], _int),
+    "nf4_dequant": ([_vp, _vp, _int, _i64, _fp, _vp, _vp], _int),
+    "lora_profile_begin": ([_int], _int),
+    "lora_profile_end": ([], _int),
+    "lora_profile_kinds": ([], _int),
+    "lora_profile_kind_name": ([_int], ctypes.c_char_p),
+    "lora_profile_query": ([_int, ctypes.POINTER(_dbl), ctypes.POINTER(_int), ctypes.POINTER(_dbl),
+                            ctypes.POINTER(_dbl)], _int),
+}
+
+EXPORTS = tuple(_SIGS)
+
+
+class LoraError(RuntimeError):
+    def __init__(self, fn, code):
+        self.code = code
+        msg = _lib.lora_strerror(code).decode() if _lib is not None else str(code)
+        super().__init__(f"{fn} failed: {msg} ({code})")
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m lora_linear_layers_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+def lib():
+    return load()
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise LoraError(fn, rc)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LORA_F32
+    if t.dtype == torch.bfloat16:
+        return LORA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _table_ptr(table16):
+    tab = (ctypes.c_float * 16)(*[float(v) for v in table16])
+    return tab
+
+
+def workspace_bytes(op: int, dtype: int, M: int, d_in: int, d_out: int, r: int) -> int:
+    return int(lib().lora_workspace_bytes(op, dtype, M, d_in, d_out, r))
+
+
+def _workspace(op, dtype, M, d_in, d_out, r, device, ws=None):
+    n = workspace_bytes(op, dtype, M, d_in, d_out, r)
+    if ws is not None:
+        return ws
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def profile_begin(max_launches: int = 4096):
+    _check("lora_profile_begin", lib().lora_profile_begin(max_launches))
+
+
+def profile_end():
+    _check("lora_profile_end", lib().lora_profile_end())
+
+
+def profile_report():
+    """{kind name: (total_ms, count, total_flop, total_bytes)} for kinds that ran."""
+    out = {}
+    ms, n, fl, by = ctypes.c_double(), ctypes.c_int(), ctypes.c_double(), ctypes.c_double()
+    for k in range(lib().lora_profile_kinds()):
+        _check("lora_profile_query", lib().lora_profile_query(k, ctypes.byref(ms), ctypes.byref(n),
+                                                              ctypes.byref(fl), ctypes.byref(by)))
+        if n.value:
+            out[lib().lora_profile_kind_name(k).decode()] = (ms.value, n.value, fl.value, by.value)
+    return out

@@ -1,0 +1,580 @@
+// api.cpp - the C ABI declared in include/lora_linear.h: argument validation
+// (before any HIP call), workspace layout, tile choice and the sequence of
+// launches for each entry point.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <vector>
+
+#include "../../include/lora_linear.h"
+#include "launch.h"
+
+using namespace lora;
+
+namespace {
+
+constexpr int64_t kMaxRank = 256;
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t rup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == LORA_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// device check: gfx950 only, checked once per device
+// ---------------------------------------------------------------------------
+std::atomic<int> g_dev_state[64];  // 0 unknown, 1 ok, 2 bad
+std::mutex g_dev_mu;
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LORA_ERR_DEVICE;
+  int s = g_dev_state[dev].load(std::memory_order_acquire);
+  if (s == 0) {
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LORA_ERR_DEVICE;
+      s = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      g_dev_state[dev].store(s, std::memory_order_release);
+    }
+  }
+  return s == 1 ? LORA_OK : LORA_ERR_DEVICE;
+}
+
+// ---------------------------------------------------------------------------
+// workspace layout
+// ---------------------------------------------------------------------------
+struct Layout {
+  int64_t r8 = 0, M8 = 0;
+  size_t bpad = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, total = 0;
+  int splits_dA = 1, splits_dB = 1;
+  int64_t ksplit_dA = 0, ksplit_dB = 0;
+};
+
+// Split of the token contraction for dA / dB: enough workgroups to cover the
+// chip (~2 per CU), each split a multiple of 64 tokens and at least 256 long.
+void choose_split(int64_t M, int64_t N, int* splits, int64_t* ksplit) {
+  const int64_t tiles_n = cdiv(N, 256);
+  int64_t s = cdiv(512, tiles_n);
+  const int64_t smax = cdiv(M, 256);
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  int64_t ks = rup(cdiv(M, s), 64);
+  if (ks < 64) ks = 64;
+  *ksplit = ks;
+  *splits = (int)cdiv(M, ks);
+  if (*splits < 1) *splits = 1;
+}
+
+Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+  Layout L;
+  const size_t eb = elem_bytes(dtype);
+  L.r8 = rup(r, 8);
+  L.M8 = rup(M, 8);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD;
+  if (r % 8) L.bpad = take(size_t(d_out) * L.r8 * eb);
+  if (!bwd) {
+    L.p = take(size_t(M) * L.r8 * eb);
+  } else {
+    if (op == LORA_OP_ROPE_BWD) L.g = take(size_t(M) * d_out * eb);
+    L.pt = take(size_t(L.r8) * L.M8 * eb);
+    L.qs = take(size_t(L.M8) * L.r8 * eb);
+    L.qt = take(size_t(L.r8) * L.M8 * eb);
+    choose_split(M, d_in, &L.splits_dA, &L.ksplit_dA);
+    choose_split(M, d_out, &L.splits_dB, &L.ksplit_dB);
+    size_t pa = size_t(L.splits_dA) * L.r8 * d_in * 4;
+    size_t pb = size_t(L.splits_dB) * L.r8 * d_out * 4;
+    L.part = take(pa > pb ? pa : pb);
+  }
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// validation
+// ---------------------------------------------------------------------------
+int check_sizes(int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+  if (M < 0 || M >= kMaxDim) return LORA_ERR_SHAPE;
+  if (d_in < 8 || d_out < 8 || d_in % 8 || d_out % 8 || d_in >= kMaxDim || d_out >= kMaxDim) return LORA_ERR_SHAPE;
+  if (r < 1 || r > kMaxRank) return LORA_ERR_SHAPE;
+  return LORA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (!q) return LORA_ERR_NULL;
+  for (const void* q : ps)
+    if (!aligned16(q)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+int check_ws(const Layout& L, const void* ws, size_t ws_bytes) {
+  if (L.total == 0) return LORA_OK;
+  if (!ws || ws_bytes < L.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+#define TRY(x)                       \
+  do {                               \
+    int _rc = (x);                   \
+    if (_rc != LORA_OK) return _rc;  \
+  } while (0)
+
+#define HIPTRY(x)                                  \
+  do {                                             \
+    if ((x) != hipSuccess) return LORA_ERR_DEVICE; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// launch profiling: HIP events around every launch while enabled
+// ---------------------------------------------------------------------------
+enum ProfKind : int {
+  K_PAD = G_KIND_COUNT,
+  K_ROPE_INV,
+  K_REDUCE,
+  K_FILL,
+  K_ROPE_CACHE,
+  K_NF4_DEQ,
+  K_PROF_COUNT
+};
+
+const char* kind_name(int k) {
+  static const char* names[K_PROF_COUNT] = {
+      "gemm_bf16_256x256_nt_store", "gemm_bf16_256x256_nt_rope", "gemm_bf16_128x128_nt_store",
+      "gemm_bf16_128x128_nt_rope",  "gemm_bf16_256x256_nn_store", "gemm_bf16_128x128_nn_store",
+      "gemm_nf4_256x256_nt_store",  "gemm_nf4_128x128_nt_store",  "gemm_nf4_256x256_nn_store",
+      "gemm_nf4_128x128_nn_store",  "panel_bf16_nt_store",        "panel_bf16_nt_store_t",
+      "panel_bf16_nn_both",         "split_bf16_nn_partial",      "gemm_f32_64x128_nt_store",
+      "gemm_f32_64x128_nt_rope",    "gemm_f32_64x128_nn_store",   "panel_f32_nt_store",
+      "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
+      "pad_cols",                   "rope_inverse",               "reduce_splits",
+      "fill_zero",                  "rope_cache",                 "nf4_dequant"};
+  return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
+}
+
+struct ProfEntry {
+  int kind;
+  double flop, bytes;
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  std::vector<ProfEntry> ent;
+  size_t n = 0;
+} g_prof;
+
+template <class F>
+hipError_t timed(int kind, double flop, double bytes, hipStream_t st, F&& f) {
+  if (!g_prof.on) return f();
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on || g_prof.n >= g_prof.ent.size()) return f();
+  const size_t i = g_prof.n++;
+  if (hipEventRecord(g_prof.ev[2 * i], st) != hipSuccess) return hipErrorUnknown;
+  hipError_t e = f();
+  if (hipEventRecord(g_prof.ev[2 * i + 1], st) != hipSuccess && e == hipSuccess) e = hipErrorUnknown;
+  g_prof.ent[i] = ProfEntry{kind, flop, bytes};
+  return e;
+}
+
+hipError_t gemm(GemmKind k, const GemmArgs& a, int splits, hipStream_t st, double flop, double bytes) {
+  return timed(k, flop, bytes, st, [&] { return launch_gemm(k, a, splits, st); });
+}
+
+// ---------------------------------------------------------------------------
+// tile choice
+// ---------------------------------------------------------------------------
+// 256x256 tiles when they still give at least one tile per CU, else 128x128.
+bool use_big(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
+
+GemmArgs blank() {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.alpha = 1.f;
+  return a;
+}
+
+// ---------------------------------------------------------------------------
+// forward (shared by the plain, RoPE and NF4 entry points)
+// ---------------------------------------------------------------------------
+struct Nf4W {
+  const uint8_t* codes;
+  const float* absmax;
+  const float* table;  // host
+};
+
+struct Rope {
+  const int32_t* pos;
+  const float* cosc;
+  const float* sinc;
+};
+
+int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                 const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, void* Y, void* ws,
+                 const Layout& L, hipStream_t st) {
+  if (M == 0) return LORA_OK;
+  const bool f32 = dtype == LORA_F32;
+  const int eb = elem_bytes(dtype);
+  char* w = static_cast<char*>(ws);
+  const void* Bsrc = B;
+  if (r % 8) {
+    HIPTRY(timed(K_PAD, 0, 2.0 * d_out * L.r8 * eb, st,
+                 [&] { return launch_pad_cols(eb, B, w + L.bpad, d_out, r, L.r8, st); }));
+    Bsrc = w + L.bpad;
+  }
+  void* P = w + L.p;
+  const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r), e = double(eb);
+  // panel: P = s * X A^T  [M, r8] (columns r..r8 are exact zeros)
+  {
+    GemmArgs a = blank();
+    a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
+    a.m_load = M; a.m_store = M; a.n_load = r; a.n_store = L.r8;
+    a.c = P; a.ldc = L.r8; a.alpha = scale;
+    HIPTRY(gemm(f32 ? G_F32_PANEL_NT_STORE : G_BF16_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki,
+                (Md * ki + rr * ki + Md * L.r8) * e));
+  }
+  // main: Y = [X | P] [W | B]^T, optional RoPE epilogue
+  GemmArgs a = blank();
+  a.a1 = X; a.lda1 = d_in; a.b1 = W; a.ldb1 = d_in; a.K1 = d_in;
+  a.a2 = P; a.lda2 = L.r8; a.b2 = Bsrc; a.ldb2 = L.r8; a.K2 = r;
+  a.m_load = M; a.m_store = M; a.n_load = d_out; a.n_store = d_out;
+  a.c = Y; a.ldc = d_out;
+  GemmKind k;
+  const bool big = use_big(M, d_out);
+  if (nf4) {
+    a.codes = nf4->codes; a.absmax = nf4->absmax; a.codes_ld = d_in / 2; a.blocks_per_row = d_in / 64;
+    for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
+    k = big ? G_NF4_BIG_NT_STORE : G_NF4_MED_NT_STORE;
+  } else if (rope) {
+    a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc;
+    k = f32 ? G_F32_NT_ROPE : (big ? G_BF16_BIG_NT_ROPE : G_BF16_MED_NT_ROPE);
+  } else {
+    k = f32 ? G_F32_NT_STORE : (big ? G_BF16_BIG_NT_STORE : G_BF16_MED_NT_STORE);
+  }
+  const double wbytes = nf4 ? ko * ki / 2 + ko * ki / 64 * 4 : ko * ki * e;
+  HIPTRY(gemm(k, a, 1, st, 2 * Md * ko * (ki + rr), (Md * ki + Md * rr + ko * rr + Md * ko) * e + wbytes));
+  return LORA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// backward
+// ---------------------------------------------------------------------------
+int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                  const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, const void* dY,
+                  void* dX, float* dA, float* dB, void* ws, const Layout& L, hipStream_t st) {
+  if (M == 0) {
+    HIPTRY(timed(K_FILL, 0, 4.0 * r * d_in, st, [&] { return launch_fill_zero(dA, r * d_in, st); }));
+    HIPTRY(timed(K_FILL, 0, 4.0 * r * d_out, st, [&] { return launch_fill_zero(dB, d_out * r, st); }));
+    return LORA_OK;
+  }
+  const bool f32 = dtype == LORA_F32;
+  const int eb = elem_bytes(dtype);
+  char* w = static_cast<char*>(ws);
+  const void* Bsrc = B;
+  if (r % 8) {
+    HIPTRY(timed(K_PAD, 0, 2.0 * d_out * L.r8 * eb, st,
+                 [&] { return launch_pad_cols(eb, B, w + L.bpad, d_out, r, L.r8, st); }));
+    Bsrc = w + L.bpad;
+  }
+  const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r), e = double(eb);
+  const void* G = dY;
+  if (rope) {
+    HIPTRY(timed(K_ROPE_INV, 3.0 * Md * ko, 2 * Md * ko * e + Md * 64 * 8, st, [&] {
+      return launch_rope_inverse(eb, dY, w + L.g, M, d_out, rope->pos, rope->cosc, rope->sinc, st);
+    }));
+    G = w + L.g;
+  }
+  void* Pt = w + L.pt;
+  void* Qs = w + L.qs;
+  void* Qt = w + L.qt;
+  float* part = reinterpret_cast<float*>(w + L.part);
+  // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
+  {
+    GemmArgs a = blank();
+    a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
+    a.m_load = M; a.m_store = L.M8; a.n_load = r; a.n_store = L.r8;
+    a.ct = Pt; a.ldct = L.M8; a.alpha = scale;
+    HIPTRY(gemm(f32 ? G_F32_PANEL_NT_STORE_T : G_BF16_PANEL_NT_STORE_T, a, 1, st, 2 * Md * rr * ki,
+                (Md * ki + rr * ki + Md * L.r8) * e));
+  }
+  // Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
+  {
+    GemmArgs a = blank();
+    a.a1 = G; a.lda1 = d_out; a.b1 = Bsrc; a.ldb1 = L.r8; a.K1 = d_out;
+    a.m_load = M; a.m_store = L.M8; a.n_load = L.r8; a.n_store = L.r8;
+    a.c = Qs; a.ldc = L.r8; a.ct = Qt; a.ldct = L.M8; a.alpha = scale;
+    HIPTRY(gemm(f32 ? G_F32_PANEL_NN_BOTH : G_BF16_PANEL_NN_BOTH, a, 1, st, 2 * Md * rr * ko,
+                (Md * ko + rr * ko + 2 * Md * L.r8) * e));
+  }
+  // dX = [G | Qs] [W ; A]
+  if (dX) {
+    GemmArgs a = blank();
+    a.a1 = G; a.lda1 = d_out; a.b1 = W; a.ldb1 = d_in; a.K1 = d_out;
+    a.a2 = Qs; a.lda2 = L.r8; a.b2 = A; a.ldb2 = d_in; a.K2 = r;
+    a.m_load = M; a.m_store = M; a.n_load = d_in; a.n_store = d_in;
+    a.c = dX; a.ldc = d_in;
+    GemmKind k;
+    const bool big = use_big(M, d_in);
+    if (nf4) {
+      a.codes = nf4->codes; a.absmax = nf4->absmax; a.codes_ld = d_in / 2; a.blocks_per_row = d_in / 64;
+      for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
+      k = big ? G_NF4_BIG_NN_STORE : G_NF4_MED_NN_STORE;
+    } else {
+      k = f32 ? G_F32_NN_STORE : (big ? G_BF16_BIG_NN_STORE : G_BF16_MED_NN_STORE);
+    }
+    const double wbytes = nf4 ? ko * ki / 2 + ko * ki / 64 * 4 : ko * ki * e;
+    HIPTRY(gemm(k, a, 1, st, 2 * Md * ki * (ko + rr), (Md * ko + Md * rr + rr * ki + Md * ki) * e + wbytes));
+  }
+  const GemmKind ksplit = f32 ? G_F32_SPLIT_NN_PARTIAL : G_BF16_SPLIT_NN_PARTIAL;
+  // dB^T = Pt G  -> partials [splits][r8, d_out] -> dB [d_out, r]
+  {
+    GemmArgs a = blank();
+    a.a1 = Pt; a.lda1 = L.M8; a.b1 = G; a.ldb1 = d_out; a.K1 = M;
+    a.m_load = L.r8; a.m_store = L.r8; a.n_load = d_out; a.n_store = d_out;
+    a.k_split = L.ksplit_dB; a.c = part; a.ldc = d_out; a.part_stride = L.r8 * d_out;
+    HIPTRY(gemm(ksplit, a, L.splits_dB, st, 2 * rr * ko * Md,
+                (rr * Md + Md * ko) * e + 4.0 * L.splits_dB * L.r8 * ko));
+    HIPTRY(timed(K_REDUCE, double(L.splits_dB) * rr * ko, 4.0 * (L.splits_dB + 1) * rr * ko, st, [&] {
+      return launch_reduce_splits(part, L.splits_dB, r, d_out, L.r8 * d_out, true, dB, st);
+    }));
+  }
+  // dA = Qt X -> partials [splits][r8, d_in] -> dA [r, d_in]
+  {
+    GemmArgs a = blank();
+    a.a1 = Qt; a.lda1 = L.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
+    a.m_load = L.r8; a.m_store = L.r8; a.n_load = d_in; a.n_store = d_in;
+    a.k_split = L.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = L.r8 * d_in;
+    HIPTRY(gemm(ksplit, a, L.splits_dA, st, 2 * rr * ki * Md,
+                (rr * Md + Md * ki) * e + 4.0 * L.splits_dA * L.r8 * ki));
+    HIPTRY(timed(K_REDUCE, double(L.splits_dA) * rr * ki, 4.0 * (L.splits_dA + 1) * rr * ki, st, [&] {
+      return launch_reduce_splits(part, L.splits_dA, r, d_in, L.r8 * d_in, false, dA, st);
+    }));
+  }
+  return LORA_OK;
+}
+
+int check_rope(int head_dim, int64_t d_out, int64_t M, const int32_t* pos, const float* c, const float* s,
+               int64_t max_pos) {
+  if (head_dim != 128 || d_out % 128) return LORA_ERR_SHAPE;
+  if (max_pos < 1) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({c, s}));
+  return M > 0 ? check_ptrs({pos}) : LORA_OK;
+}
+
+int check_nf4(int64_t d_in, int blocksize, const uint8_t* codes, const float* absmax, const float* table) {
+  if (blocksize != 64 || d_in % 64) return LORA_ERR_SHAPE;
+  if (!table) return LORA_ERR_NULL;
+  return check_ptrs({codes, absmax});
+}
+
+}  // namespace
+
+// ===========================================================================
+// exported C ABI
+// ===========================================================================
+extern "C" {
+
+int lora_abi_version(void) { return LORA_ABI_VERSION; }
+
+const char* lora_strerror(int code) {
+  switch (code) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL: return "null pointer";
+    case LORA_ERR_SHAPE: return "unsupported shape";
+    case LORA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case LORA_ERR_DTYPE: return "unsupported dtype";
+    case LORA_ERR_WORKSPACE: return "workspace too small";
+    case LORA_ERR_DEVICE: return "device error (not gfx950, or launch failed)";
+    default: return "unknown error";
+  }
+}
+
+size_t lora_workspace_bytes(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+  if (op < LORA_OP_FWD || op > LORA_OP_NF4_BWD) return 0;
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  if (check_sizes(M, d_in, d_out, r) != LORA_OK) return 0;
+  return make_layout(op, dtype, M, d_in, d_out, r).total;
+}
+
+int lora_linear_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                    const void* W, const void* A, const void* B, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y}));
+  const Layout L = make_layout(LORA_OP_FWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  return forward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, nullptr, Y, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+int lora_linear_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                    const void* W, const void* A, const void* B, const void* dY, void* dX, float* dA, float* dB,
+                    void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B, dA, dB}));
+  if (M > 0) TRY(check_ptrs({X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  const Layout L = make_layout(LORA_OP_BWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  return backward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, nullptr, dY, dX, dA, dB, ws, L,
+                       static_cast<hipStream_t>(stream));
+}
+
+int lora_rope_cache(int64_t max_pos, int head_dim, double theta, float* cos_cache, float* sin_cache,
+                    void* stream) {
+  if (max_pos < 1 || head_dim < 2 || head_dim % 2 || !(theta > 0.0)) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({cos_cache, sin_cache}));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIPTRY(timed(K_ROPE_CACHE, 0, 8.0 * max_pos * (head_dim / 2), st,
+               [&] { return launch_rope_cache(max_pos, head_dim, theta, cos_cache, sin_cache, st); }));
+  return LORA_OK;
+}
+
+int lora_qk_rope_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                     const void* W, const void* A, const void* B, int head_dim, const int32_t* positions,
+                     const float* cos_cache, const float* sin_cache, int64_t max_pos, void* Y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y}));
+  TRY(check_rope(head_dim, d_out, M, positions, cos_cache, sin_cache, max_pos));
+  const Layout L = make_layout(LORA_OP_ROPE_FWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  const Rope rp{positions, cos_cache, sin_cache};
+  return forward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, &rp, Y, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+int lora_qk_rope_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                     const void* W, const void* A, const void* B, int head_dim, const int32_t* positions,
+                     const float* cos_cache, const float* sin_cache, int64_t max_pos, const void* dY, void* dX,
+                     float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B, dA, dB}));
+  if (M > 0) TRY(check_ptrs({X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  TRY(check_rope(head_dim, d_out, M, positions, cos_cache, sin_cache, max_pos));
+  const Layout L = make_layout(LORA_OP_ROPE_BWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  const Rope rp{positions, cos_cache, sin_cache};
+  return backward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, &rp, dY, dX, dA, dB, ws, L,
+                       static_cast<hipStream_t>(stream));
+}
+
+int nf4_lora_linear_fwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                        const uint8_t* W_nf4, const float* absmax, int blocksize, const float* table16,
+                        const void* A, const void* B, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y}));
+  TRY(check_nf4(d_in, blocksize, W_nf4, absmax, table16));
+  const Layout L = make_layout(LORA_OP_NF4_FWD, LORA_BF16, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  const Nf4W q{W_nf4, absmax, table16};
+  return forward_impl(LORA_BF16, M, d_in, d_out, r, scale, X, nullptr, &q, A, B, nullptr, Y, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+int nf4_lora_linear_bwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                        const uint8_t* W_nf4, const float* absmax, int blocksize, const float* table16,
+                        const void* A, const void* B, const void* dY, void* dX, float* dA, float* dB, void* ws,
+                        size_t ws_bytes, void* stream) {
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({A, B, dA, dB}));
+  if (M > 0) TRY(check_ptrs({X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  TRY(check_nf4(d_in, blocksize, W_nf4, absmax, table16));
+  const Layout L = make_layout(LORA_OP_NF4_BWD, LORA_BF16, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  const Nf4W q{W_nf4, absmax, table16};
+  return backward_impl(LORA_BF16, M, d_in, d_out, r, scale, X, nullptr, &q, A, B, nullptr, dY, dX, dA, dB, ws, L,
+                       static_cast<hipStream_t>(stream));
+}
+
+int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_t n, const float* table16,
+                uint16_t* out_bf16, void* stream) {
+  if (blocksize != 64 || n < 0 || n % 64) return LORA_ERR_SHAPE;
+  if (!table16) return LORA_ERR_NULL;
+  TRY(check_ptrs({W_nf4, absmax, out_bf16}));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIPTRY(timed(K_NF4_DEQ, 2.0 * n, n / 2.0 + n / 16.0 + 2.0 * n, st,
+               [&] { return launch_nf4_dequant(W_nf4, absmax, n, table16, out_bf16, st); }));
+  return LORA_OK;
+}
+
+int lora_profile_begin(int max_launches) {
+  if (max_launches < 1) return LORA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  const size_t want = 2 * size_t(max_launches);
+  while (g_prof.ev.size() < want) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return LORA_ERR_DEVICE;
+    g_prof.ev.push_back(e);
+  }
+  g_prof.ent.assign(size_t(max_launches), ProfEntry{-1, 0, 0});
+  g_prof.n = 0;
+  g_prof.on = true;
+  return LORA_OK;
+}
+
+int lora_profile_end(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  return LORA_OK;
+}
+
+int lora_profile_kinds(void) { return K_PROF_COUNT; }
+
+const char* lora_profile_kind_name(int kind) { return kind_name(kind); }
+
+int lora_profile_query(int kind, double* total_ms, int* count, double* total_flop, double* total_bytes) {
+  if (!total_ms || !count || !total_flop || !total_bytes) return LORA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  double ms = 0, fl = 0, by = 0;
+  int c = 0;
+  for (size_t i = 0; i < g_prof.n; ++i) {
+    if (g_prof.ent[i].kind != kind) continue;
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) return LORA_ERR_DEVICE;
+    ms += t;
+    fl += g_prof.ent[i].flop;
+    by += g_prof.ent[i].bytes;
+    ++c;
+  }
+  *total_ms = ms;
+  *count = c;
+  *total_flop = fl;
+  *total_bytes = by;
+  return LORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,258 @@
+// kernels.hip - gfx950 device code of the fused LoRA linear layer: the GEMM
+// instances and the small element-wise kernels around them, plus their
+// host-side launchers (internal interface in launch.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+#include "launch.h"
+
+namespace lora {
+
+namespace {
+
+template <typename T, int BM, int BN, int WM, int WN, bool B_NN, int EPI, int BL>
+hipError_t run(GemmArgs a, int splits, hipStream_t st) {
+  a.tiles_m = (int)((a.m_store + BM - 1) / BM);
+  const int64_t tiles_n = (a.n_store + BN - 1) / BN;
+  const int64_t nblocks = (int64_t)a.tiles_m * tiles_n;
+  if (nblocks <= 0 || splits <= 0) return hipSuccess;
+  dim3 grid((unsigned)nblocks, 1, (unsigned)splits);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, B_NN, EPI, BL>), grid, dim3(64 * WM * WN), 0, st,
+                     a);
+  return hipGetLastError();
+}
+
+using bf = uint16_t;
+
+}  // namespace
+
+TileShape gemm_tile(GemmKind k) {
+  switch (k) {
+    case G_BF16_BIG_NT_STORE:
+    case G_BF16_BIG_NT_ROPE:
+    case G_BF16_BIG_NN_STORE:
+    case G_NF4_BIG_NT_STORE:
+    case G_NF4_BIG_NN_STORE:
+      return {256, 256};
+    case G_BF16_MED_NT_STORE:
+    case G_BF16_MED_NT_ROPE:
+    case G_BF16_MED_NN_STORE:
+    case G_NF4_MED_NT_STORE:
+    case G_NF4_MED_NN_STORE:
+      return {128, 128};
+    case G_BF16_PANEL_NT_STORE:
+    case G_BF16_PANEL_NT_STORE_T:
+    case G_BF16_PANEL_NN_BOTH:
+    case G_F32_PANEL_NT_STORE:
+    case G_F32_PANEL_NT_STORE_T:
+    case G_F32_PANEL_NN_BOTH:
+      return {64, 64};
+    case G_BF16_SPLIT_NN_PARTIAL:
+    case G_F32_SPLIT_NN_PARTIAL:
+      return {64, 256};
+    case G_F32_NT_STORE:
+    case G_F32_NT_ROPE:
+    case G_F32_NN_STORE:
+      return {64, 128};
+    default:
+      return {0, 0};
+  }
+}
+
+hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
+  switch (k) {
+    case G_BF16_BIG_NT_STORE: return run<bf, 256, 256, 4, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NT_ROPE: return run<bf, 256, 256, 4, 2, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NT_ROPE: return run<bf, 128, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NN_STORE: return run<bf, 256, 256, 4, 2, true, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_NF4_BIG_NT_STORE: return run<bf, 256, 256, 4, 2, false, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_NF4_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_NF4_BIG_NN_STORE: return run<bf, 256, 256, 4, 2, true, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_NF4_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_BF16_PANEL_NT_STORE: return run<bf, 64, 64, 2, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_PANEL_NT_STORE_T: return run<bf, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
+    case G_BF16_PANEL_NN_BOTH: return run<bf, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
+    case G_BF16_SPLIT_NN_PARTIAL: return run<bf, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_F32_NT_STORE: return run<float, 64, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_F32_NT_ROPE: return run<float, 64, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
+    case G_F32_NN_STORE: return run<float, 64, 128, 4, 1, true, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_F32_PANEL_NT_STORE: return run<float, 64, 64, 2, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_F32_PANEL_NT_STORE_T: return run<float, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
+    case G_F32_PANEL_NN_BOTH: return run<float, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
+    case G_F32_SPLIT_NN_PARTIAL: return run<float, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// small kernels
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ void pad_cols_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int64_t r,
+                                int64_t r_pad) {
+  const int64_t n = rows * r_pad;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / r_pad, j = e - i * r_pad;
+    dst[e] = j < r ? src[i * r + j] : T(0);
+  }
+}
+
+static unsigned grid_for(int64_t n, int threads) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b > 65535 * 4) b = 65535 * 4;
+  return (unsigned)(b > 0 ? b : 1);
+}
+
+hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t rows, int64_t r, int64_t r_pad,
+                           hipStream_t st) {
+  const int64_t n = rows * r_pad;
+  if (n <= 0) return hipSuccess;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(pad_cols_kernel<uint16_t>, dim3(grid_for(n, 256)), dim3(256), 0, st,
+                       (const uint16_t*)src, (uint16_t*)dst, rows, r, r_pad);
+  else
+    hipLaunchKernelGGL(pad_cols_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const float*)src,
+                       (float*)dst, rows, r, r_pad);
+  return hipGetLastError();
+}
+
+template <typename T>
+__device__ __forceinline__ float ld_as_f32(const T* p, int64_t i) {
+  if constexpr (sizeof(T) == 2)
+    return __builtin_bit_cast(float, (uint32_t)p[i] << 16);
+  else
+    return p[i];
+}
+
+// One thread per (row t, head h, group of 8 frequencies): rotates the pairs
+// (h*128 + f, h*128 + f + 64) for f in [8q, 8q+8) by the negated angle:
+//   g1 = y1 cos + y2 sin,   g2 = y2 cos - y1 sin.
+template <typename T>
+__global__ void rope_inverse_kernel(const T* __restrict__ dY, T* __restrict__ G, int64_t M, int64_t d_out,
+                                    const int32_t* __restrict__ pos, const float* __restrict__ cosc,
+                                    const float* __restrict__ sinc) {
+  const int64_t heads = d_out / 128;
+  const int64_t n = M * heads * 8;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t q = e & 7;
+    const int64_t th = e >> 3;
+    const int64_t t = th / heads, h = th - t * heads;
+    const int64_t prow = (int64_t)pos[t] * 64;
+    const int64_t base = t * d_out + h * 128;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t f = q * 8 + u;
+      const float c = cosc[prow + f], s = sinc[prow + f];
+      const float y1 = ld_as_f32(dY, base + f), y2 = ld_as_f32(dY, base + f + 64);
+      const float g1 = y1 * c + y2 * s, g2 = y2 * c - y1 * s;
+      if constexpr (sizeof(T) == 2) {
+        G[base + f] = f2bf(g1);
+        G[base + f + 64] = f2bf(g2);
+      } else {
+        G[base + f] = g1;
+        G[base + f + 64] = g2;
+      }
+    }
+  }
+}
+
+hipError_t launch_rope_inverse(int elem_bytes, const void* dY, void* G, int64_t M, int64_t d_out,
+                               const int32_t* pos, const float* cosc, const float* sinc, hipStream_t st) {
+  const int64_t n = M * (d_out / 128) * 8;
+  if (n <= 0) return hipSuccess;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(rope_inverse_kernel<uint16_t>, dim3(grid_for(n, 256)), dim3(256), 0, st,
+                       (const uint16_t*)dY, (uint16_t*)G, M, d_out, pos, cosc, sinc);
+  else
+    hipLaunchKernelGGL(rope_inverse_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const float*)dY,
+                       (float*)G, M, d_out, pos, cosc, sinc);
+  return hipGetLastError();
+}
+
+__global__ void rope_cache_kernel(int64_t max_pos, int half, double theta, float* __restrict__ cosc,
+                                  float* __restrict__ sinc) {
+  const int64_t n = max_pos * half;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = e / half;
+    const int i = (int)(e - p * half);
+    const double inv_freq = pow(theta, -(2.0 * i) / (2.0 * half));
+    const double a = (double)p * inv_freq;
+    cosc[e] = (float)cos(a);
+    sinc[e] = (float)sin(a);
+  }
+}
+
+hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float* cosc, float* sinc,
+                             hipStream_t st) {
+  const int64_t n = max_pos * (head_dim / 2);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_cache_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, max_pos, head_dim / 2, theta,
+                     cosc, sinc);
+  return hipGetLastError();
+}
+
+__global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t rows, int64_t N,
+                                     int64_t part_stride, int transpose, float* __restrict__ out) {
+  const int64_t n = rows * N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t q = e / N, c = e - q * N;
+    float s = 0.f;
+    for (int z = 0; z < splits; ++z) s += part[(int64_t)z * part_stride + e];
+    if (transpose)
+      out[c * rows + q] = s;
+    else
+      out[e] = s;
+  }
+}
+
+hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N, int64_t part_stride,
+                                bool transpose, float* out, hipStream_t st) {
+  const int64_t n = rows * N;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, part, splits, rows, N,
+                     part_stride, transpose ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+    p[e] = 0.f;
+}
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
+struct Table16 {
+  float v[16];
+};
+
+// One thread per code byte (two elements); the same byte -> bf16x2 routine as
+// the NF4 GEMM load stage.  Blocks of 64 elements share one absmax.
+__global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ absmax, int64_t nbytes,
+                                                          Table16 tab, uint32_t* __restrict__ out) {
+  __shared__ float2 tab2[256];
+  nf4_fill_tab2(tab2, tab.v, threadIdx.x, blockDim.x);
+  __syncthreads();
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nbytes; j += (int64_t)gridDim.x * blockDim.x)
+    out[j] = nf4_byte_to_bf16x2(tab2, codes[j], absmax[j >> 5]);
+}
+
+hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* table16,
+                              uint16_t* out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  Table16 t;
+  for (int i = 0; i < 16; ++i) t.v[i] = table16[i];
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(n / 2, 256)), dim3(256), 0, st, codes, absmax, n / 2, t,
+                     (uint32_t*)out);
+  return hipGetLastError();
+}
+
+}  // namespace lora

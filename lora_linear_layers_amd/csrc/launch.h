@@ -1,0 +1,70 @@
+// launch.h - internal launch interface between the C ABI (api.cpp) and the
+// device code (kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace lora {
+
+// GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
+// epilogue.  "BIG" = 256x256 tiles (8 waves), "MED" = 128x128 (4 waves),
+// "PANEL" = 64x64 rank-r panels, "SPLIT" = 64x256 split-contraction partials.
+enum GemmKind : int {
+  G_BF16_BIG_NT_STORE,
+  G_BF16_BIG_NT_ROPE,
+  G_BF16_MED_NT_STORE,
+  G_BF16_MED_NT_ROPE,
+  G_BF16_BIG_NN_STORE,
+  G_BF16_MED_NN_STORE,
+  G_NF4_BIG_NT_STORE,
+  G_NF4_MED_NT_STORE,
+  G_NF4_BIG_NN_STORE,
+  G_NF4_MED_NN_STORE,
+  G_BF16_PANEL_NT_STORE,
+  G_BF16_PANEL_NT_STORE_T,
+  G_BF16_PANEL_NN_BOTH,
+  G_BF16_SPLIT_NN_PARTIAL,
+  G_F32_NT_STORE,
+  G_F32_NT_ROPE,
+  G_F32_NN_STORE,
+  G_F32_PANEL_NT_STORE,
+  G_F32_PANEL_NT_STORE_T,
+  G_F32_PANEL_NN_BOTH,
+  G_F32_SPLIT_NN_PARTIAL,
+  G_KIND_COUNT
+};
+
+struct TileShape {
+  int bm, bn;
+};
+TileShape gemm_tile(GemmKind k);
+
+// Sets a.tiles_m from a.m_store and launches over (tiles_m * tiles_n, 1, splits).
+hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st);
+
+// dst[i, j] = j < r ? src[i, j] : 0 for a [rows, r] matrix widened to [rows, r_pad].
+hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t rows, int64_t r,
+                           int64_t r_pad, hipStream_t st);
+
+// G = R(-angle) dY for rotate-half pairs of 128-wide heads.
+hipError_t launch_rope_inverse(int elem_bytes, const void* dY, void* G, int64_t M, int64_t d_out,
+                               const int32_t* pos, const float* cosc, const float* sinc,
+                               hipStream_t st);
+
+hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float* cosc, float* sinc,
+                             hipStream_t st);
+
+// out = sum over z < splits of part[z] (fixed order).  part[z] is [rows_pad, N]
+// fp32.  transpose = false: out[q * N + n]; true: out[n * rows + q]; q < rows.
+hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N,
+                                int64_t part_stride, bool transpose, float* out, hipStream_t st);
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n,
+                              const float* table16, uint16_t* out, hipStream_t st);
+
+}  // namespace lora

@@ -1,0 +1,159 @@
+"""Python entry points with the C ABI's names (include/lora_linear.h).
+
+Each call validates tensor placement/contiguity, allocates outputs (and the
+workspace when none is passed) with torch, and calls the library on the
+current HIP stream.  Row-major shapes:
+
+    X [M, d_in]   W [d_out, d_in]   A [r, d_in]   B [d_out, r]   Y, dY [M, d_out]
+
+scale is s = alpha / r.  dA and dB come back in fp32.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+def _dims(X, W_rows, W_cols, A, B):
+    M, d_in = X.shape
+    r = A.shape[0]
+    if A.shape != (r, d_in) or B.shape != (W_rows, r) or W_cols != d_in:
+        raise ValueError("shape mismatch: X [M,d_in], W [d_out,d_in], A [r,d_in], B [d_out,r]")
+    return M, d_in, W_rows, r
+
+
+def lora_linear_fwd(X, W, A, B, scale: float, Y=None, ws=None):
+    """Y = X W^T + scale (X A^T) B^T."""
+    L._contig(X, W, A, B, Y)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    ws = L._workspace(L.OP_FWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_linear_fwd", L.lib().lora_linear_fwd(
+        dt, M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B), L._ptr(Y),
+        L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return Y
+
+
+def lora_linear_bwd(X, W, A, B, scale: float, dY, need_dX: bool = True, ws=None, out=None):
+    """(dX or None, dA fp32, dB fp32) for upstream gradient dY; X A^T is recomputed."""
+    L._contig(X, W, A, B, dY)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    if out is None:
+        dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+        dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+        dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+    else:
+        dX, dA, dB = out
+    ws = L._workspace(L.OP_BWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_linear_bwd", L.lib().lora_linear_bwd(
+        dt, M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B), L._ptr(dY), L._ptr(dX),
+        L._ptr(dA), L._ptr(dB), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return dX, dA, dB
+
+
+def rope_cache(max_pos: int, head_dim: int = 128, theta: float = 500000.0, device="cuda"):
+    """(cos, sin) fp32 [max_pos, head_dim/2], filled on the device in fp64."""
+    cos = torch.empty(max_pos, head_dim // 2, dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    L._check("lora_rope_cache", L.lib().lora_rope_cache(max_pos, head_dim, float(theta), L._ptr(cos), L._ptr(sin),
+                                                        L._stream(cos.device)))
+    return cos, sin
+
+
+def lora_qk_rope_fwd(X, W, A, B, scale: float, positions, cos, sin, head_dim: int = 128, Y=None, ws=None):
+    """RoPE(X W^T + scale (X A^T) B^T) with the rotation as the GEMM epilogue."""
+    L._contig(X, W, A, B, positions, cos, sin, Y)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    if positions.dtype != torch.int32 or positions.numel() != M:
+        raise ValueError("positions must be int32 [M]")
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    ws = L._workspace(L.OP_ROPE_FWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_qk_rope_fwd", L.lib().lora_qk_rope_fwd(
+        dt, M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B), head_dim,
+        L._ptr(positions), L._ptr(cos), L._ptr(sin), cos.shape[0], L._ptr(Y), L._ptr(ws), ws.numel(),
+        L._stream(X.device)))
+    return Y
+
+
+def lora_qk_rope_bwd(X, W, A, B, scale: float, positions, cos, sin, dY, head_dim: int = 128,
+                     need_dX: bool = True, ws=None):
+    """Backward of lora_qk_rope_fwd: inverse rotation of dY, then the LoRA backward."""
+    L._contig(X, W, A, B, positions, cos, sin, dY)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+    dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+    dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+    ws = L._workspace(L.OP_ROPE_BWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_qk_rope_bwd", L.lib().lora_qk_rope_bwd(
+        dt, M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B), head_dim,
+        L._ptr(positions), L._ptr(cos), L._ptr(sin), cos.shape[0], L._ptr(dY), L._ptr(dX), L._ptr(dA), L._ptr(dB),
+        L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return dX, dA, dB
+
+
+def nf4_lora_linear_fwd(X, codes, absmax, table16, A, B, scale: float, d_out: int, blocksize: int = 64,
+                        Y=None, ws=None):
+    """Forward with the NF4 base weight dequantised inside the GEMM load stage."""
+    L._contig(X, codes, absmax, A, B, Y)
+    M, d_in = X.shape
+    r = A.shape[0]
+    if X.dtype != torch.bfloat16:
+        raise TypeError("NF4 path takes bf16 activations")
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    ws = L._workspace(L.OP_NF4_FWD, L.LORA_BF16, M, d_in, d_out, r, X.device, ws)
+    tab = L._table_ptr(table16)
+    L._check("nf4_lora_linear_fwd", L.lib().nf4_lora_linear_fwd(
+        M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(codes), L._ptr(absmax), blocksize, tab, L._ptr(A),
+        L._ptr(B), L._ptr(Y), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return Y
+
+
+def nf4_lora_linear_bwd(X, codes, absmax, table16, A, B, scale: float, dY, blocksize: int = 64,
+                        need_dX: bool = True, ws=None):
+    """(dX or None, dA, dB) with the NF4 base weight; no dW."""
+    L._contig(X, codes, absmax, A, B, dY)
+    M, d_in = X.shape
+    d_out = dY.shape[1]
+    r = A.shape[0]
+    dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+    dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+    dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+    ws = L._workspace(L.OP_NF4_BWD, L.LORA_BF16, M, d_in, d_out, r, X.device, ws)
+    tab = L._table_ptr(table16)
+    L._check("nf4_lora_linear_bwd", L.lib().nf4_lora_linear_bwd(
+        M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(codes), L._ptr(absmax), blocksize, tab, L._ptr(A),
+        L._ptr(B), L._ptr(dY), L._ptr(dX), L._ptr(dA), L._ptr(dB), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return dX, dA, dB
+
+
+def nf4_dequant(codes, absmax, table16, n: int, blocksize: int = 64):
+    """bf16 [n] from NF4 codes with the GEMM load stage's own routine."""
+    out = torch.empty(n, dtype=torch.bfloat16, device=codes.device)
+    tab = L._table_ptr(table16)
+    L._check("nf4_dequant", L.lib().nf4_dequant(L._ptr(codes), L._ptr(absmax), blocksize, n, tab, L._ptr(out),
+                                                L._stream(codes.device)))
+    return out
+
+
+class LoraLinearFunction(torch.autograd.Function):
+    """Autograd wrapper: gradients for X, A and B (W frozen); A and B grads in fp32."""
+
+    @staticmethod
+    def forward(ctx, X, W, A, B, scale):
+        ctx.save_for_backward(X, W, A, B)
+        ctx.scale = scale
+        return lora_linear_fwd(X, W, A, B, scale)
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, W, A, B = ctx.saved_tensors
+        dX, dA, dB = lora_linear_bwd(X, W, A, B, ctx.scale, dY.contiguous(), need_dX=ctx.needs_input_grad[0])
+        return dX, None, dA.to(A.dtype), dB.to(B.dtype), None

@@ -1,0 +1,133 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol the header declares, sizes workspaces, and rejects bad arguments
+before any HIP call (so these run with fake, never-dereferenced pointers)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import lora_linear_layers_amd as L
+from lora_linear_layers_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_linear.h")
+
+OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EDEV = 0, -1, -2, -3, -4, -5, -6
+P = 0x100000  # fake 16-byte-aligned address; validation never dereferences it
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def test_header_declares_the_abi():
+    assert _declared() == set(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for name in _declared():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_and_strerror(lib):
+    assert lib.lora_abi_version() == 1
+    for code in (OK, ENULL, ESHAPE, EALIGN, EDTYPE, EWS, EDEV):
+        assert lib.lora_strerror(code)
+    assert lib.lora_strerror(-99) == b"unknown error"
+
+
+def test_workspace_sizes(lib):
+    f = lib.lora_workspace_bytes
+    # forward: the [M, r8] panel (bf16): 8192 * 64 * 2
+    assert f(_lib.OP_FWD, 1, 8192, 4096, 14336, 64) == 8192 * 64 * 2
+    # r not a multiple of 8 adds a padded copy of B
+    assert f(_lib.OP_FWD, 1, 100, 64, 64, 3) > f(_lib.OP_FWD, 1, 100, 64, 64, 8) - 100 * 8 * 2
+    bwd = f(_lib.OP_BWD, 1, 8192, 4096, 14336, 64)
+    assert bwd >= 3 * 8192 * 64 * 2  # Pt, Qs, Qt
+    assert f(_lib.OP_ROPE_BWD, 1, 8192, 4096, 4096, 64) >= f(_lib.OP_BWD, 1, 8192, 4096, 4096, 64) + 8192 * 4096 * 2
+    assert f(_lib.OP_FWD, 0, 128, 256, 256, 8) == 128 * 8 * 4
+    assert f(_lib.OP_FWD, 1, 0, 64, 64, 8) == 0
+    # invalid arguments give 0
+    assert f(9, 1, 8, 8, 8, 8) == 0
+    assert f(_lib.OP_FWD, 7, 8, 8, 8, 8) == 0
+    assert f(_lib.OP_FWD, 1, 8, 12, 8, 8) == 0
+
+
+def _fwd(lib, dtype=1, M=16, d_in=64, d_out=64, r=8, X=P, W=P, A=P, B=P, Y=P, ws=P, wsb=1 << 30):
+    return lib.lora_linear_fwd(dtype, M, d_in, d_out, r, 1.0, X, W, A, B, Y, ws, wsb, None)
+
+
+def _bwd(lib, dtype=1, M=16, d_in=64, d_out=64, r=8, dY=P, dX=P, dA=P, dB=P, ws=P, wsb=1 << 30):
+    return lib.lora_linear_bwd(dtype, M, d_in, d_out, r, 1.0, P, P, P, P, dY, dX, dA, dB, ws, wsb, None)
+
+
+def test_fwd_validation(lib):
+    assert _fwd(lib, dtype=2) == EDTYPE
+    assert _fwd(lib, X=None) == ENULL
+    assert _fwd(lib, W=None) == ENULL
+    assert _fwd(lib, M=0, W=None) == ENULL
+    assert _fwd(lib, Y=None) == ENULL
+    assert _fwd(lib, d_in=12) == ESHAPE
+    assert _fwd(lib, d_out=0) == ESHAPE
+    assert _fwd(lib, r=0) == ESHAPE
+    assert _fwd(lib, r=257) == ESHAPE
+    assert _fwd(lib, M=-1) == ESHAPE
+    assert _fwd(lib, W=P + 8) == EALIGN
+    assert _fwd(lib, wsb=10) == EWS
+    assert _fwd(lib, ws=None) == EWS
+    assert _fwd(lib, ws=P + 4) == EALIGN
+
+
+def test_bwd_validation(lib):
+    assert _bwd(lib, dA=None) == ENULL
+    assert _bwd(lib, dB=None) == ENULL
+    assert _bwd(lib, dY=None) == ENULL
+    assert _bwd(lib, dX=P + 2) == EALIGN
+    assert _bwd(lib, wsb=1000) == EWS
+    assert _bwd(lib, dtype=-1) == EDTYPE
+
+
+def test_rope_validation(lib):
+    def call(head_dim=128, d_out=256, pos=P, cs=P, max_pos=16):
+        return lib.lora_qk_rope_fwd(1, 16, 64, d_out, 8, 1.0, P, P, P, P, head_dim, pos, cs, P, max_pos, P, P,
+                                    1 << 30, None)
+    assert call(head_dim=64) == ESHAPE
+    assert call(d_out=192) == ESHAPE
+    assert call(pos=None) == ENULL
+    assert call(cs=P + 4) == EALIGN
+    assert call(max_pos=0) == ESHAPE
+    assert lib.lora_rope_cache(0, 128, 5e5, P, P, None) == ESHAPE
+    assert lib.lora_rope_cache(16, 128, -1.0, P, P, None) == ESHAPE
+    assert lib.lora_rope_cache(16, 128, 5e5, None, P, None) == ENULL
+
+
+def test_nf4_validation(lib):
+    tab = (ctypes.c_float * 16)(*range(16))
+
+    def call(d_in=128, bs=64, codes=P, table=tab):
+        return lib.nf4_lora_linear_fwd(16, d_in, 64, 8, 1.0, P, codes, P, bs, table, P, P, P, P, 1 << 30, None)
+    assert call(bs=32) == ESHAPE
+    assert call(d_in=96) == ESHAPE
+    assert call(codes=None) == ENULL
+    assert call(table=None) == ENULL
+    assert lib.nf4_dequant(P, P, 64, 100, tab, P, None) == ESHAPE
+    assert lib.nf4_dequant(P, P, 64, 128, None, P, None) == ENULL
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="checks the no-GPU path only")
+def test_valid_call_without_gpu_reports_device_error(lib):
+    # Arguments pass validation; with no device the library reports LORA_ERR_DEVICE
+    # and launches nothing.
+    assert _fwd(lib) == EDEV
