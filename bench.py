@@ -1,0 +1,308 @@
+#!/usr/bin/env python3
+"""Throughput of the fused LoRA linear layer (forward + backward) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3]
+
+One step is one forward and one backward through every projection of the
+workload (the whole hot path): Y = X W^T + s (X A^T) B^T with the optional RoPE
+epilogue or NF4 base weight, then dX, dA, dB with X A^T recomputed.  Inputs
+are seeded synthetic tensors drawn directly in HBM before timing.
+
+Prints ONE JSON line: TFLOP/s of useful work (2M(2dk + 3r(d+k)) per
+projection), tokens/s, the fraction of the bf16 dense MFMA peak, a roofline
+entry for the dominant kernel (its launches timed with HIP events on the
+library's stream during the timed steps), and the float64 oracle timed on a
+bounded token sample on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused LoRA linear fwd+bwd TFLOP/s & tokens/s, % bf16 MFMA peak, 1 GPU"
+PEAK = {"bf16": 2516.6, "f32": 157.3}  # TFLOP/s, dense MFMA (MI355X: 256 CU x 2.4 GHz)
+HBM_PEAK = 8000.0  # GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["lora_linear_layers_amd/csrc/gemm.h", "lora_linear_layers_amd/csrc/kernels.hip",
+                  "lora_linear_layers_amd/csrc/api.cpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload: 1..5 (3 = Llama-3-8B MLP)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (reference kernel for HBM counters)")
+    return ap.parse_args()
+
+
+class Workload:
+    """Device tensors and preallocated outputs for every projection of a config."""
+
+    def __init__(self, cfg, device="cuda"):
+        import torch
+
+        import lora_linear_layers_amd as L
+        from synth import gen
+        from synth.configs import Inputs
+
+        self.cfg = cfg
+        self.L = L
+        inp = Inputs(cfg, device=device)
+        self.items = []
+        xs = {}
+        M, r = cfg.M, cfg.r
+        if any(p.rope for p in cfg.projections):
+            self.pos = inp.positions()
+            self.cos, self.sin = L.rope_cache(cfg.seq_len, cfg.head_dim, cfg.rope_theta, device=device)
+        self.table = gen.nf4_table()
+        wsmax = 0
+        dt = L.LORA_F32 if cfg.dtype == "f32" else L.LORA_BF16
+        for p in cfg.projections:
+            if p.x_group not in xs:
+                xs[p.x_group] = inp.X(p)
+            it = {"p": p, "X": xs[p.x_group], "A": inp.A(p), "B": inp.B(p), "dY": inp.dY(p)}
+            if cfg.nf4:
+                it["codes"], it["absmax"] = inp.nf4(p)
+                ops = (L.OP_NF4_FWD, L.OP_NF4_BWD)
+            else:
+                it["W"] = inp.W(p)
+                ops = (L.OP_ROPE_FWD, L.OP_ROPE_BWD) if p.rope else (L.OP_FWD, L.OP_BWD)
+            tdt = it["X"].dtype
+            it["Y"] = torch.empty(M, p.d_out, dtype=tdt, device=device)
+            it["dX"] = torch.empty(M, p.d_in, dtype=tdt, device=device)
+            it["dA"] = torch.empty(r, p.d_in, dtype=torch.float32, device=device)
+            it["dB"] = torch.empty(p.d_out, r, dtype=torch.float32, device=device)
+            for op in ops:
+                wsmax = max(wsmax, L.workspace_bytes(op, dt, M, p.d_in, p.d_out, r))
+            self.items.append(it)
+        self.ws = torch.empty(max(wsmax, 256), dtype=torch.uint8, device=device)
+        torch.cuda.synchronize()
+
+    def step(self):
+        L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
+        for it in self.items:
+            p = it["p"]
+            if cfg.nf4:
+                L.nf4_lora_linear_fwd(it["X"], it["codes"], it["absmax"], self.table, it["A"], it["B"], s,
+                                      p.d_out, Y=it["Y"], ws=ws)
+            elif p.rope:
+                L.lora_qk_rope_fwd(it["X"], it["W"], it["A"], it["B"], s, self.pos, self.cos, self.sin,
+                                   Y=it["Y"], ws=ws)
+            else:
+                L.lora_linear_fwd(it["X"], it["W"], it["A"], it["B"], s, Y=it["Y"], ws=ws)
+        for it in reversed(self.items):
+            p = it["p"]
+            out = (it["dX"], it["dA"], it["dB"])
+            if cfg.nf4:
+                _nf4_bwd(L, it, self.table, s, ws, out)
+            elif p.rope:
+                _rope_bwd(L, it, self, s, ws, out)
+            else:
+                L.lora_linear_bwd(it["X"], it["W"], it["A"], it["B"], s, it["dY"], ws=ws, out=out)
+
+
+def _rope_bwd(L, it, w, s, ws, out):
+    from lora_linear_layers_amd import _lib
+
+    X, W, A, B, dY = it["X"], it["W"], it["A"], it["B"], it["dY"]
+    M, d_in = X.shape
+    d_out, r = B.shape
+    dt = _lib._dtype_code(X)
+    dX, dA, dB = out
+    _lib._check("lora_qk_rope_bwd", _lib.lib().lora_qk_rope_bwd(
+        dt, M, d_in, d_out, r, float(s), _lib._ptr(X), _lib._ptr(W), _lib._ptr(A), _lib._ptr(B), 128,
+        _lib._ptr(w.pos), _lib._ptr(w.cos), _lib._ptr(w.sin), w.cos.shape[0], _lib._ptr(dY), _lib._ptr(dX),
+        _lib._ptr(dA), _lib._ptr(dB), _lib._ptr(ws), ws.numel(), _lib._stream(X.device)))
+
+
+def _nf4_bwd(L, it, table, s, ws, out):
+    from lora_linear_layers_amd import _lib
+
+    X, A, B, dY = it["X"], it["A"], it["B"], it["dY"]
+    M, d_in = X.shape
+    d_out, r = B.shape
+    dX, dA, dB = out
+    tab = _lib._table_ptr(table)
+    _lib._check("nf4_lora_linear_bwd", _lib.lib().nf4_lora_linear_bwd(
+        M, d_in, d_out, r, float(s), _lib._ptr(X), _lib._ptr(it["codes"]), _lib._ptr(it["absmax"]), 64, tab,
+        _lib._ptr(A), _lib._ptr(B), _lib._ptr(dY), _lib._ptr(dX), _lib._ptr(dA), _lib._ptr(dB), _lib._ptr(ws),
+        ws.numel(), _lib._stream(X.device)))
+
+
+def cpu_baseline(cfg, work, target_s):
+    """The float64 oracle, untuned, on the first S tokens of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    cpu = []
+    for it in work.items:
+        d = {"p": it["p"], "A": it["A"].cpu(), "B": it["B"].cpu()}
+        if cfg.nf4:
+            d["codes"], d["absmax"] = it["codes"].cpu().numpy(), it["absmax"].cpu().numpy()
+        else:
+            d["W"] = it["W"].cpu()
+        d["Xf"], d["dYf"] = it["X"], it["dY"]
+        cpu.append(d)
+    pos_all = work.pos.cpu().numpy() if hasattr(work, "pos") else None
+
+    def run(S):
+        t0 = time.perf_counter()
+        for d in cpu:
+            p = d["p"]
+            X, dY = d["Xf"][:S].cpu(), d["dYf"][:S].cpu()
+            s = cfg.scale
+            if cfg.nf4:
+                O.nf4_lora_forward(X, d["codes"], d["absmax"], work.table, d["A"], d["B"], s, p.d_out, p.d_in)
+                O.nf4_lora_backward(X, d["codes"], d["absmax"], work.table, d["A"], d["B"], s, dY, p.d_out, p.d_in)
+            elif p.rope:
+                O.qk_rope_forward(X, d["W"], d["A"], d["B"], s, pos_all[:S])
+                O.qk_rope_backward(X, d["W"], d["A"], d["B"], s, pos_all[:S], dY)
+            else:
+                O.lora_forward(X, d["W"], d["A"], d["B"], s)
+                O.lora_backward(X, d["W"], d["A"], d["B"], s, dY)
+        return time.perf_counter() - t0
+
+    # a first sample fixes the per-token cost (its fixed part, the weights'
+    # widening to float64, makes the estimate conservative); then the largest
+    # sample expected to fit the time target, up to the whole workload
+    S0 = min(cfg.M, 512)
+    t0 = run(S0)
+    S = int(min(cfg.M, S0 * target_s / max(t0, 1e-3)))
+    S = max(S0, (S // 64) * 64 if S < cfg.M else cfg.M)
+    t = run(S) if S != S0 else t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [torch.get_num_threads()])
+    flop = cfg.useful_flop(S)
+    return {"value": S / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.M} tokens through all {len(cfg.projections)} projections, "
+                      f"forward+backward, float64 numpy ({t:.1f} s; {flop / t / 1e9:.1f} GFLOP/s useful)",
+            "seconds": round(t, 2), "tflops_equiv": flop / t / 1e12}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import lora_linear_layers_amd as L
+    from lora_linear_layers_amd import _lib
+    from synth import CONFIGS
+
+    L.load()
+    cfg = CONFIGS[args.config]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    work = Workload(cfg, device=dev)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    for _ in range(args.warmup):
+        work.step()
+    torch.cuda.synchronize()
+
+    launches_per_step = 16 * len(cfg.projections)
+    _lib.profile_begin(launches_per_step * max(args.steps, 1) + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        work.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.profile_end()
+    rep = _lib.profile_report()
+
+    sec = (t1 - t0) / max(args.steps, 1)
+    flop = cfg.useful_flop()
+    tflops = flop / sec / 1e12
+    tokens = cfg.M / sec
+    peak = PEAK["f32" if cfg.dtype == "f32" else "bf16"]
+
+    kernels = {}
+    for name, (ms, n, fl, by) in sorted(rep.items(), key=lambda kv: -kv[1][0]):
+        kernels[name] = {"launches": n, "avg_us": round(1e3 * ms / n, 2), "share": round(ms / (sec * 1e3 * args.steps), 4),
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
+                         "gbps": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+    dom = max(rep.items(), key=lambda kv: kv[1][0])
+    dname, (dms, dn, dfl, dby) = dom
+    kpeak = PEAK["f32" if "f32" in dname else "bf16"]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get("kernels", {}).get(dname)
+            if ent and tr.get("kernel_hash") == kernel_hash() and tr.get("config") == cfg.cfg_id:
+                traffic = ent["bytes_per_launch"]
+        except (ValueError, KeyError):
+            traffic = None
+    roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": kpeak,
+                "unit": "TFLOP/s", "frac": round(achieved / kpeak, 4), "traffic": traffic,
+                "avg_launch_us": round(1e3 * dms / dn, 1), "flop_per_launch": dfl / dn,
+                "algorithmic_bytes_per_launch": dby / dn}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "tokens_per_s": round(tokens, 1),
+        "pct_bf16_peak": round(100.0 * tflops / PEAK["bf16"], 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else ("nf4w-bf16" if cfg.nf4 else "bf16"),
+        "data": "synthetic (seeded splitmix64 draws: X,dY~N(0,1), W~N(0,1/d_in), A~U(+-1/sqrt(d_in)), "
+                "B~N(0,0.02); NF4 codes uniform)",
+        "config": {"workload": cfg.name, "tokens": cfg.M, "batch": cfg.batch, "seq_len": cfg.seq_len,
+                   "r": cfg.r, "alpha": cfg.alpha, "nf4_base": cfg.nf4,
+                   "projections": [f"{p.name} {p.d_in}->{p.d_out}{' +rope' if p.rope else ''}"
+                                   for p in cfg.projections],
+                   "useful_tflop_per_step": round(flop / 1e12, 4), "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, work, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
