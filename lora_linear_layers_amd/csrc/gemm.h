@@ -19,15 +19,25 @@
 //   Bop, BL_NF4      : segment 1 is W given as NF4 codes + absmax; segment 2 plain.
 //
 // Tiles: BM x BN per workgroup, 128 bytes of contraction per stage (64 bf16 or
-// 32 fp32), two LDS stages, one barrier per stage.  Waves form a WM x WN grid
-// and each owns a (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks.
+// 32 fp32), two LDS stages.  Waves form a WM x WN grid and each owns a
+// (BM/WM) x (BN/WN) sub-tile of 16x16 MFMA blocks.
+//
+// Schedules.  With 8 waves (two per SIMD) the workgroup runs a ping-pong:
+// waves 0-3 (one per SIMD) and waves 4-7 alternate between a compute phase
+// (fragment reads + MFMAs on stage t) and a memory phase (write the stage t+1
+// operand they loaded into LDS, then issue the global loads of stage t+2).
+// Group 0 moves the A operand, group 1 the B operand.  Phases are separated
+// by raw s_barriers (no memory fence, so loads stay in flight across them), and
+// every SIMD always has one wave issuing MFMAs.  Configurations with 4 waves
+// use one double-buffered loop in which every thread loads both operands.
 // bf16 uses v_mfma_f32_16x16x32_bf16, fp32 uses v_mfma_f32_16x16x4_f32 (true
 // fp32 products, no reduced-precision inputs).
 //
 // LDS rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored at
-// chunk c ^ ((r & 7) ^ ((r >> 3) & 1)), which spreads both the 16-byte stores
-// of the loaders and the 16-byte fragment reads of 16 consecutive rows over
-// distinct banks.
+// chunk c ^ (r & 7).  Measured on gfx950 (LDS bank-conflict counters): with
+// this swizzle a 64-lane ds_read_b128 of 16 consecutive rows at one chunk
+// takes 4 cycles with no conflicts (256 B/clk), and the loaders' row-major
+// ds_write_b128 are conflict-free as well.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -77,7 +87,7 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return (row << 7) + ((chunk ^ ((row & 7) ^ ((row >> 3) & 1))) << 4);
+  return (row << 7) + ((chunk ^ (row & 7)) << 4);
 }
 
 __device__ __forceinline__ uint16_t f2bf(float x) {
@@ -112,33 +122,54 @@ __device__ __forceinline__ void nf4_fill_tab2(float2* tab2, const float* table, 
 template <typename T, int BM, int BN, int WM, int WN, bool B_NN, int EPI, int BL>
 struct GemmCfg {
   static constexpr int NT = 64 * WM * WN;
+  static constexpr bool PP = (WM * WN == 8);   // ping-pong schedule
+  static constexpr int NTL = PP ? NT / 2 : NT;  // threads per loading role
   static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte chunk
   static constexpr int BK = 128 / (int)sizeof(T);
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 16, FN = TN / 16;
   static constexpr int STAGE = (BM + BN) * 128;
   static constexpr int LDS = 2 * STAGE + (BL == BL_NF4 ? 2048 : 0);
-  // per-thread load counts
-  static constexpr int CA = (BM * 8 + NT - 1) / NT;             // A chunks
-  static constexpr int CB = (BN * 8 + NT - 1) / NT;             // B chunks (NT layout)
-  static constexpr int NBLK = 8 * (BN / E);                     // B blocks (NN layout), E x E each
-  static constexpr int CBN = (NBLK + NT - 1) / NT;
-  static constexpr int NF4U = BN * 2;                           // NF4 half-row units (NT layout)
-  static constexpr int CNF = (NF4U + NT - 1) / NT;
-  static constexpr int NF4B = 8 * (BN / 8);                     // NF4 8x8 blocks (NN layout)
-  static constexpr int CNFB = (NF4B + NT - 1) / NT;
+  // per loading thread
+  static constexpr int CA = BM * 8 / NTL;                       // A chunks
+  static constexpr int CB = BN * 8 / NTL;                       // B chunks (weight layout)
+  static constexpr int NBLK = 8 * (BN / E);                     // B blocks (contraction-row layout), E x E
+  static constexpr int CBN = (NBLK + NTL - 1) / NTL;
+  static constexpr int NF4U = BN * 2;                           // NF4 half-row units (weight layout)
+  static constexpr int CNF = (NF4U + NTL - 1) / NTL;
+  static constexpr int NF4B = BN;                               // NF4 8x8 blocks (contraction-row layout)
+  static constexpr int CNFB = (NF4B + NTL - 1) / NTL;
+  static constexpr int PB_PLAIN = B_NN ? CBN * E : CB;          // B prefetch, 16-byte registers
+  static constexpr int PB_NF4 = B_NN ? CNFB * 2 : CNF;
+  static constexpr int PB = (BL == BL_NF4 && PB_NF4 > PB_PLAIN) ? PB_NF4 : PB_PLAIN;
+  static constexpr int PAM = BL == BL_NF4 ? (B_NN ? CNFB * 8 : CNF) : 1;
+  static constexpr int OFFB = PP ? 0 : CA;                      // B registers follow A's unless roles split
+  static constexpr int PRE = PP ? (CA > PB ? CA : PB) : CA + PB;
   static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "tile/wave mismatch");
+  static_assert((BM * 8) % NTL == 0 && (BN * 8) % NTL == 0, "16-byte chunks must divide over the threads");
   static_assert(EPI != EPI_ROPE || TN == 128, "RoPE epilogue needs 128-wide wave columns");
   static_assert(BL == BL_PLAIN || sizeof(T) == 2, "NF4 weights feed bf16 MFMA");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
+// Workgroup barrier for LDS hand-offs: this wave's LDS traffic is complete,
+// then s_barrier.  Unlike __syncthreads() it carries no memory fence, so global
+// loads already in flight stay in flight.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <typename T, int BM, int BN, int WM, int WN, bool B_NN, int EPI, int BL>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_kernel(const GemmArgs p) {
   using C = GemmCfg<T, BM, BN, WM, WN, B_NN, EPI, BL>;
-  constexpr int NT = C::NT, E = C::E, BK = C::BK, FM = C::FM, FN = C::FN;
+  constexpr int NT = C::NT, NTL = C::NTL, E = C::E, BK = C::BK, FM = C::FM, FN = C::FN;
   constexpr bool BF16 = sizeof(T) == 2;
+  constexpr bool PP = C::PP;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   float2* tab2 = reinterpret_cast<float2*>(smem + 2 * C::STAGE);
 
@@ -146,6 +177,10 @@ gemm_kernel(const GemmArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l16 = lane & 15, g = lane >> 4;
+  // loading roles: with the ping-pong, waves 0..3 move A and waves 4..7 move B
+  const bool role_a = PP ? tid < NTL : true;
+  const bool role_b = PP ? tid >= NTL : true;
+  const int lt = PP ? (tid & (NTL - 1)) : tid;
 
   const int bid = blockIdx.x;
   const int64_t m0 = (int64_t)(bid % p.tiles_m) * BM;
@@ -162,47 +197,84 @@ gemm_kernel(const GemmArgs p) {
   const int nk2 = (EPI == EPI_PARTIAL) ? 0 : (int)((p.K2 + BK - 1) / BK);
   const int nk = nk1 + nk2;
 
-  if constexpr (BL == BL_NF4) {
-    nf4_fill_tab2(tab2, p.nf4_table, tid, NT);
-  }
-
-  // ---------------- prefetch registers ----------------
-  u32x4 ra[C::CA];
-  u32x4 rb[B_NN ? 1 : C::CB];
-  u32x4 rbn[B_NN ? C::CBN * E : 1];
-  u32x4 rnf[BL == BL_NF4 && !B_NN ? C::CNF : 1];
-  float ramf[BL == BL_NF4 && !B_NN ? C::CNF : 1];
-  uint32_t rnfb[BL == BL_NF4 && B_NN ? C::CNFB * 8 : 1];
-  float ramb[BL == BL_NF4 && B_NN ? C::CNFB * 8 : 1];
-
+  // ---------------- prefetch registers (shared by the two roles) ----------
+  u32x4 pre[C::PRE];
+  float pam[C::PAM];
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-  auto load_stage = [&](int t) {
-    const bool seg1 = t < nk1;
-    const T* A = reinterpret_cast<const T*>(seg1 ? p.a1 : p.a2);
-    const T* B = reinterpret_cast<const T*>(seg1 ? p.b1 : p.b2);
-    const int64_t lda = seg1 ? p.lda1 : p.lda2;
-    const int64_t ldb = seg1 ? p.ldb1 : p.ldb2;
-    const int64_t kb = seg1 ? kbeg + (int64_t)t * BK : (int64_t)(t - nk1) * BK;
-    const int64_t kv = seg1 ? kend : p.K2;
-    // A: BM rows x 8 chunks
+  // Segment-1 loads of tiles that lie wholly inside the operands take a
+  // wave-uniform base plus a fixed 32-bit per-lane byte offset (no masks, no
+  // per-load 64-bit address arithmetic); tails and segment 2 use masked loads.
+  const bool a_full = m0 + BM <= p.m_load;
+  const bool b_full = n0 + BN <= p.n_load;
+  const char* a1t = reinterpret_cast<const char*>(p.a1) + m0 * p.lda1 * (int64_t)sizeof(T);
+  const char* b1t = reinterpret_cast<const char*>(p.b1) + (B_NN ? n0 : n0 * p.ldb1) * (int64_t)sizeof(T);
+  // per-lane offsets, shared like the prefetch registers: A's first, then B's
+  // (with the ping-pong each wave only holds its own role's)
+  constexpr int NOB = B_NN ? C::CBN : C::CB;
+  constexpr int OFFO = PP ? 0 : C::CA;
+  uint32_t off[PP ? (C::CA > NOB ? C::CA : NOB) : C::CA + NOB];
+  uint32_t* offa = off;
+  uint32_t* offb = off + OFFO;
+  if (role_a) {
 #pragma unroll
     for (int i = 0; i < C::CA; ++i) {
-      const int q = tid + i * NT;
-      const int row = q >> 3, c = q & 7;
-      const int64_t gm = m0 + row, gk = kb + c * E;
-      u32x4 v = zero4;
-      if (q < BM * 8 && gm < p.m_load && gk < kv)
-        v = *reinterpret_cast<const u32x4*>(A + gm * lda + gk);
-      ra[i] = v;
+      const int q = lt + i * NTL;
+      offa[i] = (uint32_t)(((q >> 3) * p.lda1 + (q & 7) * E) * (int64_t)sizeof(T));
     }
+  }
+  if (role_b) {
+    if constexpr (!B_NN) {
+#pragma unroll
+      for (int i = 0; i < C::CB; ++i) {
+        const int q = lt + i * NTL;
+        offb[i] = (uint32_t)(((q >> 3) * p.ldb1 + (q & 7) * E) * (int64_t)sizeof(T));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::CBN; ++i) {
+        const int q = lt + i * NTL;
+        offb[i] = (uint32_t)(((q & 7) * E * p.ldb1 + (q >> 3) * E) * (int64_t)sizeof(T));
+      }
+    }
+  }
+
+  // ---- A role: global -> registers ----
+  auto load_a = [&](int t) {
+    const bool seg1 = t < nk1;
+    const int64_t kb = seg1 ? kbeg + (int64_t)t * BK : (int64_t)(t - nk1) * BK;
+    if (seg1 && a_full && kb + BK <= kend) {
+      const char* base = a1t + kb * (int64_t)sizeof(T);
+#pragma unroll
+      for (int i = 0; i < C::CA; ++i) pre[i] = *reinterpret_cast<const u32x4*>(base + offa[i]);
+      return;
+    }
+    const T* A = reinterpret_cast<const T*>(seg1 ? p.a1 : p.a2);
+    const int64_t lda = seg1 ? p.lda1 : p.lda2;
+    const int64_t kv = seg1 ? kend : p.K2;
+#pragma unroll
+    for (int i = 0; i < C::CA; ++i) {
+      const int q = lt + i * NTL;
+      const int64_t gm = m0 + (q >> 3), gk = kb + (q & 7) * E;
+      u32x4 v = zero4;
+      if (gm < p.m_load && gk < kv) v = *reinterpret_cast<const u32x4*>(A + gm * lda + gk);
+      pre[i] = v;
+    }
+  };
+
+  // ---- B role: global -> registers ----
+  auto load_b = [&](int t) {
+    u32x4* rb = pre + C::OFFB;
+    const bool seg1 = t < nk1;
+    const int64_t kb = seg1 ? kbeg + (int64_t)t * BK : (int64_t)(t - nk1) * BK;
+    const int64_t kv = seg1 ? kend : p.K2;
     if constexpr (BL == BL_NF4) {
       if (seg1) {
         if constexpr (!B_NN) {
           // W rows n, 64 contraction elements = one NF4 block per row per stage
 #pragma unroll
           for (int i = 0; i < C::CNF; ++i) {
-            const int u = tid + i * NT;
+            const int u = lt + i * NTL;
             const int row = u >> 1, half = u & 1;
             const int64_t gn = n0 + row;
             u32x4 v = zero4;
@@ -211,14 +283,14 @@ gemm_kernel(const GemmArgs p) {
               v = *reinterpret_cast<const u32x4*>(p.codes + gn * p.codes_ld + (kb >> 1) + half * 16);
               am = p.absmax[gn * p.blocks_per_row + (kb >> 6)];
             }
-            rnf[i] = v;
-            ramf[i] = am;
+            rb[i] = v;
+            pam[i] = am;
           }
         } else {
           // W rows = contraction (d_out), columns = n (d_in): 8x8 blocks
 #pragma unroll
           for (int i = 0; i < C::CNFB; ++i) {
-            const int q = tid + i * NT;
+            const int q = lt + i * NTL;
             const int kbk = q & 7, nb = q >> 3;
             const int64_t gn = n0 + nb * 8;
 #pragma unroll
@@ -230,61 +302,86 @@ gemm_kernel(const GemmArgs p) {
                 v = *reinterpret_cast<const uint32_t*>(p.codes + gk * p.codes_ld + (gn >> 1));
                 am = p.absmax[gk * p.blocks_per_row + (gn >> 6)];
               }
-              rnfb[i * 8 + rr] = v;
-              ramb[i * 8 + rr] = am;
+              rb[i * 2 + (rr >> 2)][rr & 3] = v;
+              pam[i * 8 + rr] = am;
             }
           }
         }
         return;
       }
     }
+    if (BL == BL_PLAIN && seg1 && b_full && kb + BK <= kend) {
+      if constexpr (!B_NN) {
+        const char* base = b1t + kb * (int64_t)sizeof(T);
+#pragma unroll
+        for (int i = 0; i < C::CB; ++i) rb[i] = *reinterpret_cast<const u32x4*>(base + offb[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::CBN; ++i) {
+          const int q = lt + i * NTL;
+#pragma unroll
+          for (int rr = 0; rr < E; ++rr) {
+            const char* base = b1t + (kb + rr) * p.ldb1 * (int64_t)sizeof(T);
+            u32x4 v = zero4;
+            if (q < C::NBLK) v = *reinterpret_cast<const u32x4*>(base + offb[i]);
+            rb[i * E + rr] = v;
+          }
+        }
+      }
+      return;
+    }
+    const T* B = reinterpret_cast<const T*>(seg1 ? p.b1 : p.b2);
+    const int64_t ldb = seg1 ? p.ldb1 : p.ldb2;
     if constexpr (!B_NN) {
 #pragma unroll
       for (int i = 0; i < C::CB; ++i) {
-        const int q = tid + i * NT;
-        const int row = q >> 3, c = q & 7;
-        const int64_t gn = n0 + row, gk = kb + c * E;
+        const int q = lt + i * NTL;
+        const int64_t gn = n0 + (q >> 3), gk = kb + (q & 7) * E;
         u32x4 v = zero4;
-        if (q < BN * 8 && gn < p.n_load && gk < kv)
-          v = *reinterpret_cast<const u32x4*>(B + gn * ldb + gk);
+        if (gn < p.n_load && gk < kv) v = *reinterpret_cast<const u32x4*>(B + gn * ldb + gk);
         rb[i] = v;
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::CBN; ++i) {
-        const int q = tid + i * NT;
+        const int q = lt + i * NTL;
         const int kbk = q & 7, nb = q >> 3;
         const int64_t gn = n0 + nb * E;
 #pragma unroll
         for (int rr = 0; rr < E; ++rr) {
           const int64_t gk = kb + kbk * E + rr;
           u32x4 v = zero4;
-          if (q < C::NBLK && gn < p.n_load && gk < kv)
-            v = *reinterpret_cast<const u32x4*>(B + gk * ldb + gn);
-          rbn[i * E + rr] = v;
+          if (q < C::NBLK && gn < p.n_load && gk < kv) v = *reinterpret_cast<const u32x4*>(B + gk * ldb + gn);
+          rb[i * E + rr] = v;
         }
       }
     }
   };
 
-  auto store_stage = [&](int t, int s) {
+  // ---- A role: registers -> LDS stage s ----
+  auto store_a = [&](int s) {
     char* sA = smem + s * C::STAGE;
-    char* sB = sA + BM * 128;
 #pragma unroll
     for (int i = 0; i < C::CA; ++i) {
-      const int q = tid + i * NT;
-      if (q < BM * 8) *reinterpret_cast<u32x4*>(sA + lds_off(q >> 3, q & 7)) = ra[i];
+      const int q = lt + i * NTL;
+      *reinterpret_cast<u32x4*>(sA + lds_off(q >> 3, q & 7)) = pre[i];
     }
+  };
+
+  // ---- B role: registers -> LDS stage s (transposing / dequantising) ----
+  auto store_b = [&](int t, int s) {
+    const u32x4* rb = pre + C::OFFB;
+    char* sB = smem + s * C::STAGE + BM * 128;
     if constexpr (BL == BL_NF4) {
       if (t < nk1) {
         if constexpr (!B_NN) {
 #pragma unroll
           for (int i = 0; i < C::CNF; ++i) {
-            const int u = tid + i * NT;
+            const int u = lt + i * NTL;
             if (u < C::NF4U) {
               const int row = u >> 1, half = u & 1;
-              const u32x4 v = rnf[i];
-              const float am = ramf[i];
+              const u32x4 v = rb[i];
+              const float am = pam[i];
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
                 const uint32_t word = v[w];  // 4 bytes = 8 elements
@@ -300,15 +397,15 @@ gemm_kernel(const GemmArgs p) {
         } else {
 #pragma unroll
           for (int i = 0; i < C::CNFB; ++i) {
-            const int q = tid + i * NT;
+            const int q = lt + i * NTL;
             if (q < C::NF4B) {
               const int kbk = q & 7, nb = q >> 3;
               // dequantise the 8x8 block: rows rr (contraction), columns j (n)
               uint32_t pk[8][4];  // [rr][byte] -> bf16x2 of columns 2b, 2b+1
 #pragma unroll
               for (int rr = 0; rr < 8; ++rr) {
-                const uint32_t word = rnfb[i * 8 + rr];
-                const float am = ramb[i * 8 + rr];
+                const uint32_t word = rb[i * 2 + (rr >> 2)][rr & 3];
+                const float am = pam[i * 8 + rr];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) pk[rr][b] = nf4_byte_to_bf16x2(tab2, word >> (8 * b), am);
               }
@@ -331,13 +428,13 @@ gemm_kernel(const GemmArgs p) {
     if constexpr (!B_NN) {
 #pragma unroll
       for (int i = 0; i < C::CB; ++i) {
-        const int q = tid + i * NT;
-        if (q < BN * 8) *reinterpret_cast<u32x4*>(sB + lds_off(q >> 3, q & 7)) = rb[i];
+        const int q = lt + i * NTL;
+        *reinterpret_cast<u32x4*>(sB + lds_off(q >> 3, q & 7)) = rb[i];
       }
     } else {
 #pragma unroll
       for (int i = 0; i < C::CBN; ++i) {
-        const int q = tid + i * NT;
+        const int q = lt + i * NTL;
         if (q < C::NBLK) {
           const int kbk = q & 7, nb = q >> 3;
           if constexpr (BF16) {
@@ -348,8 +445,8 @@ gemm_kernel(const GemmArgs p) {
               u32x4 o;
 #pragma unroll
               for (int pp = 0; pp < 4; ++pp) {
-                const uint32_t x0 = rbn[i * 8 + 2 * pp][j >> 1];
-                const uint32_t x1 = rbn[i * 8 + 2 * pp + 1][j >> 1];
+                const uint32_t x0 = rb[i * 8 + 2 * pp][j >> 1];
+                const uint32_t x1 = rb[i * 8 + 2 * pp + 1][j >> 1];
                 o[pp] = (j & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
               }
               *reinterpret_cast<u32x4*>(sB + lds_off(nb * 8 + j, kbk)) = o;
@@ -359,16 +456,25 @@ gemm_kernel(const GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               u32x4 o;
-              o[0] = rbn[i * 4 + 0][j];
-              o[1] = rbn[i * 4 + 1][j];
-              o[2] = rbn[i * 4 + 2][j];
-              o[3] = rbn[i * 4 + 3][j];
+              o[0] = rb[i * 4 + 0][j];
+              o[1] = rb[i * 4 + 1][j];
+              o[2] = rb[i * 4 + 2][j];
+              o[3] = rb[i * 4 + 3][j];
               *reinterpret_cast<u32x4*>(sB + lds_off(nb * 4 + j, kbk)) = o;
             }
           }
         }
       }
     }
+  };
+
+  auto load_role = [&](int t) {
+    if (role_a) load_a(t);
+    if (role_b) load_b(t);
+  };
+  auto store_role = [&](int t, int s) {
+    if (role_a) store_a(s);
+    if (role_b) store_b(t, s);
   };
 
   f32x4 acc[FM][FN];
@@ -435,17 +541,41 @@ gemm_kernel(const GemmArgs p) {
     }
   };
 
-  // ---------------- main loop: two LDS stages, one barrier per stage -------
+  // ---------------- main loop ----------------
   if (nk > 0) {
-    load_stage(0);
-    if constexpr (BL == BL_NF4) __syncthreads();  // tab2 ready
-    store_stage(0, 0);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-      if (t + 1 < nk) load_stage(t + 1);
-      compute_stage(t & 1);
-      if (t + 1 < nk) store_stage(t + 1, (t + 1) & 1);
+    if constexpr (BL == BL_NF4) {
+      nf4_fill_tab2(tab2, p.nf4_table, tid, NT);
+      __syncthreads();  // tab2 ready before the first dequantising store
+    }
+    load_role(0);
+    store_role(0, 0);
+    if constexpr (PP) {
+      if (nk > 1) load_role(1);
+      lds_barrier();
+      const bool first = wave < WM * WN / 2;  // computes in the first phase of each stage
+      for (int t = 0; t < nk; ++t) {
+        if (first) {
+          compute_stage(t & 1);
+          lds_barrier();
+          if (t + 1 < nk) store_role(t + 1, (t + 1) & 1);
+          if (t + 2 < nk) load_role(t + 2);
+          lds_barrier();
+        } else {
+          if (t + 1 < nk) store_role(t + 1, (t + 1) & 1);
+          if (t + 2 < nk) load_role(t + 2);
+          lds_barrier();
+          compute_stage(t & 1);
+          lds_barrier();
+        }
+      }
+    } else {
       __syncthreads();
+      for (int t = 0; t < nk; ++t) {
+        if (t + 1 < nk) load_role(t + 1);
+        compute_stage(t & 1);
+        if (t + 1 < nk) store_role(t + 1, (t + 1) & 1);
+        __syncthreads();
+      }
     }
   }
 

@@ -62,15 +62,15 @@ TileShape gemm_tile(GemmKind k) {
 
 hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
   switch (k) {
-    case G_BF16_BIG_NT_STORE: return run<bf, 256, 256, 4, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
-    case G_BF16_BIG_NT_ROPE: return run<bf, 256, 256, 4, 2, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NT_STORE: return run<bf, 256, 256, 2, 4, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NT_ROPE: return run<bf, 256, 256, 2, 2, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_ROPE: return run<bf, 128, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
-    case G_BF16_BIG_NN_STORE: return run<bf, 256, 256, 4, 2, true, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NN_STORE: return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_PLAIN>(a, splits, st);
-    case G_NF4_BIG_NT_STORE: return run<bf, 256, 256, 4, 2, false, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_NF4_BIG_NT_STORE: return run<bf, 256, 256, 2, 4, false, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_NF4>(a, splits, st);
-    case G_NF4_BIG_NN_STORE: return run<bf, 256, 256, 4, 2, true, EPI_STORE, BL_NF4>(a, splits, st);
+    case G_NF4_BIG_NN_STORE: return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_NF4>(a, splits, st);
     case G_BF16_PANEL_NT_STORE: return run<bf, 64, 64, 2, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_BF16_PANEL_NT_STORE_T: return run<bf, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
