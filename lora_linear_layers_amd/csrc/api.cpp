@@ -54,7 +54,7 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t r8 = 0, M8 = 0;
-  size_t bpad = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, total = 0;
+  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, total = 0;
   int splits_dA = 1, splits_dB = 1;
   int64_t ksplit_dA = 0, ksplit_dB = 0;
 };
@@ -92,6 +92,7 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.p = take(size_t(M) * L.r8 * eb);
   } else {
     if (op == LORA_OP_ROPE_BWD) L.g = take(size_t(M) * d_out * eb);
+    if (eb == 2) L.bt = take(size_t(L.r8) * d_out * eb);
     L.pt = take(size_t(L.r8) * L.M8 * eb);
     L.qs = take(size_t(L.M8) * L.r8 * eb);
     L.qt = take(size_t(L.r8) * L.M8 * eb);
@@ -151,6 +152,8 @@ enum ProfKind : int {
   K_FILL,
   K_ROPE_CACHE,
   K_NF4_DEQ,
+  K_PANEL,
+  K_TRANSPOSE,
   K_PROF_COUNT
 };
 
@@ -164,7 +167,8 @@ const char* kind_name(int k) {
       "gemm_f32_64x128_nt_rope",    "gemm_f32_64x128_nn_store",   "panel_f32_nt_store",
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
       "pad_cols",                   "rope_inverse",               "reduce_splits",
-      "fill_zero",                  "rope_cache",                 "nf4_dequant"};
+      "fill_zero",                  "rope_cache",                 "nf4_dequant",
+      "panel_bf16_stream",          "transpose_pad"};
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
 
@@ -242,13 +246,19 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   void* P = w + L.p;
   const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r), e = double(eb);
   // panel: P = s * X A^T  [M, r8] (columns r..r8 are exact zeros)
-  {
+  if (f32) {
     GemmArgs a = blank();
     a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
     a.m_load = M; a.m_store = M; a.n_load = r; a.n_store = L.r8;
     a.c = P; a.ldc = L.r8; a.alpha = scale;
-    HIPTRY(gemm(f32 ? G_F32_PANEL_NT_STORE : G_BF16_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki,
-                (Md * ki + rr * ki + Md * L.r8) * e));
+    HIPTRY(gemm(G_F32_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
+  } else {
+    PanelArgs pa{};
+    pa.x = static_cast<const uint16_t*>(X); pa.ldx = d_in; pa.w = static_cast<const uint16_t*>(A); pa.ldw = d_in;
+    pa.M = M; pa.K = d_in; pa.n_valid = r; pa.m_store = M; pa.n_store = L.r8; pa.alpha = scale;
+    pa.out = static_cast<uint16_t*>(P); pa.ldo = L.r8;
+    HIPTRY(timed(K_PANEL, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e, st,
+                 [&] { return launch_panel(pa, st); }));
   }
   // main: Y = [X | P] [W | B]^T, optional RoPE epilogue
   GemmArgs a = blank();
@@ -305,23 +315,42 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   void* Qs = w + L.qs;
   void* Qt = w + L.qt;
   float* part = reinterpret_cast<float*>(w + L.part);
-  // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
-  {
-    GemmArgs a = blank();
-    a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
-    a.m_load = M; a.m_store = L.M8; a.n_load = r; a.n_store = L.r8;
-    a.ct = Pt; a.ldct = L.M8; a.alpha = scale;
-    HIPTRY(gemm(f32 ? G_F32_PANEL_NT_STORE_T : G_BF16_PANEL_NT_STORE_T, a, 1, st, 2 * Md * rr * ki,
-                (Md * ki + rr * ki + Md * L.r8) * e));
-  }
-  // Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
-  {
-    GemmArgs a = blank();
-    a.a1 = G; a.lda1 = d_out; a.b1 = Bsrc; a.ldb1 = L.r8; a.K1 = d_out;
-    a.m_load = M; a.m_store = L.M8; a.n_load = L.r8; a.n_store = L.r8;
-    a.c = Qs; a.ldc = L.r8; a.ct = Qt; a.ldct = L.M8; a.alpha = scale;
-    HIPTRY(gemm(f32 ? G_F32_PANEL_NN_BOTH : G_BF16_PANEL_NN_BOTH, a, 1, st, 2 * Md * rr * ko,
-                (Md * ko + rr * ko + 2 * Md * L.r8) * e));
+  if (f32) {
+    // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
+    {
+      GemmArgs a = blank();
+      a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
+      a.m_load = M; a.m_store = L.M8; a.n_load = r; a.n_store = L.r8;
+      a.ct = Pt; a.ldct = L.M8; a.alpha = scale;
+      HIPTRY(gemm(G_F32_PANEL_NT_STORE_T, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
+    }
+    // Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
+    {
+      GemmArgs a = blank();
+      a.a1 = G; a.lda1 = d_out; a.b1 = Bsrc; a.ldb1 = L.r8; a.K1 = d_out;
+      a.m_load = M; a.m_store = L.M8; a.n_load = L.r8; a.n_store = L.r8;
+      a.c = Qs; a.ldc = L.r8; a.ct = Qt; a.ldct = L.M8; a.alpha = scale;
+      HIPTRY(gemm(G_F32_PANEL_NN_BOTH, a, 1, st, 2 * Md * rr * ko, (Md * ko + rr * ko + 2 * Md * L.r8) * e));
+    }
+  } else {
+    // Pt = (s X A^T)^T  [r8, M8], recomputed from X (rows M..M8 and columns r..r8 are zeros)
+    PanelArgs pa{};
+    pa.x = static_cast<const uint16_t*>(X); pa.ldx = d_in; pa.w = static_cast<const uint16_t*>(A); pa.ldw = d_in;
+    pa.M = M; pa.K = d_in; pa.n_valid = r; pa.m_store = L.M8; pa.n_store = L.r8; pa.alpha = scale;
+    pa.outt = static_cast<uint16_t*>(Pt); pa.ldot = L.M8;
+    HIPTRY(timed(K_PANEL, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e, st,
+                 [&] { return launch_panel(pa, st); }));
+    // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
+    uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
+    HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
+      return launch_transpose_pad(static_cast<const uint16_t*>(B), Bt, d_out, r, L.r8, st);
+    }));
+    PanelArgs pq{};
+    pq.x = static_cast<const uint16_t*>(G); pq.ldx = d_out; pq.w = Bt; pq.ldw = d_out;
+    pq.M = M; pq.K = d_out; pq.n_valid = r; pq.m_store = L.M8; pq.n_store = L.r8; pq.alpha = scale;
+    pq.out = static_cast<uint16_t*>(Qs); pq.ldo = L.r8; pq.outt = static_cast<uint16_t*>(Qt); pq.ldot = L.M8;
+    HIPTRY(timed(K_PANEL, 2 * Md * rr * ko, (Md * ko + rr * ko + 2 * Md * L.r8) * e, st,
+                 [&] { return launch_panel(pq, st); }));
   }
   // dX = [G | Qs] [W ; A]
   if (dX) {

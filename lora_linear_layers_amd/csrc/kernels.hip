@@ -6,6 +6,7 @@
 
 #include "gemm.h"
 #include "launch.h"
+#include "panel.h"
 
 namespace lora {
 
@@ -87,9 +88,27 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
   }
 }
 
+hipError_t launch_panel(const PanelArgs& a, hipStream_t st) {
+  const int64_t gx = (a.m_store + panel::ROWS - 1) / panel::ROWS;
+  const int64_t gy = (a.n_store + panel::COLS - 1) / panel::COLS;
+  if (gx <= 0 || gy <= 0) return hipSuccess;
+  hipLaunchKernelGGL(panel_kernel<panel::WAVES>, dim3((unsigned)gx, (unsigned)gy), dim3(64 * panel::WAVES), 0, st, a);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // small kernels
 // ---------------------------------------------------------------------------
+
+// Bt[q, i] = q < r ? B[i, q] : 0 for B [rows, r] -> Bt [r_pad, rows].
+__global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t rows,
+                                     int64_t r, int64_t r_pad) {
+  const int64_t n = rows * r_pad;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t q = e / rows, i = e - q * rows;
+    dst[e] = q < r ? src[i * r + q] : (uint16_t)0;
+  }
+}
 
 template <typename T>
 __global__ void pad_cols_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int64_t r,
@@ -105,6 +124,14 @@ static unsigned grid_for(int64_t n, int threads) {
   int64_t b = (n + threads - 1) / threads;
   if (b > 65535 * 4) b = 65535 * 4;
   return (unsigned)(b > 0 ? b : 1);
+}
+
+hipError_t launch_transpose_pad(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t r, int64_t r_pad,
+                                hipStream_t st) {
+  const int64_t n = rows * r_pad;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_pad_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, src, dst, rows, r, r_pad);
+  return hipGetLastError();
 }
 
 hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t rows, int64_t r, int64_t r_pad,

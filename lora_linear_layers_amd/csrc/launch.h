@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "gemm.h"
+#include "panel.h"
 
 namespace lora {
 
@@ -44,6 +45,13 @@ TileShape gemm_tile(GemmKind k);
 
 // Sets a.tiles_m from a.m_store and launches over (tiles_m * tiles_n, 1, splits).
 hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st);
+
+// Rank-r panel out = alpha X R^T (bf16), see panel.h.
+hipError_t launch_panel(const PanelArgs& a, hipStream_t st);
+
+// Bt[q, i] = q < r ? B[i, q] : 0, bf16 [rows, r] -> [r_pad, rows].
+hipError_t launch_transpose_pad(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t r, int64_t r_pad,
+                                hipStream_t st);
 
 // dst[i, j] = j < r ? src[i, j] : 0 for a [rows, r] matrix widened to [rows, r_pad].
 hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t rows, int64_t r,
