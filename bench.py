@@ -52,7 +52,76 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for HBM counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE run, WRITE_SIZE run of this script with --copy-calibration), then exit")
     return ap.parse_args()
+
+
+# rocprofv3 kernel names -> the library profiler's kind names
+KIND_OF = {
+    "gemm_kernel<unsigned short, 256, 256, 2, 4, false, 0, 0>": "gemm_bf16_256x256_nt_store",
+    "gemm_kernel<unsigned short, 256, 256, 2, 4, true, 0, 0>": "gemm_bf16_256x256_nn_store",
+    "gemm_kernel<unsigned short, 256, 256, 2, 2, false, 3, 0>": "gemm_bf16_256x256_nt_rope",
+    "gemm_kernel<unsigned short, 128, 128, 4, 1, false, 0, 0>": "gemm_bf16_128x128_nt_store",
+    "gemm_kernel<unsigned short, 128, 128, 4, 1, false, 3, 0>": "gemm_bf16_128x128_nt_rope",
+    "gemm_kernel<unsigned short, 128, 128, 4, 1, true, 0, 0>": "gemm_bf16_128x128_nn_store",
+    "gemm_kernel<unsigned short, 256, 256, 2, 4, false, 0, 1>": "gemm_nf4_256x256_nt_store",
+    "gemm_kernel<unsigned short, 256, 256, 2, 4, true, 0, 1>": "gemm_nf4_256x256_nn_store",
+    "gemm_kernel<unsigned short, 128, 128, 4, 1, false, 0, 1>": "gemm_nf4_128x128_nt_store",
+    "gemm_kernel<unsigned short, 128, 128, 4, 1, true, 0, 1>": "gemm_nf4_128x128_nn_store",
+    "gemm_kernel<unsigned short, 64, 256, 1, 4, true, 4, 0>": "split_bf16_nn_partial",
+    "panel_kernel<8>": "panel_bf16_stream",
+    "reduce_splits_kernel": "reduce_splits",
+    "transpose_pad_kernel": "transpose_pad",
+    "rope_inverse_kernel": "rope_inverse",
+}
+
+
+def _kind(name):
+    for k, v in KIND_OF.items():
+        if k in name:
+            return v
+    return None
+
+
+def traffic_from(fetch_csv, write_csv, cfg_id):
+    """HBM bytes per launch of each library kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled so that a 1 GiB device copy reads and
+    writes exactly 1 GiB."""
+    import csv
+
+    def per_dispatch(path, counter):
+        vals, grid = {}, {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+            grid[key] = int(r["Grid_Size"])
+        return vals, grid
+
+    out = {}
+    factors = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals, grid = per_dispatch(path, counter)
+        # the 1 GiB device-to-device copy of --copy-calibration: the runtime's
+        # copy kernel with the largest reading of this counter
+        copies = [v for (d, n), v in vals.items() if "copyBuffer" in n]
+        ref = max(copies) if copies else None
+        factor = (float(1 << 30) / (ref * 1024.0)) if ref else 1.0
+        factors[counter] = {"copy_kib": ref, "scale": factor}
+        sums = {}
+        for (d, n), v in vals.items():
+            k = _kind(n)
+            if k:
+                s, c = sums.get(k, (0.0, 0))
+                sums[k] = (s + v * 1024.0 * factor, c + 1)
+        for k, (s, c) in sums.items():
+            out.setdefault(k, {})[counter.lower() + "_bytes_per_launch"] = s / c
+    for k, v in out.items():
+        v["bytes_per_launch"] = v.get("fetch_size_bytes_per_launch", 0.0) + v.get("write_size_bytes_per_launch", 0.0)
+    return {"config": cfg_id, "kernel_hash": kernel_hash(), "scale": factors, "kernels": out}
 
 
 class Workload:
@@ -203,6 +272,13 @@ def cpu_baseline(cfg, work, target_s):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        t = traffic_from(args.traffic_from[0], args.traffic_from[1], args.config)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); "

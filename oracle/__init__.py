@@ -7,6 +7,8 @@ share no code.
 from .lora_oracle import (  # noqa: F401
     lora_forward,
     lora_backward,
+    lora_grad_x,
+    lora_grad_ab,
     lora_panel,
     rope_angles,
     rope_rotate,

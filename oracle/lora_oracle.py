@@ -68,6 +68,20 @@ def lora_forward(X, W, A, B, s: float) -> np.ndarray:
     return X @ W.T + s * (P @ B.T)
 
 
+def lora_grad_x(W, A, B, s: float, G) -> np.ndarray:
+    """dX = G W + s (G B) A: the input gradient (row-wise in G)."""
+    W, A, B, G = map(_f64, (W, A, B, G))
+    return G @ W + s * ((G @ B) @ A)
+
+
+def lora_grad_ab(X, A, B, s: float, G):
+    """(dA, dB) = (s (G B)^T X, s G^T (X A^T)), with X A^T recomputed ([P1] 反向传播优化)."""
+    X, A, B, G = map(_f64, (X, A, B, G))
+    P = X @ A.T
+    Q = G @ B
+    return s * (Q.T @ X), s * (G.T @ P)
+
+
 def lora_backward(X, W, A, B, s: float, G):
     """(dX, dA, dB) for upstream gradient G = dL/dY; no dW (W is frozen, [P3] QLoRA paragraph).
 
@@ -76,12 +90,8 @@ def lora_backward(X, W, A, B, s: float, G):
       dB = s G^T P
       dA = s (G B)^T X
     """
-    X, W, A, B, G = map(_f64, (X, W, A, B, G))
-    P = X @ A.T
-    Q = G @ B
-    dX = G @ W + s * (Q @ A)
-    dB = s * (G.T @ P)
-    dA = s * (Q.T @ X)
+    dX = lora_grad_x(W, A, B, s, G)
+    dA, dB = lora_grad_ab(X, A, B, s, G)
     return dX, dA, dB
 
 
