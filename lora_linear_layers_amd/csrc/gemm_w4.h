@@ -1,0 +1,386 @@
+// gemm_w4.h - the whole-tile bf16 GEMM of the fused LoRA linear layer on
+// gfx950: 256 x 256 x 64 tiles, 4 waves of 128 x 128, one wave per SIMD,
+// v_mfma_f32_32x32x16_bf16 with the accumulators in the accumulation
+// registers.
+//
+// Same contraction as gemm.h (two segments into one fp32 accumulator: the
+// forward [X | sXA^T] [W | B]^T and the input gradient [G | sGB] [W ; A] of
+// page "UnSloth加速微调体验…", section 算子融合), for the shapes that
+// dominate the layer: every tile whole in m and n and the first segment a
+// whole number of 64-wide stages; the rank-r segment may be ragged.
+//
+// Why this shape.  Measured with the SQ counters on MI355X, the GEMM runs
+// power-limited (about 1.8 GHz) and what separates a fast kernel from a slow
+// one is the share of cycles the MFMA pipe is busy; LDS traffic is the main
+// thing that steals those cycles.  A 128 x 128 wave tile reads each LDS row
+// twice per stage (a 64 x 128 one three times on average), and with one wave
+// per SIMD each wave owns 512 registers: 256 accumulators, two sets of
+// fragments and the register staging of the next global tile, so nothing
+// spills and no loop-invariant address is recomputed.
+//
+// Per stage t (LDS buffer t & 1) each wave runs four contraction steps of 16
+// MFMAs, each MFMA followed by one memory operation:
+//   step 0: reads of step 1's fragments, then LDS writes of stage t+1's A
+//           tile (from registers, into the other buffer)
+//   step 1: reads of step 2's fragments, then stage t+1's B tile
+//   step 2: reads of step 3's fragments, then global loads of a later A tile
+//   barrier (stage t+1 is complete, nobody reads buffer t & 1 any more)
+//   step 3: reads of stage t+1's step-0 fragments, then the later B tile
+// so the LDS and the load path see an even stream and the LDS latency at
+// stage boundaries is hidden as well.
+//
+// 32x32x16 MFMA: A lane l holds row l % 32, contraction 8 (l / 32) .. +7; B
+// lane l holds column l % 32, the same contraction range; the 16 fp32 results
+// of lane l are rows 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+//
+// LDS: [A 0][A 1][B 0][B 1], 256 rows of 128 bytes each, chunk c of row r at
+// chunk c ^ ((r >> 1) & 7) (conflict-free for these fragment reads and the
+// tile writes; measured with the LDS bank-conflict counter).
+#pragma once
+
+#include <type_traits>
+
+#include "gemm.h"
+
+namespace lora {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace w4 {
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int NT = 256;
+constexpr int TM = 128, TN = 128;          // wave tile, 2 x 2 waves
+constexpr int FM = TM / 32, FN = TN / 32;  // 4 x 4 MFMA blocks
+constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;
+constexpr int B_BASE = 2 * A_STAGE;
+constexpr int LDS = 2 * (A_STAGE + B_STAGE);
+constexpr int BIG = 0x40000000;        // resource size with nothing masked
+constexpr uint32_t OOB = 0x40000000u;  // lane offset that reads zero
+}  // namespace w4
+
+template <bool B_NN, int EPI, int PF>
+__global__ void __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_w4_kernel(const GemmArgs p) {
+  using namespace w4;
+  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE, "store or RoPE epilogue");
+  static_assert(PF == 1 || PF == 2, "one or two staged tiles");
+  __shared__ __attribute__((aligned(16))) char smem[LDS];
+  // keep the MFMA accumulators in the accumulation registers
+  asm volatile("" ::: "a0");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int lt = tid;
+
+  const int bid = blockIdx.x;
+  const int64_t m0 = (int64_t)(bid % p.tiles_m) * BM;
+  const int64_t n0 = (int64_t)(bid / p.tiles_m) * BN;
+  const int nk1 = (int)(p.K1 / BK);
+  const int nk = nk1 + (int)((p.K2 + BK - 1) / BK);
+
+  // ---- loaders ----
+  // Row-major chunks (A; B in the weight layout): lane lt moves chunk lt & 7
+  // of rows (lt >> 3) + 32 i, i < 8.  B_NN: lane lt moves the 8 x 8 block of
+  // contraction rows 8 (lt & 7) + i and columns 8 (lt >> 3) .. +7.  Every
+  // load is a raw buffer load (wave-uniform resource + one lane offset); an
+  // offset at or beyond the resource's size reads zero, which masks the
+  // ragged rank-r segment.
+  const int kc = (lt & 7) * 8;
+  const char* ga1 = reinterpret_cast<const char*>(p.a1) + m0 * p.lda1 * 2;
+  const char* ga2 = reinterpret_cast<const char*>(p.a2) + m0 * p.lda2 * 2;
+  const uint32_t va1 = (uint32_t)((lt >> 3) * p.lda1 * 2 + (lt & 7) * 16);
+  const uint32_t va2 = (uint32_t)((lt >> 3) * p.lda2 * 2 + (lt & 7) * 16);
+  const char* gb1 = reinterpret_cast<const char*>(p.b1) + (B_NN ? n0 * 2 : n0 * p.ldb1 * 2);
+  const char* gb2 = reinterpret_cast<const char*>(p.b2) + (B_NN ? n0 * 2 : n0 * p.ldb2 * 2);
+  const uint32_t vb1 = B_NN ? (uint32_t)(kc * p.ldb1 * 2 + (lt >> 3) * 16)
+                            : (uint32_t)((lt >> 3) * p.ldb1 * 2 + (lt & 7) * 16);
+  const uint32_t vb2 = B_NN ? (uint32_t)(kc * p.ldb2 * 2 + (lt >> 3) * 16)
+                            : (uint32_t)((lt >> 3) * p.ldb2 * 2 + (lt & 7) * 16);
+  // segment 2 of B_NN: rows at or beyond K2 lie past the resource's end
+  const int nrecb2 = B_NN ? (int)(p.K2 * p.ldb2 * 2 - n0 * 2) : BIG;
+  // per-segment strides, pinned in scalar registers (a select between two
+  // kernel arguments is otherwise turned into a load from a selected
+  // address inside the loop, whose wait drains every LDS operation)
+  const uint32_t isa1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda1 * 2));
+  const uint32_t isa2 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda2 * 2));
+  const uint32_t isb1 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(p.ldb1 * 2) : (uint32_t)(32 * p.ldb1 * 2));
+  const uint32_t isb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(p.ldb2 * 2) : (uint32_t)(32 * p.ldb2 * 2));
+  const int64_t kstb1 = B_NN ? (int64_t)BK * p.ldb1 * 2 : (int64_t)BK * 2;
+  const uint32_t kstb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(BK * p.ldb2 * 2) : (uint32_t)(BK * 2));
+  const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
+
+  u32x4 sa[PF][8], sb[PF][8];
+
+  // Global loads of stage u (u < nk): a per-stage descriptor (uniform
+  // resource, lane offset, stride between a lane's 8 chunks), then one
+  // 16-byte load per chunk into staging buffer b.
+  struct LoadDesc {
+    __amdgpu_buffer_rsrc_t r;
+    uint32_t vo, is;
+  };
+  auto desc_a = [&](int u) {
+    const bool seg1 = u < nk1;
+    const int tt = u - nk1;
+    const char* base = seg1 ? ga1 + (int64_t)u * (BK * 2) : ga2;
+    LoadDesc d;
+    d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, BIG, 0x00020000);
+    d.vo = seg1 ? va1 : (tt * BK + kc < k2 ? va2 + (uint32_t)(tt * BK * 2) : OOB);
+    d.is = seg1 ? isa1 : isa2;
+    return d;
+  };
+  auto desc_b = [&](int u) {
+    const bool seg1 = u < nk1;
+    const int tt = u - nk1;
+    LoadDesc d;
+    const char* base = seg1 ? gb1 + (int64_t)u * kstb1 : gb2;
+    d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (B_NN && !seg1) ? nrecb2 : BIG,
+                                            0x00020000);
+    if constexpr (!B_NN)
+      d.vo = seg1 ? vb1 : (tt * BK + kc < k2 ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
+    else
+      d.vo = seg1 ? vb1 : vb2 + (uint32_t)tt * kstb2;
+    d.is = seg1 ? isb1 : isb2;
+    return d;
+  };
+  auto ld = [&](const LoadDesc& d, int i) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(d.r, (int)(d.vo + i * d.is), 0, 0));
+  };
+  auto load_a = [&](int u, auto bsel) {
+    constexpr int b = decltype(bsel)::value;
+    const LoadDesc d = desc_a(u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sa[b][i] = ld(d, i);
+  };
+  auto load_b = [&](int u, auto bsel) {
+    constexpr int b = decltype(bsel)::value;
+    const LoadDesc d = desc_b(u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sb[b][i] = ld(d, i);
+  };
+
+  // ---- registers -> LDS buffer st ----
+  // rows (lt >> 3) + 32 i all have (row >> 1) & 7 = (lt >> 4) & 7
+  const uint32_t wr_off = (uint32_t)(lt >> 3) * 128 + (uint32_t)(((lt & 7) ^ ((lt >> 4) & 7)) << 4);
+  // transposed B: row nb*8 + j has (row >> 1) & 7 = 4 (nb & 1) + (j >> 1)
+  const uint32_t nn_wbase = (uint32_t)B_BASE + (uint32_t)(lt >> 3) * 8 * 128 +
+                            (uint32_t)(((lt & 7) ^ (((lt >> 3) & 1) << 2)) << 4);
+  // one 16-byte LDS write of chunk i of the staged A / B tile into buffer st
+  auto st_a = [&](int st, auto bsel, int i) {
+    constexpr int b = decltype(bsel)::value;
+    *reinterpret_cast<u32x4*>(smem + wr_off + st * A_STAGE + i * 32 * 128) = sa[b][i];
+  };
+  auto st_b = [&](int st, auto bsel, int i) {
+    constexpr int b = decltype(bsel)::value;
+    if constexpr (!B_NN) {
+      *reinterpret_cast<u32x4*>(smem + B_BASE + wr_off + st * B_STAGE + i * 32 * 128) = sb[b][i];
+    } else {
+      // 8x8 transpose of 16-bit values: column i of the block (n = 8 nb + i)
+      // becomes chunk kbk of LDS row n, stored at byte
+      // nn_wbase ^ ((i >> 1) << 4) plus i * 128.  The empty asm keeps the
+      // addresses from being precomputed and held across the loop.
+      uint32_t wb = nn_wbase;
+      asm volatile("" : "+v"(wb));
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t x0 = sb[b][2 * q][i >> 1], x1 = sb[b][2 * q + 1][i >> 1];
+        o[q] = (i & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
+      }
+      *reinterpret_cast<u32x4*>(smem + ((wb ^ (uint32_t)((i >> 1) << 4)) + st * B_STAGE + i * 128)) = o;
+    }
+  };
+  auto store_a = [&](int st, auto bsel) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st_a(st, bsel, i);
+  };
+  auto store_b = [&](int st, auto bsel) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) st_b(st, bsel, i);
+  };
+
+  // ---- fragments ----
+  // A rows wm*TM + 32 i + l32 and B rows wn*TN + 32 j + l32 all have
+  // (row >> 1) & 7 = (l32 >> 1) & 7.
+  const uint32_t ra = (uint32_t)(wm * TM + l32) * 128;
+  const uint32_t rb = (uint32_t)B_BASE + (uint32_t)(wn * TN + l32) * 128;
+  const int swz = (l32 >> 1) & 7;
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto rd = [&](int st, int s, auto fsel) {
+    constexpr int f = decltype(fsel)::value;
+    const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[f][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + i * 32 * 128));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[f][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + j * 32 * 128));
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  // MFMA number q (0..15) of a contraction step: block (q / 4, q % 4)
+  auto mf = [&](auto fsel, int q) {
+    constexpr int f = decltype(fsel)::value;
+    acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][q >> 2], fb[f][q & 3], acc[q >> 2][q & 3], 0, 0, 0);
+  };
+  // issue-order fence: nothing is scheduled across it
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // one stage t (LDS buffer ST = t & 1); stage t+1 is staged in registers
+  // sa/sb[(t+1) % PF]; loads issued here are for stage t+1+PF (clamped to the
+  // last stage: a repeated load past the end is harmless)
+  // one fragment read (k < 8: A block k, else B block k - 8) of step s
+  auto rd1 = [&](int st, int s, auto fsel, int k) {
+    constexpr int f = decltype(fsel)::value;
+    const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
+    if (k < FM)
+      fa[f][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + k * 32 * 128));
+    else
+      fb[f][k - FM] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + (k - FM) * 32 * 128));
+  };
+
+  auto stage = [&](int t, auto stsel) {
+    constexpr int ST = decltype(stsel)::value;
+    constexpr int U = ST ^ 1;
+    using SB = std::integral_constant<int, (ST + 1) % PF>;
+    const int nxt = t + 1 + PF < nk ? t + 1 + PF : nk - 1;
+    // Issue order, fixed by fences: every MFMA is followed by one memory
+    // operation, so the LDS and the load path see an even stream:
+    //   step 0: 8 x (MFMA, fragment read for step 1), 8 x (MFMA, A-tile write)
+    //   step 1: 8 x (MFMA, read for step 2),          8 x (MFMA, B-tile write)
+    //   step 2: 8 x (MFMA, read for step 3),          8 x (MFMA, A-tile load)
+    //   barrier
+    //   step 3: 8 x (MFMA, read of stage t+1 step 0), 8 x (MFMA, B-tile load)
+    // (a step's first MFMA only waits for reads issued before the previous
+    // step's writes: LDS operations complete in order)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I0{}, q);
+      rd1(ST, 1, I1{}, q);
+      fence();
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I0{}, 8 + q);
+      st_a(U, SB{}, q);
+      fence();
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I1{}, q);
+      rd1(ST, 2, I0{}, q);
+      fence();
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I1{}, 8 + q);
+      st_b(U, SB{}, q);
+      fence();
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I0{}, q);
+      rd1(ST, 3, I1{}, q);
+      fence();
+    }
+    {
+      const LoadDesc d = desc_a(nxt);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        mf(I0{}, 8 + q);
+        sa[SB::value][q] = ld(d, q);
+        fence();
+      }
+    }
+    lds_barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      mf(I1{}, q);
+      rd1(U, 0, I0{}, q);
+      fence();
+    }
+    {
+      const LoadDesc d = desc_b(nxt);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        mf(I1{}, 8 + q);
+        sb[SB::value][q] = ld(d, q);
+        fence();
+      }
+    }
+  };
+
+  // ---------------- main loop ----------------
+  if (nk > 0) {
+    load_a(0, I0{});
+    load_b(0, I0{});
+    store_a(0, I0{});
+    store_b(0, I0{});
+    if (PF == 1) {
+      load_a(nk > 1 ? 1 : 0, I0{});
+      load_b(nk > 1 ? 1 : 0, I0{});
+    } else {
+      load_a(nk > 1 ? 1 : 0, std::integral_constant<int, 1 % PF>{});
+      load_b(nk > 1 ? 1 : 0, std::integral_constant<int, 1 % PF>{});
+      load_a(nk > 2 ? 2 : nk - 1, I0{});
+      load_b(nk > 2 ? 2 : nk - 1, I0{});
+    }
+    lds_barrier();
+    rd(0, 0, I0{});
+    int t = 0;
+    for (; t + 1 < nk; t += 2) {
+      stage(t, I0{});
+      stage(t + 1, I1{});
+    }
+    if (t < nk) stage(t, I0{});
+  }
+
+  // ---------------- epilogue ----------------
+  // acc[i][j][v] = C[row, col]: row = m0 + wm*TM + 32 i + 8 (v / 4) + 4 hh + v % 4,
+  //                            col = n0 + wn*TN + 32 j + l32
+  const int64_t rbase = m0 + wm * TM + 4 * hh;
+  const int64_t cbase = n0 + wn * TN + l32;
+  uint16_t* out = reinterpret_cast<uint16_t*>(p.c);
+  if constexpr (EPI == EPI_ROPE) {
+    // a wave's 128 columns are one head: column 32 j + l32 (j < 2) pairs with
+    // column 32 (j + 2) + l32 = +64, both in this lane; cos/sin row = positions[row]
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+        const int64_t prow = (int64_t)p.pos[row] * 64;
+#pragma unroll
+        for (int j = 0; j < FN / 2; ++j) {
+          const int f = 32 * j + l32;
+          const int64_t col = cbase + 32 * j;
+          const float cs = p.cosc[prow + f], sn = p.sinc[prow + f];
+          const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
+          out[row * p.ldc + col] = f2bf(z1 * cs - z2 * sn);
+          out[row * p.ldc + col + 64] = f2bf(z2 * cs + z1 * sn);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) out[row * p.ldc + cbase + 32 * j] = f2bf(acc[i][j][v] * p.alpha);
+      }
+  }
+}
+
+}  // namespace lora

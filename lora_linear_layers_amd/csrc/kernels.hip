@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "gemm.h"
+#include "gemm_w4.h"
 #include "launch.h"
 #include "panel.h"
 
@@ -21,6 +24,24 @@ hipError_t run(GemmArgs a, int splits, hipStream_t st) {
   dim3 grid((unsigned)nblocks, 1, (unsigned)splits);
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, WM, WN, B_NN, EPI, BL>), grid, dim3(64 * WM * WN), 0, st,
                      a);
+  return hipGetLastError();
+}
+
+// Whole-tile launches (every tile inside m and n, the first contraction
+// segment a whole number of 64-wide stages, no split, every lane offset of a
+// tile below the 1 GiB buffer-resource range) take gemm_w4_kernel.
+bool whole_tiles(const GemmArgs& a, int splits) {
+  const int64_t ld = std::max(std::max(a.lda1, a.lda2), std::max(a.ldb1, a.ldb2));
+  return splits == 1 && a.m_load == a.m_store && a.m_store % w4::BM == 0 && a.n_load == a.n_store &&
+         a.n_store % w4::BN == 0 && a.K1 % w4::BK == 0 && ld * 2 * (w4::BM + w4::BK) < (int64_t)w4::BIG;
+}
+
+template <bool B_NN, int EPI>
+hipError_t run_whole(GemmArgs a, hipStream_t st) {
+  a.tiles_m = (int)(a.m_store / w4::BM);
+  const int64_t nblocks = (int64_t)a.tiles_m * (a.n_store / w4::BN);
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_w4_kernel<B_NN, EPI, 2>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -63,11 +84,17 @@ TileShape gemm_tile(GemmKind k) {
 
 hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
   switch (k) {
-    case G_BF16_BIG_NT_STORE: return run<bf, 256, 256, 2, 4, false, EPI_STORE, BL_PLAIN>(a, splits, st);
-    case G_BF16_BIG_NT_ROPE: return run<bf, 256, 256, 2, 2, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NT_STORE:
+      if (whole_tiles(a, splits)) return run_whole<false, EPI_STORE>(a, st);
+      return run<bf, 256, 256, 2, 4, false, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NT_ROPE:
+      if (whole_tiles(a, splits)) return run_whole<false, EPI_ROPE>(a, st);
+      return run<bf, 256, 256, 2, 2, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_ROPE: return run<bf, 128, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
-    case G_BF16_BIG_NN_STORE: return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_PLAIN>(a, splits, st);
+    case G_BF16_BIG_NN_STORE:
+      if (whole_tiles(a, splits)) return run_whole<true, EPI_STORE>(a, st);
+      return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_NF4_BIG_NT_STORE: return run<bf, 256, 256, 2, 4, false, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_NF4>(a, splits, st);

@@ -82,6 +82,70 @@ def test_integer_inputs_exact(lib, dtype, M, d_in, d_out, r):
     assert np.array_equal(cpu64(dB), dBr)
 
 
+# Whole-tile shapes: M, d_out and d_in multiples of 256 with at least 256
+# tiles of 256 x 256 in the forward and in the input gradient, so both run on
+# the whole-tile ping-pong kernel; ragged ranks exercise its masked rank-r
+# segment.  Y and dX are compared on 256 sampled rows, dA and dB in full.
+WHOLE = [(4096, 4096, 4096, 1), (4096, 4096, 4096, 24), (4096, 4096, 4096, 100),
+         (4096, 4096, 4096, 256), (8192, 4096, 2048, 64)]
+
+
+def _sample_rows(M, n=256, seed=5):
+    rng = np.random.default_rng(seed)
+    return np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), n - 2, replace=False)]))
+
+
+@pytest.mark.parametrize("shape", WHOLE, ids=[f"{m}x{i}x{o}r{r}" for m, i, o, r in WHOLE])
+def test_whole_tile_parity(lib, shape):
+    M, d_in, d_out, r = shape
+    s = 16.0 / r
+    X, W, A, B, dY = lora_inputs(900 + r, M, d_in, d_out, r, "bf16")
+    Y = lib.lora_linear_fwd(X, W, A, B, s)
+    dX, dA, dB = lib.lora_linear_bwd(X, W, A, B, s, dY)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M)
+    tr = torch.from_numpy(rows).cuda()
+    Yr = O.lora_forward(X[tr], W, A, B, s)
+    dXr = O.lora_grad_x(W, A, B, s, dY[tr])
+    dAr, dBr = O.lora_grad_ab(X, A, B, s, dY)
+    errs = dict(Y=rel(Y[tr], Yr), dX=rel(dX[tr], dXr), dA=rel(dA, dAr), dB=rel(dB, dBr))
+    print(shape, errs)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
+def _sparse_int(g, shape, density, device="cuda"):
+    v = torch.randint(-1, 2, shape, generator=g)
+    keep = torch.rand(shape, generator=g) < density
+    return (v * keep).to(torch.bfloat16).to(device)
+
+
+def test_whole_tile_integer_exact(lib):
+    # Sparse {-1, 0, 1} inputs keep every sum, panel and output a small
+    # integer (checked below), so the whole-tile kernel must match exactly.
+    M, d_in, d_out, r, s = 4096, 4096, 4096, 16, 1.0
+    g = torch.Generator().manual_seed(77)
+    X = _sparse_int(g, (M, d_in), 1 / 16)
+    W = _sparse_int(g, (d_out, d_in), 1.0)
+    A = _sparse_int(g, (r, d_in), 1.0)
+    B = _sparse_int(g, (d_out, r), 1 / 4)
+    dY = _sparse_int(g, (M, d_out), 1 / 16)
+    Y = lib.lora_linear_fwd(X, W, A, B, s)
+    dX, dA, dB = lib.lora_linear_bwd(X, W, A, B, s, dY)
+    torch.cuda.synchronize()
+    rows = _sample_rows(M, 512, 6)
+    tr = torch.from_numpy(rows).cuda()
+    Yr = O.lora_forward(X[tr], W, A, B, s)
+    dXr = O.lora_grad_x(W, A, B, s, dY[tr])
+    dAr, dBr = O.lora_grad_ab(X, A, B, s, dY)
+    P, Q = O.lora_panel(X, A), cpu64(dY) @ cpu64(B)
+    assert np.abs(P).max() <= 256 and np.abs(Q).max() <= 256
+    assert np.abs(Yr).max() <= 256 and np.abs(dXr).max() <= 256
+    assert np.array_equal(cpu64(Y[tr]), Yr)
+    assert np.array_equal(cpu64(dX[tr]), dXr)
+    assert np.array_equal(cpu64(dA), dAr)
+    assert np.array_equal(cpu64(dB), dBr)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_w_zero_isolates_lora_term(lib, dtype):
     M, d_in, d_out, r = 777, 512, 640, 16
@@ -153,6 +217,7 @@ def test_rope_cache_values(lib):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,d_in,d_out,r,seq", [(300, 264, 256, 16, 100), (2100, 1024, 4096, 64, 2048),
+                                              (4096, 1024, 4096, 40, 2048),
                                                 (4096, 512, 1024, 8, 4096), (4100, 256, 4096, 16, 2048)])
 def test_rope_fwd_bwd_parity(lib, dtype, M, d_in, d_out, r, seq):
     X, W, A, B, dY = lora_inputs(17 + M, M, d_in, d_out, r, dtype)
