@@ -60,6 +60,11 @@ def parse():
 
 # rocprofv3 kernel names -> the library profiler's kind names
 KIND_OF = {
+    "gemm_w4_kernel<false, 0, 2>": "gemm_bf16_256x256_nt_store",
+    "gemm_w4_kernel<true, 0, 2>": "gemm_bf16_256x256_nn_store",
+    "gemm_w4_kernel<false, 3, 2>": "gemm_bf16_256x256_nt_rope",
+    "gemm_kernel<unsigned short, 256, 64, 4, 1, false, 4, 0>": "panel_bf16_256x64_split",
+    "panel_reduce_kernel": "panel_reduce",
     "gemm_kernel<unsigned short, 256, 256, 2, 4, false, 0, 0>": "gemm_bf16_256x256_nt_store",
     "gemm_kernel<unsigned short, 256, 256, 2, 4, true, 0, 0>": "gemm_bf16_256x256_nn_store",
     "gemm_kernel<unsigned short, 256, 256, 2, 2, false, 3, 0>": "gemm_bf16_256x256_nt_rope",
@@ -71,7 +76,6 @@ KIND_OF = {
     "gemm_kernel<unsigned short, 128, 128, 4, 1, false, 0, 1>": "gemm_nf4_128x128_nt_store",
     "gemm_kernel<unsigned short, 128, 128, 4, 1, true, 0, 1>": "gemm_nf4_128x128_nn_store",
     "gemm_kernel<unsigned short, 64, 256, 1, 4, true, 4, 0>": "split_bf16_nn_partial",
-    "panel_kernel<8>": "panel_bf16_stream",
     "reduce_splits_kernel": "reduce_splits",
     "transpose_pad_kernel": "transpose_pad",
     "rope_inverse_kernel": "rope_inverse",

@@ -54,10 +54,28 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t r8 = 0, M8 = 0;
-  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, total = 0;
+  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, total = 0;
   int splits_dA = 1, splits_dB = 1;
   int64_t ksplit_dA = 0, ksplit_dB = 0;
+  int splits_p = 1, splits_q = 1;  // bf16 rank-r panels: P = X A^T, Q = G B
+  int64_t ksplit_p = 0, ksplit_q = 0;
 };
+
+// Split of the contraction of a bf16 rank-r panel (256 x 64 tiles): about 1.5
+// workgroups per CU, each split a multiple of 64 and at least 8 stages long.
+void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit) {
+  int64_t tiles = cdiv(M, 256) * cdiv(r8, 64);
+  if (tiles < 1) tiles = 1;
+  int64_t s = cdiv(384, tiles);
+  int64_t smax = K / 512;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s > 32) s = 32;
+  if (s < 1) s = 1;
+  const int64_t ks = rup(cdiv(K, s), 64);
+  *ksplit = ks;
+  *splits = (int)cdiv(K, ks);
+}
 
 // Split of the token contraction for dA / dB: enough workgroups to cover the
 // chip (~2 per CU), each split a multiple of 64 tokens and at least 256 long.
@@ -88,6 +106,15 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
   };
   const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD;
   if (r % 8) L.bpad = take(size_t(d_out) * L.r8 * eb);
+  if (eb == 2) {
+    panel_split(M, d_in, L.r8, &L.splits_p, &L.ksplit_p);
+    int sp = L.splits_p;
+    if (bwd) {
+      panel_split(M, d_out, L.r8, &L.splits_q, &L.ksplit_q);
+      if (L.splits_q > sp) sp = L.splits_q;
+    }
+    L.ppart = take(size_t(sp) * L.M8 * L.r8 * 4);
+  }
   if (!bwd) {
     L.p = take(size_t(M) * L.r8 * eb);
   } else {
@@ -166,9 +193,9 @@ const char* kind_name(int k) {
       "panel_bf16_nn_both",         "split_bf16_nn_partial",      "gemm_f32_64x128_nt_store",
       "gemm_f32_64x128_nt_rope",    "gemm_f32_64x128_nn_store",   "panel_f32_nt_store",
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
-      "pad_cols",                   "rope_inverse",               "reduce_splits",
-      "fill_zero",                  "rope_cache",                 "nf4_dequant",
-      "panel_bf16_stream",          "transpose_pad"};
+      "panel_bf16_256x64_split",    "pad_cols",                   "rope_inverse",
+      "reduce_splits",              "fill_zero",                  "rope_cache",
+      "nf4_dequant",                "panel_reduce",               "transpose_pad"};
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
 
@@ -215,6 +242,25 @@ GemmArgs blank() {
   return a;
 }
 
+// bf16 rank-r panel v = alpha * X R^T over a contraction of K: split partials
+// (256 x 64 tiles) into part, then the fixed-order reduction into out
+// (row-major [rows, ldo]) and/or outt (transposed [r8, ldot]); rows in
+// [M, rows) and columns in [r, r8) are zeros.
+int panel_bf16(const void* X, int64_t ldx, const void* R, int64_t ldr, int64_t M, int64_t rows, int64_t K, int64_t r,
+               int64_t r8, int splits, int64_t ksplit, float alpha, float* part, uint16_t* out, int64_t ldo,
+               uint16_t* outt, int64_t ldot, hipStream_t st) {
+  GemmArgs a = blank();
+  a.a1 = X; a.lda1 = ldx; a.b1 = R; a.ldb1 = ldr; a.K1 = K;
+  a.m_load = M; a.m_store = rows; a.n_load = r; a.n_store = r8;
+  a.k_split = ksplit; a.c = part; a.ldc = r8; a.part_stride = rows * r8;
+  const double Md = double(M), kd = double(K), rd = double(r);
+  HIPTRY(gemm(G_BF16_PANEL_SPLIT_NT, a, splits, st, 2 * Md * rd * kd,
+              (Md * kd + rd * kd) * 2 + 4.0 * splits * rows * r8));
+  HIPTRY(timed(K_PANEL, double(splits) * rows * r8, 4.0 * splits * rows * r8 + 2.0 * rows * r8 * ((out ? 1 : 0) + (outt ? 1 : 0)),
+               st, [&] { return launch_panel_reduce(part, splits, rows * r8, r8, rows, r8, alpha, out, ldo, outt, ldot, st); }));
+  return LORA_OK;
+}
+
 // ---------------------------------------------------------------------------
 // forward (shared by the plain, RoPE and NF4 entry points)
 // ---------------------------------------------------------------------------
@@ -253,12 +299,8 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     a.c = P; a.ldc = L.r8; a.alpha = scale;
     HIPTRY(gemm(G_F32_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
   } else {
-    PanelArgs pa{};
-    pa.x = static_cast<const uint16_t*>(X); pa.ldx = d_in; pa.w = static_cast<const uint16_t*>(A); pa.ldw = d_in;
-    pa.M = M; pa.K = d_in; pa.n_valid = r; pa.m_store = M; pa.n_store = L.r8; pa.alpha = scale;
-    pa.out = static_cast<uint16_t*>(P); pa.ldo = L.r8;
-    HIPTRY(timed(K_PANEL, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e, st,
-                 [&] { return launch_panel(pa, st); }));
+    TRY(panel_bf16(X, d_in, A, d_in, M, M, d_in, r, L.r8, L.splits_p, L.ksplit_p, scale,
+                   reinterpret_cast<float*>(w + L.ppart), static_cast<uint16_t*>(P), L.r8, nullptr, 0, st));
   }
   // main: Y = [X | P] [W | B]^T, optional RoPE epilogue
   GemmArgs a = blank();
@@ -334,23 +376,16 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     }
   } else {
     // Pt = (s X A^T)^T  [r8, M8], recomputed from X (rows M..M8 and columns r..r8 are zeros)
-    PanelArgs pa{};
-    pa.x = static_cast<const uint16_t*>(X); pa.ldx = d_in; pa.w = static_cast<const uint16_t*>(A); pa.ldw = d_in;
-    pa.M = M; pa.K = d_in; pa.n_valid = r; pa.m_store = L.M8; pa.n_store = L.r8; pa.alpha = scale;
-    pa.outt = static_cast<uint16_t*>(Pt); pa.ldot = L.M8;
-    HIPTRY(timed(K_PANEL, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e, st,
-                 [&] { return launch_panel(pa, st); }));
+    float* pp = reinterpret_cast<float*>(w + L.ppart);
+    TRY(panel_bf16(X, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, scale, pp, nullptr, 0,
+                   static_cast<uint16_t*>(Pt), L.M8, st));
     // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
     uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
     HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
       return launch_transpose_pad(static_cast<const uint16_t*>(B), Bt, d_out, r, L.r8, st);
     }));
-    PanelArgs pq{};
-    pq.x = static_cast<const uint16_t*>(G); pq.ldx = d_out; pq.w = Bt; pq.ldw = d_out;
-    pq.M = M; pq.K = d_out; pq.n_valid = r; pq.m_store = L.M8; pq.n_store = L.r8; pq.alpha = scale;
-    pq.out = static_cast<uint16_t*>(Qs); pq.ldo = L.r8; pq.outt = static_cast<uint16_t*>(Qt); pq.ldot = L.M8;
-    HIPTRY(timed(K_PANEL, 2 * Md * rr * ko, (Md * ko + rr * ko + 2 * Md * L.r8) * e, st,
-                 [&] { return launch_panel(pq, st); }));
+    TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, scale, pp,
+                   static_cast<uint16_t*>(Qs), L.r8, static_cast<uint16_t*>(Qt), L.M8, st));
   }
   // dX = [G | Qs] [W ; A]
   if (dX) {

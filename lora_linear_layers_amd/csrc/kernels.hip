@@ -73,6 +73,8 @@ TileShape gemm_tile(GemmKind k) {
     case G_BF16_SPLIT_NN_PARTIAL:
     case G_F32_SPLIT_NN_PARTIAL:
       return {64, 256};
+    case G_BF16_PANEL_SPLIT_NT:
+      return {256, 64};
     case G_F32_NT_STORE:
     case G_F32_NT_ROPE:
     case G_F32_NN_STORE:
@@ -111,6 +113,7 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_F32_PANEL_NT_STORE_T: return run<float, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
     case G_F32_PANEL_NN_BOTH: return run<float, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
     case G_F32_SPLIT_NN_PARTIAL: return run<float, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_BF16_PANEL_SPLIT_NT: return run<bf, 256, 64, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -249,12 +252,15 @@ hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float*
   return hipGetLastError();
 }
 
+constexpr int kMaxSplits = 64;
+
 __global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t rows, int64_t N,
                                      int64_t part_stride, int transpose, float* __restrict__ out) {
   const int64_t n = rows * N;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t q = e / N, c = e - q * N;
     float s = 0.f;
+#pragma unroll 8
     for (int z = 0; z < splits; ++z) s += part[(int64_t)z * part_stride + e];
     if (transpose)
       out[c * rows + q] = s;
@@ -267,8 +273,58 @@ hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int
                                 bool transpose, float* out, hipStream_t st) {
   const int64_t n = rows * N;
   if (n <= 0) return hipSuccess;
+  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
   hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, part, splits, rows, N,
                      part_stride, transpose ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+constexpr int kMaxPanelSplits = 32;
+
+// One 16-row x 64-column tile of the panel per workgroup: fixed-order sum of
+// the split partials (consecutive threads read consecutive columns), scale,
+// then the row-major and/or (through LDS) the transposed bf16 stores.
+__global__ void __launch_bounds__(256) panel_reduce_kernel(const float* __restrict__ part, int splits,
+                                                           int64_t part_stride, int64_t ldp, int64_t rows, int64_t n,
+                                                           float alpha, uint16_t* __restrict__ out, int64_t ldo,
+                                                           uint16_t* __restrict__ outt, int64_t ldot) {
+  __shared__ float tile[16][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
+  const int cc = threadIdx.x & 63;
+  for (int rr = threadIdx.x >> 6; rr < 16; rr += 4) {
+    const int64_t q = r0 + rr, c = c0 + cc;
+    float v = 0.f;
+    if (q < rows && c < n) {
+      // all split loads in flight at once, then the sum in split order
+      const float* src = part + q * ldp + c;
+      float pv[kMaxPanelSplits];
+#pragma unroll
+      for (int z = 0; z < kMaxPanelSplits; ++z) pv[z] = z < splits ? src[(int64_t)z * part_stride] : 0.f;
+      float s = 0.f;
+#pragma unroll
+      for (int z = 0; z < kMaxPanelSplits; ++z) s += pv[z];
+      v = s * alpha;
+      if (out) out[q * ldo + c] = f2bf(v);
+    }
+    tile[rr][cc] = v;
+  }
+  if (!outt) return;
+  __syncthreads();
+  for (int e = threadIdx.x; e < 16 * 64; e += 256) {
+    const int ct = e >> 4, rt = e & 15;  // consecutive threads: consecutive rows of the transpose
+    const int64_t q = r0 + rt, c = c0 + ct;
+    if (q < rows && c < n) outt[c * ldot + q] = f2bf(tile[rt][ct]);
+  }
+}
+
+hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_stride, int64_t ldp, int64_t rows,
+                               int64_t n, float alpha, uint16_t* out, int64_t ldo, uint16_t* outt, int64_t ldot,
+                               hipStream_t st) {
+  if (rows <= 0 || n <= 0) return hipSuccess;
+  if (splits < 1 || splits > kMaxPanelSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((n + 63) / 64));
+  hipLaunchKernelGGL(panel_reduce_kernel, grid, dim3(256), 0, st, part, splits, part_stride, ldp, rows, n, alpha, out,
+                     ldo, outt, ldot);
   return hipGetLastError();
 }
 

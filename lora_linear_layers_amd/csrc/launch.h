@@ -11,8 +11,9 @@
 namespace lora {
 
 // GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
-// epilogue.  "BIG" = 256x256 tiles (8 waves), "MED" = 128x128 (4 waves),
-// "PANEL" = 64x64 rank-r panels, "SPLIT" = 64x256 split-contraction partials.
+// epilogue.  "BIG" = 256x256 tiles, "MED" = 128x128 (4 waves), "PANEL" =
+// 64x64 rank-r panels, "SPLIT" = 64x256 split-contraction partials,
+// "PANEL_SPLIT" = 256x64 split-contraction partials of a rank-r panel.
 enum GemmKind : int {
   G_BF16_BIG_NT_STORE,
   G_BF16_BIG_NT_ROPE,
@@ -35,6 +36,7 @@ enum GemmKind : int {
   G_F32_PANEL_NT_STORE_T,
   G_F32_PANEL_NN_BOTH,
   G_F32_SPLIT_NN_PARTIAL,
+  G_BF16_PANEL_SPLIT_NT,
   G_KIND_COUNT
 };
 
@@ -69,6 +71,13 @@ hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float*
 // fp32.  transpose = false: out[q * N + n]; true: out[n * rows + q]; q < rows.
 hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N,
                                 int64_t part_stride, bool transpose, float* out, hipStream_t st);
+
+// Rank-r panel from split partials: v = alpha * sum over z < splits of
+// part[z][q, c] (fixed order) for q < rows, c < n; written as bf16 to
+// out[q * ldo + c] and/or outt[c * ldot + q] (either may be null).
+hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_stride, int64_t ldp, int64_t rows,
+                               int64_t n, float alpha, uint16_t* out, int64_t ldo, uint16_t* outt, int64_t ldot,
+                               hipStream_t st);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 
