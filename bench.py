@@ -30,7 +30,8 @@ METRIC = "fused LoRA linear fwd+bwd TFLOP/s & tokens/s, % bf16 MFMA peak, 1 GPU"
 PEAK = {"bf16": 2516.6, "f32": 157.3}  # TFLOP/s, dense MFMA (MI355X: 256 CU x 2.4 GHz)
 HBM_PEAK = 8000.0  # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["lora_linear_layers_amd/csrc/gemm.h", "lora_linear_layers_amd/csrc/kernels.hip",
+KERNEL_SOURCES = ["lora_linear_layers_amd/csrc/gemm.h", "lora_linear_layers_amd/csrc/gemm_w4.h",
+                  "lora_linear_layers_amd/csrc/panel.h", "lora_linear_layers_amd/csrc/kernels.hip",
                   "lora_linear_layers_amd/csrc/api.cpp"]
 
 
