@@ -179,6 +179,63 @@ int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_
                 const float* table16, uint16_t* out_bf16, void* stream);
 
 /*
+ * Groups of projections that read the same input X: q/k/v of attention,
+ * gate/up of the MLP.  Page "UnSloth加速微调体验…", section RoPE缓存集成 fuses
+ * q_proj with its LoRA branch; page "Unsloth框架：高效LLM微调与LoRA优化实践",
+ * section 3.1 (graph rewriting), merges adjacent linear layers; page
+ * "Unsloth自动化优化：无需手动调参的实现原理", section 3.3, walks the layer as
+ * the segments q, k, v, o, gate, up, down.  A group call runs the
+ * rank-r panels of all its members in ONE pass over X, with A_1 .. A_n stacked:
+ * the forward panel s X A^T, the backward's recomputation of X A^T and the dA
+ * contraction over X.  Everything else runs per member exactly as in the
+ * single-projection entry points, so every member's outputs equal that
+ * member's single call up to rounding order.
+ *
+ * `members` is a HOST array of n (1 <= n <= LORA_GROUP_MAX) descriptions whose
+ * pointers are device pointers.  Per member: d_out, r and the pointer rules
+ * are those of one projection; `scale` is its s; `rope` = 1 gives it the RoPE
+ * epilogue of lora_qk_rope_fwd with the group's head_dim / positions / caches
+ * (then head_dim must be 128 and d_out a multiple of it); `W_nf4` (with
+ * `absmax`, blocksize 64, d_in a multiple of 64, bf16 only, no RoPE) replaces W
+ * by an NF4 base weight decoded with the HOST table `table16` as in
+ * nf4_lora_linear_fwd.  Forward writes every member's Y.  Backward writes
+ * every member's dA, dB and, where dX is not NULL, the member's own input
+ * gradient (not summed over the group).  The rope and table arguments may be
+ * NULL when no member needs them.
+ */
+#define LORA_GROUP_MAX 8
+typedef struct lora_group_member {
+  int64_t d_out, r;
+  float scale;
+  int rope;
+  const void* W;          /* [d_out, d_in], or NULL when W_nf4 is given */
+  const uint8_t* W_nf4;   /* NF4 codes [d_out * d_in / 2], or NULL */
+  const float* absmax;    /* [d_out * d_in / 64] with W_nf4 */
+  const void* A;          /* [r, d_in] */
+  const void* B;          /* [d_out, r] */
+  void* Y;                /* forward output [M, d_out] */
+  const void* dY;         /* backward input [M, d_out] */
+  void* dX;               /* backward output [M, d_in], or NULL */
+  float* dA;              /* backward output [r, d_in] fp32 */
+  float* dB;              /* backward output [d_out, r] fp32 */
+} lora_group_member;
+
+/* Workspace bytes of lora_group_fwd (backward = 0) or lora_group_bwd (1); 0 for
+ * invalid arguments. */
+size_t lora_group_workspace_bytes(int backward, int dtype, int64_t M, int64_t d_in, int n,
+                                  const lora_group_member* members);
+
+int lora_group_fwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* members,
+                   const void* X, int head_dim, const int32_t* positions, const float* cos_cache,
+                   const float* sin_cache, int64_t max_pos, const float* table16, void* ws,
+                   size_t ws_bytes, void* stream);
+
+int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* members,
+                   const void* X, int head_dim, const int32_t* positions, const float* cos_cache,
+                   const float* sin_cache, int64_t max_pos, const float* table16, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
  * Launch profiling (measurement hook, not part of the layer's arithmetic).
  * Between lora_profile_begin and lora_profile_end every kernel the library
  * launches is bracketed by two HIP events on its stream, and the launch's

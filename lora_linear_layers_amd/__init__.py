@@ -9,6 +9,8 @@ forms dW.
 """
 from ._lib import (  # noqa: F401
     EXPORTS,
+    GROUP_MAX,
+    GroupMember,
     LIB_PATH,
     LORA_BF16,
     LORA_F32,
@@ -25,6 +27,8 @@ from ._lib import (  # noqa: F401
 )
 from .functional import (  # noqa: F401
     LoraLinearFunction,
+    lora_group_bwd,
+    lora_group_fwd,
     lora_linear_bwd,
     lora_linear_fwd,
     lora_qk_rope_bwd,

@@ -23,6 +23,18 @@ _i64, _f32, _vp, _sz, _int, _dbl = (ctypes.c_int64, ctypes.c_float, ctypes.c_voi
                                     ctypes.c_int, ctypes.c_double)
 _fp = ctypes.POINTER(ctypes.c_float)
 
+GROUP_MAX = 8
+
+
+class GroupMember(ctypes.Structure):
+    """struct lora_group_member of the C ABI."""
+    _fields_ = [("d_out", _i64), ("r", _i64), ("scale", _f32), ("rope", _int), ("W", _vp), ("W_nf4", _vp),
+                ("absmax", _vp), ("A", _vp), ("B", _vp), ("Y", _vp), ("dY", _vp), ("dX", _vp), ("dA", _vp),
+                ("dB", _vp)]
+
+
+_mp = ctypes.POINTER(GroupMember)
+
 _SIGS = {
     "lora_abi_version": ([], _int),
     "lora_strerror": ([_int], ctypes.c_char_p),
@@ -40,6 +52,9 @@ _SIGS = {
     "nf4_lora_linear_bwd": ([_i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _int, _fp, _vp, _vp, _vp, _vp, _vp, _vp,
                              _vp, _sz, _vp], _int),
     "nf4_dequant": ([_vp, _vp, _int, _i64, _fp, _vp, _vp], _int),
+    "lora_group_workspace_bytes": ([_int, _int, _i64, _i64, _int, _mp], _sz),
+    "lora_group_fwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
+    "lora_group_bwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
     "lora_profile_begin": ([_int], _int),
     "lora_profile_end": ([], _int),
     "lora_profile_kinds": ([], _int),

@@ -77,11 +77,12 @@ void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit)
   *splits = (int)cdiv(K, ks);
 }
 
-// Split of the token contraction for dA / dB: enough workgroups to cover the
-// chip (~2 per CU), each split a multiple of 64 tokens and at least 256 long.
-void choose_split(int64_t M, int64_t N, int* splits, int64_t* ksplit) {
-  const int64_t tiles_n = cdiv(N, 256);
-  int64_t s = cdiv(512, tiles_n);
+// Split of the token contraction for dA / dB ([rows, N] outputs in 64 x 256
+// tiles): enough workgroups to cover the chip (~2 per CU), each split a
+// multiple of 64 tokens and at least 256 long.
+void choose_split(int64_t M, int64_t rows, int64_t N, int* splits, int64_t* ksplit) {
+  const int64_t tiles = cdiv(rows, 64) * cdiv(N, 256);
+  int64_t s = cdiv(512, tiles);
   const int64_t smax = cdiv(M, 256);
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -123,8 +124,8 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.pt = take(size_t(L.r8) * L.M8 * eb);
     L.qs = take(size_t(L.M8) * L.r8 * eb);
     L.qt = take(size_t(L.r8) * L.M8 * eb);
-    choose_split(M, d_in, &L.splits_dA, &L.ksplit_dA);
-    choose_split(M, d_out, &L.splits_dB, &L.ksplit_dB);
+    choose_split(M, L.r8, d_in, &L.splits_dA, &L.ksplit_dA);
+    choose_split(M, L.r8, d_out, &L.splits_dB, &L.ksplit_dB);
     size_t pa = size_t(L.splits_dA) * L.r8 * d_in * 4;
     size_t pb = size_t(L.splits_dB) * L.r8 * d_out * 4;
     L.part = take(pa > pb ? pa : pb);
@@ -181,6 +182,7 @@ enum ProfKind : int {
   K_NF4_DEQ,
   K_PANEL,
   K_TRANSPOSE,
+  K_COPY_ROWS,
   K_PROF_COUNT
 };
 
@@ -195,7 +197,8 @@ const char* kind_name(int k) {
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
       "panel_bf16_256x64_split",    "pad_cols",                   "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
-      "nf4_dequant",                "panel_reduce",               "transpose_pad"};
+      "nf4_dequant",                "panel_reduce",               "transpose_pad",
+      "copy_rows"};
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
 
@@ -247,7 +250,7 @@ GemmArgs blank() {
 // (row-major [rows, ldo]) and/or outt (transposed [r8, ldot]); rows in
 // [M, rows) and columns in [r, r8) are zeros.
 int panel_bf16(const void* X, int64_t ldx, const void* R, int64_t ldr, int64_t M, int64_t rows, int64_t K, int64_t r,
-               int64_t r8, int splits, int64_t ksplit, float alpha, float* part, uint16_t* out, int64_t ldo,
+               int64_t r8, int splits, int64_t ksplit, const ColScale& cs, float* part, uint16_t* out, int64_t ldo,
                uint16_t* outt, int64_t ldot, hipStream_t st) {
   GemmArgs a = blank();
   a.a1 = X; a.lda1 = ldx; a.b1 = R; a.ldb1 = ldr; a.K1 = K;
@@ -257,7 +260,7 @@ int panel_bf16(const void* X, int64_t ldx, const void* R, int64_t ldr, int64_t M
   HIPTRY(gemm(G_BF16_PANEL_SPLIT_NT, a, splits, st, 2 * Md * rd * kd,
               (Md * kd + rd * kd) * 2 + 4.0 * splits * rows * r8));
   HIPTRY(timed(K_PANEL, double(splits) * rows * r8, 4.0 * splits * rows * r8 + 2.0 * rows * r8 * ((out ? 1 : 0) + (outt ? 1 : 0)),
-               st, [&] { return launch_panel_reduce(part, splits, rows * r8, r8, rows, r8, alpha, out, ldo, outt, ldot, st); }));
+               st, [&] { return launch_panel_reduce(part, splits, rows * r8, r8, rows, r8, cs, out, ldo, outt, ldot, st); }));
   return LORA_OK;
 }
 
@@ -276,9 +279,11 @@ struct Rope {
   const float* sinc;
 };
 
+// Pext: when not NULL, the panel s X A^T is already in Pext (row stride
+// ldpext, columns r..r8 zero) and is not computed here (group calls).
 int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
                  const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, void* Y, void* ws,
-                 const Layout& L, hipStream_t st) {
+                 const Layout& L, hipStream_t st, const void* Pext = nullptr, int64_t ldpext = 0) {
   if (M == 0) return LORA_OK;
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
@@ -289,23 +294,26 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
                  [&] { return launch_pad_cols(eb, B, w + L.bpad, d_out, r, L.r8, st); }));
     Bsrc = w + L.bpad;
   }
-  void* P = w + L.p;
+  const void* P = Pext ? Pext : static_cast<const void*>(w + L.p);
+  const int64_t ldp = Pext ? ldpext : L.r8;
   const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r), e = double(eb);
   // panel: P = s * X A^T  [M, r8] (columns r..r8 are exact zeros)
-  if (f32) {
+  if (Pext) {
+    // computed by the caller
+  } else if (f32) {
     GemmArgs a = blank();
     a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
     a.m_load = M; a.m_store = M; a.n_load = r; a.n_store = L.r8;
-    a.c = P; a.ldc = L.r8; a.alpha = scale;
+    a.c = w + L.p; a.ldc = L.r8; a.alpha = scale;
     HIPTRY(gemm(G_F32_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
   } else {
-    TRY(panel_bf16(X, d_in, A, d_in, M, M, d_in, r, L.r8, L.splits_p, L.ksplit_p, scale,
-                   reinterpret_cast<float*>(w + L.ppart), static_cast<uint16_t*>(P), L.r8, nullptr, 0, st));
+    TRY(panel_bf16(X, d_in, A, d_in, M, M, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale),
+                   reinterpret_cast<float*>(w + L.ppart), reinterpret_cast<uint16_t*>(w + L.p), L.r8, nullptr, 0, st));
   }
   // main: Y = [X | P] [W | B]^T, optional RoPE epilogue
   GemmArgs a = blank();
   a.a1 = X; a.lda1 = d_in; a.b1 = W; a.ldb1 = d_in; a.K1 = d_in;
-  a.a2 = P; a.lda2 = L.r8; a.b2 = Bsrc; a.ldb2 = L.r8; a.K2 = r;
+  a.a2 = P; a.lda2 = ldp; a.b2 = Bsrc; a.ldb2 = L.r8; a.K2 = r;
   a.m_load = M; a.m_store = M; a.n_load = d_out; a.n_store = d_out;
   a.c = Y; a.ldc = d_out;
   GemmKind k;
@@ -328,9 +336,20 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
 // ---------------------------------------------------------------------------
 // backward
 // ---------------------------------------------------------------------------
+// Rank-r panels of one member of a bf16 group: Pt (= (s X A^T)^T, rows of
+// stride M8) is already computed; Q = s G B is written into the group's
+// arrays (Qs row stride ldqs, Qt row stride M8); dA is left to the group.
+struct PanelSlices {
+  const void* Pt;
+  void* Qs;
+  int64_t ldqs;
+  void* Qt;
+};
+
 int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
                   const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, const void* dY,
-                  void* dX, float* dA, float* dB, void* ws, const Layout& L, hipStream_t st) {
+                  void* dX, float* dA, float* dB, void* ws, const Layout& L, hipStream_t st,
+                  const PanelSlices* ov = nullptr) {
   if (M == 0) {
     HIPTRY(timed(K_FILL, 0, 4.0 * r * d_in, st, [&] { return launch_fill_zero(dA, r * d_in, st); }));
     HIPTRY(timed(K_FILL, 0, 4.0 * r * d_out, st, [&] { return launch_fill_zero(dB, d_out * r, st); }));
@@ -353,9 +372,10 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     }));
     G = w + L.g;
   }
-  void* Pt = w + L.pt;
-  void* Qs = w + L.qs;
-  void* Qt = w + L.qt;
+  const void* Pt = ov ? ov->Pt : w + L.pt;
+  void* Qs = ov ? ov->Qs : w + L.qs;
+  const int64_t ldqs = ov ? ov->ldqs : L.r8;
+  void* Qt = ov ? ov->Qt : w + L.qt;
   float* part = reinterpret_cast<float*>(w + L.part);
   if (f32) {
     // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
@@ -363,7 +383,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
       GemmArgs a = blank();
       a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
       a.m_load = M; a.m_store = L.M8; a.n_load = r; a.n_store = L.r8;
-      a.ct = Pt; a.ldct = L.M8; a.alpha = scale;
+      a.ct = w + L.pt; a.ldct = L.M8; a.alpha = scale;
       HIPTRY(gemm(G_F32_PANEL_NT_STORE_T, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
     }
     // Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
@@ -377,21 +397,22 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   } else {
     // Pt = (s X A^T)^T  [r8, M8], recomputed from X (rows M..M8 and columns r..r8 are zeros)
     float* pp = reinterpret_cast<float*>(w + L.ppart);
-    TRY(panel_bf16(X, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, scale, pp, nullptr, 0,
-                   static_cast<uint16_t*>(Pt), L.M8, st));
+    if (!ov)
+      TRY(panel_bf16(X, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale), pp,
+                     nullptr, 0, reinterpret_cast<uint16_t*>(w + L.pt), L.M8, st));
     // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
     uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
     HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
       return launch_transpose_pad(static_cast<const uint16_t*>(B), Bt, d_out, r, L.r8, st);
     }));
-    TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, scale, pp,
-                   static_cast<uint16_t*>(Qs), L.r8, static_cast<uint16_t*>(Qt), L.M8, st));
+    TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, col_scale(scale), pp,
+                   static_cast<uint16_t*>(Qs), ldqs, static_cast<uint16_t*>(Qt), L.M8, st));
   }
   // dX = [G | Qs] [W ; A]
   if (dX) {
     GemmArgs a = blank();
     a.a1 = G; a.lda1 = d_out; a.b1 = W; a.ldb1 = d_in; a.K1 = d_out;
-    a.a2 = Qs; a.lda2 = L.r8; a.b2 = A; a.ldb2 = d_in; a.K2 = r;
+    a.a2 = Qs; a.lda2 = ldqs; a.b2 = A; a.ldb2 = d_in; a.K2 = r;
     a.m_load = M; a.m_store = M; a.n_load = d_in; a.n_store = d_in;
     a.c = dX; a.ldc = d_in;
     GemmKind k;
@@ -420,7 +441,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     }));
   }
   // dA = Qt X -> partials [splits][r8, d_in] -> dA [r, d_in]
-  {
+  if (!ov) {
     GemmArgs a = blank();
     a.a1 = Qt; a.lda1 = L.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
     a.m_load = L.r8; a.m_store = L.r8; a.n_load = d_in; a.n_store = d_in;
@@ -446,6 +467,183 @@ int check_nf4(int64_t d_in, int blocksize, const uint8_t* codes, const float* ab
   if (blocksize != 64 || d_in % 64) return LORA_ERR_SHAPE;
   if (!table) return LORA_ERR_NULL;
   return check_ptrs({codes, absmax});
+}
+
+// ---------------------------------------------------------------------------
+// groups of projections sharing X
+// ---------------------------------------------------------------------------
+// bf16 workspace: Acat = [A_1; ..; A_n] with each A_g padded to r8_g rows
+// (rt = sum r8_g rows, member g at row off[g]); forward: the group panel
+// P = [s_1 X A_1^T | ..] [M, rt]; backward: Pt [rt, M8], Qs [M8, rt] and
+// Qt [rt, M8].  One shared region follows, used in turn by the group panel's
+// split partials, each member's own scratch, and the dA partials.
+struct GroupLayout {
+  int64_t rt = 0, M8 = 0, off[LORA_GROUP_MAX] = {};
+  size_t acat = 0, p = 0, pt = 0, qs = 0, qt = 0, shared = 0, total = 0;
+  int splits_g = 1, splits_dA = 1;
+  int64_t ksplit_g = 0, ksplit_dA = 0;
+  Layout mem[LORA_GROUP_MAX];
+};
+
+int member_op(bool bwd, const lora_group_member& m) {
+  if (m.W_nf4) return bwd ? LORA_OP_NF4_BWD : LORA_OP_NF4_FWD;
+  if (m.rope) return bwd ? LORA_OP_ROPE_BWD : LORA_OP_ROPE_FWD;
+  return bwd ? LORA_OP_BWD : LORA_OP_FWD;
+}
+
+GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* mb) {
+  GroupLayout G;
+  const size_t eb = elem_bytes(dtype);
+  G.M8 = rup(M, 8);
+  size_t shared = 0;
+  for (int g = 0; g < n; ++g) {
+    G.off[g] = G.rt;
+    G.rt += rup(mb[g].r, 8);
+    G.mem[g] = make_layout(member_op(bwd, mb[g]), dtype, M, d_in, mb[g].d_out, mb[g].r);
+    if (G.mem[g].total > shared) shared = G.mem[g].total;
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (eb == 2) {
+    G.acat = take(size_t(G.rt) * d_in * eb);
+    panel_split(M, d_in, G.rt, &G.splits_g, &G.ksplit_g);
+    const size_t pp = size_t(G.splits_g) * G.M8 * G.rt * 4;
+    if (pp > shared) shared = pp;
+    if (!bwd) {
+      G.p = take(size_t(M) * G.rt * eb);
+    } else {
+      G.pt = take(size_t(G.rt) * G.M8 * eb);
+      G.qs = take(size_t(G.M8) * G.rt * eb);
+      G.qt = take(size_t(G.rt) * G.M8 * eb);
+      choose_split(M, G.rt, d_in, &G.splits_dA, &G.ksplit_dA);
+      const size_t pa = size_t(G.splits_dA) * G.rt * d_in * 4;
+      if (pa > shared) shared = pa;
+    }
+  }
+  G.shared = take(shared);
+  G.total = off;
+  return G;
+}
+
+// Validation of a whole group before any launch.
+int check_group(bool bwd, int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X,
+                int head_dim, const int32_t* pos, const float* cosc, const float* sinc, int64_t max_pos,
+                const float* table16) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (!mb) return LORA_ERR_NULL;
+  if (n < 1 || n > LORA_GROUP_MAX) return LORA_ERR_SHAPE;
+  if (M > 0) TRY(check_ptrs({X}));
+  for (int g = 0; g < n; ++g) {
+    const lora_group_member& m = mb[g];
+    TRY(check_sizes(M, d_in, m.d_out, m.r));
+    TRY(check_ptrs({m.A, m.B}));
+    if (m.W_nf4) {
+      if (dtype != LORA_BF16) return LORA_ERR_DTYPE;
+      if (m.rope) return LORA_ERR_SHAPE;
+      TRY(check_nf4(d_in, 64, m.W_nf4, m.absmax, table16));
+    } else {
+      TRY(check_ptrs({m.W}));
+    }
+    if (m.rope) TRY(check_rope(head_dim, m.d_out, M, pos, cosc, sinc, max_pos));
+    if (!bwd) {
+      if (M > 0) TRY(check_ptrs({m.Y}));
+    } else {
+      TRY(check_ptrs({m.dA, m.dB}));
+      if (M > 0) TRY(check_ptrs({m.dY}));
+      if (m.dX && !aligned16(m.dX)) return LORA_ERR_ALIGN;
+    }
+  }
+  return LORA_OK;
+}
+
+int check_group_ws(const GroupLayout& G, const void* ws, size_t ws_bytes) {
+  if (G.total == 0) return LORA_OK;
+  if (!ws || ws_bytes < G.total) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+// Acat rows of every member (rows r..r8 of each block are zeros) and the
+// per-column scales of the group panel.
+int group_acat(int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G, uint16_t* acat, ColScale* cs,
+               hipStream_t st) {
+  cs->n = n;
+  for (int g = 0; g < n; ++g) {
+    const int64_t r8 = rup(mb[g].r, 8);
+    HIPTRY(timed(K_COPY_ROWS, 0, 2.0 * (mb[g].r + r8) * d_in, st, [&] {
+      return launch_copy_rows(static_cast<const uint16_t*>(mb[g].A), d_in, mb[g].r, d_in, acat + G.off[g] * d_in,
+                              d_in, r8, st);
+    }));
+    cs->end[g] = G.off[g] + r8;
+    cs->s[g] = mb[g].scale;
+  }
+  return LORA_OK;
+}
+
+int group_forward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X,
+                  const Rope* rope, const float* table16, void* ws, const GroupLayout& G, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  char* sh = w + G.shared;
+  const bool share = dtype == LORA_BF16 && M > 0;
+  uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
+  if (share) {
+    ColScale cs{};
+    TRY(group_acat(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+    TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
+                   reinterpret_cast<float*>(sh), P, G.rt, nullptr, 0, st));
+  }
+  for (int g = 0; g < n; ++g) {
+    const lora_group_member& m = mb[g];
+    const Nf4W q{m.W_nf4, m.absmax, table16};
+    TRY(forward_impl(dtype, M, d_in, m.d_out, m.r, m.scale, X, m.W, m.W_nf4 ? &q : nullptr, m.A, m.B,
+                     m.rope ? rope : nullptr, m.Y, sh, G.mem[g], st, share ? P + G.off[g] : nullptr, G.rt));
+  }
+  return LORA_OK;
+}
+
+int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X,
+                   const Rope* rope, const float* table16, void* ws, const GroupLayout& G, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  char* sh = w + G.shared;
+  const bool share = dtype == LORA_BF16 && M > 0;
+  uint16_t* Pt = reinterpret_cast<uint16_t*>(w + G.pt);
+  uint16_t* Qs = reinterpret_cast<uint16_t*>(w + G.qs);
+  uint16_t* Qt = reinterpret_cast<uint16_t*>(w + G.qt);
+  if (share) {
+    ColScale cs{};
+    TRY(group_acat(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+    TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, G.M8, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
+                   reinterpret_cast<float*>(sh), nullptr, 0, Pt, G.M8, st));
+  }
+  for (int g = 0; g < n; ++g) {
+    const lora_group_member& m = mb[g];
+    const Nf4W q{m.W_nf4, m.absmax, table16};
+    const PanelSlices ov{Pt + G.off[g] * G.M8, Qs + G.off[g], G.rt, Qt + G.off[g] * G.M8};
+    TRY(backward_impl(dtype, M, d_in, m.d_out, m.r, m.scale, X, m.W, m.W_nf4 ? &q : nullptr, m.A, m.B,
+                      m.rope ? rope : nullptr, m.dY, m.dX, m.dA, m.dB, sh, G.mem[g], st, share ? &ov : nullptr));
+  }
+  if (!share) return LORA_OK;
+  // dA of every member in one pass over X: Qt X -> partials [splits][rt, d_in]
+  float* part = reinterpret_cast<float*>(sh);
+  const double Md = double(M), ki = double(d_in), rr = double(G.rt);
+  GemmArgs a = blank();
+  a.a1 = Qt; a.lda1 = G.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
+  a.m_load = G.rt; a.m_store = G.rt; a.n_load = d_in; a.n_store = d_in;
+  a.k_split = G.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = G.rt * d_in;
+  HIPTRY(gemm(G_BF16_SPLIT_NN_PARTIAL, a, G.splits_dA, st, 2 * rr * ki * Md,
+              (rr * Md + Md * ki) * 2 + 4.0 * G.splits_dA * G.rt * ki));
+  for (int g = 0; g < n; ++g) {
+    const double rg = double(mb[g].r);
+    HIPTRY(timed(K_REDUCE, double(G.splits_dA) * rg * ki, 4.0 * (G.splits_dA + 1) * rg * ki, st, [&] {
+      return launch_reduce_splits(part + G.off[g] * d_in, G.splits_dA, mb[g].r, d_in, G.rt * d_in, false, mb[g].dA,
+                                  st);
+    }));
+  }
+  return LORA_OK;
 }
 
 }  // namespace
@@ -593,6 +791,39 @@ int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_
   HIPTRY(timed(K_NF4_DEQ, 2.0 * n, n / 2.0 + n / 16.0 + 2.0 * n, st,
                [&] { return launch_nf4_dequant(W_nf4, absmax, n, table16, out_bf16, st); }));
   return LORA_OK;
+}
+
+size_t lora_group_workspace_bytes(int backward, int dtype, int64_t M, int64_t d_in, int n,
+                                  const lora_group_member* members) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  if (!members || n < 1 || n > LORA_GROUP_MAX) return 0;
+  for (int g = 0; g < n; ++g)
+    if (check_sizes(M, d_in, members[g].d_out, members[g].r) != LORA_OK) return 0;
+  return make_group_layout(backward != 0, dtype, M, d_in, n, members).total;
+}
+
+int lora_group_fwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* members, const void* X,
+                   int head_dim, const int32_t* positions, const float* cos_cache, const float* sin_cache,
+                   int64_t max_pos, const float* table16, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_group(false, dtype, M, d_in, n, members, X, head_dim, positions, cos_cache, sin_cache, max_pos,
+                  table16));
+  const GroupLayout G = make_group_layout(false, dtype, M, d_in, n, members);
+  TRY(check_group_ws(G, ws, ws_bytes));
+  TRY(check_device());
+  const Rope rp{positions, cos_cache, sin_cache};
+  return group_forward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
+}
+
+int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* members, const void* X,
+                   int head_dim, const int32_t* positions, const float* cos_cache, const float* sin_cache,
+                   int64_t max_pos, const float* table16, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_group(true, dtype, M, d_in, n, members, X, head_dim, positions, cos_cache, sin_cache, max_pos,
+                  table16));
+  const GroupLayout G = make_group_layout(true, dtype, M, d_in, n, members);
+  TRY(check_group_ws(G, ws, ws_bytes));
+  TRY(check_device());
+  const Rope rp{positions, cos_cache, sin_cache};
+  return group_backward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
 }
 
 int lora_profile_begin(int max_launches) {

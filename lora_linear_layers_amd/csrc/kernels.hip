@@ -286,11 +286,15 @@ constexpr int kMaxPanelSplits = 32;
 // then the row-major and/or (through LDS) the transposed bf16 stores.
 __global__ void __launch_bounds__(256) panel_reduce_kernel(const float* __restrict__ part, int splits,
                                                            int64_t part_stride, int64_t ldp, int64_t rows, int64_t n,
-                                                           float alpha, uint16_t* __restrict__ out, int64_t ldo,
+                                                           ColScale scale, uint16_t* __restrict__ out, int64_t ldo,
                                                            uint16_t* __restrict__ outt, int64_t ldot) {
   __shared__ float tile[16][65];
   const int64_t r0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
   const int cc = threadIdx.x & 63;
+  float alpha = scale.s[0];
+#pragma unroll
+  for (int i = kColScaleMax - 1; i >= 0; --i)
+    if (i < scale.n && c0 + cc < scale.end[i]) alpha = scale.s[i];
   for (int rr = threadIdx.x >> 6; rr < 16; rr += 4) {
     const int64_t q = r0 + rr, c = c0 + cc;
     float v = 0.f;
@@ -318,13 +322,31 @@ __global__ void __launch_bounds__(256) panel_reduce_kernel(const float* __restri
 }
 
 hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_stride, int64_t ldp, int64_t rows,
-                               int64_t n, float alpha, uint16_t* out, int64_t ldo, uint16_t* outt, int64_t ldot,
-                               hipStream_t st) {
+                               int64_t n, const ColScale& scale, uint16_t* out, int64_t ldo, uint16_t* outt,
+                               int64_t ldot, hipStream_t st) {
   if (rows <= 0 || n <= 0) return hipSuccess;
-  if (splits < 1 || splits > kMaxPanelSplits) return hipErrorInvalidValue;
+  if (splits < 1 || splits > kMaxPanelSplits || scale.n < 1 || scale.n > kColScaleMax) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((n + 63) / 64));
-  hipLaunchKernelGGL(panel_reduce_kernel, grid, dim3(256), 0, st, part, splits, part_stride, ldp, rows, n, alpha, out,
+  hipLaunchKernelGGL(panel_reduce_kernel, grid, dim3(256), 0, st, part, splits, part_stride, ldp, rows, n, scale, out,
                      ldo, outt, ldot);
+  return hipGetLastError();
+}
+
+__global__ void copy_rows_kernel(const uint16_t* __restrict__ src, int64_t lds, int64_t rows, int64_t cols,
+                                 uint16_t* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
+  const int64_t n = rows_pad * cols;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / cols, j = e - i * cols;
+    dst[i * ldd + j] = i < rows ? src[i * lds + j] : (uint16_t)0;
+  }
+}
+
+hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, int64_t rows, int64_t cols, uint16_t* dst,
+                            int64_t ldd, int64_t rows_pad, hipStream_t st) {
+  const int64_t n = rows_pad * cols;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_rows_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, src, lds, rows, cols, dst, ldd,
+                     rows_pad);
   return hipGetLastError();
 }
 

@@ -72,12 +72,33 @@ hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float*
 hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N,
                                 int64_t part_stride, bool transpose, float* out, hipStream_t st);
 
-// Rank-r panel from split partials: v = alpha * sum over z < splits of
+// Per-column scale of a panel: column c takes s[i] for the first i < n with
+// c < end[i] (one entry per projection of a group; n = 1 for one projection).
+constexpr int kColScaleMax = 8;
+struct ColScale {
+  int n;
+  int64_t end[kColScaleMax];
+  float s[kColScaleMax];
+};
+inline ColScale col_scale(float s) {
+  ColScale c{};
+  c.n = 1;
+  c.end[0] = INT64_MAX;
+  c.s[0] = s;
+  return c;
+}
+
+// Rank-r panel from split partials: v = scale(c) * sum over z < splits of
 // part[z][q, c] (fixed order) for q < rows, c < n; written as bf16 to
 // out[q * ldo + c] and/or outt[c * ldot + q] (either may be null).
 hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_stride, int64_t ldp, int64_t rows,
-                               int64_t n, float alpha, uint16_t* out, int64_t ldo, uint16_t* outt, int64_t ldot,
-                               hipStream_t st);
+                               int64_t n, const ColScale& scale, uint16_t* out, int64_t ldo, uint16_t* outt,
+                               int64_t ldot, hipStream_t st);
+
+// dst rows [0, rows_pad) of width cols (row stride ldd) = src rows [0, rows)
+// (row stride lds) followed by zero rows; bf16.
+hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, int64_t rows, int64_t cols, uint16_t* dst,
+                            int64_t ldd, int64_t rows_pad, hipStream_t st);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 

@@ -143,6 +143,95 @@ def nf4_dequant(codes, absmax, table16, n: int, blocksize: int = 64):
     return out
 
 
+def _group_members(X, members):
+    """ctypes array of lora_group_member from dicts with keys A, B, scale and
+    either W or (codes, absmax), plus an optional rope flag."""
+    n = len(members)
+    if not 1 <= n <= L.GROUP_MAX:
+        raise ValueError(f"a group holds 1..{L.GROUP_MAX} projections")
+    arr = (L.GroupMember * n)()
+    M, d_in = X.shape
+    for g, m in enumerate(members):
+        A, B = m["A"], m["B"]
+        W, codes, absmax = m.get("W"), m.get("codes"), m.get("absmax")
+        L._contig(A, B, W, codes, absmax)
+        r, d_out = A.shape[0], B.shape[0]
+        if A.shape != (r, d_in) or B.shape != (d_out, r) or (W is not None and W.shape != (d_out, d_in)):
+            raise ValueError("shape mismatch: X [M,d_in], W [d_out,d_in], A [r,d_in], B [d_out,r]")
+        if (W is None) == (codes is None):
+            raise ValueError("each member takes exactly one of W and NF4 codes")
+        e = arr[g]
+        e.d_out, e.r, e.scale, e.rope = d_out, r, float(m["scale"]), int(bool(m.get("rope", False)))
+        e.W, e.W_nf4, e.absmax = (L._ptr(t) for t in (W, codes, absmax))
+        e.A, e.B = L._ptr(A), L._ptr(B)
+    return arr
+
+
+def _group_ws(backward, dt, M, d_in, arr, device, ws):
+    n = int(L.lib().lora_group_workspace_bytes(int(backward), dt, M, d_in, len(arr), arr))
+    if ws is not None:
+        return ws
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def _group_rope(positions, cos, sin, M):
+    if positions is None:
+        return None, None, None, 0
+    L._contig(positions, cos, sin)
+    if positions.dtype != torch.int32 or positions.numel() != M:
+        raise ValueError("positions must be int32 [M]")
+    return L._ptr(positions), L._ptr(cos), L._ptr(sin), cos.shape[0]
+
+
+def lora_group_fwd(X, members, positions=None, cos=None, sin=None, table16=None, head_dim: int = 128, ws=None):
+    """[Y_1, .., Y_n] of projections sharing X, the rank-r panels in one pass over X."""
+    L._contig(X)
+    M, d_in = X.shape
+    dt = L._dtype_code(X)
+    arr = _group_members(X, members)
+    Ys = []
+    for g, m in enumerate(members):
+        Y = torch.empty(M, arr[g].d_out, dtype=X.dtype, device=X.device)
+        arr[g].Y = L._ptr(Y)
+        Ys.append(Y)
+    pos, c, s, max_pos = _group_rope(positions, cos, sin, M)
+    tab = L._table_ptr(table16) if table16 is not None else None
+    ws = _group_ws(False, dt, M, d_in, arr, X.device, ws)
+    L._check("lora_group_fwd", L.lib().lora_group_fwd(
+        dt, M, d_in, len(arr), arr, L._ptr(X), head_dim, pos, c, s, max_pos, tab, L._ptr(ws), ws.numel(),
+        L._stream(X.device)))
+    return Ys
+
+
+def lora_group_bwd(X, members, dYs, positions=None, cos=None, sin=None, table16=None, head_dim: int = 128,
+                   need_dX: bool = True, ws=None):
+    """[(dX_g or None, dA_g fp32, dB_g fp32)] per member; dX_g is the member's own
+    input gradient (the caller sums them)."""
+    L._contig(X, *dYs)
+    M, d_in = X.shape
+    dt = L._dtype_code(X)
+    arr = _group_members(X, members)
+    if len(dYs) != len(arr):
+        raise ValueError("one dY per member")
+    outs = []
+    for g in range(len(arr)):
+        d_out, r = arr[g].d_out, arr[g].r
+        if dYs[g].shape != (M, d_out):
+            raise ValueError("dY shape mismatch")
+        dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+        dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+        dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+        arr[g].dY, arr[g].dX, arr[g].dA, arr[g].dB = L._ptr(dYs[g]), L._ptr(dX), L._ptr(dA), L._ptr(dB)
+        outs.append((dX, dA, dB))
+    pos, c, s, max_pos = _group_rope(positions, cos, sin, M)
+    tab = L._table_ptr(table16) if table16 is not None else None
+    ws = _group_ws(True, dt, M, d_in, arr, X.device, ws)
+    L._check("lora_group_bwd", L.lib().lora_group_bwd(
+        dt, M, d_in, len(arr), arr, L._ptr(X), head_dim, pos, c, s, max_pos, tab, L._ptr(ws), ws.numel(),
+        L._stream(X.device)))
+    return outs
+
+
 class LoraLinearFunction(torch.autograd.Function):
     """Autograd wrapper: gradients for X, A and B (W frozen); A and B grads in fp32."""
 

@@ -132,3 +132,66 @@ def test_valid_call_without_gpu_reports_device_error(lib):
     # Arguments pass validation; with no device the library reports LORA_ERR_DEVICE
     # and launches nothing.
     assert _fwd(lib) == EDEV
+
+
+def _members(n=2, **kw):
+    arr = (_lib.GroupMember * n)()
+    for g in range(n):
+        e = arr[g]
+        e.d_out, e.r, e.scale, e.rope = 64 * (g + 1), 8 + g, 1.0, 0
+        e.W, e.A, e.B, e.Y, e.dY, e.dX, e.dA, e.dB = (P,) * 8
+        for k, v in kw.items():
+            setattr(e, k, v)
+    return arr
+
+
+def test_group_workspace_sizes(lib):
+    f = lib.lora_group_workspace_bytes
+    m = _members(3)
+    fwd, bwd = f(0, 1, 4096, 1024, 3, m), f(1, 1, 4096, 1024, 3, m)
+    rt = 8 + 16 + 16  # ranks 8, 9, 10 padded to multiples of 8
+    assert fwd >= rt * 1024 * 2 + 4096 * rt * 2  # Acat and the group panel
+    assert bwd >= rt * 1024 * 2 + 3 * 4096 * rt * 2  # Acat, Pt, Qs, Qt
+    # fp32 groups run member by member: the largest member's own workspace
+    single = max(lib.lora_workspace_bytes(_lib.OP_BWD, 0, 4096, 1024, 64 * (g + 1), 8 + g) for g in range(3))
+    assert f(1, 0, 4096, 1024, 3, m) == single
+    assert f(0, 1, 8, 8, 0, m) == 0
+    assert f(0, 1, 8, 8, 9, _members(9)) == 0
+    assert f(0, 5, 8, 64, 3, m) == 0
+    assert f(0, 1, 8, 64, 3, None) == 0
+    assert f(0, 1, 8, 64, 1, _members(1, r=0)) == 0
+
+
+def _gfwd(lib, m, n=None, dtype=1, X=P, head_dim=128, pos=P, cs=P, max_pos=16, table=None, ws=P, wsb=1 << 30):
+    n = len(m) if n is None else n
+    return lib.lora_group_fwd(dtype, 16, 64, n, m, X, head_dim, pos, cs, cs, max_pos, table, ws, wsb, None)
+
+
+def _gbwd(lib, m, dtype=1, ws=P, wsb=1 << 30):
+    return lib.lora_group_bwd(dtype, 16, 64, len(m), m, P, 128, P, P, P, 16, None, ws, wsb, None)
+
+
+def test_group_validation(lib):
+    tab = (ctypes.c_float * 16)(*range(16))
+    assert _gfwd(lib, _members(2), n=0) == ESHAPE
+    assert _gfwd(lib, _members(9)) == ESHAPE
+    assert _gfwd(lib, None, n=1) == ENULL
+    assert _gfwd(lib, _members(2), dtype=3) == EDTYPE
+    assert _gfwd(lib, _members(2), X=None) == ENULL
+    assert _gfwd(lib, _members(2, Y=None)) == ENULL
+    assert _gfwd(lib, _members(2, A=P + 2)) == EALIGN
+    assert _gfwd(lib, _members(2, r=300)) == ESHAPE
+    assert _gfwd(lib, _members(2, W=None)) == ENULL
+    # RoPE members need head_dim 128 and d_out a multiple of it
+    assert _gfwd(lib, _members(1, rope=1), head_dim=64) == ESHAPE
+    assert _gfwd(lib, _members(2, rope=1)) == ESHAPE  # member 0 has d_out 64
+    assert _gfwd(lib, _members(1, rope=1, d_out=128), pos=None) == ENULL
+    # NF4 members: bf16 only, table required, no RoPE
+    assert _gfwd(lib, _members(1, W=None, W_nf4=P, absmax=P), table=tab, dtype=0) == EDTYPE
+    assert _gfwd(lib, _members(1, W=None, W_nf4=P, absmax=P)) == ENULL
+    assert _gfwd(lib, _members(1, W=None, W_nf4=P, absmax=P, rope=1, d_out=128), table=tab) == ESHAPE
+    assert _gfwd(lib, _members(2), wsb=100) == EWS
+    assert _gbwd(lib, _members(2, dA=None)) == ENULL
+    assert _gbwd(lib, _members(2, dY=None)) == ENULL
+    assert _gbwd(lib, _members(2, dX=P + 8)) == EALIGN
+    assert _gbwd(lib, _members(2), wsb=100) == EWS
