@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload: 1..5 (3 = Llama-3-8B MLP)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-group", action="store_true",
+                    help="run projections that share X one by one instead of as one group")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for HBM counters)")
@@ -80,6 +82,7 @@ KIND_OF = {
     "reduce_splits_kernel": "reduce_splits",
     "transpose_pad_kernel": "transpose_pad",
     "rope_inverse_kernel": "rope_inverse",
+    "copy_rows_kernel": "copy_rows",
 }
 
 
@@ -132,7 +135,7 @@ def traffic_from(fetch_csv, write_csv, cfg_id):
 class Workload:
     """Device tensors and preallocated outputs for every projection of a config."""
 
-    def __init__(self, cfg, device="cuda"):
+    def __init__(self, cfg, device="cuda", group=True):
         import torch
 
         import lora_linear_layers_amd as L
@@ -169,12 +172,44 @@ class Workload:
             for op in ops:
                 wsmax = max(wsmax, L.workspace_bytes(op, dt, M, p.d_in, p.d_out, r))
             self.items.append(it)
+        # projections that read the same X run as one group (in config order)
+        self.groups = []
+        for it in self.items:
+            if group and self.groups and self.groups[-1][0]["p"].x_group == it["p"].x_group:
+                self.groups[-1].append(it)
+            else:
+                self.groups.append([it])
+        self.members = []
+        for grp in self.groups:
+            ms = []
+            for it in grp:
+                m = {"A": it["A"], "B": it["B"], "scale": cfg.scale, "rope": it["p"].rope}
+                if cfg.nf4:
+                    m["codes"], m["absmax"] = it["codes"], it["absmax"]
+                else:
+                    m["W"] = it["W"]
+                ms.append(m)
+            self.members.append(ms)
+            if len(grp) > 1:
+                arr = L.functional._group_members(grp[0]["X"], ms)
+                for bwd in (0, 1):
+                    wsmax = max(wsmax, int(L.lib().lora_group_workspace_bytes(bwd, dt, M, grp[0]["p"].d_in,
+                                                                             len(arr), arr)))
         self.ws = torch.empty(max(wsmax, 256), dtype=torch.uint8, device=device)
         torch.cuda.synchronize()
 
+    def _rope_args(self):
+        return (self.pos, self.cos, self.sin) if hasattr(self, "pos") else (None, None, None)
+
     def step(self):
         L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
-        for it in self.items:
+        tab = self.table if cfg.nf4 else None
+        for grp, ms in zip(self.groups, self.members):
+            if len(grp) > 1:
+                L.lora_group_fwd(grp[0]["X"], ms, *self._rope_args(), table16=tab, ws=ws,
+                                 Ys=[it["Y"] for it in grp])
+                continue
+            it = grp[0]
             p = it["p"]
             if cfg.nf4:
                 L.nf4_lora_linear_fwd(it["X"], it["codes"], it["absmax"], self.table, it["A"], it["B"], s,
@@ -184,7 +219,12 @@ class Workload:
                                    Y=it["Y"], ws=ws)
             else:
                 L.lora_linear_fwd(it["X"], it["W"], it["A"], it["B"], s, Y=it["Y"], ws=ws)
-        for it in reversed(self.items):
+        for grp, ms in reversed(list(zip(self.groups, self.members))):
+            if len(grp) > 1:
+                L.lora_group_bwd(grp[0]["X"], ms, [it["dY"] for it in grp], *self._rope_args(), table16=tab,
+                                 ws=ws, outs=[(it["dX"], it["dA"], it["dB"]) for it in grp])
+                continue
+            it = grp[0]
             p = it["p"]
             out = (it["dX"], it["dA"], it["dB"])
             if cfg.nf4:
@@ -300,7 +340,7 @@ def main():
     cfg = CONFIGS[args.config]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    work = Workload(cfg, device=dev)
+    work = Workload(cfg, device=dev, group=not args.no_group)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -375,6 +415,7 @@ def main():
                    "r": cfg.r, "alpha": cfg.alpha, "nf4_base": cfg.nf4,
                    "projections": [f"{p.name} {p.d_in}->{p.d_out}{' +rope' if p.rope else ''}"
                                    for p in cfg.projections],
+                   "x_groups": [[it["p"].name for it in grp] for grp in work.groups],
                    "useful_tflop_per_step": round(flop / 1e12, 4), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,

@@ -155,10 +155,17 @@ int lora_qk_rope_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
  * e/2, high nibble for even e.  absmax: device fp32 [d_out * d_in / blocksize],
  * one per block of `blocksize` consecutive elements.  table16: HOST pointer to
  * the 16 fp32 code values (copied into the launch).  The weight used is
- *     W[e] = bf16_rne(fp32_rne(table16[code_e] * absmax[e / blocksize])),
- * formed inside the GEMM's load stage, never written to memory.
+ *     W[e] = bf16_rne(fp32_rne(table16[code_e] * absmax[e / blocksize])).
+ * Below LORA_NF4_DEQUANT_MIN_TOKENS tokens (M) it is formed inside the GEMM's
+ * load stage and never written to memory: there the GEMM is bound by reading
+ * W, and the codes are a quarter of its bf16 bytes.  From that M on, the same
+ * routine writes W once per call into the workspace (2 * d_out * d_in bytes,
+ * included in lora_workspace_bytes) and the bf16 GEMMs read it: there the GEMM
+ * is bound by the matrix cores, and the load stage would repeat the lookup
+ * once per 256-row tile of X.  Both give the same W bit for bit.
  * blocksize must be 64 and d_in a multiple of 64.  X, A, B, Y are bf16.
  */
+#define LORA_NF4_DEQUANT_MIN_TOKENS 512
 int nf4_lora_linear_fwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
                         const void* X, const uint8_t* W_nf4, const float* absmax, int blocksize,
                         const float* table16, const void* A, const void* B, void* Y, void* ws,
@@ -189,7 +196,8 @@ int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_
  * the forward panel s X A^T, the backward's recomputation of X A^T and the dA
  * contraction over X.  Everything else runs per member exactly as in the
  * single-projection entry points, so every member's outputs equal that
- * member's single call up to rounding order.
+ * member's single call up to rounding order.  (fp32 groups run their members
+ * one after another.)
  *
  * `members` is a HOST array of n (1 <= n <= LORA_GROUP_MAX) descriptions whose
  * pointers are device pointers.  Per member: d_out, r and the pointer rules

@@ -54,7 +54,8 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t r8 = 0, M8 = 0;
-  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, total = 0;
+  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, total = 0;
+  bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
   int splits_dA = 1, splits_dB = 1;
   int64_t ksplit_dA = 0, ksplit_dB = 0;
   int splits_p = 1, splits_q = 1;  // bf16 rank-r panels: P = X A^T, Q = G B
@@ -106,6 +107,10 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     return at;
   };
   const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD;
+  if ((op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD) && M >= LORA_NF4_DEQUANT_MIN_TOKENS) {
+    L.dequant = true;
+    L.wdq = take(size_t(d_out) * d_in * 2);
+  }
   if (r % 8) L.bpad = take(size_t(d_out) * L.r8 * eb);
   if (eb == 2) {
     panel_split(M, d_in, L.r8, &L.splits_p, &L.ksplit_p);
@@ -279,6 +284,14 @@ struct Rope {
   const float* sinc;
 };
 
+// W [n] bf16 from NF4 codes with the load stage's own routine (one pass).
+int dequant_w(const Nf4W& q, int64_t n, void* out, hipStream_t st) {
+  HIPTRY(timed(K_NF4_DEQ, 2.0 * n, n / 2.0 + n / 16.0 + 2.0 * n, st, [&] {
+    return launch_nf4_dequant(q.codes, q.absmax, n, q.table, static_cast<uint16_t*>(out), st);
+  }));
+  return LORA_OK;
+}
+
 // Pext: when not NULL, the panel s X A^T is already in Pext (row stride
 // ldpext, columns r..r8 zero) and is not computed here (group calls).
 int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
@@ -288,6 +301,11 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  if (nf4 && L.dequant) {
+    TRY(dequant_w(*nf4, d_out * d_in, w + L.wdq, st));
+    W = w + L.wdq;
+    nf4 = nullptr;
+  }
   const void* Bsrc = B;
   if (r % 8) {
     HIPTRY(timed(K_PAD, 0, 2.0 * d_out * L.r8 * eb, st,
@@ -358,6 +376,11 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  if (nf4 && L.dequant) {
+    TRY(dequant_w(*nf4, d_out * d_in, w + L.wdq, st));
+    W = w + L.wdq;
+    nf4 = nullptr;
+  }
   const void* Bsrc = B;
   if (r % 8) {
     HIPTRY(timed(K_PAD, 0, 2.0 * d_out * L.r8 * eb, st,

@@ -365,25 +365,38 @@ struct Table16 {
   float v[16];
 };
 
-// One thread per code byte (two elements); the same byte -> bf16x2 routine as
-// the NF4 GEMM load stage.  Blocks of 64 elements share one absmax.
+// The same byte -> bf16x2 routine as the NF4 GEMM load stage.  Per thread and
+// iteration: 16 code bytes (32 elements, half of one 64-element absmax block)
+// in one 16-byte load, four 16-byte stores of bf16.
 __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ codes,
-                                                          const float* __restrict__ absmax, int64_t nbytes,
-                                                          Table16 tab, uint32_t* __restrict__ out) {
+                                                          const float* __restrict__ absmax, int64_t nchunks,
+                                                          Table16 tab, u32x4* __restrict__ out) {
   __shared__ float2 tab2[256];
   nf4_fill_tab2(tab2, tab.v, threadIdx.x, blockDim.x);
   __syncthreads();
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nbytes; j += (int64_t)gridDim.x * blockDim.x)
-    out[j] = nf4_byte_to_bf16x2(tab2, codes[j], absmax[j >> 5]);
+  const u32x4* src = reinterpret_cast<const u32x4*>(codes);
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nchunks; j += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4 c = src[j];
+    const float am = absmax[j >> 1];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      u32x4 o;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) o[b] = nf4_byte_to_bf16x2(tab2, c[w] >> (8 * b), am);
+      out[4 * j + w] = o;
+    }
+  }
 }
 
 hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* table16,
                               uint16_t* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;
+  if (n % 64) return hipErrorInvalidValue;
   Table16 t;
   for (int i = 0; i < 16; ++i) t.v[i] = table16[i];
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(n / 2, 256)), dim3(256), 0, st, codes, absmax, n / 2, t,
-                     (uint32_t*)out);
+  const int64_t nchunks = n / 32;
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(nchunks, 256)), dim3(256), 0, st, codes, absmax, nchunks, t,
+                     reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
 

@@ -183,17 +183,20 @@ def _group_rope(positions, cos, sin, M):
     return L._ptr(positions), L._ptr(cos), L._ptr(sin), cos.shape[0]
 
 
-def lora_group_fwd(X, members, positions=None, cos=None, sin=None, table16=None, head_dim: int = 128, ws=None):
+def lora_group_fwd(X, members, positions=None, cos=None, sin=None, table16=None, head_dim: int = 128, ws=None,
+                   Ys=None):
     """[Y_1, .., Y_n] of projections sharing X, the rank-r panels in one pass over X."""
     L._contig(X)
     M, d_in = X.shape
     dt = L._dtype_code(X)
     arr = _group_members(X, members)
-    Ys = []
-    for g, m in enumerate(members):
-        Y = torch.empty(M, arr[g].d_out, dtype=X.dtype, device=X.device)
+    if Ys is None:
+        Ys = [torch.empty(M, arr[g].d_out, dtype=X.dtype, device=X.device) for g in range(len(arr))]
+    for g, Y in enumerate(Ys):
+        L._contig(Y)
+        if Y.shape != (M, arr[g].d_out) or Y.dtype != X.dtype:
+            raise ValueError("Y shape or dtype mismatch")
         arr[g].Y = L._ptr(Y)
-        Ys.append(Y)
     pos, c, s, max_pos = _group_rope(positions, cos, sin, M)
     tab = L._table_ptr(table16) if table16 is not None else None
     ws = _group_ws(False, dt, M, d_in, arr, X.device, ws)
@@ -204,7 +207,7 @@ def lora_group_fwd(X, members, positions=None, cos=None, sin=None, table16=None,
 
 
 def lora_group_bwd(X, members, dYs, positions=None, cos=None, sin=None, table16=None, head_dim: int = 128,
-                   need_dX: bool = True, ws=None):
+                   need_dX: bool = True, ws=None, outs=None):
     """[(dX_g or None, dA_g fp32, dB_g fp32)] per member; dX_g is the member's own
     input gradient (the caller sums them)."""
     L._contig(X, *dYs)
@@ -213,23 +216,30 @@ def lora_group_bwd(X, members, dYs, positions=None, cos=None, sin=None, table16=
     arr = _group_members(X, members)
     if len(dYs) != len(arr):
         raise ValueError("one dY per member")
-    outs = []
+    res = []
     for g in range(len(arr)):
         d_out, r = arr[g].d_out, arr[g].r
         if dYs[g].shape != (M, d_out):
             raise ValueError("dY shape mismatch")
-        dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
-        dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
-        dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+        if outs is None:
+            dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+            dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+            dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+        else:
+            dX, dA, dB = outs[g]
+            L._contig(dX, dA, dB)
+            if (dX is not None and dX.shape != (M, d_in)) or dA.shape != (r, d_in) or dB.shape != (d_out, r) \
+                    or dA.dtype != torch.float32 or dB.dtype != torch.float32:
+                raise ValueError("output shape or dtype mismatch")
         arr[g].dY, arr[g].dX, arr[g].dA, arr[g].dB = L._ptr(dYs[g]), L._ptr(dX), L._ptr(dA), L._ptr(dB)
-        outs.append((dX, dA, dB))
+        res.append((dX, dA, dB))
     pos, c, s, max_pos = _group_rope(positions, cos, sin, M)
     tab = L._table_ptr(table16) if table16 is not None else None
     ws = _group_ws(True, dt, M, d_in, arr, X.device, ws)
     L._check("lora_group_bwd", L.lib().lora_group_bwd(
         dt, M, d_in, len(arr), arr, L._ptr(X), head_dim, pos, c, s, max_pos, tab, L._ptr(ws), ws.numel(),
         L._stream(X.device)))
-    return outs
+    return res
 
 
 class LoraLinearFunction(torch.autograd.Function):
