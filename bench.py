@@ -31,8 +31,7 @@ PEAK = {"bf16": 2516.6, "f32": 157.3}  # TFLOP/s, dense MFMA (MI355X: 256 CU x 2
 HBM_PEAK = 8000.0  # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["lora_linear_layers_amd/csrc/gemm.h", "lora_linear_layers_amd/csrc/gemm_w4.h",
-                  "lora_linear_layers_amd/csrc/panel.h", "lora_linear_layers_amd/csrc/kernels.hip",
-                  "lora_linear_layers_amd/csrc/api.cpp"]
+                  "lora_linear_layers_amd/csrc/kernels.hip", "lora_linear_layers_amd/csrc/api.cpp"]
 
 
 def kernel_hash() -> str:
@@ -50,6 +49,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, help="workload: 1..5 (3 = Llama-3-8B MLP)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--call-reps", type=int, default=10,
+                    help="HIP-event repetitions of each call for the per-call median/p10/p90 (0 = skip)")
+    ap.add_argument("--no-small-token", action="store_true", help="skip the few-token HBM sweep")
     ap.add_argument("--no-group", action="store_true",
                     help="run projections that share X one by one instead of as one group")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
@@ -201,38 +203,163 @@ class Workload:
     def _rope_args(self):
         return (self.pos, self.cos, self.sin) if hasattr(self, "pos") else (None, None, None)
 
-    def step(self):
+    def call_name(self, gi):
+        return "+".join(it["p"].name for it in self.groups[gi])
+
+    def call_flop(self, gi, bwd):
+        """Useful FLOP of one call: 2M(dk + r(d+k)) forward, 2M(dk + 2r(d+k)) backward."""
+        M, r = self.cfg.M, self.cfg.r
+        f = 0.0
+        for it in self.groups[gi]:
+            p = it["p"]
+            f += 2.0 * M * (p.d_in * p.d_out + (2 if bwd else 1) * r * (p.d_in + p.d_out))
+        return f
+
+    def fwd(self, gi):
         L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
-        tab = self.table if cfg.nf4 else None
-        for grp, ms in zip(self.groups, self.members):
-            if len(grp) > 1:
-                L.lora_group_fwd(grp[0]["X"], ms, *self._rope_args(), table16=tab, ws=ws,
-                                 Ys=[it["Y"] for it in grp])
-                continue
-            it = grp[0]
-            p = it["p"]
-            if cfg.nf4:
-                L.nf4_lora_linear_fwd(it["X"], it["codes"], it["absmax"], self.table, it["A"], it["B"], s,
-                                      p.d_out, Y=it["Y"], ws=ws)
-            elif p.rope:
-                L.lora_qk_rope_fwd(it["X"], it["W"], it["A"], it["B"], s, self.pos, self.cos, self.sin,
-                                   Y=it["Y"], ws=ws)
+        grp, ms = self.groups[gi], self.members[gi]
+        if len(grp) > 1:
+            L.lora_group_fwd(grp[0]["X"], ms, *self._rope_args(), table16=self.table if cfg.nf4 else None, ws=ws,
+                             Ys=[it["Y"] for it in grp])
+            return
+        it = grp[0]
+        p = it["p"]
+        if cfg.nf4:
+            L.nf4_lora_linear_fwd(it["X"], it["codes"], it["absmax"], self.table, it["A"], it["B"], s,
+                                  p.d_out, Y=it["Y"], ws=ws)
+        elif p.rope:
+            L.lora_qk_rope_fwd(it["X"], it["W"], it["A"], it["B"], s, self.pos, self.cos, self.sin,
+                               Y=it["Y"], ws=ws)
+        else:
+            L.lora_linear_fwd(it["X"], it["W"], it["A"], it["B"], s, Y=it["Y"], ws=ws)
+
+    def bwd(self, gi):
+        L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
+        grp, ms = self.groups[gi], self.members[gi]
+        if len(grp) > 1:
+            L.lora_group_bwd(grp[0]["X"], ms, [it["dY"] for it in grp], *self._rope_args(),
+                             table16=self.table if cfg.nf4 else None, ws=ws,
+                             outs=[(it["dX"], it["dA"], it["dB"]) for it in grp])
+            return
+        it = grp[0]
+        p = it["p"]
+        out = (it["dX"], it["dA"], it["dB"])
+        if cfg.nf4:
+            _nf4_bwd(L, it, self.table, s, ws, out)
+        elif p.rope:
+            _rope_bwd(L, it, self, s, ws, out)
+        else:
+            L.lora_linear_bwd(it["X"], it["W"], it["A"], it["B"], s, it["dY"], ws=ws, out=out)
+
+    def step(self):
+        """One pass of the layer over the batch: every projection's forward, then
+        every backward in reverse order."""
+        for gi in range(len(self.groups)):
+            self.fwd(gi)
+        for gi in reversed(range(len(self.groups))):
+            self.bwd(gi)
+
+
+def _pct(ts):
+    ts = sorted(ts)
+    pick = lambda q: ts[min(len(ts) - 1, int(round(q * (len(ts) - 1))))]  # noqa: E731
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4)}
+
+
+def per_call_times(work, reps):
+    """HIP-event time of each call (forward and backward apart), median/p10/p90 in ms."""
+    import torch
+
+    out = {}
+    for gi in range(len(work.groups)):
+        res = {}
+        for kind, fn in (("fwd", work.fwd), ("bwd", work.bwd)):
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn(gi)
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            res[kind + "_ms"] = _pct(ts)
+        t = res["fwd_ms"]["median"] + res["bwd_ms"]["median"]
+        res["tflops"] = round((work.call_flop(gi, False) + work.call_flop(gi, True)) / (t * 1e-3) / 1e12, 1)
+        out[work.call_name(gi)] = res
+    return out
+
+
+def small_token_sweep(device, reps=10):
+    """Few-token cases, where reading W bounds the layer: the Llama-3-8B q
+    projection (4096->4096, r 16, RoPE, bf16) and the Qwen1.5-32B-shaped gate
+    projection (5120->27392, r 64, NF4 W), M in {16, 64, 128}.  Each timed call
+    follows a 1 GiB write that evicts the 256 MB MALL, so W comes from HBM.
+    GB/s = minimum HBM bytes of the call / its HIP-event time."""
+    import math
+
+    import torch
+
+    import lora_linear_layers_amd as L
+    from synth import gen
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    tab = gen.nf4_table()
+    res = {}
+    cases = [("q_proj 4096->4096 r16 rope bf16", 4096, 4096, 16, True, False),
+             ("gate_proj 5120->27392 r64 nf4", 5120, 27392, 64, False, True)]
+    for name, k, d, r, rope, nf4 in cases:
+        seed = 9000 + d
+        A = gen.to_storage(gen.uniform_sym(seed + 2, r * k, 1.0 / math.sqrt(k), device=device), (r, k), "bf16")
+        B = gen.to_storage(gen.normal(seed + 3, d * r, math.sqrt(0.02), device=device), (d, r), "bf16")
+        if nf4:
+            codes = gen.nf4_random_codes(seed + 1, d * k, device=device)
+            absmax = gen.nf4_random_absmax(seed + 4, d * k // 64, 1.0 / math.sqrt(k), device=device)
+            wbytes = d * k / 2 + d * k / 64 * 4
+        else:
+            W = gen.to_storage(gen.normal(seed + 1, d * k, 1.0 / math.sqrt(k), device=device), (d, k), "bf16")
+            wbytes = 2.0 * d * k
+        cos, sin = L.rope_cache(2048, 128, 500000.0, device=device)
+        for M in (16, 64, 128):
+            X = gen.to_storage(gen.normal(seed + 5, M * k, 1.0, device=device), (M, k), "bf16")
+            dY = gen.to_storage(gen.normal(seed + 6, M * d, 1.0, device=device), (M, d), "bf16")
+            pos = torch.from_numpy(gen.positions_mod(M, 2048)).to(device)
+            op_f, op_b = (L.OP_NF4_FWD, L.OP_NF4_BWD) if nf4 else \
+                ((L.OP_ROPE_FWD, L.OP_ROPE_BWD) if rope else (L.OP_FWD, L.OP_BWD))
+            wsb = max(L.workspace_bytes(op, L.LORA_BF16, M, k, d, r) for op in (op_f, op_b))
+            ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=device)
+            Y = torch.empty(M, d, dtype=torch.bfloat16, device=device)
+            outs = (torch.empty(M, k, dtype=torch.bfloat16, device=device),
+                    torch.empty(r, k, dtype=torch.float32, device=device),
+                    torch.empty(d, r, dtype=torch.float32, device=device))
+            if nf4:
+                f = lambda: L.nf4_lora_linear_fwd(X, codes, absmax, tab, A, B, 0.25, d, Y=Y, ws=ws)  # noqa: E731
+                it = {"X": X, "codes": codes, "absmax": absmax, "A": A, "B": B, "dY": dY}
+                b = lambda: _nf4_bwd(L, it, tab, 0.25, ws, outs)  # noqa: E731
             else:
-                L.lora_linear_fwd(it["X"], it["W"], it["A"], it["B"], s, Y=it["Y"], ws=ws)
-        for grp, ms in reversed(list(zip(self.groups, self.members))):
-            if len(grp) > 1:
-                L.lora_group_bwd(grp[0]["X"], ms, [it["dY"] for it in grp], *self._rope_args(), table16=tab,
-                                 ws=ws, outs=[(it["dX"], it["dA"], it["dB"]) for it in grp])
-                continue
-            it = grp[0]
-            p = it["p"]
-            out = (it["dX"], it["dA"], it["dB"])
-            if cfg.nf4:
-                _nf4_bwd(L, it, self.table, s, ws, out)
-            elif p.rope:
-                _rope_bwd(L, it, self, s, ws, out)
-            else:
-                L.lora_linear_bwd(it["X"], it["W"], it["A"], it["B"], s, it["dY"], ws=ws, out=out)
+                f = lambda: L.lora_qk_rope_fwd(X, W, A, B, 1.0, pos, cos, sin, Y=Y, ws=ws)  # noqa: E731
+                it = {"X": X, "W": W, "A": A, "B": B, "dY": dY}
+                w = type("R", (), {"pos": pos, "cos": cos, "sin": sin})
+                b = lambda: _rope_bwd(L, it, w, 1.0, ws, outs)  # noqa: E731
+            fb = M * k * 2 + wbytes + r * k * 2 + d * r * 2 + M * d * 2
+            bb = M * k * 2 + M * d * 2 + wbytes + r * k * 2 + d * r * 2 + M * k * 2 + 4.0 * r * (k + d)
+            row = {}
+            for kind, fn, by in (("fwd", f, fb), ("bwd", b, bb)):
+                fn()
+                ts = []
+                for i in range(reps):
+                    flush.fill_(i & 255)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    e1.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                t = _pct(ts)
+                row[kind] = {"ms": t, "min_bytes": by, "gbps": round(by / (t["median"] * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(by / (t["median"] * 1e-3) / 8e12, 3)}
+            res[f"{name} M={M}"] = row
+    del flush
+    return res
 
 
 def _rope_bwd(L, it, w, s, ws, out):
@@ -261,6 +388,13 @@ def _nf4_bwd(L, it, table, s, ws, out):
         M, d_in, d_out, r, float(s), _lib._ptr(X), _lib._ptr(it["codes"]), _lib._ptr(it["absmax"]), 64, tab,
         _lib._ptr(A), _lib._ptr(B), _lib._ptr(dY), _lib._ptr(dX), _lib._ptr(dA), _lib._ptr(dB), _lib._ptr(ws),
         ws.numel(), _lib._stream(X.device)))
+
+
+def _rocm_version():
+    try:
+        return open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        return None
 
 
 def cpu_baseline(cfg, work, target_s):
@@ -394,6 +528,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / kpeak, 4), "traffic": traffic,
                 "avg_launch_us": round(1e3 * dms / dn, 1), "flop_per_launch": dfl / dn,
                 "algorithmic_bytes_per_launch": dby / dn}
+    if kpeak == PEAK["bf16"]:
+        # the dense bf16 rate this chip sustains under its own power limit
+        # (MFMA-only probe), as a second reference next to the published peak
+        mr = _lib.mfma_rate(device=dev)
+        roofline["peak_measured"] = round(mr, 1)
+        roofline["frac_of_measured"] = round(achieved / mr, 4)
+    calls = per_call_times(work, args.call_reps) if args.call_reps > 0 else None
 
     out = {
         "metric": METRIC,
@@ -419,8 +560,12 @@ def main():
                    "useful_tflop_per_step": round(flop / 1e12, 4), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,
+        "calls": calls,
         "device": torch.cuda.get_device_name(0),
+        "rocm": _rocm_version(),
     }
+    if not args.no_small_token:
+        out["small_token"] = small_token_sweep(dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, work, args.cpu_seconds)
     print(json.dumps(out), flush=True)

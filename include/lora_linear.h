@@ -75,7 +75,8 @@ enum {
   LORA_OP_ROPE_FWD = 2,
   LORA_OP_ROPE_BWD = 3,
   LORA_OP_NF4_FWD = 4,
-  LORA_OP_NF4_BWD = 5
+  LORA_OP_NF4_BWD = 5,
+  LORA_OP_MERGE = 6
 };
 
 /* Library version; equals LORA_ABI_VERSION of the header it was built from. */
@@ -186,6 +187,24 @@ int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_
                 const float* table16, uint16_t* out_bf16, void* stream);
 
 /*
+ * Merge for inference: W_out = W + scale * B A, one GEMM over the rank (fp32
+ * accumulation) whose epilogue adds W and rounds once to the output type.
+ * Page "微调太慢？试试Unsloth：实测训练速度翻倍，显存占用减半", section 5.1: for
+ * inference the adapter is folded into the main weight, so no rank-r branch
+ * runs per token; page "Unsloth自动化优化：无需手动调参的实现原理", section 3.2:
+ * the adapter product and the original weight combined in one kernel.
+ * Unmerge is the same call with -scale (it restores W up to the output type's
+ * rounding, since the merge rounded).  W_out may be W (in place: every element
+ * is read and written by the same thread, and by no other).  dtype LORA_F32 or
+ * LORA_BF16; W, W_out [d_out, d_in], A [r, d_in], B [d_out, r]; workspace of
+ * lora_workspace_bytes(LORA_OP_MERGE, dtype, 0, d_in, d_out, r) bytes (a
+ * padded copy of B when r is not a multiple of 8, else none).  An NF4 weight
+ * cannot absorb the adapter without re-quantising; there is no NF4 merge.
+ */
+int lora_merge(int dtype, int64_t d_out, int64_t d_in, int64_t r, float scale, const void* W, const void* A,
+               const void* B, void* W_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Groups of projections that read the same input X: q/k/v of attention,
  * gate/up of the MLP.  Page "UnSloth加速微调体验…", section RoPE缓存集成 fuses
  * q_proj with its LoRA branch; page "Unsloth框架：高效LLM微调与LoRA优化实践",
@@ -260,6 +279,17 @@ int lora_profile_end(void);
 int lora_profile_kinds(void);
 const char* lora_profile_kind_name(int kind);
 int lora_profile_query(int kind, double* total_ms, int* count, double* total_flop, double* total_bytes);
+
+/*
+ * MFMA rate probe (measurement hook, not part of the layer's arithmetic): an
+ * asynchronous launch of `blocks` workgroups of 4 waves (one per SIMD), each
+ * wave running `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
+ * register operands, so the work is blocks * 4 * iters * 8 * 32768 FLOP; the
+ * caller times it on `stream`.  This is the dense bf16 rate the chip sustains
+ * under its own power and clock limits, next to the published peak.  out:
+ * device fp32 [blocks * 256].  LORA_ERR_SHAPE if iters or blocks < 1.
+ */
+int lora_mfma_rate(int iters, int blocks, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     LORA_F32,
     OP_BWD,
     OP_FWD,
+    OP_MERGE,
     OP_NF4_BWD,
     OP_NF4_FWD,
     OP_ROPE_BWD,
@@ -31,6 +32,7 @@ from .functional import (  # noqa: F401
     lora_group_fwd,
     lora_linear_bwd,
     lora_linear_fwd,
+    lora_merge,
     lora_qk_rope_bwd,
     lora_qk_rope_fwd,
     nf4_dequant,

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora_linear.so")
 
 LORA_F32, LORA_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD = range(6)
+OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD, OP_MERGE = range(7)
 
 _lib = None
 
@@ -55,6 +55,8 @@ _SIGS = {
     "lora_group_workspace_bytes": ([_int, _int, _i64, _i64, _int, _mp], _sz),
     "lora_group_fwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
     "lora_group_bwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
+    "lora_merge": ([_int, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "lora_mfma_rate": ([_int, _int, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),
     "lora_profile_end": ([], _int),
     "lora_profile_kinds": ([], _int),
@@ -142,6 +144,19 @@ def profile_begin(max_launches: int = 4096):
 
 def profile_end():
     _check("lora_profile_end", lib().lora_profile_end())
+
+
+def mfma_rate(iters: int = 4096, blocks: int = 1024, device=None) -> float:
+    """Dense bf16 MFMA TFLOP/s the chip sustains right now (lora_mfma_rate)."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=device or "cuda")
+    st = _stream(out.device)
+    _check("lora_mfma_rate", lib().lora_mfma_rate(iters, blocks, _ptr(out), st))  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _check("lora_mfma_rate", lib().lora_mfma_rate(iters, blocks, _ptr(out), st))
+    e1.record()
+    e1.synchronize()
+    return blocks * 4.0 * iters * 8 * 32768 / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def profile_report():

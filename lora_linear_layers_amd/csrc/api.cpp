@@ -54,7 +54,9 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t r8 = 0, M8 = 0;
-  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, total = 0;
+  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, spart = 0, total = 0;
+  int splits_main = 1;  // contraction splits of the Y (forward) or dX (backward) GEMM
+  int64_t ksplit_main = 0;
   bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
   int splits_dA = 1, splits_dB = 1;
   int64_t ksplit_dA = 0, ksplit_dB = 0;
@@ -63,12 +65,13 @@ struct Layout {
 };
 
 // Split of the contraction of a bf16 rank-r panel (256 x 64 tiles): about 1.5
-// workgroups per CU, each split a multiple of 64 and at least 8 stages long.
+// workgroups per CU, at most 32 splits, each a multiple of 64 and at least 8
+// stages long (4 when a few tokens leave fewer than 16 tiles).
 void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit) {
   int64_t tiles = cdiv(M, 256) * cdiv(r8, 64);
   if (tiles < 1) tiles = 1;
   int64_t s = cdiv(384, tiles);
-  int64_t smax = K / 512;
+  int64_t smax = tiles < 16 ? K / 256 : K / 512;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;
   if (s > 32) s = 32;
@@ -95,6 +98,24 @@ void choose_split(int64_t M, int64_t rows, int64_t N, int* splits, int64_t* kspl
   if (*splits < 1) *splits = 1;
 }
 
+// Contraction split of the layer's Y or dX GEMM [M, N] over K when its
+// 128x128 tiles cannot give every CU one (few tokens): about two workgroups
+// per CU, at most 16 splits, each a multiple of 64 and at least 256 long.
+// bf16 only; 1 = no split.
+void main_split(int64_t M, int64_t N, int64_t K, int* splits, int64_t* ksplit) {
+  *splits = 1;
+  *ksplit = K;
+  const int64_t tiles = cdiv(M, 128) * cdiv(N, 128);
+  if (M == 0 || tiles >= 256) return;
+  int64_t s = cdiv(512, tiles);
+  if (s > K / 256) s = K / 256;
+  if (s > 16) s = 16;
+  if (s < 2) return;
+  const int64_t ks = rup(cdiv(K, s), 64);
+  *ksplit = ks;
+  *splits = (int)cdiv(K, ks);
+}
+
 Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
   Layout L;
   const size_t eb = elem_bytes(dtype);
@@ -106,6 +127,11 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     off = align256(off + bytes);
     return at;
   };
+  if (op == LORA_OP_MERGE) {
+    if (r % 8) L.bpad = take(size_t(d_out) * L.r8 * eb);
+    L.total = off;
+    return L;
+  }
   const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD;
   if ((op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD) && M >= LORA_NF4_DEQUANT_MIN_TOKENS) {
     L.dequant = true;
@@ -121,8 +147,16 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     }
     L.ppart = take(size_t(sp) * L.M8 * L.r8 * 4);
   }
+  if (eb == 2) {
+    if (bwd)
+      main_split(M, d_in, d_out, &L.splits_main, &L.ksplit_main);
+    else
+      main_split(M, d_out, d_in, &L.splits_main, &L.ksplit_main);
+  }
+  const size_t sp = L.splits_main > 1 ? size_t(L.splits_main) * M * (bwd ? d_in : d_out) * 4 : 0;
   if (!bwd) {
     L.p = take(size_t(M) * L.r8 * eb);
+    if (sp) L.spart = take(sp);
   } else {
     if (op == LORA_OP_ROPE_BWD) L.g = take(size_t(M) * d_out * eb);
     if (eb == 2) L.bt = take(size_t(L.r8) * d_out * eb);
@@ -133,7 +167,9 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     choose_split(M, L.r8, d_out, &L.splits_dB, &L.ksplit_dB);
     size_t pa = size_t(L.splits_dA) * L.r8 * d_in * 4;
     size_t pb = size_t(L.splits_dB) * L.r8 * d_out * 4;
+    if (sp > pa) pa = sp;  // the dX partials are reduced before dB and dA start
     L.part = take(pa > pb ? pa : pb);
+    L.spart = L.part;
   }
   L.total = off;
   return L;
@@ -188,22 +224,25 @@ enum ProfKind : int {
   K_PANEL,
   K_TRANSPOSE,
   K_COPY_ROWS,
+  K_FINISH,
   K_PROF_COUNT
 };
 
 const char* kind_name(int k) {
-  static const char* names[K_PROF_COUNT] = {
+  static const char* names[] = {
       "gemm_bf16_256x256_nt_store", "gemm_bf16_256x256_nt_rope", "gemm_bf16_128x128_nt_store",
       "gemm_bf16_128x128_nt_rope",  "gemm_bf16_256x256_nn_store", "gemm_bf16_128x128_nn_store",
       "gemm_nf4_256x256_nt_store",  "gemm_nf4_128x128_nt_store",  "gemm_nf4_256x256_nn_store",
-      "gemm_nf4_128x128_nn_store",  "panel_bf16_nt_store",        "panel_bf16_nt_store_t",
-      "panel_bf16_nn_both",         "split_bf16_nn_partial",      "gemm_f32_64x128_nt_store",
+      "gemm_nf4_128x128_nn_store",  "split_bf16_nn_partial",      "gemm_f32_64x128_nt_store",
       "gemm_f32_64x128_nt_rope",    "gemm_f32_64x128_nn_store",   "panel_f32_nt_store",
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
-      "panel_bf16_256x64_split",    "pad_cols",                   "rope_inverse",
+      "panel_bf16_256x64_split",    "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
+      "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
+      "merge_f32_64x128",           "pad_cols",                   "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
-      "copy_rows"};
+      "copy_rows",                  "split_finish"};
+  static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
 
@@ -347,7 +386,23 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     k = f32 ? G_F32_NT_STORE : (big ? G_BF16_BIG_NT_STORE : G_BF16_MED_NT_STORE);
   }
   const double wbytes = nf4 ? ko * ki / 2 + ko * ki / 64 * 4 : ko * ki * e;
-  HIPTRY(gemm(k, a, 1, st, 2 * Md * ko * (ki + rr), (Md * ki + Md * rr + ko * rr + Md * ko) * e + wbytes));
+  const double flop = 2 * Md * ko * (ki + rr), bytes = (Md * ki + Md * rr + ko * rr + Md * ko) * e + wbytes;
+  if (!f32 && L.splits_main > 1) {
+    // few tokens: split partials over d_in (the rank-r segment in the last
+    // split), then the fixed-order sum with the store / RoPE epilogue
+    const int S = L.splits_main;
+    float* part = reinterpret_cast<float*>(w + L.spart);
+    a.k_split = L.ksplit_main; a.c = part; a.ldc = d_out; a.part_stride = M * d_out;
+    HIPTRY(gemm(nf4 ? G_NF4_MED_NT_PARTIAL : G_BF16_MED_NT_PARTIAL, a, S, st, flop,
+                bytes - Md * ko * e + 4.0 * S * Md * ko));
+    HIPTRY(timed(K_FINISH, double(S) * Md * ko, 4.0 * S * Md * ko + Md * ko * e, st, [&] {
+      return launch_split_finish(part, S, M * d_out, M, d_out, static_cast<uint16_t*>(Y), d_out,
+                                 rope ? rope->pos : nullptr, rope ? rope->cosc : nullptr,
+                                 rope ? rope->sinc : nullptr, st);
+    }));
+    return LORA_OK;
+  }
+  HIPTRY(gemm(k, a, 1, st, flop, bytes));
   return LORA_OK;
 }
 
@@ -448,7 +503,22 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
       k = f32 ? G_F32_NN_STORE : (big ? G_BF16_BIG_NN_STORE : G_BF16_MED_NN_STORE);
     }
     const double wbytes = nf4 ? ko * ki / 2 + ko * ki / 64 * 4 : ko * ki * e;
-    HIPTRY(gemm(k, a, 1, st, 2 * Md * ki * (ko + rr), (Md * ko + Md * rr + rr * ki + Md * ki) * e + wbytes));
+    const double flop = 2 * Md * ki * (ko + rr), bytes = (Md * ko + Md * rr + rr * ki + Md * ki) * e + wbytes;
+    if (!f32 && L.splits_main > 1) {
+      // few tokens: split partials over d_out (the rank-r segment in the last
+      // split), then the fixed-order sum
+      const int S = L.splits_main;
+      float* sp = reinterpret_cast<float*>(w + L.spart);
+      a.k_split = L.ksplit_main; a.c = sp; a.ldc = d_in; a.part_stride = M * d_in;
+      HIPTRY(gemm(nf4 ? G_NF4_MED_NN_PARTIAL : G_BF16_MED_NN_PARTIAL, a, S, st, flop,
+                  bytes - Md * ki * e + 4.0 * S * Md * ki));
+      HIPTRY(timed(K_FINISH, double(S) * Md * ki, 4.0 * S * Md * ki + Md * ki * e, st, [&] {
+        return launch_split_finish(sp, S, M * d_in, M, d_in, static_cast<uint16_t*>(dX), d_in, nullptr, nullptr,
+                                   nullptr, st);
+      }));
+    } else {
+      HIPTRY(gemm(k, a, 1, st, flop, bytes));
+    }
   }
   const GemmKind ksplit = f32 ? G_F32_SPLIT_NN_PARTIAL : G_BF16_SPLIT_NN_PARTIAL;
   // dB^T = Pt G  -> partials [splits][r8, d_out] -> dB [d_out, r]
@@ -692,7 +762,7 @@ const char* lora_strerror(int code) {
 }
 
 size_t lora_workspace_bytes(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
-  if (op < LORA_OP_FWD || op > LORA_OP_NF4_BWD) return 0;
+  if (op < LORA_OP_FWD || op > LORA_OP_MERGE) return 0;
   if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
   if (check_sizes(M, d_in, d_out, r) != LORA_OK) return 0;
   return make_layout(op, dtype, M, d_in, d_out, r).total;
@@ -847,6 +917,42 @@ int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   TRY(check_device());
   const Rope rp{positions, cos_cache, sin_cache};
   return group_backward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
+}
+
+int lora_merge(int dtype, int64_t d_out, int64_t d_in, int64_t r, float scale, const void* W, const void* A,
+               const void* B, void* W_out, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(0, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B, W_out}));
+  const Layout L = make_layout(LORA_OP_MERGE, dtype, 0, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int eb = elem_bytes(dtype);
+  const void* Bsrc = B;
+  if (r % 8) {
+    Bsrc = static_cast<char*>(ws) + L.bpad;
+    HIPTRY(timed(K_PAD, 0, 2.0 * d_out * L.r8 * eb, st, [&] {
+      return launch_pad_cols(eb, B, const_cast<void*>(Bsrc), d_out, r, L.r8, st);
+    }));
+  }
+  // W_out [d_out, d_in] = scale * B [d_out, r8] A [r, d_in] + W
+  GemmArgs a = blank();
+  a.a1 = Bsrc; a.lda1 = L.r8; a.b1 = A; a.ldb1 = d_in; a.K1 = r;
+  a.m_load = d_out; a.m_store = d_out; a.n_load = d_in; a.n_store = d_in;
+  a.c = W_out; a.ldc = d_in; a.cin = W; a.ldcin = d_in; a.alpha = scale;
+  const double ko = double(d_out), ki = double(d_in), rr = double(r), e = double(eb);
+  HIPTRY(gemm(dtype == LORA_F32 ? G_F32_NN_ADD : G_BF16_MED_NN_ADD, a, 1, st, 2 * ko * ki * rr,
+              (2 * ko * ki + ko * rr + rr * ki) * e));
+  return LORA_OK;
+}
+
+int lora_mfma_rate(int iters, int blocks, float* out, void* stream) {
+  if (iters < 1 || blocks < 1) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({out}));
+  TRY(check_device());
+  HIPTRY(launch_mfma_rate(iters, blocks, out, static_cast<hipStream_t>(stream)));
+  return LORA_OK;
 }
 
 int lora_profile_begin(int max_launches) {

@@ -54,7 +54,8 @@ enum Epi : int {
   EPI_STORE_T = 1,     // Ct[n, m] = alpha * acc           (type T)
   EPI_STORE_BOTH = 2,  // both of the above
   EPI_ROPE = 3,        // rotate (n, n+64) pairs of 128-wide heads, then store
-  EPI_PARTIAL = 4      // fp32 partial slab of split z: C[z][m, n] = acc
+  EPI_PARTIAL = 4,     // fp32 partial slab of split z: C[z][m, n] = acc
+  EPI_ADD = 5          // C[m, n] = alpha * acc + Cin[m, n]  (type T; C may be Cin)
 };
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
@@ -84,6 +85,8 @@ struct GemmArgs {
   int64_t codes_ld;         // bytes per W row (= d_in / 2)
   int64_t blocks_per_row;   // absmax entries per W row (= d_in / 64)
   float nf4_table[16];
+  const void* cin;          // EPI_ADD: the addend, row stride ldcin
+  int64_t ldcin;
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -96,6 +99,14 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_in(const void* c, int64_t idx) {
+  if constexpr (sizeof(T) == 2)
+    return static_cast<float>(__builtin_bit_cast(__bf16, reinterpret_cast<const uint16_t*>(c)[idx]));
+  else
+    return reinterpret_cast<const float*>(c)[idx];
 }
 
 template <typename T>
@@ -194,7 +205,8 @@ gemm_kernel(const GemmArgs p) {
     kend = kbeg + p.k_split < p.K1 ? kbeg + p.k_split : p.K1;
   }
   const int nk1 = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
-  const int nk2 = (EPI == EPI_PARTIAL) ? 0 : (int)((p.K2 + BK - 1) / BK);
+  // with split partials only the last split runs segment 2
+  const int nk2 = (EPI == EPI_PARTIAL && z + 1 < (int)gridDim.z) ? 0 : (int)((p.K2 + BK - 1) / BK);
   const int nk = nk1 + nk2;
 
   // ---------------- prefetch registers (shared by the two roles) ----------
@@ -630,7 +642,11 @@ gemm_kernel(const GemmArgs p) {
         for (int j = 0; j < FN; ++j) {
           const int64_t col = cbase + j * 16;
           if (col >= p.n_store) continue;
-          const float y = acc[i][j][v] * p.alpha;
+          float y = acc[i][j][v] * p.alpha;
+          if constexpr (EPI == EPI_ADD) {
+            y += load_in<T>(p.cin, row * p.ldcin + col);
+            store_out<T>(p.c, row * p.ldc + col, y);
+          }
           if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_BOTH) store_out<T>(p.c, row * p.ldc + col, y);
           if constexpr (EPI == EPI_STORE_T || EPI == EPI_STORE_BOTH) store_out<T>(p.ct, col * p.ldct + row, y);
         }

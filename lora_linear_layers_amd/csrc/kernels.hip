@@ -9,7 +9,6 @@
 #include "gemm.h"
 #include "gemm_w4.h"
 #include "launch.h"
-#include "panel.h"
 
 namespace lora {
 
@@ -62,10 +61,12 @@ TileShape gemm_tile(GemmKind k) {
     case G_BF16_MED_NN_STORE:
     case G_NF4_MED_NT_STORE:
     case G_NF4_MED_NN_STORE:
+    case G_BF16_MED_NT_PARTIAL:
+    case G_BF16_MED_NN_PARTIAL:
+    case G_NF4_MED_NT_PARTIAL:
+    case G_NF4_MED_NN_PARTIAL:
+    case G_BF16_MED_NN_ADD:
       return {128, 128};
-    case G_BF16_PANEL_NT_STORE:
-    case G_BF16_PANEL_NT_STORE_T:
-    case G_BF16_PANEL_NN_BOTH:
     case G_F32_PANEL_NT_STORE:
     case G_F32_PANEL_NT_STORE_T:
     case G_F32_PANEL_NN_BOTH:
@@ -78,6 +79,7 @@ TileShape gemm_tile(GemmKind k) {
     case G_F32_NT_STORE:
     case G_F32_NT_ROPE:
     case G_F32_NN_STORE:
+    case G_F32_NN_ADD:
       return {64, 128};
     default:
       return {0, 0};
@@ -102,9 +104,6 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_NF4_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_BIG_NN_STORE: return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_NF4>(a, splits, st);
-    case G_BF16_PANEL_NT_STORE: return run<bf, 64, 64, 2, 2, false, EPI_STORE, BL_PLAIN>(a, splits, st);
-    case G_BF16_PANEL_NT_STORE_T: return run<bf, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
-    case G_BF16_PANEL_NN_BOTH: return run<bf, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
     case G_BF16_SPLIT_NN_PARTIAL: return run<bf, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_F32_NT_STORE: return run<float, 64, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_F32_NT_ROPE: return run<float, 64, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
@@ -114,16 +113,14 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_F32_PANEL_NN_BOTH: return run<float, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
     case G_F32_SPLIT_NN_PARTIAL: return run<float, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_PANEL_SPLIT_NT: return run<bf, 256, 64, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NN_PARTIAL: return run<bf, 128, 128, 4, 1, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_NF4_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_NF4>(a, splits, st);
+    case G_NF4_MED_NN_PARTIAL: return run<bf, 128, 128, 4, 1, true, EPI_PARTIAL, BL_NF4>(a, splits, st);
+    case G_BF16_MED_NN_ADD: return run<bf, 128, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
+    case G_F32_NN_ADD: return run<float, 64, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_panel(const PanelArgs& a, hipStream_t st) {
-  const int64_t gx = (a.m_store + panel::ROWS - 1) / panel::ROWS;
-  const int64_t gy = (a.n_store + panel::COLS - 1) / panel::COLS;
-  if (gx <= 0 || gy <= 0) return hipSuccess;
-  hipLaunchKernelGGL(panel_kernel<panel::WAVES>, dim3((unsigned)gx, (unsigned)gy), dim3(64 * panel::WAVES), 0, st, a);
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -279,6 +276,68 @@ hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int
   return hipGetLastError();
 }
 
+// Outputs of a contraction-split GEMM (few tokens): y[m, n] = sum over
+// z < splits of part[z][m, n] in split order, then for q/k projections the
+// RoPE rotation of the pairs (n, n + 64) of each 128-wide head (cos/sin row
+// positions[m]), stored as bf16.  One thread per 4 consecutive columns (with
+// RoPE: 4 columns of a head's first half and their 4 partners).
+template <bool ROPE>
+__global__ void __launch_bounds__(256) split_finish_kernel(const float* __restrict__ part, int splits,
+                                                           int64_t part_stride, int64_t M, int64_t N,
+                                                           uint16_t* __restrict__ out, int64_t ldo,
+                                                           const int32_t* __restrict__ pos,
+                                                           const float* __restrict__ cosc,
+                                                           const float* __restrict__ sinc) {
+  const int64_t per_row = ROPE ? N / 8 : N / 4;
+  const int64_t items = M * per_row;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < items; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = e / per_row, q = e - m * per_row;
+    const int64_t c = ROPE ? (q >> 4) * 128 + (q & 15) * 4 : q * 4;
+    const float* src = part + m * N + c;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+    for (int z = 0; z < splits; ++z) {
+      const float4 v = *reinterpret_cast<const float4*>(src + (int64_t)z * part_stride);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      if constexpr (ROPE) {
+        const float4 u = *reinterpret_cast<const float4*>(src + 64 + (int64_t)z * part_stride);
+        b.x += u.x; b.y += u.y; b.z += u.z; b.w += u.w;
+      }
+    }
+    uint16_t* dst = out + m * ldo + c;
+    if constexpr (ROPE) {
+      const int64_t prow = (int64_t)pos[m] * 64 + (c & 127);
+      const float4 cs = *reinterpret_cast<const float4*>(cosc + prow);
+      const float4 sn = *reinterpret_cast<const float4*>(sinc + prow);
+      const float y1[4] = {a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y, a.z * cs.z - b.z * sn.z,
+                           a.w * cs.w - b.w * sn.w};
+      const float y2[4] = {b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y, b.z * cs.z + a.z * sn.z,
+                           b.w * cs.w + a.w * sn.w};
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      *reinterpret_cast<uint2*>(dst + 64) = make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+    } else {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+    }
+  }
+}
+
+hipError_t launch_split_finish(const float* part, int splits, int64_t part_stride, int64_t M, int64_t N,
+                               uint16_t* out, int64_t ldo, const int32_t* pos, const float* cosc, const float* sinc,
+                               hipStream_t st) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1 || splits > kMaxSplits || N % 8 || ldo % 4 || part_stride % 4) return hipErrorInvalidValue;
+  if (pos) {
+    if (N % 128) return hipErrorInvalidValue;
+    const int64_t items = M * (N / 8);
+    hipLaunchKernelGGL(split_finish_kernel<true>, dim3(grid_for(items, 256)), dim3(256), 0, st, part, splits,
+                       part_stride, M, N, out, ldo, pos, cosc, sinc);
+  } else {
+    const int64_t items = M * (N / 4);
+    hipLaunchKernelGGL(split_finish_kernel<false>, dim3(grid_for(items, 256)), dim3(256), 0, st, part, splits,
+                       part_stride, M, N, out, ldo, pos, cosc, sinc);
+  }
+  return hipGetLastError();
+}
+
 constexpr int kMaxPanelSplits = 32;
 
 // One 16-row x 64-column tile of the panel per workgroup: fixed-order sum of
@@ -397,6 +456,54 @@ hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t
   const int64_t nchunks = n / 32;
   hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(nchunks, 256)), dim3(256), 0, st, codes, absmax, nchunks, t,
                      reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+// Dense bf16 MFMA rate of this chip under its own power and clock limits:
+// each wave runs `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16 on
+// register operands (pseudo-random bf16 values in [-2, 2), four operand
+// pairs in turn so the inputs keep changing), one wave per SIMD.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mfma_rate_kernel(int iters, float* __restrict__ out) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  bf16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t h = (t * 0x9E3779B9u) ^ ((uint32_t)(i * 4 + e) * 0x85EBCA6Bu);
+      h ^= h >> 15;
+      h *= 0x2C1B3C6Du;
+      h ^= h >> 12;
+      // two bf16: random sign, exponent 126 or 127, random mantissa
+      const uint32_t lo = ((h & 1u) << 15) | ((126u + ((h >> 1) & 1u)) << 7) | ((h >> 2) & 0x7Fu);
+      const uint32_t hi = (((h >> 9) & 1u) << 15) | ((126u + ((h >> 10) & 1u)) << 7) | ((h >> 11) & 0x7Fu);
+      w[e] = lo | (hi << 16);
+    }
+    if (i < 4)
+      a[i] = __builtin_bit_cast(bf16x8, w);
+    else
+      b[i - 4] = __builtin_bit_cast(bf16x8, w);
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j & 3], b[(j >> 1) & 3], acc[j], 0, 0, 0);
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += acc[j][0] + acc[j][15];
+  out[t] = sum;
+}
+
+hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, iters, out);
   return hipGetLastError();
 }
 

@@ -6,14 +6,16 @@
 #include <stdint.h>
 
 #include "gemm.h"
-#include "panel.h"
 
 namespace lora {
 
 // GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
 // epilogue.  "BIG" = 256x256 tiles, "MED" = 128x128 (4 waves), "PANEL" =
 // 64x64 rank-r panels, "SPLIT" = 64x256 split-contraction partials,
-// "PANEL_SPLIT" = 256x64 split-contraction partials of a rank-r panel.
+// "PANEL_SPLIT" = 256x64 split-contraction partials of a rank-r panel,
+// "MED_*_PARTIAL" = 128x128 split-contraction partials of the layer's own
+// GEMMs when their tiles alone cannot fill the chip (few tokens), "ADD" =
+// the product plus an addend (the merge of the adapter into W).
 enum GemmKind : int {
   G_BF16_BIG_NT_STORE,
   G_BF16_BIG_NT_ROPE,
@@ -25,9 +27,6 @@ enum GemmKind : int {
   G_NF4_MED_NT_STORE,
   G_NF4_BIG_NN_STORE,
   G_NF4_MED_NN_STORE,
-  G_BF16_PANEL_NT_STORE,
-  G_BF16_PANEL_NT_STORE_T,
-  G_BF16_PANEL_NN_BOTH,
   G_BF16_SPLIT_NN_PARTIAL,
   G_F32_NT_STORE,
   G_F32_NT_ROPE,
@@ -37,6 +36,12 @@ enum GemmKind : int {
   G_F32_PANEL_NN_BOTH,
   G_F32_SPLIT_NN_PARTIAL,
   G_BF16_PANEL_SPLIT_NT,
+  G_BF16_MED_NT_PARTIAL,
+  G_BF16_MED_NN_PARTIAL,
+  G_NF4_MED_NT_PARTIAL,
+  G_NF4_MED_NN_PARTIAL,
+  G_BF16_MED_NN_ADD,
+  G_F32_NN_ADD,
   G_KIND_COUNT
 };
 
@@ -47,9 +52,6 @@ TileShape gemm_tile(GemmKind k);
 
 // Sets a.tiles_m from a.m_store and launches over (tiles_m * tiles_n, 1, splits).
 hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st);
-
-// Rank-r panel out = alpha X R^T (bf16), see panel.h.
-hipError_t launch_panel(const PanelArgs& a, hipStream_t st);
 
 // Bt[q, i] = q < r ? B[i, q] : 0, bf16 [rows, r] -> [r_pad, rows].
 hipError_t launch_transpose_pad(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t r, int64_t r_pad,
@@ -100,7 +102,18 @@ hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_strid
 hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, int64_t rows, int64_t cols, uint16_t* dst,
                             int64_t ldd, int64_t rows_pad, hipStream_t st);
 
+// out [M, N] bf16 (row stride ldo) = fixed-order sum of split partials
+// (part[z * part_stride + m * N + n]); with pos != NULL also the RoPE rotation
+// of the pairs (n, n + 64) of each 128-wide head (N a multiple of 128).
+hipError_t launch_split_finish(const float* part, int splits, int64_t part_stride, int64_t M, int64_t N,
+                               uint16_t* out, int64_t ldo, const int32_t* pos, const float* cosc, const float* sinc,
+                               hipStream_t st);
+
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// blocks x 256 threads of the MFMA-rate kernel (iters rounds of 8 MFMAs per
+// wave); out [blocks * 256] receives one float per thread.
+hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st);
 
 hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n,
                               const float* table16, uint16_t* out, hipStream_t st);

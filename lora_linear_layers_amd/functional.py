@@ -143,6 +143,22 @@ def nf4_dequant(codes, absmax, table16, n: int, blocksize: int = 64):
     return out
 
 
+def lora_merge(W, A, B, scale: float, out=None, ws=None):
+    """W + scale B A in W's dtype (out may be W itself); -scale unmerges."""
+    L._contig(W, A, B, out)
+    d_out, d_in = W.shape
+    r = A.shape[0]
+    if A.shape != (r, d_in) or B.shape != (d_out, r):
+        raise ValueError("shape mismatch: W [d_out,d_in], A [r,d_in], B [d_out,r]")
+    dt = L._dtype_code(W)
+    if out is None:
+        out = torch.empty_like(W)
+    ws = L._workspace(L.OP_MERGE, dt, 0, d_in, d_out, r, W.device, ws)
+    L._check("lora_merge", L.lib().lora_merge(dt, d_out, d_in, r, float(scale), L._ptr(W), L._ptr(A), L._ptr(B),
+                                              L._ptr(out), L._ptr(ws), ws.numel(), L._stream(W.device)))
+    return out
+
+
 def _group_members(X, members):
     """ctypes array of lora_group_member from dicts with keys A, B, scale and
     either W or (codes, absmax), plus an optional rope flag."""

@@ -195,3 +195,28 @@ def test_group_validation(lib):
     assert _gbwd(lib, _members(2, dY=None)) == ENULL
     assert _gbwd(lib, _members(2, dX=P + 8)) == EALIGN
     assert _gbwd(lib, _members(2), wsb=100) == EWS
+
+
+def test_mfma_rate_validation(lib):
+    assert lib.lora_mfma_rate(0, 4, P, None) == ESHAPE
+    assert lib.lora_mfma_rate(4, 0, P, None) == ESHAPE
+    assert lib.lora_mfma_rate(4, 4, None, None) == ENULL
+    assert lib.lora_mfma_rate(4, 4, P + 4, None) == EALIGN
+
+
+def test_merge_validation(lib):
+    def call(dtype=1, d_out=64, d_in=64, r=8, W=P, A=P, B=P, out=P, ws=P, wsb=1 << 20):
+        return lib.lora_merge(dtype, d_out, d_in, r, 1.0, W, A, B, out, ws, wsb, None)
+    assert call(dtype=2) == EDTYPE
+    assert call(d_in=12) == ESHAPE
+    assert call(r=0) == ESHAPE
+    assert call(r=300) == ESHAPE
+    assert call(W=None) == ENULL
+    assert call(out=None) == ENULL
+    assert call(A=P + 8) == EALIGN
+    assert call(r=3, wsb=10) == EWS
+    assert call(r=3, ws=None) == EWS
+    f = lib.lora_workspace_bytes
+    assert f(_lib.OP_MERGE, 1, 0, 64, 64, 8) == 0
+    assert f(_lib.OP_MERGE, 1, 0, 64, 96, 3) == 96 * 8 * 2
+    assert f(_lib.OP_MERGE, 0, 0, 64, 96, 3) == 96 * 8 * 4
