@@ -22,5 +22,9 @@ from .lora_oracle import (  # noqa: F401
     nf4_lora_forward,
     nf4_lora_backward,
     merged_weight,
+    silu,
+    swiglu_forward,
+    swiglu_grad,
+    swiglu_backward,
     rel_err,
 )

@@ -20,10 +20,13 @@ section or equation on it:
   [P3] "Unsloth教程：本地微调大模型速度提升数倍，显存节省60%", section
        显存优化策略, 4-bit QLoRA paragraph: base weight in NormalFloat4, only
        the LoRA adapters train (no dW).
+  [P4] "Unsloth框架：高效LLM微调与LoRA优化实践", section 3.1: the graph
+       rewriter merges adjacent linear layers with their activation function.
   [P5] "Unsloth自动化优化：无需手动调参的实现原理", section 3.2: the fused
        kernel is equivalent to A@B added to the original weight; section 5:
        NF4 is the default 4-bit format, and fusion changes the order of the
-       gradient arithmetic, so results are equal up to rounding only.
+       gradient arithmetic, so results are equal up to rounding only;
+       section 1: the layer types it recognises include SwiGLU.
 
 Readings where the pages are silent or garbled (each also listed in the design
 notes):
@@ -34,7 +37,10 @@ notes):
   * RoPE pairs element i with i + D/2 inside each head of width D
     ("rotate-half"), angle pos * theta^(-2i/D), theta = 5e5;
   * NF4: blocks of 64 consecutive elements of row-major W [d_out, d_in];
-    element 2j in the high nibble of byte j; value = bf16(f32(table[c] * absmax)).
+    element 2j in the high nibble of byte j; value = bf16(f32(table[c] * absmax));
+  * SwiGLU (named, not defined, on the pages): the Llama MLP's gated unit
+    h = silu(g) * u elementwise, g and u the gate and up projections of the
+    same x, silu(z) = z / (1 + e^-z).
 
 Layout: row-major, one token per row.  X [M, d_in], W [d_out, d_in],
 A [r, d_in], B [d_out, r], Y and dY [M, d_out].
@@ -212,6 +218,43 @@ def nf4_encode(W, table, blocksize: int = 64):
     codes = codes.reshape(n)
     packed = ((codes[0::2] << 4) | codes[1::2]).astype(np.uint8)
     return packed, am.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU on the gate / up pair ([P4] 3.1, [P5] section 1)
+# ---------------------------------------------------------------------------
+
+def silu(z) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_forward(X, Wg, Ag, Bg, sg, Wu, Au, Bu, su):
+    """(H, G, U): G and U the two LoRA projections of X, H = silu(G) * U."""
+    G = lora_forward(X, Wg, Ag, Bg, sg)
+    U = lora_forward(X, Wu, Au, Bu, su)
+    return silu(G) * U, G, U
+
+
+def swiglu_grad(dH, G, U):
+    """(dG, dU) of H = silu(G) * U: dU = dH silu(G), dG = dH U silu'(G) with
+    silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))."""
+    dH, G, U = map(_f64, (dH, G, U))
+    sg = 1.0 / (1.0 + np.exp(-G))
+    return dH * U * sg * (1.0 + G * (1.0 - sg)), dH * G * sg
+
+
+def swiglu_backward(X, Wg, Ag, Bg, sg, Wu, Au, Bu, su, dH, G=None, U=None):
+    """(dX, dAg, dBg, dAu, dBu) of H = silu(G) U: the two LoRA backwards with
+    upstream gradients dG and dU, input gradients summed.  G and U default to
+    the exact forward values."""
+    if G is None or U is None:
+        _, G, U = swiglu_forward(X, Wg, Ag, Bg, sg, Wu, Au, Bu, su)
+    dG, dU = swiglu_grad(dH, G, U)
+    dXg, dAg, dBg = lora_backward(X, Wg, Ag, Bg, sg, dG)
+    dXu, dAu, dBu = lora_backward(X, Wu, Au, Bu, su, dU)
+    return dXg + dXu, dAg, dBg, dAu, dBu
 
 
 def nf4_lora_forward(X, codes, absmax, table, A, B, s, d_out, d_in, blocksize=64):

@@ -333,3 +333,80 @@ def test_nf4_encode_zero_block_and_ties():
 def test_rel_err():
     assert O.rel_err(np.array([1.0, 2.0]), np.array([1.0, 4.0])) == 0.5
     assert O.rel_err(np.zeros(3), np.zeros(3)) == 0.0
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU on the gate / up pair
+# ---------------------------------------------------------------------------
+
+def test_silu_closed_forms():
+    e = math.e
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert abs(O.silu(np.array([1.0]))[0] - e / (1 + e)) < 1e-16
+    assert abs(O.silu(np.array([-1.0]))[0] + 1 / (1 + e)) < 1e-16
+    # large |z|: silu(z) -> z, silu(-z) -> -z e^-z
+    assert O.silu(np.array([40.0]))[0] == 40.0
+    assert abs(O.silu(np.array([-40.0]))[0] / (-40.0 * math.exp(-40.0)) - 1) < 1e-12
+    # the minimum: silu'(z*) = 0 means sigmoid(z*) = 1 + 1/z*, so silu(z*) = z* + 1;
+    # z* = -1 - W0(1/e) with the principal Lambert W value W0(1/e) = 0.2784645427610738
+    z = -1.2784645427610738
+    assert abs(O.silu(np.array([z]))[0] - (z + 1)) < 1e-15
+    dG, _ = O.swiglu_grad(np.array([1.0]), np.array([z]), np.array([1.0]))
+    assert abs(dG[0]) < 1e-15
+
+
+def test_swiglu_hand_worked_1x1():
+    # x = 2, gate: w = 1, a = 1, b = 0.5, s = 2 -> g = 2 + 2 * 0.5 * 2 = 4;
+    # up: w = -1, a = b = 0 -> u = -2; h = silu(4) u = -2 * 4 / (1 + e^-4)
+    X = np.array([[2.0]])
+    H, G, U = O.swiglu_forward(X, [[1.0]], [[1.0]], [[0.5]], 2.0, [[-1.0]], [[0.0]], [[0.0]], 1.0)
+    assert G[0, 0] == 4.0 and U[0, 0] == -2.0
+    assert abs(H[0, 0] - (-8.0 / (1.0 + math.exp(-4.0)))) < 1e-15
+
+
+def test_swiglu_grad_matches_finite_differences():
+    G, U, dH = _rand(4, 6) * 3, _rand(4, 6), _rand(4, 6)
+    dG, dU = O.swiglu_grad(dH, G, U)
+    h = 1e-6
+    # elementwise: perturb one entry at a time
+    num_g = np.zeros_like(G)
+    num_u = np.zeros_like(U)
+    for idx in np.ndindex(G.shape):
+        Gp, Gm = G.copy(), G.copy()
+        Gp[idx] += h
+        Gm[idx] -= h
+        num_g[idx] = (np.sum(dH * O.silu(Gp) * U) - np.sum(dH * O.silu(Gm) * U)) / (2 * h)
+        Up, Um = U.copy(), U.copy()
+        Up[idx] += h
+        Um[idx] -= h
+        num_u[idx] = (np.sum(dH * O.silu(G) * Up) - np.sum(dH * O.silu(G) * Um)) / (2 * h)
+    assert np.abs(num_g - dG).max() < 1e-8
+    assert np.abs(num_u - dU).max() < 1e-8
+
+
+def test_swiglu_backward_matches_finite_differences():
+    M, k, d, rg, ru = 3, 5, 4, 2, 3
+    X = _rand(M, k)
+    Wg, Ag, Bg = _rand(d, k), _rand(rg, k), _rand(d, rg)
+    Wu, Au, Bu = _rand(d, k), _rand(ru, k), _rand(d, ru)
+    sg, su = 2.0, 0.5
+    dH = _rand(M, d)
+    dX, dAg, dBg, dAu, dBu = O.swiglu_backward(X, Wg, Ag, Bg, sg, Wu, Au, Bu, su, dH)
+
+    def f():
+        H, _, _ = O.swiglu_forward(X, Wg, Ag, Bg, sg, Wu, Au, Bu, su)
+        return float(np.sum(dH * H))
+    # the loss is smooth but not linear: central differences, O(h^2) error
+    for P, g in ((X, dX), (Ag, dAg), (Bg, dBg), (Au, dAu), (Bu, dBu)):
+        assert np.abs(_fd(f, P, h=1e-5) - g).max() < 1e-6 * max(1.0, np.abs(g).max())
+
+
+def test_swiglu_zero_up_adapter_has_zero_gradients():
+    # Au = Bu = 0: dAu = su (dU Bu)^T X and dBu = su dU^T (X Au^T) vanish
+    # whatever dU is, while the gate adapter still receives a gradient
+    M, k, d = 2, 3, 4
+    X, Wg, Ag, Bg, Wu = _rand(M, k), _rand(d, k), _rand(1, k), _rand(d, 1), _rand(d, k)
+    Z = np.zeros
+    dX, dAg, dBg, dAu, dBu = O.swiglu_backward(X, Wg, Ag, Bg, 1.0, Wu, Z((1, k)), Z((d, 1)), 1.0, _rand(M, d))
+    assert np.all(dAu == 0.0) and np.all(dBu == 0.0)
+    assert np.abs(dAg).max() > 0 and np.abs(dBg).max() > 0
