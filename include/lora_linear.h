@@ -263,6 +263,45 @@ int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
                    size_t ws_bytes, void* stream);
 
 /*
+ * SwiGLU on a gate / up pair that reads the same X (the gated unit of the
+ * Llama MLP): G and U are the two fused LoRA projections of X (each as
+ * lora_linear_fwd or nf4_lora_linear_fwd), H = silu(G) * U elementwise,
+ * silu(z) = z / (1 + e^-z).  Page "Unsloth框架：高效LLM微调与LoRA优化实践",
+ * section 3.1: the graph rewriter merges adjacent linear layers with their
+ * activation function; page "Unsloth自动化优化：无需手动调参的实现原理",
+ * section 1: SwiGLU is one of the module types it optimises.
+ * members[0] is the gate and members[1] the up projection (lora_group_member
+ * with equal d_out, rope = 0, W or W_nf4 as in the group calls); their rank-r
+ * panels run in one pass over X as in lora_group_fwd.  With bf16, M a multiple
+ * of 256, d_out of 128, d_in of 64 (and for an NF4 member M >= 512, where its
+ * weight is dequantised once), gate and up run as ONE GEMM whose epilogue
+ * forms H from the fp32 accumulators; other shapes form G and U with the group
+ * path and H in an elementwise pass from G and U rounded to the dtype.
+ * H: [M, d_out] in the dtype.  members[g].Y, when not NULL, receives G (g = 0)
+ * and U (g = 1) in the dtype, as the backward needs them.
+ */
+int lora_swiglu_fwd(int dtype, int64_t M, int64_t d_in, const lora_group_member* members, const void* X,
+                    const float* table16, void* H, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of lora_swiglu_fwd for the upstream gradient dH [M, d_out]:
+ * dG = dH * U * silu'(G) and dU = dH * silu(G) (G, U as the forward stored
+ * them; silu'(z) = s (1 + z (1 - s)), s = 1 / (1 + e^-z)), then the LoRA
+ * backward of both projections with their panels shared as in lora_group_bwd.
+ * dX [M, d_in] (NULL: skipped) receives the SUM of the two input gradients;
+ * members[g].dA and .dB receive each adapter's gradients (fp32, overwritten);
+ * members[g].dY, .dX and .Y are not used.
+ */
+int lora_swiglu_bwd(int dtype, int64_t M, int64_t d_in, const lora_group_member* members, const void* X,
+                    const float* table16, const void* dH, const void* G, const void* U, void* dX, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Workspace bytes of lora_swiglu_fwd (backward = 0) or lora_swiglu_bwd (1); 0
+ * for invalid arguments. */
+size_t lora_swiglu_workspace_bytes(int backward, int dtype, int64_t M, int64_t d_in,
+                                   const lora_group_member* members);
+
+/*
  * Launch profiling (measurement hook, not part of the layer's arithmetic).
  * Between lora_profile_begin and lora_profile_end every kernel the library
  * launches is bracketed by two HIP events on its stream, and the launch's

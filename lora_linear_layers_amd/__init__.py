@@ -35,6 +35,8 @@ from .functional import (  # noqa: F401
     lora_merge,
     lora_qk_rope_bwd,
     lora_qk_rope_fwd,
+    lora_swiglu_bwd,
+    lora_swiglu_fwd,
     nf4_dequant,
     nf4_lora_linear_bwd,
     nf4_lora_linear_fwd,

@@ -55,6 +55,9 @@ _SIGS = {
     "lora_group_workspace_bytes": ([_int, _int, _i64, _i64, _int, _mp], _sz),
     "lora_group_fwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
     "lora_group_bwd": ([_int, _i64, _i64, _int, _mp, _vp, _int, _vp, _vp, _vp, _i64, _fp, _vp, _sz, _vp], _int),
+    "lora_swiglu_fwd": ([_int, _i64, _i64, _mp, _vp, _fp, _vp, _vp, _sz, _vp], _int),
+    "lora_swiglu_bwd": ([_int, _i64, _i64, _mp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "lora_swiglu_workspace_bytes": ([_int, _int, _i64, _i64, _mp], _sz),
     "lora_merge": ([_int, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "lora_mfma_rate": ([_int, _int, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),

@@ -225,6 +225,7 @@ enum ProfKind : int {
   K_TRANSPOSE,
   K_COPY_ROWS,
   K_FINISH,
+  K_SWIGLU,
   K_PROF_COUNT
 };
 
@@ -238,10 +239,10 @@ const char* kind_name(int k) {
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
       "panel_bf16_256x64_split",    "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
       "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
-      "merge_f32_64x128",           "pad_cols",                   "rope_inverse",
+      "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "pad_cols",                   "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
-      "copy_rows",                  "split_finish"};
+      "copy_rows",                  "split_finish",               "swiglu_elementwise"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -739,6 +740,160 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   return LORA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// SwiGLU on a gate / up pair
+// ---------------------------------------------------------------------------
+// Workspace: the pair's group layout first (Acat, panels, shared scratch),
+// then forward: the dequantised NF4 weights and padded B's of the fused GEMM,
+// or G and U for the elementwise path; backward: dG, dU and the up's input
+// gradient before it is added to dX.
+struct SwigluLayout {
+  GroupLayout G;
+  bool fused = false;
+  size_t wg = 0, wu = 0, bg = 0, bu = 0, gbuf = 0, ubuf = 0, dg = 0, du = 0, dxu = 0, total = 0;
+};
+
+bool swiglu_fusable(int dtype, int64_t M, int64_t d_in, const lora_group_member* mb) {
+  const bool nf4 = mb[0].W_nf4 || mb[1].W_nf4;
+  return dtype == LORA_BF16 && M > 0 && M % 256 == 0 && mb[0].d_out % 128 == 0 && d_in % 64 == 0 &&
+         (!nf4 || M >= LORA_NF4_DEQUANT_MIN_TOKENS) && d_in * 2 * (256 + 64) < (int64_t(1) << 30);
+}
+
+SwigluLayout make_swiglu_layout(bool bwd, int dtype, int64_t M, int64_t d_in, const lora_group_member* mb) {
+  SwigluLayout S;
+  S.G = make_group_layout(bwd, dtype, M, d_in, 2, mb);
+  const size_t eb = elem_bytes(dtype);
+  const int64_t d = mb[0].d_out;
+  size_t off = S.G.total;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  if (!bwd) {
+    S.fused = swiglu_fusable(dtype, M, d_in, mb);
+    if (S.fused) {
+      if (mb[0].W_nf4) S.wg = take(size_t(d) * d_in * 2);
+      if (mb[1].W_nf4) S.wu = take(size_t(d) * d_in * 2);
+      if (mb[0].r % 8) S.bg = take(size_t(d) * rup(mb[0].r, 8) * 2);
+      if (mb[1].r % 8) S.bu = take(size_t(d) * rup(mb[1].r, 8) * 2);
+    } else {
+      S.gbuf = take(size_t(M) * d * eb);
+      S.ubuf = take(size_t(M) * d * eb);
+    }
+  } else {
+    S.dg = take(size_t(M) * d * eb);
+    S.du = take(size_t(M) * d * eb);
+    S.dxu = take(size_t(M) * d_in * eb);
+  }
+  S.total = off;
+  return S;
+}
+
+int check_swiglu(bool bwd, int dtype, int64_t M, int64_t d_in, const lora_group_member* mb, const void* X,
+                 const float* table16) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  if (!mb) return LORA_ERR_NULL;
+  if (M > 0) TRY(check_ptrs({X}));
+  for (int g = 0; g < 2; ++g) {
+    const lora_group_member& m = mb[g];
+    TRY(check_sizes(M, d_in, m.d_out, m.r));
+    if (m.rope || m.d_out != mb[0].d_out) return LORA_ERR_SHAPE;
+    TRY(check_ptrs({m.A, m.B}));
+    if (m.W_nf4) {
+      if (dtype != LORA_BF16) return LORA_ERR_DTYPE;
+      TRY(check_nf4(d_in, 64, m.W_nf4, m.absmax, table16));
+    } else {
+      TRY(check_ptrs({m.W}));
+    }
+    if (bwd) TRY(check_ptrs({m.dA, m.dB}));
+    if (!bwd && m.Y && !aligned16(m.Y)) return LORA_ERR_ALIGN;
+  }
+  return LORA_OK;
+}
+
+int check_ws_bytes(size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return LORA_OK;
+  if (!ws || ws_bytes < need) return LORA_ERR_WORKSPACE;
+  if (!aligned16(ws)) return LORA_ERR_ALIGN;
+  return LORA_OK;
+}
+
+int swiglu_forward(int dtype, int64_t M, int64_t d_in, const lora_group_member* mb, const void* X,
+                   const float* table16, void* H, void* ws, const SwigluLayout& S, hipStream_t st) {
+  if (M == 0) return LORA_OK;
+  char* w = static_cast<char*>(ws);
+  const int64_t d = mb[0].d_out;
+  const int eb = elem_bytes(dtype);
+  if (!S.fused) {
+    lora_group_member m[2] = {mb[0], mb[1]};
+    m[0].Y = mb[0].Y ? mb[0].Y : w + S.gbuf;
+    m[1].Y = mb[1].Y ? mb[1].Y : w + S.ubuf;
+    TRY(group_forward(dtype, M, d_in, 2, m, X, nullptr, table16, ws, S.G, st));
+    HIPTRY(timed(K_SWIGLU, 4.0 * M * d, 3.0 * M * d * eb, st,
+                 [&] { return launch_swiglu_apply(eb, m[0].Y, m[1].Y, H, M * d, st); }));
+    return LORA_OK;
+  }
+  const GroupLayout& G = S.G;
+  // the pair's rank-r panels in one pass over X: P = [sg X Ag^T | su X Au^T]
+  ColScale cs{};
+  TRY(group_acat(d_in, 2, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+  uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
+  TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
+                 reinterpret_cast<float*>(w + G.shared), P, G.rt, nullptr, 0, st));
+  const void* Wp[2];
+  const void* Bp[2];
+  const size_t woff[2] = {S.wg, S.wu}, boff[2] = {S.bg, S.bu};
+  for (int g = 0; g < 2; ++g) {
+    Wp[g] = mb[g].W;
+    if (mb[g].W_nf4) {
+      TRY(dequant_w(Nf4W{mb[g].W_nf4, mb[g].absmax, table16}, d * d_in, w + woff[g], st));
+      Wp[g] = w + woff[g];
+    }
+    Bp[g] = mb[g].B;
+    if (mb[g].r % 8) {
+      const int64_t r8 = rup(mb[g].r, 8);
+      HIPTRY(timed(K_PAD, 0, 2.0 * d * r8 * 2, st,
+                   [&] { return launch_pad_cols(2, mb[g].B, w + boff[g], d, mb[g].r, r8, st); }));
+      Bp[g] = w + boff[g];
+    }
+  }
+  // gate and up as one GEMM over [X | P]: rows of Wg and Wu interleaved in
+  // 32-row blocks, epilogue H = silu(g) u (and G, U when asked for)
+  GemmArgs a = blank();
+  a.a1 = X; a.lda1 = d_in; a.b1 = Wp[0]; a.b1u = Wp[1]; a.ldb1 = d_in; a.K1 = d_in;
+  a.a2 = P; a.lda2 = G.rt; a.b2 = Bp[0]; a.ldb2 = rup(mb[0].r, 8); a.b2u = Bp[1]; a.ldb2u = rup(mb[1].r, 8);
+  a.K2 = G.rt; a.k2_split = rup(mb[0].r, 8);
+  a.m_load = M; a.m_store = M; a.n_load = 2 * d; a.n_store = 2 * d;
+  a.c = H; a.ldc = d; a.cg = mb[0].Y; a.cu = mb[1].Y;
+  const double Md = double(M), ki = double(d_in), ko = double(d), rt = double(mb[0].r + mb[1].r);
+  const double outs = 1.0 + (mb[0].Y ? 1 : 0) + (mb[1].Y ? 1 : 0);
+  HIPTRY(gemm(G_BF16_WHOLE_SWIGLU, a, 1, st, 2 * Md * ko * (2 * ki) + 2 * Md * ko * rt,
+              (Md * ki + Md * rt + 2 * ko * ki + ko * rt) * 2 + outs * Md * ko * 2));
+  return LORA_OK;
+}
+
+int swiglu_backward(int dtype, int64_t M, int64_t d_in, const lora_group_member* mb, const void* X,
+                    const float* table16, const void* dH, const void* Gs, const void* Us, void* dX, void* ws,
+                    const SwigluLayout& S, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const int64_t d = mb[0].d_out;
+  const int eb = elem_bytes(dtype);
+  lora_group_member m[2] = {mb[0], mb[1]};
+  if (M > 0)
+    HIPTRY(timed(K_SWIGLU, 10.0 * M * d, 5.0 * M * d * eb, st,
+                 [&] { return launch_swiglu_grad(eb, dH, Gs, Us, w + S.dg, w + S.du, M * d, st); }));
+  m[0].dY = w + S.dg;
+  m[1].dY = w + S.du;
+  m[0].dX = dX;
+  m[1].dX = dX ? w + S.dxu : nullptr;
+  TRY(group_backward(dtype, M, d_in, 2, m, X, nullptr, table16, ws, S.G, st));
+  if (dX && M > 0)
+    HIPTRY(timed(K_SWIGLU, 1.0 * M * d_in, 3.0 * M * d_in * eb, st,
+                 [&] { return launch_add_into(eb, dX, w + S.dxu, M * d_in, st); }));
+  return LORA_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -945,6 +1100,39 @@ int lora_merge(int dtype, int64_t d_out, int64_t d_in, int64_t r, float scale, c
   HIPTRY(gemm(dtype == LORA_F32 ? G_F32_NN_ADD : G_BF16_MED_NN_ADD, a, 1, st, 2 * ko * ki * rr,
               (2 * ko * ki + ko * rr + rr * ki) * e));
   return LORA_OK;
+}
+
+size_t lora_swiglu_workspace_bytes(int backward, int dtype, int64_t M, int64_t d_in,
+                                   const lora_group_member* members) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
+  if (!members) return 0;
+  for (int g = 0; g < 2; ++g)
+    if (check_sizes(M, d_in, members[g].d_out, members[g].r) != LORA_OK || members[g].d_out != members[0].d_out)
+      return 0;
+  return make_swiglu_layout(backward != 0, dtype, M, d_in, members).total;
+}
+
+int lora_swiglu_fwd(int dtype, int64_t M, int64_t d_in, const lora_group_member* members, const void* X,
+                    const float* table16, void* H, void* ws, size_t ws_bytes, void* stream) {
+  TRY(check_swiglu(false, dtype, M, d_in, members, X, table16));
+  if (M > 0) TRY(check_ptrs({H}));
+  const SwigluLayout S = make_swiglu_layout(false, dtype, M, d_in, members);
+  TRY(check_ws_bytes(S.total, ws, ws_bytes));
+  TRY(check_device());
+  return swiglu_forward(dtype, M, d_in, members, X, table16, H, ws, S, static_cast<hipStream_t>(stream));
+}
+
+int lora_swiglu_bwd(int dtype, int64_t M, int64_t d_in, const lora_group_member* members, const void* X,
+                    const float* table16, const void* dH, const void* G, const void* U, void* dX, void* ws,
+                    size_t ws_bytes, void* stream) {
+  TRY(check_swiglu(true, dtype, M, d_in, members, X, table16));
+  if (M > 0) TRY(check_ptrs({dH, G, U}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  const SwigluLayout S = make_swiglu_layout(true, dtype, M, d_in, members);
+  TRY(check_ws_bytes(S.total, ws, ws_bytes));
+  TRY(check_device());
+  return swiglu_backward(dtype, M, d_in, members, X, table16, dH, G, U, dX, ws, S,
+                         static_cast<hipStream_t>(stream));
 }
 
 int lora_mfma_rate(int iters, int blocks, float* out, void* stream) {

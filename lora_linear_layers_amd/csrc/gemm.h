@@ -55,7 +55,8 @@ enum Epi : int {
   EPI_STORE_BOTH = 2,  // both of the above
   EPI_ROPE = 3,        // rotate (n, n+64) pairs of 128-wide heads, then store
   EPI_PARTIAL = 4,     // fp32 partial slab of split z: C[z][m, n] = acc
-  EPI_ADD = 5          // C[m, n] = alpha * acc + Cin[m, n]  (type T; C may be Cin)
+  EPI_ADD = 5,         // C[m, n] = alpha * acc + Cin[m, n]  (type T; C may be Cin)
+  EPI_SWIGLU = 6       // whole-tile kernel only: gate/up pair -> silu(g) * u (see gemm_w4.h)
 };
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
@@ -87,6 +88,15 @@ struct GemmArgs {
   float nf4_table[16];
   const void* cin;          // EPI_ADD: the addend, row stride ldcin
   int64_t ldcin;
+  // EPI_SWIGLU: b1 / b2 are the gate's W and padded B, b1u / b2u the up's
+  // (b2u row stride ldb2u); rank columns [0, k2_split) of segment 2 belong to
+  // the gate, [k2_split, K2) to the up; c = silu(g) * u, and g / u are also
+  // stored to cg / cu (row stride ldc) when not NULL
+  const void* b1u;
+  const void* b2u;
+  int64_t ldb2u, k2_split;
+  void* cg;
+  void* cu;
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {

@@ -62,7 +62,13 @@ template <bool B_NN, int EPI, int PF>
 __global__ void __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_w4_kernel(const GemmArgs p) {
   using namespace w4;
-  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE, "store or RoPE epilogue");
+  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_SWIGLU, "store, RoPE or SwiGLU epilogue");
+  static_assert(EPI != EPI_SWIGLU || !B_NN, "SwiGLU pairs rows of two weights");
+  // SwiGLU: B-tile rows 32 i .. 32 i + 31 come from the gate's weight for
+  // even i and from the up's for odd i, rows c0 + 32 (i / 2) + .. of each
+  // (c0 = n0 / 2), so MFMA blocks j = 0, 2 of a wave hold gate outputs and
+  // j = 1, 3 the up outputs of the same columns
+  constexpr bool SW = EPI == EPI_SWIGLU;
   static_assert(PF == 1 || PF == 2, "one or two staged tiles");
   __shared__ __attribute__((aligned(16))) char smem[LDS];
   // keep the MFMA accumulators in the accumulation registers
@@ -93,8 +99,11 @@ gemm_w4_kernel(const GemmArgs p) {
   const char* ga2 = reinterpret_cast<const char*>(p.a2) + m0 * p.lda2 * 2;
   const uint32_t va1 = (uint32_t)((lt >> 3) * p.lda1 * 2 + (lt & 7) * 16);
   const uint32_t va2 = (uint32_t)((lt >> 3) * p.lda2 * 2 + (lt & 7) * 16);
-  const char* gb1 = reinterpret_cast<const char*>(p.b1) + (B_NN ? n0 * 2 : n0 * p.ldb1 * 2);
-  const char* gb2 = reinterpret_cast<const char*>(p.b2) + (B_NN ? n0 * 2 : n0 * p.ldb2 * 2);
+  const int64_t nb0 = SW ? n0 / 2 : n0;  // first weight row of the tile
+  const char* gb1 = reinterpret_cast<const char*>(p.b1) + (B_NN ? n0 * 2 : nb0 * p.ldb1 * 2);
+  const char* gb2 = reinterpret_cast<const char*>(p.b2) + (B_NN ? n0 * 2 : nb0 * p.ldb2 * 2);
+  const char* gb1u = SW ? reinterpret_cast<const char*>(p.b1u) + nb0 * p.ldb1 * 2 : gb1;
+  const char* gb2u = SW ? reinterpret_cast<const char*>(p.b2u) + nb0 * p.ldb2u * 2 : gb2;
   const uint32_t vb1 = B_NN ? (uint32_t)(kc * p.ldb1 * 2 + (lt >> 3) * 16)
                             : (uint32_t)((lt >> 3) * p.ldb1 * 2 + (lt & 7) * 16);
   const uint32_t vb2 = B_NN ? (uint32_t)(kc * p.ldb2 * 2 + (lt >> 3) * 16)
@@ -111,6 +120,10 @@ gemm_w4_kernel(const GemmArgs p) {
   const int64_t kstb1 = B_NN ? (int64_t)BK * p.ldb1 * 2 : (int64_t)BK * 2;
   const uint32_t kstb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(BK * p.ldb2 * 2) : (uint32_t)(BK * 2));
   const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
+  // SwiGLU segment 2 of the up rows: rank column k of Pcat is column k - k2s of B_up
+  const int k2s = SW ? __builtin_amdgcn_readfirstlane((int)p.k2_split) : 0;
+  const uint32_t vb2u = SW ? (uint32_t)((lt >> 3) * p.ldb2u * 2) : 0u;
+  const uint32_t isb2u = SW ? __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb2u * 2)) : 0u;
 
   u32x4 sa[PF][8], sb[PF][8];
 
@@ -120,6 +133,9 @@ gemm_w4_kernel(const GemmArgs p) {
   struct LoadDesc {
     __amdgpu_buffer_rsrc_t r;
     uint32_t vo, is;
+    // SwiGLU B tiles: the up rows' resource, lane offset and stride
+    __amdgpu_buffer_rsrc_t r2;
+    uint32_t vo2, is2;
   };
   auto desc_a = [&](int u) {
     const bool seg1 = u < nk1;
@@ -129,6 +145,9 @@ gemm_w4_kernel(const GemmArgs p) {
     d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, BIG, 0x00020000);
     d.vo = seg1 ? va1 : (tt * BK + kc < k2 ? va2 + (uint32_t)(tt * BK * 2) : OOB);
     d.is = seg1 ? isa1 : isa2;
+    d.r2 = d.r;
+    d.vo2 = 0;
+    d.is2 = 0;
     return d;
   };
   auto desc_b = [&](int u) {
@@ -138,15 +157,39 @@ gemm_w4_kernel(const GemmArgs p) {
     const char* base = seg1 ? gb1 + (int64_t)u * kstb1 : gb2;
     d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (B_NN && !seg1) ? nrecb2 : BIG,
                                             0x00020000);
-    if constexpr (!B_NN)
-      d.vo = seg1 ? vb1 : (tt * BK + kc < k2 ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
-    else
-      d.vo = seg1 ? vb1 : vb2 + (uint32_t)tt * kstb2;
+    if constexpr (SW) {
+      // gate rows: rank columns [0, k2s); up rows: [k2s, K2) shifted to B_up's own columns
+      const int kk = tt * BK + kc;
+      d.vo = seg1 ? vb1 : (kk < k2s ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
+      const char* base2 = seg1 ? gb1u + (int64_t)u * kstb1 : gb2u;
+      d.r2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base2), (short)0, BIG, 0x00020000);
+      d.vo2 = seg1 ? vb1 : (kk >= k2s && kk < k2 ? vb2u + (uint32_t)((kk - k2s) * 2) : OOB);
+      d.is2 = seg1 ? isb1 : isb2u;
+    } else {
+      if constexpr (!B_NN)
+        d.vo = seg1 ? vb1 : (tt * BK + kc < k2 ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
+      else
+        d.vo = seg1 ? vb1 : vb2 + (uint32_t)tt * kstb2;
+      d.r2 = d.r;
+      d.vo2 = 0;
+      d.is2 = 0;
+    }
     d.is = seg1 ? isb1 : isb2;
     return d;
   };
   auto ld = [&](const LoadDesc& d, int i) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(d.r, (int)(d.vo + i * d.is), 0, 0));
+  };
+  // chunk i of a B tile (SwiGLU: alternate weights, 32 rows of each per pair)
+  auto ldb = [&](const LoadDesc& d, int i) {
+    if constexpr (SW) {
+      if (i & 1)
+        return __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(d.r2, (int)(d.vo2 + (i >> 1) * d.is2), 0, 0));
+      return __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(d.r, (int)(d.vo + (i >> 1) * d.is), 0, 0));
+    }
+    return ld(d, i);
   };
   auto load_a = [&](int u, auto bsel) {
     constexpr int b = decltype(bsel)::value;
@@ -158,7 +201,7 @@ gemm_w4_kernel(const GemmArgs p) {
     constexpr int b = decltype(bsel)::value;
     const LoadDesc d = desc_b(u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sb[b][i] = ld(d, i);
+    for (int i = 0; i < 8; ++i) sb[b][i] = ldb(d, i);
   };
 
   // ---- registers -> LDS buffer st ----
@@ -315,7 +358,7 @@ gemm_w4_kernel(const GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         mf(I1{}, 8 + q);
-        sb[SB::value][q] = ld(d, q);
+        sb[SB::value][q] = ldb(d, q);
         fence();
       }
     }
@@ -369,6 +412,26 @@ gemm_w4_kernel(const GemmArgs p) {
           const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
           out[row * p.ldc + col] = f2bf(z1 * cs - z2 * sn);
           out[row * p.ldc + col + 64] = f2bf(z2 * cs + z1 * sn);
+        }
+      }
+  } else if constexpr (SW) {
+    // blocks j = 0, 2: gate, j = 1, 3: up, of the output columns
+    // n0 / 2 + 64 wn + 32 (j / 2) + l32
+    const int64_t hbase = nb0 + 64 * wn + l32;
+    uint16_t* og = reinterpret_cast<uint16_t*>(p.cg);
+    uint16_t* ou = reinterpret_cast<uint16_t*>(p.cu);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
+          const int64_t o = row * p.ldc + hbase + 32 * jj;
+          out[o] = f2bf(g / (1.f + __expf(-g)) * u);
+          if (og) og[o] = f2bf(g);
+          if (ou) ou[o] = f2bf(u);
         }
       }
   } else {

@@ -30,7 +30,7 @@ hipError_t run(GemmArgs a, int splits, hipStream_t st) {
 // segment a whole number of 64-wide stages, no split, every lane offset of a
 // tile below the 1 GiB buffer-resource range) take gemm_w4_kernel.
 bool whole_tiles(const GemmArgs& a, int splits) {
-  const int64_t ld = std::max(std::max(a.lda1, a.lda2), std::max(a.ldb1, a.ldb2));
+  const int64_t ld = std::max(std::max(std::max(a.lda1, a.lda2), std::max(a.ldb1, a.ldb2)), a.ldb2u);
   return splits == 1 && a.m_load == a.m_store && a.m_store % w4::BM == 0 && a.n_load == a.n_store &&
          a.n_store % w4::BN == 0 && a.K1 % w4::BK == 0 && ld * 2 * (w4::BM + w4::BK) < (int64_t)w4::BIG;
 }
@@ -74,6 +74,8 @@ TileShape gemm_tile(GemmKind k) {
     case G_BF16_SPLIT_NN_PARTIAL:
     case G_F32_SPLIT_NN_PARTIAL:
       return {64, 256};
+    case G_BF16_WHOLE_SWIGLU:
+      return {256, 256};
     case G_BF16_PANEL_SPLIT_NT:
       return {256, 64};
     case G_F32_NT_STORE:
@@ -118,6 +120,9 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_NF4_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_NF4>(a, splits, st);
     case G_NF4_MED_NN_PARTIAL: return run<bf, 128, 128, 4, 1, true, EPI_PARTIAL, BL_NF4>(a, splits, st);
     case G_BF16_MED_NN_ADD: return run<bf, 128, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
+    case G_BF16_WHOLE_SWIGLU:
+      if (!whole_tiles(a, splits)) return hipErrorInvalidValue;
+      return run_whole<false, EPI_SWIGLU>(a, st);
     case G_F32_NN_ADD: return run<float, 64, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
     default: return hipErrorInvalidValue;
   }
@@ -335,6 +340,89 @@ hipError_t launch_split_finish(const float* part, int splits, int64_t part_strid
     hipLaunchKernelGGL(split_finish_kernel<false>, dim3(grid_for(items, 256)), dim3(256), 0, st, part, splits,
                        part_stride, M, N, out, ldo, pos, cosc, sinc);
   }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SwiGLU elementwise passes (gate/up pairs whose shapes the fused whole-tile
+// epilogue does not cover, and the backward): fp32 arithmetic on T values,
+// silu(z) = z / (1 + e^-z), sigmoid s = 1 / (1 + e^-z).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p, int64_t i) {
+  if constexpr (sizeof(T) == 2)
+    return static_cast<float>(__builtin_bit_cast(__bf16, reinterpret_cast<const uint16_t*>(p)[i]));
+  else
+    return p[i];
+}
+
+template <typename T>
+__device__ __forceinline__ void st_elem(T* p, int64_t i, float v) {
+  if constexpr (sizeof(T) == 2)
+    reinterpret_cast<uint16_t*>(p)[i] = f2bf(v);
+  else
+    p[i] = v;
+}
+
+// H = silu(G) * U
+template <typename T>
+__global__ void swiglu_apply_kernel(const T* __restrict__ G, const T* __restrict__ U, T* __restrict__ H, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const float g = ld_elem(G, e), u = ld_elem(U, e);
+    st_elem(H, e, g / (1.f + __expf(-g)) * u);
+  }
+}
+
+// dG = dH U s (1 + G (1 - s)), dU = dH G s, s = sigmoid(G)
+template <typename T>
+__global__ void swiglu_grad_kernel(const T* __restrict__ dH, const T* __restrict__ G, const T* __restrict__ U,
+                                   T* __restrict__ dG, T* __restrict__ dU, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const float h = ld_elem(dH, e), g = ld_elem(G, e), u = ld_elem(U, e);
+    const float sg = 1.f / (1.f + __expf(-g));
+    st_elem(dG, e, h * u * sg * (1.f + g * (1.f - sg)));
+    st_elem(dU, e, h * g * sg);
+  }
+}
+
+// dst += src
+template <typename T>
+__global__ void add_into_kernel(T* __restrict__ dst, const T* __restrict__ src, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+    st_elem(dst, e, ld_elem(dst, e) + ld_elem(src, e));
+}
+
+hipError_t launch_swiglu_apply(int elem_bytes, const void* G, const void* U, void* H, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(swiglu_apply_kernel<__bf16>, dim3(grid_for(n, 256)), dim3(256), 0, st,
+                       (const __bf16*)G, (const __bf16*)U, (__bf16*)H, n);
+  else
+    hipLaunchKernelGGL(swiglu_apply_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const float*)G,
+                       (const float*)U, (float*)H, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_grad(int elem_bytes, const void* dH, const void* G, const void* U, void* dG, void* dU,
+                              int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(swiglu_grad_kernel<__bf16>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const __bf16*)dH,
+                       (const __bf16*)G, (const __bf16*)U, (__bf16*)dG, (__bf16*)dU, n);
+  else
+    hipLaunchKernelGGL(swiglu_grad_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const float*)dH,
+                       (const float*)G, (const float*)U, (float*)dG, (float*)dU, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_into(int elem_bytes, void* dst, const void* src, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(add_into_kernel<__bf16>, dim3(grid_for(n, 256)), dim3(256), 0, st, (__bf16*)dst,
+                       (const __bf16*)src, n);
+  else
+    hipLaunchKernelGGL(add_into_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (float*)dst,
+                       (const float*)src, n);
   return hipGetLastError();
 }
 

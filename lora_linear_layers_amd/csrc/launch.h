@@ -42,6 +42,7 @@ enum GemmKind : int {
   G_NF4_MED_NN_PARTIAL,
   G_BF16_MED_NN_ADD,
   G_F32_NN_ADD,
+  G_BF16_WHOLE_SWIGLU,
   G_KIND_COUNT
 };
 
@@ -110,6 +111,13 @@ hipError_t launch_split_finish(const float* part, int splits, int64_t part_strid
                                hipStream_t st);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
+
+// SwiGLU elementwise passes over n elements of bf16 (elem_bytes 2) or fp32:
+// H = silu(G) U; dG = dH U silu'(G), dU = dH silu(G); dst += src.
+hipError_t launch_swiglu_apply(int elem_bytes, const void* G, const void* U, void* H, int64_t n, hipStream_t st);
+hipError_t launch_swiglu_grad(int elem_bytes, const void* dH, const void* G, const void* U, void* dG, void* dU,
+                              int64_t n, hipStream_t st);
+hipError_t launch_add_into(int elem_bytes, void* dst, const void* src, int64_t n, hipStream_t st);
 
 // blocks x 256 threads of the MFMA-rate kernel (iters rounds of 8 MFMAs per
 // wave); out [blocks * 256] receives one float per thread.

@@ -258,6 +258,64 @@ def lora_group_bwd(X, members, dYs, positions=None, cos=None, sin=None, table16=
     return res
 
 
+def _swiglu_ws(backward, dt, M, d_in, arr, device, ws):
+    n = int(L.lib().lora_swiglu_workspace_bytes(int(backward), dt, M, d_in, arr))
+    if ws is not None:
+        return ws
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def lora_swiglu_fwd(X, members, table16=None, H=None, store_gu: bool = True, ws=None):
+    """(H, G, U) for the gate (members[0]) and up (members[1]) projections of X:
+    H = silu(G) * U; G and U come back (for the backward) when store_gu, else None."""
+    L._contig(X, H)
+    if len(members) != 2:
+        raise ValueError("SwiGLU takes the gate and the up projection")
+    M, d_in = X.shape
+    dt = L._dtype_code(X)
+    arr = _group_members(X, members)
+    d = arr[0].d_out
+    if H is None:
+        H = torch.empty(M, d, dtype=X.dtype, device=X.device)
+    G = U = None
+    if store_gu:
+        G = torch.empty(M, d, dtype=X.dtype, device=X.device)
+        U = torch.empty(M, d, dtype=X.dtype, device=X.device)
+        arr[0].Y, arr[1].Y = L._ptr(G), L._ptr(U)
+    tab = L._table_ptr(table16) if table16 is not None else None
+    ws = _swiglu_ws(False, dt, M, d_in, arr, X.device, ws)
+    L._check("lora_swiglu_fwd", L.lib().lora_swiglu_fwd(dt, M, d_in, arr, L._ptr(X), tab, L._ptr(H), L._ptr(ws),
+                                                        ws.numel(), L._stream(X.device)))
+    return H, G, U
+
+
+def lora_swiglu_bwd(X, members, dH, G, U, table16=None, need_dX: bool = True, ws=None):
+    """(dX or None, [(dA_gate, dB_gate), (dA_up, dB_up)]); dX sums both input gradients."""
+    L._contig(X, dH, G, U)
+    if len(members) != 2:
+        raise ValueError("SwiGLU takes the gate and the up projection")
+    M, d_in = X.shape
+    dt = L._dtype_code(X)
+    arr = _group_members(X, members)
+    d = arr[0].d_out
+    for t in (dH, G, U):
+        if t.shape != (M, d):
+            raise ValueError("dH, G and U must be [M, d_out]")
+    dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+    grads = []
+    for g in range(2):
+        dA = torch.empty(arr[g].r, d_in, dtype=torch.float32, device=X.device)
+        dB = torch.empty(d, arr[g].r, dtype=torch.float32, device=X.device)
+        arr[g].dA, arr[g].dB = L._ptr(dA), L._ptr(dB)
+        grads.append((dA, dB))
+    tab = L._table_ptr(table16) if table16 is not None else None
+    ws = _swiglu_ws(True, dt, M, d_in, arr, X.device, ws)
+    L._check("lora_swiglu_bwd", L.lib().lora_swiglu_bwd(
+        dt, M, d_in, arr, L._ptr(X), tab, L._ptr(dH), L._ptr(G), L._ptr(U), L._ptr(dX), L._ptr(ws), ws.numel(),
+        L._stream(X.device)))
+    return dX, grads
+
+
 class LoraLinearFunction(torch.autograd.Function):
     """Autograd wrapper: gradients for X, A and B (W frozen); A and B grads in fp32."""
 

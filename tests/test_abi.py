@@ -220,3 +220,31 @@ def test_merge_validation(lib):
     assert f(_lib.OP_MERGE, 1, 0, 64, 64, 8) == 0
     assert f(_lib.OP_MERGE, 1, 0, 64, 96, 3) == 96 * 8 * 2
     assert f(_lib.OP_MERGE, 0, 0, 64, 96, 3) == 96 * 8 * 4
+
+
+def test_swiglu_validation_and_workspace(lib):
+    f = lib.lora_swiglu_workspace_bytes
+    m = _members(2, d_out=1024, r=16)
+    fused = f(0, 1, 4096, 4096, m)  # whole tiles: one GEMM, no G/U buffers
+    ragged = f(0, 1, 4100, 4096, m)  # elementwise path: G and U in the workspace
+    assert ragged >= 2 * 4100 * 1024 * 2 and fused < ragged
+    assert f(1, 1, 4096, 4096, m) >= 2 * 4096 * 1024 * 2 + 4096 * 4096 * 2  # dG, dU, up's dX
+    assert f(0, 1, 16, 64, _members(2)) == 0  # unequal d_out
+    assert f(0, 5, 16, 64, m) == 0
+
+    def fwd(mb, dtype=1, H=P, X=P, wsb=1 << 30):
+        return lib.lora_swiglu_fwd(dtype, 16, 64, mb, X, None, H, P, wsb, None)
+    assert fwd(_members(2)) == ESHAPE  # d_out 64 vs 128
+    assert fwd(_members(2, d_out=64, rope=1)) == ESHAPE
+    assert fwd(_members(2, d_out=64), H=None) == ENULL
+    assert fwd(_members(2, d_out=64), X=None) == ENULL
+    assert fwd(_members(2, d_out=64, Y=P + 2)) == EALIGN
+    assert fwd(_members(2, d_out=64, W=None, W_nf4=P, absmax=P)) == ENULL  # NF4 without a table
+    assert fwd(_members(2, d_out=64), wsb=10) == EWS
+    assert fwd(None) == ENULL
+
+    def bwd(mb, dH=P, dX=P):
+        return lib.lora_swiglu_bwd(1, 16, 64, mb, P, None, dH, P, P, dX, P, 1 << 30, None)
+    assert bwd(_members(2, d_out=64), dH=None) == ENULL
+    assert bwd(_members(2, d_out=64, dA=None)) == ENULL
+    assert bwd(_members(2, d_out=64), dX=P + 4) == EALIGN
