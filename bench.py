@@ -289,6 +289,77 @@ def per_call_times(work, reps):
     return out
 
 
+def _time_ms(fn, reps):
+    import torch
+
+    fn()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return _pct(ts)
+
+
+def next_rows(work, reps=10):
+    """The rows beyond the layer itself, on this workload's gate / up pair:
+    SwiGLU (fused epilogue vs. the pair's plain group forward) and the merge of
+    the gate adapter into its weight (HBM-bound: W read and written once)."""
+    import torch
+
+    L, cfg = work.L, work.cfg
+    pair = [it for it in work.items if it["p"].name in ("gate_proj", "up_proj")]
+    if len(pair) != 2 or cfg.dtype == "f32":
+        return None
+    out = {}
+    M, s = cfg.M, cfg.scale
+    X = pair[0]["X"]
+    k, d = pair[0]["p"].d_in, pair[0]["p"].d_out
+    tab = work.table if cfg.nf4 else None
+    ms = []
+    for it in pair:
+        m = {"A": it["A"], "B": it["B"], "scale": s}
+        if cfg.nf4:
+            m["codes"], m["absmax"] = it["codes"], it["absmax"]
+        else:
+            m["W"] = it["W"]
+        ms.append(m)
+    H = torch.empty(M, d, dtype=X.dtype, device=X.device)
+    G, U = pair[0]["Y"], pair[1]["Y"]
+    dH = pair[0]["dY"]
+    fwd_flop = 2.0 * 2 * M * (d * k + cfg.r * (d + k))
+    bwd_flop = 2.0 * 2 * M * (d * k + 2 * cfg.r * (d + k))
+    arr = L.functional._group_members(X, ms)
+    wsb = max(int(L.lib().lora_swiglu_workspace_bytes(b, L.LORA_BF16, M, k, arr)) for b in (0, 1))
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=X.device)
+    sw = {}
+    sw["fwd_with_gu_ms"] = _time_ms(lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, ws=ws), reps)
+    sw["fwd_h_only_ms"] = _time_ms(lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, store_gu=False, ws=ws), reps)
+    sw["group_fwd_ms"] = _time_ms(lambda: L.lora_group_fwd(X, ms, table16=tab, Ys=[G, U], ws=work.ws), reps)
+    Gs, Us = L.lora_swiglu_fwd(X, ms, table16=tab, ws=ws)[1:]
+    sw["bwd_ms"] = _time_ms(lambda: L.lora_swiglu_bwd(X, ms, dH, Gs, Us, table16=tab, ws=ws), reps)
+    for key, fl in (("fwd_with_gu_ms", fwd_flop), ("fwd_h_only_ms", fwd_flop), ("group_fwd_ms", fwd_flop),
+                    ("bwd_ms", bwd_flop)):
+        sw[key.replace("_ms", "_tflops")] = round(fl / (sw[key]["median"] * 1e-3) / 1e12, 1)
+    sw["shape"] = f"gate/up {k}->{d}, M={M}, r={cfg.r}" + (", NF4 W" if cfg.nf4 else "")
+    out["swiglu"] = sw
+    del ws, Gs, Us
+    if not cfg.nf4:
+        it = pair[0]
+        Wm = torch.empty_like(it["W"])
+        mws = torch.empty(max(L.workspace_bytes(L.OP_MERGE, L.LORA_BF16, 0, k, d, cfg.r), 256),
+                          dtype=torch.uint8, device=X.device)
+        t = _time_ms(lambda: L.lora_merge(it["W"], it["A"], it["B"], s, out=Wm, ws=mws), reps)
+        by = 2.0 * 2 * d * k + 2.0 * cfg.r * (d + k)
+        out["merge"] = {"shape": f"W {d}x{k}, r={cfg.r}", "ms": t, "min_bytes": by,
+                        "gbps": round(by / (t["median"] * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(by / (t["median"] * 1e-3) / 8e12, 3)}
+    return out
+
+
 def small_token_sweep(device, reps=10):
     """Few-token cases, where reading W bounds the layer: the Llama-3-8B q
     projection (4096->4096, r 16, RoPE, bf16) and the Qwen1.5-32B-shaped gate
@@ -566,6 +637,8 @@ def main():
     }
     if not args.no_small_token:
         out["small_token"] = small_token_sweep(dev)
+    if args.call_reps > 0:
+        out["next_rows"] = next_rows(work, args.call_reps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, work, args.cpu_seconds)
     print(json.dumps(out), flush=True)
