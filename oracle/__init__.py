@@ -22,6 +22,9 @@ from .lora_oracle import (  # noqa: F401
     nf4_lora_forward,
     nf4_lora_backward,
     merged_weight,
+    dropout_keep,
+    lora_dropout_forward,
+    lora_dropout_backward,
     silu,
     swiglu_forward,
     swiglu_grad,

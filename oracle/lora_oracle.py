@@ -17,6 +17,8 @@ section or equation on it:
          the rotation applied inside the q/k projection.
   [P2] "微调太慢？试试Unsloth：实测训练速度翻倍，显存占用减半", section 5.1:
        for inference the LoRA weights are merged into the main weight.
+  [P2] section 3.3, configuration E: LoRA dropout 0.05 (a weak effect on the
+       loss); [P4] section 2.2: get_peft_model(..., lora_dropout=0.1).
   [P3] "Unsloth教程：本地微调大模型速度提升数倍，显存节省60%", section
        显存优化策略, 4-bit QLoRA paragraph: base weight in NormalFloat4, only
        the LoRA adapters train (no dW).
@@ -38,6 +40,10 @@ notes):
     ("rotate-half"), angle pos * theta^(-2i/D), theta = 5e5;
   * NF4: blocks of 64 consecutive elements of row-major W [d_out, d_in];
     element 2j in the high nibble of byte j; value = bf16(f32(table[c] * absmax));
+  * LoRA dropout (a rate on the pages, not a definition): inverted dropout on
+    the adapter's input only, D(x) = x * keep / (1 - p) with keep ~ Bernoulli(1 - p)
+    per element of X; the base path W x sees x unchanged.  The keep mask is an
+    input (bit-packed, bit b of byte [i, j] keeps element (i, 8 j + b));
   * SwiGLU (named, not defined, on the pages): the Llama MLP's gated unit
     h = silu(g) * u elementwise, g and u the gate and up projections of the
     same x, silu(z) = z / (1 + e^-z).
@@ -218,6 +224,38 @@ def nf4_encode(W, table, blocksize: int = 64):
     codes = codes.reshape(n)
     packed = ((codes[0::2] << 4) | codes[1::2]).astype(np.uint8)
     return packed, am.astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# LoRA dropout on the adapter's input ([P2] 3.3, [P4] 2.2)
+# ---------------------------------------------------------------------------
+
+def dropout_keep(bits, M: int, d_in: int) -> np.ndarray:
+    """bool [M, d_in] keep mask from the packed bytes [M, d_in / 8]: bit b
+    (least significant first) of byte (i, j) is element (i, 8 j + b)."""
+    b = np.asarray(bits, dtype=np.uint8).reshape(M, d_in // 8)
+    out = np.zeros((M, d_in), dtype=bool)
+    for bit in range(8):
+        out[:, bit::8] = (b >> bit) & 1
+    return out
+
+
+def lora_dropout_forward(X, W, A, B, s: float, p: float, keep) -> np.ndarray:
+    """Y = X W^T + s (D A^T) B^T with D = X * keep / (1 - p)."""
+    X, W, A, B = map(_f64, (X, W, A, B))
+    D = X * np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    return X @ W.T + s * ((D @ A.T) @ B.T)
+
+
+def lora_dropout_backward(X, W, A, B, s: float, p: float, keep, G):
+    """(dX, dA, dB) of lora_dropout_forward for upstream G:
+      dX = G W + s ((G B) A) * keep / (1 - p)   (the adapter's path passes the mask)
+      dA = s (G B)^T D,  dB = s G^T (D A^T)."""
+    X, W, A, B, G = map(_f64, (X, W, A, B, G))
+    k = np.asarray(keep, dtype=np.float64) / (1.0 - p)
+    D = X * k
+    Q = G @ B
+    return G @ W + s * (Q @ A) * k, s * (Q.T @ D), s * (G.T @ (D @ A.T))
 
 
 # ---------------------------------------------------------------------------

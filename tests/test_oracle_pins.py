@@ -410,3 +410,58 @@ def test_swiglu_zero_up_adapter_has_zero_gradients():
     dX, dAg, dBg, dAu, dBu = O.swiglu_backward(X, Wg, Ag, Bg, 1.0, Wu, Z((1, k)), Z((d, 1)), 1.0, _rand(M, d))
     assert np.all(dAu == 0.0) and np.all(dBu == 0.0)
     assert np.abs(dAg).max() > 0 and np.abs(dBg).max() > 0
+
+
+# ---------------------------------------------------------------------------
+# LoRA dropout on the adapter's input
+# ---------------------------------------------------------------------------
+
+def test_dropout_keep_bit_order():
+    # byte 0b00000101 keeps elements 0 and 2; 0x80 keeps element 7 of its group
+    k = O.dropout_keep(np.array([[0b00000101, 0x80]], dtype=np.uint8), 1, 16)
+    assert k.tolist() == [[True, False, True] + [False] * 12 + [True]]
+
+
+def test_dropout_hand_worked():
+    # x = [2, 4], W = [[1, 1]], A = [[1, 1]], B = [[1]], s = 1, p = 0.5, keep = [1, 0]:
+    # D = [4, 0], A D = 4, y = 6 + 4 = 10
+    Y = O.lora_dropout_forward([[2.0, 4.0]], [[1.0, 1.0]], [[1.0, 1.0]], [[1.0]], 1.0, 0.5, [[True, False]])
+    assert Y[0, 0] == 10.0
+
+
+def test_dropout_special_cases():
+    M, k, d, r = 4, 8, 5, 2
+    X, W, A, B, G = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r), _rand(M, d)
+    ones, zeros = np.ones((M, k), bool), np.zeros((M, k), bool)
+    # p = 0 and every element kept: the plain layer
+    assert np.abs(O.lora_dropout_forward(X, W, A, B, 2.0, 0.0, ones) - O.lora_forward(X, W, A, B, 2.0)).max() < 1e-12
+    for a, b in zip(O.lora_dropout_backward(X, W, A, B, 2.0, 0.0, ones, G), O.lora_backward(X, W, A, B, 2.0, G)):
+        assert np.abs(a - b).max() < 1e-12
+    # nothing kept: the adapter sees zeros, so it contributes nothing and gets no gradient
+    assert np.abs(O.lora_dropout_forward(X, W, A, B, 2.0, 0.3, zeros) - X @ W.T).max() < 1e-12
+    dX, dA, dB = O.lora_dropout_backward(X, W, A, B, 2.0, 0.3, zeros, G)
+    assert np.abs(dX - G @ W).max() < 1e-12 and np.all(dA == 0) and np.all(dB == 0)
+
+
+def test_dropout_backward_matches_finite_differences():
+    M, k, d, r = 3, 8, 4, 2
+    X, W, A, B, G = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r), _rand(M, d)
+    keep = RNG.random((M, k)) < 0.7
+    s, p = 2.0, 0.3
+    dX, dA, dB = O.lora_dropout_backward(X, W, A, B, s, p, keep, G)
+    f = lambda: float(np.sum(G * O.lora_dropout_forward(X, W, A, B, s, p, keep)))  # noqa: E731
+    # linear in each of X, A, B for a fixed mask: central differences are exact up to rounding
+    assert np.abs(_fd(f, X) - dX).max() < 1e-9
+    assert np.abs(_fd(f, A) - dA).max() < 1e-9
+    assert np.abs(_fd(f, B) - dB).max() < 1e-9
+
+
+def test_dropout_is_unbiased_over_masks():
+    # inverted dropout keeps the expectation: the mean over many masks tends to
+    # the plain layer (tolerance 5 standard errors of the mean)
+    M, k, d, r, p = 2, 6, 3, 2, 0.4
+    X, W, A, B = _rand(M, k), _rand(d, k), _rand(r, k), _rand(d, r)
+    rng = np.random.default_rng(11)
+    ys = np.stack([O.lora_dropout_forward(X, W, A, B, 1.0, p, rng.random((M, k)) >= p) for _ in range(20000)])
+    se = ys.std(axis=0) / np.sqrt(len(ys))
+    assert np.all(np.abs(ys.mean(axis=0) - O.lora_forward(X, W, A, B, 1.0)) <= 5 * se + 1e-12)
