@@ -76,7 +76,9 @@ enum {
   LORA_OP_ROPE_BWD = 3,
   LORA_OP_NF4_FWD = 4,
   LORA_OP_NF4_BWD = 5,
-  LORA_OP_MERGE = 6
+  LORA_OP_MERGE = 6,
+  LORA_OP_DROPOUT_FWD = 7,
+  LORA_OP_DROPOUT_BWD = 8
 };
 
 /* Library version; equals LORA_ABI_VERSION of the header it was built from. */
@@ -185,6 +187,28 @@ int nf4_lora_linear_bwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float
  */
 int nf4_dequant(const uint8_t* W_nf4, const float* absmax, int blocksize, int64_t n,
                 const float* table16, uint16_t* out_bf16, void* stream);
+
+/*
+ * LoRA dropout on the adapter's input (page "微调太慢？试试Unsloth…", section
+ * 3.3, configuration E trains with dropout 0.05; page "Unsloth框架：高效LLM微调
+ * 与LoRA优化实践", section 2.2, passes lora_dropout = 0.1): inverted dropout
+ * D = X * keep / (1 - p) feeds only the rank-r branch, the base path sees X:
+ *     Y  = X W^T + s (D A^T) B^T
+ *     dX = G W + s ((G B) A) * keep / (1 - p),  dA = s (G B)^T D,  dB = s G^T (D A^T).
+ * keep: device bit mask [M, d_in / 8] bytes, bit b of byte (i, j) keeps element
+ * (i, 8 j + b); the caller draws it (the library has no random generator) and
+ * passes the same mask to the backward.  0 <= p < 1.  The masked copy of X is
+ * exact and 1 / (1 - p) joins s in the rank-r panels; the masked rank-r term
+ * of dX is a separate rank-r GEMM added into dX.  Other arguments, workspace
+ * (op LORA_OP_DROPOUT_FWD / _BWD) and errors as lora_linear_fwd / _bwd;
+ * LORA_ERR_SHAPE if p is outside [0, 1).
+ */
+int lora_dropout_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                     const uint8_t* keep, const void* X, const void* W, const void* A, const void* B, void* Y,
+                     void* ws, size_t ws_bytes, void* stream);
+int lora_dropout_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                     const uint8_t* keep, const void* X, const void* W, const void* A, const void* B,
+                     const void* dY, void* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Merge for inference: W_out = W + scale * B A, one GEMM over the rank (fp32

@@ -15,6 +15,8 @@ from ._lib import (  # noqa: F401
     LORA_BF16,
     LORA_F32,
     OP_BWD,
+    OP_DROPOUT_BWD,
+    OP_DROPOUT_FWD,
     OP_FWD,
     OP_MERGE,
     OP_NF4_BWD,
@@ -28,6 +30,8 @@ from ._lib import (  # noqa: F401
 )
 from .functional import (  # noqa: F401
     LoraLinearFunction,
+    lora_dropout_bwd,
+    lora_dropout_fwd,
     lora_group_bwd,
     lora_group_fwd,
     lora_linear_bwd,

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora_linear.so")
 
 LORA_F32, LORA_BF16 = 0, 1
-OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD, OP_MERGE = range(7)
+OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD, OP_MERGE, OP_DROPOUT_FWD, OP_DROPOUT_BWD = range(9)
 
 _lib = None
 
@@ -59,6 +59,10 @@ _SIGS = {
     "lora_swiglu_bwd": ([_int, _i64, _i64, _mp, _vp, _fp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
     "lora_swiglu_workspace_bytes": ([_int, _int, _i64, _i64, _mp], _sz),
     "lora_merge": ([_int, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "lora_dropout_fwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                         _int),
+    "lora_dropout_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                          _vp, _sz, _vp], _int),
     "lora_mfma_rate": ([_int, _int, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),
     "lora_profile_end": ([], _int),

@@ -54,7 +54,8 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct Layout {
   int64_t r8 = 0, M8 = 0;
-  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, spart = 0, total = 0;
+  size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, spart = 0, xm = 0,
+         total = 0;
   int splits_main = 1;  // contraction splits of the Y (forward) or dX (backward) GEMM
   int64_t ksplit_main = 0;
   bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
@@ -132,7 +133,8 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.total = off;
     return L;
   }
-  const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD;
+  const bool drop = op == LORA_OP_DROPOUT_FWD || op == LORA_OP_DROPOUT_BWD;
+  const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD || op == LORA_OP_DROPOUT_BWD;
   if ((op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD) && M >= LORA_NF4_DEQUANT_MIN_TOKENS) {
     L.dequant = true;
     L.wdq = take(size_t(d_out) * d_in * 2);
@@ -171,6 +173,7 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.part = take(pa > pb ? pa : pb);
     L.spart = L.part;
   }
+  if (drop) L.xm = take(size_t(M) * d_in * eb);
   L.total = off;
   return L;
 }
@@ -226,6 +229,7 @@ enum ProfKind : int {
   K_COPY_ROWS,
   K_FINISH,
   K_SWIGLU,
+  K_MASK,
   K_PROF_COUNT
 };
 
@@ -239,10 +243,12 @@ const char* kind_name(int k) {
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
       "panel_bf16_256x64_split",    "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
       "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
-      "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "pad_cols",                   "rope_inverse",
+      "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "dropout_dx_bf16_128x128",
+      "dropout_dx_f32_64x128",      "pad_cols",                   "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
-      "copy_rows",                  "split_finish",               "swiglu_elementwise"};
+      "copy_rows",                  "split_finish",               "swiglu_elementwise",
+      "dropout_mask_copy"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -336,7 +342,10 @@ int dequant_w(const Nf4W& q, int64_t n, void* out, hipStream_t st) {
 // ldpext, columns r..r8 zero) and is not computed here (group calls).
 int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
                  const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, void* Y, void* ws,
-                 const Layout& L, hipStream_t st, const void* Pext = nullptr, int64_t ldpext = 0) {
+                 const Layout& L, hipStream_t st, const void* Pext = nullptr, int64_t ldpext = 0,
+                 const void* Xa = nullptr) {
+  // Xa: the adapter's input when it differs from X (LoRA dropout)
+  const void* Xp = Xa ? Xa : X;
   if (M == 0) return LORA_OK;
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
@@ -360,12 +369,12 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     // computed by the caller
   } else if (f32) {
     GemmArgs a = blank();
-    a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
+    a.a1 = Xp; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
     a.m_load = M; a.m_store = M; a.n_load = r; a.n_store = L.r8;
     a.c = w + L.p; a.ldc = L.r8; a.alpha = scale;
     HIPTRY(gemm(G_F32_PANEL_NT_STORE, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
   } else {
-    TRY(panel_bf16(X, d_in, A, d_in, M, M, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale),
+    TRY(panel_bf16(Xp, d_in, A, d_in, M, M, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale),
                    reinterpret_cast<float*>(w + L.ppart), reinterpret_cast<uint16_t*>(w + L.p), L.r8, nullptr, 0, st));
   }
   // main: Y = [X | P] [W | B]^T, optional RoPE epilogue
@@ -423,7 +432,10 @@ struct PanelSlices {
 int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
                   const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, const void* dY,
                   void* dX, float* dA, float* dB, void* ws, const Layout& L, hipStream_t st,
-                  const PanelSlices* ov = nullptr) {
+                  const PanelSlices* ov = nullptr, const void* Xa = nullptr, const uint8_t* keep = nullptr) {
+  // LoRA dropout: Xa is the adapter's (masked) input and `keep` the mask that
+  // the rank-r term of dX passes through; X itself still feeds the base path
+  const void* Xp = Xa ? Xa : X;
   if (M == 0) {
     HIPTRY(timed(K_FILL, 0, 4.0 * r * d_in, st, [&] { return launch_fill_zero(dA, r * d_in, st); }));
     HIPTRY(timed(K_FILL, 0, 4.0 * r * d_out, st, [&] { return launch_fill_zero(dB, d_out * r, st); }));
@@ -460,7 +472,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
     {
       GemmArgs a = blank();
-      a.a1 = X; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
+      a.a1 = Xp; a.lda1 = d_in; a.b1 = A; a.ldb1 = d_in; a.K1 = d_in;
       a.m_load = M; a.m_store = L.M8; a.n_load = r; a.n_store = L.r8;
       a.ct = w + L.pt; a.ldct = L.M8; a.alpha = scale;
       HIPTRY(gemm(G_F32_PANEL_NT_STORE_T, a, 1, st, 2 * Md * rr * ki, (Md * ki + rr * ki + Md * L.r8) * e));
@@ -477,7 +489,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     // Pt = (s X A^T)^T  [r8, M8], recomputed from X (rows M..M8 and columns r..r8 are zeros)
     float* pp = reinterpret_cast<float*>(w + L.ppart);
     if (!ov)
-      TRY(panel_bf16(X, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale), pp,
+      TRY(panel_bf16(Xp, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale), pp,
                      nullptr, 0, reinterpret_cast<uint16_t*>(w + L.pt), L.M8, st));
     // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
     uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
@@ -487,11 +499,12 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, col_scale(scale), pp,
                    static_cast<uint16_t*>(Qs), ldqs, static_cast<uint16_t*>(Qt), L.M8, st));
   }
-  // dX = [G | Qs] [W ; A]
+  // dX = [G | Qs] [W ; A]; with a dropout mask the rank-r term is added
+  // separately, masked: dX = G W, then dX += keep * (Qs A)
   if (dX) {
     GemmArgs a = blank();
     a.a1 = G; a.lda1 = d_out; a.b1 = W; a.ldb1 = d_in; a.K1 = d_out;
-    a.a2 = Qs; a.lda2 = ldqs; a.b2 = A; a.ldb2 = d_in; a.K2 = r;
+    a.a2 = Qs; a.lda2 = ldqs; a.b2 = A; a.ldb2 = d_in; a.K2 = keep ? 0 : r;
     a.m_load = M; a.m_store = M; a.n_load = d_in; a.n_store = d_in;
     a.c = dX; a.ldc = d_in;
     GemmKind k;
@@ -520,6 +533,14 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     } else {
       HIPTRY(gemm(k, a, 1, st, flop, bytes));
     }
+    if (keep) {
+      GemmArgs b = blank();
+      b.a1 = Qs; b.lda1 = ldqs; b.b1 = A; b.ldb1 = d_in; b.K1 = r;
+      b.m_load = M; b.m_store = M; b.n_load = d_in; b.n_store = d_in;
+      b.c = dX; b.ldc = d_in; b.cin = dX; b.ldcin = d_in; b.mask = keep; b.mask_ld = d_in / 8;
+      HIPTRY(gemm(f32 ? G_F32_NN_ADD_MASKED : G_BF16_MED_NN_ADD_MASKED, b, 1, st, 2 * Md * ki * rr,
+                  (Md * rr + rr * ki + 2 * Md * ki) * e + Md * ki / 8));
+    }
   }
   const GemmKind ksplit = f32 ? G_F32_SPLIT_NN_PARTIAL : G_BF16_SPLIT_NN_PARTIAL;
   // dB^T = Pt G  -> partials [splits][r8, d_out] -> dB [d_out, r]
@@ -537,7 +558,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   // dA = Qt X -> partials [splits][r8, d_in] -> dA [r, d_in]
   if (!ov) {
     GemmArgs a = blank();
-    a.a1 = Qt; a.lda1 = L.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
+    a.a1 = Qt; a.lda1 = L.M8; a.b1 = Xp; a.ldb1 = d_in; a.K1 = M;
     a.m_load = L.r8; a.m_store = L.r8; a.n_load = d_in; a.n_store = d_in;
     a.k_split = L.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = L.r8 * d_in;
     HIPTRY(gemm(ksplit, a, L.splits_dA, st, 2 * rr * ki * Md,
@@ -917,7 +938,7 @@ const char* lora_strerror(int code) {
 }
 
 size_t lora_workspace_bytes(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
-  if (op < LORA_OP_FWD || op > LORA_OP_MERGE) return 0;
+  if (op < LORA_OP_FWD || op > LORA_OP_DROPOUT_BWD) return 0;
   if (dtype != LORA_F32 && dtype != LORA_BF16) return 0;
   if (check_sizes(M, d_in, d_out, r) != LORA_OK) return 0;
   return make_layout(op, dtype, M, d_in, d_out, r).total;
@@ -1072,6 +1093,46 @@ int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   TRY(check_device());
   const Rope rp{positions, cos_cache, sin_cache};
   return group_backward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
+}
+
+int lora_dropout_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                     const uint8_t* keep, const void* X, const void* W, const void* A, const void* B, void* Y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  if (!(p >= 0.f && p < 1.f)) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({W, A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y, keep}));
+  const Layout L = make_layout(LORA_OP_DROPOUT_FWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* Xm = static_cast<char*>(ws) + L.xm;
+  HIPTRY(timed(K_MASK, 0, (2.0 * elem_bytes(dtype) + 0.125) * M * d_in, st,
+               [&] { return launch_mask_copy(elem_bytes(dtype), X, keep, Xm, M * d_in, st); }));
+  return forward_impl(dtype, M, d_in, d_out, r, scale / (1.f - p), X, W, nullptr, A, B, nullptr, Y, ws, L, st,
+                      nullptr, 0, Xm);
+}
+
+int lora_dropout_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                     const uint8_t* keep, const void* X, const void* W, const void* A, const void* B, const void* dY,
+                     void* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  if (!(p >= 0.f && p < 1.f)) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({W, A, B, dA, dB}));
+  if (M > 0) TRY(check_ptrs({X, dY, keep}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  const Layout L = make_layout(LORA_OP_DROPOUT_BWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* Xm = static_cast<char*>(ws) + L.xm;
+  if (M > 0)
+    HIPTRY(timed(K_MASK, 0, (2.0 * elem_bytes(dtype) + 0.125) * M * d_in, st,
+                 [&] { return launch_mask_copy(elem_bytes(dtype), X, keep, Xm, M * d_in, st); }));
+  return backward_impl(dtype, M, d_in, d_out, r, scale / (1.f - p), X, W, nullptr, A, B, nullptr, dY, dX, dA, dB,
+                       ws, L, st, nullptr, Xm, keep);
 }
 
 int lora_merge(int dtype, int64_t d_out, int64_t d_in, int64_t r, float scale, const void* W, const void* A,

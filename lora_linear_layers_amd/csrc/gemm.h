@@ -56,7 +56,8 @@ enum Epi : int {
   EPI_ROPE = 3,        // rotate (n, n+64) pairs of 128-wide heads, then store
   EPI_PARTIAL = 4,     // fp32 partial slab of split z: C[z][m, n] = acc
   EPI_ADD = 5,         // C[m, n] = alpha * acc + Cin[m, n]  (type T; C may be Cin)
-  EPI_SWIGLU = 6       // whole-tile kernel only: gate/up pair -> silu(g) * u (see gemm_w4.h)
+  EPI_SWIGLU = 6,      // whole-tile kernel only: gate/up pair -> silu(g) * u (see gemm_w4.h)
+  EPI_ADD_MASKED = 7   // C[m, n] = keep(m, n) ? alpha * acc + Cin[m, n] : Cin[m, n]
 };
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
@@ -97,6 +98,9 @@ struct GemmArgs {
   int64_t ldb2u, k2_split;
   void* cg;
   void* cu;
+  // EPI_ADD_MASKED: keep bit of (m, n) = bit n % 8 of mask[m * mask_ld + n / 8]
+  const uint8_t* mask;
+  int64_t mask_ld;
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {
@@ -653,7 +657,10 @@ gemm_kernel(const GemmArgs p) {
           const int64_t col = cbase + j * 16;
           if (col >= p.n_store) continue;
           float y = acc[i][j][v] * p.alpha;
-          if constexpr (EPI == EPI_ADD) {
+          if constexpr (EPI == EPI_ADD_MASKED) {
+            if (!((p.mask[row * p.mask_ld + (col >> 3)] >> (col & 7)) & 1)) y = 0.f;
+          }
+          if constexpr (EPI == EPI_ADD || EPI == EPI_ADD_MASKED) {
             y += load_in<T>(p.cin, row * p.ldcin + col);
             store_out<T>(p.c, row * p.ldc + col, y);
           }

@@ -66,6 +66,7 @@ TileShape gemm_tile(GemmKind k) {
     case G_NF4_MED_NT_PARTIAL:
     case G_NF4_MED_NN_PARTIAL:
     case G_BF16_MED_NN_ADD:
+    case G_BF16_MED_NN_ADD_MASKED:
       return {128, 128};
     case G_F32_PANEL_NT_STORE:
     case G_F32_PANEL_NT_STORE_T:
@@ -82,6 +83,7 @@ TileShape gemm_tile(GemmKind k) {
     case G_F32_NT_ROPE:
     case G_F32_NN_STORE:
     case G_F32_NN_ADD:
+    case G_F32_NN_ADD_MASKED:
       return {64, 128};
     default:
       return {0, 0};
@@ -124,6 +126,8 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
       if (!whole_tiles(a, splits)) return hipErrorInvalidValue;
       return run_whole<false, EPI_SWIGLU>(a, st);
     case G_F32_NN_ADD: return run<float, 64, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
+    case G_BF16_MED_NN_ADD_MASKED: return run<bf, 128, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);
+    case G_F32_NN_ADD_MASKED: return run<float, 64, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -423,6 +427,53 @@ hipError_t launch_add_into(int elem_bytes, void* dst, const void* src, int64_t n
   else
     hipLaunchKernelGGL(add_into_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (float*)dst,
                        (const float*)src, n);
+  return hipGetLastError();
+}
+
+// The adapter's input under LoRA dropout: out = X where the keep bit is set,
+// else 0 (exact: no scaling here).  One mask byte and 8 elements per thread
+// and iteration; bit b of byte e keeps element 8 e + b.
+__global__ void mask_copy_bf16_kernel(const u32x4* __restrict__ X, const uint8_t* __restrict__ keep,
+                                      u32x4* __restrict__ out, int64_t n8) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t k = keep[e];
+    u32x4 v = X[e];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      v[q] &= (((k >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) | (((k >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+    out[e] = v;
+  }
+}
+
+__global__ void mask_copy_f32_kernel(const float4* __restrict__ X, const uint8_t* __restrict__ keep,
+                                     float4* __restrict__ out, int64_t n8) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t k = keep[e];
+    float4 a = X[2 * e], b = X[2 * e + 1];
+    a.x = (k & 1u) ? a.x : 0.f;
+    a.y = (k & 2u) ? a.y : 0.f;
+    a.z = (k & 4u) ? a.z : 0.f;
+    a.w = (k & 8u) ? a.w : 0.f;
+    b.x = (k & 16u) ? b.x : 0.f;
+    b.y = (k & 32u) ? b.y : 0.f;
+    b.z = (k & 64u) ? b.z : 0.f;
+    b.w = (k & 128u) ? b.w : 0.f;
+    out[2 * e] = a;
+    out[2 * e + 1] = b;
+  }
+}
+
+hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, void* out, int64_t n,
+                            hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(mask_copy_bf16_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, st, (const u32x4*)X, keep,
+                       (u32x4*)out, n8);
+  else
+    hipLaunchKernelGGL(mask_copy_f32_kernel, dim3(grid_for(n8, 256)), dim3(256), 0, st, (const float4*)X, keep,
+                       (float4*)out, n8);
   return hipGetLastError();
 }
 

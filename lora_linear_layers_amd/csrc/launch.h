@@ -43,6 +43,8 @@ enum GemmKind : int {
   G_BF16_MED_NN_ADD,
   G_F32_NN_ADD,
   G_BF16_WHOLE_SWIGLU,
+  G_BF16_MED_NN_ADD_MASKED,
+  G_F32_NN_ADD_MASKED,
   G_KIND_COUNT
 };
 
@@ -118,6 +120,11 @@ hipError_t launch_swiglu_apply(int elem_bytes, const void* G, const void* U, voi
 hipError_t launch_swiglu_grad(int elem_bytes, const void* dH, const void* G, const void* U, void* dG, void* dU,
                               int64_t n, hipStream_t st);
 hipError_t launch_add_into(int elem_bytes, void* dst, const void* src, int64_t n, hipStream_t st);
+
+// out = X with the elements whose keep bit is clear set to 0 (n elements,
+// n % 8 == 0, bit b of keep[e] is element 8 e + b).
+hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, void* out, int64_t n,
+                            hipStream_t st);
 
 // blocks x 256 threads of the MFMA-rate kernel (iters rounds of 8 MFMAs per
 // wave); out [blocks * 256] receives one float per thread.

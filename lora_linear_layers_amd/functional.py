@@ -143,6 +143,43 @@ def nf4_dequant(codes, absmax, table16, n: int, blocksize: int = 64):
     return out
 
 
+def lora_dropout_fwd(X, W, A, B, scale: float, p: float, keep, Y=None, ws=None):
+    """Y = X W^T + scale (D A^T) B^T, D = X * keep / (1 - p); keep is the packed
+    uint8 bit mask [M, d_in / 8] (bit b of byte (i, j) keeps element (i, 8 j + b))."""
+    L._contig(X, W, A, B, keep, Y)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    _check_keep(keep, M, d_in)
+    dt = L._dtype_code(X)
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    ws = L._workspace(L.OP_DROPOUT_FWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_dropout_fwd", L.lib().lora_dropout_fwd(
+        dt, M, d_in, d_out, r, float(scale), float(p), L._ptr(keep), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B),
+        L._ptr(Y), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return Y
+
+
+def lora_dropout_bwd(X, W, A, B, scale: float, p: float, keep, dY, need_dX: bool = True, ws=None):
+    """(dX or None, dA fp32, dB fp32) of lora_dropout_fwd with the same keep mask."""
+    L._contig(X, W, A, B, keep, dY)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    _check_keep(keep, M, d_in)
+    dt = L._dtype_code(X)
+    dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+    dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+    dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+    ws = L._workspace(L.OP_DROPOUT_BWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_dropout_bwd", L.lib().lora_dropout_bwd(
+        dt, M, d_in, d_out, r, float(scale), float(p), L._ptr(keep), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B),
+        L._ptr(dY), L._ptr(dX), L._ptr(dA), L._ptr(dB), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return dX, dA, dB
+
+
+def _check_keep(keep, M, d_in):
+    if keep.dtype != torch.uint8 or keep.numel() != M * d_in // 8:
+        raise ValueError("keep must be a uint8 bit mask of M * d_in / 8 bytes")
+
+
 def lora_merge(W, A, B, scale: float, out=None, ws=None):
     """W + scale B A in W's dtype (out may be W itself); -scale unmerges."""
     L._contig(W, A, B, out)

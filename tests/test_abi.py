@@ -248,3 +248,24 @@ def test_swiglu_validation_and_workspace(lib):
     assert bwd(_members(2, d_out=64), dH=None) == ENULL
     assert bwd(_members(2, d_out=64, dA=None)) == ENULL
     assert bwd(_members(2, d_out=64), dX=P + 4) == EALIGN
+
+
+def test_dropout_validation_and_workspace(lib):
+    def fwd(p=0.1, keep=P, X=P, M=16, wsb=1 << 30):
+        return lib.lora_dropout_fwd(1, M, 64, 64, 8, 1.0, p, keep, X, P, P, P, P, P, wsb, None)
+    assert fwd(p=1.0) == ESHAPE
+    assert fwd(p=-0.1) == ESHAPE
+    assert fwd(p=float("nan")) == ESHAPE
+    assert fwd(keep=None) == ENULL
+    assert fwd(keep=P + 8) == EALIGN
+    assert fwd(wsb=10) == EWS
+
+    def bwd(dX=P, dA=P, keep=P):
+        return lib.lora_dropout_bwd(1, 16, 64, 64, 8, 1.0, 0.1, keep, P, P, P, P, P, dX, dA, P, P, 1 << 30, None)
+    assert bwd(keep=None) == ENULL
+    assert bwd(dA=None) == ENULL
+    assert bwd(dX=P + 2) == EALIGN
+    f = lib.lora_workspace_bytes
+    # the masked copy of X joins the plain layer's workspace
+    assert f(_lib.OP_DROPOUT_FWD, 1, 4096, 4096, 4096, 16) >= f(_lib.OP_FWD, 1, 4096, 4096, 4096, 16) + 4096 * 4096 * 2
+    assert f(_lib.OP_DROPOUT_BWD, 0, 4096, 4096, 4096, 16) >= f(_lib.OP_BWD, 0, 4096, 4096, 4096, 16) + 4096 * 4096 * 4
