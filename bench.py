@@ -349,6 +349,29 @@ def next_rows(work, reps=10):
     del ws, Gs, Us
     if not cfg.nf4:
         it = pair[0]
+        # LoRA dropout (p = 0.05) on the gate projection vs the plain layer
+        p = 0.05
+        g = torch.Generator(device=X.device).manual_seed(3407)
+        keep = (torch.rand(M, k // 8, 8, generator=g, device=X.device) >= p).to(torch.uint8)
+        keep = (keep << torch.arange(8, dtype=torch.uint8, device=X.device)).sum(-1).to(torch.uint8).contiguous()
+        dws = torch.empty(max(L.workspace_bytes(op, L.LORA_BF16, M, k, d, cfg.r)
+                              for op in (L.OP_DROPOUT_FWD, L.OP_DROPOUT_BWD)), dtype=torch.uint8, device=X.device)
+        one_fwd = 2.0 * M * (d * k + cfg.r * (d + k))
+        one_bwd = 2.0 * M * (d * k + 2 * cfg.r * (d + k))
+        dr = {"shape": f"{it['p'].name} {k}->{d}, M={M}, r={cfg.r}, p={p}"}
+        dr["fwd_ms"] = _time_ms(lambda: L.lora_dropout_fwd(X, it["W"], it["A"], it["B"], s, p, keep, Y=it["Y"],
+                                                            ws=dws), reps)
+        dr["bwd_ms"] = _time_ms(lambda: L.lora_dropout_bwd(X, it["W"], it["A"], it["B"], s, p, keep, it["dY"],
+                                                            ws=dws), reps)
+        dr["plain_fwd_ms"] = _time_ms(lambda: L.lora_linear_fwd(X, it["W"], it["A"], it["B"], s, Y=it["Y"], ws=dws),
+                                      reps)
+        dr["plain_bwd_ms"] = _time_ms(lambda: L.lora_linear_bwd(X, it["W"], it["A"], it["B"], s, it["dY"], ws=dws,
+                                                                out=(it["dX"], it["dA"], it["dB"])), reps)
+        for key, fl in (("fwd_ms", one_fwd), ("bwd_ms", one_bwd), ("plain_fwd_ms", one_fwd),
+                        ("plain_bwd_ms", one_bwd)):
+            dr[key.replace("_ms", "_tflops")] = round(fl / (dr[key]["median"] * 1e-3) / 1e12, 1)
+        out["dropout"] = dr
+        del dws, keep
         Wm = torch.empty_like(it["W"])
         mws = torch.empty(max(L.workspace_bytes(L.OP_MERGE, L.LORA_BF16, 0, k, d, cfg.r), 256),
                           dtype=torch.uint8, device=X.device)

@@ -116,14 +116,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <typename T>
-__device__ __forceinline__ float load_in(const void* c, int64_t idx) {
-  if constexpr (sizeof(T) == 2)
-    return static_cast<float>(__builtin_bit_cast(__bf16, reinterpret_cast<const uint16_t*>(c)[idx]));
-  else
-    return reinterpret_cast<const float*>(c)[idx];
-}
-
-template <typename T>
 __device__ __forceinline__ void store_out(void* c, int64_t idx, float v) {
   if constexpr (sizeof(T) == 2)
     reinterpret_cast<uint16_t*>(c)[idx] = f2bf(v);
@@ -645,6 +637,64 @@ gemm_kernel(const GemmArgs p) {
           store_out<T>(p.c, row * p.ldc + col + 64, z2 * cs + z1 * sn);
         }
       }
+  } else if constexpr (EPI == EPI_ADD || EPI == EPI_ADD_MASKED) {
+    // Staged through LDS in blocks of RB rows (fp32, row pitch BN + 4 floats:
+    // the 16x16 output layout writes without bank conflicts), then each thread
+    // adds 8 consecutive outputs to the addend with 16-byte accesses and one
+    // keep byte per 8 columns (n_store is a multiple of 8).
+    constexpr int PITCH = BN + 4;
+    constexpr int RB0 = C::LDS / (PITCH * 4);
+    constexpr int RB = RB0 >= BM ? BM : (RB0 / C::TM) * C::TM;
+    static_assert(RB >= C::TM, "the LDS holds at least one wave's rows");
+    float* stile = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    for (int rb = 0; rb < BM; rb += RB) {
+      if (wm * C::TM >= rb && wm * C::TM < rb + RB) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              stile[(wm * C::TM + i * 16 + 4 * g + v - rb) * PITCH + wn * C::TN + j * 16 + l16] =
+                  acc[i][j][v] * p.alpha;
+      }
+      __syncthreads();
+      const int rows_here = BM - rb < RB ? BM - rb : RB;  // the tile's last block may be shorter
+      for (int c = tid; c < rows_here * (BN / 8); c += NT) {
+        const int lr = c / (BN / 8), lc = (c % (BN / 8)) * 8;
+        const int64_t row = m0 + rb + lr, col = n0 + lc;
+        if (row >= p.m_store || col >= p.n_store) continue;
+        const float4 y0 = *reinterpret_cast<const float4*>(stile + lr * PITCH + lc);
+        const float4 y1 = *reinterpret_cast<const float4*>(stile + lr * PITCH + lc + 4);
+        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        uint32_t keep = 0xFFu;
+        if constexpr (EPI == EPI_ADD_MASKED) keep = p.mask[row * p.mask_ld + (col >> 3)];
+        if constexpr (BF16) {
+          const u32x4 in = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.cin) + row * p.ldcin + col);
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float lo = __builtin_bit_cast(float, in[q] << 16), hi = __builtin_bit_cast(float, in[q] & 0xFFFF0000u);
+            if ((keep >> (2 * q)) & 1u) lo += y[2 * q];
+            if ((keep >> (2 * q + 1)) & 1u) hi += y[2 * q + 1];
+            o[q] = pack_bf16x2(lo, hi);
+          }
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.c) + row * p.ldc + col) = o;
+        } else {
+          const float* in = reinterpret_cast<const float*>(p.cin) + row * p.ldcin + col;
+          float4 a = *reinterpret_cast<const float4*>(in), b = *reinterpret_cast<const float4*>(in + 4);
+          float o[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if ((keep >> e) & 1u) o[e] += y[e];
+          float* out = reinterpret_cast<float*>(p.c) + row * p.ldc + col;
+          *reinterpret_cast<float4*>(out) = make_float4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<float4*>(out + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+      }
+      __syncthreads();
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -656,14 +706,7 @@ gemm_kernel(const GemmArgs p) {
         for (int j = 0; j < FN; ++j) {
           const int64_t col = cbase + j * 16;
           if (col >= p.n_store) continue;
-          float y = acc[i][j][v] * p.alpha;
-          if constexpr (EPI == EPI_ADD_MASKED) {
-            if (!((p.mask[row * p.mask_ld + (col >> 3)] >> (col & 7)) & 1)) y = 0.f;
-          }
-          if constexpr (EPI == EPI_ADD || EPI == EPI_ADD_MASKED) {
-            y += load_in<T>(p.cin, row * p.ldcin + col);
-            store_out<T>(p.c, row * p.ldc + col, y);
-          }
+          const float y = acc[i][j][v] * p.alpha;
           if constexpr (EPI == EPI_STORE || EPI == EPI_STORE_BOTH) store_out<T>(p.c, row * p.ldc + col, y);
           if constexpr (EPI == EPI_STORE_T || EPI == EPI_STORE_BOTH) store_out<T>(p.ct, col * p.ldct + row, y);
         }
