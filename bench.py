@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--call-reps", type=int, default=10,
                     help="HIP-event repetitions of each call for the per-call median/p10/p90 (0 = skip)")
     ap.add_argument("--no-small-token", action="store_true", help="skip the few-token HBM sweep")
+    ap.add_argument("--no-wt", action="store_true",
+                    help="do not keep W^T of the frozen weights (the backward then transposes W per call)")
     ap.add_argument("--no-group", action="store_true",
                     help="run projections that share X one by one instead of as one group")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
@@ -85,6 +87,7 @@ KIND_OF = {
     "transpose_pad_kernel": "transpose_pad",
     "rope_inverse_kernel": "rope_inverse",
     "copy_rows_kernel": "copy_rows",
+    "transpose_tile_kernel": "transpose_w",
 }
 
 
@@ -137,7 +140,7 @@ def traffic_from(fetch_csv, write_csv, cfg_id):
 class Workload:
     """Device tensors and preallocated outputs for every projection of a config."""
 
-    def __init__(self, cfg, device="cuda", group=True):
+    def __init__(self, cfg, device="cuda", group=True, keep_wt=True):
         import torch
 
         import lora_linear_layers_amd as L
@@ -190,9 +193,13 @@ class Workload:
                     m["codes"], m["absmax"] = it["codes"], it["absmax"]
                 else:
                     m["W"] = it["W"]
+                    if keep_wt and cfg.dtype == "bf16":
+                        # the frozen weight's transpose, made once: the backward's
+                        # input gradient reads it (outside the timed steps)
+                        m["W_t"] = L.lora_transpose(it["W"])
                 ms.append(m)
             self.members.append(ms)
-            if len(grp) > 1:
+            if len(grp) > 1 or any("W_t" in m for m in ms):
                 arr = L.functional._group_members(grp[0]["X"], ms)
                 for bwd in (0, 1):
                     wsmax = max(wsmax, int(L.lib().lora_group_workspace_bytes(bwd, dt, M, grp[0]["p"].d_in,
@@ -215,10 +222,13 @@ class Workload:
             f += 2.0 * M * (p.d_in * p.d_out + (2 if bwd else 1) * r * (p.d_in + p.d_out))
         return f
 
+    def _as_group(self, gi):
+        return len(self.groups[gi]) > 1 or any("W_t" in m for m in self.members[gi])
+
     def fwd(self, gi):
         L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
         grp, ms = self.groups[gi], self.members[gi]
-        if len(grp) > 1:
+        if self._as_group(gi):
             L.lora_group_fwd(grp[0]["X"], ms, *self._rope_args(), table16=self.table if cfg.nf4 else None, ws=ws,
                              Ys=[it["Y"] for it in grp])
             return
@@ -236,7 +246,7 @@ class Workload:
     def bwd(self, gi):
         L, cfg, ws, s = self.L, self.cfg, self.ws, self.cfg.scale
         grp, ms = self.groups[gi], self.members[gi]
-        if len(grp) > 1:
+        if self._as_group(gi):
             L.lora_group_bwd(grp[0]["X"], ms, [it["dY"] for it in grp], *self._rope_args(),
                              table16=self.table if cfg.nf4 else None, ws=ws,
                              outs=[(it["dX"], it["dA"], it["dB"]) for it in grp])
@@ -568,7 +578,7 @@ def main():
     cfg = CONFIGS[args.config]
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    work = Workload(cfg, device=dev, group=not args.no_group)
+    work = Workload(cfg, device=dev, group=not args.no_group, keep_wt=not args.no_wt)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -651,6 +661,7 @@ def main():
                    "projections": [f"{p.name} {p.d_in}->{p.d_out}{' +rope' if p.rope else ''}"
                                    for p in cfg.projections],
                    "x_groups": [[it["p"].name for it in grp] for grp in work.groups],
+                   "frozen_w_transposed": (not args.no_wt) and cfg.dtype == "bf16" and not cfg.nf4,
                    "useful_tflop_per_step": round(flop / 1e12, 4), "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "kernels": kernels,

@@ -41,6 +41,7 @@ from .functional import (  # noqa: F401
     lora_qk_rope_fwd,
     lora_swiglu_bwd,
     lora_swiglu_fwd,
+    lora_transpose,
     nf4_dequant,
     nf4_lora_linear_bwd,
     nf4_lora_linear_fwd,

@@ -30,7 +30,7 @@ class GroupMember(ctypes.Structure):
     """struct lora_group_member of the C ABI."""
     _fields_ = [("d_out", _i64), ("r", _i64), ("scale", _f32), ("rope", _int), ("W", _vp), ("W_nf4", _vp),
                 ("absmax", _vp), ("A", _vp), ("B", _vp), ("Y", _vp), ("dY", _vp), ("dX", _vp), ("dA", _vp),
-                ("dB", _vp)]
+                ("dB", _vp), ("W_t", _vp)]
 
 
 _mp = ctypes.POINTER(GroupMember)
@@ -64,6 +64,7 @@ _SIGS = {
     "lora_dropout_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _sz, _vp], _int),
     "lora_mfma_rate": ([_int, _int, _vp, _vp], _int),
+    "lora_transpose": ([_vp, _i64, _i64, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),
     "lora_profile_end": ([], _int),
     "lora_profile_kinds": ([], _int),

@@ -59,11 +59,18 @@ struct Layout {
   int splits_main = 1;  // contraction splits of the Y (forward) or dX (backward) GEMM
   int64_t ksplit_main = 0;
   bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
+  // dX on whole tiles: W^T [d_in, d_out] and A^T [d_in, r8] in the workspace,
+  // and the input gradient runs through the forward-orientation kernel
+  bool dx_nt = false;
+  size_t wt = 0, at = 0;
   int splits_dA = 1, splits_dB = 1;
   int64_t ksplit_dA = 0, ksplit_dB = 0;
   int splits_p = 1, splits_q = 1;  // bf16 rank-r panels: P = X A^T, Q = G B
   int64_t ksplit_p = 0, ksplit_q = 0;
 };
+
+// 256x256 tiles when they still give at least one tile per CU, else 128x128.
+bool use_big(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
 
 // Split of the contraction of a bf16 rank-r panel (256 x 64 tiles): about 1.5
 // workgroups per CU, at most 32 splits, each a multiple of 64 and at least 8
@@ -117,7 +124,8 @@ void main_split(int64_t M, int64_t N, int64_t K, int* splits, int64_t* ksplit) {
   *splits = (int)cdiv(K, ks);
 }
 
-Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+// have_wt: the caller supplies W^T, so the backward needs no room for it.
+Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, bool have_wt = false) {
   Layout L;
   const size_t eb = elem_bytes(dtype);
   L.r8 = rup(r, 8);
@@ -156,6 +164,13 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
       main_split(M, d_out, d_in, &L.splits_main, &L.ksplit_main);
   }
   const size_t sp = L.splits_main > 1 ? size_t(L.splits_main) * M * (bwd ? d_in : d_out) * 4 : 0;
+  const bool nf4op = op == LORA_OP_NF4_BWD;
+  if (bwd && eb == 2 && L.splits_main == 1 && (!nf4op || L.dequant) && M % 256 == 0 && d_in % 256 == 0 &&
+      d_out % 64 == 0 && use_big(M, d_in)) {
+    L.dx_nt = true;
+    if (!have_wt) L.wt = take(size_t(d_in) * d_out * 2);
+    L.at = take(size_t(d_in) * L.r8 * 2);
+  }
   if (!bwd) {
     L.p = take(size_t(M) * L.r8 * eb);
     if (sp) L.spart = take(sp);
@@ -230,6 +245,7 @@ enum ProfKind : int {
   K_FINISH,
   K_SWIGLU,
   K_MASK,
+  K_TRANSPOSE_W,
   K_PROF_COUNT
 };
 
@@ -248,7 +264,7 @@ const char* kind_name(int k) {
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
       "copy_rows",                  "split_finish",               "swiglu_elementwise",
-      "dropout_mask_copy"};
+      "dropout_mask_copy",          "transpose_w"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -286,8 +302,6 @@ hipError_t gemm(GemmKind k, const GemmArgs& a, int splits, hipStream_t st, doubl
 // ---------------------------------------------------------------------------
 // tile choice
 // ---------------------------------------------------------------------------
-// 256x256 tiles when they still give at least one tile per CU, else 128x128.
-bool use_big(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
 
 GemmArgs blank() {
   GemmArgs a;
@@ -432,7 +446,8 @@ struct PanelSlices {
 int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
                   const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, const void* dY,
                   void* dX, float* dA, float* dB, void* ws, const Layout& L, hipStream_t st,
-                  const PanelSlices* ov = nullptr, const void* Xa = nullptr, const uint8_t* keep = nullptr) {
+                  const PanelSlices* ov = nullptr, const void* Xa = nullptr, const uint8_t* keep = nullptr,
+                  const void* Wt_in = nullptr) {
   // LoRA dropout: Xa is the adapter's (masked) input and `keep` the mask that
   // the rank-r term of dX passes through; X itself still feeds the base path
   const void* Xp = Xa ? Xa : X;
@@ -501,7 +516,29 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   }
   // dX = [G | Qs] [W ; A]; with a dropout mask the rank-r term is added
   // separately, masked: dX = G W, then dX += keep * (Qs A)
-  if (dX) {
+  if (dX && L.dx_nt) {
+    // W read with its contraction rows costs the whole-tile kernel ~12 % more
+    // than the same product read as W^T, which one transposing pass gives
+    const void* Wt = Wt_in;
+    uint16_t* At = reinterpret_cast<uint16_t*>(w + L.at);
+    if (!Wt) {
+      uint16_t* wt = reinterpret_cast<uint16_t*>(w + L.wt);
+      HIPTRY(timed(K_TRANSPOSE_W, 0, 4.0 * ko * ki, st, [&] {
+        return launch_transpose_tile(static_cast<const uint16_t*>(W), d_in, d_out, d_in, wt, d_out, d_out, st);
+      }));
+      Wt = wt;
+    }
+    HIPTRY(timed(K_TRANSPOSE_W, 0, 2.0 * rr * ki + 2.0 * ki * L.r8, st, [&] {
+      return launch_transpose_tile(static_cast<const uint16_t*>(A), d_in, r, d_in, At, L.r8, L.r8, st);
+    }));
+    GemmArgs a = blank();
+    a.a1 = G; a.lda1 = d_out; a.b1 = Wt; a.ldb1 = d_out; a.K1 = d_out;
+    a.a2 = Qs; a.lda2 = ldqs; a.b2 = At; a.ldb2 = L.r8; a.K2 = keep ? 0 : r;
+    a.m_load = M; a.m_store = M; a.n_load = d_in; a.n_store = d_in;
+    a.c = dX; a.ldc = d_in;
+    HIPTRY(gemm(G_BF16_BIG_NT_STORE, a, 1, st, 2 * Md * ki * (ko + rr),
+                (Md * ko + Md * rr + rr * ki + Md * ki + ko * ki) * e));
+  } else if (dX) {
     GemmArgs a = blank();
     a.a1 = G; a.lda1 = d_out; a.b1 = W; a.ldb1 = d_in; a.K1 = d_out;
     a.a2 = Qs; a.lda2 = ldqs; a.b2 = A; a.ldb2 = d_in; a.K2 = keep ? 0 : r;
@@ -533,14 +570,14 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     } else {
       HIPTRY(gemm(k, a, 1, st, flop, bytes));
     }
-    if (keep) {
-      GemmArgs b = blank();
-      b.a1 = Qs; b.lda1 = ldqs; b.b1 = A; b.ldb1 = d_in; b.K1 = r;
-      b.m_load = M; b.m_store = M; b.n_load = d_in; b.n_store = d_in;
-      b.c = dX; b.ldc = d_in; b.cin = dX; b.ldcin = d_in; b.mask = keep; b.mask_ld = d_in / 8;
-      HIPTRY(gemm(f32 ? G_F32_NN_ADD_MASKED : G_BF16_MED_NN_ADD_MASKED, b, 1, st, 2 * Md * ki * rr,
-                  (Md * rr + rr * ki + 2 * Md * ki) * e + Md * ki / 8));
-    }
+  }
+  if (dX && keep) {
+    GemmArgs b = blank();
+    b.a1 = Qs; b.lda1 = ldqs; b.b1 = A; b.ldb1 = d_in; b.K1 = r;
+    b.m_load = M; b.m_store = M; b.n_load = d_in; b.n_store = d_in;
+    b.c = dX; b.ldc = d_in; b.cin = dX; b.ldcin = d_in; b.mask = keep; b.mask_ld = d_in / 8;
+    HIPTRY(gemm(f32 ? G_F32_NN_ADD_MASKED : G_BF16_MED_NN_ADD_MASKED, b, 1, st, 2 * Md * ki * rr,
+                (Md * rr + rr * ki + 2 * Md * ki) * e + Md * ki / 8));
   }
   const GemmKind ksplit = f32 ? G_F32_SPLIT_NN_PARTIAL : G_BF16_SPLIT_NN_PARTIAL;
   // dB^T = Pt G  -> partials [splits][r8, d_out] -> dB [d_out, r]
@@ -614,7 +651,8 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
   for (int g = 0; g < n; ++g) {
     G.off[g] = G.rt;
     G.rt += rup(mb[g].r, 8);
-    G.mem[g] = make_layout(member_op(bwd, mb[g]), dtype, M, d_in, mb[g].d_out, mb[g].r);
+    G.mem[g] = make_layout(member_op(bwd, mb[g]), dtype, M, d_in, mb[g].d_out, mb[g].r,
+                           mb[g].W_t != nullptr && !mb[g].W_nf4);
     if (G.mem[g].total > shared) shared = G.mem[g].total;
   }
   size_t off = 0;
@@ -664,6 +702,7 @@ int check_group(bool bwd, int dtype, int64_t M, int64_t d_in, int n, const lora_
       TRY(check_ptrs({m.W}));
     }
     if (m.rope) TRY(check_rope(head_dim, m.d_out, M, pos, cosc, sinc, max_pos));
+    if (m.W_t && !aligned16(m.W_t)) return LORA_ERR_ALIGN;
     if (!bwd) {
       if (M > 0) TRY(check_ptrs({m.Y}));
     } else {
@@ -739,7 +778,8 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
     const Nf4W q{m.W_nf4, m.absmax, table16};
     const PanelSlices ov{Pt + G.off[g] * G.M8, Qs + G.off[g], G.rt, Qt + G.off[g] * G.M8};
     TRY(backward_impl(dtype, M, d_in, m.d_out, m.r, m.scale, X, m.W, m.W_nf4 ? &q : nullptr, m.A, m.B,
-                      m.rope ? rope : nullptr, m.dY, m.dX, m.dA, m.dB, sh, G.mem[g], st, share ? &ov : nullptr));
+                      m.rope ? rope : nullptr, m.dY, m.dX, m.dA, m.dB, sh, G.mem[g], st, share ? &ov : nullptr,
+                      nullptr, nullptr, G.mem[g].dx_nt && !m.W_nf4 ? m.W_t : nullptr));
   }
   if (!share) return LORA_OK;
   // dA of every member in one pass over X: Qt X -> partials [splits][rt, d_in]
@@ -829,6 +869,7 @@ int check_swiglu(bool bwd, int dtype, int64_t M, int64_t d_in, const lora_group_
     }
     if (bwd) TRY(check_ptrs({m.dA, m.dB}));
     if (!bwd && m.Y && !aligned16(m.Y)) return LORA_ERR_ALIGN;
+    if (m.W_t && !aligned16(m.W_t)) return LORA_ERR_ALIGN;
   }
   return LORA_OK;
 }
@@ -1194,6 +1235,18 @@ int lora_swiglu_bwd(int dtype, int64_t M, int64_t d_in, const lora_group_member*
   TRY(check_device());
   return swiglu_backward(dtype, M, d_in, members, X, table16, dH, G, U, dX, ws, S,
                          static_cast<hipStream_t>(stream));
+}
+
+int lora_transpose(const void* src, int64_t rows, int64_t cols, void* dst, void* stream) {
+  if (rows < 8 || cols < 8 || rows % 8 || cols % 8 || rows >= kMaxDim || cols >= kMaxDim) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({src, dst}));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIPTRY(timed(K_TRANSPOSE_W, 0, 4.0 * rows * cols, st, [&] {
+    return launch_transpose_tile(static_cast<const uint16_t*>(src), cols, rows, cols, static_cast<uint16_t*>(dst), rows,
+                                 rows, st);
+  }));
+  return LORA_OK;
 }
 
 int lora_mfma_rate(int iters, int blocks, float* out, void* stream) {

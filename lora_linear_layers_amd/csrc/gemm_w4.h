@@ -104,9 +104,11 @@ gemm_w4_kernel(const GemmArgs p) {
   const char* gb2 = reinterpret_cast<const char*>(p.b2) + (B_NN ? n0 * 2 : nb0 * p.ldb2 * 2);
   const char* gb1u = SW ? reinterpret_cast<const char*>(p.b1u) + nb0 * p.ldb1 * 2 : gb1;
   const char* gb2u = SW ? reinterpret_cast<const char*>(p.b2u) + nb0 * p.ldb2u * 2 : gb2;
-  const uint32_t vb1 = B_NN ? (uint32_t)(kc * p.ldb1 * 2 + (lt >> 3) * 16)
+  // B_NN: lane lt moves chunk lt & 31 (8 columns) of contraction rows
+  // (lt >> 5) + 8 i, i < 8: each load instruction covers two whole 512-byte rows
+  const uint32_t vb1 = B_NN ? (uint32_t)((lt >> 5) * p.ldb1 * 2 + (lt & 31) * 16)
                             : (uint32_t)((lt >> 3) * p.ldb1 * 2 + (lt & 7) * 16);
-  const uint32_t vb2 = B_NN ? (uint32_t)(kc * p.ldb2 * 2 + (lt >> 3) * 16)
+  const uint32_t vb2 = B_NN ? (uint32_t)((lt >> 5) * p.ldb2 * 2 + (lt & 31) * 16)
                             : (uint32_t)((lt >> 3) * p.ldb2 * 2 + (lt & 7) * 16);
   // segment 2 of B_NN: rows at or beyond K2 lie past the resource's end
   const int nrecb2 = B_NN ? (int)(p.K2 * p.ldb2 * 2 - n0 * 2) : BIG;
@@ -115,8 +117,8 @@ gemm_w4_kernel(const GemmArgs p) {
   // address inside the loop, whose wait drains every LDS operation)
   const uint32_t isa1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda1 * 2));
   const uint32_t isa2 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda2 * 2));
-  const uint32_t isb1 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(p.ldb1 * 2) : (uint32_t)(32 * p.ldb1 * 2));
-  const uint32_t isb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(p.ldb2 * 2) : (uint32_t)(32 * p.ldb2 * 2));
+  const uint32_t isb1 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(8 * p.ldb1 * 2) : (uint32_t)(32 * p.ldb1 * 2));
+  const uint32_t isb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(8 * p.ldb2 * 2) : (uint32_t)(32 * p.ldb2 * 2));
   const int64_t kstb1 = B_NN ? (int64_t)BK * p.ldb1 * 2 : (int64_t)BK * 2;
   const uint32_t kstb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(BK * p.ldb2 * 2) : (uint32_t)(BK * 2));
   const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
@@ -207,9 +209,15 @@ gemm_w4_kernel(const GemmArgs p) {
   // ---- registers -> LDS buffer st ----
   // rows (lt >> 3) + 32 i all have (row >> 1) & 7 = (lt >> 4) & 7
   const uint32_t wr_off = (uint32_t)(lt >> 3) * 128 + (uint32_t)(((lt & 7) ^ ((lt >> 4) & 7)) << 4);
-  // transposed B: row nb*8 + j has (row >> 1) & 7 = 4 (nb & 1) + (j >> 1)
-  const uint32_t nn_wbase = (uint32_t)B_BASE + (uint32_t)(lt >> 3) * 8 * 128 +
-                            (uint32_t)(((lt & 7) ^ (((lt >> 3) & 1) << 2)) << 4);
+  // B_NN tile in LDS: [64 contraction rows][256 columns], 512-byte rows, the
+  // 16-byte chunk c of row k stored at chunk c ^ nn_swz(k) (nn_swz(k) = 2 f(k),
+  // f(k) = (k & 3) | ((k >> 1) & 4)), which keeps both the whole-row writes
+  // and the transposing fragment reads free of bank conflicts.  Row
+  // (lt >> 5) + 8 i has nn_swz = 2 ((lt >> 5) & 3) ^ 8 (i & 1).
+  const uint32_t nn_w0 = (uint32_t)B_BASE + (uint32_t)(lt >> 5) * 512 +
+                         (uint32_t)(((lt & 31) ^ (2 * ((lt >> 5) & 3))) << 4);
+  const uint32_t nn_w1 = (uint32_t)B_BASE + (uint32_t)(lt >> 5) * 512 +
+                         (uint32_t)(((lt & 31) ^ (2 * ((lt >> 5) & 3)) ^ 8) << 4);
   // one 16-byte LDS write of chunk i of the staged A / B tile into buffer st
   auto st_a = [&](int st, auto bsel, int i) {
     constexpr int b = decltype(bsel)::value;
@@ -220,19 +228,8 @@ gemm_w4_kernel(const GemmArgs p) {
     if constexpr (!B_NN) {
       *reinterpret_cast<u32x4*>(smem + B_BASE + wr_off + st * B_STAGE + i * 32 * 128) = sb[b][i];
     } else {
-      // 8x8 transpose of 16-bit values: column i of the block (n = 8 nb + i)
-      // becomes chunk kbk of LDS row n, stored at byte
-      // nn_wbase ^ ((i >> 1) << 4) plus i * 128.  The empty asm keeps the
-      // addresses from being precomputed and held across the loop.
-      uint32_t wb = nn_wbase;
-      asm volatile("" : "+v"(wb));
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t x0 = sb[b][2 * q][i >> 1], x1 = sb[b][2 * q + 1][i >> 1];
-        o[q] = (i & 1) ? ((x0 >> 16) | (x1 & 0xFFFF0000u)) : ((x0 & 0xFFFFu) | (x1 << 16));
-      }
-      *reinterpret_cast<u32x4*>(smem + ((wb ^ (uint32_t)((i >> 1) << 4)) + st * B_STAGE + i * 128)) = o;
+      // chunk as loaded: contraction row (lt >> 5) + 8 i
+      *reinterpret_cast<u32x4*>(smem + (i & 1 ? nn_w1 : nn_w0) + st * B_STAGE + i * 8 * 512) = sb[b][i];
     }
   };
   auto store_a = [&](int st, auto bsel) {
@@ -251,6 +248,39 @@ gemm_w4_kernel(const GemmArgs p) {
   const uint32_t rb = (uint32_t)B_BASE + (uint32_t)(wn * TN + l32) * 128;
   const int swz = (l32 >> 1) & 7;
   bf16x8 fa[2][FM], fb[2][FN];
+  // B_NN fragments from ds_read_b64_tr_b16: within each 16-lane group, lane i
+  // receives element (4 q + i / 4, i % 4) of the group's 4 x 4 loads (q < 4),
+  // so pointing lane i at contraction row k0 + i / 4 and columns
+  // n0 + 4 (i % 4) .. +3 hands it rows k0 .. k0 + 3 of column n0 + i.  Lane l
+  // of the 32x32x16 fragment needs column 32 j + l % 32 and rows 8 (l / 32) ..
+  // +7 of step s: group gq = l >> 4 takes columns n0 = 32 j + 16 (gq & 1) and
+  // rows 16 s + 8 (gq >> 1) + 4 h, h < 2.  The row's swizzle is the same for
+  // every s, j, h: f = ((l & 15) >> 2) | 4 (gq >> 1).
+  uint32_t nn_r[FN];
+  if constexpr (B_NN) {
+    const int gq = lane >> 4, i16 = lane & 15;
+    const int f = (i16 >> 2) | ((gq >> 1) << 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int chunk = (wn * TN + 32 * j + 16 * (gq & 1) + 4 * (i16 & 3)) >> 3;
+      nn_r[j] = (uint32_t)B_BASE + (uint32_t)(8 * (gq >> 1) + (i16 >> 2)) * 512 +
+                (uint32_t)((chunk ^ (2 * f)) << 4) + (uint32_t)((i16 & 1) << 3);
+    }
+  }
+  auto rd_nn = [&](int st, int s, int j) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    i16x4 h[2];
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+      h[hq] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+          (__attribute__((address_space(3))) char*)smem + nn_r[j] + st * B_STAGE + (16 * s + 4 * hq) * 512));
+    u32x4 v;
+    v[0] = (uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16);
+    v[1] = (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16);
+    v[2] = (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16);
+    v[3] = (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16);
+    return __builtin_bit_cast(bf16x8, v);
+  };
   auto rd = [&](int st, int s, auto fsel) {
     constexpr int f = decltype(fsel)::value;
     const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
@@ -258,8 +288,12 @@ gemm_w4_kernel(const GemmArgs p) {
     for (int i = 0; i < FM; ++i)
       fa[f][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + i * 32 * 128));
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[f][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + j * 32 * 128));
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (B_NN)
+        fb[f][j] = rd_nn(st, s, j);
+      else
+        fb[f][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + j * 32 * 128));
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -289,6 +323,8 @@ gemm_w4_kernel(const GemmArgs p) {
     const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
     if (k < FM)
       fa[f][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + k * 32 * 128));
+    else if constexpr (B_NN)
+      fb[f][k - FM] = rd_nn(st, s, k - FM);
     else
       fb[f][k - FM] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + (k - FM) * 32 * 128));
   };

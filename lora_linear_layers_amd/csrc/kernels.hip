@@ -146,6 +146,42 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, uint16_t*
   }
 }
 
+// dst[c, q] = q < R ? src[q, c] : 0 for c < C, q < Rpad: a bf16 transpose
+// through a 64 x 64 LDS tile, 16-byte loads and stores (C and Rpad multiples
+// of 8).
+__global__ void __launch_bounds__(256) transpose_tile_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                             int64_t R, int64_t C, uint16_t* __restrict__ dst,
+                                                             int64_t ldd, int64_t Rpad) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
+  const int64_t c0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 512; e += 256) {
+    const int rr = e >> 3, ch = e & 7;
+    const int64_t q = q0 + rr, c = c0 + 8 * ch;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < R && c < C) v = *reinterpret_cast<const u32x4*>(src + q * lds + c);
+    *reinterpret_cast<u32x4*>(&t[rr][8 * ch]) = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 512; e += 256) {
+    const int cc = e >> 3, qc = e & 7;
+    const int64_t c = c0 + cc, q = q0 + 8 * qc;
+    if (c >= C || q >= Rpad) continue;
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = (uint32_t)t[8 * qc + 2 * k][cc] | ((uint32_t)t[8 * qc + 2 * k + 1][cc] << 16);
+    *reinterpret_cast<u32x4*>(dst + c * ldd + q) = o;
+  }
+}
+
+hipError_t launch_transpose_tile(const uint16_t* src, int64_t lds, int64_t R, int64_t C, uint16_t* dst, int64_t ldd,
+                                 int64_t Rpad, hipStream_t st) {
+  if (R <= 0 || C <= 0 || Rpad <= 0) return hipSuccess;
+  if (C % 8 || Rpad % 8 || Rpad < R || ldd < Rpad || ldd % 8 || lds % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((Rpad + 63) / 64));
+  hipLaunchKernelGGL(transpose_tile_kernel, grid, dim3(256), 0, st, src, lds, R, C, dst, ldd, Rpad);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ void pad_cols_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t rows, int64_t r,
                                 int64_t r_pad) {

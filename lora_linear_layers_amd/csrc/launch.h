@@ -60,6 +60,11 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st);
 hipError_t launch_transpose_pad(const uint16_t* src, uint16_t* dst, int64_t rows, int64_t r, int64_t r_pad,
                                 hipStream_t st);
 
+// dst[c, q] = q < R ? src[q, c] : 0 (c < C, q < Rpad; row strides lds, ldd):
+// src [R, C] bf16 transposed to [C, Rpad] with zero columns R..Rpad.
+hipError_t launch_transpose_tile(const uint16_t* src, int64_t lds, int64_t R, int64_t C, uint16_t* dst, int64_t ldd,
+                                 int64_t Rpad, hipStream_t st);
+
 // dst[i, j] = j < r ? src[i, j] : 0 for a [rows, r] matrix widened to [rows, r_pad].
 hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t rows, int64_t r,
                            int64_t r_pad, hipStream_t st);

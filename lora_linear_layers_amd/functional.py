@@ -180,6 +180,19 @@ def _check_keep(keep, M, d_in):
         raise ValueError("keep must be a uint8 bit mask of M * d_in / 8 bytes")
 
 
+def lora_transpose(W, out=None):
+    """W^T (bf16) through the library's tiled transpose, e.g. the frozen
+    weight's transpose that group members take as W_t."""
+    L._contig(W, out)
+    if W.dtype != torch.bfloat16 or W.dim() != 2:
+        raise TypeError("bf16 matrix expected")
+    rows, cols = W.shape
+    if out is None:
+        out = torch.empty(cols, rows, dtype=W.dtype, device=W.device)
+    L._check("lora_transpose", L.lib().lora_transpose(L._ptr(W), rows, cols, L._ptr(out), L._stream(W.device)))
+    return out
+
+
 def lora_merge(W, A, B, scale: float, out=None, ws=None):
     """W + scale B A in W's dtype (out may be W itself); -scale unmerges."""
     L._contig(W, A, B, out)
@@ -206,8 +219,8 @@ def _group_members(X, members):
     M, d_in = X.shape
     for g, m in enumerate(members):
         A, B = m["A"], m["B"]
-        W, codes, absmax = m.get("W"), m.get("codes"), m.get("absmax")
-        L._contig(A, B, W, codes, absmax)
+        W, codes, absmax, Wt = m.get("W"), m.get("codes"), m.get("absmax"), m.get("W_t")
+        L._contig(A, B, W, codes, absmax, Wt)
         r, d_out = A.shape[0], B.shape[0]
         if A.shape != (r, d_in) or B.shape != (d_out, r) or (W is not None and W.shape != (d_out, d_in)):
             raise ValueError("shape mismatch: X [M,d_in], W [d_out,d_in], A [r,d_in], B [d_out,r]")
@@ -215,7 +228,9 @@ def _group_members(X, members):
             raise ValueError("each member takes exactly one of W and NF4 codes")
         e = arr[g]
         e.d_out, e.r, e.scale, e.rope = d_out, r, float(m["scale"]), int(bool(m.get("rope", False)))
-        e.W, e.W_nf4, e.absmax = (L._ptr(t) for t in (W, codes, absmax))
+        if Wt is not None and (Wt.shape != (d_in, d_out) or Wt.dtype != torch.bfloat16):
+            raise ValueError("W_t must be the bf16 [d_in, d_out] transpose of W")
+        e.W, e.W_nf4, e.absmax, e.W_t = (L._ptr(t) for t in (W, codes, absmax, Wt))
         e.A, e.B = L._ptr(A), L._ptr(B)
     return arr
 

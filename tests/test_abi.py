@@ -269,3 +269,16 @@ def test_dropout_validation_and_workspace(lib):
     # the masked copy of X joins the plain layer's workspace
     assert f(_lib.OP_DROPOUT_FWD, 1, 4096, 4096, 4096, 16) >= f(_lib.OP_FWD, 1, 4096, 4096, 4096, 16) + 4096 * 4096 * 2
     assert f(_lib.OP_DROPOUT_BWD, 0, 4096, 4096, 4096, 16) >= f(_lib.OP_BWD, 0, 4096, 4096, 4096, 16) + 4096 * 4096 * 4
+
+
+def test_transpose_and_wt_validation(lib):
+    assert lib.lora_transpose(P, 12, 64, P, None) == ESHAPE
+    assert lib.lora_transpose(P, 64, 0, P, None) == ESHAPE
+    assert lib.lora_transpose(None, 64, 64, P, None) == ENULL
+    assert lib.lora_transpose(P, 64, 64, P + 2, None) == EALIGN
+    assert _gfwd(lib, _members(2, W_t=P + 8)) == EALIGN
+    # a caller-held W^T removes the per-call transpose from the workspace
+    m = _members(1, d_out=4096, r=16)
+    mt = _members(1, d_out=4096, r=16, W_t=P)
+    f = lib.lora_group_workspace_bytes
+    assert f(1, 1, 8192, 4096, 1, m) - f(1, 1, 8192, 4096, 1, mt) >= 4096 * 4096 * 2 - 256

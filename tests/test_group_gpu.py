@@ -218,3 +218,29 @@ def test_group_m_zero_and_no_dx(lib, dtype):
 
 def gen_dtype(dtype):
     return torch.float32 if dtype == "f32" else torch.bfloat16
+
+
+def test_transpose_exact(lib):
+    W = draw(5, (1032, 520), "normal", 1.0, "bf16")
+    Wt = lib.lora_transpose(W)
+    torch.cuda.synchronize()
+    assert torch.equal(Wt, W.t().contiguous())
+
+
+def test_group_backward_with_caller_wt_is_bit_equal(lib):
+    # whole tiles: dX reads W^T; a caller-held W^T gives the same bits as the
+    # per-call transpose
+    M, d_in = 4096, 4096
+    X = draw(61, (M, d_in), "normal", 1.0, "bf16")
+    members, with_t, dYs = [], [], []
+    for g, (d_out, r) in enumerate([(1024, 16), (2048, 64)]):
+        W, A, B, dY = _member_inputs(62 + 10 * g, M, d_in, d_out, r, "bf16")
+        members.append(dict(W=W, A=A, B=B, scale=1.0))
+        with_t.append(dict(W=W, A=A, B=B, scale=1.0, W_t=lib.lora_transpose(W)))
+        dYs.append(dY)
+    a = lib.lora_group_bwd(X, members, dYs)
+    b = lib.lora_group_bwd(X, with_t, dYs)
+    torch.cuda.synchronize()
+    for ga, gb in zip(a, b):
+        for x, y in zip(ga, gb):
+            assert torch.equal(x, y)
