@@ -432,22 +432,71 @@ gemm_w4_kernel(const GemmArgs p) {
   const int64_t cbase = n0 + wn * TN + l32;
   uint16_t* out = reinterpret_cast<uint16_t*>(p.c);
   if constexpr (EPI == EPI_ROPE) {
+    // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
+    // first (free after the main loop): 16-byte loads, all in flight together.
+    // Row q's 64 values sit rotated by 32 when (q >> 2) & 1, so the epilogue's
+    // reads (rows q and q + 4, 32 consecutive frequencies each) hit distinct banks.
+    __syncthreads();
+    float* cs_l = reinterpret_cast<float*>(smem);
+    float* sn_l = cs_l + BM * 64;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float4 buf[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = tid + NT * (16 * half + k);
+        const int q = c >> 5, part = c & 31;
+        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)p.pos[m0 + q] * 64 + 4 * (part & 15);
+        buf[k] = *reinterpret_cast<const float4*>(src);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = tid + NT * (16 * half + k);
+        const int q = c >> 5, part = c & 31;
+        float* dst = (part < 16 ? cs_l : sn_l) + q * 64 + ((4 * (part & 15) + 32 * ((q >> 2) & 1)) & 63);
+        *reinterpret_cast<float4*>(dst) = buf[k];
+      }
+    }
+    __syncthreads();
     // a wave's 128 columns are one head: column 32 j + l32 (j < 2) pairs with
-    // column 32 (j + 2) + l32 = +64, both in this lane; cos/sin row = positions[row]
+    // column 32 (j + 2) + l32 = +64, both in this lane.  Per 32-row block the
+    // 64 cos/sin values are all read before any is used, so the reads overlap.
+    // The lane's indices are derived afresh here: values kept from before the
+    // main loop would be spilled, and each reload's wait between the stores
+    // also waits for every store issued before it.
+    int te = threadIdx.x;
+    asm volatile("" : "+v"(te));
+    const int l32 = te & 31, hh = (te >> 5) & 1;
+    const int wm = __builtin_amdgcn_readfirstlane(te >> 7), wn = __builtin_amdgcn_readfirstlane((te >> 6) & 1);
+    const int64_t cbase = n0 + wn * TN + l32;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
-        const int64_t prow = (int64_t)p.pos[row] * 64;
+      for (int vb = 0; vb < 4; ++vb) {
+        // 4 rows at a time: 16 reads in flight, then their 16 stores
+        float cs[4][2], sn[4][2];
 #pragma unroll
-        for (int j = 0; j < FN / 2; ++j) {
-          const int f = 32 * j + l32;
-          const int64_t col = cbase + 32 * j;
-          const float cs = p.cosc[prow + f], sn = p.sinc[prow + f];
-          const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
-          out[row * p.ldc + col] = f2bf(z1 * cs - z2 * sn);
-          out[row * p.ldc + col + 64] = f2bf(z2 * cs + z1 * sn);
+        for (int vv = 0; vv < 4; ++vv) {
+          const int q = wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int li = q * 64 + ((32 * j + l32 + 32 * ((q >> 2) & 1)) & 63);
+            cs[vv][j] = cs_l[li];
+            sn[vv][j] = sn_l[li];
+          }
+        }
+        fence();
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int v = 4 * vb + vv;
+          const int64_t row = m0 + wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int64_t col = cbase + 32 * j;
+            const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
+            out[row * p.ldc + col] = f2bf(z1 * cs[vv][j] - z2 * sn[vv][j]);
+            out[row * p.ldc + col + 64] = f2bf(z2 * cs[vv][j] + z1 * sn[vv][j]);
+          }
         }
       }
   } else if constexpr (SW) {
