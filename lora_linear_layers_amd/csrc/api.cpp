@@ -459,7 +459,15 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
-  if (nf4 && L.dequant) {
+  if (nf4 && L.dequant && L.dx_nt && dX && !Wt_in) {
+    // the backward reads W only as W^T: dequantise straight into it
+    HIPTRY(timed(K_NF4_DEQ, 2.0 * d_out * d_in, (0.5 + 1.0 / 16 + 2.0) * d_out * d_in, st, [&] {
+      return launch_nf4_dequant_t(nf4->codes, nf4->absmax, d_out, d_in, nf4->table,
+                                  reinterpret_cast<uint16_t*>(w + L.wt), st);
+    }));
+    Wt_in = w + L.wt;
+    nf4 = nullptr;
+  } else if (nf4 && L.dequant && dX) {
     TRY(dequant_w(*nf4, d_out * d_in, w + L.wdq, st));
     W = w + L.wdq;
     nf4 = nullptr;

@@ -622,6 +622,58 @@ __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restr
   }
 }
 
+// W^T [cols, rows] bf16 straight from NF4 codes of W [rows, cols] (cols a
+// multiple of 64): a 64 x 64 tile per workgroup, the load stage's own byte ->
+// bf16x2 routine into LDS, then 16-byte stores of the transposed rows.
+__global__ void __launch_bounds__(256) nf4_dequant_t_kernel(const uint8_t* __restrict__ codes,
+                                                            const float* __restrict__ absmax, int64_t rows,
+                                                            int64_t cols, Table16 tab, uint16_t* __restrict__ out) {
+  __shared__ float2 tab2[256];
+  __shared__ __attribute__((aligned(16))) uint32_t t[64][36];  // 64 rows x 64 bf16 (+ pad)
+  nf4_fill_tab2(tab2, tab.v, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+  if (threadIdx.x < 128) {
+    const int rr = threadIdx.x >> 1, half = threadIdx.x & 1;  // 32 elements = 16 code bytes
+    const int64_t row = r0 + rr;
+    u32x4 o[4] = {};
+    if (row < rows) {
+      const int64_t e0 = row * cols + c0 + 32 * half;  // first element (cols % 64 == 0: one absmax)
+      const u32x4 c = *reinterpret_cast<const u32x4*>(codes + e0 / 2);
+      const float am = absmax[e0 >> 6];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) o[w][b] = nf4_byte_to_bf16x2(tab2, c[w] >> (8 * b), am);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) *reinterpret_cast<u32x4*>(&t[rr][16 * half + 4 * w]) = o[w];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 512; e += 256) {
+    const int cc = e >> 3, qc = e & 7;  // output row c0 + cc, columns r0 + 8 qc .. +7
+    const int64_t c = c0 + cc, r = r0 + 8 * qc;
+    if (r >= rows) continue;
+    const uint16_t* tt = reinterpret_cast<const uint16_t*>(&t[0][0]);
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = (uint32_t)tt[(8 * qc + 2 * k) * 72 + cc] | ((uint32_t)tt[(8 * qc + 2 * k + 1) * 72 + cc] << 16);
+    *reinterpret_cast<u32x4*>(out + c * rows + r) = v;
+  }
+}
+
+hipError_t launch_nf4_dequant_t(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                                const float* table16, uint16_t* out, hipStream_t st) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (cols % 64 || rows % 8) return hipErrorInvalidValue;
+  Table16 t;
+  for (int i = 0; i < 16; ++i) t.v[i] = table16[i];
+  const dim3 grid((unsigned)(cols / 64), (unsigned)((rows + 63) / 64));
+  hipLaunchKernelGGL(nf4_dequant_t_kernel, grid, dim3(256), 0, st, codes, absmax, rows, cols, t, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n, const float* table16,
                               uint16_t* out, hipStream_t st) {
   if (n <= 0) return hipSuccess;

@@ -135,6 +135,11 @@ hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, 
 // wave); out [blocks * 256] receives one float per thread.
 hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st);
 
+// W^T [cols, rows] bf16 from the NF4 codes of W [rows, cols] (cols % 64 == 0,
+// rows % 8 == 0), the same values as launch_nf4_dequant.
+hipError_t launch_nf4_dequant_t(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
+                                const float* table16, uint16_t* out, hipStream_t st);
+
 hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t n,
                               const float* table16, uint16_t* out, hipStream_t st);
 

@@ -301,3 +301,19 @@ def test_nf4_fwd_bwd_parity(lib, M, d_in, d_out, r):
     Yb = lib.lora_linear_fwd(X, Wd, A, B, s)
     torch.cuda.synchronize()
     assert torch.equal(Y, Yb)
+
+
+def test_nf4_whole_tile_backward_equals_bf16_on_dequantised(lib):
+    # from 512 tokens on whole tiles the NF4 backward dequantises straight
+    # into W^T; the result must equal, bit for bit, the bf16 backward on the
+    # dequantised weight (which transposes W itself)
+    tab = gen.nf4_table()
+    M, d_in, d_out, r = 4096, 4096, 1024, 16
+    X, _, A, B, dY = lora_inputs(8, M, d_in, d_out, r, "bf16")
+    codes, absmax = _nf4_weight(9, d_out, d_in)
+    g = lib.nf4_lora_linear_bwd(X, codes, absmax, tab, A, B, 2.0, dY)
+    Wd = lib.nf4_dequant(codes, absmax, tab, d_out * d_in).view(d_out, d_in)
+    g0 = lib.lora_linear_bwd(X, Wd, A, B, 2.0, dY)
+    torch.cuda.synchronize()
+    for a, b in zip(g, g0):
+        assert torch.equal(a, b)
