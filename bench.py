@@ -31,6 +31,7 @@ PEAK = {"bf16": 2516.6, "f32": 157.3}  # TFLOP/s, dense MFMA (MI355X: 256 CU x 2
 HBM_PEAK = 8000.0  # GB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["lora_linear_layers_amd/csrc/gemm.h", "lora_linear_layers_amd/csrc/gemm_w4.h",
+                  "lora_linear_layers_amd/csrc/gemm_w4_nt.h",
                   "lora_linear_layers_amd/csrc/kernels.hip", "lora_linear_layers_amd/csrc/api.cpp"]
 
 
@@ -67,9 +68,10 @@ def parse():
 
 # rocprofv3 kernel names -> the library profiler's kind names
 KIND_OF = {
-    "gemm_w4_kernel<false, 0, 2>": "gemm_bf16_256x256_nt_store",
-    "gemm_w4_kernel<true, 0, 2>": "gemm_bf16_256x256_nn_store",
-    "gemm_w4_kernel<false, 3, 2>": "gemm_bf16_256x256_nt_rope",
+    "gemm_w4_nt_kernel<0>": "gemm_bf16_256x256_nt_store",
+    "gemm_w4_nt_kernel<3>": "gemm_bf16_256x256_nt_rope",
+    "gemm_w4_nt_kernel<6>": "gemm_bf16_256x256_swiglu",
+    "gemm_w4_nn_kernel<2>": "gemm_bf16_256x256_nn_store",
     "gemm_kernel<unsigned short, 256, 64, 4, 1, false, 4, 0>": "panel_bf16_256x64_split",
     "panel_reduce_kernel": "panel_reduce",
     "gemm_kernel<unsigned short, 256, 256, 2, 4, false, 0, 0>": "gemm_bf16_256x256_nt_store",

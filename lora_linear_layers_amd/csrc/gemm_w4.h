@@ -1,5 +1,5 @@
-// gemm_w4.h - the whole-tile bf16 GEMM of the fused LoRA linear layer on
-// gfx950: 256 x 256 x 64 tiles, 4 waves of 128 x 128, one wave per SIMD,
+// gemm_w4.h - the whole-tile bf16 GEMMs of the fused LoRA linear layer on
+// gfx950: 256 x 256 tiles, 4 waves of 128 x 128, one wave per SIMD,
 // v_mfma_f32_32x32x16_bf16 with the accumulators in the accumulation
 // registers.
 //
@@ -9,6 +9,12 @@
 // dominate the layer: every tile whole in m and n and the first segment a
 // whole number of 64-wide stages; the rank-r segment may be ragged.
 //
+// This file holds what both orientations share (the tile constants and the
+// epilogues) and the NN kernel, whose second operand is stored contraction-
+// major (the input gradient through W when no W^T is at hand).  The NT
+// kernel, which every large forward GEMM and the input gradient through W^T
+// run, is in gemm_w4_nt.h.
+//
 // Why this shape.  Measured with the SQ counters on MI355X, the GEMM runs
 // power-limited (about 1.8 GHz) and what separates a fast kernel from a slow
 // one is the share of cycles the MFMA pipe is busy; LDS traffic is the main
@@ -17,6 +23,171 @@
 // per SIMD each wave owns 512 registers: 256 accumulators, two sets of
 // fragments and the register staging of the next global tile, so nothing
 // spills and no loop-invariant address is recomputed.
+//
+// 32x32x16 MFMA: A lane l holds row l % 32, contraction 8 (l / 32) .. +7; B
+// lane l holds column l % 32, the same contraction range; the 16 fp32 results
+// of lane l are rows 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
+#pragma once
+
+#include <type_traits>
+
+#include "gemm.h"
+
+namespace lora {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace w4 {
+constexpr int BM = 256, BN = 256;
+constexpr int NT = 256;
+constexpr int TM = 128, TN = 128;          // wave tile, 2 x 2 waves
+constexpr int FM = TM / 32, FN = TN / 32;  // 4 x 4 MFMA blocks
+constexpr int BK = 64;                     // NN stage depth
+constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;
+constexpr int B_BASE = 2 * A_STAGE;
+constexpr int LDS = 2 * (A_STAGE + B_STAGE);
+constexpr int BIG = 0x40000000;        // resource size with nothing masked
+constexpr uint32_t OOB = 0x40000000u;  // lane offset that reads zero
+}  // namespace w4
+
+// ---------------------------------------------------------------------------
+// Epilogues of a 256 x 256 tile from the accumulators of the calling wave:
+//   acc[i][j][v] = C[row, col], row = m0 + wm*TM + 32 i + 8 (v / 4) + 4 hh + v % 4,
+//                               col = n0 + wn*TN + 32 j + l32
+// (wm, wn the wave's position, l32 / hh the lane's).  The lane indices are
+// derived afresh from threadIdx: values kept from before the main loop would
+// be spilled, and each reload's wait between the stores also waits for every
+// store issued before it.  smem (at least 2 x 256 x 64 floats) must be free:
+// the RoPE epilogue stages its cos/sin rows there.
+//   EPI_STORE:  C = alpha acc, bf16.
+//   EPI_ROPE:   a wave's 128 columns are one head; columns c and c + 64 are
+//               rotated together by the angle of the row's position (page
+//               "UnSloth加速微调体验…", section RoPE缓存集成).
+//   EPI_SWIGLU: MFMA blocks j = 0, 2 hold the gate and j = 1, 3 the up
+//               projection of output columns n0 / 2 + 64 wn + 32 (j / 2) + l32;
+//               C = silu(g) u, and g / u are also stored to cg / cu when
+//               set.
+template <int EPI>
+__device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4::FM][w4::FN], char* smem,
+                                            int64_t m0, int64_t n0) {
+  using namespace w4;
+  auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
+  int te = threadIdx.x;
+  asm volatile("" : "+v"(te));
+  const int l32 = te & 31, hh = (te >> 5) & 1;
+  const int wm = __builtin_amdgcn_readfirstlane(te >> 7), wn = __builtin_amdgcn_readfirstlane((te >> 6) & 1);
+  const int64_t rbase = m0 + wm * TM + 4 * hh;
+  const int64_t cbase = n0 + wn * TN + l32;
+  uint16_t* out = reinterpret_cast<uint16_t*>(p.c);
+  if constexpr (EPI == EPI_ROPE) {
+    // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
+    // first: 16-byte loads, all in flight together.  Row q's 64 values sit
+    // rotated by 32 when (q >> 2) & 1, so the reads below (rows q and q + 4,
+    // 32 consecutive frequencies each) hit distinct banks.
+    __syncthreads();
+    float* cs_l = reinterpret_cast<float*>(smem);
+    float* sn_l = cs_l + BM * 64;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float4 buf[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = te + NT * (16 * half + k);
+        const int q = c >> 5, part = c & 31;
+        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)p.pos[m0 + q] * 64 + 4 * (part & 15);
+        buf[k] = *reinterpret_cast<const float4*>(src);
+      }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int c = te + NT * (16 * half + k);
+        const int q = c >> 5, part = c & 31;
+        float* dst = (part < 16 ? cs_l : sn_l) + q * 64 + ((4 * (part & 15) + 32 * ((q >> 2) & 1)) & 63);
+        *reinterpret_cast<float4*>(dst) = buf[k];
+      }
+    }
+    __syncthreads();
+    // column 32 j + l32 (j < 2) pairs with column 32 (j + 2) + l32 = +64, both
+    // in this lane
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb) {
+        // 4 rows at a time: 16 reads in flight, then their 16 stores
+        float cs[4][2], sn[4][2];
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int q = wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int li = q * 64 + ((32 * j + l32 + 32 * ((q >> 2) & 1)) & 63);
+            cs[vv][j] = cs_l[li];
+            sn[vv][j] = sn_l[li];
+          }
+        }
+        fence();
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int v = 4 * vb + vv;
+          const int64_t row = m0 + wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int64_t col = cbase + 32 * j;
+            const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
+            out[row * p.ldc + col] = f2bf(z1 * cs[vv][j] - z2 * sn[vv][j]);
+            out[row * p.ldc + col + 64] = f2bf(z2 * cs[vv][j] + z1 * sn[vv][j]);
+          }
+        }
+      }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int64_t hbase = n0 / 2 + 64 * wn + l32;
+    uint16_t* og = reinterpret_cast<uint16_t*>(p.cg);
+    uint16_t* ou = reinterpret_cast<uint16_t*>(p.cu);
+    // GU: 0 neither G nor U stored, 1 both, 2 either one (tested per store)
+    auto emit = [&](auto gu_c) {
+      constexpr int GU = decltype(gu_c)::value;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
+            const int64_t o = row * p.ldc + hbase + 32 * jj;
+            out[o] = f2bf(g / (1.f + __expf(-g)) * u);
+            if constexpr (GU == 1) {
+              og[o] = f2bf(g);
+              ou[o] = f2bf(u);
+            } else if constexpr (GU == 2) {
+              if (og) og[o] = f2bf(g);
+              if (ou) ou[o] = f2bf(u);
+            }
+          }
+        }
+    };
+    if (og && ou)
+      emit(std::integral_constant<int, 1>{});
+    else if (!og && !ou)
+      emit(std::integral_constant<int, 0>{});
+    else
+      emit(std::integral_constant<int, 2>{});
+  } else {
+    static_assert(EPI == EPI_STORE, "store, RoPE or SwiGLU epilogue");
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) out[row * p.ldc + cbase + 32 * j] = f2bf(acc[i][j][v] * p.alpha);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NN kernel: C = alpha (A1 B1 + A2 B2), A row-major [m][k], B contraction-
+// major [k][n] (W itself for the input gradient G W; A of the adapter for
+// the rank segment), 256 x 256 x 64 stages, register-staged global tiles.
 //
 // Per stage t (LDS buffer t & 1) each wave runs four contraction steps of 16
 // MFMAs, each MFMA followed by one memory operation:
@@ -29,46 +200,16 @@
 // so the LDS and the load path see an even stream and the LDS latency at
 // stage boundaries is hidden as well.
 //
-// 32x32x16 MFMA: A lane l holds row l % 32, contraction 8 (l / 32) .. +7; B
-// lane l holds column l % 32, the same contraction range; the 16 fp32 results
-// of lane l are rows 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
-//
-// LDS: [A 0][A 1][B 0][B 1], 256 rows of 128 bytes each, chunk c of row r at
-// chunk c ^ ((r >> 1) & 7) (conflict-free for these fragment reads and the
-// tile writes; measured with the LDS bank-conflict counter).
-#pragma once
-
-#include <type_traits>
-
-#include "gemm.h"
-
-namespace lora {
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-namespace w4 {
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int NT = 256;
-constexpr int TM = 128, TN = 128;          // wave tile, 2 x 2 waves
-constexpr int FM = TM / 32, FN = TN / 32;  // 4 x 4 MFMA blocks
-constexpr int A_STAGE = BM * 128, B_STAGE = BN * 128;
-constexpr int B_BASE = 2 * A_STAGE;
-constexpr int LDS = 2 * (A_STAGE + B_STAGE);
-constexpr int BIG = 0x40000000;        // resource size with nothing masked
-constexpr uint32_t OOB = 0x40000000u;  // lane offset that reads zero
-}  // namespace w4
-
-template <bool B_NN, int EPI, int PF>
+// LDS: [A 0][A 1][B 0][B 1].  A: 256 rows of 128 bytes each, chunk c of row r
+// at chunk c ^ ((r >> 1) & 7).  B: [64 contraction rows][256 columns],
+// 512-byte rows, the 16-byte chunk c of row k stored at chunk c ^ nn_swz(k)
+// (nn_swz(k) = 2 f(k), f(k) = (k & 3) | ((k >> 1) & 4)).  Both keep the tile
+// writes and the fragment reads free of bank conflicts (measured with the LDS
+// bank-conflict counter).
+template <int PF>
 __global__ void __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_w4_kernel(const GemmArgs p) {
+gemm_w4_nn_kernel(const GemmArgs p) {
   using namespace w4;
-  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_SWIGLU, "store, RoPE or SwiGLU epilogue");
-  static_assert(EPI != EPI_SWIGLU || !B_NN, "SwiGLU pairs rows of two weights");
-  // SwiGLU: B-tile rows 32 i .. 32 i + 31 come from the gate's weight for
-  // even i and from the up's for odd i, rows c0 + 32 (i / 2) + .. of each
-  // (c0 = n0 / 2), so MFMA blocks j = 0, 2 of a wave hold gate outputs and
-  // j = 1, 3 the up outputs of the same columns
-  constexpr bool SW = EPI == EPI_SWIGLU;
   static_assert(PF == 1 || PF == 2, "one or two staged tiles");
   __shared__ __attribute__((aligned(16))) char smem[LDS];
   // keep the MFMA accumulators in the accumulation registers
@@ -88,44 +229,33 @@ gemm_w4_kernel(const GemmArgs p) {
   const int nk = nk1 + (int)((p.K2 + BK - 1) / BK);
 
   // ---- loaders ----
-  // Row-major chunks (A; B in the weight layout): lane lt moves chunk lt & 7
-  // of rows (lt >> 3) + 32 i, i < 8.  B_NN: lane lt moves the 8 x 8 block of
-  // contraction rows 8 (lt & 7) + i and columns 8 (lt >> 3) .. +7.  Every
-  // load is a raw buffer load (wave-uniform resource + one lane offset); an
-  // offset at or beyond the resource's size reads zero, which masks the
-  // ragged rank-r segment.
+  // A: lane lt moves chunk lt & 7 of rows (lt >> 3) + 32 i, i < 8.  B: lane
+  // lt moves chunk lt & 31 (8 columns) of contraction rows (lt >> 5) + 8 i,
+  // i < 8: each load instruction covers two whole 512-byte rows.  Every load
+  // is a raw buffer load (wave-uniform resource + one lane offset); an offset
+  // at or beyond the resource's size reads zero, which masks the ragged
+  // rank-r segment.
   const int kc = (lt & 7) * 8;
   const char* ga1 = reinterpret_cast<const char*>(p.a1) + m0 * p.lda1 * 2;
   const char* ga2 = reinterpret_cast<const char*>(p.a2) + m0 * p.lda2 * 2;
   const uint32_t va1 = (uint32_t)((lt >> 3) * p.lda1 * 2 + (lt & 7) * 16);
   const uint32_t va2 = (uint32_t)((lt >> 3) * p.lda2 * 2 + (lt & 7) * 16);
-  const int64_t nb0 = SW ? n0 / 2 : n0;  // first weight row of the tile
-  const char* gb1 = reinterpret_cast<const char*>(p.b1) + (B_NN ? n0 * 2 : nb0 * p.ldb1 * 2);
-  const char* gb2 = reinterpret_cast<const char*>(p.b2) + (B_NN ? n0 * 2 : nb0 * p.ldb2 * 2);
-  const char* gb1u = SW ? reinterpret_cast<const char*>(p.b1u) + nb0 * p.ldb1 * 2 : gb1;
-  const char* gb2u = SW ? reinterpret_cast<const char*>(p.b2u) + nb0 * p.ldb2u * 2 : gb2;
-  // B_NN: lane lt moves chunk lt & 31 (8 columns) of contraction rows
-  // (lt >> 5) + 8 i, i < 8: each load instruction covers two whole 512-byte rows
-  const uint32_t vb1 = B_NN ? (uint32_t)((lt >> 5) * p.ldb1 * 2 + (lt & 31) * 16)
-                            : (uint32_t)((lt >> 3) * p.ldb1 * 2 + (lt & 7) * 16);
-  const uint32_t vb2 = B_NN ? (uint32_t)((lt >> 5) * p.ldb2 * 2 + (lt & 31) * 16)
-                            : (uint32_t)((lt >> 3) * p.ldb2 * 2 + (lt & 7) * 16);
-  // segment 2 of B_NN: rows at or beyond K2 lie past the resource's end
-  const int nrecb2 = B_NN ? (int)(p.K2 * p.ldb2 * 2 - n0 * 2) : BIG;
+  const char* gb1 = reinterpret_cast<const char*>(p.b1) + n0 * 2;
+  const char* gb2 = reinterpret_cast<const char*>(p.b2) + n0 * 2;
+  const uint32_t vb1 = (uint32_t)((lt >> 5) * p.ldb1 * 2 + (lt & 31) * 16);
+  const uint32_t vb2 = (uint32_t)((lt >> 5) * p.ldb2 * 2 + (lt & 31) * 16);
+  // segment 2 of B: rows at or beyond K2 lie past the resource's end
+  const int nrecb2 = (int)(p.K2 * p.ldb2 * 2 - n0 * 2);
   // per-segment strides, pinned in scalar registers (a select between two
   // kernel arguments is otherwise turned into a load from a selected
   // address inside the loop, whose wait drains every LDS operation)
   const uint32_t isa1 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda1 * 2));
   const uint32_t isa2 = __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.lda2 * 2));
-  const uint32_t isb1 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(8 * p.ldb1 * 2) : (uint32_t)(32 * p.ldb1 * 2));
-  const uint32_t isb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(8 * p.ldb2 * 2) : (uint32_t)(32 * p.ldb2 * 2));
-  const int64_t kstb1 = B_NN ? (int64_t)BK * p.ldb1 * 2 : (int64_t)BK * 2;
-  const uint32_t kstb2 = __builtin_amdgcn_readfirstlane(B_NN ? (uint32_t)(BK * p.ldb2 * 2) : (uint32_t)(BK * 2));
+  const uint32_t isb1 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * p.ldb1 * 2));
+  const uint32_t isb2 = __builtin_amdgcn_readfirstlane((uint32_t)(8 * p.ldb2 * 2));
+  const int64_t kstb1 = (int64_t)BK * p.ldb1 * 2;
+  const uint32_t kstb2 = __builtin_amdgcn_readfirstlane((uint32_t)(BK * p.ldb2 * 2));
   const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
-  // SwiGLU segment 2 of the up rows: rank column k of Pcat is column k - k2s of B_up
-  const int k2s = SW ? __builtin_amdgcn_readfirstlane((int)p.k2_split) : 0;
-  const uint32_t vb2u = SW ? (uint32_t)((lt >> 3) * p.ldb2u * 2) : 0u;
-  const uint32_t isb2u = SW ? __builtin_amdgcn_readfirstlane((uint32_t)(32 * p.ldb2u * 2)) : 0u;
 
   u32x4 sa[PF][8], sb[PF][8];
 
@@ -135,9 +265,6 @@ gemm_w4_kernel(const GemmArgs p) {
   struct LoadDesc {
     __amdgpu_buffer_rsrc_t r;
     uint32_t vo, is;
-    // SwiGLU B tiles: the up rows' resource, lane offset and stride
-    __amdgpu_buffer_rsrc_t r2;
-    uint32_t vo2, is2;
   };
   auto desc_a = [&](int u) {
     const bool seg1 = u < nk1;
@@ -147,9 +274,6 @@ gemm_w4_kernel(const GemmArgs p) {
     d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, BIG, 0x00020000);
     d.vo = seg1 ? va1 : (tt * BK + kc < k2 ? va2 + (uint32_t)(tt * BK * 2) : OOB);
     d.is = seg1 ? isa1 : isa2;
-    d.r2 = d.r;
-    d.vo2 = 0;
-    d.is2 = 0;
     return d;
   };
   auto desc_b = [&](int u) {
@@ -157,41 +281,13 @@ gemm_w4_kernel(const GemmArgs p) {
     const int tt = u - nk1;
     LoadDesc d;
     const char* base = seg1 ? gb1 + (int64_t)u * kstb1 : gb2;
-    d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (B_NN && !seg1) ? nrecb2 : BIG,
-                                            0x00020000);
-    if constexpr (SW) {
-      // gate rows: rank columns [0, k2s); up rows: [k2s, K2) shifted to B_up's own columns
-      const int kk = tt * BK + kc;
-      d.vo = seg1 ? vb1 : (kk < k2s ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
-      const char* base2 = seg1 ? gb1u + (int64_t)u * kstb1 : gb2u;
-      d.r2 = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base2), (short)0, BIG, 0x00020000);
-      d.vo2 = seg1 ? vb1 : (kk >= k2s && kk < k2 ? vb2u + (uint32_t)((kk - k2s) * 2) : OOB);
-      d.is2 = seg1 ? isb1 : isb2u;
-    } else {
-      if constexpr (!B_NN)
-        d.vo = seg1 ? vb1 : (tt * BK + kc < k2 ? vb2 + (uint32_t)(tt * BK * 2) : OOB);
-      else
-        d.vo = seg1 ? vb1 : vb2 + (uint32_t)tt * kstb2;
-      d.r2 = d.r;
-      d.vo2 = 0;
-      d.is2 = 0;
-    }
+    d.r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, seg1 ? BIG : nrecb2, 0x00020000);
+    d.vo = seg1 ? vb1 : vb2 + (uint32_t)tt * kstb2;
     d.is = seg1 ? isb1 : isb2;
     return d;
   };
   auto ld = [&](const LoadDesc& d, int i) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(d.r, (int)(d.vo + i * d.is), 0, 0));
-  };
-  // chunk i of a B tile (SwiGLU: alternate weights, 32 rows of each per pair)
-  auto ldb = [&](const LoadDesc& d, int i) {
-    if constexpr (SW) {
-      if (i & 1)
-        return __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(d.r2, (int)(d.vo2 + (i >> 1) * d.is2), 0, 0));
-      return __builtin_bit_cast(u32x4,
-                                __builtin_amdgcn_raw_buffer_load_b128(d.r, (int)(d.vo + (i >> 1) * d.is), 0, 0));
-    }
-    return ld(d, i);
   };
   auto load_a = [&](int u, auto bsel) {
     constexpr int b = decltype(bsel)::value;
@@ -203,17 +299,13 @@ gemm_w4_kernel(const GemmArgs p) {
     constexpr int b = decltype(bsel)::value;
     const LoadDesc d = desc_b(u);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sb[b][i] = ldb(d, i);
+    for (int i = 0; i < 8; ++i) sb[b][i] = ld(d, i);
   };
 
   // ---- registers -> LDS buffer st ----
   // rows (lt >> 3) + 32 i all have (row >> 1) & 7 = (lt >> 4) & 7
   const uint32_t wr_off = (uint32_t)(lt >> 3) * 128 + (uint32_t)(((lt & 7) ^ ((lt >> 4) & 7)) << 4);
-  // B_NN tile in LDS: [64 contraction rows][256 columns], 512-byte rows, the
-  // 16-byte chunk c of row k stored at chunk c ^ nn_swz(k) (nn_swz(k) = 2 f(k),
-  // f(k) = (k & 3) | ((k >> 1) & 4)), which keeps both the whole-row writes
-  // and the transposing fragment reads free of bank conflicts.  Row
-  // (lt >> 5) + 8 i has nn_swz = 2 ((lt >> 5) & 3) ^ 8 (i & 1).
+  // B row (lt >> 5) + 8 i has nn_swz = 2 ((lt >> 5) & 3) ^ 8 (i & 1)
   const uint32_t nn_w0 = (uint32_t)B_BASE + (uint32_t)(lt >> 5) * 512 +
                          (uint32_t)(((lt & 31) ^ (2 * ((lt >> 5) & 3))) << 4);
   const uint32_t nn_w1 = (uint32_t)B_BASE + (uint32_t)(lt >> 5) * 512 +
@@ -225,12 +317,8 @@ gemm_w4_kernel(const GemmArgs p) {
   };
   auto st_b = [&](int st, auto bsel, int i) {
     constexpr int b = decltype(bsel)::value;
-    if constexpr (!B_NN) {
-      *reinterpret_cast<u32x4*>(smem + B_BASE + wr_off + st * B_STAGE + i * 32 * 128) = sb[b][i];
-    } else {
-      // chunk as loaded: contraction row (lt >> 5) + 8 i
-      *reinterpret_cast<u32x4*>(smem + (i & 1 ? nn_w1 : nn_w0) + st * B_STAGE + i * 8 * 512) = sb[b][i];
-    }
+    // chunk as loaded: contraction row (lt >> 5) + 8 i
+    *reinterpret_cast<u32x4*>(smem + (i & 1 ? nn_w1 : nn_w0) + st * B_STAGE + i * 8 * 512) = sb[b][i];
   };
   auto store_a = [&](int st, auto bsel) {
 #pragma unroll
@@ -242,13 +330,11 @@ gemm_w4_kernel(const GemmArgs p) {
   };
 
   // ---- fragments ----
-  // A rows wm*TM + 32 i + l32 and B rows wn*TN + 32 j + l32 all have
-  // (row >> 1) & 7 = (l32 >> 1) & 7.
+  // A rows wm*TM + 32 i + l32 all have (row >> 1) & 7 = (l32 >> 1) & 7.
   const uint32_t ra = (uint32_t)(wm * TM + l32) * 128;
-  const uint32_t rb = (uint32_t)B_BASE + (uint32_t)(wn * TN + l32) * 128;
   const int swz = (l32 >> 1) & 7;
   bf16x8 fa[2][FM], fb[2][FN];
-  // B_NN fragments from ds_read_b64_tr_b16: within each 16-lane group, lane i
+  // B fragments from ds_read_b64_tr_b16: within each 16-lane group, lane i
   // receives element (4 q + i / 4, i % 4) of the group's 4 x 4 loads (q < 4),
   // so pointing lane i at contraction row k0 + i / 4 and columns
   // n0 + 4 (i % 4) .. +3 hands it rows k0 .. k0 + 3 of column n0 + i.  Lane l
@@ -257,7 +343,7 @@ gemm_w4_kernel(const GemmArgs p) {
   // rows 16 s + 8 (gq >> 1) + 4 h, h < 2.  The row's swizzle is the same for
   // every s, j, h: f = ((l & 15) >> 2) | 4 (gq >> 1).
   uint32_t nn_r[FN];
-  if constexpr (B_NN) {
+  {
     const int gq = lane >> 4, i16 = lane & 15;
     const int f = (i16 >> 2) | ((gq >> 1) << 2);
 #pragma unroll
@@ -288,12 +374,7 @@ gemm_w4_kernel(const GemmArgs p) {
     for (int i = 0; i < FM; ++i)
       fa[f][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + i * 32 * 128));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      if constexpr (B_NN)
-        fb[f][j] = rd_nn(st, s, j);
-      else
-        fb[f][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + j * 32 * 128));
-    }
+    for (int j = 0; j < FN; ++j) fb[f][j] = rd_nn(st, s, j);
   };
 
   f32x16 acc[FM][FN];
@@ -314,21 +395,19 @@ gemm_w4_kernel(const GemmArgs p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // one stage t (LDS buffer ST = t & 1); stage t+1 is staged in registers
-  // sa/sb[(t+1) % PF]; loads issued here are for stage t+1+PF (clamped to the
-  // last stage: a repeated load past the end is harmless)
-  // one fragment read (k < 8: A block k, else B block k - 8) of step s
+  // one fragment read (k < 4: A block k, else B block k - 4) of step s
   auto rd1 = [&](int st, int s, auto fsel, int k) {
     constexpr int f = decltype(fsel)::value;
     const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
     if (k < FM)
       fa[f][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + ra + c + st * A_STAGE + k * 32 * 128));
-    else if constexpr (B_NN)
-      fb[f][k - FM] = rd_nn(st, s, k - FM);
     else
-      fb[f][k - FM] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + rb + c + st * B_STAGE + (k - FM) * 32 * 128));
+      fb[f][k - FM] = rd_nn(st, s, k - FM);
   };
 
+  // one stage t (LDS buffer ST = t & 1); stage t+1 is staged in registers
+  // sa/sb[(t+1) % PF]; loads issued here are for stage t+1+PF (clamped to the
+  // last stage: a repeated load past the end is harmless)
   auto stage = [&](int t, auto stsel) {
     constexpr int ST = decltype(stsel)::value;
     constexpr int U = ST ^ 1;
@@ -394,7 +473,7 @@ gemm_w4_kernel(const GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         mf(I1{}, 8 + q);
-        sb[SB::value][q] = ldb(d, q);
+        sb[SB::value][q] = ld(d, q);
         fence();
       }
     }
@@ -425,110 +504,7 @@ gemm_w4_kernel(const GemmArgs p) {
     if (t < nk) stage(t, I0{});
   }
 
-  // ---------------- epilogue ----------------
-  // acc[i][j][v] = C[row, col]: row = m0 + wm*TM + 32 i + 8 (v / 4) + 4 hh + v % 4,
-  //                            col = n0 + wn*TN + 32 j + l32
-  const int64_t rbase = m0 + wm * TM + 4 * hh;
-  const int64_t cbase = n0 + wn * TN + l32;
-  uint16_t* out = reinterpret_cast<uint16_t*>(p.c);
-  if constexpr (EPI == EPI_ROPE) {
-    // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
-    // first (free after the main loop): 16-byte loads, all in flight together.
-    // Row q's 64 values sit rotated by 32 when (q >> 2) & 1, so the epilogue's
-    // reads (rows q and q + 4, 32 consecutive frequencies each) hit distinct banks.
-    __syncthreads();
-    float* cs_l = reinterpret_cast<float*>(smem);
-    float* sn_l = cs_l + BM * 64;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float4 buf[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int c = tid + NT * (16 * half + k);
-        const int q = c >> 5, part = c & 31;
-        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)p.pos[m0 + q] * 64 + 4 * (part & 15);
-        buf[k] = *reinterpret_cast<const float4*>(src);
-      }
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int c = tid + NT * (16 * half + k);
-        const int q = c >> 5, part = c & 31;
-        float* dst = (part < 16 ? cs_l : sn_l) + q * 64 + ((4 * (part & 15) + 32 * ((q >> 2) & 1)) & 63);
-        *reinterpret_cast<float4*>(dst) = buf[k];
-      }
-    }
-    __syncthreads();
-    // a wave's 128 columns are one head: column 32 j + l32 (j < 2) pairs with
-    // column 32 (j + 2) + l32 = +64, both in this lane.  Per 32-row block the
-    // 64 cos/sin values are all read before any is used, so the reads overlap.
-    // The lane's indices are derived afresh here: values kept from before the
-    // main loop would be spilled, and each reload's wait between the stores
-    // also waits for every store issued before it.
-    int te = threadIdx.x;
-    asm volatile("" : "+v"(te));
-    const int l32 = te & 31, hh = (te >> 5) & 1;
-    const int wm = __builtin_amdgcn_readfirstlane(te >> 7), wn = __builtin_amdgcn_readfirstlane((te >> 6) & 1);
-    const int64_t cbase = n0 + wn * TN + l32;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int vb = 0; vb < 4; ++vb) {
-        // 4 rows at a time: 16 reads in flight, then their 16 stores
-        float cs[4][2], sn[4][2];
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          const int q = wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
-#pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const int li = q * 64 + ((32 * j + l32 + 32 * ((q >> 2) & 1)) & 63);
-            cs[vv][j] = cs_l[li];
-            sn[vv][j] = sn_l[li];
-          }
-        }
-        fence();
-#pragma unroll
-        for (int vv = 0; vv < 4; ++vv) {
-          const int v = 4 * vb + vv;
-          const int64_t row = m0 + wm * TM + 32 * i + 8 * vb + vv + 4 * hh;
-#pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const int64_t col = cbase + 32 * j;
-            const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
-            out[row * p.ldc + col] = f2bf(z1 * cs[vv][j] - z2 * sn[vv][j]);
-            out[row * p.ldc + col + 64] = f2bf(z2 * cs[vv][j] + z1 * sn[vv][j]);
-          }
-        }
-      }
-  } else if constexpr (SW) {
-    // blocks j = 0, 2: gate, j = 1, 3: up, of the output columns
-    // n0 / 2 + 64 wn + 32 (j / 2) + l32
-    const int64_t hbase = nb0 + 64 * wn + l32;
-    uint16_t* og = reinterpret_cast<uint16_t*>(p.cg);
-    uint16_t* ou = reinterpret_cast<uint16_t*>(p.cu);
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
-          const int64_t o = row * p.ldc + hbase + 32 * jj;
-          out[o] = f2bf(g / (1.f + __expf(-g)) * u);
-          if (og) og[o] = f2bf(g);
-          if (ou) ou[o] = f2bf(u);
-        }
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
-#pragma unroll
-        for (int j = 0; j < FN; ++j) out[row * p.ldc + cbase + 32 * j] = f2bf(acc[i][j][v] * p.alpha);
-      }
-  }
+  w4_epilogue<EPI_STORE>(p, acc, smem, m0, n0);
 }
 
 }  // namespace lora

@@ -8,6 +8,7 @@
 
 #include "gemm.h"
 #include "gemm_w4.h"
+#include "gemm_w4_nt.h"
 #include "launch.h"
 
 namespace lora {
@@ -28,7 +29,8 @@ hipError_t run(GemmArgs a, int splits, hipStream_t st) {
 
 // Whole-tile launches (every tile inside m and n, the first contraction
 // segment a whole number of 64-wide stages, no split, every lane offset of a
-// tile below the 1 GiB buffer-resource range) take gemm_w4_kernel.
+// tile below the 1 GiB buffer-resource range) take gemm_w4_nt_kernel (NT) or
+// gemm_w4_nn_kernel (NN).
 bool whole_tiles(const GemmArgs& a, int splits) {
   const int64_t ld = std::max(std::max(std::max(a.lda1, a.lda2), std::max(a.ldb1, a.ldb2)), a.ldb2u);
   return splits == 1 && a.m_load == a.m_store && a.m_store % w4::BM == 0 && a.n_load == a.n_store &&
@@ -37,10 +39,14 @@ bool whole_tiles(const GemmArgs& a, int splits) {
 
 template <bool B_NN, int EPI>
 hipError_t run_whole(GemmArgs a, hipStream_t st) {
+  static_assert(!B_NN || EPI == EPI_STORE, "the NN kernel stores");
   a.tiles_m = (int)(a.m_store / w4::BM);
   const int64_t nblocks = (int64_t)a.tiles_m * (a.n_store / w4::BN);
   if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_w4_kernel<B_NN, EPI, 2>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
+  if constexpr (B_NN)
+    hipLaunchKernelGGL((gemm_w4_nn_kernel<2>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_w4_nt_kernel<EPI>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
   return hipGetLastError();
 }
 
