@@ -2,43 +2,42 @@
 // operands row-major with the contraction contiguous ([X | sXA^T] [W | B]^T of
 // the forward, [G | sGB] [W^T | A^T]^T of the input gradient through W^T;
 // page "UnSloth加速微调体验…", section 算子融合), 256 x 256 tiles, 4 waves of
-// 128 x 128, 32-deep contraction stages.
+// 128 x 128, 64-deep contraction stages.
 //
 // Global tiles go straight to LDS: buffer_load_dwordx4 with the lds flag
-// writes each lane's 16 bytes at M0 + 16 lane of the LDS with no register
-// staging and no LDS write instruction, so the LDS port serves only the
-// fragment reads and the DMA stream.  The DMA runs LEAD = 3 stages ahead
-// through a ring of 4 LDS buffers of 32 KiB (A 256 rows x 64 bytes, then B):
-// measured on MI355X, a lead of 2 leaves the waves waiting on HBM latency, a
-// lead of 4 (five buffers, all 160 KiB) gains nothing over 3.
+// writes each lane's 16 bytes at M0 + 16 lane with no register staging and
+// no LDS write instruction.  One instruction moves 8 rows x 128 bytes, whole
+// cache lines (measured on MI355X: 64-byte row pieces, as a 32-deep stage
+// reads them, cost about 10% of the GEMM's time).
 //
-// Stage t, ring buffer t % 4, two contraction steps of 16 MFMAs each:
-//   step 0: MFMAs of step 0; the 8 fragment reads of step 1 (after the first
-//           8 MFMAs), then 4 DMAs of stage t+3's A tile into buffer (t+3) % 4
-//   wait for stage t+1's DMAs (vmcnt), barrier
-//   step 1: MFMAs of step 1; the 8 reads of stage t+1's step-0 fragments,
-//           then 4 DMAs of stage t+3's B tile
-// Buffer (t+3) % 4 = (t-1) % 4 was last read in stage t-1's step 0, which
-// every wave finished before the barrier of stage t-1, so the DMA may
-// overwrite it.  vmcnt counts a wave's own DMAs, completed in order: at
-// stage t's barrier stages t+2 (8) and t+3's A (4) may still fly.
+// LDS is a ring of 5 slots of 32 KiB, each one operand tile of a stage (256
+// rows x 128 bytes): A of stage t in slot 2t mod 5, B in slot 2t+1 mod 5.
+// Stage t runs four contraction steps of 16 MFMAs:
+//   step 0: reads of step 1's fragments; DMA of half of A(t+2)
+//   step 1: reads of step 2's fragments; DMA of the other half of A(t+2)
+//   step 2: reads of step 3's fragments
+//   wait for this wave's DMAs of stage t+1 (vmcnt), barrier
+//   step 3: reads of stage t+1's step-0 fragments; DMA of B(t+2)
+// A(t+2) goes to slot 2t+4 = slot of B(t-1), free since the barrier of stage
+// t-1; B(t+2) to slot 2t+5 = slot of A(t), free since the barrier just
+// passed (every read of stage t happened before it).  vmcnt counts a wave's
+// own DMAs, which complete in order: at stage t's wait only A(t+2) (8) may
+// still fly.  One barrier per 64-deep stage.
 //
-// DMA lane mapping: instruction i (< 4) of wave w moves tile rows
-// 16 (4 w + i) + lane / 4, lane lands at byte 16 lane of the instruction's
-// 1 KiB block, i.e. row 16 (4 w + i) + lane / 4, physical chunk lane & 3.
-// The LDS row holds logical 16-byte chunk c at physical chunk
-// c ^ ((row >> 2) & 3), so the lane fetches logical chunk
-// (lane & 3) ^ ((lane >> 4) & 3).  A fragment read (32 rows, one chunk each,
-// rows l32 of a 32-row block) then touches 8 rows per bank group and is
-// conflict-free (checked for every lane by a CPU model of the banks).
+// Slot layout: row r at byte 128 r, logical 16-byte chunk c at physical chunk
+// c ^ ((r >> 1) & 7).  DMA instruction i (< 8) of wave w moves rows
+// 64 w + 8 i + lane / 8; the lane lands at physical chunk lane & 7, so it
+// fetches logical chunk (lane & 7) ^ ((lane >> 4) | 4 (i & 1)).  Fragment
+// reads (32 rows l32 of a block, chunk 2 s + l / 32) are conflict-free (a CPU
+// model of the banks checks every lane).
 //
 // SwiGLU (EPI_SWIGLU): B-tile rows 32 b .. 32 b + 31 come from the gate's
 // weight for even b and from the up's for odd b, rows n0 / 2 + 32 (b / 2) +
 // .. of each, so MFMA blocks j = 0, 2 of a wave hold gate outputs and
 // j = 1, 3 the up outputs of the same columns.  Wave w's B instructions
-// i = 0, 1 move gate rows n0 / 2 + 32 w + 16 i + lane / 4, i = 2, 3 the same
-// rows of the up weight.  In the rank segment, columns [0, k2_split) belong
-// to the gate's B and [k2_split, K2) to the up's (its own columns from 0).
+// i < 4 move gate rows n0 / 2 + 32 w + 8 i + lane / 8, i >= 4 the same rows
+// of the up weight.  In the rank segment, columns [0, k2_split) belong to the
+// gate's B and [k2_split, K2) to the up's (its own columns from 0).
 #pragma once
 
 #include <type_traits>
@@ -48,10 +47,11 @@
 namespace lora {
 
 namespace w4nt {
-constexpr int BK = 32;
-constexpr int A_BYTES = w4::BM * 64, B_BYTES = w4::BN * 64, STAGE = A_BYTES + B_BYTES;
-constexpr int NBUF = 4, LEAD = NBUF - 1;
-constexpr int LDS = NBUF * STAGE;
+constexpr int BK = 64;
+constexpr int SLOT = w4::BM * 128;  // one operand tile of a stage
+constexpr int NSLOT = 5;
+constexpr int LDS = NSLOT * SLOT;
+static_assert(w4::BM == w4::BN, "A and B tiles share the slot size");
 static_assert(LDS >= 2 * w4::BM * 64 * 4, "the RoPE epilogue stages its cos/sin rows in the ring");
 
 // s_waitcnt immediate: vmcnt = n (0..63), expcnt and lgkmcnt unconstrained
@@ -64,10 +64,8 @@ template <int EPI>
 __global__ void __launch_bounds__(w4::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 gemm_w4_nt_kernel(const GemmArgs p) {
   using namespace w4;
-  using w4nt::A_BYTES;
-  using w4nt::LEAD;
-  using w4nt::NBUF;
-  using w4nt::STAGE;
+  using w4nt::NSLOT;
+  using w4nt::SLOT;
   using w4nt::vmcnt_imm;
   constexpr int BKS = w4nt::BK;
   static_assert(EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_SWIGLU, "store, RoPE or SwiGLU epilogue");
@@ -87,10 +85,12 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   const int nk = nk1 + (int)((p.K2 + BKS - 1) / BKS);
 
   // ---- DMA addressing ----
-  // dr: the lane's row within an instruction's 16, dc: its logical chunk.
-  // Row offsets of instruction 0; instruction i adds i * is (SwiGLU B:
-  // (i & 1) * is, the weight chosen by i >> 1).
-  const int dr = lane >> 2, dc = (lane & 3) ^ ((lane >> 4) & 3);
+  // dr: the lane's row within an instruction's 8; dce / dco: its logical
+  // chunk for even / odd instructions.  Offsets of instruction 0 (even) and
+  // 1 (odd); instruction i adds (i >> 1) * is (SwiGLU B: ((i & 3) >> 1) * is,
+  // the weight chosen by i >> 2).
+  const int dr = lane >> 3;
+  const int dce = (lane & 7) ^ (lane >> 4), dco = (lane & 7) ^ ((lane >> 4) | 4);
   const int64_t nb0 = SW ? n0 / 2 : n0;  // first weight row of the tile
   const int rowa = 64 * wave + dr;
   const int rowb = SW ? 32 * wave + dr : 64 * wave + dr;
@@ -100,77 +100,84 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   const char* gb2 = reinterpret_cast<const char*>(p.b2) + nb0 * p.ldb2 * 2;
   const char* gb1u = SW ? reinterpret_cast<const char*>(p.b1u) + nb0 * p.ldb1 * 2 : gb1;
   const char* gb2u = SW ? reinterpret_cast<const char*>(p.b2u) + nb0 * p.ldb2u * 2 : gb2;
-  const uint32_t va1 = (uint32_t)(rowa * p.lda1 * 2 + dc * 16);
-  const uint32_t va2 = (uint32_t)(rowa * p.lda2 * 2 + dc * 16);
-  const uint32_t vb1 = (uint32_t)(rowb * p.ldb1 * 2 + dc * 16);
-  const uint32_t vb2 = (uint32_t)(rowb * p.ldb2 * 2 + dc * 16);
-  const uint32_t vb2u = SW ? (uint32_t)(rowb * p.ldb2u * 2) : 0u;
-  // strides between a wave's instructions, pinned in scalar registers
+  // row parts of the lane offsets (+ 8 rows for odd instructions)
+  const uint32_t ra1 = (uint32_t)(rowa * p.lda1 * 2), ra2 = (uint32_t)(rowa * p.lda2 * 2);
+  const uint32_t rb1 = (uint32_t)(rowb * p.ldb1 * 2), rb2 = (uint32_t)(rowb * p.ldb2 * 2);
+  const uint32_t rb2u = SW ? (uint32_t)(rowb * p.ldb2u * 2) : 0u;
+  const uint32_t va1[2] = {ra1 + (uint32_t)(dce * 16), ra1 + (uint32_t)(8 * p.lda1 * 2 + dco * 16)};
+  const uint32_t vb1[2] = {rb1 + (uint32_t)(dce * 16), rb1 + (uint32_t)(8 * p.ldb1 * 2 + dco * 16)};
+  // strides between a wave's instruction pairs, pinned in scalar registers
   const uint32_t isa1 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.lda1 * 2));
   const uint32_t isa2 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.lda2 * 2));
   const uint32_t isb1 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb1 * 2));
   const uint32_t isb2 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb2 * 2));
   const uint32_t isb2u = SW ? __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb2u * 2)) : 0u;
+  const uint32_t oda2 = (uint32_t)(8 * p.lda2 * 2), odb2 = (uint32_t)(8 * p.ldb2 * 2);
+  const uint32_t odb2u = SW ? (uint32_t)(8 * p.ldb2u * 2) : 0u;
   const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
   const int k2s = SW ? __builtin_amdgcn_readfirstlane((int)p.k2_split) : 0;
 
-  // One DMA: stage u, operand op (0 A, 1 B), instruction i, ring buffer b.
+  // One DMA: stage u, operand op (0 A, 1 B), instruction i (< 8), slot s.
   // SEG2: u is a stage of the rank segment, whose chunks at or past K2 come
   // back as zero through an out-of-range offset.
-  auto dma = [&](int u, int b, int op, int i, auto seg2_c) {
+  auto dma = [&](int u, int s, int op, int i, auto seg2_c) {
     constexpr bool SEG2 = decltype(seg2_c)::value;
-    const bool up = SW && op == 1 && i >= 2;
-    const int ii = (SW && op == 1) ? (i & 1) : i;
+    const bool up = SW && op == 1 && i >= 4;
+    const int odd = i & 1;
+    const int pair = (SW && op == 1) ? ((i & 3) >> 1) : (i >> 1);
+    const int dc = odd ? dco : dce;
     const char* base;
     uint32_t vo, is;
     if constexpr (!SEG2) {
       base = (op == 0 ? ga1 : (up ? gb1u : gb1)) + (int64_t)u * (BKS * 2);
-      vo = op == 0 ? va1 : vb1;
+      vo = op == 0 ? va1[odd] : vb1[odd];
       is = op == 0 ? isa1 : isb1;
     } else {
       const int tt = u - nk1;
       const int kk = tt * BKS + 8 * dc;  // the lane's first rank column
+      const uint32_t kc = (uint32_t)(tt * BKS * 2 + dc * 16);
       if (op == 0) {
         base = ga2;
-        vo = kk < k2 ? va2 + (uint32_t)(tt * BKS * 2) : w4::OOB;
+        vo = kk < k2 ? ra2 + (odd ? oda2 : 0u) + kc : w4::OOB;
         is = isa2;
       } else if (!SW) {
         base = gb2;
-        vo = kk < k2 ? vb2 + (uint32_t)(tt * BKS * 2) : w4::OOB;
+        vo = kk < k2 ? rb2 + (odd ? odb2 : 0u) + kc : w4::OOB;
         is = isb2;
       } else if (!up) {
         base = gb2;
-        vo = kk < k2s ? vb2 + (uint32_t)(tt * BKS * 2) : w4::OOB;
+        vo = kk < k2s ? rb2 + (odd ? odb2 : 0u) + kc : w4::OOB;
         is = isb2;
       } else {
         base = gb2u;
-        vo = kk >= k2s && kk < k2 ? vb2u + (uint32_t)((kk - k2s) * 2) : w4::OOB;
+        vo = kk >= k2s && kk < k2 ? rb2u + (odd ? odb2u : 0u) + (uint32_t)((kk - k2s) * 2) : w4::OOB;
         is = isb2u;
       }
     }
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, BIG, 0x00020000);
-    char* dst = smem + b * STAGE + op * A_BYTES + (4 * wave + i) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, (int)(vo + (uint32_t)ii * is), 0, 0, 0);
+    char* dst = smem + s * SLOT + (8 * wave + i) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, (int)(vo + (uint32_t)pair * is), 0, 0, 0);
   };
 
   // ---- fragments ----
-  // lane reads row 32 blk + l32 of its wave's half, logical chunk 2 s + hh
-  const int sw = (l32 >> 2) & 3;
-  const uint32_t oa0 = (uint32_t)(wm * TM + l32) * 64 + (uint32_t)(((0 + hh) ^ sw) << 4);
-  const uint32_t oa1 = (uint32_t)(wm * TM + l32) * 64 + (uint32_t)(((2 + hh) ^ sw) << 4);
-  const uint32_t ob0 = (uint32_t)A_BYTES + (uint32_t)(wn * TN + l32) * 64 + (uint32_t)(((0 + hh) ^ sw) << 4);
-  const uint32_t ob1 = (uint32_t)A_BYTES + (uint32_t)(wn * TN + l32) * 64 + (uint32_t)(((2 + hh) ^ sw) << 4);
+  // A rows wm*TM + 32 blk + l32 and B rows wn*TN + 32 blk + l32 all have
+  // (row >> 1) & 7 = (l32 >> 1) & 7.
+  const uint32_t ra = (uint32_t)(wm * TM + l32) * 128;
+  const uint32_t rb = (uint32_t)(wn * TN + l32) * 128;
+  const int swz = (l32 >> 1) & 7;
   bf16x8 fa[2][FM], fb[2][FN];
-  // read k of step s (k < 4: A block k, else B block k - 4) of buffer b into set f
-  auto rd1 = [&](int b, int s, auto fsel, int k) {
+  // read k of step s (k < 4: A block k from slot sa, else B block k - 4 from
+  // slot sb) into set f
+  auto rd1 = [&](int sa, int sb, int s, auto fsel, int k) {
     constexpr int f = decltype(fsel)::value;
-    const char* sb = smem + b * STAGE;
+    const uint32_t c = (uint32_t)(((2 * s + hh) ^ swz) << 4);
     if (k < FM)
-      fa[f][k] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + (s ? oa1 : oa0) + k * 32 * 64));
+      fa[f][k] = __builtin_bit_cast(bf16x8,
+                                    *reinterpret_cast<const u32x4*>(smem + sa * SLOT + ra + c + k * 32 * 128));
     else
-      fb[f][k - FM] =
-          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sb + (s ? ob1 : ob0) + (k - FM) * 32 * 64));
+      fb[f][k - FM] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(smem + sb * SLOT + rb + c + (k - FM) * 32 * 128));
   };
 
   f32x16 acc[FM][FN];
@@ -194,59 +201,74 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   using F_ = std::false_type;
 
   if (nk > 0) {
-    // prologue: stages 0 .. LEAD-1 in flight; wait for stage 0 only
+    // prologue: stages 0 and 1 in flight (slots 0 .. 3); wait for stage 0
 #pragma unroll
-    for (int u = 0; u < LEAD; ++u) {
+    for (int u = 0; u < 2; ++u) {
       if (u < nk) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (u < nk1) {
-            dma(u, u, 0, i, F_{});
-            dma(u, u, 1, i, F_{});
-          } else {
-            dma(u, u, 0, i, T_{});
-            dma(u, u, 1, i, T_{});
+        for (int op = 0; op < 2; ++op)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            if (u < nk1)
+              dma(u, 2 * u + op, op, i, F_{});
+            else
+              dma(u, 2 * u + op, op, i, T_{});
           }
-        }
       }
     }
-    static_assert(LEAD == 3, "prologue waits are written for a lead of 3");
-    if (nk >= 3)
+    if (nk >= 2)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
-    else if (nk == 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     lds_barrier();
 #pragma unroll
-    for (int k = 0; k < 8; ++k) rd1(0, 0, I0{}, k);
+    for (int k = 0; k < 8; ++k) rd1(0, 1, 0, I0{}, k);
 
-    // One stage.  ISSUE: 0 none, 1 stage t + LEAD of the main segment, 2 of
-    // the rank segment.  VM: DMAs that may still fly at the mid-stage wait
-    // (everything after stage t+1).  NEXT: stage t+1 exists.
-    auto stage = [&](int t, auto issue_c, auto vm_c, auto next_c) {
-      constexpr int ISSUE = decltype(issue_c)::value, VM = decltype(vm_c)::value;
+    // One stage.  ISSUE: 0 none, 1 stage t+2 of the main segment, 2 of the
+    // rank segment.  NEXT: stage t+1 exists.
+    auto stage = [&](int t, auto issue_c, auto next_c) {
+      constexpr int ISSUE = decltype(issue_c)::value;
       constexpr bool NEXT = decltype(next_c)::value;
       using S2 = std::integral_constant<bool, ISSUE == 2>;
-      const int cur = t % NBUF, nxt = (t + 1) % NBUF, far = (t + LEAD) % NBUF;
+      const int sa = (2 * t) % NSLOT, sb = (2 * t + 1) % NSLOT;
+      const int na = (2 * t + 2) % NSLOT, nb = (2 * t + 3) % NSLOT;
+      const int fa2 = (2 * t + 4) % NSLOT;  // A(t+2): the slot of B(t-1)
+      const int fb2 = sa;                   // B(t+2): the slot of A(t)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         mf(I0{}, q);
         if (q < 8)
-          rd1(cur, 1, I1{}, q);
+          rd1(sa, sb, 1, I1{}, q);
         else if (ISSUE && (q & 1) == 0)
-          dma(t + LEAD, far, 0, (q - 8) >> 1, S2{});
+          dma(t + 2, fa2, 0, (q - 8) >> 1, S2{});
         fence();
       }
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(VM));
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        mf(I1{}, q);
+        if (q < 8)
+          rd1(sa, sb, 2, I0{}, q);
+        else if (ISSUE && (q & 1) == 0)
+          dma(t + 2, fa2, 0, 4 + ((q - 8) >> 1), S2{});
+        fence();
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        mf(I0{}, q);
+        if (q < 8) rd1(sa, sb, 3, I1{}, q);
+        fence();
+      }
+      // stage t+1 has landed (only A(t+2) may still fly), and every wave is
+      // done with stage t's slots
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(ISSUE ? 8 : 0));
       lds_barrier();
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         mf(I1{}, q);
         if (q < 8) {
-          if (NEXT) rd1(nxt, 0, I0{}, q);
-        } else if (ISSUE && (q & 1) == 0) {
-          dma(t + LEAD, far, 1, (q - 8) >> 1, S2{});
+          if (NEXT) rd1(na, nb, 0, I0{}, q);
+        } else if (ISSUE) {
+          dma(t + 2, fb2, 1, q - 8, S2{});
         }
         fence();
       }
@@ -255,13 +277,10 @@ gemm_w4_nt_kernel(const GemmArgs p) {
     using N1 = std::integral_constant<int, 1>;
     using N2 = std::integral_constant<int, 2>;
     int t = 0;
-    for (; t + LEAD < nk1; ++t) stage(t, N1{}, std::integral_constant<int, 12>{}, T_{});
-    for (; t + LEAD < nk; ++t) stage(t, N2{}, std::integral_constant<int, 12>{}, T_{});
-    // the last stages issue nothing; with j stages after it, a stage lets the
-    // DMAs of j - 1 of them fly
-    if (nk - 1 - t == 2) stage(t++, N0{}, std::integral_constant<int, 8>{}, T_{});
-    if (nk - 1 - t == 1) stage(t++, N0{}, std::integral_constant<int, 0>{}, T_{});
-    stage(t, N0{}, std::integral_constant<int, 0>{}, F_{});
+    for (; t + 2 < nk1; ++t) stage(t, N1{}, T_{});
+    for (; t + 2 < nk; ++t) stage(t, N2{}, T_{});
+    if (t + 1 < nk) stage(t++, N0{}, T_{});
+    stage(t, N0{}, F_{});
   }
 
   // (the RoPE epilogue reuses the ring for its cos/sin rows after a barrier)
