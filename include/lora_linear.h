@@ -350,9 +350,14 @@ int lora_transpose(const void* src, int64_t rows, int64_t cols, void* dst, void*
  *     event creation fails.
  *   lora_profile_query: totals over the recorded launches of `kind`:
  *     summed event time in ms, launch count, summed FLOP, summed bytes.
+ *   lora_profile_only: from now on record only launches of `kind` (-1: every
+ *     kind, the state at load); the others run without events, so a timed run
+ *     can bracket one kernel kind without slowing the rest.  LORA_ERR_SHAPE if
+ *     kind is outside [-1, lora_profile_kinds()).  No HIP call.
  */
 int lora_profile_begin(int max_launches);
 int lora_profile_end(void);
+int lora_profile_only(int kind);
 int lora_profile_kinds(void);
 const char* lora_profile_kind_name(int kind);
 int lora_profile_query(int kind, double* total_ms, int* count, double* total_flop, double* total_bytes);

@@ -67,6 +67,7 @@ _SIGS = {
     "lora_transpose": ([_vp, _i64, _i64, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),
     "lora_profile_end": ([], _int),
+    "lora_profile_only": ([_int], _int),
     "lora_profile_kinds": ([], _int),
     "lora_profile_kind_name": ([_int], ctypes.c_char_p),
     "lora_profile_query": ([_int, ctypes.POINTER(_dbl), ctypes.POINTER(_int), ctypes.POINTER(_dbl),
@@ -152,6 +153,15 @@ def profile_begin(max_launches: int = 4096):
 
 def profile_end():
     _check("lora_profile_end", lib().lora_profile_end())
+
+
+def profile_only(kind_name=None):
+    """Record only launches of the named kind (None: every kind)."""
+    k = -1
+    if kind_name is not None:
+        names = [lib().lora_profile_kind_name(i).decode() for i in range(lib().lora_profile_kinds())]
+        k = names.index(kind_name)
+    _check("lora_profile_only", lib().lora_profile_only(k))
 
 
 def mfma_rate(iters: int = 4096, blocks: int = 1024, device=None) -> float:

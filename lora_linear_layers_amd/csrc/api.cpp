@@ -280,13 +280,14 @@ struct Profiler {
   std::vector<hipEvent_t> ev;  // 2 per slot
   std::vector<ProfEntry> ent;
   size_t n = 0;
+  int only = -1;  // record only this kind (-1: all)
 } g_prof;
 
 template <class F>
 hipError_t timed(int kind, double flop, double bytes, hipStream_t st, F&& f) {
   if (!g_prof.on) return f();
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  if (!g_prof.on || g_prof.n >= g_prof.ent.size()) return f();
+  if (!g_prof.on || g_prof.n >= g_prof.ent.size() || (g_prof.only >= 0 && kind != g_prof.only)) return f();
   const size_t i = g_prof.n++;
   if (hipEventRecord(g_prof.ev[2 * i], st) != hipSuccess) return hipErrorUnknown;
   hipError_t e = f();
@@ -1283,6 +1284,13 @@ int lora_profile_begin(int max_launches) {
 int lora_profile_end(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
   g_prof.on = false;
+  return LORA_OK;
+}
+
+int lora_profile_only(int kind) {
+  if (kind < -1 || kind >= K_PROF_COUNT) return LORA_ERR_SHAPE;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.only = kind;
   return LORA_OK;
 }
 

@@ -204,6 +204,14 @@ def test_mfma_rate_validation(lib):
     assert lib.lora_mfma_rate(4, 4, P + 4, None) == EALIGN
 
 
+def test_profile_only_validation(lib):
+    n = lib.lora_profile_kinds()
+    assert lib.lora_profile_only(-2) == ESHAPE
+    assert lib.lora_profile_only(n) == ESHAPE
+    assert lib.lora_profile_only(n - 1) == 0
+    assert lib.lora_profile_only(-1) == 0
+
+
 def test_merge_validation(lib):
     def call(dtype=1, d_out=64, d_in=64, r=8, W=P, A=P, B=P, out=P, ws=P, wsb=1 << 20):
         return lib.lora_merge(dtype, d_out, d_in, r, 1.0, W, A, B, out, ws, wsb, None)
