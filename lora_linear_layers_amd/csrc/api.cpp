@@ -72,13 +72,17 @@ struct Layout {
 // 256x256 tiles when they still give at least one tile per CU, else 128x128.
 bool use_big(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; }
 
-// Split of the contraction of a bf16 rank-r panel (256 x 64 tiles): about 1.5
-// workgroups per CU, at most 32 splits, each a multiple of 64 and at least 8
-// stages long (4 when a few tokens leave fewer than 16 tiles).
+// Split of the contraction of a bf16 rank-r panel: up to 128 columns, 256-row
+// tiles with every column (panel_dma_kernel) and about one block per CU;
+// wider panels, 256 x 64 tiles and about 1.5 per CU.  At most 32 splits, each
+// a multiple of 64 and at least 8 stages long (4 when a few tokens leave
+// fewer than 16 tiles).
 void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit) {
-  int64_t tiles = cdiv(M, 256) * cdiv(r8, 64);
+  // up to 128 columns: one 256-row tile holds every column and one block per
+  // CU runs (160 KB of LDS each); wider panels take 64-column tiles
+  int64_t tiles = r8 <= 128 ? cdiv(M, PANEL_BM) : cdiv(M, 256) * cdiv(r8, 64);
   if (tiles < 1) tiles = 1;
-  int64_t s = cdiv(384, tiles);
+  int64_t s = cdiv(r8 <= 128 ? 256 : 384, tiles);
   int64_t smax = tiles < 16 ? K / 256 : K / 512;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;

@@ -1,0 +1,191 @@
+// gemm_panel.h - the rank-r panel GEMM: fp32 split partials of X R^T for a
+// tall X [M, K] (bf16, row-major) and a short R [r, K] (the adapter's A, a
+// group's stacked A's, or B^T for the backward's dY B), the first step of
+// both the forward (X A^T) and the backward's recompute and dY B (page
+// "UnSloth加速微调体验…", sections 算子融合 and 反向传播优化).
+//
+// The work is a stream of X: 2 r FLOP per element read, far below the
+// machine balance, so the kernel is built for HBM bandwidth (on MI355X a
+// plain streaming read reaches about 6.1 TB/s, from L2 about 21 TB/s through
+// the LDS DMA path).  A BM-row tile covers every panel column (BN = 64 or 128
+// >= r), so X is read exactly once; global tiles go straight to LDS
+// (buffer_load_dwordx4 ... lds, 8 rows x 128 bytes per instruction) through a
+// ring of NS stages issued NS - 1 stages ahead, 100+ KB in flight per CU.
+// The contraction is split over gridDim / tiles_m blocks per row tile; split
+// z writes its fp32 partial to C + z part_stride (rows at or past m_store and
+// columns at or past n_store are not written), and panel_reduce_kernel sums
+// the splits in order.  BM = 128 (launch.h): against 64 it halves the re-reads
+// of R (from L2) per byte of X, against 256 it halves the splits, so the
+// fp32 partials and the per-block pipeline fill; measured on the Llama-3-8B
+// MLP panels the three differ by 5 %, 128 first.
+//
+// Stage t (64-deep): wait for this wave's DMAs of stage t (vmcnt: stages
+// t+1 .. t+NS-2 may still fly), barrier (every wave's stage t landed, every
+// wave done with stage t-1), issue stage t+NS-1 into stage t-1's slot, then
+// four contraction steps.  Stages past the end issue DMAs at an out-of-range
+// offset (zeros into a free slot), so every wait has the same count; the
+// kernel waits for them before it ends.  Rows at or past m_load and
+// contraction chunks at or past the split's end read zero the same way.
+//
+// Waves: 4 x 1 over a 256-row tile, else 2 x 2; each wave's part is FM x FN
+// blocks of v_mfma_f32_32x32x16_bf16.  LDS rows are 128 bytes with 16-byte
+// chunk c at chunk c ^ ((row >> 1) & 7); DMA instruction i of wave w moves
+// rows 8 (i + IW w) + lane / 8 (IW instructions per wave, even), the lane
+// landing at physical chunk lane & 7, i.e. logical chunk
+// (lane & 7) ^ ((lane >> 4) | 4 (i & 1)) (the same lane mapping as the
+// whole-tile NT kernel).
+#pragma once
+
+#include <type_traits>
+
+#include "gemm_w4.h"
+
+namespace lora {
+
+namespace pdma {
+constexpr int BK = 64, NT = 256;
+template <int BM, int BN>
+struct Cfg {
+  static constexpr int A_BYTES = BM * 128, B_BYTES = BN * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NS0 = (160 * 1024) / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;  // ring stages
+  static constexpr int IA = BM / 8 / 4;         // A instructions per wave
+  static constexpr int IB = BN / 8 / 4;         // B instructions per wave
+  static constexpr int PER = IA + IB;           // DMAs per wave per stage
+  // waves: 4 x 1 over 256 rows, else 2 x 2
+  static constexpr int WM = BM == 256 ? 4 : 2, WN = 4 / WM;
+  static constexpr int FM = BM / WM / 32, FN = BN / WN / 32;  // MFMA blocks per wave
+  static_assert(IA % 2 == 0 && IB % 2 == 0, "row parity pattern of the DMA lane mapping");
+  static_assert(FM >= 1 && FN >= 1, "wave tile of at least one 32 x 32 block");
+};
+
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
+}  // namespace pdma
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(pdma::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+panel_dma_kernel(const GemmArgs p) {
+  using namespace pdma;
+  using C = Cfg<BM, BN>;
+  constexpr int NS = C::NS, LEAD = NS - 1, FM = C::FM, FN = C::FN;
+  constexpr int A_BYTES = C::A_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * C::STAGE];
+  asm volatile("" ::: "a0");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int mt = (int)(blockIdx.x % p.tiles_m), z = (int)(blockIdx.x / p.tiles_m);
+  const int64_t m0 = (int64_t)mt * BM;
+  const int64_t kbeg = (int64_t)z * p.k_split;
+  const int64_t kend = kbeg + p.k_split < p.K1 ? kbeg + p.k_split : p.K1;
+  const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
+
+  // ---- DMA addressing ----
+  const int dr = lane >> 3;
+  const int dce = (lane & 7) ^ (lane >> 4), dco = (lane & 7) ^ ((lane >> 4) | 4);
+  const char* ga = reinterpret_cast<const char*>(p.a1) + (m0 * p.lda1 + kbeg) * 2;
+  const char* gb = reinterpret_cast<const char*>(p.b1) + kbeg * 2;
+  const int klen = (int)(kend - kbeg);
+  const int64_t mrem = p.m_load - m0;  // rows of X left from the tile's first
+  const int64_t nrem = p.n_load;       // rows of R
+  // A instruction i: rows 8 (i + IA w) + dr; B instruction i: 8 (i + IB w) + dr
+  auto dma = [&](int u, int s, int op, int i) {
+    const int odd = i & 1;
+    const int dc = odd ? dco : dce;
+    const int row = 8 * (i + (op == 0 ? C::IA : C::IB) * wave) + dr;
+    const int64_t ld = op == 0 ? p.lda1 : p.ldb1;
+    const int kk = u * BK + 8 * dc;
+    const bool ok = kk < klen && row < (op == 0 ? mrem : nrem);
+    uint32_t vo = ok ? (uint32_t)(row * ld * 2 + kk * 2) : w4::OOB;
+    asm volatile("" : "+v"(vo));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(op == 0 ? ga : gb), (short)0, w4::BIG, 0x00020000);
+    char* dst = smem + s * C::STAGE + (op == 0 ? 0 : A_BYTES) + (8 * (i + (op == 0 ? C::IA : C::IB) * wave)) * 128;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)vo, 0, 0,
+                                             0);
+  };
+  auto issue = [&](int u) {
+    const int s = u % NS;
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) dma(u, s, 0, i);
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i) dma(u, s, 1, i);
+  };
+
+  // ---- fragments ----
+  const int swz = (l32 >> 1) & 7;
+  const uint32_t ra = (uint32_t)(wm * (BM / C::WM) + l32) * 128;
+  const uint32_t rb = (uint32_t)A_BYTES + (uint32_t)(wn * (BN / C::WN) + l32) * 128;
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto rd = [&](int s, int st, auto fsel) {
+    constexpr int f = decltype(fsel)::value;
+    const uint32_t c = (uint32_t)(((2 * st + hh) ^ swz) << 4);
+    const char* base = smem + s * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[f][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + ra + c + i * 32 * 128));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[f][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + rb + c + j * 32 * 128));
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto step = [&](auto fsel) {
+    constexpr int f = decltype(fsel)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  if (nk > 0) {
+#pragma unroll
+    for (int u = 0; u < LEAD; ++u) issue(u);
+    for (int t = 0; t < nk; ++t) {
+      const int s = t % NS;
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(C::PER * (LEAD - 1)));
+      lds_barrier();
+      issue(t + LEAD);  // into stage t-1's slot; zeros past the end
+      rd(s, 0, I0{});
+      rd(s, 1, I1{});
+      step(I0{});
+      rd(s, 2, I0{});
+      step(I1{});
+      rd(s, 3, I1{});
+      step(I0{});
+      step(I1{});
+    }
+    // the DMAs issued past the end must land before the block's LDS is freed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  // fp32 partial: acc[i][j][v] = C[m0 + wm BM / WM + 32 i + 8 (v / 4) + 4 hh + v % 4,
+  //                                  wn BN / WN + 32 j + l32]
+  float* out = reinterpret_cast<float*>(p.c) + (int64_t)z * p.part_stride;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int64_t row = m0 + wm * (BM / C::WM) + 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (row >= p.m_store) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = wn * (BN / C::WN) + 32 * j + l32;
+        if (col < p.n_store) out[row * p.ldc + col] = acc[i][j][v];
+      }
+    }
+}
+
+}  // namespace lora

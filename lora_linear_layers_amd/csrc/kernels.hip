@@ -9,6 +9,7 @@
 #include "gemm.h"
 #include "gemm_w4.h"
 #include "gemm_w4_nt.h"
+#include "gemm_panel.h"
 #include "launch.h"
 
 namespace lora {
@@ -48,6 +49,25 @@ hipError_t run_whole(GemmArgs a, hipStream_t st) {
   else
     hipLaunchKernelGGL((gemm_w4_nt_kernel<EPI>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
   return hipGetLastError();
+}
+
+// rank-r panel split partials (K1 only, at most 128 panel columns): one
+// 256-row tile per block and split, every column in the tile
+hipError_t run_panel(GemmArgs a, int splits, hipStream_t st) {
+  constexpr int BM = PANEL_BM;
+  a.tiles_m = (int)((a.m_store + BM - 1) / BM);
+  const int64_t nblocks = (int64_t)a.tiles_m * splits;
+  if (nblocks <= 0) return hipSuccess;
+  if (a.n_store <= 64)
+    hipLaunchKernelGGL((panel_dma_kernel<BM, 64>), dim3((unsigned)nblocks), dim3(pdma::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((panel_dma_kernel<BM, 128>), dim3((unsigned)nblocks), dim3(pdma::NT), 0, st, a);
+  return hipGetLastError();
+}
+
+bool panel_fits(const GemmArgs& a) {
+  const int64_t ld = std::max(a.lda1, a.ldb1);
+  return a.K2 == 0 && a.n_store <= 128 && a.n_load <= a.n_store && ld * 2 * 256 < (int64_t)w4::BIG;
 }
 
 using bf = uint16_t;
@@ -122,7 +142,9 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_F32_PANEL_NT_STORE_T: return run<float, 64, 64, 2, 2, false, EPI_STORE_T, BL_PLAIN>(a, splits, st);
     case G_F32_PANEL_NN_BOTH: return run<float, 64, 64, 2, 2, true, EPI_STORE_BOTH, BL_PLAIN>(a, splits, st);
     case G_F32_SPLIT_NN_PARTIAL: return run<float, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
-    case G_BF16_PANEL_SPLIT_NT: return run<bf, 256, 64, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_BF16_PANEL_SPLIT_NT:
+      if (panel_fits(a)) return run_panel(a, splits, st);
+      return run<bf, 256, 64, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_PARTIAL: return run<bf, 128, 128, 4, 1, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_NF4_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_NF4>(a, splits, st);

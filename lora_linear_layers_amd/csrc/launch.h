@@ -9,6 +9,9 @@
 
 namespace lora {
 
+// rows per tile of the rank-r panel kernel (the split choice in api.cpp uses it)
+constexpr int PANEL_BM = 128;
+
 // GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
 // epilogue.  "BIG" = 256x256 tiles, "MED" = 128x128 (4 waves), "PANEL" =
 // 64x64 rank-r panels, "SPLIT" = 64x256 split-contraction partials,

@@ -50,9 +50,10 @@ def test_version_and_strerror(lib):
 
 def test_workspace_sizes(lib):
     f = lib.lora_workspace_bytes
-    # forward (bf16): the rank-r panel's split partials (8 splits of the 4096
-    # contraction, fp32 [8192, 64] each) plus the [M, r8] bf16 panel
-    assert f(_lib.OP_FWD, 1, 8192, 4096, 14336, 64) == 8 * 8192 * 64 * 4 + 8192 * 64 * 2
+    # forward (bf16): the rank-r panel's split partials (64 row tiles of 128,
+    # so 4 splits of the 4096 contraction for about one block per CU, fp32
+    # [8192, 64] each) plus the [M, r8] bf16 panel
+    assert f(_lib.OP_FWD, 1, 8192, 4096, 14336, 64) == 4 * 8192 * 64 * 4 + 8192 * 64 * 2
     # r not a multiple of 8 adds a padded copy of B
     assert f(_lib.OP_FWD, 1, 100, 64, 64, 3) > f(_lib.OP_FWD, 1, 100, 64, 64, 8) - 100 * 8 * 2
     bwd = f(_lib.OP_BWD, 1, 8192, 4096, 14336, 64)
