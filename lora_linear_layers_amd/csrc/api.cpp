@@ -11,6 +11,7 @@
 
 #include "../../include/lora_linear.h"
 #include "launch.h"
+#include "skinny.h"
 
 using namespace lora;
 
@@ -250,6 +251,7 @@ enum ProfKind : int {
   K_SWIGLU,
   K_MASK,
   K_TRANSPOSE_W,
+  K_SKINNY,
   K_PROF_COUNT
 };
 
@@ -268,7 +270,7 @@ const char* kind_name(int k) {
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
       "copy_rows",                  "split_finish",               "swiglu_elementwise",
-      "dropout_mask_copy",          "transpose_w"};
+      "dropout_mask_copy",          "transpose_w",                "skinny_fwd"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -369,6 +371,24 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  // few tokens: panel, GEMM, rank term and epilogue in one launch
+  // (bf16 W; an NF4 W keeps the split path's load-stage dequantisation)
+  const int smode = rope ? sk::ROPE : sk::PLAIN;
+  if (!f32 && !nf4 && !Pext && !Xa && skinny_fits(M, d_in, d_out, r, smode)) {
+    SkinnyArgs sa;
+    memset(&sa, 0, sizeof(sa));
+    sa.X = static_cast<const uint16_t*>(X); sa.ldx = d_in;
+    sa.W = static_cast<const uint16_t*>(W); sa.ldw = d_in;
+    sa.A = static_cast<const uint16_t*>(A); sa.B = static_cast<const uint16_t*>(B);
+    sa.Y = static_cast<uint16_t*>(Y);
+    sa.M = (int)M; sa.N = (int)d_out; sa.K = (int)d_in; sa.r = (int)r; sa.s = scale;
+    if (rope) { sa.pos = rope->pos; sa.cosc = rope->cosc; sa.sinc = rope->sinc; }
+    const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
+    HIPTRY(timed(K_SKINNY, 2 * Md * ko * ki + 2 * Md * rr * (ki + ko),
+                 (ko * ki + Md * ki + rr * ki + ko * rr + Md * ko) * 2 + (rope ? Md * 64 * 8 : 0), st,
+                 [&] { return launch_skinny_fwd(sa, smode, st); }));
+    return LORA_OK;
+  }
   if (nf4 && L.dequant) {
     TRY(dequant_w(*nf4, d_out * d_in, w + L.wdq, st));
     W = w + L.wdq;

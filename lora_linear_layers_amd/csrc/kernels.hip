@@ -10,6 +10,7 @@
 #include "gemm_w4.h"
 #include "gemm_w4_nt.h"
 #include "gemm_panel.h"
+#include "skinny.h"
 #include "launch.h"
 
 namespace lora {
@@ -760,6 +761,44 @@ mfma_rate_kernel(int iters, float* __restrict__ out) {
 hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st) {
   hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, iters, out);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// few-token fused forward
+// ---------------------------------------------------------------------------
+bool skinny_fits(int64_t M, int64_t K, int64_t N, int64_t r, int mode) {
+  const int64_t lim = int64_t(1) << 30;  // the kernel's buffer offsets stay below
+  return M >= 1 && M <= 64 && r >= 8 && r <= 64 && r % 8 == 0 && K % 8 == 0 && N * K * 2 < lim &&
+         M * K * 2 < lim && r * K * 2 < lim && N * r * 2 < lim && (mode != sk::ROPE || N % 128 == 0);
+}
+
+namespace {
+template <int MB, int NB, int RB, int MODE>
+hipError_t run_skinny(const SkinnyArgs& a, hipStream_t st) {
+  const int64_t blocks = MODE == sk::ROPE ? int64_t(a.N / 128) * 4 : (a.N + 16 * NB - 1) / (16 * NB);
+  // waves per block: more waves keep more loads in flight per CU; the
+  // partial sums (NW x MB (NB + RB) KiB of LDS) and registers bound it
+  constexpr int E = MB * (NB + RB);
+  constexpr int NW = E <= 4 ? 16 : (E <= 8 ? 8 : 4);
+  hipLaunchKernelGGL((skinny_fwd_kernel<MB, NB, RB, MODE, NW>), dim3((unsigned)blocks), dim3(64 * NW), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int MB, int RB>
+hipError_t run_skinny_mode(const SkinnyArgs& a, int mode, hipStream_t st) {
+  // 4 strips of 16 columns per block once the output is wide enough: fewer
+  // blocks, so fewer re-reads of X from L2
+  const bool wide = a.N >= 12288;
+  if (mode == sk::ROPE) return run_skinny<MB, 2, RB, sk::ROPE>(a, st);
+  return wide ? run_skinny<MB, 4, RB, sk::PLAIN>(a, st) : run_skinny<MB, 1, RB, sk::PLAIN>(a, st);
+}
+}  // namespace
+
+hipError_t launch_skinny_fwd(const SkinnyArgs& a, int mode, hipStream_t st) {
+  // 16 or 64 rows of X, rank up to 16 or 64 (rows past M and rank columns
+  // past r read as zero)
+  if (a.M <= 16) return a.r <= 16 ? run_skinny_mode<1, 1>(a, mode, st) : run_skinny_mode<1, 4>(a, mode, st);
+  return a.r <= 16 ? run_skinny_mode<4, 1>(a, mode, st) : run_skinny_mode<4, 4>(a, mode, st);
 }
 
 }  // namespace lora

@@ -138,6 +138,13 @@ hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, 
 // wave); out [blocks * 256] receives one float per thread.
 hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st);
 
+// Few-token forward in one launch (skinny.h): Y = X W^T + bf16(s X A^T) B^T,
+// mode 0 plain, 1 RoPE (pos / cosc / sinc, N % 128 == 0), bf16 W.  Requires
+// 1 <= M <= 64, r % 8 == 0, r <= 64 (skinny_fits).
+struct SkinnyArgs;
+bool skinny_fits(int64_t M, int64_t K, int64_t N, int64_t r, int mode);
+hipError_t launch_skinny_fwd(const SkinnyArgs& a, int mode, hipStream_t st);
+
 // W^T [cols, rows] bf16 from the NF4 codes of W [rows, cols] (cols % 64 == 0,
 // rows % 8 == 0), the same values as launch_nf4_dequant.
 hipError_t launch_nf4_dequant_t(const uint8_t* codes, const float* absmax, int64_t rows, int64_t cols,
