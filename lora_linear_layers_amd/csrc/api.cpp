@@ -94,12 +94,15 @@ void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit)
   *splits = (int)cdiv(K, ks);
 }
 
-// Split of the token contraction for dA / dB ([rows, N] outputs in 64 x 256
-// tiles): enough workgroups to cover the chip (~2 per CU), each split a
-// multiple of 64 tokens and at least 256 long.
+// Split of the token contraction for dA / dB ([rows, N] outputs): enough
+// workgroups to cover the chip, each split a multiple of 64 tokens and at
+// least 256 long.
 void choose_split(int64_t M, int64_t rows, int64_t N, int* splits, int64_t* ksplit) {
-  const int64_t tiles = cdiv(rows, 64) * cdiv(N, 256);
-  int64_t s = cdiv(512, tiles);
+  // 65 to 128 rows (bf16: splitnn_dma_kernel): every row in a 256-column
+  // tile and about one block per CU; else 64 x 256 tiles, about two per CU
+  const bool one = rows > 64 && rows <= 128;
+  const int64_t tiles = one ? cdiv(N, 256) : cdiv(rows, 64) * cdiv(N, 256);
+  int64_t s = cdiv(one ? 256 : 512, tiles);
   const int64_t smax = cdiv(M, 256);
   if (s > smax) s = smax;
   if (s < 1) s = 1;

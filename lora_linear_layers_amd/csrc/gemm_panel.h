@@ -188,4 +188,204 @@ panel_dma_kernel(const GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Token-split partials of the adapters' gradients for 65 to 128 rows of C
+// (a group's stacked rank; up to 64 rows the generic 64 x 256 tile already
+// reads the tall operand once, and measured faster on MI355X: two of its
+// blocks share a CU): C = Aop Bop over a range of tokens, Aop [R, M] the transposed panel (P^T for dB^T = P^T G, Q^T for
+// dA = Q^T X; rows contiguous along the tokens), Bop [M, N] the tall operand
+// (G or X, rows contiguous along N): page "UnSloth加速微调体验…", section
+// 反向传播优化.  Like the panel, a stream of the tall operand, so the same
+// design: a 256-column tile holds every row of C (R <= BR = 128), so G or X
+// is read once (64-row tiles read it twice: 176 -> 146 us for a 128-row dA
+// over an 8192 x 4096 X); both operands go to LDS by DMA through an NS-stage ring;
+// split z covers tokens [z k_split, ..) and writes its fp32 partial at
+// C + z part_stride (reduce_splits_kernel sums them in order).
+//
+// Bop is contraction-major, so its MFMA fragments come from LDS through
+// ds_read_b64_tr_b16 (the transposing LDS read): the stage's 64 token rows
+// of 512 bytes hold 16-byte chunk c of row k at chunk c ^ 2 f(k),
+// f(k) = (k & 3) | ((k >> 1) & 4) (the NN whole-tile kernel's layout,
+// conflict-free for those reads).  DMA instruction i of wave w moves token
+// rows 16 w + 2 i + lane / 32, the lane landing at physical chunk lane & 31,
+// i.e. logical chunk (lane & 31) ^ 2 f(row).  Aop rows go as in the panel
+// kernel.  Wave w computes columns 64 w .. 64 w + 63 against all BR rows.
+namespace sdma {
+constexpr int BN = 256, BK = 64, NT = 256;
+constexpr int B_BYTES = BK * BN * 2;  // 64 token rows of 512 bytes
+template <int BR>
+struct Cfg {
+  static constexpr int A_BYTES = BR * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NS = (160 * 1024) / STAGE;  // 3 for BR = 128
+  static constexpr int IA = BR / 8 / 4;  // Aop instructions per wave
+  static constexpr int IB = BK / 2 / 4;  // Bop instructions per wave
+  static constexpr int PER = IA + IB;
+  static constexpr int FM = BR / 32, FN = 2;
+  static_assert(IA % 2 == 0, "row parity pattern of the Aop lane mapping");
+};
+}  // namespace sdma
+
+template <int BR>
+__global__ void __launch_bounds__(sdma::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+splitnn_dma_kernel(const GemmArgs p) {
+  using namespace sdma;
+  using C = Cfg<BR>;
+  constexpr int NS = C::NS, LEAD = NS - 1, FM = C::FM, FN = C::FN;
+  constexpr int A_BYTES = C::A_BYTES;
+  __shared__ __attribute__((aligned(1024))) char smem[NS * C::STAGE];
+  asm volatile("" ::: "a0");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int tiles_n = (int)((p.n_store + BN - 1) / BN);
+  const int nt = (int)(blockIdx.x % tiles_n), z = (int)(blockIdx.x / tiles_n);
+  const int64_t n0 = (int64_t)nt * BN;
+  const int64_t kbeg = (int64_t)z * p.k_split;
+  const int64_t kend = kbeg + p.k_split < p.K1 ? kbeg + p.k_split : p.K1;
+  const int nk = kend > kbeg ? (int)((kend - kbeg + BK - 1) / BK) : 0;
+  const int klen = (int)(kend - kbeg);
+
+  // ---- DMA addressing ----
+  const int dce = (lane & 7) ^ (lane >> 4), dco = (lane & 7) ^ ((lane >> 4) | 4);
+  const char* ga = reinterpret_cast<const char*>(p.a1) + kbeg * 2;                   // Aop [R, ld] at token kbeg
+  const char* gb = reinterpret_cast<const char*>(p.b1) + (kbeg * p.ldb1 + n0) * 2;  // Bop token row kbeg, column n0
+  const int64_t ncols = p.n_load - n0;  // columns of Bop left from n0
+  auto dma_a = [&](int u, int s, int i) {
+    const int dc = (i & 1) ? dco : dce;
+    const int row = 8 * (i + C::IA * wave) + (lane >> 3);
+    const int kk = u * BK + 8 * dc;
+    const bool ok = kk < klen && row < p.m_load;
+    uint32_t vo = ok ? (uint32_t)(row * p.lda1 * 2 + kk * 2) : w4::OOB;
+    asm volatile("" : "+v"(vo));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(ga), (short)0, w4::BIG, 0x00020000);
+    char* dst = smem + s * C::STAGE + (8 * (i + C::IA * wave)) * 128;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)vo, 0, 0,
+                                             0);
+  };
+  auto dma_b = [&](int u, int s, int i) {
+    const int k = 16 * wave + 2 * i + (lane >> 5);  // token row within the stage
+    const int f = (k & 3) | ((k >> 1) & 4);
+    const int c = (lane & 31) ^ (2 * f);  // logical 16-byte chunk
+    const bool ok = u * BK + k < klen && 8 * c < ncols;
+    uint32_t vo = ok ? (uint32_t)(((int64_t)(u * BK + k) * p.ldb1 + 8 * c) * 2) : w4::OOB;
+    asm volatile("" : "+v"(vo));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(gb), (short)0, w4::BIG, 0x00020000);
+    char* dst = smem + s * C::STAGE + A_BYTES + (16 * wave + 2 * i) * 512;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)vo, 0, 0,
+                                             0);
+  };
+  auto issue = [&](int u) {
+    const int s = u % NS;
+#pragma unroll
+    for (int i = 0; i < C::IA; ++i) dma_a(u, s, i);
+#pragma unroll
+    for (int i = 0; i < C::IB; ++i) dma_b(u, s, i);
+  };
+
+  // ---- fragments ----
+  // Aop: row 32 i + l32, tokens 16 st + 8 hh .. +7 (chunk 2 st + hh)
+  const int swz = (l32 >> 1) & 7;
+  const uint32_t ra = (uint32_t)l32 * 128;
+  // Bop through ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+  // element (4 q + i / 4, i % 4) of the group's 4 x 4 loads, so pointing lane
+  // i at token row k0 + i / 4 and columns c0 + 4 (i % 4) .. +3 hands it token
+  // rows k0 .. k0 + 3 of column c0 + i.  Lane l of the 32x32x16 fragment needs
+  // column 32 j + l % 32 and tokens 8 (l / 32) .. +7 of step st: group
+  // gq = l >> 4 takes columns 32 j + 16 (gq & 1) and token rows
+  // 16 st + 8 (gq >> 1) + 4 h, h < 2, whose swizzle is f = ((l & 15) >> 2) | 4 (gq >> 1).
+  uint32_t nn_r[FN];
+  {
+    const int gq = lane >> 4, i16 = lane & 15;
+    const int f = (i16 >> 2) | ((gq >> 1) << 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int chunk = (64 * wave + 32 * j + 16 * (gq & 1) + 4 * (i16 & 3)) >> 3;
+      nn_r[j] = (uint32_t)A_BYTES + (uint32_t)(8 * (gq >> 1) + (i16 >> 2)) * 512 +
+                (uint32_t)((chunk ^ (2 * f)) << 4) + (uint32_t)((i16 & 1) << 3);
+    }
+  }
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto rd = [&](int s, int st, auto fsel) {
+    constexpr int fi = decltype(fsel)::value;
+    const char* base = smem + s * C::STAGE;
+    const uint32_t c = (uint32_t)(((2 * st + hh) ^ swz) << 4);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[fi][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + ra + c + i * 32 * 128));
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      typedef short i16x4 __attribute__((ext_vector_type(4)));
+      i16x4 h[2];
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq)
+        h[hq] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
+            (__attribute__((address_space(3))) char*)smem + s * C::STAGE + nn_r[j] + (16 * st + 4 * hq) * 512));
+      u32x4 v;
+      v[0] = (uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16);
+      v[1] = (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16);
+      v[2] = (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16);
+      v[3] = (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16);
+      fb[fi][j] = __builtin_bit_cast(bf16x8, v);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto step = [&](auto fsel) {
+    constexpr int fi = decltype(fsel)::value;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fi][i], fb[fi][j], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  if (nk > 0) {
+#pragma unroll
+    for (int u = 0; u < LEAD; ++u) issue(u);
+    for (int t = 0; t < nk; ++t) {
+      const int s = t % NS;
+      __builtin_amdgcn_s_waitcnt(pdma::vmcnt_imm(C::PER * (LEAD - 1)));
+      lds_barrier();
+      issue(t + LEAD);  // into stage t-1's slot; zeros past the end
+      rd(s, 0, I0{});
+      rd(s, 1, I1{});
+      step(I0{});
+      rd(s, 2, I0{});
+      step(I1{});
+      rd(s, 3, I1{});
+      step(I0{});
+      step(I1{});
+    }
+    // the DMAs issued past the end must land before the block's LDS is freed
+    __builtin_amdgcn_s_waitcnt(pdma::vmcnt_imm(0));
+  }
+
+  // fp32 partial: acc[i][j][v] = C[32 i + 8 (v / 4) + 4 hh + v % 4, n0 + 64 w + 32 j + l32]
+  float* out = reinterpret_cast<float*>(p.c) + (int64_t)z * p.part_stride;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int row = 32 * i + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (row >= p.m_store) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + 64 * wave + 32 * j + l32;
+        if (col < p.n_store) out[row * p.ldc + col] = acc[i][j][v];
+      }
+    }
+}
+
 }  // namespace lora

@@ -66,6 +66,22 @@ hipError_t run_panel(GemmArgs a, int splits, hipStream_t st) {
   return hipGetLastError();
 }
 
+// token-split partials of dA / dB for 65 to 128 rows: every row in a
+// 256-column tile, one block per tile and split
+hipError_t run_splitnn(GemmArgs a, int splits, hipStream_t st) {
+  const int64_t tiles_n = (a.n_store + sdma::BN - 1) / sdma::BN;
+  const int64_t nblocks = tiles_n * splits;
+  if (nblocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((splitnn_dma_kernel<128>), dim3((unsigned)nblocks), dim3(sdma::NT), 0, st, a);
+  return hipGetLastError();
+}
+
+bool splitnn_fits(const GemmArgs& a) {
+  return a.K2 == 0 && a.m_store > 64 && a.m_store <= 128 && a.m_load <= a.m_store && a.n_load == a.n_store &&
+         (a.k_split + sdma::BK) * a.ldb1 * 2 + a.n_store * 2 < (int64_t)w4::BIG &&
+         a.lda1 * 2 * 128 < (int64_t)w4::BIG;
+}
+
 bool panel_fits(const GemmArgs& a) {
   const int64_t ld = std::max(a.lda1, a.ldb1);
   return a.K2 == 0 && a.n_store <= 128 && a.n_load <= a.n_store && ld * 2 * 256 < (int64_t)w4::BIG;
@@ -135,7 +151,9 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_NF4_MED_NT_STORE: return run<bf, 128, 128, 4, 1, false, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_BIG_NN_STORE: return run<bf, 256, 256, 2, 4, true, EPI_STORE, BL_NF4>(a, splits, st);
     case G_NF4_MED_NN_STORE: return run<bf, 128, 128, 4, 1, true, EPI_STORE, BL_NF4>(a, splits, st);
-    case G_BF16_SPLIT_NN_PARTIAL: return run<bf, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
+    case G_BF16_SPLIT_NN_PARTIAL:
+      if (splitnn_fits(a)) return run_splitnn(a, splits, st);
+      return run<bf, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_F32_NT_STORE: return run<float, 64, 128, 4, 1, false, EPI_STORE, BL_PLAIN>(a, splits, st);
     case G_F32_NT_ROPE: return run<float, 64, 128, 4, 1, false, EPI_ROPE, BL_PLAIN>(a, splits, st);
     case G_F32_NN_STORE: return run<float, 64, 128, 4, 1, true, EPI_STORE, BL_PLAIN>(a, splits, st);
