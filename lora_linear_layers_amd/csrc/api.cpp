@@ -266,7 +266,7 @@ const char* kind_name(int k) {
       "gemm_nf4_128x128_nn_store",  "split_bf16_nn_partial",      "gemm_f32_64x128_nt_store",
       "gemm_f32_64x128_nt_rope",    "gemm_f32_64x128_nn_store",   "panel_f32_nt_store",
       "panel_f32_nt_store_t",       "panel_f32_nn_both",          "split_f32_nn_partial",
-      "panel_bf16_256x64_split",    "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
+      "panel_bf16_split",           "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
       "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
       "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "dropout_dx_bf16_128x128",
       "dropout_dx_f32_64x128",      "pad_cols",                   "rope_inverse",
