@@ -94,15 +94,16 @@ void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit)
   *splits = (int)cdiv(K, ks);
 }
 
-// Split of the token contraction for dA / dB ([rows, N] outputs): enough
-// workgroups to cover the chip, each split a multiple of 64 tokens and at
-// least 256 long.
-void choose_split(int64_t M, int64_t rows, int64_t N, int* splits, int64_t* ksplit) {
-  // 65 to 128 rows (bf16: splitnn_dma_kernel): every row in a 256-column
-  // tile and about one block per CU; else 64 x 256 tiles, about two per CU
-  const bool one = rows > 64 && rows <= 128;
+// Split of the token contraction for dA / dB ([rows, N] outputs), each split
+// a multiple of 64 tokens and at least 256 long.  bf16 (dma) up to 128 rows:
+// splitnn_dma_kernel, every row in a 256-column tile and one block per CU,
+// so at most 256 blocks; else 64 x 256 tiles, two blocks per CU, at most
+// 512.  The split count rounds down so that every block runs in the first
+// round (560 blocks for 512 slots measured 25 % slower than 504).
+void choose_split(int64_t M, int64_t rows, int64_t N, bool dma, int* splits, int64_t* ksplit) {
+  const bool one = dma && rows <= 128;
   const int64_t tiles = one ? cdiv(N, 256) : cdiv(rows, 64) * cdiv(N, 256);
-  int64_t s = cdiv(one ? 256 : 512, tiles);
+  int64_t s = (one ? 256 : 512) / tiles;
   const int64_t smax = cdiv(M, 256);
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -188,8 +189,8 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.pt = take(size_t(L.r8) * L.M8 * eb);
     L.qs = take(size_t(L.M8) * L.r8 * eb);
     L.qt = take(size_t(L.r8) * L.M8 * eb);
-    choose_split(M, L.r8, d_in, &L.splits_dA, &L.ksplit_dA);
-    choose_split(M, L.r8, d_out, &L.splits_dB, &L.ksplit_dB);
+    choose_split(M, L.r8, d_in, eb == 2, &L.splits_dA, &L.ksplit_dA);
+    choose_split(M, L.r8, d_out, eb == 2, &L.splits_dB, &L.ksplit_dB);
     size_t pa = size_t(L.splits_dA) * L.r8 * d_in * 4;
     size_t pb = size_t(L.splits_dB) * L.r8 * d_out * 4;
     if (sp > pa) pa = sp;  // the dX partials are reduced before dB and dA start
@@ -324,11 +325,28 @@ GemmArgs blank() {
 // (256 x 64 tiles) into part, then the fixed-order reduction into out
 // (row-major [rows, ldo]) and/or outt (transposed [r8, ldot]); rows in
 // [M, rows) and columns in [r, r8) are zeros.
+// Rows of a group's stacked R taken straight from each member's (n = 0: R
+// itself is the stacked matrix).
+struct PanelSrc {
+  int n = 0;
+  const void* rs[kPanelSrcMax] = {};
+  int beg[kPanelSrcMax] = {};
+  int rows[kPanelSrcMax] = {};
+};
+
 int panel_bf16(const void* X, int64_t ldx, const void* R, int64_t ldr, int64_t M, int64_t rows, int64_t K, int64_t r,
                int64_t r8, int splits, int64_t ksplit, const ColScale& cs, float* part, uint16_t* out, int64_t ldo,
-               uint16_t* outt, int64_t ldot, hipStream_t st) {
+               uint16_t* outt, int64_t ldot, hipStream_t st, const PanelSrc* src = nullptr) {
   GemmArgs a = blank();
   a.a1 = X; a.lda1 = ldx; a.b1 = R; a.ldb1 = ldr; a.K1 = K;
+  if (src) {
+    a.n_src = src->n;
+    for (int g = 0; g < src->n; ++g) {
+      a.rs[g] = src->rs[g];
+      a.rs_beg[g] = src->beg[g];
+      a.rs_rows[g] = src->rows[g];
+    }
+  }
   a.m_load = M; a.m_store = rows; a.n_load = r; a.n_store = r8;
   a.k_split = ksplit; a.c = part; a.ldc = r8; a.part_stride = rows * r8;
   const double Md = double(M), kd = double(K), rd = double(r);
@@ -708,7 +726,7 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
       G.pt = take(size_t(G.rt) * G.M8 * eb);
       G.qs = take(size_t(G.M8) * G.rt * eb);
       G.qt = take(size_t(G.rt) * G.M8 * eb);
-      choose_split(M, G.rt, d_in, &G.splits_dA, &G.ksplit_dA);
+      choose_split(M, G.rt, d_in, true, &G.splits_dA, &G.ksplit_dA);
       const size_t pa = size_t(G.splits_dA) * G.rt * d_in * 4;
       if (pa > shared) shared = pa;
     }
@@ -757,17 +775,26 @@ int check_group_ws(const GroupLayout& G, const void* ws, size_t ws_bytes) {
   return LORA_OK;
 }
 
-// Acat rows of every member (rows r..r8 of each block are zeros) and the
-// per-column scales of the group panel.
-int group_acat(int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G, uint16_t* acat, ColScale* cs,
-               hipStream_t st) {
+// The group panel's R rows and per-column scales.  The panel DMA kernel
+// reads each member's A in place; otherwise (wider stacks) the members' rows
+// are copied into acat (rows r..r8 of each block zeros).
+int group_rows(int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G, uint16_t* acat, ColScale* cs,
+               PanelSrc* src, hipStream_t st) {
   cs->n = n;
+  const bool direct = n <= kPanelSrcMax && panel_dma_fits(G.rt, d_in, d_in);
+  src->n = direct ? n : 0;
   for (int g = 0; g < n; ++g) {
     const int64_t r8 = rup(mb[g].r, 8);
-    HIPTRY(timed(K_COPY_ROWS, 0, 2.0 * (mb[g].r + r8) * d_in, st, [&] {
-      return launch_copy_rows(static_cast<const uint16_t*>(mb[g].A), d_in, mb[g].r, d_in, acat + G.off[g] * d_in,
-                              d_in, r8, st);
-    }));
+    if (direct) {
+      src->rs[g] = mb[g].A;
+      src->beg[g] = (int)G.off[g];
+      src->rows[g] = mb[g].r;
+    } else {
+      HIPTRY(timed(K_COPY_ROWS, 0, 2.0 * (mb[g].r + r8) * d_in, st, [&] {
+        return launch_copy_rows(static_cast<const uint16_t*>(mb[g].A), d_in, mb[g].r, d_in, acat + G.off[g] * d_in,
+                                d_in, r8, st);
+      }));
+    }
     cs->end[g] = G.off[g] + r8;
     cs->s[g] = mb[g].scale;
   }
@@ -782,9 +809,10 @@ int group_forward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_me
   uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
   if (share) {
     ColScale cs{};
-    TRY(group_acat(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+    PanelSrc src;
+    TRY(group_rows(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
     TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                   reinterpret_cast<float*>(sh), P, G.rt, nullptr, 0, st));
+                   reinterpret_cast<float*>(sh), P, G.rt, nullptr, 0, st, &src));
   }
   for (int g = 0; g < n; ++g) {
     const lora_group_member& m = mb[g];
@@ -805,9 +833,10 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   uint16_t* Qt = reinterpret_cast<uint16_t*>(w + G.qt);
   if (share) {
     ColScale cs{};
-    TRY(group_acat(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+    PanelSrc src;
+    TRY(group_rows(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
     TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, G.M8, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                   reinterpret_cast<float*>(sh), nullptr, 0, Pt, G.M8, st));
+                   reinterpret_cast<float*>(sh), nullptr, 0, Pt, G.M8, st, &src));
   }
   for (int g = 0; g < n; ++g) {
     const lora_group_member& m = mb[g];
@@ -935,10 +964,11 @@ int swiglu_forward(int dtype, int64_t M, int64_t d_in, const lora_group_member* 
   const GroupLayout& G = S.G;
   // the pair's rank-r panels in one pass over X: P = [sg X Ag^T | su X Au^T]
   ColScale cs{};
-  TRY(group_acat(d_in, 2, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, st));
+  PanelSrc src;
+  TRY(group_rows(d_in, 2, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
   uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
   TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                 reinterpret_cast<float*>(w + G.shared), P, G.rt, nullptr, 0, st));
+                 reinterpret_cast<float*>(w + G.shared), P, G.rt, nullptr, 0, st, &src));
   const void* Wp[2];
   const void* Bp[2];
   const size_t woff[2] = {S.wg, S.wu}, boff[2] = {S.bg, S.bu};

@@ -62,6 +62,8 @@ enum Epi : int {
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
 
+constexpr int kPanelSrcMax = 8;  // row sources of a panel's Bop (a group's members)
+
 struct GemmArgs {
   const void* a1;
   const void* b1;
@@ -101,6 +103,15 @@ struct GemmArgs {
   // EPI_ADD_MASKED: keep bit of (m, n) = bit n % 8 of mask[m * mask_ld + n / 8]
   const uint8_t* mask;
   int64_t mask_ld;
+  // panel_dma_kernel with n_src > 0: Bop rows [rs_beg[g], rs_beg[g] + 8k) of
+  // the tile (up to the next source's rs_beg, or n_store) come from rs[g],
+  // its row 0 first and its rows at or past rs_rows[g] read as zeros (row
+  // stride ldb1; rs_beg[0] = 0, every rs_beg a multiple of 8).  n_src = 0:
+  // every row from b1.
+  int n_src;
+  const void* rs[kPanelSrcMax];
+  int rs_beg[kPanelSrcMax];
+  int rs_rows[kPanelSrcMax];
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {

@@ -87,22 +87,41 @@ panel_dma_kernel(const GemmArgs p) {
   const int dr = lane >> 3;
   const int dce = (lane & 7) ^ (lane >> 4), dco = (lane & 7) ^ ((lane >> 4) | 4);
   const char* ga = reinterpret_cast<const char*>(p.a1) + (m0 * p.lda1 + kbeg) * 2;
-  const char* gb = reinterpret_cast<const char*>(p.b1) + kbeg * 2;
   const int klen = (int)(kend - kbeg);
   const int64_t mrem = p.m_load - m0;  // rows of X left from the tile's first
-  const int64_t nrem = p.n_load;       // rows of R
+  // B instruction i moves the 8 tile rows 8 (i + IB w) ..: their source (one
+  // of the group's R's, or b1), the source's row of tile row 0 (rb_off) and
+  // its row count (rb_lim), fixed for the whole kernel and uniform per wave
+  const char* gb[C::IB];
+  int rb_off[C::IB], rb_lim[C::IB];
+#pragma unroll
+  for (int i = 0; i < C::IB; ++i) {
+    const int row8 = 8 * (i + C::IB * wave);
+    const void* src = p.b1;
+    int off = 0, lim = (int)p.n_load;
+    for (int g = 0; g < p.n_src; ++g)
+      if (row8 >= p.rs_beg[g]) {
+        src = p.rs[g];
+        off = p.rs_beg[g];
+        lim = p.rs_rows[g];
+      }
+    gb[i] = reinterpret_cast<const char*>(src) + kbeg * 2;
+    rb_off[i] = off;
+    rb_lim[i] = lim;
+  }
   // A instruction i: rows 8 (i + IA w) + dr; B instruction i: 8 (i + IB w) + dr
+  // of the tile, row - rb_off[i] of its source
   auto dma = [&](int u, int s, int op, int i) {
     const int odd = i & 1;
     const int dc = odd ? dco : dce;
-    const int row = 8 * (i + (op == 0 ? C::IA : C::IB) * wave) + dr;
+    const int row = 8 * (i + (op == 0 ? C::IA : C::IB) * wave) + dr - (op == 0 ? 0 : rb_off[i]);
     const int64_t ld = op == 0 ? p.lda1 : p.ldb1;
     const int kk = u * BK + 8 * dc;
-    const bool ok = kk < klen && row < (op == 0 ? mrem : nrem);
+    const bool ok = kk < klen && row < (op == 0 ? mrem : (int64_t)rb_lim[i]);
     uint32_t vo = ok ? (uint32_t)(row * ld * 2 + kk * 2) : w4::OOB;
     asm volatile("" : "+v"(vo));
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(op == 0 ? ga : gb), (short)0, w4::BIG, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(op == 0 ? ga : gb[i]), (short)0, w4::BIG, 0x00020000);
     char* dst = smem + s * C::STAGE + (op == 0 ? 0 : A_BYTES) + (8 * (i + (op == 0 ? C::IA : C::IB) * wave)) * 128;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, (int)vo, 0, 0,
                                              0);
@@ -189,14 +208,14 @@ panel_dma_kernel(const GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Token-split partials of the adapters' gradients for 65 to 128 rows of C
-// (a group's stacked rank; up to 64 rows the generic 64 x 256 tile already
-// reads the tall operand once, and measured faster on MI355X: two of its
-// blocks share a CU): C = Aop Bop over a range of tokens, Aop [R, M] the transposed panel (P^T for dB^T = P^T G, Q^T for
-// dA = Q^T X; rows contiguous along the tokens), Bop [M, N] the tall operand
+// Token-split partials of the adapters' gradients for up to 128 rows of C
+// (BR = 64: one adapter's rank; BR = 128: a group's stacked ranks):
+// C = Aop Bop over a range of tokens, Aop [R, M] the transposed panel (P^T
+// for dB^T = P^T G, Q^T for dA = Q^T X; rows contiguous along the tokens),
+// Bop [M, N] the tall operand
 // (G or X, rows contiguous along N): page "UnSloth加速微调体验…", section
 // 反向传播优化.  Like the panel, a stream of the tall operand, so the same
-// design: a 256-column tile holds every row of C (R <= BR = 128), so G or X
+// design: a 256-column tile holds every row of C (R <= BR), so G or X
 // is read once (64-row tiles read it twice: 176 -> 146 us for a 128-row dA
 // over an 8192 x 4096 X); both operands go to LDS by DMA through an NS-stage ring;
 // split z covers tokens [z k_split, ..) and writes its fp32 partial at
@@ -217,7 +236,7 @@ template <int BR>
 struct Cfg {
   static constexpr int A_BYTES = BR * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NS = (160 * 1024) / STAGE;  // 3 for BR = 128
+  static constexpr int NS = (160 * 1024) / STAGE;  // 4 for BR = 64, 3 for 128
   static constexpr int IA = BR / 8 / 4;  // Aop instructions per wave
   static constexpr int IB = BK / 2 / 4;  // Bop instructions per wave
   static constexpr int PER = IA + IB;
@@ -239,8 +258,11 @@ splitnn_dma_kernel(const GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int tiles_n = (int)((p.n_store + BN - 1) / BN);
-  const int nt = (int)(blockIdx.x % tiles_n), z = (int)(blockIdx.x / tiles_n);
+  // grid (column tiles, splits): both coordinates are workgroup ids, so
+  // scalar; the DMA resources built from them must be (a coordinate left
+  // in vector registers, as a division of a flat id leaves it, makes the
+  // compiler wrap every DMA in a loop over the lanes' values)
+  const int nt = (int)blockIdx.x, z = (int)blockIdx.y;
   const int64_t n0 = (int64_t)nt * BN;
   const int64_t kbeg = (int64_t)z * p.k_split;
   const int64_t kend = kbeg + p.k_split < p.K1 ? kbeg + p.k_split : p.K1;

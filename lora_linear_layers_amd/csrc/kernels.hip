@@ -66,30 +66,37 @@ hipError_t run_panel(GemmArgs a, int splits, hipStream_t st) {
   return hipGetLastError();
 }
 
-// token-split partials of dA / dB for 65 to 128 rows: every row in a
+// token-split partials of dA / dB for up to 128 rows: every row in a
 // 256-column tile, one block per tile and split
 hipError_t run_splitnn(GemmArgs a, int splits, hipStream_t st) {
   const int64_t tiles_n = (a.n_store + sdma::BN - 1) / sdma::BN;
-  const int64_t nblocks = tiles_n * splits;
-  if (nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((splitnn_dma_kernel<128>), dim3((unsigned)nblocks), dim3(sdma::NT), 0, st, a);
+  if (tiles_n <= 0 || splits <= 0) return hipSuccess;
+  const dim3 grid((unsigned)tiles_n, (unsigned)splits);
+  if (a.m_store <= 64)
+    hipLaunchKernelGGL((splitnn_dma_kernel<64>), grid, dim3(sdma::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((splitnn_dma_kernel<128>), grid, dim3(sdma::NT), 0, st, a);
   return hipGetLastError();
 }
 
 bool splitnn_fits(const GemmArgs& a) {
-  return a.K2 == 0 && a.m_store > 64 && a.m_store <= 128 && a.m_load <= a.m_store && a.n_load == a.n_store &&
+  return a.K2 == 0 && a.m_store > 0 && a.m_store <= 128 && a.m_load <= a.m_store && a.n_load == a.n_store &&
          (a.k_split + sdma::BK) * a.ldb1 * 2 + a.n_store * 2 < (int64_t)w4::BIG &&
          a.lda1 * 2 * 128 < (int64_t)w4::BIG;
 }
 
 bool panel_fits(const GemmArgs& a) {
-  const int64_t ld = std::max(a.lda1, a.ldb1);
-  return a.K2 == 0 && a.n_store <= 128 && a.n_load <= a.n_store && ld * 2 * 256 < (int64_t)w4::BIG;
+  return a.K2 == 0 && a.n_load <= a.n_store && panel_dma_fits(a.n_store, a.lda1, a.ldb1);
 }
 
 using bf = uint16_t;
 
 }  // namespace
+
+bool panel_dma_fits(int64_t n_store, int64_t lda, int64_t ldb) {
+  const int64_t ld = std::max(lda, ldb);
+  return n_store <= 128 && ld * 2 * 256 < (int64_t)w4::BIG;
+}
 
 TileShape gemm_tile(GemmKind k) {
   switch (k) {
@@ -163,6 +170,7 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_F32_SPLIT_NN_PARTIAL: return run<float, 64, 256, 1, 4, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_PANEL_SPLIT_NT:
       if (panel_fits(a)) return run_panel(a, splits, st);
+      if (a.n_src > 0) return hipErrorInvalidValue;  // row sources: the DMA kernel only
       return run<bf, 256, 64, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NT_PARTIAL: return run<bf, 128, 128, 4, 1, false, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_PARTIAL: return run<bf, 128, 128, 4, 1, true, EPI_PARTIAL, BL_PLAIN>(a, splits, st);
@@ -343,28 +351,81 @@ hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float*
 
 constexpr int kMaxSplits = 64;
 
-__global__ void reduce_splits_kernel(const float* __restrict__ part, int splits, int64_t rows, int64_t N,
-                                     int64_t part_stride, int transpose, float* __restrict__ out) {
-  const int64_t n = rows * N;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t q = e / N, c = e - q * N;
-    float s = 0.f;
-#pragma unroll 8
-    for (int z = 0; z < splits; ++z) s += part[(int64_t)z * part_stride + e];
-    if (transpose)
-      out[c * rows + q] = s;
-    else
-      out[e] = s;
+// Sum over z < splits of the float4 at src + z stride, in split order, with
+// the loads of up to 8 splits issued before their adds.
+__device__ __forceinline__ float4 sum_splits(const float* __restrict__ src, int splits, int64_t stride) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z0 = 0; z0 < splits; z0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int z = z0 + u < splits ? z0 + u : splits - 1;
+      v[u] = *reinterpret_cast<const float4*>(src + (int64_t)z * stride);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (z0 + u >= splits) break;
+      acc.x += v[u].x;
+      acc.y += v[u].y;
+      acc.z += v[u].z;
+      acc.w += v[u].w;
+    }
+  }
+  return acc;
+}
+
+// out[q, c] (transpose: out[c, q]) = sum over z < splits of part[z][q, c],
+// in split order, for q < rows, c < N (N a multiple of 4).  A block covers
+// 16 rows x 64 columns, thread t columns 4 (t & 15) .. +3 of row t >> 4,
+// with the float4 loads of up to 8 splits in flight before their sums.  The
+// transposed store goes through an LDS tile so that consecutive threads
+// write consecutive q.
+__global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t rows, int64_t N, int64_t part_stride,
+                                                            int transpose, float* __restrict__ out) {
+  __shared__ float tile[16][65];
+  const int tid = threadIdx.x;
+  const int64_t c0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 16;
+  const int cl = 4 * (tid & 15), rl = tid >> 4;
+  const int64_t c = c0 + cl, q = q0 + rl;
+  const bool ok = c < N && q < rows;
+  // past the end: a valid element is read and nothing is stored
+  const float* src = part + (ok ? q * N + c : 0);
+  const float4 acc = sum_splits(src, splits, part_stride);
+  if (!transpose) {
+    if (ok) {
+      float* d = out + q * N + c;
+      d[0] = acc.x;
+      d[1] = acc.y;
+      d[2] = acc.z;
+      d[3] = acc.w;
+    }
+    return;
+  }
+  float* trow = &tile[rl][cl];
+  trow[0] = acc.x;
+  trow[1] = acc.y;
+  trow[2] = acc.z;
+  trow[3] = acc.w;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = k * 256 + tid;
+    const int cc = idx >> 4, qq = idx & 15;
+    const int64_t qg = q0 + qq, cg = c0 + cc;
+    if (qg < rows && cg < N) out[cg * rows + qg] = tile[qq][cc];
   }
 }
 
 hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N, int64_t part_stride,
                                 bool transpose, float* out, hipStream_t st) {
-  const int64_t n = rows * N;
-  if (n <= 0) return hipSuccess;
-  if (splits < 1 || splits > kMaxSplits) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, part, splits, rows, N,
-                     part_stride, transpose ? 1 : 0, out);
+  if (rows <= 0 || N <= 0) return hipSuccess;
+  if (splits < 1 || splits > kMaxSplits || N % 4 || part_stride % 4 ||
+      reinterpret_cast<uintptr_t>(part) % 16)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((rows + 15) / 16));
+  hipLaunchKernelGGL(reduce_splits_kernel, grid, dim3(256), 0, st, part, splits, rows, N, part_stride,
+                     transpose ? 1 : 0, out);
   return hipGetLastError();
 }
 
@@ -562,43 +623,51 @@ hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, 
 
 constexpr int kMaxPanelSplits = 32;
 
-// One 16-row x 64-column tile of the panel per workgroup: fixed-order sum of
-// the split partials (consecutive threads read consecutive columns), scale,
-// then the row-major and/or (through LDS) the transposed bf16 stores.
+// One 16-row x 64-column tile of the panel per workgroup: the fixed-order
+// sum of the split partials (thread t: columns 4 (t & 15) .. +3 of row
+// t >> 4, the loads of up to 8 splits in flight before their sums), the
+// column scale, then the row-major and/or (through LDS) the transposed bf16
+// stores.
 __global__ void __launch_bounds__(256) panel_reduce_kernel(const float* __restrict__ part, int splits,
                                                            int64_t part_stride, int64_t ldp, int64_t rows, int64_t n,
                                                            ColScale scale, uint16_t* __restrict__ out, int64_t ldo,
                                                            uint16_t* __restrict__ outt, int64_t ldot) {
   __shared__ float tile[16][65];
-  const int64_t r0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
-  const int cc = threadIdx.x & 63;
-  float alpha = scale.s[0];
+  const int tid = threadIdx.x;
+  const int64_t q0 = (int64_t)blockIdx.x * 16, c0 = (int64_t)blockIdx.y * 64;
+  const int cl = 4 * (tid & 15), rl = tid >> 4;
+  const int64_t c = c0 + cl, q = q0 + rl;
+  const bool ok = c < n && q < rows;
+  float alpha[4];
 #pragma unroll
-  for (int i = kColScaleMax - 1; i >= 0; --i)
-    if (i < scale.n && c0 + cc < scale.end[i]) alpha = scale.s[i];
-  for (int rr = threadIdx.x >> 6; rr < 16; rr += 4) {
-    const int64_t q = r0 + rr, c = c0 + cc;
-    float v = 0.f;
-    if (q < rows && c < n) {
-      // all split loads in flight at once, then the sum in split order
-      const float* src = part + q * ldp + c;
-      float pv[kMaxPanelSplits];
+  for (int k = 0; k < 4; ++k) {
+    alpha[k] = scale.s[0];
 #pragma unroll
-      for (int z = 0; z < kMaxPanelSplits; ++z) pv[z] = z < splits ? src[(int64_t)z * part_stride] : 0.f;
-      float s = 0.f;
-#pragma unroll
-      for (int z = 0; z < kMaxPanelSplits; ++z) s += pv[z];
-      v = s * alpha;
-      if (out) out[q * ldo + c] = f2bf(v);
-    }
-    tile[rr][cc] = v;
+    for (int i = kColScaleMax - 1; i >= 0; --i)
+      if (i < scale.n && c + k < scale.end[i]) alpha[k] = scale.s[i];
+  }
+  // past the end: a valid element is read and nothing is stored
+  const float4 acc = sum_splits(part + (ok ? q * ldp + c : 0), splits, part_stride);
+  const float y[4] = {acc.x * alpha[0], acc.y * alpha[1], acc.z * alpha[2], acc.w * alpha[3]};
+  if (out && ok) {
+    uint2 pk;
+    pk.x = (uint32_t)f2bf(y[0]) | ((uint32_t)f2bf(y[1]) << 16);
+    pk.y = (uint32_t)f2bf(y[2]) | ((uint32_t)f2bf(y[3]) << 16);
+    *reinterpret_cast<uint2*>(out + q * ldo + c) = pk;
   }
   if (!outt) return;
+  float* trow = &tile[rl][cl];
+  trow[0] = y[0];
+  trow[1] = y[1];
+  trow[2] = y[2];
+  trow[3] = y[3];
   __syncthreads();
-  for (int e = threadIdx.x; e < 16 * 64; e += 256) {
-    const int ct = e >> 4, rt = e & 15;  // consecutive threads: consecutive rows of the transpose
-    const int64_t q = r0 + rt, c = c0 + ct;
-    if (q < rows && c < n) outt[c * ldot + q] = f2bf(tile[rt][ct]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = k * 256 + tid;
+    const int cc = idx >> 4, qq = idx & 15;  // consecutive threads: consecutive rows of the transpose
+    const int64_t qg = q0 + qq, cg = c0 + cc;
+    if (qg < rows && cg < n) outt[cg * ldot + qg] = f2bf(tile[qq][cc]);
   }
 }
 
@@ -607,6 +676,10 @@ hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_strid
                                int64_t ldot, hipStream_t st) {
   if (rows <= 0 || n <= 0) return hipSuccess;
   if (splits < 1 || splits > kMaxPanelSplits || scale.n < 1 || scale.n > kColScaleMax) return hipErrorInvalidValue;
+  // float4 partial loads, 4-column bf16 stores
+  if (n % 4 || ldp % 4 || part_stride % 4 || reinterpret_cast<uintptr_t>(part) % 16 ||
+      (out && (ldo % 4 || reinterpret_cast<uintptr_t>(out) % 8)))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((n + 63) / 64));
   hipLaunchKernelGGL(panel_reduce_kernel, grid, dim3(256), 0, st, part, splits, part_stride, ldp, rows, n, scale, out,
                      ldo, outt, ldot);

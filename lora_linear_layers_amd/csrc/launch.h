@@ -11,6 +11,9 @@ namespace lora {
 
 // rows per tile of the rank-r panel kernel (the split choice in api.cpp uses it)
 constexpr int PANEL_BM = 128;
+// The bf16 panel (G_BF16_PANEL_SPLIT_NT) runs panel_dma_kernel, which alone
+// takes Bop rows from several sources (GemmArgs::n_src), for these shapes.
+bool panel_dma_fits(int64_t n_store, int64_t lda, int64_t ldb);
 
 // GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
 // epilogue.  "BIG" = 256x256 tiles, "MED" = 128x128 (4 waves), "PANEL" =
