@@ -96,14 +96,17 @@ void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit)
 
 // Split of the token contraction for dA / dB ([rows, N] outputs), each split
 // a multiple of 64 tokens and at least 256 long.  bf16 (dma) up to 128 rows:
-// splitnn_dma_kernel, every row in a 256-column tile and one block per CU,
-// so at most 256 blocks; else 64 x 256 tiles, two blocks per CU, at most
-// 512.  The split count rounds down so that every block runs in the first
-// round (560 blocks for 512 slots measured 25 % slower than 504).
+// splitnn_dma_kernel, every row in a 256-column tile: up to 64 rows and 32+
+// tiles two blocks per CU (512 slots), else one (256); wider or fp32: 64 x 256
+// tiles, two blocks per CU.  The split count rounds down so that every block
+// runs in the first round (560 blocks for 512 slots measured 25 % slower than
+// 504).  More splits mean more fp32 partials to sum: with 16 tiles the
+// two-per-CU form's 32 splits cost more in the sum than they gain.
 void choose_split(int64_t M, int64_t rows, int64_t N, bool dma, int* splits, int64_t* ksplit) {
   const bool one = dma && rows <= 128;
   const int64_t tiles = one ? cdiv(N, 256) : cdiv(rows, 64) * cdiv(N, 256);
-  int64_t s = (one ? 256 : 512) / tiles;
+  const int64_t slots = one && (rows > 64 || tiles < 32) ? 256 : 512;
+  int64_t s = slots / tiles;
   const int64_t smax = cdiv(M, 256);
   if (s > smax) s = smax;
   if (s < 1) s = 1;
@@ -563,6 +566,9 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
     uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
     HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
+      // r a multiple of 8: the tiled transpose (16-byte accesses), no pad rows
+      if (r == L.r8)
+        return launch_transpose_tile(static_cast<const uint16_t*>(B), r, d_out, r, Bt, d_out, d_out, st);
       return launch_transpose_pad(static_cast<const uint16_t*>(B), Bt, d_out, r, L.r8, st);
     }));
     TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, col_scale(scale), pp,

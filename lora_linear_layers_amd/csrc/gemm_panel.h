@@ -232,11 +232,12 @@ panel_dma_kernel(const GemmArgs p) {
 namespace sdma {
 constexpr int BN = 256, BK = 64, NT = 256;
 constexpr int B_BYTES = BK * BN * 2;  // 64 token rows of 512 bytes
-template <int BR>
+template <int BR, int NS_>
 struct Cfg {
   static constexpr int A_BYTES = BR * 128;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int NS = (160 * 1024) / STAGE;  // 4 for BR = 64, 3 for 128
+  static constexpr int NS = NS_;  // ring stages
+  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "the ring fits the LDS");
   static constexpr int IA = BR / 8 / 4;  // Aop instructions per wave
   static constexpr int IB = BK / 2 / 4;  // Bop instructions per wave
   static constexpr int PER = IA + IB;
@@ -245,11 +246,11 @@ struct Cfg {
 };
 }  // namespace sdma
 
-template <int BR>
-__global__ void __launch_bounds__(sdma::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BR, int NS_>
+__global__ void __launch_bounds__(sdma::NT) __attribute__((amdgpu_waves_per_eu(1, 2)))
 splitnn_dma_kernel(const GemmArgs p) {
   using namespace sdma;
-  using C = Cfg<BR>;
+  using C = Cfg<BR, NS_>;
   constexpr int NS = C::NS, LEAD = NS - 1, FM = C::FM, FN = C::FN;
   constexpr int A_BYTES = C::A_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[NS * C::STAGE];

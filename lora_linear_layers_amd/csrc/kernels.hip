@@ -72,10 +72,14 @@ hipError_t run_splitnn(GemmArgs a, int splits, hipStream_t st) {
   const int64_t tiles_n = (a.n_store + sdma::BN - 1) / sdma::BN;
   if (tiles_n <= 0 || splits <= 0) return hipSuccess;
   const dim3 grid((unsigned)tiles_n, (unsigned)splits);
-  if (a.m_store <= 64)
-    hipLaunchKernelGGL((splitnn_dma_kernel<64>), grid, dim3(sdma::NT), 0, st, a);
+  // up to 64 rows and more blocks than CUs: two blocks per CU (80 KB rings of
+  // 2 stages), else one per CU with every stage the LDS holds
+  if (a.m_store <= 64 && tiles_n * splits > 256)
+    hipLaunchKernelGGL((splitnn_dma_kernel<64, 2>), grid, dim3(sdma::NT), 0, st, a);
+  else if (a.m_store <= 64)
+    hipLaunchKernelGGL((splitnn_dma_kernel<64, 4>), grid, dim3(sdma::NT), 0, st, a);
   else
-    hipLaunchKernelGGL((splitnn_dma_kernel<128>), grid, dim3(sdma::NT), 0, st, a);
+    hipLaunchKernelGGL((splitnn_dma_kernel<128, 3>), grid, dim3(sdma::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -207,23 +211,28 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, uint16_t*
 __global__ void __launch_bounds__(256) transpose_tile_kernel(const uint16_t* __restrict__ src, int64_t lds,
                                                              int64_t R, int64_t C, uint16_t* __restrict__ dst,
                                                              int64_t ldd, int64_t Rpad) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[64][72];
+  // tile row rr holds its 16-byte chunk ch at chunk ch ^ ((rr >> 3) & 7): the
+  // column reads below (rows 8 qc + 2 k, qc < 8, of one column) then fall in
+  // 8 different chunks, so in different banks (with a plain or padded
+  // 16-byte-aligned row they share one bank, 8 ways)
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][64];
   const int64_t c0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 64;
   for (int e = threadIdx.x; e < 512; e += 256) {
     const int rr = e >> 3, ch = e & 7;
     const int64_t q = q0 + rr, c = c0 + 8 * ch;
     u32x4 v = {0u, 0u, 0u, 0u};
     if (q < R && c < C) v = *reinterpret_cast<const u32x4*>(src + q * lds + c);
-    *reinterpret_cast<u32x4*>(&t[rr][8 * ch]) = v;
+    *reinterpret_cast<u32x4*>(&t[rr][8 * (ch ^ ((rr >> 3) & 7))]) = v;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 512; e += 256) {
     const int cc = e >> 3, qc = e & 7;
     const int64_t c = c0 + cc, q = q0 + 8 * qc;
     if (c >= C || q >= Rpad) continue;
+    const int col = 8 * ((cc >> 3) ^ qc) + (cc & 7);  // rows 8 qc .. 8 qc + 7 share (row >> 3) & 7 = qc
     u32x4 o;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = (uint32_t)t[8 * qc + 2 * k][cc] | ((uint32_t)t[8 * qc + 2 * k + 1][cc] << 16);
+    for (int k = 0; k < 4; ++k) o[k] = (uint32_t)t[8 * qc + 2 * k][col] | ((uint32_t)t[8 * qc + 2 * k + 1][col] << 16);
     *reinterpret_cast<u32x4*>(dst + c * ldd + q) = o;
   }
 }
