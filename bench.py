@@ -71,6 +71,7 @@ KIND_OF = {
     "gemm_w4_nt_kernel<0>": "gemm_bf16_256x256_nt_store",
     "gemm_w4_nt_kernel<3>": "gemm_bf16_256x256_nt_rope",
     "gemm_w4_nt_kernel<6>": "gemm_bf16_256x256_swiglu",
+    "gemm_w4_nt_kernel<8>": "gemm_bf16_256x256_nt_group",
     "gemm_w4_nn_kernel<2>": "gemm_bf16_256x256_nn_store",
     "gemm_kernel<unsigned short, 256, 64, 4, 1, false, 4, 0>": "panel_bf16_split",
     "panel_dma_kernel": "panel_bf16_split",

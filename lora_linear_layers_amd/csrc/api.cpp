@@ -5,6 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -273,7 +274,8 @@ const char* kind_name(int k) {
       "panel_bf16_split",           "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
       "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
       "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "dropout_dx_bf16_128x128",
-      "dropout_dx_f32_64x128",      "pad_cols",                   "rope_inverse",
+      "dropout_dx_f32_64x128",      "gemm_bf16_256x256_nt_group", "pad_cols",
+      "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
       "copy_rows",                  "split_finish",               "swiglu_elementwise",
@@ -807,6 +809,55 @@ int group_rows(int64_t d_in, int n, const lora_group_member* mb, const GroupLayo
   return LORA_OK;
 }
 
+// Every member's forward GEMM in one whole-tile launch: bf16 W, M a multiple
+// of 256, each d_out a multiple of 256 (its tiles whole) and r of 8 (B read
+// as it is).  A k or v projection of 1024 outputs alone gives 128 tiles for
+// 256 CUs (and runs the 128 x 128 kernel); stacked with q and each other they
+// share the launch's waves of tiles.
+bool group_gemm_fits(int64_t M, int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G) {
+  if (M <= 0 || M % 256 || d_in % 64 || n > kGroupGemmMax) return false;
+  int64_t ld = std::max(d_in, G.rt);
+  for (int g = 0; g < n; ++g) {
+    if (mb[g].W_nf4 || mb[g].d_out % 256 || mb[g].r % 8) return false;
+    ld = std::max(ld, mb[g].r);
+  }
+  return whole_ld_fits(ld);
+}
+
+int group_gemm(int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X, const Rope* rope,
+               const uint16_t* P, const GroupLayout& G, hipStream_t st) {
+  GemmArgs a = blank();
+  a.a1 = X; a.lda1 = d_in; a.ldb1 = d_in; a.K1 = d_in; a.lda2 = G.rt;
+  a.m_load = M; a.m_store = M;
+  if (rope) { a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc; }
+  a.n_mem = n;
+  const int64_t tiles_m = M / 256;
+  int64_t cols = 0, ldb2 = 0;
+  double flop = 0, bytes = 2.0 * M * d_in;
+  for (int g = 0; g < n; ++g) {
+    const lora_group_member& m = mb[g];
+    a.mem_tile0[g] = (int)(tiles_m * (cols / 256));
+    a.mem_b1[g] = m.W;
+    a.mem_b2[g] = m.B;
+    a.mem_ldb2[g] = (int)m.r;
+    a.mem_a2[g] = P + G.off[g];
+    a.mem_k2[g] = (int)m.r;
+    a.mem_c[g] = m.Y;
+    a.mem_ldc[g] = (int)m.d_out;
+    a.mem_rope[g] = m.rope ? 1 : 0;
+    cols += m.d_out;
+    ldb2 = std::max(ldb2, m.r);
+    const double Md = double(M), ko = double(m.d_out), ki = double(d_in), rr = double(m.r);
+    flop += 2 * Md * ko * (ki + rr);
+    bytes += (Md * rr + ko * rr + Md * ko + ko * ki) * 2;
+  }
+  a.mem_tile0[n] = (int)(tiles_m * (cols / 256));
+  a.n_load = cols; a.n_store = cols;
+  a.ldb2 = ldb2;  // the widest member's, for the kernel's offset-range check
+  HIPTRY(gemm(G_BF16_WHOLE_GROUP, a, 1, st, flop, bytes));
+  return LORA_OK;
+}
+
 int group_forward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X,
                   const Rope* rope, const float* table16, void* ws, const GroupLayout& G, hipStream_t st) {
   char* w = static_cast<char*>(ws);
@@ -819,6 +870,7 @@ int group_forward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_me
     TRY(group_rows(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
     TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
                    reinterpret_cast<float*>(sh), P, G.rt, nullptr, 0, st, &src));
+    if (group_gemm_fits(M, d_in, n, mb, G)) return group_gemm(M, d_in, n, mb, X, rope, P, G, st);
   }
   for (int g = 0; g < n; ++g) {
     const lora_group_member& m = mb[g];

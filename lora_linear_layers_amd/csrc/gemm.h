@@ -57,12 +57,14 @@ enum Epi : int {
   EPI_PARTIAL = 4,     // fp32 partial slab of split z: C[z][m, n] = acc
   EPI_ADD = 5,         // C[m, n] = alpha * acc + Cin[m, n]  (type T; C may be Cin)
   EPI_SWIGLU = 6,      // whole-tile kernel only: gate/up pair -> silu(g) * u (see gemm_w4.h)
-  EPI_ADD_MASKED = 7   // C[m, n] = keep(m, n) ? alpha * acc + Cin[m, n] : Cin[m, n]
+  EPI_ADD_MASKED = 7,  // C[m, n] = keep(m, n) ? alpha * acc + Cin[m, n] : Cin[m, n]
+  EPI_GROUP = 8        // whole-tile kernel only: several projections' GEMMs, store or RoPE per member
 };
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
 
 constexpr int kPanelSrcMax = 8;  // row sources of a panel's Bop (a group's members)
+constexpr int kGroupGemmMax = 8;  // members of one group GEMM launch
 
 struct GemmArgs {
   const void* a1;
@@ -112,6 +114,23 @@ struct GemmArgs {
   const void* rs[kPanelSrcMax];
   int rs_beg[kPanelSrcMax];
   int rs_rows[kPanelSrcMax];
+  // gemm_w4_nt_kernel<EPI_GROUP>: the forward GEMMs of n_mem projections of
+  // one X in one launch.  Blocks [mem_tile0[g], mem_tile0[g + 1]) are member
+  // g's whole tiles (tiles_m per 256 of its columns, in the single GEMM's
+  // order); per member its W (row stride ldb1), B (row stride mem_ldb2), its
+  // columns of the stacked panel (mem_a2, row stride lda2), rank mem_k2, Y
+  // (mem_c, row stride mem_ldc = its column count) and the RoPE epilogue
+  // (mem_rope) or the store.
+  int n_mem;
+  int mem_tile0[kGroupGemmMax + 1];
+  const void* mem_b1[kGroupGemmMax];
+  const void* mem_b2[kGroupGemmMax];
+  const void* mem_a2[kGroupGemmMax];
+  void* mem_c[kGroupGemmMax];
+  int mem_k2[kGroupGemmMax];
+  int mem_ldb2[kGroupGemmMax];
+  int mem_ldc[kGroupGemmMax];
+  int mem_rope[kGroupGemmMax];
 };
 
 __device__ __forceinline__ int lds_off(int row, int chunk) {

@@ -69,7 +69,7 @@ constexpr uint32_t OOB = 0x40000000u;  // lane offset that reads zero
 //               set.
 template <int EPI>
 __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4::FM][w4::FN], char* smem,
-                                            int64_t m0, int64_t n0) {
+                                            int64_t m0, int64_t n0, void* c_out, int64_t ldc) {
   using namespace w4;
   auto fence = [] { __builtin_amdgcn_sched_barrier(0); };
   int te = threadIdx.x;
@@ -78,7 +78,7 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
   const int wm = __builtin_amdgcn_readfirstlane(te >> 7), wn = __builtin_amdgcn_readfirstlane((te >> 6) & 1);
   const int64_t rbase = m0 + wm * TM + 4 * hh;
   const int64_t cbase = n0 + wn * TN + l32;
-  uint16_t* out = reinterpret_cast<uint16_t*>(p.c);
+  uint16_t* out = reinterpret_cast<uint16_t*>(c_out);
   if constexpr (EPI == EPI_ROPE) {
     // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
     // first: 16-byte loads, all in flight together.  Row q's 64 values sit
@@ -133,8 +133,8 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
           for (int j = 0; j < FN / 2; ++j) {
             const int64_t col = cbase + 32 * j;
             const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
-            out[row * p.ldc + col] = f2bf(z1 * cs[vv][j] - z2 * sn[vv][j]);
-            out[row * p.ldc + col + 64] = f2bf(z2 * cs[vv][j] + z1 * sn[vv][j]);
+            out[row * ldc + col] = f2bf(z1 * cs[vv][j] - z2 * sn[vv][j]);
+            out[row * ldc + col + 64] = f2bf(z2 * cs[vv][j] + z1 * sn[vv][j]);
           }
         }
       }
@@ -153,7 +153,7 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
-            const int64_t o = row * p.ldc + hbase + 32 * jj;
+            const int64_t o = row * ldc + hbase + 32 * jj;
             out[o] = f2bf(g / (1.f + __expf(-g)) * u);
             if constexpr (GU == 1) {
               og[o] = f2bf(g);
@@ -179,7 +179,7 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
       for (int v = 0; v < 16; ++v) {
         const int64_t row = rbase + 32 * i + 8 * (v >> 2) + (v & 3);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) out[row * p.ldc + cbase + 32 * j] = f2bf(acc[i][j][v] * p.alpha);
+        for (int j = 0; j < FN; ++j) out[row * ldc + cbase + 32 * j] = f2bf(acc[i][j][v] * p.alpha);
       }
   }
 }
@@ -504,7 +504,7 @@ gemm_w4_nn_kernel(const GemmArgs p) {
     if (t < nk) stage(t, I0{});
   }
 
-  w4_epilogue<EPI_STORE>(p, acc, smem, m0, n0);
+  w4_epilogue<EPI_STORE>(p, acc, smem, m0, n0, p.c, p.ldc);
 }
 
 }  // namespace lora

@@ -31,6 +31,14 @@
 // reads (32 rows l32 of a block, chunk 2 s + l / 32) are conflict-free (a CPU
 // model of the banks checks every lane).
 //
+// Group (EPI_GROUP): the forward GEMMs of several projections of one X in
+// one launch.  Each block first finds its member (blocks [mem_tile0[g],
+// mem_tile0[g + 1]), a scalar search over the kernel arguments) and takes
+// that member's W, B, panel columns, rank, output and epilogue (RoPE or
+// store); the main loop is the single GEMM's.  q, k and v of an attention
+// block at 8192 tokens: 512 + 128 + 128 tiles in one launch instead of 512
+// whole tiles plus two 128 x 128-tile launches.
+//
 // SwiGLU (EPI_SWIGLU): B-tile rows 32 b .. 32 b + 31 come from the gate's
 // weight for even b and from the up's for odd b, rows n0 / 2 + 32 (b / 2) +
 // .. of each, so MFMA blocks j = 0, 2 of a wave hold gate outputs and
@@ -68,8 +76,10 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   using w4nt::SLOT;
   using w4nt::vmcnt_imm;
   constexpr int BKS = w4nt::BK;
-  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_SWIGLU, "store, RoPE or SwiGLU epilogue");
+  static_assert(EPI == EPI_STORE || EPI == EPI_ROPE || EPI == EPI_SWIGLU || EPI == EPI_GROUP,
+                "store, RoPE, SwiGLU or group epilogue");
   constexpr bool SW = EPI == EPI_SWIGLU;
+  constexpr bool GR = EPI == EPI_GROUP;
   __shared__ __attribute__((aligned(1024))) char smem[w4nt::LDS];
   // keep the MFMA accumulators in the accumulation registers
   asm volatile("" ::: "a0");
@@ -78,11 +88,33 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int bid = blockIdx.x;
+  // the block's GEMM: one projection, or (group) the member whose tiles hold
+  // this block, all of its parameters uniform
+  int bid = blockIdx.x;
+  const void* pa2 = p.a2;
+  const void* pb1 = p.b1;
+  const void* pb2 = p.b2;
+  int64_t ldb2 = p.ldb2, K2 = p.K2;
+  void* pc = p.c;
+  int64_t ldc = p.ldc;
+  int rope = 0;
+  if constexpr (GR) {
+    int g = 0;
+    for (int i = 1; i < p.n_mem; ++i) g = bid >= p.mem_tile0[i] ? i : g;
+    bid -= p.mem_tile0[g];
+    pa2 = p.mem_a2[g];
+    pb1 = p.mem_b1[g];
+    pb2 = p.mem_b2[g];
+    ldb2 = p.mem_ldb2[g];
+    K2 = p.mem_k2[g];
+    pc = p.mem_c[g];
+    ldc = p.mem_ldc[g];
+    rope = p.mem_rope[g];
+  }
   const int64_t m0 = (int64_t)(bid % p.tiles_m) * BM;
   const int64_t n0 = (int64_t)(bid / p.tiles_m) * BN;
   const int nk1 = (int)(p.K1 / BKS);
-  const int nk = nk1 + (int)((p.K2 + BKS - 1) / BKS);
+  const int nk = nk1 + (int)((K2 + BKS - 1) / BKS);
 
   // ---- DMA addressing ----
   // dr: the lane's row within an instruction's 8; dce / dco: its logical
@@ -95,14 +127,14 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   const int rowa = 64 * wave + dr;
   const int rowb = SW ? 32 * wave + dr : 64 * wave + dr;
   const char* ga1 = reinterpret_cast<const char*>(p.a1) + m0 * p.lda1 * 2;
-  const char* ga2 = reinterpret_cast<const char*>(p.a2) + m0 * p.lda2 * 2;
-  const char* gb1 = reinterpret_cast<const char*>(p.b1) + nb0 * p.ldb1 * 2;
-  const char* gb2 = reinterpret_cast<const char*>(p.b2) + nb0 * p.ldb2 * 2;
+  const char* ga2 = reinterpret_cast<const char*>(pa2) + m0 * p.lda2 * 2;
+  const char* gb1 = reinterpret_cast<const char*>(pb1) + nb0 * p.ldb1 * 2;
+  const char* gb2 = reinterpret_cast<const char*>(pb2) + nb0 * ldb2 * 2;
   const char* gb1u = SW ? reinterpret_cast<const char*>(p.b1u) + nb0 * p.ldb1 * 2 : gb1;
   const char* gb2u = SW ? reinterpret_cast<const char*>(p.b2u) + nb0 * p.ldb2u * 2 : gb2;
   // row parts of the lane offsets (+ 8 rows for odd instructions)
   const uint32_t ra1 = (uint32_t)(rowa * p.lda1 * 2), ra2 = (uint32_t)(rowa * p.lda2 * 2);
-  const uint32_t rb1 = (uint32_t)(rowb * p.ldb1 * 2), rb2 = (uint32_t)(rowb * p.ldb2 * 2);
+  const uint32_t rb1 = (uint32_t)(rowb * p.ldb1 * 2), rb2 = (uint32_t)(rowb * ldb2 * 2);
   const uint32_t rb2u = SW ? (uint32_t)(rowb * p.ldb2u * 2) : 0u;
   const uint32_t va1[2] = {ra1 + (uint32_t)(dce * 16), ra1 + (uint32_t)(8 * p.lda1 * 2 + dco * 16)};
   const uint32_t vb1[2] = {rb1 + (uint32_t)(dce * 16), rb1 + (uint32_t)(8 * p.ldb1 * 2 + dco * 16)};
@@ -110,11 +142,11 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   const uint32_t isa1 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.lda1 * 2));
   const uint32_t isa2 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.lda2 * 2));
   const uint32_t isb1 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb1 * 2));
-  const uint32_t isb2 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb2 * 2));
+  const uint32_t isb2 = __builtin_amdgcn_readfirstlane((uint32_t)(16 * ldb2 * 2));
   const uint32_t isb2u = SW ? __builtin_amdgcn_readfirstlane((uint32_t)(16 * p.ldb2u * 2)) : 0u;
-  const uint32_t oda2 = (uint32_t)(8 * p.lda2 * 2), odb2 = (uint32_t)(8 * p.ldb2 * 2);
+  const uint32_t oda2 = (uint32_t)(8 * p.lda2 * 2), odb2 = (uint32_t)(8 * ldb2 * 2);
   const uint32_t odb2u = SW ? (uint32_t)(8 * p.ldb2u * 2) : 0u;
-  const int k2 = __builtin_amdgcn_readfirstlane((int)p.K2);
+  const int k2 = __builtin_amdgcn_readfirstlane((int)K2);
   const int k2s = SW ? __builtin_amdgcn_readfirstlane((int)p.k2_split) : 0;
 
   // One DMA: stage u, operand op (0 A, 1 B), instruction i (< 8), slot s.
@@ -284,7 +316,14 @@ gemm_w4_nt_kernel(const GemmArgs p) {
   }
 
   // (the RoPE epilogue reuses the ring for its cos/sin rows after a barrier)
-  w4_epilogue<EPI>(p, acc, smem, m0, n0);
+  if constexpr (GR) {
+    if (rope)
+      w4_epilogue<EPI_ROPE>(p, acc, smem, m0, n0, pc, ldc);
+    else
+      w4_epilogue<EPI_STORE>(p, acc, smem, m0, n0, pc, ldc);
+  } else {
+    w4_epilogue<EPI>(p, acc, smem, m0, n0, pc, ldc);
+  }
 }
 
 }  // namespace lora

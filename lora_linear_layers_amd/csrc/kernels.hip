@@ -97,6 +97,8 @@ using bf = uint16_t;
 
 }  // namespace
 
+bool whole_ld_fits(int64_t ld) { return ld * 2 * (w4::BM + w4::BK) < (int64_t)w4::BIG; }
+
 bool panel_dma_fits(int64_t n_store, int64_t lda, int64_t ldb) {
   const int64_t ld = std::max(lda, ldb);
   return n_store <= 128 && ld * 2 * 256 < (int64_t)w4::BIG;
@@ -130,6 +132,7 @@ TileShape gemm_tile(GemmKind k) {
     case G_F32_SPLIT_NN_PARTIAL:
       return {64, 256};
     case G_BF16_WHOLE_SWIGLU:
+    case G_BF16_WHOLE_GROUP:
       return {256, 256};
     case G_BF16_PANEL_SPLIT_NT:
       return {256, 64};
@@ -184,6 +187,12 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
     case G_BF16_WHOLE_SWIGLU:
       if (!whole_tiles(a, splits)) return hipErrorInvalidValue;
       return run_whole<false, EPI_SWIGLU>(a, st);
+    case G_BF16_WHOLE_GROUP:
+      // the members' tile ranges must tile the launch exactly
+      if (!whole_tiles(a, splits) || a.n_mem < 1 || a.n_mem > kGroupGemmMax || a.mem_tile0[0] != 0 ||
+          (int64_t)a.mem_tile0[a.n_mem] != (a.m_store / w4::BM) * (a.n_store / w4::BN))
+        return hipErrorInvalidValue;
+      return run_whole<false, EPI_GROUP>(a, st);
     case G_F32_NN_ADD: return run<float, 64, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_ADD_MASKED: return run<bf, 128, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);
     case G_F32_NN_ADD_MASKED: return run<float, 64, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);

@@ -14,6 +14,9 @@ constexpr int PANEL_BM = 128;
 // The bf16 panel (G_BF16_PANEL_SPLIT_NT) runs panel_dma_kernel, which alone
 // takes Bop rows from several sources (GemmArgs::n_src), for these shapes.
 bool panel_dma_fits(int64_t n_store, int64_t lda, int64_t ldb);
+// The whole-tile kernels' buffer offsets stay in range for operands with row
+// strides up to ld (elements).
+bool whole_ld_fits(int64_t ld);
 
 // GEMM instances.  Suffixes: NT/NN = layout of the second operand, then the
 // epilogue.  "BIG" = 256x256 tiles, "MED" = 128x128 (4 waves), "PANEL" =
@@ -51,6 +54,7 @@ enum GemmKind : int {
   G_BF16_WHOLE_SWIGLU,
   G_BF16_MED_NN_ADD_MASKED,
   G_F32_NN_ADD_MASKED,
+  G_BF16_WHOLE_GROUP,  // several projections' forward GEMMs in one whole-tile launch (GemmArgs::n_mem)
   G_KIND_COUNT
 };
 

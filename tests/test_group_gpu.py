@@ -65,6 +65,64 @@ def test_group_parity(lib, dtype, case):
         assert all(e <= TOL[dtype] for e in errs.values()), (g, errs)
 
 
+def _group_kinds(fn):
+    from lora_linear_layers_amd import _lib
+    _lib.profile_begin(512)
+    out = fn()
+    torch.cuda.synchronize()
+    _lib.profile_end()
+    return out, set(_lib.profile_report())
+
+
+# (M, d_in, [(d_out, r, rope), ...]): every member's tiles whole and r a
+# multiple of 8, so the forward runs every member's GEMM in one launch: RoPE
+# and store members mixed, members of one and of two column tiles.
+GROUP_GEMM = [
+    (512, 512, [(512, 16, True), (256, 8, True), (256, 24, False)]),
+    (256, 320, [(256, 8, False), (768, 16, True)]),
+]
+
+
+@pytest.mark.parametrize("case", GROUP_GEMM, ids=[f"M{g[0]}_k{g[1]}_n{len(g[2])}" for g in GROUP_GEMM])
+def test_group_gemm_parity(lib, case):
+    M, d_in, spec = case
+    seq = 128
+    X = draw(900 + M, (M, d_in), "normal", 1.0, "bf16")
+    pos = torch.from_numpy(gen.positions_mod(M, seq)).cuda()
+    cos, sin = lib.rope_cache(seq, 128, 500000.0)
+    members, dYs = [], []
+    for g, (d_out, r, rope) in enumerate(spec):
+        W, A, B, dY = _member_inputs(910 + 10 * g + M, M, d_in, d_out, r, "bf16")
+        members.append(dict(W=W, A=A, B=B, scale=(16.0 + 8 * g) / r, rope=rope))
+        dYs.append(dY)
+    Ys, kinds = _group_kinds(lambda: lib.lora_group_fwd(X, members, pos, cos, sin))
+    assert kinds & {k for k in kinds if k.startswith("gemm")} == {"gemm_bf16_256x256_nt_group"}, kinds
+    p = pos.cpu().numpy()
+    for g, m in enumerate(members):
+        Yr = O.qk_rope_forward(X, m["W"], m["A"], m["B"], m["scale"], p) if m["rope"] else \
+            O.lora_forward(X, m["W"], m["A"], m["B"], m["scale"])
+        err = rel(Ys[g], Yr)
+        print(case[:2], g, spec[g], err)
+        assert err <= TOL["bf16"], (g, err)
+
+
+def test_group_gemm_integer_exact(lib):
+    # small integers: every product and sum exact on both sides, so each
+    # member's Y from the one-launch group GEMM equals the oracle exactly
+    M, d_in = 256, 64
+    X, _, _, _, _ = int_inputs(41, M, d_in, 8, 1, "bf16")
+    members = []
+    for g, (d_out, r) in enumerate([(256, 8), (512, 16)]):
+        _, W, A, B, _ = int_inputs(43 + g, M, d_in, d_out, r, "bf16")
+        members.append(dict(W=W, A=A, B=B, scale=float(2 - g)))
+    Ys, kinds = _group_kinds(lambda: lib.lora_group_fwd(X, members))
+    assert "gemm_bf16_256x256_nt_group" in kinds, kinds
+    for g, m in enumerate(members):
+        Yr = O.lora_forward(X, m["W"], m["A"], m["B"], m["scale"])
+        assert np.abs(Yr).max() <= 256
+        assert np.array_equal(cpu64(Ys[g]), Yr), g
+
+
 def test_group_whole_tile_parity(lib):
     # q, k, v of one attention block at full width: q (and dX of every member)
     # on the whole-tile kernel; Y and dX on sampled rows, dA and dB in full.
