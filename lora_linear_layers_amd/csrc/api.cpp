@@ -69,6 +69,7 @@ struct Layout {
   int64_t ksplit_dA = 0, ksplit_dB = 0;
   int splits_p = 1, splits_q = 1;  // bf16 rank-r panels: P = X A^T, Q = G B
   int64_t ksplit_p = 0, ksplit_q = 0;
+  size_t partb = 0;  // bf16: the dB partials, apart from dA's so one launch sums both
 };
 
 // 256x256 tiles when they still give at least one tile per CU, else 128x128.
@@ -198,7 +199,12 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     size_t pa = size_t(L.splits_dA) * L.r8 * d_in * 4;
     size_t pb = size_t(L.splits_dB) * L.r8 * d_out * 4;
     if (sp > pa) pa = sp;  // the dX partials are reduced before dB and dA start
-    L.part = take(pa > pb ? pa : pb);
+    if (eb == 2) {
+      L.part = take(pa);
+      L.partb = take(pb);
+    } else {
+      L.part = take(pa > pb ? pa : pb);
+    }
     L.spart = L.part;
   }
   if (drop) L.xm = take(size_t(M) * d_in * eb);
@@ -492,6 +498,13 @@ struct PanelSlices {
   void* Qs;
   int64_t ldqs;
   void* Qt;
+  // the group's: B^T and A^T made for every member in one launch (NULL:
+  // made here), the member's own dB partials, and the batch that sums them
+  // with every member's dA after the group's dA contraction
+  const void* Bt = nullptr;
+  const void* At = nullptr;
+  float* partb = nullptr;
+  ReduceBatch* red = nullptr;
 };
 
 int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
@@ -542,6 +555,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const int64_t ldqs = ov ? ov->ldqs : L.r8;
   void* Qt = ov ? ov->Qt : w + L.qt;
   float* part = reinterpret_cast<float*>(w + L.part);
+  bool at_done = false;  // A^T made with B^T (bf16)
   if (f32) {
     // Pt = (s X A^T)^T  [r8, M8]  (recomputed; pads are zeros)
     {
@@ -565,14 +579,29 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     if (!ov)
       TRY(panel_bf16(Xp, d_in, A, d_in, M, L.M8, d_in, r, L.r8, L.splits_p, L.ksplit_p, col_scale(scale), pp,
                      nullptr, 0, reinterpret_cast<uint16_t*>(w + L.pt), L.M8, st));
-    // Bt = B^T [r8, d_out]; then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
-    uint16_t* Bt = reinterpret_cast<uint16_t*>(w + L.bt);
-    HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
-      // r a multiple of 8: the tiled transpose (16-byte accesses), no pad rows
-      if (r == L.r8)
-        return launch_transpose_tile(static_cast<const uint16_t*>(B), r, d_out, r, Bt, d_out, d_out, st);
-      return launch_transpose_pad(static_cast<const uint16_t*>(B), Bt, d_out, r, L.r8, st);
-    }));
+    // Bt = B^T [r8, d_out] (and A^T for the whole-tile dX below, in the same
+    // launch); then Qs = s G B [M8, r8] and Qt = Qs^T [r8, M8]
+    const void* Bt = ov ? ov->Bt : nullptr;
+    if (!Bt) {
+      uint16_t* bt = reinterpret_cast<uint16_t*>(w + L.bt);
+      Bt = bt;
+      const bool with_at = dX && L.dx_nt && !(ov && ov->At);
+      if (r == L.r8) {
+        // the tiled transpose (16-byte accesses); r a multiple of 8, no pad rows
+        TransposeBatch tb;
+        HIPTRY(tb.add(static_cast<const uint16_t*>(B), r, d_out, r, bt, d_out, d_out));
+        if (with_at)
+          HIPTRY(tb.add(static_cast<const uint16_t*>(A), d_in, r, d_in, reinterpret_cast<uint16_t*>(w + L.at), L.r8,
+                        L.r8));
+        HIPTRY(timed(K_TRANSPOSE, 0, 4.0 * rr * (d_out + (with_at ? d_in : 0)), st,
+                     [&] { return launch_transpose_batch(tb, st); }));
+        at_done = with_at;
+      } else {
+        HIPTRY(timed(K_TRANSPOSE, 0, 2.0 * d_out * (rr + L.r8) * e / 2, st, [&] {
+          return launch_transpose_pad(static_cast<const uint16_t*>(B), bt, d_out, r, L.r8, st);
+        }));
+      }
+    }
     TRY(panel_bf16(G, d_out, Bt, d_out, M, L.M8, d_out, r, L.r8, L.splits_q, L.ksplit_q, col_scale(scale), pp,
                    static_cast<uint16_t*>(Qs), ldqs, static_cast<uint16_t*>(Qt), L.M8, st));
   }
@@ -582,7 +611,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     // W read with its contraction rows costs the whole-tile kernel ~12 % more
     // than the same product read as W^T, which one transposing pass gives
     const void* Wt = Wt_in;
-    uint16_t* At = reinterpret_cast<uint16_t*>(w + L.at);
+    const void* At = ov && ov->At ? ov->At : w + L.at;
     if (!Wt) {
       uint16_t* wt = reinterpret_cast<uint16_t*>(w + L.wt);
       HIPTRY(timed(K_TRANSPOSE_W, 0, 4.0 * ko * ki, st, [&] {
@@ -590,9 +619,11 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
       }));
       Wt = wt;
     }
-    HIPTRY(timed(K_TRANSPOSE_W, 0, 2.0 * rr * ki + 2.0 * ki * L.r8, st, [&] {
-      return launch_transpose_tile(static_cast<const uint16_t*>(A), d_in, r, d_in, At, L.r8, L.r8, st);
-    }));
+    if (!(ov && ov->At) && !at_done)
+      HIPTRY(timed(K_TRANSPOSE_W, 0, 2.0 * rr * ki + 2.0 * ki * L.r8, st, [&] {
+        return launch_transpose_tile(static_cast<const uint16_t*>(A), d_in, r, d_in,
+                                     reinterpret_cast<uint16_t*>(w + L.at), L.r8, L.r8, st);
+      }));
     GemmArgs a = blank();
     a.a1 = G; a.lda1 = d_out; a.b1 = Wt; a.ldb1 = d_out; a.K1 = d_out;
     a.a2 = Qs; a.lda2 = ldqs; a.b2 = At; a.ldb2 = L.r8; a.K2 = keep ? 0 : r;
@@ -642,17 +673,25 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
                 (Md * rr + rr * ki + 2 * Md * ki) * e + Md * ki / 8));
   }
   const GemmKind ksplit = f32 ? G_F32_SPLIT_NN_PARTIAL : G_BF16_SPLIT_NN_PARTIAL;
+  // bf16: the dB partials have their own buffer and both sums run as one
+  // launch (a group's: one for all its members, after the group's dA)
+  float* partb = f32 ? part : (ov && ov->partb ? ov->partb : reinterpret_cast<float*>(w + L.partb));
+  ReduceBatch own;
+  ReduceBatch* red = f32 ? nullptr : (ov && ov->red ? ov->red : &own);
   // dB^T = Pt G  -> partials [splits][r8, d_out] -> dB [d_out, r]
   {
     GemmArgs a = blank();
     a.a1 = Pt; a.lda1 = L.M8; a.b1 = G; a.ldb1 = d_out; a.K1 = M;
     a.m_load = L.r8; a.m_store = L.r8; a.n_load = d_out; a.n_store = d_out;
-    a.k_split = L.ksplit_dB; a.c = part; a.ldc = d_out; a.part_stride = L.r8 * d_out;
+    a.k_split = L.ksplit_dB; a.c = partb; a.ldc = d_out; a.part_stride = L.r8 * d_out;
     HIPTRY(gemm(ksplit, a, L.splits_dB, st, 2 * rr * ko * Md,
                 (rr * Md + Md * ko) * e + 4.0 * L.splits_dB * L.r8 * ko));
-    HIPTRY(timed(K_REDUCE, double(L.splits_dB) * rr * ko, 4.0 * (L.splits_dB + 1) * rr * ko, st, [&] {
-      return launch_reduce_splits(part, L.splits_dB, r, d_out, L.r8 * d_out, true, dB, st);
-    }));
+    if (red)
+      HIPTRY(red->add(partb, L.splits_dB, r, d_out, L.r8 * d_out, true, dB));
+    else
+      HIPTRY(timed(K_REDUCE, double(L.splits_dB) * rr * ko, 4.0 * (L.splits_dB + 1) * rr * ko, st, [&] {
+        return launch_reduce_splits(partb, L.splits_dB, r, d_out, L.r8 * d_out, true, dB, st);
+      }));
   }
   // dA = Qt X -> partials [splits][r8, d_in] -> dA [r, d_in]
   if (!ov) {
@@ -662,10 +701,17 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
     a.k_split = L.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = L.r8 * d_in;
     HIPTRY(gemm(ksplit, a, L.splits_dA, st, 2 * rr * ki * Md,
                 (rr * Md + Md * ki) * e + 4.0 * L.splits_dA * L.r8 * ki));
-    HIPTRY(timed(K_REDUCE, double(L.splits_dA) * rr * ki, 4.0 * (L.splits_dA + 1) * rr * ki, st, [&] {
-      return launch_reduce_splits(part, L.splits_dA, r, d_in, L.r8 * d_in, false, dA, st);
-    }));
+    if (red)
+      HIPTRY(red->add(part, L.splits_dA, r, d_in, L.r8 * d_in, false, dA));
+    else
+      HIPTRY(timed(K_REDUCE, double(L.splits_dA) * rr * ki, 4.0 * (L.splits_dA + 1) * rr * ki, st, [&] {
+        return launch_reduce_splits(part, L.splits_dA, r, d_in, L.r8 * d_in, false, dA, st);
+      }));
   }
+  if (red == &own)
+    HIPTRY(timed(K_REDUCE, double(L.splits_dB) * rr * ko + (ov ? 0.0 : double(L.splits_dA) * rr * ki),
+                 4.0 * (L.splits_dB + 1) * rr * ko + (ov ? 0.0 : 4.0 * (L.splits_dA + 1) * rr * ki), st,
+                 [&] { return launch_reduce_batch(own, st); }));
   return LORA_OK;
 }
 
@@ -694,6 +740,9 @@ int check_nf4(int64_t d_in, int blocksize, const uint8_t* codes, const float* ab
 struct GroupLayout {
   int64_t rt = 0, M8 = 0, off[LORA_GROUP_MAX] = {};
   size_t acat = 0, p = 0, pt = 0, qs = 0, qt = 0, shared = 0, total = 0;
+  // bf16 backward, per member: B^T, A^T and the dB partials, kept until the
+  // group's batched transposes and sums
+  size_t bt[LORA_GROUP_MAX] = {}, at[LORA_GROUP_MAX] = {}, partb[LORA_GROUP_MAX] = {};
   int splits_g = 1, splits_dA = 1;
   int64_t ksplit_g = 0, ksplit_dA = 0;
   Layout mem[LORA_GROUP_MAX];
@@ -734,6 +783,12 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
       G.pt = take(size_t(G.rt) * G.M8 * eb);
       G.qs = take(size_t(G.M8) * G.rt * eb);
       G.qt = take(size_t(G.rt) * G.M8 * eb);
+      for (int g = 0; g < n; ++g) {
+        const Layout& L = G.mem[g];
+        G.bt[g] = take(size_t(L.r8) * mb[g].d_out * eb);
+        G.at[g] = take(size_t(d_in) * L.r8 * eb);
+        G.partb[g] = take(size_t(L.splits_dB) * L.r8 * mb[g].d_out * 4);
+      }
       choose_split(M, G.rt, d_in, true, &G.splits_dA, &G.ksplit_dA);
       const size_t pa = size_t(G.splits_dA) * G.rt * d_in * 4;
       if (pa > shared) shared = pa;
@@ -896,10 +951,38 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
     TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, G.M8, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
                    reinterpret_cast<float*>(sh), nullptr, 0, Pt, G.M8, st, &src));
   }
+  // every member's B^T (r a multiple of 8) and A^T (whole-tile dX) in one launch
+  TransposeBatch tb;
+  bool have_bt[LORA_GROUP_MAX] = {}, have_at[LORA_GROUP_MAX] = {};
+  double tbytes = 0;
+  if (share) {
+    for (int g = 0; g < n; ++g) {
+      const lora_group_member& m = mb[g];
+      const Layout& L = G.mem[g];
+      if (m.r == L.r8) {
+        HIPTRY(tb.add(static_cast<const uint16_t*>(m.B), m.r, m.d_out, m.r, reinterpret_cast<uint16_t*>(w + G.bt[g]),
+                      m.d_out, m.d_out));
+        have_bt[g] = true;
+        tbytes += 4.0 * m.r * m.d_out;
+        if (m.dX && L.dx_nt) {
+          HIPTRY(tb.add(static_cast<const uint16_t*>(m.A), d_in, m.r, d_in, reinterpret_cast<uint16_t*>(w + G.at[g]),
+                        L.r8, L.r8));
+          have_at[g] = true;
+          tbytes += 4.0 * m.r * d_in;
+        }
+      }
+    }
+    HIPTRY(timed(K_TRANSPOSE, 0, tbytes, st, [&] { return launch_transpose_batch(tb, st); }));
+  }
+  ReduceBatch red;
   for (int g = 0; g < n; ++g) {
     const lora_group_member& m = mb[g];
     const Nf4W q{m.W_nf4, m.absmax, table16};
-    const PanelSlices ov{Pt + G.off[g] * G.M8, Qs + G.off[g], G.rt, Qt + G.off[g] * G.M8};
+    PanelSlices ov{Pt + G.off[g] * G.M8, Qs + G.off[g], G.rt, Qt + G.off[g] * G.M8};
+    ov.Bt = have_bt[g] ? w + G.bt[g] : nullptr;
+    ov.At = have_at[g] ? w + G.at[g] : nullptr;
+    ov.partb = reinterpret_cast<float*>(w + G.partb[g]);
+    ov.red = &red;
     TRY(backward_impl(dtype, M, d_in, m.d_out, m.r, m.scale, X, m.W, m.W_nf4 ? &q : nullptr, m.A, m.B,
                       m.rope ? rope : nullptr, m.dY, m.dX, m.dA, m.dB, sh, G.mem[g], st, share ? &ov : nullptr,
                       nullptr, nullptr, G.mem[g].dx_nt && !m.W_nf4 ? m.W_t : nullptr));
@@ -914,13 +997,16 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   a.k_split = G.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = G.rt * d_in;
   HIPTRY(gemm(G_BF16_SPLIT_NN_PARTIAL, a, G.splits_dA, st, 2 * rr * ki * Md,
               (rr * Md + Md * ki) * 2 + 4.0 * G.splits_dA * G.rt * ki));
+  // every member's dA and (added by the members) dB sums in one launch
+  double rflop = 0, rbytes = 0;
   for (int g = 0; g < n; ++g) {
-    const double rg = double(mb[g].r);
-    HIPTRY(timed(K_REDUCE, double(G.splits_dA) * rg * ki, 4.0 * (G.splits_dA + 1) * rg * ki, st, [&] {
-      return launch_reduce_splits(part + G.off[g] * d_in, G.splits_dA, mb[g].r, d_in, G.rt * d_in, false, mb[g].dA,
-                                  st);
-    }));
+    const double rg = double(mb[g].r), ko = double(mb[g].d_out);
+    const int sb = G.mem[g].splits_dB;
+    HIPTRY(red.add(part + G.off[g] * d_in, G.splits_dA, mb[g].r, d_in, G.rt * d_in, false, mb[g].dA));
+    rflop += double(G.splits_dA) * rg * ki + double(sb) * rg * ko;
+    rbytes += 4.0 * (G.splits_dA + 1) * rg * ki + 4.0 * (sb + 1) * rg * ko;
   }
+  HIPTRY(timed(K_REDUCE, rflop, rbytes, st, [&] { return launch_reduce_batch(red, st); }));
   return LORA_OK;
 }
 

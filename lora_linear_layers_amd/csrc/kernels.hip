@@ -217,15 +217,15 @@ __global__ void transpose_pad_kernel(const uint16_t* __restrict__ src, uint16_t*
 // dst[c, q] = q < R ? src[q, c] : 0 for c < C, q < Rpad: a bf16 transpose
 // through a 64 x 64 LDS tile, 16-byte loads and stores (C and Rpad multiples
 // of 8).
-__global__ void __launch_bounds__(256) transpose_tile_kernel(const uint16_t* __restrict__ src, int64_t lds,
-                                                             int64_t R, int64_t C, uint16_t* __restrict__ dst,
-                                                             int64_t ldd, int64_t Rpad) {
-  // tile row rr holds its 16-byte chunk ch at chunk ch ^ ((rr >> 3) & 7): the
-  // column reads below (rows 8 qc + 2 k, qc < 8, of one column) then fall in
-  // 8 different chunks, so in different banks (with a plain or padded
-  // 16-byte-aligned row they share one bank, 8 ways)
-  __shared__ __attribute__((aligned(16))) uint16_t t[64][64];
-  const int64_t c0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 64;
+// One 64 x 64 tile of dst[c, q] = q < R ? src[q, c] : 0, columns c0 .., rows
+// of the transpose q0 ...
+// The tile row rr holds its 16-byte chunk ch at chunk ch ^ ((rr >> 3) & 7): the
+// column reads below (rows 8 qc + 2 k, qc < 8, of one column) then fall in
+// 8 different chunks, so in different banks (with a plain or padded
+// 16-byte-aligned row they share one bank, 8 ways)
+__device__ __forceinline__ void transpose_tile(const uint16_t* __restrict__ src, int64_t lds, int64_t R, int64_t C,
+                                               uint16_t* __restrict__ dst, int64_t ldd, int64_t Rpad, int64_t c0,
+                                               int64_t q0, uint16_t (*t)[64]) {
   for (int e = threadIdx.x; e < 512; e += 256) {
     const int rr = e >> 3, ch = e & 7;
     const int64_t q = q0 + rr, c = c0 + 8 * ch;
@@ -244,6 +244,44 @@ __global__ void __launch_bounds__(256) transpose_tile_kernel(const uint16_t* __r
     for (int k = 0; k < 4; ++k) o[k] = (uint32_t)t[8 * qc + 2 * k][col] | ((uint32_t)t[8 * qc + 2 * k + 1][col] << 16);
     *reinterpret_cast<u32x4*>(dst + c * ldd + q) = o;
   }
+}
+
+__global__ void __launch_bounds__(256) transpose_tile_kernel(const uint16_t* __restrict__ src, int64_t lds,
+                                                             int64_t R, int64_t C, uint16_t* __restrict__ dst,
+                                                             int64_t ldd, int64_t Rpad) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][64];
+  transpose_tile(src, lds, R, C, dst, ldd, Rpad, (int64_t)blockIdx.x * 64, (int64_t)blockIdx.y * 64, t);
+}
+
+// the jobs' tiles, job by job (the job of a block: a scalar search)
+__global__ void __launch_bounds__(256) transpose_batch_kernel(const TransposeBatch b) {
+  __shared__ __attribute__((aligned(16))) uint16_t t[64][64];
+  const int blk = blockIdx.x;
+  int g = 0;
+  for (int i = 1; i < b.n; ++i) g = blk >= b.j[i].block0 ? i : g;
+  const TransposeJob& J = b.j[g];
+  const int lb = blk - J.block0;
+  transpose_tile(J.src, J.lds, J.R, J.C, J.dst, J.ldd, J.Rpad, (int64_t)(lb % J.tiles_c) * 64,
+                 (int64_t)(lb / J.tiles_c) * 64, t);
+}
+
+hipError_t TransposeBatch::add(const uint16_t* src, int64_t lds, int64_t R, int64_t C, uint16_t* dst, int64_t ldd,
+                               int64_t Rpad) {
+  if (R <= 0 || C <= 0 || Rpad <= 0) return hipSuccess;  // nothing to do
+  if (n >= kBatchJobsMax || C % 8 || Rpad % 8 || Rpad < R || ldd < Rpad || ldd % 8 || lds % 8)
+    return hipErrorInvalidValue;
+  const int64_t tc = (C + 63) / 64, tiles = tc * ((Rpad + 63) / 64);
+  if (blocks + tiles > INT32_MAX) return hipErrorInvalidValue;
+  j[n] = TransposeJob{src, dst, lds, R, C, ldd, Rpad, blocks, (int)tc};
+  blocks += (int)tiles;
+  ++n;
+  return hipSuccess;
+}
+
+hipError_t launch_transpose_batch(const TransposeBatch& b, hipStream_t st) {
+  if (b.n == 0 || b.blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_batch_kernel, dim3((unsigned)b.blocks), dim3(256), 0, st, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_transpose_tile(const uint16_t* src, int64_t lds, int64_t R, int64_t C, uint16_t* dst, int64_t ldd,
@@ -394,16 +432,14 @@ __device__ __forceinline__ float4 sum_splits(const float* __restrict__ src, int 
 
 // out[q, c] (transpose: out[c, q]) = sum over z < splits of part[z][q, c],
 // in split order, for q < rows, c < N (N a multiple of 4).  A block covers
-// 16 rows x 64 columns, thread t columns 4 (t & 15) .. +3 of row t >> 4,
-// with the float4 loads of up to 8 splits in flight before their sums.  The
-// transposed store goes through an LDS tile so that consecutive threads
-// write consecutive q.
-__global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restrict__ part, int splits,
-                                                            int64_t rows, int64_t N, int64_t part_stride,
-                                                            int transpose, float* __restrict__ out) {
-  __shared__ float tile[16][65];
+// 16 rows x 64 columns (from q0, c0), thread t columns 4 (t & 15) .. +3 of
+// row t >> 4, with the float4 loads of up to 8 splits in flight before their
+// sums.  The transposed store goes through an LDS tile so that consecutive
+// threads write consecutive q.
+__device__ __forceinline__ void reduce_tile(const float* __restrict__ part, int splits, int64_t rows, int64_t N,
+                                            int64_t part_stride, int transpose, float* __restrict__ out,
+                                            int64_t c0, int64_t q0, float (*tile)[65]) {
   const int tid = threadIdx.x;
-  const int64_t c0 = (int64_t)blockIdx.x * 64, q0 = (int64_t)blockIdx.y * 16;
   const int cl = 4 * (tid & 15), rl = tid >> 4;
   const int64_t c = c0 + cl, q = q0 + rl;
   const bool ok = c < N && q < rows;
@@ -433,6 +469,46 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restr
     const int64_t qg = q0 + qq, cg = c0 + cc;
     if (qg < rows && cg < N) out[cg * rows + qg] = tile[qq][cc];
   }
+}
+
+__global__ void __launch_bounds__(256) reduce_splits_kernel(const float* __restrict__ part, int splits,
+                                                            int64_t rows, int64_t N, int64_t part_stride,
+                                                            int transpose, float* __restrict__ out) {
+  __shared__ float tile[16][65];
+  reduce_tile(part, splits, rows, N, part_stride, transpose, out, (int64_t)blockIdx.x * 64,
+              (int64_t)blockIdx.y * 16, tile);
+}
+
+// the jobs' tiles, job by job (the job of a block: a scalar search)
+__global__ void __launch_bounds__(256) reduce_batch_kernel(const ReduceBatch b) {
+  __shared__ float tile[16][65];
+  const int blk = blockIdx.x;
+  int g = 0;
+  for (int i = 1; i < b.n; ++i) g = blk >= b.j[i].block0 ? i : g;
+  const ReduceJob& J = b.j[g];
+  const int lb = blk - J.block0;
+  reduce_tile(J.part, J.splits, J.rows, J.N, J.part_stride, J.transpose, J.out, (int64_t)(lb % J.tiles_n) * 64,
+              (int64_t)(lb / J.tiles_n) * 16, tile);
+}
+
+hipError_t ReduceBatch::add(const float* part, int splits, int64_t rows, int64_t N, int64_t part_stride,
+                            bool transpose, float* out) {
+  if (rows <= 0 || N <= 0) return hipSuccess;  // nothing to do
+  if (n >= kBatchJobsMax || splits < 1 || splits > kMaxSplits || N % 4 || part_stride % 4 ||
+      reinterpret_cast<uintptr_t>(part) % 16)
+    return hipErrorInvalidValue;
+  const int64_t tn = (N + 63) / 64, tiles = tn * ((rows + 15) / 16);
+  if (blocks + tiles > INT32_MAX) return hipErrorInvalidValue;
+  j[n] = ReduceJob{part, out, rows, N, part_stride, splits, transpose ? 1 : 0, blocks, (int)tn};
+  blocks += (int)tiles;
+  ++n;
+  return hipSuccess;
+}
+
+hipError_t launch_reduce_batch(const ReduceBatch& b, hipStream_t st) {
+  if (b.n == 0 || b.blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(reduce_batch_kernel, dim3((unsigned)b.blocks), dim3(256), 0, st, b);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N, int64_t part_stride,

@@ -92,6 +92,38 @@ hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float*
 hipError_t launch_reduce_splits(const float* part, int splits, int64_t rows, int64_t N,
                                 int64_t part_stride, bool transpose, float* out, hipStream_t st);
 
+// Several independent launch_reduce_splits / launch_transpose_tile jobs in ONE
+// launch (a layer's dA and dB sums, a group's A^T and B^T): the blocks are
+// dealt to the jobs in order.  add() checks each job as the single launch
+// would and returns hipErrorInvalidValue (job not added) otherwise.
+constexpr int kBatchJobsMax = 16;
+struct ReduceJob {
+  const float* part;
+  float* out;
+  int64_t rows, N, part_stride;
+  int splits, transpose, block0, tiles_n;
+};
+struct ReduceBatch {
+  int n = 0, blocks = 0;
+  ReduceJob j[kBatchJobsMax];
+  hipError_t add(const float* part, int splits, int64_t rows, int64_t N, int64_t part_stride, bool transpose,
+                 float* out);
+};
+hipError_t launch_reduce_batch(const ReduceBatch& b, hipStream_t st);
+
+struct TransposeJob {
+  const uint16_t* src;
+  uint16_t* dst;
+  int64_t lds, R, C, ldd, Rpad;
+  int block0, tiles_c;
+};
+struct TransposeBatch {
+  int n = 0, blocks = 0;
+  TransposeJob j[kBatchJobsMax];
+  hipError_t add(const uint16_t* src, int64_t lds, int64_t R, int64_t C, uint16_t* dst, int64_t ldd, int64_t Rpad);
+};
+hipError_t launch_transpose_batch(const TransposeBatch& b, hipStream_t st);
+
 // Per-column scale of a panel: column c takes s[i] for the first i < n with
 // c < end[i] (one entry per projection of a group; n = 1 for one projection).
 constexpr int kColScaleMax = 8;
