@@ -92,7 +92,6 @@ KIND_OF = {
     "reduce_splits_kernel": "reduce_splits",
     "transpose_pad_kernel": "transpose_pad",
     "rope_inverse_kernel": "rope_inverse",
-    "copy_rows_kernel": "copy_rows",
     "transpose_tile_kernel": "transpose_w",
     "split_finish_kernel": "split_finish",
 }

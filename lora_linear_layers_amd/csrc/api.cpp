@@ -81,11 +81,11 @@ bool use_big(int64_t M, int64_t N) { return cdiv(M, 256) * cdiv(N, 256) >= 256; 
 // a multiple of 64 and at least 8 stages long (4 when a few tokens leave
 // fewer than 16 tiles).
 void panel_split(int64_t M, int64_t K, int64_t r8, int* splits, int64_t* ksplit) {
-  // up to 128 columns: one 256-row tile holds every column and one block per
-  // CU runs (160 KB of LDS each); wider panels take 64-column tiles
-  int64_t tiles = r8 <= 128 ? cdiv(M, PANEL_BM) : cdiv(M, 256) * cdiv(r8, 64);
+  // up to 256 columns: one 128-row tile holds every column and one block per
+  // CU runs (up to 160 KB of LDS each); wider panels take 64-column tiles
+  int64_t tiles = r8 <= 256 ? cdiv(M, PANEL_BM) : cdiv(M, 256) * cdiv(r8, 64);
   if (tiles < 1) tiles = 1;
-  int64_t s = cdiv(r8 <= 128 ? 256 : 384, tiles);
+  int64_t s = cdiv(r8 <= 256 ? 256 : 384, tiles);
   int64_t smax = tiles < 16 ? K / 256 : K / 512;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;
@@ -260,7 +260,6 @@ enum ProfKind : int {
   K_NF4_DEQ,
   K_PANEL,
   K_TRANSPOSE,
-  K_COPY_ROWS,
   K_FINISH,
   K_SWIGLU,
   K_MASK,
@@ -284,7 +283,7 @@ const char* kind_name(int k) {
       "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_pad",
-      "copy_rows",                  "split_finish",               "swiglu_elementwise",
+      "split_finish",               "swiglu_elementwise",
       "dropout_mask_copy",          "transpose_w",                "skinny_fwd"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
@@ -732,19 +731,27 @@ int check_nf4(int64_t d_in, int blocksize, const uint8_t* codes, const float* ab
 // ---------------------------------------------------------------------------
 // groups of projections sharing X
 // ---------------------------------------------------------------------------
-// bf16 workspace: Acat = [A_1; ..; A_n] with each A_g padded to r8_g rows
-// (rt = sum r8_g rows, member g at row off[g]); forward: the group panel
-// P = [s_1 X A_1^T | ..] [M, rt]; backward: Pt [rt, M8], Qs [M8, rt] and
-// Qt [rt, M8].  One shared region follows, used in turn by the group panel's
-// split partials, each member's own scratch, and the dA partials.
+// bf16: the members' rank rows stacked, each padded to r8_g (rt = sum r8_g,
+// member g at row off[g]), in sub-groups of consecutive members within the
+// DMA kernels' row limits (a wider member alone): each panel sub-group (up
+// to 256 rows) is one pass over X for the forward panel and one for the
+// backward's recomputation, each dA sub-group (up to 128) one pass for dA,
+// reading each member's A in place.  Workspace: forward the panel P = [s_1 X A_1^T | ..] [M, rt];
+// backward Pt [rt, M8], Qs [M8, rt], Qt [rt, M8] and per member B^T, A^T
+// and its dB partials (kept until the group's batched transposes and sums).
+// One shared region follows, used in turn by the panels' split partials,
+// each member's own scratch, and the sub-groups' dA partials.
 struct GroupLayout {
-  int64_t rt = 0, M8 = 0, off[LORA_GROUP_MAX] = {};
-  size_t acat = 0, p = 0, pt = 0, qs = 0, qt = 0, shared = 0, total = 0;
-  // bf16 backward, per member: B^T, A^T and the dB partials, kept until the
-  // group's batched transposes and sums
+  int64_t rt = 0, M8 = 0, off[LORA_GROUP_MAX + 1] = {};
+  size_t p = 0, pt = 0, qs = 0, qt = 0, shared = 0, total = 0;
   size_t bt[LORA_GROUP_MAX] = {}, at[LORA_GROUP_MAX] = {}, partb[LORA_GROUP_MAX] = {};
-  int splits_g = 1, splits_dA = 1;
-  int64_t ksplit_g = 0, ksplit_dA = 0;
+  // panel sub-groups (at most 256 rows: panel_dma_kernel) and dA sub-groups
+  // (at most 128: splitnn_dma_kernel); s: members [g0[s], g0[s + 1])
+  int nsub = 0, sub_g0[LORA_GROUP_MAX + 1] = {};
+  int nasub = 0, asub_g0[LORA_GROUP_MAX + 1] = {};
+  int splits_p[LORA_GROUP_MAX] = {}, splits_a[LORA_GROUP_MAX] = {};
+  int64_t ksplit_p[LORA_GROUP_MAX] = {}, ksplit_a[LORA_GROUP_MAX] = {};
+  size_t part_a[LORA_GROUP_MAX] = {};  // floats from the shared region to dA sub-group s's partials
   Layout mem[LORA_GROUP_MAX];
 };
 
@@ -766,6 +773,15 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
                            mb[g].W_t != nullptr && !mb[g].W_nf4);
     if (G.mem[g].total > shared) shared = G.mem[g].total;
   }
+  G.off[n] = G.rt;
+  // (operands too wide for the panel DMA kernel: every member alone)
+  const bool stack = panel_dma_fits(256, d_in, d_in);
+  for (int g = 0; g < n; ++g) {
+    if (g == 0 || !stack || G.off[g + 1] - G.off[G.sub_g0[G.nsub - 1]] > 256) G.sub_g0[G.nsub++] = g;
+    if (g == 0 || G.off[g + 1] - G.off[G.asub_g0[G.nasub - 1]] > 128) G.asub_g0[G.nasub++] = g;
+  }
+  G.sub_g0[G.nsub] = n;
+  G.asub_g0[G.nasub] = n;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -773,10 +789,12 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
     return at;
   };
   if (eb == 2) {
-    G.acat = take(size_t(G.rt) * d_in * eb);
-    panel_split(M, d_in, G.rt, &G.splits_g, &G.ksplit_g);
-    const size_t pp = size_t(G.splits_g) * G.M8 * G.rt * 4;
-    if (pp > shared) shared = pp;
+    for (int s = 0; s < G.nsub; ++s) {
+      const int64_t rs = G.off[G.sub_g0[s + 1]] - G.off[G.sub_g0[s]];
+      panel_split(M, d_in, rs, &G.splits_p[s], &G.ksplit_p[s]);
+      const size_t pp = size_t(G.splits_p[s]) * G.M8 * rs * 4;  // the panels run one after another
+      if (pp > shared) shared = pp;
+    }
     if (!bwd) {
       G.p = take(size_t(M) * G.rt * eb);
     } else {
@@ -789,8 +807,13 @@ GroupLayout make_group_layout(bool bwd, int dtype, int64_t M, int64_t d_in, int 
         G.at[g] = take(size_t(d_in) * L.r8 * eb);
         G.partb[g] = take(size_t(L.splits_dB) * L.r8 * mb[g].d_out * 4);
       }
-      choose_split(M, G.rt, d_in, true, &G.splits_dA, &G.ksplit_dA);
-      const size_t pa = size_t(G.splits_dA) * G.rt * d_in * 4;
+      size_t pa = 0;  // every sub-group's dA partials until the batched sum
+      for (int s = 0; s < G.nasub; ++s) {
+        const int64_t rs = G.off[G.asub_g0[s + 1]] - G.off[G.asub_g0[s]];
+        choose_split(M, rs, d_in, true, &G.splits_a[s], &G.ksplit_a[s]);
+        G.part_a[s] = pa / 4;
+        pa = align256(pa + size_t(G.splits_a[s]) * rs * d_in * 4);
+      }
       if (pa > shared) shared = pa;
     }
   }
@@ -838,28 +861,29 @@ int check_group_ws(const GroupLayout& G, const void* ws, size_t ws_bytes) {
   return LORA_OK;
 }
 
-// The group panel's R rows and per-column scales.  The panel DMA kernel
-// reads each member's A in place; otherwise (wider stacks) the members' rows
-// are copied into acat (rows r..r8 of each block zeros).
-int group_rows(int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G, uint16_t* acat, ColScale* cs,
-               PanelSrc* src, hipStream_t st) {
-  cs->n = n;
-  const bool direct = n <= kPanelSrcMax && panel_dma_fits(G.rt, d_in, d_in);
-  src->n = direct ? n : 0;
-  for (int g = 0; g < n; ++g) {
-    const int64_t r8 = rup(mb[g].r, 8);
-    if (direct) {
-      src->rs[g] = mb[g].A;
-      src->beg[g] = (int)G.off[g];
-      src->rows[g] = mb[g].r;
-    } else {
-      HIPTRY(timed(K_COPY_ROWS, 0, 2.0 * (mb[g].r + r8) * d_in, st, [&] {
-        return launch_copy_rows(static_cast<const uint16_t*>(mb[g].A), d_in, mb[g].r, d_in, acat + G.off[g] * d_in,
-                                d_in, r8, st);
-      }));
+// The group's rank-r panels s_g X A_g^T, one pass over X per sub-group, each
+// member's A read in place (a wider member alone: its A is the panel's R):
+// P into out (rows of `rows`, row stride rt) and/or P^T into outt ([rt, M8]).
+int group_panel(int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X, const GroupLayout& G,
+                float* part, uint16_t* out, int64_t rows, uint16_t* outt, hipStream_t st) {
+  for (int s = 0; s < G.nsub; ++s) {
+    const int g0 = G.sub_g0[s], g1 = G.sub_g0[s + 1];
+    const int64_t o0 = G.off[g0], rs = G.off[g1] - o0;
+    ColScale cs{};
+    cs.n = g1 - g0;
+    PanelSrc src;
+    src.n = g1 - g0;
+    for (int g = g0; g < g1; ++g) {
+      cs.end[g - g0] = G.off[g + 1] - o0;
+      cs.s[g - g0] = mb[g].scale;
+      src.rs[g - g0] = mb[g].A;
+      src.beg[g - g0] = (int)(G.off[g] - o0);
+      src.rows[g - g0] = (int)mb[g].r;
     }
-    cs->end[g] = G.off[g] + r8;
-    cs->s[g] = mb[g].scale;
+    const bool multi = panel_dma_fits(rs, d_in, d_in);
+    TRY(panel_bf16(X, d_in, mb[g0].A, d_in, M, rows, d_in, multi ? rs : mb[g0].r, rs, G.splits_p[s], G.ksplit_p[s],
+                   cs, part, out ? out + o0 : nullptr, G.rt, outt ? outt + o0 * G.M8 : nullptr, G.M8, st,
+                   multi ? &src : nullptr));
   }
   return LORA_OK;
 }
@@ -920,11 +944,7 @@ int group_forward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_me
   const bool share = dtype == LORA_BF16 && M > 0;
   uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
   if (share) {
-    ColScale cs{};
-    PanelSrc src;
-    TRY(group_rows(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
-    TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                   reinterpret_cast<float*>(sh), P, G.rt, nullptr, 0, st, &src));
+    TRY(group_panel(M, d_in, n, mb, X, G, reinterpret_cast<float*>(sh), P, M, nullptr, st));
     if (group_gemm_fits(M, d_in, n, mb, G)) return group_gemm(M, d_in, n, mb, X, rope, P, G, st);
   }
   for (int g = 0; g < n; ++g) {
@@ -945,11 +965,7 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   uint16_t* Qs = reinterpret_cast<uint16_t*>(w + G.qs);
   uint16_t* Qt = reinterpret_cast<uint16_t*>(w + G.qt);
   if (share) {
-    ColScale cs{};
-    PanelSrc src;
-    TRY(group_rows(d_in, n, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
-    TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, G.M8, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                   reinterpret_cast<float*>(sh), nullptr, 0, Pt, G.M8, st, &src));
+    TRY(group_panel(M, d_in, n, mb, X, G, reinterpret_cast<float*>(sh), nullptr, G.M8, Pt, st));
   }
   // every member's B^T (r a multiple of 8) and A^T (whole-tile dX) in one launch
   TransposeBatch tb;
@@ -988,23 +1004,29 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
                       nullptr, nullptr, G.mem[g].dx_nt && !m.W_nf4 ? m.W_t : nullptr));
   }
   if (!share) return LORA_OK;
-  // dA of every member in one pass over X: Qt X -> partials [splits][rt, d_in]
+  // dA of every member of a sub-group in one pass over X: Qt rows X ->
+  // partials [splits][rows, d_in]; then every dA and dB sum in one launch
   float* part = reinterpret_cast<float*>(sh);
-  const double Md = double(M), ki = double(d_in), rr = double(G.rt);
-  GemmArgs a = blank();
-  a.a1 = Qt; a.lda1 = G.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
-  a.m_load = G.rt; a.m_store = G.rt; a.n_load = d_in; a.n_store = d_in;
-  a.k_split = G.ksplit_dA; a.c = part; a.ldc = d_in; a.part_stride = G.rt * d_in;
-  HIPTRY(gemm(G_BF16_SPLIT_NN_PARTIAL, a, G.splits_dA, st, 2 * rr * ki * Md,
-              (rr * Md + Md * ki) * 2 + 4.0 * G.splits_dA * G.rt * ki));
-  // every member's dA and (added by the members) dB sums in one launch
+  const double Md = double(M), ki = double(d_in);
   double rflop = 0, rbytes = 0;
-  for (int g = 0; g < n; ++g) {
-    const double rg = double(mb[g].r), ko = double(mb[g].d_out);
-    const int sb = G.mem[g].splits_dB;
-    HIPTRY(red.add(part + G.off[g] * d_in, G.splits_dA, mb[g].r, d_in, G.rt * d_in, false, mb[g].dA));
-    rflop += double(G.splits_dA) * rg * ki + double(sb) * rg * ko;
-    rbytes += 4.0 * (G.splits_dA + 1) * rg * ki + 4.0 * (sb + 1) * rg * ko;
+  for (int s = 0; s < G.nasub; ++s) {
+    const int g0 = G.asub_g0[s], g1 = G.asub_g0[s + 1];
+    const int64_t o0 = G.off[g0], rs = G.off[g1] - o0;
+    float* ps = part + G.part_a[s];
+    const int S = G.splits_a[s];
+    GemmArgs a = blank();
+    a.a1 = Qt + o0 * G.M8; a.lda1 = G.M8; a.b1 = X; a.ldb1 = d_in; a.K1 = M;
+    a.m_load = rs; a.m_store = rs; a.n_load = d_in; a.n_store = d_in;
+    a.k_split = G.ksplit_a[s]; a.c = ps; a.ldc = d_in; a.part_stride = rs * d_in;
+    HIPTRY(gemm(G_BF16_SPLIT_NN_PARTIAL, a, S, st, 2 * double(rs) * ki * Md,
+                (double(rs) * Md + Md * ki) * 2 + 4.0 * S * rs * ki));
+    for (int g = g0; g < g1; ++g) {
+      const double rg = double(mb[g].r), ko = double(mb[g].d_out);
+      const int sb = G.mem[g].splits_dB;
+      HIPTRY(red.add(ps + (G.off[g] - o0) * d_in, S, mb[g].r, d_in, rs * d_in, false, mb[g].dA));
+      rflop += double(S) * rg * ki + double(sb) * rg * ko;
+      rbytes += 4.0 * (S + 1) * rg * ki + 4.0 * (sb + 1) * rg * ko;
+    }
   }
   HIPTRY(timed(K_REDUCE, rflop, rbytes, st, [&] { return launch_reduce_batch(red, st); }));
   return LORA_OK;
@@ -1107,12 +1129,8 @@ int swiglu_forward(int dtype, int64_t M, int64_t d_in, const lora_group_member* 
   }
   const GroupLayout& G = S.G;
   // the pair's rank-r panels in one pass over X: P = [sg X Ag^T | su X Au^T]
-  ColScale cs{};
-  PanelSrc src;
-  TRY(group_rows(d_in, 2, mb, G, reinterpret_cast<uint16_t*>(w + G.acat), &cs, &src, st));
   uint16_t* P = reinterpret_cast<uint16_t*>(w + G.p);
-  TRY(panel_bf16(X, d_in, w + G.acat, d_in, M, M, d_in, G.rt, G.rt, G.splits_g, G.ksplit_g, cs,
-                 reinterpret_cast<float*>(w + G.shared), P, G.rt, nullptr, 0, st, &src));
+  TRY(group_panel(M, d_in, 2, mb, X, G, reinterpret_cast<float*>(w + G.shared), P, M, nullptr, st));
   const void* Wp[2];
   const void* Bp[2];
   const size_t woff[2] = {S.wg, S.wu}, boff[2] = {S.bg, S.bu};

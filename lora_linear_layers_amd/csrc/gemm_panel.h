@@ -7,8 +7,8 @@
 // The work is a stream of X: 2 r FLOP per element read, far below the
 // machine balance, so the kernel is built for HBM bandwidth (on MI355X a
 // plain streaming read reaches about 6.1 TB/s, from L2 about 21 TB/s through
-// the LDS DMA path).  A BM-row tile covers every panel column (BN = 64 or 128
-// >= r), so X is read exactly once; global tiles go straight to LDS
+// the LDS DMA path).  A BM-row tile covers every panel column (BN = 64, 128
+// or 256 >= r), so X is read exactly once; global tiles go straight to LDS
 // (buffer_load_dwordx4 ... lds, 8 rows x 128 bytes per instruction) through a
 // ring of NS stages issued NS - 1 stages ahead, 100+ KB in flight per CU.
 // The contraction is split over gridDim / tiles_m blocks per row tile; split

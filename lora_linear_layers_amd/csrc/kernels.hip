@@ -52,8 +52,8 @@ hipError_t run_whole(GemmArgs a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// rank-r panel split partials (K1 only, at most 128 panel columns): one
-// 256-row tile per block and split, every column in the tile
+// rank-r panel split partials (K1 only, at most 256 panel columns): one
+// 128-row tile per block and split, every column in the tile
 hipError_t run_panel(GemmArgs a, int splits, hipStream_t st) {
   constexpr int BM = PANEL_BM;
   a.tiles_m = (int)((a.m_store + BM - 1) / BM);
@@ -61,8 +61,10 @@ hipError_t run_panel(GemmArgs a, int splits, hipStream_t st) {
   if (nblocks <= 0) return hipSuccess;
   if (a.n_store <= 64)
     hipLaunchKernelGGL((panel_dma_kernel<BM, 64>), dim3((unsigned)nblocks), dim3(pdma::NT), 0, st, a);
-  else
+  else if (a.n_store <= 128)
     hipLaunchKernelGGL((panel_dma_kernel<BM, 128>), dim3((unsigned)nblocks), dim3(pdma::NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((panel_dma_kernel<BM, 256>), dim3((unsigned)nblocks), dim3(pdma::NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -101,7 +103,7 @@ bool whole_ld_fits(int64_t ld) { return ld * 2 * (w4::BM + w4::BK) < (int64_t)w4
 
 bool panel_dma_fits(int64_t n_store, int64_t lda, int64_t ldb) {
   const int64_t ld = std::max(lda, ldb);
-  return n_store <= 128 && ld * 2 * 256 < (int64_t)w4::BIG;
+  return n_store <= 256 && ld * 2 * 256 < (int64_t)w4::BIG;
 }
 
 TileShape gemm_tile(GemmKind k) {
@@ -777,24 +779,6 @@ hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_strid
   const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((n + 63) / 64));
   hipLaunchKernelGGL(panel_reduce_kernel, grid, dim3(256), 0, st, part, splits, part_stride, ldp, rows, n, scale, out,
                      ldo, outt, ldot);
-  return hipGetLastError();
-}
-
-__global__ void copy_rows_kernel(const uint16_t* __restrict__ src, int64_t lds, int64_t rows, int64_t cols,
-                                 uint16_t* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
-  const int64_t n = rows_pad * cols;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t i = e / cols, j = e - i * cols;
-    dst[i * ldd + j] = i < rows ? src[i * lds + j] : (uint16_t)0;
-  }
-}
-
-hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, int64_t rows, int64_t cols, uint16_t* dst,
-                            int64_t ldd, int64_t rows_pad, hipStream_t st) {
-  const int64_t n = rows_pad * cols;
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(copy_rows_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, src, lds, rows, cols, dst, ldd,
-                     rows_pad);
   return hipGetLastError();
 }
 

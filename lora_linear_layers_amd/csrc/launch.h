@@ -147,11 +147,6 @@ hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_strid
                                int64_t n, const ColScale& scale, uint16_t* out, int64_t ldo, uint16_t* outt,
                                int64_t ldot, hipStream_t st);
 
-// dst rows [0, rows_pad) of width cols (row stride ldd) = src rows [0, rows)
-// (row stride lds) followed by zero rows; bf16.
-hipError_t launch_copy_rows(const uint16_t* src, int64_t lds, int64_t rows, int64_t cols, uint16_t* dst,
-                            int64_t ldd, int64_t rows_pad, hipStream_t st);
-
 // out [M, N] bf16 (row stride ldo) = fixed-order sum of split partials
 // (part[z * part_stride + m * N + n]); with pos != NULL also the RoPE rotation
 // of the pairs (n, n + 64) of each 128-wide head (N a multiple of 128).

@@ -151,8 +151,8 @@ def test_group_workspace_sizes(lib):
     m = _members(3)
     fwd, bwd = f(0, 1, 4096, 1024, 3, m), f(1, 1, 4096, 1024, 3, m)
     rt = 8 + 16 + 16  # ranks 8, 9, 10 padded to multiples of 8
-    assert fwd >= rt * 1024 * 2 + 4096 * rt * 2  # Acat and the group panel
-    assert bwd >= rt * 1024 * 2 + 3 * 4096 * rt * 2  # Acat, Pt, Qs, Qt
+    assert fwd >= 4096 * rt * 2  # the group panel
+    assert bwd >= 3 * 4096 * rt * 2  # Pt, Qs, Qt
     # fp32 groups run member by member: the largest member's own workspace
     single = max(lib.lora_workspace_bytes(_lib.OP_BWD, 0, 4096, 1024, 64 * (g + 1), 8 + g) for g in range(3))
     assert f(1, 0, 4096, 1024, 3, m) == single

@@ -37,6 +37,9 @@ GROUPS = [
     (2100, 1024, [(4096, 64, True), (1024, 64, True), (1024, 64, False)]),
     (4096, 1024, [(4096, 24, False), (1024, 100, True), (2048, 1, False), (512, 8, False)]),
     (129, 520, [(392, 16, False)]),
+    # a member wider than 128 rank rows between two narrow ones: each alone
+    # in its pass over X (the wide one on the generic panel and dA kernels)
+    (600, 512, [(256, 8, False), (512, 200, True), (256, 16, False)]),
 ]
 
 
