@@ -90,7 +90,9 @@ KIND_OF = {
     "gemm_kernel<unsigned short, 128, 128, 4, 1, true, 0, 1>": "gemm_nf4_128x128_nn_store",
     "gemm_kernel<unsigned short, 64, 256, 1, 4, true, 4, 0>": "split_bf16_nn_partial",
     "reduce_splits_kernel": "reduce_splits",
-    "transpose_pad_kernel": "transpose_pad",
+    "transpose_pad_kernel": "transpose_ab",
+    "transpose_batch_kernel": "transpose_ab",
+    "reduce_batch_kernel": "reduce_splits",
     "rope_inverse_kernel": "rope_inverse",
     "transpose_tile_kernel": "transpose_w",
     "split_finish_kernel": "split_finish",

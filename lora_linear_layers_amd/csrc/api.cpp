@@ -282,7 +282,7 @@ const char* kind_name(int k) {
       "dropout_dx_f32_64x128",      "gemm_bf16_256x256_nt_group", "pad_cols",
       "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
-      "nf4_dequant",                "panel_reduce",               "transpose_pad",
+      "nf4_dequant",                "panel_reduce",               "transpose_ab",
       "split_finish",               "swiglu_elementwise",
       "dropout_mask_copy",          "transpose_w",                "skinny_fwd"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");

@@ -109,6 +109,44 @@ def test_group_gemm_parity(lib, case):
         assert err <= TOL["bf16"], (g, err)
 
 
+def test_group_eight_members(lib):
+    # the largest group: 8 members at a size where every dX runs on whole
+    # tiles, so 16 batched transposes (B^T and A^T of each), 16 batched sums
+    # (dA and dB of each), 8 entries of the group GEMM's member table and one
+    # 64-row panel pass; RoPE on every other member.  Y and dX on sampled
+    # rows, dA and dB in full.
+    M, d_in, seq = 4096, 4096, 4096
+    X = draw(1200, (M, d_in), "normal", 1.0, "bf16")
+    pos = torch.from_numpy(gen.positions_mod(M, seq)).cuda()
+    cos, sin = lib.rope_cache(seq, 128, 500000.0)
+    members, dYs = [], []
+    for g in range(8):
+        W, A, B, dY = _member_inputs(1210 + 10 * g, M, d_in, 256, 8, "bf16")
+        members.append(dict(W=W, A=A, B=B, scale=2.0 + g, rope=g % 2 == 0))
+        dYs.append(dY)
+    (Ys, grads), kinds = _group_kinds(lambda: (lib.lora_group_fwd(X, members, pos, cos, sin),
+                                               lib.lora_group_bwd(X, members, dYs, pos, cos, sin)))
+    assert {"gemm_bf16_256x256_nt_group", "gemm_bf16_256x256_nt_store", "reduce_splits", "transpose_ab"} <= kinds
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([[0, M - 1], rng.choice(np.arange(1, M - 1), 126, replace=False)]))
+    tr = torch.from_numpy(rows).cuda()
+    p = pos.cpu().numpy()
+    for g, m in enumerate(members):
+        W, A, B, s = m["W"], m["A"], m["B"], m["scale"]
+        dX, dA, dB = grads[g]
+        if m["rope"]:
+            Yr = O.qk_rope_forward(X[tr], W, A, B, s, p[rows])
+            G = O.rope_rotate(dYs[g], p, 128, 500000.0, inverse=True)
+        else:
+            Yr = O.lora_forward(X[tr], W, A, B, s)
+            G = cpu64(dYs[g])
+        dXr = O.lora_grad_x(W, A, B, s, G[rows])
+        dAr, dBr = O.lora_grad_ab(X, A, B, s, G)
+        errs = dict(Y=rel(Ys[g][tr], Yr), dX=rel(dX[tr], dXr), dA=rel(dA, dAr), dB=rel(dB, dBr))
+        print(g, errs)
+        assert all(e <= TOL["bf16"] for e in errs.values()), (g, errs)
+
+
 def test_group_gemm_integer_exact(lib):
     # small integers: every product and sum exact on both sides, so each
     # member's Y from the one-launch group GEMM equals the oracle exactly
