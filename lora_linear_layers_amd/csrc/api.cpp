@@ -1035,7 +1035,7 @@ int group_backward(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
 // ---------------------------------------------------------------------------
 // SwiGLU on a gate / up pair
 // ---------------------------------------------------------------------------
-// Workspace: the pair's group layout first (Acat, panels, shared scratch),
+// Workspace: the pair's group layout first (panels, shared scratch),
 // then forward: the dequantised NF4 weights and padded B's of the fused GEMM,
 // or G and U for the elementwise path; backward: dG, dU and the up's input
 // gradient before it is added to dX.
