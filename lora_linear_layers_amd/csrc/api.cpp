@@ -895,12 +895,14 @@ int group_panel(int64_t M, int64_t d_in, int n, const lora_group_member* mb, con
 // share the launch's waves of tiles.
 bool group_gemm_fits(int64_t M, int64_t d_in, int n, const lora_group_member* mb, const GroupLayout& G) {
   if (M <= 0 || M % 256 || d_in % 64 || n > kGroupGemmMax) return false;
-  int64_t ld = std::max(d_in, G.rt);
+  int64_t ld = std::max(d_in, G.rt), cols = 0;
   for (int g = 0; g < n; ++g) {
     if (mb[g].W_nf4 || mb[g].d_out % 256 || mb[g].r % 8) return false;
     ld = std::max(ld, mb[g].r);
+    cols += mb[g].d_out;
   }
-  return whole_ld_fits(ld);
+  // the member table holds tile numbers as int
+  return whole_ld_fits(ld) && (M / 256) * (cols / 256) <= INT32_MAX;
 }
 
 int group_gemm(int64_t M, int64_t d_in, int n, const lora_group_member* mb, const void* X, const Rope* rope,

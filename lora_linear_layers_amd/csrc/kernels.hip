@@ -43,9 +43,11 @@ bool whole_tiles(const GemmArgs& a, int splits) {
 template <bool B_NN, int EPI>
 hipError_t run_whole(GemmArgs a, hipStream_t st) {
   static_assert(!B_NN || EPI == EPI_STORE, "the NN kernel stores");
-  a.tiles_m = (int)(a.m_store / w4::BM);
-  const int64_t nblocks = (int64_t)a.tiles_m * (a.n_store / w4::BN);
+  const int64_t tiles_m = a.m_store / w4::BM;
+  const int64_t nblocks = tiles_m * (a.n_store / w4::BN);
   if (nblocks <= 0) return hipSuccess;
+  if (nblocks > INT32_MAX) return hipErrorInvalidValue;  // one block per tile, a 1D grid
+  a.tiles_m = (int)tiles_m;
   if constexpr (B_NN)
     hipLaunchKernelGGL((gemm_w4_nn_kernel<2>), dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
   else
