@@ -88,6 +88,17 @@ def test_integer_brute_force_exact(M, k, d, r):
     assert dB.tolist() == [[float(v) for v in row] for row in bB]
 
 
+def test_panel_brute_force_exact():
+    # P[t][q] = sum_j X[t][j] A[q][j]: the rank-r projection A x of each token,
+    # summed exactly over Fractions on small integers, and a hand value.
+    X, A = _small_ints((4, 7)), _small_ints((3, 7))
+    ref = [[float(sum(Fraction(A[q][j]) * Fraction(X[t][j]) for j in range(7))) for q in range(3)] for t in range(4)]
+    assert O.lora_panel(X, A).tolist() == ref
+    # x = [1, 2, 3], A = [[1, 0, -1], [2, 1, 0]]: A x = [1 - 3, 2 + 2] = [-2, 4]
+    P = O.lora_panel(np.array([[1.0, 2.0, 3.0]]), np.array([[1.0, 0.0, -1.0], [2.0, 1.0, 0.0]]))
+    assert P.tolist() == [[-2.0, 4.0]]
+
+
 def test_brute_force_float_shapes():
     X, W, A, B = _rand(2, 6), _rand(5, 6), _rand(3, 6), _rand(5, 3)
     ref = np.array([[float(v) for v in row] for row in _brute_forward(X.tolist(), W.tolist(), A.tolist(), B.tolist(), 0.25)])
@@ -223,6 +234,33 @@ def test_rope_relative_position():
         lhs = np.sum(O.rope_rotate(q, [m], 128, 5e5) * O.rope_rotate(k, [n], 128, 5e5))
         rhs = np.sum(q * O.rope_rotate(k, [n - m], 128, 5e5))
         assert abs(lhs - rhs) < 1e-10
+
+
+def test_qk_rope_projection_hand_worked():
+    # head_dim 4, position 1, theta = 4 / pi^2: pair (0, 2) turns by 1 rad and
+    # pair (1, 3) by theta^(-1/2) = pi / 2.  x = [1, 2, 3, 4], W = I,
+    # A = [1, 0, 0, 0] (r = 1, A x = 1), B = e_3, s = 2: before the rotation
+    # z = x + s B (A x) = [1, 2, 3, 6].  Rotating (z_i, z_{i+2}) by +a gives
+    # (z_i cos a - z_{i+2} sin a, z_{i+2} cos a + z_i sin a):
+    #   pair 0: (cos 1 - 3 sin 1, 3 cos 1 + sin 1);  pair 1: (-6, 2).
+    theta = 4.0 / math.pi ** 2
+    X = np.array([[1.0, 2.0, 3.0, 4.0]])
+    W = np.eye(4)
+    A = np.array([[1.0, 0.0, 0.0, 0.0]])
+    B = np.array([[0.0], [0.0], [0.0], [1.0]])
+    c, sn = math.cos(1.0), math.sin(1.0)
+    Y = O.qk_rope_forward(X, W, A, B, 2.0, [1], head_dim=4, theta=theta)
+    assert np.abs(Y - np.array([[c - 3 * sn, -6.0, 3 * c + sn, 2.0]])).max() < 1e-14
+    # Backward, dY = [1, 1, 0, 0]: G rotates each pair by -a,
+    # (g_i cos a + g_{i+2} sin a, g_{i+2} cos a - g_i sin a):
+    #   G = [cos 1, 0, -sin 1, -1];  G B = G[3] = -1;  A x = 1
+    #   dX = G W + s (G B) A = [cos 1 - 2, 0, -sin 1, -1]
+    #   dA = s (G B)^T x = -2 [1, 2, 3, 4];  dB = s G^T (A x) = 2 G^T
+    dX, dA, dB = O.qk_rope_backward(X, W, A, B, 2.0, [1], np.array([[1.0, 1.0, 0.0, 0.0]]), head_dim=4,
+                                    theta=theta)
+    assert np.abs(dX - np.array([[c - 2.0, 0.0, -sn, -1.0]])).max() < 1e-14
+    assert np.abs(dA - np.array([[-2.0, -4.0, -6.0, -8.0]])).max() < 1e-14
+    assert np.abs(dB - np.array([[2 * c], [0.0], [-2 * sn], [-2.0]])).max() < 1e-14
 
 
 def test_rope_backward_matches_finite_differences():
