@@ -57,6 +57,8 @@ def parse():
                     help="do not keep W^T of the frozen weights (the backward then transposes W per call)")
     ap.add_argument("--no-group", action="store_true",
                     help="run projections that share X one by one instead of as one group")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only the chosen workload (not every other one as well)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for the CPU sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for HBM counters)")
@@ -509,6 +511,23 @@ def _rocm_version():
         return None
 
 
+def _host_cpu():
+    """The host's CPU model and how many logical CPUs this process may use."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
 def cpu_baseline(cfg, work, target_s):
     """The float64 oracle, untuned, on the first S tokens of the same workload."""
     import numpy as np
@@ -564,9 +583,133 @@ def cpu_baseline(cfg, work, target_s):
     what = f"the first {S} of {cfg.M} tokens" if S < cfg.M else f"all {cfg.M} tokens"
     what = f"{passes} passes of {what}" if passes > 1 else what
     return {"value": S * passes / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "host": _host_cpu(),
             "sample": f"{what} through all {len(cfg.projections)} projections, forward+backward, "
                       f"float64 numpy ({t:.1f} s; {flop / t / 1e9:.1f} GFLOP/s useful)",
             "seconds": round(t, 2), "tflops_equiv": flop / t / 1e12}
+
+
+def timed_run(work, cfg, steps, warmup, detail=False):
+    """W untimed steps, then K timed steps of the whole path.  HIP events (on
+    the library's launch stream) bracket only the launches of the kind that
+    dominates the step (found in an untimed pre-pass with every launch
+    bracketed), so the other launches run without events.  Returns the
+    seconds per step and the roofline entry of that kind; with detail, also a
+    per-kind breakdown from a few fully bracketed steps after the timed
+    region (their events slow them a little; shares are of their own time)."""
+    import torch
+
+    from lora_linear_layers_amd import _lib
+
+    for _ in range(warmup):
+        work.step()
+    torch.cuda.synchronize()
+    launches_per_step = 16 * len(cfg.projections)
+    _lib.profile_only(None)
+    _lib.profile_begin(launches_per_step + 64)
+    work.step()
+    torch.cuda.synchronize()
+    _lib.profile_end()
+    dname = max(_lib.profile_report().items(), key=lambda kv: kv[1][0])[0]
+
+    _lib.profile_only(dname)
+    _lib.profile_begin(launches_per_step * max(steps, 1) + 64)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        work.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    _lib.profile_end()
+    _lib.profile_only(None)
+    dms, dn, dfl, dby = _lib.profile_report()[dname]
+    sec = (t1 - t0) / max(steps, 1)
+
+    kpeak = PEAK["f32" if "f32" in dname else "bf16"]
+    achieved = dfl / (dms * 1e-3) / 1e12
+    # below the ridge point (peak FLOP/s over HBM bytes/s) the kind is HBM-bound
+    bound = "mfma" if dfl / max(dby, 1.0) >= kpeak * 1e12 / (HBM_PEAK * 1e9) else "hbm"
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            ent = tr.get("kernels", {}).get(dname)
+            if ent and tr.get("kernel_hash") == kernel_hash() and tr.get("config") == cfg.cfg_id:
+                traffic = ent["bytes_per_launch"]
+        except (ValueError, KeyError):
+            traffic = None
+    roofline = {"bound": bound, "kernel": dname, "achieved": round(achieved, 1), "peak": kpeak,
+                "unit": "TFLOP/s", "frac": round(achieved / kpeak, 4), "traffic": traffic,
+                "avg_launch_us": round(1e3 * dms / dn, 1), "flop_per_launch": dfl / dn,
+                "algorithmic_bytes_per_launch": dby / dn,
+                "achieved_gbps": round(dby / (dms * 1e-3) / 1e9, 1)}
+    out = {"sec": sec, "roofline": roofline, "kernels": None, "nb": 0}
+    if detail:
+        nb = max(1, min(steps, 3))
+        _lib.profile_begin(launches_per_step * nb + 64)
+        torch.cuda.synchronize()
+        tb0 = time.perf_counter()
+        for _ in range(nb):
+            work.step()
+        torch.cuda.synchronize()
+        tb1 = time.perf_counter()
+        _lib.profile_end()
+        kernels = {}
+        for name, (ms, n, fl, by) in sorted(_lib.profile_report().items(), key=lambda kv: -kv[1][0]):
+            kernels[name] = {"launches": n, "avg_us": round(1e3 * ms / n, 2),
+                             "share": round(ms / ((tb1 - tb0) * 1e3), 4),
+                             "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
+                             "gbps": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+        out["kernels"], out["nb"] = kernels, nb
+    return out
+
+
+def other_configs(args, dev, skip):
+    """Every other workload at the same steps and warmup: TFLOP/s, tokens/s
+    and the dominant kernel's roofline entry; the fp32 single-layer workload
+    (launch-latency bound) also as forward and backward microseconds."""
+    import torch
+
+    from synth import CONFIGS
+
+    out = {}
+    for cid, cfg in CONFIGS.items():
+        if cid == skip:
+            continue
+        work = Workload(cfg, device=dev)
+        res = timed_run(work, cfg, args.steps, args.warmup)
+        sec = res["sec"]
+        flop = cfg.useful_flop()
+        ent = {"workload": cfg.name, "tflops": round(flop / sec / 1e12, 3),
+               "tokens_per_s": round(cfg.M / sec, 1), "ms_per_step": round(sec * 1e3, 4),
+               "pct_bf16_peak": round(100.0 * flop / sec / 1e12 / PEAK["bf16"], 2),
+               "dtype": "f32" if cfg.dtype == "f32" else ("nf4w-bf16" if cfg.nf4 else "bf16"),
+               "x_groups": [[it["p"].name for it in grp] for grp in work.groups],
+               "roofline": res["roofline"]}
+        if cfg.dtype == "f32":
+            reps = max(args.steps, 20)
+            for kind, fn in (("fwd_us", work.fwd), ("bwd_us", work.bwd)):
+                ent[kind] = {k: round(v * 1e3, 2) for k, v in _time_ms(lambda: fn(0), reps).items()}
+        out[f"c{cid}"] = ent
+        del work
+        torch.cuda.empty_cache()
+    return out
+
+
+def without_wt(args, dev, cfg):
+    """The workload with the backward transposing each frozen W per call
+    instead of reading a caller-held W^T, and the bytes that W^T keeps
+    resident."""
+    import torch
+
+    work = Workload(cfg, device=dev, keep_wt=False)
+    res = timed_run(work, cfg, args.steps, args.warmup)
+    sec = res["sec"]
+    del work
+    torch.cuda.empty_cache()
+    wt_bytes = sum(2 * p.d_in * p.d_out for p in cfg.projections)
+    return {"tflops": round(cfg.useful_flop() / sec / 1e12, 2), "ms_per_step": round(sec * 1e3, 3),
+            "w_t_resident_bytes": wt_bytes}
 
 
 def main():
@@ -605,79 +748,17 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    for _ in range(args.warmup):
-        work.step()
-    torch.cuda.synchronize()
-
-    launches_per_step = 16 * len(cfg.projections)
-    # untimed pre-pass with every launch bracketed by events: which kernel
-    # kind dominates the step
-    _lib.profile_only(None)
-    _lib.profile_begin(launches_per_step + 64)
-    work.step()
-    torch.cuda.synchronize()
-    _lib.profile_end()
-    dname = max(_lib.profile_report().items(), key=lambda kv: kv[1][0])[0]
-
-    # timed region: HIP events (on the library's launch stream) bracket only
-    # the dominant kind's launches, the others run unbracketed
-    _lib.profile_only(dname)
-    _lib.profile_begin(launches_per_step * max(args.steps, 1) + 64)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        work.step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    _lib.profile_end()
-    _lib.profile_only(None)
-    dms, dn, dfl, dby = _lib.profile_report()[dname]
-
-    # per-kind breakdown from a separate, fully bracketed pass after the
-    # timed region (its events slow it a little; shares are of its own time)
-    nb = max(1, min(args.steps, 3))
-    _lib.profile_begin(launches_per_step * nb + 64)
-    torch.cuda.synchronize()
-    tb0 = time.perf_counter()
-    for _ in range(nb):
-        work.step()
-    torch.cuda.synchronize()
-    tb1 = time.perf_counter()
-    _lib.profile_end()
-    rep = _lib.profile_report()
-
-    sec = (t1 - t0) / max(args.steps, 1)
+    res = timed_run(work, cfg, args.steps, args.warmup, detail=True)
+    sec, roofline, kernels, nb = res["sec"], res["roofline"], res["kernels"], res["nb"]
     flop = cfg.useful_flop()
     tflops = flop / sec / 1e12
     tokens = cfg.M / sec
-    peak = PEAK["f32" if cfg.dtype == "f32" else "bf16"]
-
-    kernels = {}
-    for name, (ms, n, fl, by) in sorted(rep.items(), key=lambda kv: -kv[1][0]):
-        kernels[name] = {"launches": n, "avg_us": round(1e3 * ms / n, 2), "share": round(ms / ((tb1 - tb0) * 1e3), 4),
-                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2) if ms > 0 else None,
-                         "gbps": round(by / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
-    kpeak = PEAK["f32" if "f32" in dname else "bf16"]
-    achieved = dfl / (dms * 1e-3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        try:
-            tr = json.load(open(TRAFFIC_FILE))
-            ent = tr.get("kernels", {}).get(dname)
-            if ent and tr.get("kernel_hash") == kernel_hash() and tr.get("config") == cfg.cfg_id:
-                traffic = ent["bytes_per_launch"]
-        except (ValueError, KeyError):
-            traffic = None
-    roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": kpeak,
-                "unit": "TFLOP/s", "frac": round(achieved / kpeak, 4), "traffic": traffic,
-                "avg_launch_us": round(1e3 * dms / dn, 1), "flop_per_launch": dfl / dn,
-                "algorithmic_bytes_per_launch": dby / dn}
-    if kpeak == PEAK["bf16"]:
+    if roofline["peak"] == PEAK["bf16"]:
         # the dense bf16 rate this chip sustains under its own power limit
         # (MFMA-only probe), as a second reference next to the published peak
         mr = _lib.mfma_rate(device=dev)
         roofline["peak_measured"] = round(mr, 1)
-        roofline["frac_of_measured"] = round(achieved / mr, 4)
+        roofline["frac_of_measured"] = round(roofline["achieved"] / mr, 4)
     calls = per_call_times(work, args.call_reps) if args.call_reps > 0 else None
 
     out = {
@@ -714,6 +795,10 @@ def main():
         out["small_token"] = small_token_sweep(dev)
     if args.call_reps > 0:
         out["next_rows"] = next_rows(work, args.call_reps)
+    if not args.no_configs:
+        if cfg.dtype == "bf16" and not cfg.nf4 and not args.no_wt:
+            out["config"]["without_w_t"] = without_wt(args, dev, cfg)
+        out["configs"] = other_configs(args, dev, cfg.cfg_id)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, work, args.cpu_seconds)
     print(json.dumps(out), flush=True)

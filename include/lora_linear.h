@@ -132,8 +132,12 @@ int lora_rope_cache(int64_t max_pos, int head_dim, double theta, float* cos_cach
  * multiple of it), element i pairs with i + 64 and rotates by the angle whose
  * cos/sin sit in row positions[t] of the caches (rotate-half pairing):
  *     y_i = z_i cos - z_{i+64} sin,   y_{i+64} = z_{i+64} cos + z_i sin,
- * where z is the fused LoRA output.  positions: device int32 [M], each in
- * [0, max_pos) (the caller guarantees it; it is not checked on the device).
+ * where z is the fused LoRA output.  positions: device int32 [M], each
+ * meant to lie in [0, max_pos).  The host cannot read them before the launch;
+ * the kernels check each one against max_pos and read no cache row for a
+ * position outside that range: such a row of y comes out as zeros (and in
+ * the backward its gradient is taken as zero), so a bad position never reads
+ * outside the caches.
  */
 int lora_qk_rope_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
                      const void* X, const void* W, const void* A, const void* B, int head_dim,

@@ -380,6 +380,7 @@ struct Rope {
   const int32_t* pos;
   const float* cosc;
   const float* sinc;
+  int64_t max_pos;  // rows of the cache: a position outside [0, max_pos) gives zeros
 };
 
 // W [n] bf16 from NF4 codes with the load stage's own routine (one pass).
@@ -413,7 +414,7 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     sa.A = static_cast<const uint16_t*>(A); sa.B = static_cast<const uint16_t*>(B);
     sa.Y = static_cast<uint16_t*>(Y);
     sa.M = (int)M; sa.N = (int)d_out; sa.K = (int)d_in; sa.r = (int)r; sa.s = scale;
-    if (rope) { sa.pos = rope->pos; sa.cosc = rope->cosc; sa.sinc = rope->sinc; }
+    if (rope) { sa.pos = rope->pos; sa.cosc = rope->cosc; sa.sinc = rope->sinc; sa.max_pos = rope->max_pos; }
     const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
     HIPTRY(timed(K_SKINNY, 2 * Md * ko * ki + 2 * Md * rr * (ki + ko),
                  (ko * ki + Md * ki + rr * ki + ko * rr + Md * ko) * 2 + (rope ? Md * 64 * 8 : 0), st,
@@ -460,7 +461,7 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
     k = big ? G_NF4_BIG_NT_STORE : G_NF4_MED_NT_STORE;
   } else if (rope) {
-    a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc;
+    a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc; a.max_pos = rope->max_pos;
     k = f32 ? G_F32_NT_ROPE : (big ? G_BF16_BIG_NT_ROPE : G_BF16_MED_NT_ROPE);
   } else {
     k = f32 ? G_F32_NT_STORE : (big ? G_BF16_BIG_NT_STORE : G_BF16_MED_NT_STORE);
@@ -478,7 +479,7 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
     HIPTRY(timed(K_FINISH, double(S) * Md * ko, 4.0 * S * Md * ko + Md * ko * e, st, [&] {
       return launch_split_finish(part, S, M * d_out, M, d_out, static_cast<uint16_t*>(Y), d_out,
                                  rope ? rope->pos : nullptr, rope ? rope->cosc : nullptr,
-                                 rope ? rope->sinc : nullptr, st);
+                                 rope ? rope->sinc : nullptr, rope ? rope->max_pos : 0, st);
     }));
     return LORA_OK;
   }
@@ -545,7 +546,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const void* G = dY;
   if (rope) {
     HIPTRY(timed(K_ROPE_INV, 3.0 * Md * ko, 2 * Md * ko * e + Md * 64 * 8, st, [&] {
-      return launch_rope_inverse(eb, dY, w + L.g, M, d_out, rope->pos, rope->cosc, rope->sinc, st);
+      return launch_rope_inverse(eb, dY, w + L.g, M, d_out, rope->pos, rope->cosc, rope->sinc, rope->max_pos, st);
     }));
     G = w + L.g;
   }
@@ -657,7 +658,7 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
                   bytes - Md * ki * e + 4.0 * S * Md * ki));
       HIPTRY(timed(K_FINISH, double(S) * Md * ki, 4.0 * S * Md * ki + Md * ki * e, st, [&] {
         return launch_split_finish(sp, S, M * d_in, M, d_in, static_cast<uint16_t*>(dX), d_in, nullptr, nullptr,
-                                   nullptr, st);
+                                   nullptr, 0, st);
       }));
     } else {
       HIPTRY(gemm(k, a, 1, st, flop, bytes));
@@ -910,7 +911,7 @@ int group_gemm(int64_t M, int64_t d_in, int n, const lora_group_member* mb, cons
   GemmArgs a = blank();
   a.a1 = X; a.lda1 = d_in; a.ldb1 = d_in; a.K1 = d_in; a.lda2 = G.rt;
   a.m_load = M; a.m_store = M;
-  if (rope) { a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc; }
+  if (rope) { a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc; a.max_pos = rope->max_pos; }
   a.n_mem = n;
   const int64_t tiles_m = M / 256;
   int64_t cols = 0, ldb2 = 0;
@@ -1266,7 +1267,7 @@ int lora_qk_rope_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
   const Layout L = make_layout(LORA_OP_ROPE_FWD, dtype, M, d_in, d_out, r);
   TRY(check_ws(L, ws, ws_bytes));
   TRY(check_device());
-  const Rope rp{positions, cos_cache, sin_cache};
+  const Rope rp{positions, cos_cache, sin_cache, max_pos};
   return forward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, &rp, Y, ws, L,
                       static_cast<hipStream_t>(stream));
 }
@@ -1284,7 +1285,7 @@ int lora_qk_rope_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
   const Layout L = make_layout(LORA_OP_ROPE_BWD, dtype, M, d_in, d_out, r);
   TRY(check_ws(L, ws, ws_bytes));
   TRY(check_device());
-  const Rope rp{positions, cos_cache, sin_cache};
+  const Rope rp{positions, cos_cache, sin_cache, max_pos};
   return backward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, &rp, dY, dX, dA, dB, ws, L,
                        static_cast<hipStream_t>(stream));
 }
@@ -1350,7 +1351,7 @@ int lora_group_fwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   const GroupLayout G = make_group_layout(false, dtype, M, d_in, n, members);
   TRY(check_group_ws(G, ws, ws_bytes));
   TRY(check_device());
-  const Rope rp{positions, cos_cache, sin_cache};
+  const Rope rp{positions, cos_cache, sin_cache, max_pos};
   return group_forward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
 }
 
@@ -1362,7 +1363,7 @@ int lora_group_bwd(int dtype, int64_t M, int64_t d_in, int n, const lora_group_m
   const GroupLayout G = make_group_layout(true, dtype, M, d_in, n, members);
   TRY(check_group_ws(G, ws, ws_bytes));
   TRY(check_device());
-  const Rope rp{positions, cos_cache, sin_cache};
+  const Rope rp{positions, cos_cache, sin_cache, max_pos};
   return group_backward(dtype, M, d_in, n, members, X, &rp, table16, ws, G, static_cast<hipStream_t>(stream));
 }
 

@@ -63,6 +63,11 @@ enum Epi : int {
 
 enum BLoad : int { BL_PLAIN = 0, BL_NF4 = 1 };
 
+// A RoPE position outside [0, max_pos) names no row of the cos / sin cache:
+// such a row reads no cache memory and its cos and sin are taken as zero (its
+// outputs come out as zeros).
+__device__ __forceinline__ bool rope_pos_ok(int32_t q, int64_t max_pos) { return q >= 0 && q < max_pos; }
+
 constexpr int kPanelSrcMax = 8;  // row sources of a panel's Bop (a group's members)
 constexpr int kGroupGemmMax = 8;  // members of one group GEMM launch
 
@@ -86,6 +91,7 @@ struct GemmArgs {
   const int32_t* pos;       // EPI_ROPE
   const float* cosc;
   const float* sinc;
+  int64_t max_pos;          // rows of the cos / sin cache
   const uint8_t* codes;     // BL_NF4: packed codes of W [n_load rows? see loader], bytes per row
   const float* absmax;
   int64_t codes_ld;         // bytes per W row (= d_in / 2)
@@ -655,13 +661,15 @@ gemm_kernel(const GemmArgs p) {
       for (int v = 0; v < 4; ++v) {
         const int64_t row = rbase + i * 16 + v;
         if (row >= p.m_store) continue;
-        const int64_t prow = (int64_t)p.pos[row] * 64;
+        const int32_t q = p.pos[row];
+        const bool ok = rope_pos_ok(q, p.max_pos);
+        const int64_t prow = ok ? (int64_t)q * 64 : 0;
 #pragma unroll
         for (int j = 0; j < FN / 2; ++j) {
           const int f = j * 16 + l16;
           const int64_t col = cbase + j * 16;
           if (col >= p.n_store) continue;
-          const float cs = p.cosc[prow + f], sn = p.sinc[prow + f];
+          const float cs = ok ? p.cosc[prow + f] : 0.f, sn = ok ? p.sinc[prow + f] : 0.f;
           const float z1 = acc[i][j][v] * p.alpha, z2 = acc[i][j + FN / 2][v] * p.alpha;
           store_out<T>(p.c, row * p.ldc + col, z1 * cs - z2 * sn);
           store_out<T>(p.c, row * p.ldc + col + 64, z2 * cs + z1 * sn);

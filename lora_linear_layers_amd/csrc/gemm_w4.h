@@ -94,8 +94,9 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
       for (int k = 0; k < 16; ++k) {
         const int c = te + NT * (16 * half + k);
         const int q = c >> 5, part = c & 31;
-        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)p.pos[m0 + q] * 64 + 4 * (part & 15);
-        buf[k] = *reinterpret_cast<const float4*>(src);
+        const int32_t ps = p.pos[m0 + q];
+        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)ps * 64 + 4 * (part & 15);
+        buf[k] = rope_pos_ok(ps, p.max_pos) ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
       for (int k = 0; k < 16; ++k) {

@@ -349,19 +349,21 @@ __device__ __forceinline__ float ld_as_f32(const T* p, int64_t i) {
 template <typename T>
 __global__ void rope_inverse_kernel(const T* __restrict__ dY, T* __restrict__ G, int64_t M, int64_t d_out,
                                     const int32_t* __restrict__ pos, const float* __restrict__ cosc,
-                                    const float* __restrict__ sinc) {
+                                    const float* __restrict__ sinc, int64_t max_pos) {
   const int64_t heads = d_out / 128;
   const int64_t n = M * heads * 8;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t q = e & 7;
     const int64_t th = e >> 3;
     const int64_t t = th / heads, h = th - t * heads;
-    const int64_t prow = (int64_t)pos[t] * 64;
+    const int32_t ps = pos[t];
+    const bool ok = rope_pos_ok(ps, max_pos);
+    const int64_t prow = ok ? (int64_t)ps * 64 : 0;
     const int64_t base = t * d_out + h * 128;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int64_t f = q * 8 + u;
-      const float c = cosc[prow + f], s = sinc[prow + f];
+      const float c = ok ? cosc[prow + f] : 0.f, s = ok ? sinc[prow + f] : 0.f;
       const float y1 = ld_as_f32(dY, base + f), y2 = ld_as_f32(dY, base + f + 64);
       const float g1 = y1 * c + y2 * s, g2 = y2 * c - y1 * s;
       if constexpr (sizeof(T) == 2) {
@@ -376,15 +378,16 @@ __global__ void rope_inverse_kernel(const T* __restrict__ dY, T* __restrict__ G,
 }
 
 hipError_t launch_rope_inverse(int elem_bytes, const void* dY, void* G, int64_t M, int64_t d_out,
-                               const int32_t* pos, const float* cosc, const float* sinc, hipStream_t st) {
+                               const int32_t* pos, const float* cosc, const float* sinc, int64_t max_pos,
+                               hipStream_t st) {
   const int64_t n = M * (d_out / 128) * 8;
   if (n <= 0) return hipSuccess;
   if (elem_bytes == 2)
     hipLaunchKernelGGL(rope_inverse_kernel<uint16_t>, dim3(grid_for(n, 256)), dim3(256), 0, st,
-                       (const uint16_t*)dY, (uint16_t*)G, M, d_out, pos, cosc, sinc);
+                       (const uint16_t*)dY, (uint16_t*)G, M, d_out, pos, cosc, sinc, max_pos);
   else
     hipLaunchKernelGGL(rope_inverse_kernel<float>, dim3(grid_for(n, 256)), dim3(256), 0, st, (const float*)dY,
-                       (float*)G, M, d_out, pos, cosc, sinc);
+                       (float*)G, M, d_out, pos, cosc, sinc, max_pos);
   return hipGetLastError();
 }
 
@@ -539,7 +542,7 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
                                                            uint16_t* __restrict__ out, int64_t ldo,
                                                            const int32_t* __restrict__ pos,
                                                            const float* __restrict__ cosc,
-                                                           const float* __restrict__ sinc) {
+                                                           const float* __restrict__ sinc, int64_t max_pos) {
   const int64_t per_row = ROPE ? N / 8 : N / 4;
   const int64_t items = M * per_row;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < items; e += (int64_t)gridDim.x * blockDim.x) {
@@ -557,9 +560,12 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
     }
     uint16_t* dst = out + m * ldo + c;
     if constexpr (ROPE) {
-      const int64_t prow = (int64_t)pos[m] * 64 + (c & 127);
-      const float4 cs = *reinterpret_cast<const float4*>(cosc + prow);
-      const float4 sn = *reinterpret_cast<const float4*>(sinc + prow);
+      const int32_t ps = pos[m];
+      const bool ok = rope_pos_ok(ps, max_pos);
+      const int64_t prow = (int64_t)ps * 64 + (c & 127);
+      const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 cs = ok ? *reinterpret_cast<const float4*>(cosc + prow) : zero;
+      const float4 sn = ok ? *reinterpret_cast<const float4*>(sinc + prow) : zero;
       const float y1[4] = {a.x * cs.x - b.x * sn.x, a.y * cs.y - b.y * sn.y, a.z * cs.z - b.z * sn.z,
                            a.w * cs.w - b.w * sn.w};
       const float y2[4] = {b.x * cs.x + a.x * sn.x, b.y * cs.y + a.y * sn.y, b.z * cs.z + a.z * sn.z,
@@ -574,18 +580,18 @@ __global__ void __launch_bounds__(256) split_finish_kernel(const float* __restri
 
 hipError_t launch_split_finish(const float* part, int splits, int64_t part_stride, int64_t M, int64_t N,
                                uint16_t* out, int64_t ldo, const int32_t* pos, const float* cosc, const float* sinc,
-                               hipStream_t st) {
+                               int64_t max_pos, hipStream_t st) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (splits < 1 || splits > kMaxSplits || N % 8 || ldo % 4 || part_stride % 4) return hipErrorInvalidValue;
   if (pos) {
     if (N % 128) return hipErrorInvalidValue;
     const int64_t items = M * (N / 8);
     hipLaunchKernelGGL(split_finish_kernel<true>, dim3(grid_for(items, 256)), dim3(256), 0, st, part, splits,
-                       part_stride, M, N, out, ldo, pos, cosc, sinc);
+                       part_stride, M, N, out, ldo, pos, cosc, sinc, max_pos);
   } else {
     const int64_t items = M * (N / 4);
     hipLaunchKernelGGL(split_finish_kernel<false>, dim3(grid_for(items, 256)), dim3(256), 0, st, part, splits,
-                       part_stride, M, N, out, ldo, pos, cosc, sinc);
+                       part_stride, M, N, out, ldo, pos, cosc, sinc, max_pos);
   }
   return hipGetLastError();
 }

@@ -81,7 +81,7 @@ hipError_t launch_pad_cols(int elem_bytes, const void* src, void* dst, int64_t r
 
 // G = R(-angle) dY for rotate-half pairs of 128-wide heads.
 hipError_t launch_rope_inverse(int elem_bytes, const void* dY, void* G, int64_t M, int64_t d_out,
-                               const int32_t* pos, const float* cosc, const float* sinc,
+                               const int32_t* pos, const float* cosc, const float* sinc, int64_t max_pos,
                                hipStream_t st);
 
 hipError_t launch_rope_cache(int64_t max_pos, int head_dim, double theta, float* cosc, float* sinc,
@@ -149,10 +149,11 @@ hipError_t launch_panel_reduce(const float* part, int splits, int64_t part_strid
 
 // out [M, N] bf16 (row stride ldo) = fixed-order sum of split partials
 // (part[z * part_stride + m * N + n]); with pos != NULL also the RoPE rotation
-// of the pairs (n, n + 64) of each 128-wide head (N a multiple of 128).
+// of the pairs (n, n + 64) of each 128-wide head (N a multiple of 128; a
+// position outside [0, max_pos) gives zeros).
 hipError_t launch_split_finish(const float* part, int splits, int64_t part_stride, int64_t M, int64_t N,
                                uint16_t* out, int64_t ldo, const int32_t* pos, const float* cosc, const float* sinc,
-                               hipStream_t st);
+                               int64_t max_pos, hipStream_t st);
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t st);
 

@@ -72,6 +72,7 @@ struct SkinnyArgs {
   const int32_t* pos;  // ROPE: position of each row; cos / sin rows of 64
   const float* cosc;
   const float* sinc;
+  int64_t max_pos;     // rows of the cos / sin cache
 };
 
 // MB: 16-row blocks of X (M <= 16 MB); NB: 16-column strips per block; RB:
@@ -256,8 +257,10 @@ skinny_fwd_kernel(const SkinnyArgs p) {
     if (row >= p.M) continue;
     if constexpr (MODE == sk::ROPE) {
       const int f = (n0 & 127) + l16;  // frequency index (< 64) of the pair
-      const int64_t cr = (int64_t)p.pos[row] * 64 + f;
-      const float cs = p.cosc[cr], sn = p.sinc[cr];
+      const int32_t ps = p.pos[row];
+      const bool ok = rope_pos_ok(ps, p.max_pos);
+      const int64_t cr = ok ? (int64_t)ps * 64 + f : 0;
+      const float cs = ok ? p.cosc[cr] : 0.f, sn = ok ? p.sinc[cr] : 0.f;
       const float z1 = y[0][v], z2 = y[1][v];
       p.Y[(int64_t)row * p.N + n0 + l16] = f2bf(z1 * cs - z2 * sn);
       p.Y[(int64_t)row * p.N + n0 + 64 + l16] = f2bf(z2 * cs + z1 * sn);

@@ -47,3 +47,14 @@ def cpu64(t):
 
 def rel(got, ref):
     return O.rel_err(cpu64(got) if torch.is_tensor(got) else got, ref)
+
+
+def sample_rows(M, seq_len, batch, n=256, seed=99):
+    """n seeded token rows of an [M, .] output, every sequence's first and last
+    token among them (all rows when M <= n)."""
+    if M <= n:
+        return np.arange(M)
+    must = sorted({b * seq_len for b in range(batch)} | {b * seq_len + seq_len - 1 for b in range(batch)})
+    rng = np.random.default_rng(seed)
+    rest = rng.choice(np.setdiff1d(np.arange(M), must), n - len(must), replace=False)
+    return np.sort(np.concatenate([must, rest]))

@@ -1,9 +1,11 @@
-"""Full-size parity: every projection of the five workloads, through the same
-entry points and launch configuration bench.py times, against the float64
-oracle.  All of dA and dB are compared; Y and dX on 256 seeded rows that
-include every sequence's first and last token (the oracle is row-wise in
-them).  Bar: max|gpu - ref| / max|ref| <= 1e-5 (fp32 workload) or 2e-2 (bf16
-inputs, fp32 accumulate)."""
+"""Full-size parity of every projection of the five workloads, each through
+its single-projection entry point (lora_linear_*, lora_qk_rope_*,
+nf4_lora_linear_*), against the float64 oracle.  The group calls with a
+caller-held W^T that bench.py times are covered at the same sizes by
+test_bench_workload_gpu.  All of dA and dB are compared; Y and dX on 256
+seeded rows that include every sequence's first and last token (the oracle is
+row-wise in them).  Bar: max|gpu - ref| / max|ref| <= 1e-5 (fp32 workload) or
+2e-2 (bf16 inputs, fp32 accumulate)."""
 import numpy as np
 import pytest
 import torch
@@ -11,21 +13,11 @@ import torch
 import oracle as O
 from synth import CONFIGS, gen
 from synth.configs import Inputs
-from tests.helpers import cpu64, rel
+from tests.helpers import cpu64, rel, sample_rows
 
 pytestmark = pytest.mark.gpu
 
 CASES = [(c, p.name) for c, cfg in CONFIGS.items() for p in cfg.projections]
-
-
-def _rows(cfg, n=256, seed=99):
-    M, S = cfg.M, cfg.seq_len
-    if M <= n:
-        return np.arange(M)
-    must = sorted({b * S for b in range(cfg.batch)} | {b * S + S - 1 for b in range(cfg.batch)})
-    rng = np.random.default_rng(seed)
-    rest = rng.choice(np.setdiff1d(np.arange(M), must), n - len(must), replace=False)
-    return np.sort(np.concatenate([must, rest]))
 
 
 @pytest.mark.parametrize("cfg_id,pname", CASES, ids=[f"c{c}-{p}" for c, p in CASES])
@@ -53,7 +45,7 @@ def test_full_size_parity(lib, cfg_id, pname):
         dX, dA, dB = lib.lora_linear_bwd(X, W, A, B, s, dY)
     torch.cuda.synchronize()
 
-    rows = _rows(cfg)
+    rows = sample_rows(cfg.M, cfg.seq_len, cfg.batch)
     tr = torch.from_numpy(rows).cuda()
     if cfg.nf4:
         W64 = O.nf4_dequant(codes.cpu().numpy(), absmax.cpu().numpy(), table, p.d_out, p.d_in)

@@ -252,6 +252,38 @@ def test_rope_position_zero_is_identity(lib, dtype):
         assert torch.equal(a, b)
 
 
+# each RoPE path: one-launch few-token forward, few-token split partials,
+# generic 128 x 128 tiles, whole 256 x 256 tiles
+@pytest.mark.parametrize("M,d_out", [(40, 512), (200, 512), (2048, 2048), (4096, 4096)])
+def test_rope_out_of_range_positions_give_zero_rows(lib, M, d_out):
+    # positions just outside [0, max_pos) read no cache row: their rows of Y
+    # are zeros and their gradient is taken as zero; every other row is the
+    # plain RoPE layer's
+    d_in, r, seq = 256, 16, 64
+    X, W, A, B, dY = lora_inputs(29 + M, M, d_in, d_out, r, "bf16")
+    p = gen.positions_mod(M, seq).astype(np.int32)
+    bad = np.array([1, M // 2, M - 1])
+    p[bad] = [seq, -1, seq + 3]
+    pos = torch.from_numpy(p).cuda()
+    cos, sin = lib.rope_cache(seq, 128, 500000.0)
+    s = 1.0
+    Y = lib.lora_qk_rope_fwd(X, W, A, B, s, pos, cos, sin)
+    dX, dA, dB = lib.lora_qk_rope_bwd(X, W, A, B, s, pos, cos, sin, dY)
+    torch.cuda.synchronize()
+    good = np.setdiff1d(np.arange(M), bad)
+    pc = np.where((p >= 0) & (p < seq), p, 0)
+    assert np.all(cpu64(Y)[bad] == 0.0)
+    assert rel(Y[torch.from_numpy(good).cuda()], O.qk_rope_forward(X[torch.from_numpy(good).cuda()], W, A, B, s,
+                                                                      pc[good])) <= TOL["bf16"]
+    dY0 = cpu64(dY)
+    dY0[bad] = 0.0
+    dXr, dAr, dBr = O.qk_rope_backward(X, W, A, B, s, pc, dY0)
+    assert np.all(cpu64(dX)[bad] == 0.0)
+    errs = dict(dX=rel(dX, dXr), dA=rel(dA, dAr), dB=rel(dB, dBr))
+    print(M, d_out, errs)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
 # ---------------------------------------------------------------------------
 # NF4
 # ---------------------------------------------------------------------------
