@@ -65,7 +65,8 @@ enum {
   LORA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned */
   LORA_ERR_DTYPE = -4,     /* unknown dtype, or a dtype the entry point does not take */
   LORA_ERR_WORKSPACE = -5, /* ws_bytes < lora_workspace_bytes(...) or ws NULL when needed */
-  LORA_ERR_DEVICE = -6     /* current device is not gfx950, or a launch failed */
+  LORA_ERR_DEVICE = -6,    /* current device is not gfx950, or a launch failed */
+  LORA_ERR_SCRATCH = -7    /* lora_linear_fwd_noalloc: the problem needs more than the static scratch */
 };
 
 /* operation ids for lora_workspace_bytes */
@@ -104,6 +105,25 @@ size_t lora_workspace_bytes(int op, int dtype, int64_t M, int64_t d_in, int64_t 
 int lora_linear_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
                     const void* X, const void* W, const void* A, const void* B, void* Y,
                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * lora_linear_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same result as lora_linear_fwd, bit for bit, with no workspace
+ * argument.  Its scratch is a static device array inside the library,
+ * LORA_STATIC_SCRATCH_BYTES (32 MiB) per GPU, held by every GPU the library
+ * runs on until the process ends; the call itself never allocates or frees
+ * memory.  The caller still passes X, W, A, B and Y.  Problems whose
+ * workspace (lora_workspace_bytes(LORA_OP_FWD, ...)) exceeds that size
+ * return LORA_ERR_SCRATCH before any launch (bf16 at r = 64 fits up to about
+ * 87000 tokens at the large-weight shapes).  All calls on one GPU share its array, which keeps the last
+ * call's contents: calls that overlap on one GPU (different streams, or
+ * threads without ordering) race and must be serialised by the caller.
+ */
+#define LORA_STATIC_SCRATCH_BYTES (32u << 20)
+int lora_linear_fwd_noalloc(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                            const void* X, const void* W, const void* A, const void* B, void* Y,
+                            void* stream);
 
 /*
  * Backward: dX = dY W + s (dY B) A (skipped when dX is NULL),

@@ -36,6 +36,7 @@ from .functional import (  # noqa: F401
     lora_group_fwd,
     lora_linear_bwd,
     lora_linear_fwd,
+    lora_linear_fwd_noalloc,
     lora_merge,
     lora_qk_rope_bwd,
     lora_qk_rope_fwd,

@@ -15,6 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblora_linear.so")
 
 LORA_F32, LORA_BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 32 << 20  # LORA_STATIC_SCRATCH_BYTES of the header
 OP_FWD, OP_BWD, OP_ROPE_FWD, OP_ROPE_BWD, OP_NF4_FWD, OP_NF4_BWD, OP_MERGE, OP_DROPOUT_FWD, OP_DROPOUT_BWD = range(9)
 
 _lib = None
@@ -40,6 +41,7 @@ _SIGS = {
     "lora_strerror": ([_int], ctypes.c_char_p),
     "lora_workspace_bytes": ([_int, _int, _i64, _i64, _i64, _i64], _sz),
     "lora_linear_fwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _int),
+    "lora_linear_fwd_noalloc": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp], _int),
     "lora_linear_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                          _vp], _int),
     "lora_rope_cache": ([_i64, _int, _dbl, _vp, _vp, _vp], _int),

@@ -1187,6 +1187,38 @@ int swiglu_backward(int dtype, int64_t M, int64_t d_in, const lora_group_member*
   return LORA_OK;
 }
 
+// ---------------------------------------------------------------------------
+// the forward without a caller workspace: a static device array per GPU
+// ---------------------------------------------------------------------------
+// Each device the library runs on holds its own copy of `scratch` until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address of each
+// copy comes from hipGetSymbolAddress, called once per device with that
+// device current, and is kept here.
+constexpr size_t kStaticScratchBytes = size_t(LORA_STATIC_SCRATCH_BYTES);
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` on each device (NULL: not looked up yet)
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+
+int static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return LORA_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LORA_ERR_DEVICE;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LORA_OK;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1205,6 +1237,7 @@ const char* lora_strerror(int code) {
     case LORA_ERR_DTYPE: return "unsupported dtype";
     case LORA_ERR_WORKSPACE: return "workspace too small";
     case LORA_ERR_DEVICE: return "device error (not gfx950, or launch failed)";
+    case LORA_ERR_SCRATCH: return "problem needs more scratch than the library's static buffer holds";
     default: return "unknown error";
   }
 }
@@ -1225,6 +1258,21 @@ int lora_linear_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r
   const Layout L = make_layout(LORA_OP_FWD, dtype, M, d_in, d_out, r);
   TRY(check_ws(L, ws, ws_bytes));
   TRY(check_device());
+  return forward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, nullptr, Y, ws, L,
+                      static_cast<hipStream_t>(stream));
+}
+
+int lora_linear_fwd_noalloc(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
+                            const void* X, const void* W, const void* A, const void* B, void* Y, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  TRY(check_ptrs({W, A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y}));
+  const Layout L = make_layout(LORA_OP_FWD, dtype, M, d_in, d_out, r);
+  if (L.total > kStaticScratchBytes) return LORA_ERR_SCRATCH;
+  TRY(check_device());
+  void* ws = nullptr;
+  TRY(static_scratch(&ws));
   return forward_impl(dtype, M, d_in, d_out, r, scale, X, W, nullptr, A, B, nullptr, Y, ws, L,
                       static_cast<hipStream_t>(stream));
 }

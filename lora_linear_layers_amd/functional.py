@@ -37,6 +37,21 @@ def lora_linear_fwd(X, W, A, B, scale: float, Y=None, ws=None):
     return Y
 
 
+def lora_linear_fwd_noalloc(X, W, A, B, scale: float, Y=None):
+    """lora_linear_fwd with the library's static scratch instead of a
+    workspace (for callers that cannot allocate device memory; Y is allocated
+    here only when the caller passes none)."""
+    L._contig(X, W, A, B, Y)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    L._check("lora_linear_fwd_noalloc", L.lib().lora_linear_fwd_noalloc(
+        dt, M, d_in, d_out, r, float(scale), L._ptr(X), L._ptr(W), L._ptr(A), L._ptr(B), L._ptr(Y),
+        L._stream(X.device)))
+    return Y
+
+
 def lora_linear_bwd(X, W, A, B, scale: float, dY, need_dX: bool = True, ws=None, out=None):
     """(dX or None, dA fp32, dB fp32) for upstream gradient dY; X A^T is recomputed."""
     L._contig(X, W, A, B, dY)
