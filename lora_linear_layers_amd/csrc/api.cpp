@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/lora_linear.h"
+#include "few_args.h"
 #include "launch.h"
 #include "skinny.h"
 
@@ -52,6 +53,69 @@ int check_device() {
 }
 
 // ---------------------------------------------------------------------------
+// few-token plan (few.h): two launches per direction for 1 <= M <= 128
+// ---------------------------------------------------------------------------
+struct FewPlan {
+  bool ok = false;
+  int MB = 0, Mp = 0, Sp = 0, Kp = 0, Sq = 0, Kq = 0, Sk = 0, Kc = 0, n_tiles = 0;
+  size_t pp = 0, qp = 0, cp = 0, cnt = 0, g = 0, ps = 0, qs = 0, total = 0;
+};
+
+// bf16, 1 <= M <= 128, r a multiple of 8 up to 64, d_in and d_out multiples
+// of 64 (128 for RoPE), every byte offset of an operand below 2^30.  Blocks:
+// the forward's column tiles (128 of d_out) or the backward's (128 of d_in)
+// times chunks of the contraction chosen for about 384 blocks (each
+// chunk at least 256 long).  P in at most 16 chunks of d_in (the forward's
+// finishing blocks sum them with every load in flight); Q in at most 32
+// chunks of d_out of whole 128-row heads (summed with P between the
+// backward's launches, every slab's load in flight).
+FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
+  FewPlan F;
+  if (M < 1 || M > 16 * few::MAXMB || r % 8 || r > few::MAXR || d_in % 64 || d_out % 64) return F;
+  if (rope && d_out % 128) return F;
+  const int64_t lim = int64_t(1) << 30;
+  if (d_in * d_out * 2 >= lim || M * std::max(d_in, d_out) * 2 >= lim) return F;
+  // taken where it measured faster on MI355X than the skinny and split-GEMM
+  // paths (q_proj 4096 x 4096 bf16, an NF4 MLP gate 5120 -> 27392): the
+  // backward up to 64 tokens with a bf16 W, up to 128 with NF4; the forward
+  // with NF4 up to 64 tokens
+  if (bwd ? (!nf4 && M > 64) : (!nf4 || M > 64)) return F;
+  F.MB = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
+  F.Mp = 16 * F.MB;
+  const int64_t ncols = bwd ? d_in : d_out, K = bwd ? d_out : d_in;
+  F.n_tiles = (int)cdiv(ncols, few::BN);
+  int64_t sk = cdiv(384, F.n_tiles);
+  sk = std::min(sk, std::max<int64_t>(1, K / 256));
+  const int64_t kc = rup(cdiv(K, sk), 64);
+  F.Kc = (int)kc;
+  F.Sk = (int)cdiv(K, kc);
+  F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, 16), 128));
+  F.Sp = (int)cdiv(d_in, F.Kp);
+  if (bwd) {
+    F.Kq = (int)std::max<int64_t>(128, rup(cdiv(d_out, 32), 128));
+    F.Sq = (int)cdiv(d_out, F.Kq);
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  F.pp = take(size_t(F.Sp) * F.Mp * r * 4);
+  F.qp = take(size_t(F.Sq) * F.Mp * r * 4);
+  F.cp = take(size_t(F.Sk) * F.Mp * ncols * 4);
+  F.cnt = take(size_t(F.n_tiles) * 4);
+  if (bwd && rope) F.g = take(size_t(M) * d_out * 2);
+  if (bwd) {
+    F.ps = take(size_t(F.Mp) * r * 2);
+    F.qs = take(size_t(F.Mp) * r * 2);
+  }
+  F.total = off;
+  F.ok = true;
+  return F;
+}
+
+// ---------------------------------------------------------------------------
 // workspace layout
 // ---------------------------------------------------------------------------
 struct Layout {
@@ -70,6 +134,7 @@ struct Layout {
   int splits_p = 1, splits_q = 1;  // bf16 rank-r panels: P = X A^T, Q = G B
   int64_t ksplit_p = 0, ksplit_q = 0;
   size_t partb = 0;  // bf16: the dB partials, apart from dA's so one launch sums both
+  FewPlan few;       // few tokens: the two-launch path (its regions from offset 0)
 };
 
 // 256x256 tiles when they still give at least one tile per CU, else 128x128.
@@ -209,6 +274,12 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
   }
   if (drop) L.xm = take(size_t(M) * d_in * eb);
   L.total = off;
+  if (eb == 2 && !drop) {
+    const bool rope = op == LORA_OP_ROPE_FWD || op == LORA_OP_ROPE_BWD;
+    const bool nf4 = op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD;
+    L.few = few_plan(bwd, nf4, rope, M, d_in, d_out, r);
+    if (L.few.ok && L.few.total > L.total) L.total = L.few.total;
+  }
   return L;
 }
 
@@ -265,6 +336,9 @@ enum ProfKind : int {
   K_MASK,
   K_TRANSPOSE_W,
   K_SKINNY,
+  K_FEW_PANEL,
+  K_FEW_FWD,
+  K_FEW_BWD,
   K_PROF_COUNT
 };
 
@@ -284,7 +358,8 @@ const char* kind_name(int k) {
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_ab",
       "split_finish",               "swiglu_elementwise",
-      "dropout_mask_copy",          "transpose_w",                "skinny_fwd"};
+      "dropout_mask_copy",          "transpose_w",                "skinny_fwd",
+      "few_panel",                  "few_fwd",                    "few_bwd"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -391,6 +466,68 @@ int dequant_w(const Nf4W& q, int64_t n, void* out, hipStream_t st) {
   return LORA_OK;
 }
 
+// The few-token path (few.h): launch 1 (panel partials, counters cleared),
+// launch 2 (the streamed W product; the last block of each column tile adds
+// the rank term and stores).
+FewArgs few_args(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                 const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, char* w) {
+  FewArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = (int)M; a.Mp = F.Mp; a.d_in = (int)d_in; a.d_out = (int)d_out; a.r8 = (int)r; a.s = scale;
+  a.X = static_cast<const uint16_t*>(X);
+  a.W = static_cast<const uint16_t*>(W);
+  if (nf4) {
+    a.codes = nf4->codes; a.absmax = nf4->absmax;
+    for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
+    a.W = nullptr;
+  }
+  a.A = static_cast<const uint16_t*>(A); a.B = static_cast<const uint16_t*>(B);
+  if (rope) { a.rope = 1; a.pos = rope->pos; a.cosc = rope->cosc; a.sinc = rope->sinc; a.max_pos = rope->max_pos; }
+  a.Pp = reinterpret_cast<float*>(w + F.pp);
+  a.Qp = reinterpret_cast<float*>(w + F.qp);
+  a.Cp = reinterpret_cast<float*>(w + F.cp);
+  a.cnt = reinterpret_cast<int*>(w + F.cnt);
+  a.Sp = F.Sp; a.Kp = F.Kp; a.Sq = F.Sq; a.Kq = F.Kq; a.Sk = F.Sk; a.Kc = F.Kc; a.n_tiles = F.n_tiles;
+  return a;
+}
+
+int few_forward(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, void* Y, char* w,
+                hipStream_t st) {
+  FewArgs a = few_args(F, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, w);
+  a.Y = static_cast<uint16_t*>(Y);
+  const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
+  const double wb = nf4 ? ko * ki * (0.5 + 1.0 / 16) : 2.0 * ko * ki;
+  HIPTRY(timed(K_FEW_PANEL, 2 * Md * rr * ki, (Md + rr) * ki * 2 + 4.0 * F.Sp * F.Mp * rr, st,
+               [&] { return launch_few_panel(a, F.MB, st); }));
+  HIPTRY(timed(K_FEW_FWD, 2 * Md * ko * (ki + rr), wb + (Md * ki + ko * rr + Md * ko) * 2, st,
+               [&] { return launch_few_fwd(a, F.MB, nf4 != nullptr, st); }));
+  return LORA_OK;
+}
+
+int few_backward(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
+                 const void* W, const Nf4W* nf4, const void* A, const void* B, const Rope* rope, const void* dY,
+                 void* dX, float* dA, float* dB, char* w, hipStream_t st) {
+  FewArgs a = few_args(F, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, w);
+  a.dY = static_cast<const uint16_t*>(dY);
+  a.G = rope ? reinterpret_cast<uint16_t*>(w + F.g) : nullptr;
+  a.dX = static_cast<uint16_t*>(dX);
+  a.dA = dA;
+  a.dB = dB;
+  a.Ps = reinterpret_cast<uint16_t*>(w + F.ps);
+  a.Qs = reinterpret_cast<uint16_t*>(w + F.qs);
+  const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
+  const double wb = nf4 ? ko * ki * (0.5 + 1.0 / 16) : 2.0 * ko * ki;
+  HIPTRY(timed(K_FEW_PANEL, 2 * Md * rr * (ki + ko), (Md + rr) * (ki + ko) * 2 + 4.0 * (F.Sp + F.Sq) * F.Mp * rr,
+               st, [&] { return launch_few_panel(a, F.MB, st); }));
+  HIPTRY(timed(K_FEW_PANEL, 0, 4.0 * (F.Sp + F.Sq) * F.Mp * rr + 4.0 * F.Mp * rr, st,
+               [&] { return launch_few_reduce(a, st); }));
+  HIPTRY(timed(K_FEW_BWD, 2 * Md * ki * (ko + rr) + 4 * Md * rr * (ki + ko),
+               wb + (Md * ko + Md * ki + rr * ki + ko * rr + Md * ki) * 2 + 4.0 * rr * (ki + ko), st,
+               [&] { return launch_few_bwd(a, F.MB, nf4 != nullptr, st); }));
+  return LORA_OK;
+}
+
 // Pext: when not NULL, the panel s X A^T is already in Pext (row stride
 // ldpext, columns r..r8 zero) and is not computed here (group calls).
 int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, const void* X,
@@ -403,6 +540,8 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  if (!f32 && L.few.ok && !Pext && !Xa)
+    return few_forward(L.few, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, Y, w, st);
   // few tokens: panel, GEMM, rank term and epilogue in one launch
   // (bf16 W; an NF4 W keeps the split path's load-stage dequantisation)
   const int smode = rope ? sk::ROPE : sk::PLAIN;
@@ -523,6 +662,8 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  if (!f32 && L.few.ok && dX && !ov && !Xa && !keep)
+    return few_backward(L.few, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, dY, dX, dA, dB, w, st);
   if (nf4 && L.dequant && L.dx_nt && dX && !Wt_in) {
     // the backward reads W only as W^T: dequantise straight into it
     HIPTRY(timed(K_NF4_DEQ, 2.0 * d_out * d_in, (0.5 + 1.0 / 16 + 2.0) * d_out * d_in, st, [&] {

@@ -1,0 +1,1198 @@
+// few.h - the fused LoRA layer for few tokens (M <= 128, bf16 activations)
+// in two launches per direction.
+//
+//     forward   Y  = X W^T + bf16(s X A^T) B^T           (page "UnSloth加速微调
+//     backward  dX = G W + bf16(s G B) A,                  体验…", sections 算子融合
+//               dB = G^T bf16(s X A^T),                    and 反向传播优化)
+//               dA = bf16(s G B)^T X,   G = R(-angle) dY with RoPE (section
+//                                                           RoPE缓存集成), else dY
+//
+// With few tokens every operand except W is a few hundred KB: the layer is a
+// stream of W (bf16, or NF4 codes and absmax, page "Unsloth教程…", section
+// 显存优化策略, QLoRA paragraph) and launches cost as much as the stream.
+//
+//   launch 1 (few_panel_kernel): fp32 partial sums of the rank-r panels over
+//     chunks of their contraction, P = X A^T (both directions) and, in the
+//     backward, Q = G B; with RoPE it forms G from dY on load, rotating each
+//     head's pairs (i, i + 64) by the negated angle, and stores G for launch
+//     2.  It also clears launch 2's arrival counters.
+//   launch 2 (few_fwd_kernel / few_bwd_kernel): a block owns 128 output
+//     columns and one chunk of the contraction.  W tiles stream through a
+//     ring of LDS stages loaded by DMA (buffer_load ... lds, whole 128- or
+//     256-byte rows, so every request is whole cache lines); NF4 codes stream
+//     the same way and are expanded to bf16 in LDS with the load stage's own
+//     byte -> bf16 pair routine (bit-equal to nf4_dequant).  The block's fp32
+//     partial of its output tile goes to the workspace; the LAST block of a
+//     column tile to arrive (an atomic counter, device-scope release and
+//     acquire fences) sums the partials in chunk order, so the result does
+//     not depend on arrival order, adds the rank term (P_s B^T, or Q_s A:
+//     P_s = bf16(s P) and Q_s = bf16(s Q) summed from launch 1's partials in
+//     fixed order), applies RoPE or stores.  The backward's blocks also
+//     produce dB rows (every G row of a stage meets all M tokens inside one
+//     block, so dB needs no partials) and dA columns as side work.
+//
+// MFMA v_mfma_f32_16x16x32_bf16.  A lane l holds row l % 16, contraction
+// 8 (l / 16) .. +7; B lane l holds column l % 16, the same contraction; the 4
+// results of lane l are rows 4 (l / 16) + v, column l % 16.
+//
+// LDS tiles.  "NT" tiles (rows of 64 contraction elements, 128 bytes): chunk
+// c of row r at chunk c ^ (r & 7); a fragment read (16 rows, one chunk) is
+// conflict-free.  "NN" tiles (contraction rows of 128 columns, 256 bytes),
+// read with ds_read_b64_tr_b16 (in each 16-lane group, lane i points at row
+// k0 + i / 4, columns n0 + 4 (i % 4) .. +3 and receives column n0 + i, rows
+// k0 .. k0 + 3): the 32-byte segment s of row r sits at segment
+// (s & ~3) | ((s ^ r) & 3), so the four rows of a group read four different
+// 32-byte bank windows.
+#pragma once
+
+#include <type_traits>
+
+#include "few_args.h"
+#include "gemm.h"
+
+namespace lora {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t few_rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,
+                                           (int)(bytes < 0x7fffffff ? bytes : 0x7fffffff), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 few_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// One DMA instruction (SIZE bytes per lane) into LDS at lds_base + SIZE lane.
+// voff: the lane's byte offset (a loop-invariant register: a register that a
+// DMA still in flight reads must not be rewritten, so one that changed per
+// stage would make the compiler wait for every DMA before reusing it);
+// soff: the stage's scalar offset.  Out-of-range lanes carry voff >= 2^31,
+// past every resource (the scalar offset is never large enough to wrap).
+template <int SIZE = 16>
+__device__ __forceinline__ void few_dma(__amdgpu_buffer_rsrc_t r, char* lds_base, uint32_t voff, int soff) {
+  static_assert(SIZE == 16 || SIZE == 4, "16 or 4 bytes per lane");
+  auto* dst = (__attribute__((address_space(3))) void*)lds_base;
+  if constexpr (SIZE == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, (int)voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 4, (int)voff, soff, 0, 0);
+}
+
+// NT tile: byte offset of 16-byte chunk c of row r (rows of 128 bytes)
+__device__ __forceinline__ int nt_off(int r, int c) { return (r << 7) + ((c ^ (r & 7)) << 4); }
+// NN tile with rows of RB bytes (128 or 256): byte offset of 16-byte chunk c
+// of row r
+template <int RB = 256>
+__device__ __forceinline__ int nn_off(int r, int c) {
+  const int sg = c >> 1;
+  return r * RB + ((((sg & ~3) | ((sg ^ r) & 3)) << 1 | (c & 1)) << 4);
+}
+
+// B fragment of a 16x16x32 MFMA from an NN tile: columns n0 .. n0 + 15, the
+// contraction rows k0 .. k0 + 31 (k0 a multiple of 32).  Lane group gq =
+// l / 16 takes rows k0 + 8 gq .. +7 in two transposing reads of 4 rows.
+template <int RB = 256>
+__device__ __forceinline__ bf16x8 nn_frag(const char* tile, int k0, int n0, int lane) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const int gq = lane >> 4, i = lane & 15;
+  i16x4 h[2];
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
+    const int col = n0 + 4 * (i & 3);  // 4 columns = 8 bytes inside 16-byte chunk col / 8
+    const int off = nn_off<RB>(row, col >> 3) + ((col & 7) << 1);
+    h[hq] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)tile + off));
+  }
+  u32x4 v;
+  v[0] = (uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16);
+  v[1] = (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16);
+  v[2] = (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16);
+  v[3] = (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Fragment read transposed from an NT tile (rows = contraction, 64 columns):
+// lane l gets column n0 + l % 16, contraction rows k0 + 8 (l / 16) .. +7 (the
+// transposing read of nn_frag on the NT chunk layout)
+__device__ __forceinline__ bf16x8 nt_tr_frag(const char* tile, int k0, int n0, int lane) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const int gq = lane >> 4, i = lane & 15;
+  i16x4 h[2];
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
+    const int col = n0 + 4 * (i & 3);
+    const int off = nt_off(row, col >> 3) + ((col & 7) << 1);
+    h[hq] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) char*)tile + off));
+  }
+  u32x4 v;
+  v[0] = (uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16);
+  v[1] = (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16);
+  v[2] = (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16);
+  v[3] = (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 32-bit LDS address of a generic pointer into LDS
+__device__ __forceinline__ uint32_t few_lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// The LDS addresses of the two transposing reads of nn_frag / nt_tr_frag
+template <int RB = 256>
+__device__ __forceinline__ u32x2 nn_frag_addr(const char* tile, int k0, int n0, int lane) {
+  const int gq = lane >> 4, i = lane & 15;
+  u32x2 a;
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
+    const int col = n0 + 4 * (i & 3);
+    a[hq] = few_lds_addr(tile + nn_off<RB>(row, col >> 3) + ((col & 7) << 1));
+  }
+  return a;
+}
+__device__ __forceinline__ u32x2 nt_tr_frag_addr(const char* tile, int k0, int n0, int lane) {
+  const int gq = lane >> 4, i = lane & 15;
+  u32x2 a;
+#pragma unroll
+  for (int hq = 0; hq < 2; ++hq) {
+    const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
+    const int col = n0 + 4 * (i & 3);
+    a[hq] = few_lds_addr(tile + nt_off(row, col >> 3) + ((col & 7) << 1));
+  }
+  return a;
+}
+
+// N transposed fragments from their read addresses, in one asm block that
+// issues the 2N reads back to back and waits for them before it ends (no read
+// is in flight when the block's output registers are handed back).  The
+// builtin form of the read makes the compiler wait first for every LDS DMA
+// in flight, which would drain the stage ring at each read; these tiles are
+// never a DMA's destination while a DMA into them can be in flight (the ring
+// protocol's waits and barriers order them).
+#define FEW_TR(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
+template <int N>
+__device__ __forceinline__ void few_tr_frags(bf16x8 (&f)[N], const u32x2 (&a)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 fragments");
+  u32x2 h[2 * N];
+  if constexpr (N == 1) {
+    asm volatile(FEW_TR(0, 2) FEW_TR(1, 3) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1])
+                 : "v"(a[0][0]), "v"(a[0][1]));
+  } else if constexpr (N == 2) {
+    asm volatile(FEW_TR(0, 4) FEW_TR(1, 5) FEW_TR(2, 6) FEW_TR(3, 7) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]));
+  } else {
+    asm volatile(FEW_TR(0, 8) FEW_TR(1, 9) FEW_TR(2, 10) FEW_TR(3, 11) FEW_TR(4, 12) FEW_TR(5, 13)
+                     FEW_TR(6, 14) FEW_TR(7, 15) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]),
+                   "=&v"(h[6]), "=&v"(h[7])
+                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(a[2][0]), "v"(a[2][1]),
+                   "v"(a[3][0]), "v"(a[3][1]));
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const u32x4 v = {h[2 * n][0], h[2 * n][1], h[2 * n + 1][0], h[2 * n + 1][1]};
+    f[n] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+#undef FEW_TR
+
+// A or B fragment from an NT tile: rows r0 .. r0 + 15, contraction 32 s .. +31
+__device__ __forceinline__ bf16x8 nt_frag(const char* tile, int r0, int s, int lane) {
+  return __builtin_bit_cast(bf16x8,
+                            *reinterpret_cast<const u32x4*>(tile + nt_off(r0 + (lane & 15), 4 * s + (lane >> 4))));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf2f(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
+
+// cos / sin of the row's position at frequencies f .. f + 3 (zeros for a
+// position outside the cache)
+__device__ __forceinline__ void few_cs4(const FewArgs& p, int t, int f, float4& c, float4& s) {
+  const int32_t q = p.pos[t];
+  if (rope_pos_ok(q, p.max_pos)) {
+    c = *reinterpret_cast<const float4*>(p.cosc + (int64_t)q * 64 + f);
+    s = *reinterpret_cast<const float4*>(p.sinc + (int64_t)q * 64 + f);
+  } else {
+    c = make_float4(0.f, 0.f, 0.f, 0.f);
+    s = c;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch 1: panel partials.  Blocks [0, Sp): P chunk b of d_in; blocks
+// [Sp, Sp + Sq): Q chunk of d_out.  A block's 4 waves take the chunk's 32-wide
+// steps in turn (Q with RoPE: a wave takes a whole head, its pairs (i, i+64)
+// in one lane), then the waves' sums meet in LDS.
+// ---------------------------------------------------------------------------
+template <int MB>
+__global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
+  using namespace few;
+  constexpr int RB = MAXR / 16;
+  // Q: each wave's 128 rows of B (an NN tile of 64 rank columns, 16 KB);
+  // afterwards the waves' partial sums [4][MB * 16][MAXR] fp32
+  constexpr int BT = 128 * 128;
+  constexpr int RED = 4 * MB * 16 * MAXR * 4;
+  __shared__ __attribute__((aligned(16))) char smem[RED > 4 * BT ? RED : 4 * BT];
+  float(*red)[MB * 16][MAXR] = reinterpret_cast<float(*)[MB * 16][MAXR]>(smem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int rb_n = (p.r8 + 15) >> 4;  // 16-column rank blocks that exist
+
+  if (blockIdx.x == 0)
+    for (int i = tid; i < p.n_tiles; i += NT) p.cnt[i] = 0;
+
+  f32x4 acc[MB][RB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const bool isq = (int)blockIdx.x >= p.Sp;
+  if (!isq) {
+    // P chunk: [X rows] x [A rows]^T over k in [k0, k1)
+    const int k0 = blockIdx.x * p.Kp;
+    const int k1 = min(p.d_in, k0 + p.Kp);
+    const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
+    const __amdgpu_buffer_rsrc_t ra = few_rsrc(p.A, (int64_t)p.r8 * p.d_in * 2);
+    for (int k = k0 + 32 * wave; k < k1; k += 128) {
+      const int kk = k + 8 * g;  // the lane's first element (k1 - k0 is a multiple of 32)
+      bf16x8 xf[MB], af[RB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int row = 16 * mb + l16;
+        xf[mb] = __builtin_bit_cast(bf16x8, few_ld16(rx, row < p.M ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 16 * rb + l16;
+        af[rb] = __builtin_bit_cast(bf16x8, few_ld16(ra, row < p.r8 ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (rb < rb_n) acc[mb][rb] = mfma16(xf[mb], af[rb], acc[mb][rb]);
+    }
+  } else {
+    // Q chunk: [G rows] x B over i in [i0, i1), a head (128 rows of B) per
+    // wave at a time; B's rows go to the wave's NN tile (rows of 64 rank
+    // columns, zero past r8), read back with the transposing LDS read
+    const int c = blockIdx.x - p.Sp;
+    const int i0 = c * p.Kq;
+    const int i1 = min(p.d_out, i0 + p.Kq);
+    const __amdgpu_buffer_rsrc_t ry = few_rsrc(p.dY, (int64_t)p.M * p.d_out * 2);
+    const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
+    char* bt = smem + wave * BT;
+    for (int h = i0 + 128 * wave; h < i1; h += 512) {
+      // B rows h .. h + 127 (fewer at the end: zeros), 8 rank columns per
+      // 16-byte chunk: lane -> row h + lane + 64 j, chunks 0 .. 7
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = lane + 64 * j;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const bool ok = h + row < i1 && 8 * cc < p.r8;
+          const u32x4 v = few_ld16(rbr, ok ? (uint32_t)(((h + row) * p.r8 + 8 * cc) * 2) : OOB);
+          *reinterpret_cast<u32x4*>(bt + nn_off<128>(row, cc)) = v;
+        }
+      }
+      // the wave reads back only what it wrote (its LDS operations complete in order)
+      // G fragments: 4 steps of 32 rows of the head; with RoPE the lane's
+      // elements of steps 0 / 1 pair with those of steps 2 / 3
+      bf16x8 gf[4][MB];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = 16 * mb + l16;
+          const int ii = h + 32 * st + 8 * g;
+          gf[st][mb] = __builtin_bit_cast(
+              bf16x8, few_ld16(ry, row < p.M && ii < i1 ? (uint32_t)((row * p.d_out + ii) * 2) : OOB));
+        }
+      if (p.rope) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = 16 * mb + l16;
+          if (row >= p.M) continue;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int f = 32 * st + 8 * g;  // frequency of the lane's first pair
+            float4 c0, s0, c1, s1;
+            few_cs4(p, row, f, c0, s0);
+            few_cs4(p, row, f + 4, c1, s1);
+            const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const u32x4 y1 = __builtin_bit_cast(u32x4, gf[st][mb]);
+            const u32x4 y2 = __builtin_bit_cast(u32x4, gf[st + 2][mb]);
+            u32x4 g1, g2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a0 = bf2f(y1[e] & 0xffff), a1 = bf2f(y1[e] >> 16);
+              const float b0 = bf2f(y2[e] & 0xffff), b1 = bf2f(y2[e] >> 16);
+              const float c_0 = cs[2 * e], c_1 = cs[2 * e + 1], s_0 = sn[2 * e], s_1 = sn[2 * e + 1];
+              g1[e] = pack_bf16x2(a0 * c_0 + b0 * s_0, a1 * c_1 + b1 * s_1);
+              g2[e] = pack_bf16x2(b0 * c_0 - a0 * s_0, b1 * c_1 - a1 * s_1);
+            }
+            gf[st][mb] = __builtin_bit_cast(bf16x8, g1);
+            gf[st + 2][mb] = __builtin_bit_cast(bf16x8, g2);
+            const int ii = h + 32 * st + 8 * g;
+            *reinterpret_cast<u32x4*>(p.G + (int64_t)row * p.d_out + ii) = g1;
+            *reinterpret_cast<u32x4*>(p.G + (int64_t)row * p.d_out + ii + 64) = g2;
+          }
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        bf16x8 bf[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) bf[rb] = nn_frag<128>(bt, 32 * st, 16 * rb, lane);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb < rb_n) acc[mb][rb] = mfma16(gf[st][mb], bf[rb], acc[mb][rb]);
+      }
+    }
+  }
+  // the waves' sums meet in LDS (over the B tiles: every wave is done with them)
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wave][16 * mb + 4 * g + v][16 * rb + l16] = acc[mb][rb][v];
+  __syncthreads();
+  float* out = isq ? p.Qp + (int64_t)(blockIdx.x - p.Sp) * p.Mp * p.r8 : p.Pp + (int64_t)blockIdx.x * p.Mp * p.r8;
+  for (int e = tid; e < p.Mp * p.r8; e += NT) {
+    const int t = e / p.r8, q = e - t * p.r8;
+    out[e] = ((red[0][t][q] + red[1][t][q]) + red[2][t][q]) + red[3][t][q];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch 2 pieces shared by both directions
+// ---------------------------------------------------------------------------
+// The NF4 byte -> bf16 pair table, 16 copies: entry b of copy k at float2 index
+// 16 b + k.  Lane l reads copy l % 16, so the 16 lanes of a 128-byte LDS
+// cycle hit 16 different bank pairs whatever their code bytes (one shared
+// copy measured about 2x more bank-conflict cycles than LDS cycles).
+constexpr int NF4_TAB_BYTES = 256 * 16 * 8;
+
+__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float* table) {
+  for (int t = threadIdx.x; t < 256 * 16; t += few::NT) {
+    const int b = t >> 4;
+    tab[t] = f32x2{table[b >> 4], table[b & 15]};
+  }
+}
+
+// two bf16 of code byte b: bf16(f32(table[c] * absmax)) for the high and low
+// nibble (the same products as nf4_byte_to_bf16x2); tabl = tab + lane % 16
+__device__ __forceinline__ uint32_t few_nf4_pair(const f32x2* tabl, uint32_t b, float am) {
+  const f32x2 t = tabl[b << 4];
+  return pack_bf16x2(t.x * am, t.y * am);
+}
+
+// Stage ring geometry: the W slot (bf16 rows, or NF4 codes and absmax) and the
+// activation slot (MP rows of 64 elements, NT layout) of one stage, and how
+// many stages fit next to the fixed LDS (NF4: two bf16 W tiles and the byte
+// -> pair table).
+template <int MB, bool NF4, int WROWS, int WBYTES_BF16, int EXTRA = 0>
+struct FewRing {
+  static constexpr int MP = MB <= 2 ? 32 : (MB <= 4 ? 64 : 128);  // activation rows in LDS (8 per DMA, 4 waves)
+  static constexpr int XI = MP / 32;                               // activation DMAs per wave per stage
+  static constexpr int CODES = WROWS * 32;                         // NF4 codes of a stage (64 elements per row)
+  static constexpr int AM = 1024;                                   // absmax: 4 waves x 64 lanes x 4 bytes
+  static constexpr int WSLOT = NF4 ? CODES + AM : WBYTES_BF16;
+  static constexpr int XSLOT = MP * 128;
+  static constexpr int STAGE = WSLOT + XSLOT;
+  static constexpr int FIXED = (NF4 ? 2 * WBYTES_BF16 + NF4_TAB_BYTES : 0) + EXTRA;
+  static constexpr int BUDGET = 160 * 1024 - 256 - FIXED;
+  static constexpr int NS0 = BUDGET / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;
+  // (+16: the finishing handshake's flag, in the same LDS array: a second
+  // __shared__ variable gives the LDS accesses alias-scope metadata, after
+  // which the compiler waits for every DMA in flight before each LDS read)
+  static constexpr int LDS = FIXED + NS * STAGE + 16;
+  static_assert(NS >= 3, "at least three stages");
+};
+
+// Partials exchanged between the blocks of one launch are written and read
+// with device-scope (agent) relaxed atomic stores and loads: on gfx950 these
+// are plain loads and stores marked coherent at device scope, which go
+// through the XCD's L2 to the device's coherence point.  A device-scope
+// fence would instead write back and invalidate the whole L2 of the XCD
+// (measured on MI355X: about 1.2 us per fence, serialised per XCD, which on
+// a 4096 x 4096 weight stream cost 4x its time).
+__device__ __forceinline__ void few_st_dev(float* q, float v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float few_ld_dev(const float* q) {
+  return __hip_atomic_load(const_cast<float*>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The finishing handshake: every thread waits until its partial stores have
+// been performed at the coherence point (vmcnt), the block meets, then one
+// device-scope atomic per block; true in the last block of the tile, whose
+// device-scope loads (issued only after that atomic has returned) then see
+// every other block's partial.
+__device__ __forceinline__ bool few_last_arrival(int* cnt, int total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(0));
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = prev == total - 1;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// f(integral_constant<int, j>) for j = 0 .. U-1, in order
+template <int U, class F, int... js>
+__device__ __forceinline__ void few_unroll_(F&& f, std::integer_sequence<int, js...>) {
+  (f(std::integral_constant<int, js>{}), ...);
+}
+template <int U, class F>
+__device__ __forceinline__ void few_unroll(F&& f) {
+  few_unroll_<U>(f, std::make_integer_sequence<int, U>{});
+}
+
+// wait until at most n stages of this wave's DMAs (per stage PER instructions)
+// are outstanding, n in 0 .. 7
+template <int PER>
+__device__ __forceinline__ void few_wait_stages(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(0)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 1 > 63 ? 63 : PER * 1)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 2 > 63 ? 63 : PER * 2)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 3 > 63 ? 63 : PER * 3)); break;
+    case 4: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 4 > 63 ? 63 : PER * 4)); break;
+    case 5: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 5 > 63 ? 63 : PER * 5)); break;
+    default: __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(PER * 6 > 63 ? 63 : PER * 6)); break;
+  }
+}
+
+// Fixed-order sums of fp32 partial slabs, float4 at a time: out[i] =
+// sum over z < S of src[z * zstride + off[i]] for the NI offsets a thread owns
+// (off < 0: skipped, out zero), the loads of U slabs of every item in flight
+// before any add.
+template <int NI, int U = 8>
+__device__ __forceinline__ void few_sum4(const float* src, int S, int64_t zstride, const int64_t (&off)[NI],
+                                         float4 (&out)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z0 = 0; z0 < S; z0 += U) {
+    float4 v[NI][U];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        v[i][u] = (off[i] >= 0 && z0 + u < S)
+                      ? *reinterpret_cast<const float4*>(src + (int64_t)(z0 + u) * zstride + off[i])
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        out[i].x += v[i][u].x;
+        out[i].y += v[i][u].y;
+        out[i].z += v[i][u].z;
+        out[i].w += v[i][u].w;
+      }
+  }
+}
+
+// bf16(s * sum over z < S of part[z][t][q]) into an NT tile of MP rows and 64
+// columns (zeros past M and r8): four columns per item, up to four items of
+// a thread summed together
+template <int MP>
+__device__ __forceinline__ void few_panel_sum(const float* part, int S, const FewArgs& p, char* tile) {
+  constexpr int ITEMS = MP * 16;
+  for (int i0 = threadIdx.x; i0 < ITEMS; i0 += 4 * few::NT) {
+    int64_t off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int it = i0 + i * few::NT, t = it >> 4, q = 4 * (it & 15);
+      off[i] = (it < ITEMS && t < p.M && q < p.r8) ? (int64_t)t * p.r8 + q : -1;
+    }
+    float4 a[4];
+    few_sum4<4>(part, S, (int64_t)p.Mp * p.r8, off, a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int it = i0 + i * few::NT, t = it >> 4, q = 4 * (it & 15);
+      if (it >= ITEMS) continue;
+      const uint2 v = make_uint2(pack_bf16x2(p.s * a[i].x, p.s * a[i].y), pack_bf16x2(p.s * a[i].z, p.s * a[i].w));
+      *reinterpret_cast<uint2*>(tile + nt_off(t, q >> 3) + 2 * (q & 7)) = v;
+    }
+  }
+}
+
+// few_sum4 over partials written by other blocks of the same launch:
+// device-scope loads of single floats, 8 slabs of every item in flight.
+template <int NI>
+__device__ __forceinline__ void few_sum4_dev(const float* src, int S, int64_t zstride, const int64_t (&off)[NI],
+                                             float4 (&out)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int z0 = 0; z0 < S; z0 += 8) {
+    float v[NI][8][4];
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[i][u][e] = (off[i] >= 0 && z0 + u < S) ? few_ld_dev(src + (int64_t)(z0 + u) * zstride + off[i] + e) : 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        out[i].x += v[i][u][0];
+        out[i].y += v[i][u][1];
+        out[i].z += v[i][u][2];
+        out[i].w += v[i][u][3];
+      }
+  }
+}
+
+// The finishing block's output pass: y = (sum over chunks of the partials) +
+// rank term (an fp32 tile [MP][BNT] in LDS, in the same columns), then bf16
+// stores of four columns per item, or, with RoPE (BNT = 128, one head), the
+// rotation of the pairs (f, f + 64) of each row.
+template <int BNT>
+__device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, int n0, int N, uint16_t* out,
+                                           bool rope) {
+  const int64_t zs = (int64_t)p.Mp * N;
+  if (!rope) {
+    const int items = p.M * (BNT / 4);
+    for (int i0 = threadIdx.x; i0 < items; i0 += 4 * few::NT) {
+      int64_t off[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int it = i0 + i * few::NT, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
+        off[i] = (it < items && n0 + c < N) ? (int64_t)t * N + n0 + c : -1;
+      }
+      float4 a[4];
+      few_sum4_dev<4>(p.Cp, p.Sk, zs, off, a);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (off[i] < 0) continue;
+        const int it = i0 + i * few::NT, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
+        const float* r = tl + t * BNT + c;
+        *reinterpret_cast<uint2*>(out + off[i]) =
+            make_uint2(pack_bf16x2(a[i].x + r[0], a[i].y + r[1]), pack_bf16x2(a[i].z + r[2], a[i].w + r[3]));
+      }
+    }
+    return;
+  }
+  // RoPE: item = (row t, frequencies f .. f + 3); both halves summed
+  const int items = p.M * 16;
+  for (int i0 = threadIdx.x; i0 < items; i0 += 2 * few::NT) {
+    int64_t off[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = i0 + i * few::NT, t = it >> 4, f = 4 * (it & 15);
+      off[2 * i] = it < items ? (int64_t)t * N + n0 + f : -1;
+      off[2 * i + 1] = it < items ? (int64_t)t * N + n0 + f + 64 : -1;
+    }
+    float4 a[4];
+    few_sum4_dev<4>(p.Cp, p.Sk, zs, off, a);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = i0 + i * few::NT, t = it >> 4, f = 4 * (it & 15);
+      if (it >= items) continue;
+      float4 c, sn;
+      few_cs4(p, t, f, c, sn);
+      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      const float z1[4] = {a[2 * i].x, a[2 * i].y, a[2 * i].z, a[2 * i].w};
+      const float z2[4] = {a[2 * i + 1].x, a[2 * i + 1].y, a[2 * i + 1].z, a[2 * i + 1].w};
+      float y1[4], y2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float u = z1[e] + tl[t * BNT + f + e], w = z2[e] + tl[t * BNT + 64 + f + e];
+        y1[e] = u * cc[e] - w * ss[e];
+        y2[e] = w * cc[e] + u * ss[e];
+      }
+      *reinterpret_cast<uint2*>(out + off[2 * i]) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      *reinterpret_cast<uint2*>(out + off[2 * i + 1]) =
+          make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// backward, between the launches: P_s = bf16(s X A^T) and Q_s = bf16(s G B)
+// from the panel partials (block 0: P, block 1: Q), [Mp, r8] bf16 each
+// ---------------------------------------------------------------------------
+// Blocks [0, nb): P; [nb, 2 nb): Q; one float4 of the panel per thread, the
+// loads of up to 32 slabs in flight at once.
+__global__ void __launch_bounds__(few::NT) few_reduce_kernel(const FewArgs p) {
+  const int nb = gridDim.x / 2;
+  const bool q = (int)blockIdx.x >= nb;
+  const float* part = q ? p.Qp : p.Pp;
+  const int S = q ? p.Sq : p.Sp;
+  uint16_t* out = q ? p.Qs : p.Ps;
+  const int items = p.Mp * p.r8 / 4;
+  const int it = (blockIdx.x - (q ? nb : 0)) * few::NT + threadIdx.x;
+  int64_t off[1] = {it < items ? 4 * (int64_t)it : -1};
+  float4 a[1];
+  few_sum4<1, 32>(part, S, (int64_t)p.Mp * p.r8, off, a);
+  if (off[0] >= 0)
+    *reinterpret_cast<uint2*>(out + off[0]) =
+        make_uint2(pack_bf16x2(p.s * a[0].x, p.s * a[0].y), pack_bf16x2(p.s * a[0].z, p.s * a[0].w));
+}
+
+// ---------------------------------------------------------------------------
+// launch 2, forward: Y = X W^T + P_s B^T, then store or RoPE.
+// Block (blockIdx.x = tile of BNF output columns, blockIdx.y = chunk of d_in).
+// 128 columns (4 waves x 32).
+// ---------------------------------------------------------------------------
+template <int MB, bool NF4>
+__global__ void __launch_bounds__(few::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+few_fwd_kernel(const FewArgs p) {
+  using namespace few;
+  constexpr int BNF = 128;               // output columns of the block
+  constexpr int NJ = BNF / 64;          // 16-column blocks per wave
+  using R = FewRing<MB, NF4, BNF, BNF * 128>;
+  constexpr int NS = R::NS;
+  constexpr int WI = NF4 ? BNF / 128 : BNF / 32;  // W DMAs per wave per stage (8 rows of bf16, 32 rows of codes)
+  constexpr int PER = WI + R::XI + (NF4 ? 1 : 0);
+  static_assert(R::LDS >= R::MP * BNF * 4 && R::LDS >= R::MP * 128, "the finish reuses the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+  char* ring = smem + R::FIXED;
+  auto wslot = [&](int slot) { return ring + slot * R::STAGE; };
+  auto xslot = [&](int slot) { return ring + slot * R::STAGE + R::WSLOT; };
+  auto wbf = [&](int b) { return smem + b * (BNF * 128); };  // NF4: expanded bf16 W tiles
+  f32x2* tab2 = reinterpret_cast<f32x2*>(smem + 2 * BNF * 128);
+  const f32x2* tabl = tab2 + (threadIdx.x & 15);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nt = blockIdx.x, kc = blockIdx.y;
+  const int n0 = nt * BNF;
+  const int k0 = kc * p.Kc;
+  const int k1 = min(p.d_in, k0 + p.Kc);
+  const int nk = (k1 - k0) / BK;
+  if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
+
+  const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
+  __amdgpu_buffer_rsrc_t rw, rc, ram;
+  if constexpr (NF4) {
+    rc = few_rsrc(p.codes, (int64_t)p.d_out * p.d_in / 2);
+    ram = few_rsrc(p.absmax, (int64_t)p.d_out * (p.d_in / 64) * 4);
+  } else {
+    rw = few_rsrc(p.W, (int64_t)p.d_out * p.d_in * 2);
+  }
+  // DMA lane mapping of an NT tile: 8 rows x 128 bytes per instruction, the
+  // lane lands at physical chunk lane & 7 of row lane / 8 and so fetches
+  // logical chunk (lane & 7) ^ (row & 7)
+  const int drow = lane >> 3, dpc = lane & 7;
+  // the lanes' DMA offsets at stage 0 (stage st adds a scalar offset)
+  uint32_t vw[WI], vam = OOB, vx[R::XI];
+  if constexpr (NF4) {
+    // codes: instruction j moves rows 32 j .. 32 j + 31, 32 bytes each (the
+    // lane: row 32 j + lane / 2, half lane & 1), landing at byte 32 row + 16 half
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int n = n0 + 32 * (WI * wave + i) + (lane >> 1);
+      vw[i] = n < p.d_out ? (uint32_t)((int64_t)n * (p.d_in / 2) + k0 / 2 + 16 * (lane & 1)) : OOB;
+    }
+    // absmax of rows 64 wave .. + 63 (4 bytes per lane)
+    const int ar = 64 * wave + lane, na = n0 + ar;
+    if (ar < BNF && na < p.d_out) vam = (uint32_t)(((int64_t)na * (p.d_in / 64) + k0 / 64) * 4);
+  } else {
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int row = 8 * (WI * wave + i) + drow;
+      const int n = n0 + row;
+      vw[i] = n < p.d_out ? (uint32_t)(((int64_t)n * p.d_in + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R::XI; ++i) {
+    const int row = 8 * (wave + 4 * i) + drow;  // instruction wave + 4 i: rows 8 j .. 8 j + 7
+    vx[i] = row < p.M ? (uint32_t)((row * p.d_in + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+  }
+  auto issue = [&](int st, int slot) {
+    char* ws = wslot(slot);
+    if constexpr (NF4) {
+#pragma unroll
+      for (int i = 0; i < WI; ++i) few_dma(rc, ws + (WI * wave + i) * 1024, vw[i], st * (BK / 2));
+      few_dma<4>(ram, ws + R::CODES + wave * 256, vam, st * 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WI; ++i) few_dma(rw, ws + (WI * wave + i) * 1024, vw[i], st * (BK * 2));
+    }
+    char* xs = xslot(slot);
+#pragma unroll
+    for (int i = 0; i < R::XI; ++i) few_dma(rx, xs + (wave + 4 * i) * 1024, vx[i], st * (BK * 2));
+  };
+  // NF4: codes and absmax of stage st -> bf16 W tile b (NT layout)
+  auto expand = [&](int slot, int b) {
+    if constexpr (NF4) {
+      const char* ws = wslot(slot);
+      // 128 rows x 64 elements: thread t takes half t & 1 of row t / 2 (16
+      // code bytes at byte 32 row + 16 half, one absmax)
+      const int row = tid >> 1, h = tid & 1;
+      const u32x4 cw = *reinterpret_cast<const u32x4*>(ws + row * 32 + 16 * h);
+      const float am = *reinterpret_cast<const float*>(ws + R::CODES + (row >> 6) * 256 + (row & 63) * 4);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = few_nf4_pair(tabl, (cw[c] >> (8 * q)) & 0xff, am);
+        // word c holds elements 8 (4 h + c) .. +7 = logical chunk 4 h + c
+        *reinterpret_cast<u32x4*>(wbf(b) + nt_off(row, 4 * h + c)) = o;
+      }
+    }
+  };
+
+  f32x4 acc[MB][NJ];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const char* xs, const char* wt) {
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep) {
+      bf16x8 bfr[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = nt_frag(wt, (BNF / 4) * wave + 16 * j, sstep, lane);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(xs, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+      }
+    }
+  };
+
+  // prologue: stages 0 .. NS - 2 in flight
+  few_unroll<NS - 1>([&](auto sc) {
+    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
+  });
+  if constexpr (NF4) {
+    if (nk > 0) {
+      few_wait_stages<PER>(min(NS - 2, nk - 1));
+      lds_barrier();
+      expand(0, 0);
+    }
+  }
+  // The stage loop, unrolled so that every ring slot and W tile index is a
+  // constant: the compiler then tells the slot being read from the slots
+  // still filling (with runtime indices it waited for every DMA in flight
+  // before each read of a landed slot).
+  constexpr int U = (NS % 2) ? 2 * NS : NS;
+  for (int t0 = 0; t0 < nk; t0 += U) {
+    few_unroll<U>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int t = t0 + j;
+      if (t >= nk) return;
+      if constexpr (NF4) {
+        // stage t + 1's codes have landed (all waves), stage t's bf16 tile is
+        // complete, and every wave is done with the slots refilled below
+        if (t + 1 < nk) few_wait_stages<PER>(min(NS - 3, nk - 2 - t));
+        lds_barrier();
+        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+        if (t + 1 < nk) expand((j + 1) % NS, (j + 1) & 1);
+        compute(xslot(j % NS), wbf(j & 1));
+      } else {
+        few_wait_stages<PER>(min(NS - 2, nk - 1 - t));
+        lds_barrier();
+        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+        compute(xslot(j % NS), wslot(j % NS));
+      }
+    });
+  }
+
+  // ---- partial of this chunk, then the last block of the tile finishes ----
+  const int N = p.d_out;
+  float* cp = p.Cp + (int64_t)kc * p.Mp * N;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * mb + 4 * g + v;
+        const int col = n0 + (BNF / 4) * wave + 16 * j + l16;
+        if (row < p.M && col < N) few_st_dev(cp + (int64_t)row * N + col, acc[mb][j][v]);
+      }
+  if (!few_last_arrival(p.cnt + nt, p.Sk, reinterpret_cast<int*>(smem + R::LDS - 16))) return;
+
+  // P_s = bf16(s X A^T) from the panel partials (fixed order)
+  char* ps = smem;
+  __syncthreads();
+  few_panel_sum<R::MP>(p.Pp, p.Sp, p, ps);
+  __syncthreads();
+  // rank term P_s B^T by MFMA (B rows are output columns, r8 contiguous)
+  const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)N * p.r8 * 2);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sstep = 0; sstep < 2; ++sstep) {
+    const int q = 32 * sstep + 8 * g;
+    bf16x8 bfr[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int col = n0 + (BNF / 4) * wave + 16 * j + l16;
+      bfr[j] = __builtin_bit_cast(
+          bf16x8, few_ld16(rbr, (col < N && q < p.r8) ? (uint32_t)(((int64_t)col * p.r8 + q) * 2) : OOB));
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8 af = nt_frag(ps, 16 * mb, sstep, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+    }
+  }
+  // the rank term to an fp32 tile [MP][BNF] (over P_s, once every wave is done with it)
+  __syncthreads();
+  float* tl = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * BNF + (BNF / 4) * wave + 16 * j + l16] = acc[mb][j][v];
+  __syncthreads();
+  few_finish<BNF>(p, tl, n0, N, p.Y, p.rope != 0);
+}
+
+__device__ __forceinline__ float nt_get(const char* tile, int r, int c) {
+  return bf2f(*reinterpret_cast<const uint16_t*>(tile + nt_off(r, c >> 3) + 2 * (c & 7)));
+}
+
+// ---------------------------------------------------------------------------
+// launch 2, backward: dX = G W + Q_s A (partials over chunks of d_out, the
+// last block of a tile of 128 input-gradient columns finishes), dB rows of
+// the stages a block owns, dA rows of the block's columns.
+// Block (blockIdx.x = tile of 128 columns of d_in, blockIdx.y = chunk of d_out).
+// ---------------------------------------------------------------------------
+template <int MB, bool NF4>
+__global__ void __launch_bounds__(few::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+few_bwd_kernel(const FewArgs p) {
+  using namespace few;
+  constexpr int NJ = 2;  // a wave's 32 columns
+  // (a stage's NF4 codes: 64 rows x 64 bytes, the size of 128 rows of 32)
+  using R0 = FewRing<MB, NF4, 128, 64 * 256>;
+  constexpr int PT = R0::MP * 128;  // one panel tile (NT, MP rows)
+  using R = FewRing<MB, NF4, 128, 64 * 256, 2 * PT>;
+  constexpr int NS = R::NS;
+  constexpr int WI = NF4 ? 1 : 4;  // bf16: 16 instructions of 4 rows x 256 bytes; NF4: 4 of 16 rows x 64 bytes
+  constexpr int PER = WI + R::XI + (NF4 ? 1 : 0);
+  static_assert(NS * R::STAGE >= 64 * 256 && (NF4 ? 2 * 64 * 256 + NF4_TAB_BYTES : NS * R::STAGE - 64 * 256) >=
+                    R::MP * 128 * 4,
+                "the finish reuses the ring (A tile) and the W tiles or the ring (rank tile)");
+  __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+  char* ring = smem + R::FIXED;
+  auto wslot = [&](int slot) { return ring + slot * R::STAGE; };
+  auto gslot = [&](int slot) { return ring + slot * R::STAGE + R::WSLOT; };
+  char* pst = smem;       // P_s (NT)
+  char* qst = smem + PT;  // Q_s (NT)
+  auto wbf = [&](int b) { return smem + 2 * PT + b * (64 * 256); };  // NF4: expanded W tiles (NN)
+  f32x2* tab2 = reinterpret_cast<f32x2*>(smem + 2 * PT + 2 * 64 * 256);
+  const f32x2* tabl = tab2 + (threadIdx.x & 15);
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const int nt = blockIdx.x, kc = blockIdx.y;
+  const int n0 = nt * 128;
+  const int k0 = kc * p.Kc;
+  const int k1 = min(p.d_out, k0 + p.Kc);
+  const int nk = (k1 - k0) / BK;
+  if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
+  // P_s and Q_s (bf16 [Mp, r8] from few_reduce_kernel) into NT tiles, zeros
+  // past Mp and r8
+  for (int e = tid; e < 2 * R::MP * 8; e += NT) {
+    const int which = e / (R::MP * 8), t = (e >> 3) % R::MP, c = e & 7;
+    const uint16_t* src = which ? p.Qs : p.Ps;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (t < p.Mp && 8 * c < p.r8) v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.r8 + 8 * c);
+    *reinterpret_cast<u32x4*>((which ? qst : pst) + nt_off(t, c)) = v;
+  }
+
+  const uint16_t* Gm = p.rope ? p.G : p.dY;
+  const __amdgpu_buffer_rsrc_t rg = few_rsrc(Gm, (int64_t)p.M * p.d_out * 2);
+  __amdgpu_buffer_rsrc_t rw, rc, ram;
+  if constexpr (NF4) {
+    rc = few_rsrc(p.codes, (int64_t)p.d_out * p.d_in / 2);
+    ram = few_rsrc(p.absmax, (int64_t)p.d_out * (p.d_in / 64) * 4);
+  } else {
+    rw = few_rsrc(p.W, (int64_t)p.d_out * p.d_in * 2);
+  }
+  const int drow = lane >> 3, dpc = lane & 7;
+  // the lanes' DMA offsets at stage 0 (stage st adds a scalar offset: 64
+  // more W rows, 64 more G columns)
+  uint32_t vw[WI], vam = OOB, vg[R::XI];
+  if constexpr (NF4) {
+    // codes: instruction j = wave moves rows 16 j .. 16 j + 15, 64 bytes
+    // (128 columns) each; the lane: row 16 j + lane / 4, quarter lane & 3
+    const int row = 16 * wave + (lane >> 2);
+    vw[0] = n0 + 32 * (lane & 3) < p.d_in
+                ? (uint32_t)((int64_t)(k0 + row) * (p.d_in / 2) + n0 / 2 + 16 * (lane & 3))
+                : OOB;
+    // absmax: entries e = 32 wave + lane (lanes < 32): row e / 2, block e & 1
+    const int e = 32 * wave + lane;
+    const int ab = n0 / 64 + (e & 1);
+    if (lane < 32 && ab < p.d_in / 64) vam = (uint32_t)(((int64_t)(k0 + (e >> 1)) * (p.d_in / 64) + ab) * 4);
+  } else {
+    // NN tile rows of 256 bytes: instruction j moves rows 4 j .. 4 j + 3; the
+    // lane lands at physical chunk lane & 15 of row 4 j + lane / 16
+#pragma unroll
+    for (int i = 0; i < WI; ++i) {
+      const int row = 4 * (WI * wave + i) + (lane >> 4);
+      const int pc = lane & 15, psg = pc >> 1;
+      const int lsg = (psg & ~3) | ((psg ^ row) & 3);
+      const int col = n0 + 8 * ((lsg << 1) | (pc & 1));
+      vw[i] = col < p.d_in ? (uint32_t)(((int64_t)(k0 + row) * p.d_in + col) * 2) : OOB;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R::XI; ++i) {
+    const int row = 8 * (wave + 4 * i) + drow;
+    vg[i] = row < p.M ? (uint32_t)((row * p.d_out + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+  }
+  auto issue = [&](int st, int slot) {
+    char* ws = wslot(slot);
+    if constexpr (NF4) {
+      few_dma(rc, ws + wave * 1024, vw[0], st * BK * (p.d_in / 2));
+      few_dma<4>(ram, ws + R::CODES + wave * 256, vam, st * BK * (p.d_in / 64) * 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WI; ++i) few_dma(rw, ws + (WI * wave + i) * 1024, vw[i], st * BK * p.d_in * 2);
+    }
+    char* gs = gslot(slot);
+#pragma unroll
+    for (int i = 0; i < R::XI; ++i) few_dma(rg, gs + (wave + 4 * i) * 1024, vg[i], st * (BK * 2));
+  };
+  // NF4: codes of stage st -> bf16 NN tile b: thread t expands row t / 4,
+  // columns 32 (t & 3) .. +31 (one absmax block half)
+  auto expand = [&](int slot, int b) {
+    if constexpr (NF4) {
+      const char* ws = wslot(slot);
+      const int row = tid >> 2, qt = tid & 3;
+      const u32x4 c = *reinterpret_cast<const u32x4*>(ws + (row >> 4) * 1024 + (row & 15) * 64 + 16 * qt);
+      const int e = 2 * row + (qt >> 1);
+      const float am = *reinterpret_cast<const float*>(ws + R::CODES + (e >> 5) * 256 + (e & 31) * 4);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = few_nf4_pair(tabl, (c[w] >> (8 * q)) & 0xff, am);
+        *reinterpret_cast<u32x4*>(wbf(b) + nn_off<256>(row, 4 * qt + w)) = o;
+      }
+    }
+  };
+
+  f32x4 acc[MB][NJ];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const char* gs, const char* wt) {
+    // the stage's W fragments of both 32-deep steps in one batch of reads
+    bf16x8 bfr[2 * NJ];
+    u32x2 ad[2 * NJ];
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) ad[NJ * sstep + j] = nn_frag_addr<256>(wt, 32 * sstep, 32 * wave + 16 * j, lane);
+    few_tr_frags<2 * NJ>(bfr, ad);
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(gs, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[NJ * sstep + j], acc[mb][j]);
+      }
+    }
+  };
+  // dB rows of stage st (G rows i of the stage meet all M tokens here): the
+  // stage's owner block (global stage index modulo the column tiles) writes
+  // dB[i, q] = sum_t G[t, i] P_s[t, q] = (G^T P_s)[i, q], an MFMA product over
+  // the tokens (zero rows past M): A = G^T read transposed from the G tile,
+  // B = P_s read transposed from its NT tile.  Wave w: rows 16 w .. + 15.
+  // P_s fragments for dB, read once (the tile does not change)
+  constexpr int KT = R::MP / 32;
+  bf16x8 pfr[KT][MAXR / 16];
+  auto load_pfr = [&]() {
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+      u32x2 ad[MAXR / 16];
+#pragma unroll
+      for (int nb = 0; nb < MAXR / 16; ++nb) ad[nb] = nt_tr_frag_addr(pst, 32 * k, 16 * nb, lane);
+      few_tr_frags<MAXR / 16>(pfr[k], ad);
+    }
+  };
+  auto db_rows = [&](int st, int slot) {
+    const int u = (k0 + st * BK) / BK;
+    if (u % p.n_tiles != nt) return;
+    const char* gs = gslot(slot);
+    f32x4 d[MAXR / 16];
+#pragma unroll
+    for (int nb = 0; nb < MAXR / 16; ++nb) d[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 af[KT];
+    u32x2 ad[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) ad[k] = nt_tr_frag_addr(gs, 32 * k, 16 * wave, lane);
+    few_tr_frags<KT>(af, ad);
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+#pragma unroll
+      for (int nb = 0; nb < MAXR / 16; ++nb)
+        if (16 * nb < p.r8) d[nb] = mfma16(af[k], pfr[k][nb], d[nb]);
+    const int i0 = k0 + st * BK + 16 * wave;
+#pragma unroll
+    for (int nb = 0; nb < MAXR / 16; ++nb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int q = 16 * nb + l16;
+        if (q < p.r8) p.dB[(int64_t)(i0 + 4 * g + v) * p.r8 + q] = d[nb][v];
+      }
+  };
+
+  // prologue: stages 0 .. NS - 2 in flight
+  few_unroll<NS - 1>([&](auto sc) {
+    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
+  });
+  lds_barrier();  // the P_s tile is written
+  load_pfr();
+  if constexpr (NF4) {
+    if (nk > 0) {
+      few_wait_stages<PER>(min(NS - 2, nk - 1));
+      lds_barrier();
+      expand(0, 0);
+    }
+  }
+  // unrolled as in the forward: constant slot and W tile indices
+  constexpr int U = (NS % 2) ? 2 * NS : NS;
+  for (int t0 = 0; t0 < nk; t0 += U) {
+    few_unroll<U>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int t = t0 + j;
+      if (t >= nk) return;
+      if constexpr (NF4) {
+        if (t + 1 < nk) few_wait_stages<PER>(min(NS - 3, nk - 2 - t));
+        lds_barrier();
+        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+        if (t + 1 < nk) expand((j + 1) % NS, (j + 1) & 1);
+        compute(gslot(j % NS), wbf(j & 1));
+      } else {
+        few_wait_stages<PER>(min(NS - 2, nk - 1 - t));
+        lds_barrier();
+        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+        compute(gslot(j % NS), wslot(j % NS));
+      }
+      db_rows(t, j % NS);
+    });
+  }
+
+  // dA[q, j] = sum_t Q_s[t, q] X[t, j] for the block's 128 columns j and the
+  // 16-rank blocks nb = kc, kc + Sk, ...: (X^T Q_s)[j, q] by MFMA over the
+  // tokens, X [MP rows, 128 columns] staged in the ring (NN layout, zeros past
+  // M and d_in), A = X^T and B = Q_s both read transposed.  Wave w: columns
+  // 32 w .. + 31.
+  {
+    char* xt = ring;
+    __syncthreads();  // every wave is done with the ring
+    for (int e = tid; e < R::MP * 16; e += NT) {
+      const int t = e >> 4, c = e & 15;
+      const int col = n0 + 8 * c;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t < p.M && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.X + (int64_t)t * p.d_in + col);
+      *reinterpret_cast<u32x4*>(xt + nn_off<256>(t, c)) = v;
+    }
+    __syncthreads();
+    for (int nb = kc; 16 * nb < p.r8; nb += p.Sk) {
+      f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int k = 0; k < R::MP / 32; ++k) {
+        const bf16x8 bq = nt_tr_frag(qst, 32 * k, 16 * nb, lane);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) d[j] = mfma16(nn_frag<256>(xt, 32 * k, 32 * wave + 16 * j, lane), bq, d[j]);
+      }
+      const int q = 16 * nb + l16;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int col = n0 + 32 * wave + 16 * j + 4 * g + v;
+          if (q < p.r8 && col < p.d_in) p.dA[(int64_t)q * p.d_in + col] = d[j][v];
+        }
+    }
+  }
+
+  // ---- partial of this chunk; the last block of the tile finishes ----
+  const int N = p.d_in;
+  float* cp = p.Cp + (int64_t)kc * p.Mp * N;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * mb + 4 * g + v;
+        const int col = n0 + 32 * wave + 16 * j + l16;
+        if (row < p.M && col < N) few_st_dev(cp + (int64_t)row * N + col, acc[mb][j][v]);
+      }
+  if (!few_last_arrival(p.cnt + nt, p.Sk, reinterpret_cast<int*>(smem + R::LDS - 16))) return;
+
+  // rank term Q_s A: A rows q (< r8) of the block's columns into an NN tile
+  // (rows past r8 and columns past d_in zero), read like W
+  char* at = ring;
+  __syncthreads();
+  for (int e = tid; e < 64 * 16; e += NT) {
+    const int q = e >> 4, c = e & 15;
+    const int col = n0 + 8 * c;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < p.r8 && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
+    *reinterpret_cast<u32x4*>(at + nn_off<256>(q, c)) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sstep = 0; sstep < 2; ++sstep) {
+    bf16x8 bfr[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) bfr[j] = nn_frag<256>(at, 32 * sstep, 32 * wave + 16 * j, lane);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8 af = nt_frag(qst, 16 * mb, sstep, lane);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+    }
+  }
+  // the rank term to an fp32 tile [MP][128]: over the expanded W tiles and
+  // the table (NF4), else past the A tile
+  float* tl = reinterpret_cast<float*>(NF4 ? smem + 2 * PT : ring + 64 * 256);
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * 128 + 32 * wave + 16 * j + l16] = acc[mb][j][v];
+  __syncthreads();
+  few_finish<128>(p, tl, n0, N, p.dX, false);
+}
+
+}  // namespace lora

@@ -12,6 +12,7 @@
 #include "gemm_w4_nt.h"
 #include "gemm_panel.h"
 #include "skinny.h"
+#include "few.h"
 #include "launch.h"
 
 namespace lora {
@@ -1053,6 +1054,52 @@ hipError_t run_skinny_mode(const SkinnyArgs& a, int mode, hipStream_t st) {
   return wide ? run_skinny<MB, 4, RB, sk::PLAIN>(a, st) : run_skinny<MB, 1, RB, sk::PLAIN>(a, st);
 }
 }  // namespace
+
+template <int MB>
+hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
+  if (what == 0) {
+    hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
+  } else if (what == 1) {
+    const dim3 grid((unsigned)a.n_tiles, (unsigned)a.Sk);
+    if (nf4)
+      hipLaunchKernelGGL((few_fwd_kernel<MB, true>), grid, dim3(few::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((few_fwd_kernel<MB, false>), grid, dim3(few::NT), 0, st, a);
+  } else {
+    const dim3 grid((unsigned)a.n_tiles, (unsigned)a.Sk);
+    if (nf4)
+      hipLaunchKernelGGL((few_bwd_kernel<MB, true>), grid, dim3(few::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((few_bwd_kernel<MB, false>), grid, dim3(few::NT), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t few_dispatch(const FewArgs& a, int MB, int what, bool nf4, hipStream_t st) {
+  if (a.M < 1 || a.M > 16 * MB || a.Mp != 16 * MB || a.r8 < 8 || a.r8 > few::MAXR || a.r8 % 8) return hipErrorInvalidValue;
+  if (a.Sp < 1 || a.Sk < 1 || a.n_tiles < 1) return hipErrorInvalidValue;
+  switch (MB) {
+    case 1: return few_launch<1>(a, what, nf4, st);
+    case 2: return few_launch<2>(a, what, nf4, st);
+    case 4: return few_launch<4>(a, what, nf4, st);
+    case 8: return few_launch<8>(a, what, nf4, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_few_panel(const FewArgs& a, int MB, hipStream_t st) { return few_dispatch(a, MB, 0, false, st); }
+hipError_t launch_few_reduce(const FewArgs& a, hipStream_t st) {
+  if (a.Mp < 16 || a.r8 % 8 || a.Sp < 1 || a.Sq < 1) return hipErrorInvalidValue;
+  const int nb = (a.Mp * a.r8 / 4 + few::NT - 1) / few::NT;
+  hipLaunchKernelGGL(few_reduce_kernel, dim3(2 * nb), dim3(few::NT), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_few_fwd(const FewArgs& a, int MB, bool nf4, hipStream_t st) {
+  return few_dispatch(a, MB, 1, nf4, st);
+}
+hipError_t launch_few_bwd(const FewArgs& a, int MB, bool nf4, hipStream_t st) {
+  return few_dispatch(a, MB, 2, nf4, st);
+}
 
 hipError_t launch_skinny_fwd(const SkinnyArgs& a, int mode, hipStream_t st) {
   // 16 or 64 rows of X, rank up to 16 or 64 (rows past M and rank columns

@@ -1,8 +1,9 @@
-"""GPU parity at few tokens.  The dX GEMM (and the forward beyond 64 tokens,
-or with a rank that is not a multiple of 8 or above 64) splits its
-contraction into fp32 partials (the 128x128 tiles alone would leave most CUs
-idle) and a fixed-order sum finishes them (with the RoPE rotation for q/k);
-up to 64 tokens the bf16 forward is one fused launch (skinny_fwd).  The profiler
+"""GPU parity at few tokens.  Outside the few-token path's range (its own
+tests cover it) the dX GEMM (and the forward beyond 64 tokens, or with a rank
+that is not a multiple of 8 or above 64) splits its contraction into fp32
+partials (the 128x128 tiles alone would leave most CUs idle) and a
+fixed-order sum finishes them (with the RoPE rotation for q/k); up to 64
+tokens the bf16 forward is one fused launch (skinny_fwd).  The profiler
 confirms which path ran; the oracle is the float64 reference as everywhere
 else."""
 import math
@@ -14,7 +15,7 @@ import torch
 import oracle as O
 from lora_linear_layers_amd import _lib
 from synth import gen
-from tests.helpers import TOL, cpu64, lora_inputs, rel
+from tests.helpers import TOL, cpu64, few_path, lora_inputs, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +45,10 @@ def test_small_token_parity(lib, shape):
     X, W, A, B, dY = lora_inputs(300 + M, M, d_in, d_out, r, "bf16")
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (lib.lora_linear_fwd(X, W, A, B, s),
                                                    lib.lora_linear_bwd(X, W, A, B, s, dY)))
-    assert {"gemm_bf16_128x128_nn_split", "split_finish"} <= kinds, kinds
+    if few_path(True, False, M, d_in, d_out, r):
+        assert "few_bwd" in kinds, kinds
+    else:
+        assert {"gemm_bf16_128x128_nn_split", "split_finish"} <= kinds, kinds
     assert ("skinny_fwd" if fused_fwd(M, r) else "gemm_bf16_128x128_nt_split") in kinds, kinds
     Yr = O.lora_forward(X, W, A, B, s)
     dXr, dAr, dBr = O.lora_backward(X, W, A, B, s, dY)
@@ -68,7 +72,7 @@ def test_small_token_rope_parity(lib, M, d_in, d_out, r, seq):
     s = 16.0 / r
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (lib.lora_qk_rope_fwd(X, W, A, B, s, pos, cos, sin),
                                                    lib.lora_qk_rope_bwd(X, W, A, B, s, pos, cos, sin, dY)))
-    assert "split_finish" in kinds, kinds
+    assert ("few_bwd" if few_path(True, False, M, d_in, d_out, r, rope=True) else "split_finish") in kinds, kinds
     assert ("skinny_fwd" if fused_fwd(M, r) else "gemm_bf16_128x128_nt_split") in kinds, kinds
     p = pos.cpu().numpy()
     Yr = O.qk_rope_forward(X, W, A, B, s, p)
@@ -88,7 +92,9 @@ def test_small_token_nf4_parity(lib, M, d_in, d_out, r):
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (
         lib.nf4_lora_linear_fwd(X, codes, absmax, tab, A, B, s, d_out),
         lib.nf4_lora_linear_bwd(X, codes, absmax, tab, A, B, s, dY)))
-    assert {"gemm_nf4_128x128_nt_split", "gemm_nf4_128x128_nn_split", "split_finish"} <= kinds, kinds
+    fwd_few, bwd_few = few_path(False, True, M, d_in, d_out, r), few_path(True, True, M, d_in, d_out, r)
+    assert ("few_fwd" if fwd_few else "gemm_nf4_128x128_nt_split") in kinds, kinds
+    assert ("few_bwd" if bwd_few else "gemm_nf4_128x128_nn_split") in kinds, kinds
     c, am = codes.cpu().numpy(), absmax.cpu().numpy()
     Yr = O.nf4_lora_forward(X, c, am, tab, A, B, s, d_out, d_in)
     dXr, dAr, dBr = O.nf4_lora_backward(X, c, am, tab, A, B, s, dY, d_out, d_in)
@@ -111,7 +117,7 @@ def test_small_token_integer_exact(lib):
         sp((M, d_out), 1 / 8)
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (lib.lora_linear_fwd(X, W, A, B, s),
                                                    lib.lora_linear_bwd(X, W, A, B, s, dY)))
-    assert {"skinny_fwd", "gemm_bf16_128x128_nn_split"} <= kinds, kinds
+    assert {"skinny_fwd", "few_bwd"} <= kinds, kinds
     Yr = O.lora_forward(X, W, A, B, s)
     dXr, dAr, dBr = O.lora_backward(X, W, A, B, s, dY)
     assert np.abs(O.lora_panel(X, A)).max() <= 256 and np.abs(cpu64(dY) @ cpu64(B)).max() <= 256
