@@ -57,22 +57,24 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct FewPlan {
   bool ok = false;
-  int MB = 0, Mp = 0, Sp = 0, Kp = 0, Sq = 0, Kq = 0, Sk = 0, Kc = 0, n_tiles = 0;
+  int MB = 0, Mp = 0, Sp = 0, Kp = 0, Sq = 0, Kq = 0, n_tiles = 0, nkt = 0, T = 0, nblk = 0;
   size_t pp = 0, qp = 0, cp = 0, cnt = 0, g = 0, ps = 0, qs = 0, total = 0;
 };
 
 // bf16, 1 <= M <= 128, r a multiple of 8 up to 64, d_in and d_out multiples
-// of 64 (128 for RoPE), every byte offset of an operand below 2^30.  Blocks:
-// the forward's column tiles (128 of d_out) or the backward's (128 of d_in)
-// times chunks of the contraction chosen for about 384 blocks (each
-// chunk at least 256 long).  P in at most 16 chunks of d_in (the forward's
-// finishing blocks sum them with every load in flight); Q in at most 32
-// chunks of d_out of whole 128-row heads (summed with P between the
-// backward's launches, every slab's load in flight).
+// of 64 (d_in of 128 in the backward, whole column tiles, and with NF4; d_out
+// of 128 with RoPE),
+// every byte offset of an operand below 2^30.  Launch 2: the column tiles (128
+// of d_out forward, of d_in backward) times their 64-wide contraction stages,
+// cut into few::GRID equal contiguous ranges, one block each (at most as
+// many tiles as blocks, so a range covers one tile or two).  P in at most 16
+// chunks of d_in (the forward's finishing blocks sum them with every load in
+// flight); Q in at most 32 chunks of d_out of whole 128-row heads (summed with
+// P between the backward's launches, every slab's load in flight).
 FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
   FewPlan F;
   if (M < 1 || M > 16 * few::MAXMB || r % 8 || r > few::MAXR || d_in % 64 || d_out % 64) return F;
-  if (rope && d_out % 128) return F;
+  if ((rope && d_out % 128) || ((bwd || nf4) && d_in % 128)) return F;
   const int64_t lim = int64_t(1) << 30;
   if (d_in * d_out * 2 >= lim || M * std::max(d_in, d_out) * 2 >= lim) return F;
   // taken where it measured faster on MI355X than the skinny and split-GEMM
@@ -84,11 +86,10 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   F.Mp = 16 * F.MB;
   const int64_t ncols = bwd ? d_in : d_out, K = bwd ? d_out : d_in;
   F.n_tiles = (int)cdiv(ncols, few::BN);
-  int64_t sk = cdiv(384, F.n_tiles);
-  sk = std::min(sk, std::max<int64_t>(1, K / 256));
-  const int64_t kc = rup(cdiv(K, sk), 64);
-  F.Kc = (int)kc;
-  F.Sk = (int)cdiv(K, kc);
+  if (F.n_tiles > few::GRID) return F;
+  F.nkt = (int)(K / (nf4 && !bwd ? 2 * few::BK : few::BK));  // the NF4 forward's stages are 128 deep
+  F.T = F.n_tiles * F.nkt;
+  F.nblk = std::min(few::GRID, F.T);
   F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, 16), 128));
   F.Sp = (int)cdiv(d_in, F.Kp);
   if (bwd) {
@@ -103,7 +104,7 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   };
   F.pp = take(size_t(F.Sp) * F.Mp * r * 4);
   F.qp = take(size_t(F.Sq) * F.Mp * r * 4);
-  F.cp = take(size_t(F.Sk) * F.Mp * ncols * 4);
+  F.cp = take(size_t(F.nblk + F.n_tiles - 1) * F.Mp * few::BN * 4);
   F.cnt = take(size_t(F.n_tiles) * 4);
   if (bwd && rope) F.g = take(size_t(M) * d_out * 2);
   if (bwd) {
@@ -487,7 +488,8 @@ FewArgs few_args(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64
   a.Qp = reinterpret_cast<float*>(w + F.qp);
   a.Cp = reinterpret_cast<float*>(w + F.cp);
   a.cnt = reinterpret_cast<int*>(w + F.cnt);
-  a.Sp = F.Sp; a.Kp = F.Kp; a.Sq = F.Sq; a.Kq = F.Kq; a.Sk = F.Sk; a.Kc = F.Kc; a.n_tiles = F.n_tiles;
+  a.Sp = F.Sp; a.Kp = F.Kp; a.Sq = F.Sq; a.Kq = F.Kq;
+  a.n_tiles = F.n_tiles; a.nkt = F.nkt; a.T = F.T; a.nblk = F.nblk;
   return a;
 }
 

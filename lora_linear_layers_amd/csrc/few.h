@@ -1,5 +1,5 @@
-// few.h - the fused LoRA layer for few tokens (M <= 128, bf16 activations)
-// in two launches per direction.
+// few.h - the fused LoRA layer for few tokens (M <= 128, bf16 activations):
+// the NF4 forward in two launches, the backward in three.
 //
 //     forward   Y  = X W^T + bf16(s X A^T) B^T           (page "UnSloth加速微调
 //     backward  dX = G W + bf16(s G B) A,                  体验…", sections 算子融合
@@ -15,21 +15,21 @@
 //     chunks of their contraction, P = X A^T (both directions) and, in the
 //     backward, Q = G B; with RoPE it forms G from dY on load, rotating each
 //     head's pairs (i, i + 64) by the negated angle, and stores G for launch
-//     2.  It also clears launch 2's arrival counters.
-//   launch 2 (few_fwd_kernel / few_bwd_kernel): a block owns 128 output
-//     columns and one chunk of the contraction.  W tiles stream through a
-//     ring of LDS stages loaded by DMA (buffer_load ... lds, whole 128- or
-//     256-byte rows, so every request is whole cache lines); NF4 codes stream
-//     the same way and are expanded to bf16 in LDS with the load stage's own
-//     byte -> bf16 pair routine (bit-equal to nf4_dequant).  The block's fp32
-//     partial of its output tile goes to the workspace; the LAST block of a
-//     column tile to arrive (an atomic counter, device-scope release and
-//     acquire fences) sums the partials in chunk order, so the result does
-//     not depend on arrival order, adds the rank term (P_s B^T, or Q_s A:
-//     P_s = bf16(s P) and Q_s = bf16(s Q) summed from launch 1's partials in
-//     fixed order), applies RoPE or stores.  The backward's blocks also
-//     produce dB rows (every G row of a stage meets all M tokens inside one
-//     block, so dB needs no partials) and dA columns as side work.
+//     2.  It also clears the W stream's arrival counters.  The backward then
+//     sums the panels once (few_reduce_kernel): P_s = bf16(s P), Q_s = bf16(s Q).
+//   the W stream (few_fwd_nf4_kernel / few_bwd_kernel): column tiles of 128
+//     outputs, each a sequence of contraction stages; the tiles' stages in
+//     sequence are cut into 256 equal contiguous ranges, one block (one CU)
+//     each, so every CU streams the same share of W in one round.  W stages
+//     land in a ring of LDS slots by DMA (buffer_load ... lds), the stage's
+//     resource based at its tile so rows past the end read zero.  A block
+//     leaves one fp32 partial per tile it touches (at most two); the LAST
+//     block of a tile to arrive (an atomic counter; partials written and
+//     read with device-scope loads and stores) sums the tile's partials in
+//     block order, so the result does not depend on arrival order, adds the
+//     rank term (P_s B^T, or Q_s A) and applies RoPE or stores.  The
+//     backward's blocks also produce dB rows (every G row of a stage meets all
+//     M tokens inside one block, so dB needs no partials) and dA columns.
 //
 // MFMA v_mfma_f32_16x16x32_bf16.  A lane l holds row l % 16, contraction
 // 8 (l / 16) .. +7; B lane l holds column l % 16, the same contraction; the 4
@@ -390,8 +390,8 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 // copy measured about 2x more bank-conflict cycles than LDS cycles).
 constexpr int NF4_TAB_BYTES = 256 * 16 * 8;
 
-__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float* table) {
-  for (int t = threadIdx.x; t < 256 * 16; t += few::NT) {
+__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float* table, int nth = few::NT) {
+  for (int t = threadIdx.x; t < 256 * 16; t += nth) {
     const int b = t >> 4;
     tab[t] = f32x2{table[b >> 4], table[b & 15]};
   }
@@ -442,20 +442,45 @@ __device__ __forceinline__ float few_ld_dev(const float* q) {
   return __hip_atomic_load(const_cast<float*>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The finishing handshake: every thread waits until its partial stores have
-// been performed at the coherence point (vmcnt), the block meets, then one
-// device-scope atomic per block; true in the last block of the tile, whose
-// device-scope loads (issued only after that atomic has returned) then see
-// every other block's partial.
-__device__ __forceinline__ bool few_last_arrival(int* cnt, int total, int* flag) {
+// The work split of launch 2: the tiles' stages in sequence (a tile's in
+// contraction order, tiles in order), block b of nblk taking the contiguous
+// range [b T / nblk, (b + 1) T / nblk).  With n_tiles <= nblk a range holds at most
+// nkt stages, so it covers one tile or the end of one and the start of the
+// next.  nk: the range's stages; a0: its first tile; s0: the first stage's
+// index in that tile; te: the local index of tile a0's last stage in the range
+// (nk - 1 when the range stays in a0).
+struct FewSpan {
+  int nk, a0, s0, te;
+};
+__device__ __forceinline__ FewSpan few_span(const FewArgs& p, int b) {
+  const int g0 = (int)((int64_t)b * p.T / p.nblk), g1 = (int)((int64_t)(b + 1) * p.T / p.nblk);
+  FewSpan s;
+  s.nk = g1 - g0;
+  s.a0 = g0 / p.nkt;
+  s.s0 = g0 - s.a0 * p.nkt;
+  s.te = min(s.nk, p.nkt - s.s0) - 1;
+  return s;
+}
+// the block whose range holds stage x: the largest b with b T / nblk <= x
+__device__ __forceinline__ int few_blk_of(const FewArgs& p, int x) {
+  return (int)(((int64_t)(x + 1) * p.nblk - 1) / p.T);
+}
+
+// The finishing handshake, after every partial store of the block: each
+// thread waits until its stores have been performed at the coherence point
+// (vmcnt), the block meets, then one device-scope atomic per tile the block
+// covers (n of them, the tiles' counters at cnt); flag[i] is set in the block
+// that arrives last at tile i, whose device-scope loads (issued only after
+// that atomic has returned) then see every other block's partial.  total(i):
+// the blocks of tile i.
+template <class F>
+__device__ __forceinline__ void few_arrive(int* cnt, int n, F total, int* flag) {
   __builtin_amdgcn_s_waitcnt(few::vmcnt_imm(0));
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = prev == total - 1;
-  }
+  if (threadIdx.x == 0)
+    for (int i = 0; i < n; ++i)
+      flag[i] = __hip_atomic_fetch_add(cnt + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == total(i) - 1;
   __syncthreads();
-  return *flag != 0;
 }
 
 // f(integral_constant<int, j>) for j = 0 .. U-1, in order
@@ -516,21 +541,21 @@ __device__ __forceinline__ void few_sum4(const float* src, int S, int64_t zstrid
 // bf16(s * sum over z < S of part[z][t][q]) into an NT tile of MP rows and 64
 // columns (zeros past M and r8): four columns per item, up to four items of
 // a thread summed together
-template <int MP>
+template <int MP, int NTH = few::NT>
 __device__ __forceinline__ void few_panel_sum(const float* part, int S, const FewArgs& p, char* tile) {
   constexpr int ITEMS = MP * 16;
-  for (int i0 = threadIdx.x; i0 < ITEMS; i0 += 4 * few::NT) {
+  for (int i0 = threadIdx.x; i0 < ITEMS; i0 += 4 * NTH) {
     int64_t off[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int it = i0 + i * few::NT, t = it >> 4, q = 4 * (it & 15);
+      const int it = i0 + i * NTH, t = it >> 4, q = 4 * (it & 15);
       off[i] = (it < ITEMS && t < p.M && q < p.r8) ? (int64_t)t * p.r8 + q : -1;
     }
     float4 a[4];
     few_sum4<4>(part, S, (int64_t)p.Mp * p.r8, off, a);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int it = i0 + i * few::NT, t = it >> 4, q = 4 * (it & 15);
+      const int it = i0 + i * NTH, t = it >> 4, q = 4 * (it & 15);
       if (it >= ITEMS) continue;
       const uint2 v = make_uint2(pack_bf16x2(p.s * a[i].x, p.s * a[i].y), pack_bf16x2(p.s * a[i].z, p.s * a[i].w));
       *reinterpret_cast<uint2*>(tile + nt_off(t, q >> 3) + 2 * (q & 7)) = v;
@@ -570,27 +595,29 @@ __device__ __forceinline__ void few_sum4_dev(const float* src, int S, int64_t zs
 // rank term (an fp32 tile [MP][BNT] in LDS, in the same columns), then bf16
 // stores of four columns per item, or, with RoPE (BNT = 128, one head), the
 // rotation of the pairs (f, f + 64) of each row.
-template <int BNT>
-__device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, int n0, int N, uint16_t* out,
-                                           bool rope) {
-  const int64_t zs = (int64_t)p.Mp * N;
+// part: the tile's first partial slab ([Mp][BNT] each, S of them, summed in
+// slab order).
+template <int BNT, int NTH = few::NT>
+__device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, const float* part, int S, int n0,
+                                           int N, uint16_t* out, bool rope) {
+  const int64_t zs = (int64_t)p.Mp * BNT;
   if (!rope) {
     const int items = p.M * (BNT / 4);
-    for (int i0 = threadIdx.x; i0 < items; i0 += 4 * few::NT) {
+    for (int i0 = threadIdx.x; i0 < items; i0 += 4 * NTH) {
       int64_t off[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int it = i0 + i * few::NT, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
-        off[i] = (it < items && n0 + c < N) ? (int64_t)t * N + n0 + c : -1;
+        const int it = i0 + i * NTH, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
+        off[i] = (it < items && n0 + c < N) ? (int64_t)t * BNT + c : -1;
       }
       float4 a[4];
-      few_sum4_dev<4>(p.Cp, p.Sk, zs, off, a);
+      few_sum4_dev<4>(part, S, zs, off, a);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (off[i] < 0) continue;
-        const int it = i0 + i * few::NT, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
+        const int it = i0 + i * NTH, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
         const float* r = tl + t * BNT + c;
-        *reinterpret_cast<uint2*>(out + off[i]) =
+        *reinterpret_cast<uint2*>(out + (int64_t)t * N + n0 + c) =
             make_uint2(pack_bf16x2(a[i].x + r[0], a[i].y + r[1]), pack_bf16x2(a[i].z + r[2], a[i].w + r[3]));
       }
     }
@@ -598,19 +625,19 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, in
   }
   // RoPE: item = (row t, frequencies f .. f + 3); both halves summed
   const int items = p.M * 16;
-  for (int i0 = threadIdx.x; i0 < items; i0 += 2 * few::NT) {
+  for (int i0 = threadIdx.x; i0 < items; i0 += 2 * NTH) {
     int64_t off[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int it = i0 + i * few::NT, t = it >> 4, f = 4 * (it & 15);
-      off[2 * i] = it < items ? (int64_t)t * N + n0 + f : -1;
-      off[2 * i + 1] = it < items ? (int64_t)t * N + n0 + f + 64 : -1;
+      const int it = i0 + i * NTH, t = it >> 4, f = 4 * (it & 15);
+      off[2 * i] = it < items ? (int64_t)t * BNT + f : -1;
+      off[2 * i + 1] = it < items ? (int64_t)t * BNT + f + 64 : -1;
     }
     float4 a[4];
-    few_sum4_dev<4>(p.Cp, p.Sk, zs, off, a);
+    few_sum4_dev<4>(part, S, zs, off, a);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int it = i0 + i * few::NT, t = it >> 4, f = 4 * (it & 15);
+      const int it = i0 + i * NTH, t = it >> 4, f = 4 * (it & 15);
       if (it >= items) continue;
       float4 c, sn;
       few_cs4(p, t, f, c, sn);
@@ -624,9 +651,9 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, in
         y1[e] = u * cc[e] - w * ss[e];
         y2[e] = w * cc[e] + u * ss[e];
       }
-      *reinterpret_cast<uint2*>(out + off[2 * i]) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
-      *reinterpret_cast<uint2*>(out + off[2 * i + 1]) =
-          make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
+      uint16_t* o = out + (int64_t)t * N + n0 + f;
+      *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
+      *reinterpret_cast<uint2*>(o + 64) = make_uint2(pack_bf16x2(y2[0], y2[1]), pack_bf16x2(y2[2], y2[3]));
     }
   }
 }
@@ -653,192 +680,25 @@ __global__ void __launch_bounds__(few::NT) few_reduce_kernel(const FewArgs p) {
         make_uint2(pack_bf16x2(p.s * a[0].x, p.s * a[0].y), pack_bf16x2(p.s * a[0].z, p.s * a[0].w));
 }
 
-// ---------------------------------------------------------------------------
-// launch 2, forward: Y = X W^T + P_s B^T, then store or RoPE.
-// Block (blockIdx.x = tile of BNF output columns, blockIdx.y = chunk of d_in).
-// 128 columns (4 waves x 32).
-// ---------------------------------------------------------------------------
-template <int MB, bool NF4>
-__global__ void __launch_bounds__(few::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-few_fwd_kernel(const FewArgs p) {
+// The forward's finish of tile a, in the block that arrived there last: P_s
+// = bf16(s X A^T) from the panel partials, the rank term P_s B^T of the tile's
+// columns by MFMA into an fp32 tile in LDS, then the tile's partial slabs
+// summed in block order plus that term, stored or rotated (few_finish).
+template <int MB, int MP, int NW = 4>
+__device__ __forceinline__ void few_fwd_finish(const FewArgs& p, char* smem, int a) {
   using namespace few;
-  constexpr int BNF = 128;               // output columns of the block
-  constexpr int NJ = BNF / 64;          // 16-column blocks per wave
-  using R = FewRing<MB, NF4, BNF, BNF * 128>;
-  constexpr int NS = R::NS;
-  constexpr int WI = NF4 ? BNF / 128 : BNF / 32;  // W DMAs per wave per stage (8 rows of bf16, 32 rows of codes)
-  constexpr int PER = WI + R::XI + (NF4 ? 1 : 0);
-  static_assert(R::LDS >= R::MP * BNF * 4 && R::LDS >= R::MP * 128, "the finish reuses the LDS");
-  __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
-  char* ring = smem + R::FIXED;
-  auto wslot = [&](int slot) { return ring + slot * R::STAGE; };
-  auto xslot = [&](int slot) { return ring + slot * R::STAGE + R::WSLOT; };
-  auto wbf = [&](int b) { return smem + b * (BNF * 128); };  // NF4: expanded bf16 W tiles
-  f32x2* tab2 = reinterpret_cast<f32x2*>(smem + 2 * BNF * 128);
-  const f32x2* tabl = tab2 + (threadIdx.x & 15);
-
+  constexpr int BNF = 128, CW = BNF / NW, NJ = CW / 16, NTH = 64 * NW;  // CW: columns per wave
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int nt = blockIdx.x, kc = blockIdx.y;
-  const int n0 = nt * BNF;
-  const int k0 = kc * p.Kc;
-  const int k1 = min(p.d_in, k0 + p.Kc);
-  const int nk = (k1 - k0) / BK;
-  if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
-
-  const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
-  __amdgpu_buffer_rsrc_t rw, rc, ram;
-  if constexpr (NF4) {
-    rc = few_rsrc(p.codes, (int64_t)p.d_out * p.d_in / 2);
-    ram = few_rsrc(p.absmax, (int64_t)p.d_out * (p.d_in / 64) * 4);
-  } else {
-    rw = few_rsrc(p.W, (int64_t)p.d_out * p.d_in * 2);
-  }
-  // DMA lane mapping of an NT tile: 8 rows x 128 bytes per instruction, the
-  // lane lands at physical chunk lane & 7 of row lane / 8 and so fetches
-  // logical chunk (lane & 7) ^ (row & 7)
-  const int drow = lane >> 3, dpc = lane & 7;
-  // the lanes' DMA offsets at stage 0 (stage st adds a scalar offset)
-  uint32_t vw[WI], vam = OOB, vx[R::XI];
-  if constexpr (NF4) {
-    // codes: instruction j moves rows 32 j .. 32 j + 31, 32 bytes each (the
-    // lane: row 32 j + lane / 2, half lane & 1), landing at byte 32 row + 16 half
-#pragma unroll
-    for (int i = 0; i < WI; ++i) {
-      const int n = n0 + 32 * (WI * wave + i) + (lane >> 1);
-      vw[i] = n < p.d_out ? (uint32_t)((int64_t)n * (p.d_in / 2) + k0 / 2 + 16 * (lane & 1)) : OOB;
-    }
-    // absmax of rows 64 wave .. + 63 (4 bytes per lane)
-    const int ar = 64 * wave + lane, na = n0 + ar;
-    if (ar < BNF && na < p.d_out) vam = (uint32_t)(((int64_t)na * (p.d_in / 64) + k0 / 64) * 4);
-  } else {
-#pragma unroll
-    for (int i = 0; i < WI; ++i) {
-      const int row = 8 * (WI * wave + i) + drow;
-      const int n = n0 + row;
-      vw[i] = n < p.d_out ? (uint32_t)(((int64_t)n * p.d_in + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < R::XI; ++i) {
-    const int row = 8 * (wave + 4 * i) + drow;  // instruction wave + 4 i: rows 8 j .. 8 j + 7
-    vx[i] = row < p.M ? (uint32_t)((row * p.d_in + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
-  }
-  auto issue = [&](int st, int slot) {
-    char* ws = wslot(slot);
-    if constexpr (NF4) {
-#pragma unroll
-      for (int i = 0; i < WI; ++i) few_dma(rc, ws + (WI * wave + i) * 1024, vw[i], st * (BK / 2));
-      few_dma<4>(ram, ws + R::CODES + wave * 256, vam, st * 4);
-    } else {
-#pragma unroll
-      for (int i = 0; i < WI; ++i) few_dma(rw, ws + (WI * wave + i) * 1024, vw[i], st * (BK * 2));
-    }
-    char* xs = xslot(slot);
-#pragma unroll
-    for (int i = 0; i < R::XI; ++i) few_dma(rx, xs + (wave + 4 * i) * 1024, vx[i], st * (BK * 2));
-  };
-  // NF4: codes and absmax of stage st -> bf16 W tile b (NT layout)
-  auto expand = [&](int slot, int b) {
-    if constexpr (NF4) {
-      const char* ws = wslot(slot);
-      // 128 rows x 64 elements: thread t takes half t & 1 of row t / 2 (16
-      // code bytes at byte 32 row + 16 half, one absmax)
-      const int row = tid >> 1, h = tid & 1;
-      const u32x4 cw = *reinterpret_cast<const u32x4*>(ws + row * 32 + 16 * h);
-      const float am = *reinterpret_cast<const float*>(ws + R::CODES + (row >> 6) * 256 + (row & 63) * 4);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u32x4 o;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = few_nf4_pair(tabl, (cw[c] >> (8 * q)) & 0xff, am);
-        // word c holds elements 8 (4 h + c) .. +7 = logical chunk 4 h + c
-        *reinterpret_cast<u32x4*>(wbf(b) + nt_off(row, 4 * h + c)) = o;
-      }
-    }
-  };
-
-  f32x4 acc[MB][NJ];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const char* xs, const char* wt) {
-#pragma unroll
-    for (int sstep = 0; sstep < 2; ++sstep) {
-      bf16x8 bfr[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = nt_frag(wt, (BNF / 4) * wave + 16 * j, sstep, lane);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 af = nt_frag(xs, 16 * mb, sstep, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
-      }
-    }
-  };
-
-  // prologue: stages 0 .. NS - 2 in flight
-  few_unroll<NS - 1>([&](auto sc) {
-    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
-  });
-  if constexpr (NF4) {
-    if (nk > 0) {
-      few_wait_stages<PER>(min(NS - 2, nk - 1));
-      lds_barrier();
-      expand(0, 0);
-    }
-  }
-  // The stage loop, unrolled so that every ring slot and W tile index is a
-  // constant: the compiler then tells the slot being read from the slots
-  // still filling (with runtime indices it waited for every DMA in flight
-  // before each read of a landed slot).
-  constexpr int U = (NS % 2) ? 2 * NS : NS;
-  for (int t0 = 0; t0 < nk; t0 += U) {
-    few_unroll<U>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const int t = t0 + j;
-      if (t >= nk) return;
-      if constexpr (NF4) {
-        // stage t + 1's codes have landed (all waves), stage t's bf16 tile is
-        // complete, and every wave is done with the slots refilled below
-        if (t + 1 < nk) few_wait_stages<PER>(min(NS - 3, nk - 2 - t));
-        lds_barrier();
-        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
-        if (t + 1 < nk) expand((j + 1) % NS, (j + 1) & 1);
-        compute(xslot(j % NS), wbf(j & 1));
-      } else {
-        few_wait_stages<PER>(min(NS - 2, nk - 1 - t));
-        lds_barrier();
-        if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
-        compute(xslot(j % NS), wslot(j % NS));
-      }
-    });
-  }
-
-  // ---- partial of this chunk, then the last block of the tile finishes ----
-  const int N = p.d_out;
-  float* cp = p.Cp + (int64_t)kc * p.Mp * N;
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 16 * mb + 4 * g + v;
-        const int col = n0 + (BNF / 4) * wave + 16 * j + l16;
-        if (row < p.M && col < N) few_st_dev(cp + (int64_t)row * N + col, acc[mb][j][v]);
-      }
-  if (!few_last_arrival(p.cnt + nt, p.Sk, reinterpret_cast<int*>(smem + R::LDS - 16))) return;
-
-  // P_s = bf16(s X A^T) from the panel partials (fixed order)
+  const int N = p.d_out, n0 = a * BNF;
   char* ps = smem;
   __syncthreads();
-  few_panel_sum<R::MP>(p.Pp, p.Sp, p, ps);
+  few_panel_sum<MP, NTH>(p.Pp, p.Sp, p, ps);
   __syncthreads();
   // rank term P_s B^T by MFMA (B rows are output columns, r8 contiguous)
   const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)N * p.r8 * 2);
+  f32x4 acc[MB][NJ];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -849,7 +709,7 @@ few_fwd_kernel(const FewArgs p) {
     bf16x8 bfr[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + (BNF / 4) * wave + 16 * j + l16;
+      const int col = n0 + CW * wave + 16 * j + l16;
       bfr[j] = __builtin_bit_cast(
           bf16x8, few_ld16(rbr, (col < N && q < p.r8) ? (uint32_t)(((int64_t)col * p.r8 + q) * 2) : OOB));
     }
@@ -868,9 +728,191 @@ few_fwd_kernel(const FewArgs p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * BNF + (BNF / 4) * wave + 16 * j + l16] = acc[mb][j][v];
+      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * BNF + CW * wave + 16 * j + l16] = acc[mb][j][v];
   __syncthreads();
-  few_finish<BNF>(p, tl, n0, N, p.Y, p.rope != 0);
+  const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
+  few_finish<BNF, NTH>(p, tl, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, n0, N, p.Y, p.rope != 0);
+}
+
+// ---------------------------------------------------------------------------
+// launch 2, forward with an NF4 W.  Stages of 128 contraction steps (64 code
+// bytes and two absmax per W row); codes, absmax and the activations land in
+// LDS by DMA, and each lane expands the code bytes of its own MFMA B fragments
+// through the byte -> pair table: no expanded bf16 tile, one barrier a stage.
+// The expansion is VALU work of the order of the stream time, so the block
+// has 8 waves (two per SIMD, one overlapping the other's waits), 16 columns
+// each.  A tile: 128 output columns; its stages: the 128-wide steps of d_in;
+// block b streams its range of the stage sequence (few_span), so every CU the
+// same share of W; one partial per (block, tile) and the last block to arrive
+// at a tile finishes it (few_fwd_finish).
+// ---------------------------------------------------------------------------
+namespace few {
+constexpr int NW4 = 8;           // waves of the NF4 forward block
+constexpr int NT4 = 64 * NW4;    // its threads
+}  // namespace few
+
+template <int MB>
+struct FewNf4Ring {
+  static constexpr int MP = MB <= 2 ? 32 : (MB <= 4 ? 64 : 128);  // activation rows in LDS
+  static constexpr int XI = MP / 32;       // activation DMAs per wave per stage (two 64-wide NT sub-tiles)
+  static constexpr int CODES = 128 * 64;   // 8 blocks of 16 rows x 64 bytes
+  static constexpr int AM = 8 * 256;       // 8 blocks of 16 rows x 2 absmax (and 128 unused bytes)
+  static constexpr int XSLOT = 2 * MP * 128;
+  static constexpr int STAGE = CODES + AM + XSLOT;
+  static constexpr int FIXED = NF4_TAB_BYTES;
+  static constexpr int NS0 = (160 * 1024 - 256 - 16 - FIXED) / STAGE;
+  static constexpr int NS = NS0 > 8 ? 8 : NS0;
+  static constexpr int LDS = FIXED + NS * STAGE + 16;  // (+16: the handshake flags)
+  static_assert(NS >= 3, "at least three stages");
+};
+
+template <int MB>
+__global__ void __launch_bounds__(few::NT4) __attribute__((amdgpu_waves_per_eu(2, 2)))
+few_fwd_nf4_kernel(const FewArgs p) {
+  using namespace few;
+  using R = FewNf4Ring<MB>;
+  constexpr int NS = R::NS, BNF = 128, BKS = 128;
+  constexpr int PER = 2 + R::XI;  // DMAs per wave per stage: codes, absmax, activations
+  static_assert(R::LDS >= R::MP * BNF * 4, "the finish reuses the LDS");
+  __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+  f32x2* tab2 = reinterpret_cast<f32x2*>(smem);  // at LDS address 0
+  char* ring = smem + R::FIXED;
+  auto cslot = [&](int s) { return ring + s * R::STAGE; };
+  auto aslot = [&](int s) { return ring + s * R::STAGE + R::CODES; };
+  auto xslot = [&](int s) { return ring + s * R::STAGE + R::CODES + R::AM; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const FewSpan sp = few_span(p, blockIdx.x);
+  const int nk = sp.nk;
+  const bool two = sp.te < nk - 1;
+  few_fill_tab(tab2, p.nf4_table, NT4);  // read after the first stage barrier
+  // the lane's copy of the pair table: byte b's entry at 128 b + 8 (lane % 16)
+  const uint32_t rep = 8 * l16;
+
+  const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
+  // codes and absmax of the block's two tiles, each resource based at the
+  // tile's first row: rows past d_out lie past its end and read zero
+  const int64_t cb = p.d_in / 2, ab = p.d_in / 64;
+  const int64_t r0 = (int64_t)sp.a0 * BNF, r1 = (int64_t)min(sp.a0 + 1, p.n_tiles - 1) * BNF;
+  const __amdgpu_buffer_rsrc_t rc0 = few_rsrc(p.codes + r0 * cb, (p.d_out - r0) * cb);
+  const __amdgpu_buffer_rsrc_t rc1 = few_rsrc(p.codes + r1 * cb, (p.d_out - r1) * cb);
+  const __amdgpu_buffer_rsrc_t ra0 = few_rsrc(p.absmax + r0 * ab, (p.d_out - r0) * ab * 4);
+  const __amdgpu_buffer_rsrc_t ra1 = few_rsrc(p.absmax + r1 * ab, (p.d_out - r1) * ab * 4);
+  // Lane offsets at the tile's stage 0 (stage st adds a scalar offset).
+  // Codes: wave w's block holds rows 16 w .. + 15; lane L fetches the quarter
+  // L / 16 (32 elements) of row 16 w + L % 16 and lands at byte 256 (L / 16) +
+  // 16 (L % 16) of the block, so that a fragment read (16 rows, one dword each
+  // of one quarter) touches 64 different banks.
+  const uint32_t vc = (uint32_t)((16 * wave + l16) * cb + 16 * g);
+  // absmax: lane L < 32 of wave w takes row 16 w + L % 16, block L / 16
+  const uint32_t vam = lane < 32 ? (uint32_t)(((16 * wave + l16) * ab + (lane >> 4)) * 4) : OOB;
+  // activations: instruction k = wave + 8 i moves rows 8 (k % (MP / 8)) .. + 7
+  // of sub-tile k / (MP / 8) (NT rows of 64 elements)
+  const int drow = lane >> 3, dpc = lane & 7;
+  uint32_t vx[R::XI];
+#pragma unroll
+  for (int i = 0; i < R::XI; ++i) {
+    const int k = wave + NW4 * i, sub = k / (R::MP / 8);
+    const int row = 8 * (k % (R::MP / 8)) + drow;
+    vx[i] = row < p.M ? (uint32_t)((row * p.d_in + 64 * sub + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+  }
+  auto issue = [&](int t, int slot) {
+    const bool second = t > sp.te;
+    const int st = second ? t - sp.te - 1 : sp.s0 + t;
+    few_dma(second ? rc1 : rc0, cslot(slot) + wave * 1024, vc, st * (BKS / 2));
+    few_dma<4>(second ? ra1 : ra0, aslot(slot) + wave * 256, vam, st * 8);
+#pragma unroll
+    for (int i = 0; i < R::XI; ++i) {
+      const int k = wave + NW4 * i;
+      few_dma(rx, xslot(slot) + (k / (R::MP / 8)) * (R::MP * 128) + (k % (R::MP / 8)) * 1024, vx[i], st * (BKS * 2));
+    }
+  };
+
+  f32x4 acc[MB], acc0[MB];  // acc0: tile a0's sum once the range has moved on
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = acc0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // The wave's columns 16 wave + l16 are the W rows of code block wave;
+  // fragment ss covers contraction 32 ss + 8 g .. + 7 of the stage: dword g of
+  // quarter ss, scaled by the row's absmax ss / 2.  Byte q of a code dword
+  // selects the pair-table entry at ((w >> (8 q - 7)) & 0x7f80) | rep.
+  auto compute = [&](int slot) {
+    const char* cs = cslot(slot) + wave * 1024 + 16 * l16 + 4 * g;
+    const char* as = aslot(slot) + wave * 256 + 4 * l16;
+    const char* xs = xslot(slot);
+    uint32_t cw[4];
+    float am[2];
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) cw[ss] = *reinterpret_cast<const uint32_t*>(cs + 256 * ss);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) am[h] = *reinterpret_cast<const float*>(as + 64 * h);
+#pragma unroll
+    for (int ss = 0; ss < 4; ++ss) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t off = ((q == 0 ? cw[ss] << 7 : cw[ss] >> (8 * q - 7)) & 0x7f80u) | rep;
+        const f32x2 tv = *reinterpret_cast<const f32x2*>(smem + off);
+        o[q] = pack_bf16x2(tv.x * am[ss >> 1], tv.y * am[ss >> 1]);
+      }
+      const bf16x8 bfr = __builtin_bit_cast(bf16x8, o);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        acc[mb] = mfma16(nt_frag(xs + (ss >> 1) * (R::MP * 128), 16 * mb, ss & 1, lane), bfr, acc[mb]);
+    }
+  };
+  auto tile_done = [&](int t) {
+    if (t == sp.te && two) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc0[mb] = acc[mb];
+        acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+
+  few_unroll<NS - 1>([&](auto sc) {
+    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
+  });
+  constexpr int U = (NS % 2) ? 2 * NS : NS;
+  for (int t0 = 0; t0 < nk; t0 += U) {
+    few_unroll<U>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int t = t0 + j;
+      if (t >= nk) return;
+      few_wait_stages<PER>(min(NS - 2, nk - 1 - t));
+      lds_barrier();
+      if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+      compute(j % NS);
+      tile_done(t);
+    });
+  }
+
+  // ---- one partial per covered tile, then the last block of a tile finishes ----
+  const int b = blockIdx.x, na = two ? 2 : 1;
+  auto store_part = [&](const f32x4 (&v)[MB], int a) {
+    float* cp = p.Cp + (int64_t)(b + a) * p.Mp * BNF;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int vv = 0; vv < 4; ++vv) {
+        const int row = 16 * mb + 4 * g + vv;
+        if (row < p.M) few_st_dev(cp + row * BNF + 16 * wave + l16, v[mb][vv]);
+      }
+  };
+  if (two) store_part(acc0, sp.a0);
+  store_part(acc, sp.a0 + na - 1);
+  int* flag = reinterpret_cast<int*>(smem + R::LDS - 16);
+  few_arrive(p.cnt + sp.a0, na,
+             [&](int i) {
+               const int a = sp.a0 + i;
+               return few_blk_of(p, (a + 1) * p.nkt - 1) - few_blk_of(p, a * p.nkt) + 1;
+             },
+             flag);
+  const int fin0 = flag[0], fin1 = na > 1 ? flag[1] : 0;
+  for (int i = 0; i < na; ++i)
+    if (i ? fin1 : fin0) few_fwd_finish<MB, R::MP, NW4>(p, smem, sp.a0 + i);
 }
 
 __device__ __forceinline__ float nt_get(const char* tile, int r, int c) {
@@ -878,10 +920,11 @@ __device__ __forceinline__ float nt_get(const char* tile, int r, int c) {
 }
 
 // ---------------------------------------------------------------------------
-// launch 2, backward: dX = G W + Q_s A (partials over chunks of d_out, the
-// last block of a tile of 128 input-gradient columns finishes), dB rows of
-// the stages a block owns, dA rows of the block's columns.
-// Block (blockIdx.x = tile of 128 columns of d_in, blockIdx.y = chunk of d_out).
+// launch 2, backward: dX = G W + Q_s A, dB and dA.  A tile: 128 columns of d_in
+// (4 waves x 32); its stages: the 64-wide steps of d_out.  Block b streams its
+// range of the stage sequence (few_span); the last block to arrive at a tile
+// finishes it.  dB rows of stage st come from the tile st mod n_tiles, dA
+// rows of a tile from its blocks in turn.
 // ---------------------------------------------------------------------------
 template <int MB, bool NF4>
 __global__ void __launch_bounds__(few::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -911,11 +954,9 @@ few_bwd_kernel(const FewArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int nt = blockIdx.x, kc = blockIdx.y;
-  const int n0 = nt * 128;
-  const int k0 = kc * p.Kc;
-  const int k1 = min(p.d_out, k0 + p.Kc);
-  const int nk = (k1 - k0) / BK;
+  const FewSpan sp = few_span(p, blockIdx.x);
+  const int nk = sp.nk;
+  const bool two = sp.te < nk - 1;  // the range reaches tile a0 + 1
   if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
   // P_s and Q_s (bf16 [Mp, r8] from few_reduce_kernel) into NT tiles, zeros
   // past Mp and r8
@@ -929,28 +970,32 @@ few_bwd_kernel(const FewArgs p) {
 
   const uint16_t* Gm = p.rope ? p.G : p.dY;
   const __amdgpu_buffer_rsrc_t rg = few_rsrc(Gm, (int64_t)p.M * p.d_out * 2);
-  __amdgpu_buffer_rsrc_t rw, rc, ram;
+  // W (NF4: codes and absmax) of the block's two tiles, each resource based at
+  // the tile's first column (d_in is a multiple of 128: whole tiles)
+  const int64_t c0 = (int64_t)sp.a0 * 128, c1 = (int64_t)min(sp.a0 + 1, p.n_tiles - 1) * 128;
+  const int64_t nel = (int64_t)p.d_out * p.d_in;
+  __amdgpu_buffer_rsrc_t rw0, rw1, ram0, ram1;
   if constexpr (NF4) {
-    rc = few_rsrc(p.codes, (int64_t)p.d_out * p.d_in / 2);
-    ram = few_rsrc(p.absmax, (int64_t)p.d_out * (p.d_in / 64) * 4);
+    rw0 = few_rsrc(p.codes + c0 / 2, (nel - c0) / 2);
+    rw1 = few_rsrc(p.codes + c1 / 2, (nel - c1) / 2);
+    ram0 = few_rsrc(p.absmax + c0 / 64, (nel - c0) / 64 * 4);
+    ram1 = few_rsrc(p.absmax + c1 / 64, (nel - c1) / 64 * 4);
   } else {
-    rw = few_rsrc(p.W, (int64_t)p.d_out * p.d_in * 2);
+    rw0 = few_rsrc(p.W + c0, (nel - c0) * 2);
+    rw1 = few_rsrc(p.W + c1, (nel - c1) * 2);
   }
   const int drow = lane >> 3, dpc = lane & 7;
-  // the lanes' DMA offsets at stage 0 (stage st adds a scalar offset: 64
-  // more W rows, 64 more G columns)
+  // the lanes' DMA offsets at the tile's stage 0 (stage st adds a scalar
+  // offset: 64 more W rows, 64 more G columns)
   uint32_t vw[WI], vam = OOB, vg[R::XI];
   if constexpr (NF4) {
     // codes: instruction j = wave moves rows 16 j .. 16 j + 15, 64 bytes
     // (128 columns) each; the lane: row 16 j + lane / 4, quarter lane & 3
     const int row = 16 * wave + (lane >> 2);
-    vw[0] = n0 + 32 * (lane & 3) < p.d_in
-                ? (uint32_t)((int64_t)(k0 + row) * (p.d_in / 2) + n0 / 2 + 16 * (lane & 3))
-                : OOB;
+    vw[0] = (uint32_t)(row * (p.d_in / 2) + 16 * (lane & 3));
     // absmax: entries e = 32 wave + lane (lanes < 32): row e / 2, block e & 1
     const int e = 32 * wave + lane;
-    const int ab = n0 / 64 + (e & 1);
-    if (lane < 32 && ab < p.d_in / 64) vam = (uint32_t)(((int64_t)(k0 + (e >> 1)) * (p.d_in / 64) + ab) * 4);
+    if (lane < 32) vam = (uint32_t)(((e >> 1) * (p.d_in / 64) + (e & 1)) * 4);
   } else {
     // NN tile rows of 256 bytes: instruction j moves rows 4 j .. 4 j + 3; the
     // lane lands at physical chunk lane & 15 of row 4 j + lane / 16
@@ -959,21 +1004,26 @@ few_bwd_kernel(const FewArgs p) {
       const int row = 4 * (WI * wave + i) + (lane >> 4);
       const int pc = lane & 15, psg = pc >> 1;
       const int lsg = (psg & ~3) | ((psg ^ row) & 3);
-      const int col = n0 + 8 * ((lsg << 1) | (pc & 1));
-      vw[i] = col < p.d_in ? (uint32_t)(((int64_t)(k0 + row) * p.d_in + col) * 2) : OOB;
+      vw[i] = (uint32_t)((row * p.d_in + 8 * ((lsg << 1) | (pc & 1))) * 2);
     }
   }
 #pragma unroll
   for (int i = 0; i < R::XI; ++i) {
     const int row = 8 * (wave + 4 * i) + drow;
-    vg[i] = row < p.M ? (uint32_t)((row * p.d_out + k0 + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+    vg[i] = row < p.M ? (uint32_t)((row * p.d_out + 8 * (dpc ^ (row & 7))) * 2) : OOB;
   }
-  auto issue = [&](int st, int slot) {
+  // local stage t: tile a0 (stage s0 + t) up to te, then tile a0 + 1
+  auto stage_of = [&](int t) { return t > sp.te ? t - sp.te - 1 : sp.s0 + t; };
+  auto issue = [&](int t, int slot) {
+    const bool second = t > sp.te;
+    const int st = stage_of(t);
     char* ws = wslot(slot);
     if constexpr (NF4) {
+      const __amdgpu_buffer_rsrc_t rc = second ? rw1 : rw0, ra = second ? ram1 : ram0;
       few_dma(rc, ws + wave * 1024, vw[0], st * BK * (p.d_in / 2));
-      few_dma<4>(ram, ws + R::CODES + wave * 256, vam, st * BK * (p.d_in / 64) * 4);
+      few_dma<4>(ra, ws + R::CODES + wave * 256, vam, st * BK * (p.d_in / 64) * 4);
     } else {
+      const __amdgpu_buffer_rsrc_t rw = second ? rw1 : rw0;
 #pragma unroll
       for (int i = 0; i < WI; ++i) few_dma(rw, ws + (WI * wave + i) * 1024, vw[i], st * BK * p.d_in * 2);
     }
@@ -1000,11 +1050,11 @@ few_bwd_kernel(const FewArgs p) {
     }
   };
 
-  f32x4 acc[MB][NJ];
+  f32x4 acc[MB][NJ], acc0[MB][NJ];  // acc0: tile a0's sum once the range has moved on
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = acc0[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const char* gs, const char* wt) {
     // the stage's W fragments of both 32-deep steps in one batch of reads
     bf16x8 bfr[2 * NJ];
@@ -1025,7 +1075,7 @@ few_bwd_kernel(const FewArgs p) {
     }
   };
   // dB rows of stage st (G rows i of the stage meet all M tokens here): the
-  // stage's owner block (global stage index modulo the column tiles) writes
+  // block that streams stage st of tile st mod n_tiles writes
   // dB[i, q] = sum_t G[t, i] P_s[t, q] = (G^T P_s)[i, q], an MFMA product over
   // the tokens (zero rows past M): A = G^T read transposed from the G tile,
   // B = P_s read transposed from its NT tile.  Wave w: rows 16 w .. + 15.
@@ -1041,9 +1091,9 @@ few_bwd_kernel(const FewArgs p) {
       few_tr_frags<MAXR / 16>(pfr[k], ad);
     }
   };
-  auto db_rows = [&](int st, int slot) {
-    const int u = (k0 + st * BK) / BK;
-    if (u % p.n_tiles != nt) return;
+  auto db_rows = [&](int t, int slot) {
+    const int st = stage_of(t);
+    if (st % p.n_tiles != sp.a0 + (t > sp.te ? 1 : 0)) return;
     const char* gs = gslot(slot);
     f32x4 d[MAXR / 16];
 #pragma unroll
@@ -1058,7 +1108,7 @@ few_bwd_kernel(const FewArgs p) {
 #pragma unroll
       for (int nb = 0; nb < MAXR / 16; ++nb)
         if (16 * nb < p.r8) d[nb] = mfma16(af[k], pfr[k][nb], d[nb]);
-    const int i0 = k0 + st * BK + 16 * wave;
+    const int i0 = st * BK + 16 * wave;
 #pragma unroll
     for (int nb = 0; nb < MAXR / 16; ++nb)
 #pragma unroll
@@ -1066,6 +1116,18 @@ few_bwd_kernel(const FewArgs p) {
         const int q = 16 * nb + l16;
         if (q < p.r8) p.dB[(int64_t)(i0 + 4 * g + v) * p.r8 + q] = d[nb][v];
       }
+  };
+
+  auto tile_done = [&](int t) {
+    if (t == sp.te && two) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc0[mb][j] = acc[mb][j];
+          acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
   };
 
   // prologue: stages 0 .. NS - 2 in flight
@@ -1101,26 +1163,35 @@ few_bwd_kernel(const FewArgs p) {
         compute(gslot(j % NS), wslot(j % NS));
       }
       db_rows(t, j % NS);
+      tile_done(t);
     });
   }
 
-  // dA[q, j] = sum_t Q_s[t, q] X[t, j] for the block's 128 columns j and the
-  // 16-rank blocks nb = kc, kc + Sk, ...: (X^T Q_s)[j, q] by MFMA over the
-  // tokens, X [MP rows, 128 columns] staged in the ring (NN layout, zeros past
-  // M and d_in), A = X^T and B = Q_s both read transposed.  Wave w: columns
-  // 32 w .. + 31.
-  {
+  const int N = p.d_in;
+  const int b = blockIdx.x, na = two ? 2 : 1;
+  auto blo = [&](int a) { return few_blk_of(p, a * p.nkt); };
+  auto bhi = [&](int a) { return few_blk_of(p, (a + 1) * p.nkt - 1); };
+
+  // dA[q, j] = sum_t Q_s[t, q] X[t, j] for a covered tile's 128 columns j and
+  // the 16-rank blocks nb = i, i + c, ... (the block is the tile's i-th of c):
+  // (X^T Q_s)[j, q] by MFMA over the tokens, X [MP rows, 128 columns] staged
+  // in the ring (NN layout, zeros past M), A = X^T and B = Q_s both read
+  // transposed.  Wave w: columns 32 w .. + 31.
+  for (int ia = 0; ia < na; ++ia) {
+    const int a = sp.a0 + ia, n0 = a * 128;
+    const int lo = blo(a), c = bhi(a) - lo + 1;
+    if (16 * (b - lo) >= p.r8) continue;
     char* xt = ring;
     __syncthreads();  // every wave is done with the ring
     for (int e = tid; e < R::MP * 16; e += NT) {
-      const int t = e >> 4, c = e & 15;
-      const int col = n0 + 8 * c;
+      const int t = e >> 4, cc = e & 15;
+      const int col = n0 + 8 * cc;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (t < p.M && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.X + (int64_t)t * p.d_in + col);
-      *reinterpret_cast<u32x4*>(xt + nn_off<256>(t, c)) = v;
+      *reinterpret_cast<u32x4*>(xt + nn_off<256>(t, cc)) = v;
     }
     __syncthreads();
-    for (int nb = kc; 16 * nb < p.r8; nb += p.Sk) {
+    for (int nb = b - lo; 16 * nb < p.r8; nb += c) {
       f32x4 d[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int k = 0; k < R::MP / 32; ++k) {
@@ -1139,60 +1210,70 @@ few_bwd_kernel(const FewArgs p) {
     }
   }
 
-  // ---- partial of this chunk; the last block of the tile finishes ----
-  const int N = p.d_in;
-  float* cp = p.Cp + (int64_t)kc * p.Mp * N;
+  // ---- one partial per covered tile (slab b + a of tile a), then the last
+  // block to arrive at a tile finishes it ----
+  auto store_part = [&](const f32x4 (&v)[MB][NJ], int a) {
+    float* cp = p.Cp + (int64_t)(b + a) * p.Mp * 128;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = 16 * mb + 4 * g + v;
-        const int col = n0 + 32 * wave + 16 * j + l16;
-        if (row < p.M && col < N) few_st_dev(cp + (int64_t)row * N + col, acc[mb][j][v]);
-      }
-  if (!few_last_arrival(p.cnt + nt, p.Sk, reinterpret_cast<int*>(smem + R::LDS - 16))) return;
+        for (int vv = 0; vv < 4; ++vv) {
+          const int row = 16 * mb + 4 * g + vv;
+          if (row < p.M) few_st_dev(cp + row * 128 + 32 * wave + 16 * j + l16, v[mb][j][vv]);
+        }
+  };
+  if (two) store_part(acc0, sp.a0);
+  store_part(acc, sp.a0 + na - 1);
+  int* flag = reinterpret_cast<int*>(smem + R::LDS - 16);
+  few_arrive(p.cnt + sp.a0, na, [&](int i) { return bhi(sp.a0 + i) - blo(sp.a0 + i) + 1; }, flag);
+  const int fin0 = flag[0], fin1 = na > 1 ? flag[1] : 0;
 
-  // rank term Q_s A: A rows q (< r8) of the block's columns into an NN tile
-  // (rows past r8 and columns past d_in zero), read like W
-  char* at = ring;
-  __syncthreads();
-  for (int e = tid; e < 64 * 16; e += NT) {
-    const int q = e >> 4, c = e & 15;
-    const int col = n0 + 8 * c;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (q < p.r8 && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
-    *reinterpret_cast<u32x4*>(at + nn_off<256>(q, c)) = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int sstep = 0; sstep < 2; ++sstep) {
-    bf16x8 bfr[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) bfr[j] = nn_frag<256>(at, 32 * sstep, 32 * wave + 16 * j, lane);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8 af = nt_frag(qst, 16 * mb, sstep, lane);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+  for (int ia = 0; ia < na; ++ia) {
+    if (!(ia ? fin1 : fin0)) continue;
+    const int a = sp.a0 + ia, n0 = a * 128;
+    // rank term Q_s A: A rows q (< r8) of the tile's columns into an NN tile
+    // (rows past r8 zero), read like W
+    char* at = ring;
+    __syncthreads();
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int q = e >> 4, cc = e & 15;
+      const int col = n0 + 8 * cc;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q < p.r8 && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
+      *reinterpret_cast<u32x4*>(at + nn_off<256>(q, cc)) = v;
     }
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep) {
+      bf16x8 bfr[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = nn_frag<256>(at, 32 * sstep, 32 * wave + 16 * j, lane);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(qst, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+      }
+    }
+    // the rank term to an fp32 tile [MP][128]: over the expanded W tiles and
+    // the table (NF4), else past the A tile
+    float* tl = reinterpret_cast<float*>(NF4 ? smem + 2 * PT : ring + 64 * 256);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * 128 + 32 * wave + 16 * j + l16] = acc[mb][j][v];
+    __syncthreads();
+    const int lo = blo(a);
+    few_finish<128>(p, tl, p.Cp + (int64_t)(lo + a) * p.Mp * 128, bhi(a) - lo + 1, n0, N, p.dX, false);
   }
-  // the rank term to an fp32 tile [MP][128]: over the expanded W tiles and
-  // the table (NF4), else past the A tile
-  float* tl = reinterpret_cast<float*>(NF4 ? smem + 2 * PT : ring + 64 * 256);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * 128 + 32 * wave + 16 * j + l16] = acc[mb][j][v];
-  __syncthreads();
-  few_finish<128>(p, tl, n0, N, p.dX, false);
 }
 
 }  // namespace lora

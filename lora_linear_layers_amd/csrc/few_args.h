@@ -12,6 +12,7 @@ constexpr int BN = 128;                // output columns per block (one RoPE hea
 constexpr int BK = 64;                 // contraction per stage
 constexpr int MAXMB = 8;               // 16-row blocks of tokens (M <= 128)
 constexpr int MAXR = 64;               // rank (a multiple of 8)
+constexpr int GRID = 256;              // blocks of the W-streaming launch: one per MI355X CU
 constexpr uint32_t OOB = 0x80000000u;  // lane offset past every resource: reads zero
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0f70; }
 }  // namespace few
@@ -40,14 +41,15 @@ struct FewArgs {
   int rope;
   float* Pp;  // [Sp][Mp][r8] fp32 partials of X A^T
   float* Qp;  // [Sq][Mp][r8] fp32 partials of G B
-  float* Cp;  // [Sk][Mp][N] fp32 partials of the main product (N = d_out forward, d_in backward)
+  float* Cp;  // [nblk + n_tiles - 1][Mp][BN] fp32 partials of the main product, one per (block, tile)
   int* cnt;   // [n_tiles] arrival counters of launch 2 (cleared by launch 1)
   uint16_t* Ps;  // backward: bf16(s P) [Mp, r8] (few_reduce_kernel)
   uint16_t* Qs;  // backward: bf16(s Q) [Mp, r8]
   int Sp, Kp;  // P: chunks of d_in of Kp (a multiple of 32)
   int Sq, Kq;  // Q: chunks of d_out of Kq (a multiple of 128)
-  int Sk, Kc;  // launch 2: chunks of the contraction of Kc (a multiple of 64)
-  int n_tiles;
+  // launch 2: n_tiles column tiles of BN, nkt stages of BK each; block b of
+  // nblk takes the stages [b T / nblk, (b + 1) T / nblk) of the T = n_tiles nkt
+  int n_tiles, nkt, T, nblk;
 };
 
 }  // namespace lora

@@ -147,8 +147,12 @@ __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// two floats -> two bf16 (nearest even), lo in the low half: one
+// v_cvt_pk_bf16_f32 (the scalar casts of f2bf, or-ed, take three instructions)
+typedef float pk_f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 pk_bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(pk_f32x2{lo, hi}, pk_bf16x2));
 }
 
 template <typename T>

@@ -1060,13 +1060,12 @@ hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
   if (what == 0) {
     hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
   } else if (what == 1) {
-    const dim3 grid((unsigned)a.n_tiles, (unsigned)a.Sk);
-    if (nf4)
-      hipLaunchKernelGGL((few_fwd_kernel<MB, true>), grid, dim3(few::NT), 0, st, a);
-    else
-      hipLaunchKernelGGL((few_fwd_kernel<MB, false>), grid, dim3(few::NT), 0, st, a);
+    // the forward's few-token launch exists for NF4 W only (a bf16 W takes the
+    // one-launch skinny kernel)
+    if (!nf4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((few_fwd_nf4_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT4), 0, st, a);
   } else {
-    const dim3 grid((unsigned)a.n_tiles, (unsigned)a.Sk);
+    const dim3 grid((unsigned)a.nblk);
     if (nf4)
       hipLaunchKernelGGL((few_bwd_kernel<MB, true>), grid, dim3(few::NT), 0, st, a);
     else
@@ -1077,7 +1076,9 @@ hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
 
 hipError_t few_dispatch(const FewArgs& a, int MB, int what, bool nf4, hipStream_t st) {
   if (a.M < 1 || a.M > 16 * MB || a.Mp != 16 * MB || a.r8 < 8 || a.r8 > few::MAXR || a.r8 % 8) return hipErrorInvalidValue;
-  if (a.Sp < 1 || a.Sk < 1 || a.n_tiles < 1) return hipErrorInvalidValue;
+  if (a.Sp < 1 || a.n_tiles < 1 || a.n_tiles > a.nblk || a.nkt < 1 || a.T != a.n_tiles * a.nkt || a.nblk < 1 ||
+      a.nblk > few::GRID || a.nblk > a.T)
+    return hipErrorInvalidValue;
   switch (MB) {
     case 1: return few_launch<1>(a, what, nf4, st);
     case 2: return few_launch<2>(a, what, nf4, st);

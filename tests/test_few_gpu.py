@@ -1,12 +1,12 @@
 """GPU parity of the few-token path (bf16 activations, r a multiple of 8 up
 to 64; the backward up to 64 tokens with a bf16 W and 128 with NF4, the NF4
-forward up to 64): a panel-partials launch, for the backward the panel sums,
-then one launch that streams W (bf16, or NF4 codes expanded in LDS) through
-split-contraction blocks whose last arrival per column tile sums the partials
-in chunk order, adds the rank term and stores (or rotates, RoPE).
-Against the float64 oracle at the bf16 bar; repeats are bitwise equal (the
-arrival order of blocks must not change a bit); small-integer inputs are
-exact."""
+forward up to 64): a panel-partials launch (the backward then sums the
+panels), then one launch that streams W (bf16, or NF4 codes expanded on the
+fly) in 256 equal ranges of the column tiles' contraction stages; the last
+block to arrive at a tile sums its partials in block order, adds the rank term
+and stores (or rotates, RoPE).  Against the float64 oracle at the bf16 bar;
+repeats are bitwise equal (the arrival order of blocks must not change a bit);
+small-integer inputs are exact."""
 import math
 
 import numpy as np
@@ -38,10 +38,9 @@ def _check_path(kinds, nf4, M, d_in, d_out, r, rope=False):
     assert fwd or bwd, "a case outside the few-token path"
 
 
-# (M, d_in, d_out, r): every 16-row block count, ragged column tiles of both
-# directions (576 = 4.5 forward tiles, 320 = 2.5 backward tiles), one and many
-# contraction chunks, ranks 8 / 16 / 64
-SHAPES = [(1, 256, 512, 8), (5, 320, 576, 16), (16, 4096, 4096, 16), (17, 1024, 2048, 64),
+# (M, d_in, d_out, r): every 16-row block count up to 64 (the bf16 W's range),
+# ranges of one to many stages per block, ranks 8 / 16 / 64
+SHAPES = [(1, 256, 512, 8), (5, 384, 576, 16), (16, 4096, 4096, 16), (17, 1024, 2048, 64),
           (33, 2048, 1024, 8), (64, 4096, 1024, 64), (49, 512, 4096, 16), (64, 5120, 1024, 64)]
 
 
@@ -83,7 +82,8 @@ def test_few_rope_parity(lib, M, d_in, d_out, r, seq):
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
 
 
-@pytest.mark.parametrize("M,d_in,d_out,r", [(1, 512, 768, 8), (16, 5120, 2048, 64), (40, 1024, 4096, 16),
+# NF4: a ragged forward tile (704 = 5.5 tiles of 128), up to 128 tokens
+@pytest.mark.parametrize("M,d_in,d_out,r", [(1, 512, 704, 8), (16, 5120, 2048, 64), (40, 1024, 4096, 16),
                                             (128, 2048, 1024, 64)])
 def test_few_nf4_parity(lib, M, d_in, d_out, r):
     tab = gen.nf4_table()
