@@ -324,6 +324,26 @@ def _time_ms(fn, reps):
     return _pct(ts)
 
 
+def _time_interleaved(fns, reps):
+    """HIP-event times of the calls in fns (name -> callable), taken round-robin
+    (one call of each per round) so that every variant meets the same clock and
+    thermal state of the GPU; median / p10 / p90 in ms per name."""
+    import torch
+
+    for fn in fns.values():
+        fn()
+    ts = {name: [] for name in fns}
+    for _ in range(reps):
+        for name, fn in fns.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts[name].append(e0.elapsed_time(e1))
+    return {name: _pct(t) for name, t in ts.items()}
+
+
 def next_rows(work, reps=10):
     """The rows beyond the layer itself, on this workload's gate / up pair:
     SwiGLU (fused epilogue vs. the pair's plain group forward) and the merge of
@@ -353,16 +373,20 @@ def next_rows(work, reps=10):
     fwd_flop = 2.0 * 2 * M * (d * k + cfg.r * (d + k))
     bwd_flop = 2.0 * 2 * M * (d * k + 2 * cfg.r * (d + k))
     arr = L.functional._group_members(X, ms)
-    wsb = max(int(L.lib().lora_swiglu_workspace_bytes(b, L.LORA_BF16, M, k, arr)) for b in (0, 1))
+    wsb = max([int(L.lib().lora_swiglu_workspace_bytes(b, L.LORA_BF16, M, k, arr)) for b in (0, 1)] +
+              [int(L.lib().lora_group_workspace_bytes(b, L.LORA_BF16, M, k, 2, arr)) for b in (0, 1)])
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=X.device)
-    sw = {}
-    sw["fwd_with_gu_ms"] = _time_ms(lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, ws=ws), reps)
-    sw["fwd_h_only_ms"] = _time_ms(lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, store_gu=False, ws=ws), reps)
-    sw["group_fwd_ms"] = _time_ms(lambda: L.lora_group_fwd(X, ms, table16=tab, Ys=[G, U], ws=work.ws), reps)
     Gs, Us = L.lora_swiglu_fwd(X, ms, table16=tab, ws=ws)[1:]
-    sw["bwd_ms"] = _time_ms(lambda: L.lora_swiglu_bwd(X, ms, dH, Gs, Us, table16=tab, ws=ws), reps)
+    dU = pair[1]["dY"]
+    # (interleaved: the comparison meets one clock state)
+    sw = _time_interleaved({
+        "fwd_with_gu_ms": lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, ws=ws),
+        "fwd_h_only_ms": lambda: L.lora_swiglu_fwd(X, ms, table16=tab, H=H, store_gu=False, ws=ws),
+        "group_fwd_ms": lambda: L.lora_group_fwd(X, ms, table16=tab, Ys=[G, U], ws=ws),
+        "bwd_ms": lambda: L.lora_swiglu_bwd(X, ms, dH, Gs, Us, table16=tab, ws=ws),
+        "group_bwd_ms": lambda: L.lora_group_bwd(X, ms, [dH, dU], table16=tab, ws=ws)}, reps)
     for key, fl in (("fwd_with_gu_ms", fwd_flop), ("fwd_h_only_ms", fwd_flop), ("group_fwd_ms", fwd_flop),
-                    ("bwd_ms", bwd_flop)):
+                    ("bwd_ms", bwd_flop), ("group_bwd_ms", bwd_flop)):
         sw[key.replace("_ms", "_tflops")] = round(fl / (sw[key]["median"] * 1e-3) / 1e12, 1)
     sw["shape"] = f"gate/up {k}->{d}, M={M}, r={cfg.r}" + (", NF4 W" if cfg.nf4 else "")
     out["swiglu"] = sw
@@ -379,14 +403,12 @@ def next_rows(work, reps=10):
         one_fwd = 2.0 * M * (d * k + cfg.r * (d + k))
         one_bwd = 2.0 * M * (d * k + 2 * cfg.r * (d + k))
         dr = {"shape": f"{it['p'].name} {k}->{d}, M={M}, r={cfg.r}, p={p}"}
-        dr["fwd_ms"] = _time_ms(lambda: L.lora_dropout_fwd(X, it["W"], it["A"], it["B"], s, p, keep, Y=it["Y"],
-                                                            ws=dws), reps)
-        dr["bwd_ms"] = _time_ms(lambda: L.lora_dropout_bwd(X, it["W"], it["A"], it["B"], s, p, keep, it["dY"],
-                                                            ws=dws), reps)
-        dr["plain_fwd_ms"] = _time_ms(lambda: L.lora_linear_fwd(X, it["W"], it["A"], it["B"], s, Y=it["Y"], ws=dws),
-                                      reps)
-        dr["plain_bwd_ms"] = _time_ms(lambda: L.lora_linear_bwd(X, it["W"], it["A"], it["B"], s, it["dY"], ws=dws,
-                                                                out=(it["dX"], it["dA"], it["dB"])), reps)
+        dr.update(_time_interleaved({
+            "fwd_ms": lambda: L.lora_dropout_fwd(X, it["W"], it["A"], it["B"], s, p, keep, Y=it["Y"], ws=dws),
+            "plain_fwd_ms": lambda: L.lora_linear_fwd(X, it["W"], it["A"], it["B"], s, Y=it["Y"], ws=dws),
+            "bwd_ms": lambda: L.lora_dropout_bwd(X, it["W"], it["A"], it["B"], s, p, keep, it["dY"], ws=dws),
+            "plain_bwd_ms": lambda: L.lora_linear_bwd(X, it["W"], it["A"], it["B"], s, it["dY"], ws=dws,
+                                                      out=(it["dX"], it["dA"], it["dB"]))}, reps))
         for key, fl in (("fwd_ms", one_fwd), ("bwd_ms", one_bwd), ("plain_fwd_ms", one_fwd),
                         ("plain_bwd_ms", one_bwd)):
             dr[key.replace("_ms", "_tflops")] = round(fl / (dr[key]["median"] * 1e-3) / 1e12, 1)
@@ -407,8 +429,9 @@ def small_token_sweep(device, reps=10):
     """Few-token cases, where reading W bounds the layer: the Llama-3-8B q
     projection (4096->4096, r 16, RoPE, bf16) and the Qwen1.5-32B-shaped gate
     projection (5120->27392, r 64, NF4 W), M in {16, 64, 128}.  Each timed call
-    follows a 1 GiB write that evicts the 256 MB MALL, so W comes from HBM.
-    GB/s = minimum HBM bytes of the call / its HIP-event time."""
+    follows a 1 GiB read that evicts the 256 MB MALL with clean lines, so W
+    comes from HBM and no write-back of a flush's dirty lines competes with
+    it.  GB/s = minimum HBM bytes of the call / its HIP-event time."""
     import math
 
     import torch
@@ -416,7 +439,7 @@ def small_token_sweep(device, reps=10):
     import lora_linear_layers_amd as L
     from synth import gen
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=device)
     tab = gen.nf4_table()
     res = {}
     cases = [("q_proj 4096->4096 r16 rope bf16", 4096, 4096, 16, True, False),
@@ -461,7 +484,7 @@ def small_token_sweep(device, reps=10):
                 fn()
                 ts = []
                 for i in range(reps):
-                    flush.fill_(i & 255)
+                    flush.sum()
                     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     e0.record()
                     fn()

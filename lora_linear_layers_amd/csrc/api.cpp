@@ -58,6 +58,7 @@ int check_device() {
 struct FewPlan {
   bool ok = false;
   int MB = 0, Mp = 0, Sp = 0, Kp = 0, Sq = 0, Kq = 0, n_tiles = 0, nkt = 0, T = 0, nblk = 0;
+  bool fold = false;  // backward in two launches: the W stream sums the panels
   size_t pp = 0, qp = 0, cp = 0, cnt = 0, g = 0, ps = 0, qs = 0, total = 0;
 };
 
@@ -95,6 +96,9 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   if (bwd) {
     F.Kq = (int)std::max<int64_t>(128, rup(cdiv(d_out, 32), 128));
     F.Sq = (int)cdiv(d_out, F.Kq);
+    // every block of the W stream sums all the panel partials (from L2) while
+    // its first stages fly: worth a launch when they are at most 64 KB
+    F.fold = int64_t(F.Sp + F.Sq) * F.Mp * r * 4 <= (int64_t(64) << 10);
   }
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -489,7 +493,7 @@ FewArgs few_args(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64
   a.Cp = reinterpret_cast<float*>(w + F.cp);
   a.cnt = reinterpret_cast<int*>(w + F.cnt);
   a.Sp = F.Sp; a.Kp = F.Kp; a.Sq = F.Sq; a.Kq = F.Kq;
-  a.n_tiles = F.n_tiles; a.nkt = F.nkt; a.T = F.T; a.nblk = F.nblk;
+  a.n_tiles = F.n_tiles; a.nkt = F.nkt; a.T = F.T; a.nblk = F.nblk; a.fold = F.fold ? 1 : 0;
   return a;
 }
 
@@ -522,8 +526,9 @@ int few_backward(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64
   const double wb = nf4 ? ko * ki * (0.5 + 1.0 / 16) : 2.0 * ko * ki;
   HIPTRY(timed(K_FEW_PANEL, 2 * Md * rr * (ki + ko), (Md + rr) * (ki + ko) * 2 + 4.0 * (F.Sp + F.Sq) * F.Mp * rr,
                st, [&] { return launch_few_panel(a, F.MB, st); }));
-  HIPTRY(timed(K_FEW_PANEL, 0, 4.0 * (F.Sp + F.Sq) * F.Mp * rr + 4.0 * F.Mp * rr, st,
-               [&] { return launch_few_reduce(a, st); }));
+  if (!F.fold)
+    HIPTRY(timed(K_FEW_PANEL, 0, 4.0 * (F.Sp + F.Sq) * F.Mp * rr + 4.0 * F.Mp * rr, st,
+                 [&] { return launch_few_reduce(a, st); }));
   HIPTRY(timed(K_FEW_BWD, 2 * Md * ki * (ko + rr) + 4 * Md * rr * (ki + ko),
                wb + (Md * ko + Md * ki + rr * ki + ko * rr + Md * ki) * 2 + 4.0 * rr * (ki + ko), st,
                [&] { return launch_few_bwd(a, F.MB, nf4 != nullptr, st); }));

@@ -15,8 +15,10 @@
 //     chunks of their contraction, P = X A^T (both directions) and, in the
 //     backward, Q = G B; with RoPE it forms G from dY on load, rotating each
 //     head's pairs (i, i + 64) by the negated angle, and stores G for launch
-//     2.  It also clears the W stream's arrival counters.  The backward then
-//     sums the panels once (few_reduce_kernel): P_s = bf16(s P), Q_s = bf16(s Q).
+//     2.  It also clears the W stream's arrival counters.  The backward's W
+//     stream sums the panels itself, P_s = bf16(s P) and Q_s = bf16(s Q),
+//     while its first stages fly when the partials are few enough (fold);
+//     else a launch between sums them once (few_reduce_kernel).
 //   the W stream (few_fwd_nf4_kernel / few_bwd_kernel): column tiles of 128
 //     outputs, each a sequence of contraction stages; the tiles' stages in
 //     sequence are cut into 256 equal contiguous ranges, one block (one CU)
@@ -135,12 +137,6 @@ __device__ __forceinline__ bf16x8 nt_tr_frag(const char* tile, int k0, int n0, i
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// 32-bit LDS address of a generic pointer into LDS
-__device__ __forceinline__ uint32_t few_lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
 
 // The LDS addresses of the two transposing reads of nn_frag / nt_tr_frag
 template <int RB = 256>
@@ -151,7 +147,7 @@ __device__ __forceinline__ u32x2 nn_frag_addr(const char* tile, int k0, int n0, 
   for (int hq = 0; hq < 2; ++hq) {
     const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
     const int col = n0 + 4 * (i & 3);
-    a[hq] = few_lds_addr(tile + nn_off<RB>(row, col >> 3) + ((col & 7) << 1));
+    a[hq] = lds_addr(tile + nn_off<RB>(row, col >> 3) + ((col & 7) << 1));
   }
   return a;
 }
@@ -162,46 +158,11 @@ __device__ __forceinline__ u32x2 nt_tr_frag_addr(const char* tile, int k0, int n
   for (int hq = 0; hq < 2; ++hq) {
     const int row = k0 + 8 * gq + 4 * hq + (i >> 2);
     const int col = n0 + 4 * (i & 3);
-    a[hq] = few_lds_addr(tile + nt_off(row, col >> 3) + ((col & 7) << 1));
+    a[hq] = lds_addr(tile + nt_off(row, col >> 3) + ((col & 7) << 1));
   }
   return a;
 }
 
-// N transposed fragments from their read addresses, in one asm block that
-// issues the 2N reads back to back and waits for them before it ends (no read
-// is in flight when the block's output registers are handed back).  The
-// builtin form of the read makes the compiler wait first for every LDS DMA
-// in flight, which would drain the stage ring at each read; these tiles are
-// never a DMA's destination while a DMA into them can be in flight (the ring
-// protocol's waits and barriers order them).
-#define FEW_TR(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
-template <int N>
-__device__ __forceinline__ void few_tr_frags(bf16x8 (&f)[N], const u32x2 (&a)[N]) {
-  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 fragments");
-  u32x2 h[2 * N];
-  if constexpr (N == 1) {
-    asm volatile(FEW_TR(0, 2) FEW_TR(1, 3) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(h[0]), "=&v"(h[1])
-                 : "v"(a[0][0]), "v"(a[0][1]));
-  } else if constexpr (N == 2) {
-    asm volatile(FEW_TR(0, 4) FEW_TR(1, 5) FEW_TR(2, 6) FEW_TR(3, 7) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
-                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]));
-  } else {
-    asm volatile(FEW_TR(0, 8) FEW_TR(1, 9) FEW_TR(2, 10) FEW_TR(3, 11) FEW_TR(4, 12) FEW_TR(5, 13)
-                     FEW_TR(6, 14) FEW_TR(7, 15) "s_waitcnt lgkmcnt(0)"
-                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]),
-                   "=&v"(h[6]), "=&v"(h[7])
-                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(a[2][0]), "v"(a[2][1]),
-                   "v"(a[3][0]), "v"(a[3][1]));
-  }
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const u32x4 v = {h[2 * n][0], h[2 * n][1], h[2 * n + 1][0], h[2 * n + 1][1]};
-    f[n] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-#undef FEW_TR
 
 // A or B fragment from an NT tile: rows r0 .. r0 + 15, contraction 32 s .. +31
 __device__ __forceinline__ bf16x8 nt_frag(const char* tile, int r0, int s, int lane) {
@@ -592,7 +553,8 @@ __device__ __forceinline__ void few_sum4_dev(const float* src, int S, int64_t zs
 }
 
 // The finishing block's output pass: y = (sum over chunks of the partials) +
-// rank term (an fp32 tile [MP][BNT] in LDS, in the same columns), then bf16
+// rank term (an fp32 tile [MP][BNT] in LDS, in the same columns; none when tl
+// is null, the term being in a partial already), then bf16
 // stores of four columns per item, or, with RoPE (BNT = 128, one head), the
 // rotation of the pairs (f, f + 64) of each row.
 // part: the tile's first partial slab ([Mp][BNT] each, S of them, summed in
@@ -616,7 +578,10 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, co
       for (int i = 0; i < 4; ++i) {
         if (off[i] < 0) continue;
         const int it = i0 + i * NTH, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
-        const float* r = tl + t * BNT + c;
+        float r[4] = {0.f, 0.f, 0.f, 0.f};
+        if (tl)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = tl[t * BNT + c + e];
         *reinterpret_cast<uint2*>(out + (int64_t)t * N + n0 + c) =
             make_uint2(pack_bf16x2(a[i].x + r[0], a[i].y + r[1]), pack_bf16x2(a[i].z + r[2], a[i].w + r[3]));
       }
@@ -647,7 +612,7 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, co
       float y1[4], y2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float u = z1[e] + tl[t * BNT + f + e], w = z2[e] + tl[t * BNT + 64 + f + e];
+        const float u = z1[e] + (tl ? tl[t * BNT + f + e] : 0.f), w = z2[e] + (tl ? tl[t * BNT + 64 + f + e] : 0.f);
         y1[e] = u * cc[e] - w * ss[e];
         y2[e] = w * cc[e] + u * ss[e];
       }
@@ -680,60 +645,6 @@ __global__ void __launch_bounds__(few::NT) few_reduce_kernel(const FewArgs p) {
         make_uint2(pack_bf16x2(p.s * a[0].x, p.s * a[0].y), pack_bf16x2(p.s * a[0].z, p.s * a[0].w));
 }
 
-// The forward's finish of tile a, in the block that arrived there last: P_s
-// = bf16(s X A^T) from the panel partials, the rank term P_s B^T of the tile's
-// columns by MFMA into an fp32 tile in LDS, then the tile's partial slabs
-// summed in block order plus that term, stored or rotated (few_finish).
-template <int MB, int MP, int NW = 4>
-__device__ __forceinline__ void few_fwd_finish(const FewArgs& p, char* smem, int a) {
-  using namespace few;
-  constexpr int BNF = 128, CW = BNF / NW, NJ = CW / 16, NTH = 64 * NW;  // CW: columns per wave
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  const int N = p.d_out, n0 = a * BNF;
-  char* ps = smem;
-  __syncthreads();
-  few_panel_sum<MP, NTH>(p.Pp, p.Sp, p, ps);
-  __syncthreads();
-  // rank term P_s B^T by MFMA (B rows are output columns, r8 contiguous)
-  const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)N * p.r8 * 2);
-  f32x4 acc[MB][NJ];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int sstep = 0; sstep < 2; ++sstep) {
-    const int q = 32 * sstep + 8 * g;
-    bf16x8 bfr[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int col = n0 + CW * wave + 16 * j + l16;
-      bfr[j] = __builtin_bit_cast(
-          bf16x8, few_ld16(rbr, (col < N && q < p.r8) ? (uint32_t)(((int64_t)col * p.r8 + q) * 2) : OOB));
-    }
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const bf16x8 af = nt_frag(ps, 16 * mb, sstep, lane);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
-    }
-  }
-  // the rank term to an fp32 tile [MP][BNF] (over P_s, once every wave is done with it)
-  __syncthreads();
-  float* tl = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * BNF + CW * wave + 16 * j + l16] = acc[mb][j][v];
-  __syncthreads();
-  const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
-  few_finish<BNF, NTH>(p, tl, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, n0, N, p.Y, p.rope != 0);
-}
-
 // ---------------------------------------------------------------------------
 // launch 2, forward with an NF4 W.  Stages of 128 contraction steps (64 code
 // bytes and two absmax per W row); codes, absmax and the activations land in
@@ -744,7 +655,7 @@ __device__ __forceinline__ void few_fwd_finish(const FewArgs& p, char* smem, int
 // each.  A tile: 128 output columns; its stages: the 128-wide steps of d_in;
 // block b streams its range of the stage sequence (few_span), so every CU the
 // same share of W; one partial per (block, tile) and the last block to arrive
-// at a tile finishes it (few_fwd_finish).
+// at a tile sums them (few_finish).
 // ---------------------------------------------------------------------------
 namespace few {
 constexpr int NW4 = 8;           // waves of the NF4 forward block
@@ -830,9 +741,11 @@ few_fwd_nf4_kernel(const FewArgs p) {
     }
   };
 
-  f32x4 acc[MB], acc0[MB];  // acc0: tile a0's sum once the range has moved on
+  // acc0: tile a0's sum once the range has moved on; accr: tile a0 + 1's
+  // starting value (its rank term)
+  f32x4 acc[MB], acc0[MB], accr[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) acc[mb] = acc0[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = acc0[mb] = accr[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // The wave's columns 16 wave + l16 are the W rows of code block wave;
   // fragment ss covers contraction 32 ss + 8 g .. + 7 of the stage: dword g of
   // quarter ss, scaled by the row's absmax ss / 2.  Byte q of a code dword
@@ -867,14 +780,46 @@ few_fwd_nf4_kernel(const FewArgs p) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         acc0[mb] = acc[mb];
-        acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[mb] = accr[mb];
       }
     }
   };
 
+  // The rank term P_s B^T of a tile goes into the partial of the block that
+  // streams the tile's first stage (tile a0 when s0 = 0, tile a0 + 1 when the
+  // range reaches it).  Its B fragments (rows = the wave's 16 columns, r8
+  // contiguous) are loaded ahead of the DMAs; P_s is summed from the panel
+  // partials into LDS no stage uses yet (the last ring slot) while the first
+  // stages fly.
+  const bool rk0 = sp.s0 == 0;
+  const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
+  bf16x8 bq[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep) {
+      const int q = 32 * sstep + 8 * g, col = (sp.a0 + u) * BNF + 16 * wave + l16;
+      const bool ok = (u ? two : rk0) && col < p.d_out && q < p.r8;
+      bq[u][sstep] = __builtin_bit_cast(bf16x8, few_ld16(rbr, ok ? (uint32_t)((col * p.r8 + q) * 2) : OOB));
+    }
+
   few_unroll<NS - 1>([&](auto sc) {
     if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
   });
+  if (rk0 || two) {
+    char* ps = cslot(NS - 1);
+    few_panel_sum<R::MP, NT4>(p.Pp, p.Sp, p, ps);
+    __syncthreads();
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(ps, 16 * mb, sstep, lane);
+        if (rk0) acc[mb] = mfma16(af, bq[0][sstep], acc[mb]);
+        if (two) accr[mb] = mfma16(af, bq[1][sstep], accr[mb]);
+      }
+    // (the slot's first DMA, at stage 0, follows the loop's first barrier)
+  }
   constexpr int U = (NS % 2) ? 2 * NS : NS;
   for (int t0 = 0; t0 < nk; t0 += U) {
     few_unroll<U>([&](auto jc) {
@@ -911,8 +856,14 @@ few_fwd_nf4_kernel(const FewArgs p) {
              },
              flag);
   const int fin0 = flag[0], fin1 = na > 1 ? flag[1] : 0;
-  for (int i = 0; i < na; ++i)
-    if (i ? fin1 : fin0) few_fwd_finish<MB, R::MP, NW4>(p, smem, sp.a0 + i);
+  for (int i = 0; i < na; ++i) {
+    if (!(i ? fin1 : fin0)) continue;
+    // (the rank term is in the partial of the tile's first block)
+    const int a = sp.a0 + i;
+    const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
+    few_finish<BNF, NT4>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
+                         p.rope != 0);
+  }
 }
 
 __device__ __forceinline__ float nt_get(const char* tile, int r, int c) {
@@ -958,16 +909,6 @@ few_bwd_kernel(const FewArgs p) {
   const int nk = sp.nk;
   const bool two = sp.te < nk - 1;  // the range reaches tile a0 + 1
   if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
-  // P_s and Q_s (bf16 [Mp, r8] from few_reduce_kernel) into NT tiles, zeros
-  // past Mp and r8
-  for (int e = tid; e < 2 * R::MP * 8; e += NT) {
-    const int which = e / (R::MP * 8), t = (e >> 3) % R::MP, c = e & 7;
-    const uint16_t* src = which ? p.Qs : p.Ps;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (t < p.Mp && 8 * c < p.r8) v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.r8 + 8 * c);
-    *reinterpret_cast<u32x4*>((which ? qst : pst) + nt_off(t, c)) = v;
-  }
-
   const uint16_t* Gm = p.rope ? p.G : p.dY;
   const __amdgpu_buffer_rsrc_t rg = few_rsrc(Gm, (int64_t)p.M * p.d_out * 2);
   // W (NF4: codes and absmax) of the block's two tiles, each resource based at
@@ -1050,11 +991,13 @@ few_bwd_kernel(const FewArgs p) {
     }
   };
 
-  f32x4 acc[MB][NJ], acc0[MB][NJ];  // acc0: tile a0's sum once the range has moved on
+  // acc0: tile a0's sum once the range has moved on; accr: tile a0 + 1's
+  // starting value (its rank term)
+  f32x4 acc[MB][NJ], acc0[MB][NJ], accr[MB][NJ];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[mb][j] = acc0[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = acc0[mb][j] = accr[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const char* gs, const char* wt) {
     // the stage's W fragments of both 32-deep steps in one batch of reads
     bf16x8 bfr[2 * NJ];
@@ -1063,7 +1006,7 @@ few_bwd_kernel(const FewArgs p) {
     for (int sstep = 0; sstep < 2; ++sstep)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) ad[NJ * sstep + j] = nn_frag_addr<256>(wt, 32 * sstep, 32 * wave + 16 * j, lane);
-    few_tr_frags<2 * NJ>(bfr, ad);
+    lds_tr_frags<2 * NJ>(bfr, ad);
 #pragma unroll
     for (int sstep = 0; sstep < 2; ++sstep) {
 #pragma unroll
@@ -1088,7 +1031,7 @@ few_bwd_kernel(const FewArgs p) {
       u32x2 ad[MAXR / 16];
 #pragma unroll
       for (int nb = 0; nb < MAXR / 16; ++nb) ad[nb] = nt_tr_frag_addr(pst, 32 * k, 16 * nb, lane);
-      few_tr_frags<MAXR / 16>(pfr[k], ad);
+      lds_tr_frags<MAXR / 16>(pfr[k], ad);
     }
   };
   auto db_rows = [&](int t, int slot) {
@@ -1102,7 +1045,7 @@ few_bwd_kernel(const FewArgs p) {
     u32x2 ad[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) ad[k] = nt_tr_frag_addr(gs, 32 * k, 16 * wave, lane);
-    few_tr_frags<KT>(af, ad);
+    lds_tr_frags<KT>(af, ad);
 #pragma unroll
     for (int k = 0; k < KT; ++k)
 #pragma unroll
@@ -1125,17 +1068,86 @@ few_bwd_kernel(const FewArgs p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           acc0[mb][j] = acc[mb][j];
-          acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          acc[mb][j] = accr[mb][j];
         }
     }
   };
+
+  // The rank term Q_s A of a tile goes into the partial of the block that
+  // streams the tile's first stage (tile a0 when s0 = 0, tile a0 + 1 when the
+  // range reaches it), computed before the stream: its A rows (q < r8, the
+  // tile's 128 columns) are loaded here, ahead of the DMAs, and used once Q_s
+  // is in LDS.
+  const bool rk0 = sp.s0 == 0;
+  u32x4 av[2][4];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + NT * e, q = idx >> 4, cc = idx & 15;
+      const int col = (sp.a0 + u) * 128 + 8 * cc;
+      av[u][e] = u32x4{0u, 0u, 0u, 0u};
+      if ((u ? two : rk0) && q < p.r8 && col < p.d_in)
+        av[u][e] = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
+    }
 
   // prologue: stages 0 .. NS - 2 in flight
   few_unroll<NS - 1>([&](auto sc) {
     if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
   });
-  lds_barrier();  // the P_s tile is written
+  // P_s and Q_s into NT tiles (zeros past M and r8) while the first stages
+  // fly: summed here from launch 1's partials (fold), else the bf16 panels
+  // of few_reduce_kernel
+  if (p.fold) {
+    few_panel_sum<R::MP>(p.Pp, p.Sp, p, pst);
+    few_panel_sum<R::MP>(p.Qp, p.Sq, p, qst);
+  } else {
+    for (int e = tid; e < 2 * R::MP * 8; e += NT) {
+      const int which = e / (R::MP * 8), t = (e >> 3) % R::MP, c = e & 7;
+      const uint16_t* src = which ? p.Qs : p.Ps;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (t < p.Mp && 8 * c < p.r8) v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.r8 + 8 * c);
+      *reinterpret_cast<u32x4*>((which ? qst : pst) + nt_off(t, c)) = v;
+    }
+  }
+  lds_barrier();  // the P_s and Q_s tiles are written
   load_pfr();
+  // rank terms: acc (tile a0) and accr (tile a0 + 1) start from Q_s A.  The A
+  // tile goes to LDS that no stage uses yet (the last ring slot, or the second
+  // expanded W tile), as an NN tile read like W.
+  char* at = NF4 ? wbf(1) : wslot(NS - 1);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!(u ? two : rk0)) continue;
+    if (u && rk0) __syncthreads();  // every wave is done with tile a0's A
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + NT * e;
+      *reinterpret_cast<u32x4*>(at + nn_off<256>(idx >> 4, idx & 15)) = av[u][e];
+    }
+    __syncthreads();
+    bf16x8 bfr[2 * NJ];
+    u32x2 ad[2 * NJ];
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) ad[NJ * sstep + j] = nn_frag_addr<256>(at, 32 * sstep, 32 * wave + 16 * j, lane);
+    lds_tr_frags<2 * NJ>(bfr, ad);
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(qst, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (u)
+            accr[mb][j] = mfma16(af, bfr[NJ * sstep + j], accr[mb][j]);
+          else
+            acc[mb][j] = mfma16(af, bfr[NJ * sstep + j], acc[mb][j]);
+        }
+      }
+  }
+  // (the slot's first DMA, at stage 0, follows the loop's first barrier)
   if constexpr (NF4) {
     if (nk > 0) {
       few_wait_stages<PER>(min(NS - 2, nk - 1));
@@ -1233,46 +1245,10 @@ few_bwd_kernel(const FewArgs p) {
   for (int ia = 0; ia < na; ++ia) {
     if (!(ia ? fin1 : fin0)) continue;
     const int a = sp.a0 + ia, n0 = a * 128;
-    // rank term Q_s A: A rows q (< r8) of the tile's columns into an NN tile
-    // (rows past r8 zero), read like W
-    char* at = ring;
-    __syncthreads();
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int q = e >> 4, cc = e & 15;
-      const int col = n0 + 8 * cc;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < p.r8 && col < p.d_in) v = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
-      *reinterpret_cast<u32x4*>(at + nn_off<256>(q, cc)) = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sstep = 0; sstep < 2; ++sstep) {
-      bf16x8 bfr[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) bfr[j] = nn_frag<256>(at, 32 * sstep, 32 * wave + 16 * j, lane);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8 af = nt_frag(qst, 16 * mb, sstep, lane);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
-      }
-    }
-    // the rank term to an fp32 tile [MP][128]: over the expanded W tiles and
-    // the table (NF4), else past the A tile
-    float* tl = reinterpret_cast<float*>(NF4 ? smem + 2 * PT : ring + 64 * 256);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) tl[(16 * mb + 4 * g + v) * 128 + 32 * wave + 16 * j + l16] = acc[mb][j][v];
+    // (the rank term is in the partial of the tile's first block)
     __syncthreads();
     const int lo = blo(a);
-    few_finish<128>(p, tl, p.Cp + (int64_t)(lo + a) * p.Mp * 128, bhi(a) - lo + 1, n0, N, p.dX, false);
+    few_finish<128>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * 128, bhi(a) - lo + 1, n0, N, p.dX, false);
   }
 }
 

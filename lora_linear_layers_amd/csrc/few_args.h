@@ -50,6 +50,7 @@ struct FewArgs {
   // launch 2: n_tiles column tiles of BN, nkt stages of BK each; block b of
   // nblk takes the stages [b T / nblk, (b + 1) T / nblk) of the T = n_tiles nkt
   int n_tiles, nkt, T, nblk;
+  int fold;  // backward: the W stream sums P and Q from the partials itself (no few_reduce_kernel)
 };
 
 }  // namespace lora

@@ -143,6 +143,49 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
   return (row << 7) + ((chunk ^ (row & 7)) << 4);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 32-bit LDS address of a generic pointer into LDS
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// N fragments of ds_read_b64_tr_b16 pairs (the two halves of each at a[n][0]
+// and a[n][1]) in one asm block that issues the 2N reads back to back and
+// waits for them before it ends (no read is in flight when the block's output
+// registers are handed back).  The builtin form of the read makes the compiler
+// wait first for every LDS DMA in flight, which would drain a stage ring at
+// each read; callers read only slots whose DMAs their own waits and barriers
+// have already seen land.
+#define LDS_TR(o, a) "ds_read_b64_tr_b16 %" #o ", %" #a "\n\t"
+template <int N>
+__device__ __forceinline__ void lds_tr_frags(bf16x8 (&f)[N], const u32x2 (&a)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 fragments");
+  u32x2 h[2 * N];
+  if constexpr (N == 1) {
+    asm volatile(LDS_TR(0, 2) LDS_TR(1, 3) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1])
+                 : "v"(a[0][0]), "v"(a[0][1]));
+  } else if constexpr (N == 2) {
+    asm volatile(LDS_TR(0, 4) LDS_TR(1, 5) LDS_TR(2, 6) LDS_TR(3, 7) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]));
+  } else {
+    asm volatile(LDS_TR(0, 8) LDS_TR(1, 9) LDS_TR(2, 10) LDS_TR(3, 11) LDS_TR(4, 12) LDS_TR(5, 13)
+                     LDS_TR(6, 14) LDS_TR(7, 15) "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]),
+                   "=&v"(h[6]), "=&v"(h[7])
+                 : "v"(a[0][0]), "v"(a[0][1]), "v"(a[1][0]), "v"(a[1][1]), "v"(a[2][0]), "v"(a[2][1]),
+                   "v"(a[3][0]), "v"(a[3][1]));
+  }
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const u32x4 v = {h[2 * n][0], h[2 * n][1], h[2 * n + 1][0], h[2 * n + 1][1]};
+    f[n] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+#undef LDS_TR
+
 __device__ __forceinline__ uint16_t f2bf(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }

@@ -339,21 +339,14 @@ splitnn_dma_kernel(const GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
       fa[fi][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + ra + c + i * 32 * 128));
+    // (the transposing reads in one asm batch: the builtin form would make
+    // the compiler wait for every DMA of the ring in flight first)
+    u32x2 ad[FN];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      typedef short i16x4 __attribute__((ext_vector_type(4)));
-      i16x4 h[2];
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int hq = 0; hq < 2; ++hq)
-        h[hq] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(
-            (__attribute__((address_space(3))) char*)smem + s * C::STAGE + nn_r[j] + (16 * st + 4 * hq) * 512));
-      u32x4 v;
-      v[0] = (uint32_t)(uint16_t)h[0][0] | ((uint32_t)(uint16_t)h[0][1] << 16);
-      v[1] = (uint32_t)(uint16_t)h[0][2] | ((uint32_t)(uint16_t)h[0][3] << 16);
-      v[2] = (uint32_t)(uint16_t)h[1][0] | ((uint32_t)(uint16_t)h[1][1] << 16);
-      v[3] = (uint32_t)(uint16_t)h[1][2] | ((uint32_t)(uint16_t)h[1][3] << 16);
-      fb[fi][j] = __builtin_bit_cast(bf16x8, v);
-    }
+      for (int hq = 0; hq < 2; ++hq) ad[j][hq] = lds_addr(base + nn_r[j] + (16 * st + 4 * hq) * 512);
+    lds_tr_frags<FN>(fb[fi], ad);
   };
 
   f32x16 acc[FM][FN];

@@ -155,7 +155,9 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
           for (int jj = 0; jj < 2; ++jj) {
             const float g = acc[i][2 * jj][v], u = acc[i][2 * jj + 1][v];
             const int64_t o = row * ldc + hbase + 32 * jj;
-            out[o] = f2bf(g / (1.f + __expf(-g)) * u);
+            // silu(g) u with the hardware reciprocal (one instruction; the
+            // division's IEEE sequence is ten, per element of the epilogue)
+            out[o] = f2bf(g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u);
             if constexpr (GU == 1) {
               og[o] = f2bf(g);
               ou[o] = f2bf(u);

@@ -27,8 +27,6 @@ SHAPES = [(300, 264, 392, 16, 0.1), (2048, 1024, 4096, 64, 0.05), (4096, 4096, 1
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{i}x{o}r{r}p{p}" for m, i, o, r, p in SHAPES])
 def test_dropout_parity(lib, dtype, shape):
     M, d_in, d_out, r, p = shape
-    if dtype == "f32" and M * d_in * d_out > 2 ** 33:
-        pytest.skip("fp32 at this size only repeats the bf16 case")
     s = 16.0 / r
     X, W, A, B, dY = lora_inputs(500 + M, M, d_in, d_out, r, dtype)
     keep, kb = _keep(7 + M, M, d_in, p)
