@@ -80,9 +80,9 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   if (d_in * d_out * 2 >= lim || M * std::max(d_in, d_out) * 2 >= lim) return F;
   // taken where it measured faster on MI355X than the skinny and split-GEMM
   // paths (q_proj 4096 x 4096 bf16, an NF4 MLP gate 5120 -> 27392): the
-  // backward up to 64 tokens with a bf16 W, up to 128 with NF4; the forward
-  // with NF4 up to 64 tokens
-  if (bwd ? (!nf4 && M > 64) : (!nf4 || M > 64)) return F;
+  // backward, and the forward with NF4 (a bf16 forward takes the one-launch
+  // skinny kernel)
+  if (!bwd && !nf4) return F;
   F.MB = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
   F.Mp = 16 * F.MB;
   const int64_t ncols = bwd ? d_in : d_out, K = bwd ? d_out : d_in;
@@ -91,14 +91,18 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   F.nkt = (int)(K / (nf4 && !bwd ? 2 * few::BK : few::BK));  // the NF4 forward's stages are 128 deep
   F.T = F.n_tiles * F.nkt;
   F.nblk = std::min(few::GRID, F.T);
-  F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, 16), 128));
+  // the backward's W stream sums the panel partials itself (no launch
+  // between) when the panels are small, Mp r8 <= 1024: each block then loads
+  // at most 64 KB of partials, 8 chunks of each panel, from L2.  Launch 1 then
+  // has 8 chunks per panel, each block a chunk of the contraction times
+  // (Mp + r8): taken while those stay within 64K elements (128 KB)
+  auto chunk8 = [](int64_t K) { return std::max<int64_t>(128, rup(cdiv(K, 8), 128)); };
+  F.fold = bwd && F.Mp * r <= 1024 && std::max(chunk8(d_in), chunk8(d_out)) * (F.Mp + r) <= 65536;
+  F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, F.fold ? 8 : 16), 128));
   F.Sp = (int)cdiv(d_in, F.Kp);
   if (bwd) {
-    F.Kq = (int)std::max<int64_t>(128, rup(cdiv(d_out, 32), 128));
+    F.Kq = (int)std::max<int64_t>(128, rup(cdiv(d_out, F.fold ? 8 : 32), 128));
     F.Sq = (int)cdiv(d_out, F.Kq);
-    // every block of the W stream sums all the panel partials (from L2) while
-    // its first stages fly: worth a launch when they are at most 64 KB
-    F.fold = int64_t(F.Sp + F.Sq) * F.Mp * r * 4 <= (int64_t(64) << 10);
   }
   size_t off = 0;
   auto take = [&](size_t bytes) {

@@ -525,21 +525,27 @@ __device__ __forceinline__ void few_panel_sum(const float* part, int S, const Fe
 }
 
 // few_sum4 over partials written by other blocks of the same launch:
-// device-scope loads of single floats, 8 slabs of every item in flight.
+// device-scope loads, 8 slabs of every item in flight.
 template <int NI>
 __device__ __forceinline__ void few_sum4_dev(const float* src, int S, int64_t zstride, const int64_t (&off)[NI],
                                              float4 (&out)[NI]) {
+  // 16-byte buffer loads with the same cache policy as a device-scope
+  // relaxed atomic load (sc1: served at the coherence point, not from a
+  // possibly stale line of this XCD's L2); out-of-range items and slabs read
+  // zero through an offset past the resource
+  const __amdgpu_buffer_rsrc_t r = few_rsrc(src, (int64_t)S * zstride * 4);
 #pragma unroll
   for (int i = 0; i < NI; ++i) out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int z0 = 0; z0 < S; z0 += 8) {
-    float v[NI][8][4];
+    f32x4 v[NI][8];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[i][u][e] = (off[i] >= 0 && z0 + u < S) ? few_ld_dev(src + (int64_t)(z0 + u) * zstride + off[i] + e) : 0.f;
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t o =
+            (off[i] >= 0 && z0 + u < S) ? (uint32_t)(((int64_t)(z0 + u) * zstride + off[i]) * 4) : few::OOB;
+        v[i][u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 16);
+      }
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -909,6 +915,38 @@ few_bwd_kernel(const FewArgs p) {
   const int nk = sp.nk;
   const bool two = sp.te < nk - 1;  // the range reaches tile a0 + 1
   if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
+  // The P_s and Q_s tiles start as zeros (rows past Mp, columns past r8)
+  for (int e = tid; e < 2 * R::MP * 8; e += NT) *reinterpret_cast<u32x4*>(smem + 16 * e) = u32x4{0u, 0u, 0u, 0u};
+  // Their values are loaded ahead of the stream's DMAs (a load issued after
+  // them would complete only after every one of them): with fold, the panel
+  // partials of up to two 4-column items per thread (P items, then Q items;
+  // at most 8 slabs each), else the bf16 panels, 8 columns per item, up to 8
+  // items per thread.
+  const int nP4 = p.Mp * p.r8 / 4;
+  f32x4 pv[2][8];
+  u32x4 bv[8];
+  if (p.fold) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = tid + NT * k;
+      const bool q = it >= nP4;
+      const int off = 4 * (q ? it - nP4 : it), S = q ? p.Sq : p.Sp;
+      const float* src = q ? p.Qp : p.Pp;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        pv[k][z] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (it < 2 * nP4 && z < S) pv[k][z] = *reinterpret_cast<const f32x4*>(src + (int64_t)z * p.Mp * p.r8 + off);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int it = tid + NT * k, n8 = p.Mp * p.r8 / 8;
+      bv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (it < 2 * n8) bv[k] = *reinterpret_cast<const u32x4*>((it < n8 ? p.Ps : p.Qs) + 8 * (it % n8));
+    }
+  }
+  __syncthreads();  // the zeros are written
   const uint16_t* Gm = p.rope ? p.G : p.dY;
   const __amdgpu_buffer_rsrc_t rg = few_rsrc(Gm, (int64_t)p.M * p.d_out * 2);
   // W (NF4: codes and absmax) of the block's two tiles, each resource based at
@@ -1095,19 +1133,31 @@ few_bwd_kernel(const FewArgs p) {
   few_unroll<NS - 1>([&](auto sc) {
     if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
   });
-  // P_s and Q_s into NT tiles (zeros past M and r8) while the first stages
-  // fly: summed here from launch 1's partials (fold), else the bf16 panels
-  // of few_reduce_kernel
+  // P_s and Q_s into their NT tiles while the first stages fly: with fold
+  // summed here (slabs in order) from launch 1's partials, else the bf16
+  // panels of few_reduce_kernel
   if (p.fold) {
-    few_panel_sum<R::MP>(p.Pp, p.Sp, p, pst);
-    few_panel_sum<R::MP>(p.Qp, p.Sq, p, qst);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int it = tid + NT * k;
+      if (it >= 2 * nP4) continue;
+      const bool q = it >= nP4;
+      const int off = 4 * (q ? it - nP4 : it), S = q ? p.Sq : p.Sp;
+      f32x4 a = pv[k][0];
+#pragma unroll
+      for (int z = 1; z < 8; ++z)
+        if (z < S) a += pv[k][z];
+      const int t = off / p.r8, c = off % p.r8;
+      *reinterpret_cast<u32x2*>((q ? qst : pst) + nt_off(t, c >> 3) + 2 * (c & 7)) =
+          u32x2{pack_bf16x2(p.s * a[0], p.s * a[1]), pack_bf16x2(p.s * a[2], p.s * a[3])};
+    }
   } else {
-    for (int e = tid; e < 2 * R::MP * 8; e += NT) {
-      const int which = e / (R::MP * 8), t = (e >> 3) % R::MP, c = e & 7;
-      const uint16_t* src = which ? p.Qs : p.Ps;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < p.Mp && 8 * c < p.r8) v = *reinterpret_cast<const u32x4*>(src + (int64_t)t * p.r8 + 8 * c);
-      *reinterpret_cast<u32x4*>((which ? qst : pst) + nt_off(t, c)) = v;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int it = tid + NT * k, n8 = p.Mp * p.r8 / 8;
+      if (it >= 2 * n8) continue;
+      const int e = 8 * (it % n8);
+      *reinterpret_cast<u32x4*>((it < n8 ? pst : qst) + nt_off(e / p.r8, (e % p.r8) >> 3)) = bv[k];
     }
   }
   lds_barrier();  // the P_s and Q_s tiles are written

@@ -65,12 +65,11 @@ def few_path(bwd, nf4, M, d_in, d_out, r, rope=False):
     activations, 1 <= M <= 128, r a multiple of 8 up to 64, d_in and d_out
     multiples of 64 (d_out of 128 with RoPE, d_in of 128 in the backward and
     with NF4), at
-    most 256 column tiles of 128; the backward up to 64 tokens with a bf16 W
-    and up to 128 with NF4, the forward with NF4 up to 64."""
+    most 256 column tiles of 128; the backward, and the forward with NF4."""
     if not (1 <= M <= 128 and r % 8 == 0 and r <= 64 and d_in % 64 == 0 and d_out % 64 == 0):
         return False
     if (rope and d_out % 128) or ((bwd or nf4) and d_in % 128):
         return False
     if -(-(d_in if bwd else d_out) // 128) > 256:
         return False
-    return (nf4 or M <= 64) if bwd else (nf4 and M <= 64)
+    return bwd or nf4

@@ -1,6 +1,6 @@
-"""GPU parity of the few-token path (bf16 activations, r a multiple of 8 up
-to 64; the backward up to 64 tokens with a bf16 W and 128 with NF4, the NF4
-forward up to 64): a panel-partials launch (the backward then sums the
+"""GPU parity of the few-token path (1 to 128 tokens, bf16 activations, r a
+multiple of 8 up to 64; the backward, and the NF4 forward): a panel-partials
+launch (the backward then sums the
 panels), then one launch that streams W (bf16, or NF4 codes expanded on the
 fly) in 256 equal ranges of the column tiles' contraction stages; the last
 block to arrive at a tile sums its partials in block order, adds the rank term
@@ -38,10 +38,12 @@ def _check_path(kinds, nf4, M, d_in, d_out, r, rope=False):
     assert fwd or bwd, "a case outside the few-token path"
 
 
-# (M, d_in, d_out, r): every 16-row block count up to 64 (the bf16 W's range),
-# ranges of one to many stages per block, ranks 8 / 16 / 64
+# (M, d_in, d_out, r): every 16-row block count, ranges of one to many stages
+# per block, ranks 8 / 16 / 64, panels summed in the stream (fold) or between
+# the launches
 SHAPES = [(1, 256, 512, 8), (5, 384, 576, 16), (16, 4096, 4096, 16), (17, 1024, 2048, 64),
-          (33, 2048, 1024, 8), (64, 4096, 1024, 64), (49, 512, 4096, 16), (64, 5120, 1024, 64)]
+          (33, 2048, 1024, 8), (64, 4096, 1024, 64), (49, 512, 4096, 16), (100, 512, 4096, 16),
+          (128, 5120, 1024, 64)]
 
 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{i}x{o}r{r}" for m, i, o, r in SHAPES])
@@ -65,7 +67,8 @@ def test_few_parity(lib, shape):
 
 
 @pytest.mark.parametrize("M,d_in,d_out,r,seq", [(1, 1024, 512, 8, 64), (16, 4096, 4096, 16, 2048),
-                                                (64, 2048, 1024, 64, 100), (40, 1024, 4096, 16, 4096)])
+                                                (64, 2048, 1024, 64, 100), (40, 1024, 4096, 16, 4096),
+                                                (128, 1024, 4096, 16, 4096)])
 def test_few_rope_parity(lib, M, d_in, d_out, r, seq):
     X, W, A, B, dY = lora_inputs(730 + M, M, d_in, d_out, r, "bf16")
     pos = torch.from_numpy(gen.positions_mod(M, seq)).cuda()
@@ -84,7 +87,7 @@ def test_few_rope_parity(lib, M, d_in, d_out, r, seq):
 
 # NF4: a ragged forward tile (704 = 5.5 tiles of 128), up to 128 tokens
 @pytest.mark.parametrize("M,d_in,d_out,r", [(1, 512, 704, 8), (16, 5120, 2048, 64), (40, 1024, 4096, 16),
-                                            (128, 2048, 1024, 64)])
+                                            (100, 1024, 2048, 16), (128, 2048, 1024, 64)])
 def test_few_nf4_parity(lib, M, d_in, d_out, r):
     tab = gen.nf4_table()
     X, _, A, B, dY = lora_inputs(760 + M, M, d_in, d_out, r, "bf16")

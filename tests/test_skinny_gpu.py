@@ -75,9 +75,9 @@ def test_skinny_rope_parity(lib, M, d_in, d_out, r, seq):
 
 
 def test_skinny_not_taken_for_nf4(lib):
-    # an NF4 W beyond the few-token path's 64 tokens keeps the split path (its
+    # an NF4 W beyond the few-token path's 128 tokens keeps the split path (its
     # load stage dequantises in LDS tiles)
-    M, d_in, d_out, r = 100, 1024, 2048, 16
+    M, d_in, d_out, r = 200, 1024, 2048, 16
     tab = gen.nf4_table()
     X, _, A, B, _ = lora_inputs(12, M, d_in, d_out, r, "bf16")
     codes = gen.nf4_random_codes(13, d_out * d_in).cuda()
