@@ -98,6 +98,12 @@ KIND_OF = {
     "rope_inverse_kernel": "rope_inverse",
     "transpose_tile_kernel": "transpose_w",
     "split_finish_kernel": "split_finish",
+    "few_panel_kernel": "few_panel",
+    "few_reduce_kernel": "few_panel",
+    "few_fwd_nf4_kernel": "few_fwd",
+    "few_bwd_kernel": "few_bwd",
+    "nf4_dequant_t_kernel": "nf4_dequant",
+    "nf4_dequant_kernel": "nf4_dequant",
 }
 
 

@@ -1061,7 +1061,7 @@ hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
     hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
   } else if (what == 1) {
     // the forward's few-token launch exists for NF4 W only (a bf16 W takes the
-    // one-launch skinny kernel)
+    // one-launch skinny kernel, measured faster)
     if (!nf4) return hipErrorInvalidValue;
     hipLaunchKernelGGL((few_fwd_nf4_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT4), 0, st, a);
   } else {
