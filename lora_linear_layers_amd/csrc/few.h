@@ -226,24 +226,37 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
     const int k1 = min(p.d_in, k0 + p.Kp);
     const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
     const __amdgpu_buffer_rsrc_t ra = few_rsrc(p.A, (int64_t)p.r8 * p.d_in * 2);
-    for (int k = k0 + 32 * wave; k < k1; k += 128) {
-      const int kk = k + 8 * g;  // the lane's first element (k1 - k0 is a multiple of 32)
-      bf16x8 xf[MB], af[RB];
+    // UP of the wave's 32-wide steps at a time: all their loads in flight
+    // before the first product (steps past k1 load zeros and are skipped)
+    constexpr int UP = MB <= 2 ? 4 : (MB == 4 ? 2 : 1);
+    for (int kb = k0 + 32 * wave; kb < k1; kb += 128 * UP) {
+      bf16x8 xf[UP][MB], af[UP][RB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row = 16 * mb + l16;
-        xf[mb] = __builtin_bit_cast(bf16x8, few_ld16(rx, row < p.M ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+      for (int u = 0; u < UP; ++u) {
+        const int k = kb + 128 * u;
+        const int kk = k + 8 * g;  // the lane's first element (k1 - k0 is a multiple of 32)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row = 16 * mb + l16;
+          xf[u][mb] = __builtin_bit_cast(
+              bf16x8, few_ld16(rx, row < p.M && k < k1 ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = 16 * rb + l16;
+          af[u][rb] = __builtin_bit_cast(
+              bf16x8, few_ld16(ra, row < p.r8 && k < k1 ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+        }
       }
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int row = 16 * rb + l16;
-        af[rb] = __builtin_bit_cast(bf16x8, few_ld16(ra, row < p.r8 ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
+      for (int u = 0; u < UP; ++u) {
+        if (kb + 128 * u >= k1) break;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb < rb_n) acc[mb][rb] = mfma16(xf[u][mb], af[u][rb], acc[mb][rb]);
       }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          if (rb < rb_n) acc[mb][rb] = mfma16(xf[mb], af[rb], acc[mb][rb]);
     }
   } else {
     // Q chunk: [G rows] x B over i in [i0, i1), a head (128 rows of B) per
@@ -256,21 +269,9 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
     const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
     char* bt = smem + wave * BT;
     for (int h = i0 + 128 * wave; h < i1; h += 512) {
-      // B rows h .. h + 127 (fewer at the end: zeros), 8 rank columns per
-      // 16-byte chunk: lane -> row h + lane + 64 j, chunks 0 .. 7
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = lane + 64 * j;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const bool ok = h + row < i1 && 8 * cc < p.r8;
-          const u32x4 v = few_ld16(rbr, ok ? (uint32_t)(((h + row) * p.r8 + 8 * cc) * 2) : OOB);
-          *reinterpret_cast<u32x4*>(bt + nn_off<128>(row, cc)) = v;
-        }
-      }
-      // the wave reads back only what it wrote (its LDS operations complete in order)
       // G fragments: 4 steps of 32 rows of the head; with RoPE the lane's
-      // elements of steps 0 / 1 pair with those of steps 2 / 3
+      // elements of steps 0 / 1 pair with those of steps 2 / 3 (loaded first,
+      // in flight with the B rows)
       bf16x8 gf[4][MB];
 #pragma unroll
       for (int st = 0; st < 4; ++st)
@@ -281,6 +282,23 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
           gf[st][mb] = __builtin_bit_cast(
               bf16x8, few_ld16(ry, row < p.M && ii < i1 ? (uint32_t)((row * p.d_out + ii) * 2) : OOB));
         }
+      // B rows h .. h + 127 (fewer at the end: zeros), 8 rank columns per
+      // 16-byte chunk: lane -> row h + lane + 64 j, chunks 0 .. 7
+      u32x4 bv[2][8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = lane + 64 * j;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const bool ok = h + row < i1 && 8 * cc < p.r8;
+          bv[j][cc] = few_ld16(rbr, ok ? (uint32_t)(((h + row) * p.r8 + 8 * cc) * 2) : OOB);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(bt + nn_off<128>(lane + 64 * j, cc)) = bv[j][cc];
+      // the wave reads back only what it wrote (its LDS operations complete in order)
       if (p.rope) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
