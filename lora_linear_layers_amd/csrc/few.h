@@ -407,18 +407,15 @@ struct FewRing {
   static_assert(NS >= 3, "at least three stages");
 };
 
-// Partials exchanged between the blocks of one launch are written and read
-// with device-scope (agent) relaxed atomic stores and loads: on gfx950 these
-// are plain loads and stores marked coherent at device scope, which go
-// through the XCD's L2 to the device's coherence point.  A device-scope
-// fence would instead write back and invalidate the whole L2 of the XCD
-// (measured on MI355X: about 1.2 us per fence, serialised per XCD, which on
-// a 4096 x 4096 weight stream cost 4x its time).
+// Partials exchanged between the blocks of one launch are written with
+// device-scope (agent) relaxed atomic stores and read back with loads of the
+// same cache policy (few_sum4_dev): on gfx950 these are plain stores and
+// loads marked sc1, which go through the XCD's L2 to the device's coherence
+// point.  A device-scope fence would instead write back and invalidate the
+// whole L2 of the XCD (measured on MI355X: about 1.2 us per fence, serialised
+// per XCD, which on a 4096 x 4096 weight stream cost 4x its time).
 __device__ __forceinline__ void few_st_dev(float* q, float v) {
   __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float few_ld_dev(const float* q) {
-  return __hip_atomic_load(const_cast<float*>(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The work split of launch 2: the tiles' stages in sequence (a tile's in
@@ -888,10 +885,6 @@ few_fwd_nf4_kernel(const FewArgs p) {
     few_finish<BNF, NT4>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
                          p.rope != 0);
   }
-}
-
-__device__ __forceinline__ float nt_get(const char* tile, int r, int c) {
-  return bf2f(*reinterpret_cast<const uint16_t*>(tile + nt_off(r, c >> 3) + 2 * (c & 7)));
 }
 
 // ---------------------------------------------------------------------------

@@ -189,9 +189,9 @@ hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t
                               const float* table16, uint16_t* out, hipStream_t st);
 
 // Few-token path (few.h), MB = 16-row blocks of tokens (1, 2, 4 or 8): the
-// panel partials (Sp + Sq blocks); the backward's panel sums (2 blocks); the
-// forward (cdiv(d_out, 128) x Sk blocks) or the backward
-// (cdiv(d_in, 128) x Sk blocks).
+// panel partials (Sp + Sq blocks); the backward's panel sums when the stream
+// does not fold them; the W stream of the NF4 forward or of the backward
+// (nblk <= 256 blocks, each a contiguous range of the tiles' stages).
 struct FewArgs;
 hipError_t launch_few_panel(const FewArgs& a, int MB, hipStream_t st);
 hipError_t launch_few_reduce(const FewArgs& a, hipStream_t st);  // backward: P_s, Q_s between the launches
