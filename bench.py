@@ -101,6 +101,7 @@ KIND_OF = {
     "few_panel_kernel": "few_panel",
     "few_reduce_kernel": "few_panel",
     "few_fwd_nf4_kernel": "few_fwd",
+    "few_fwd_bf16_kernel": "few_fwd",
     "few_bwd_kernel": "few_bwd",
     "nf4_dequant_t_kernel": "nf4_dequant",
     "nf4_dequant_kernel": "nf4_dequant",

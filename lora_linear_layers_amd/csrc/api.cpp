@@ -79,10 +79,13 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   const int64_t lim = int64_t(1) << 30;
   if (d_in * d_out * 2 >= lim || M * std::max(d_in, d_out) * 2 >= lim) return F;
   // taken where it measured faster on MI355X than the skinny and split-GEMM
-  // paths (q_proj 4096 x 4096 bf16, an NF4 MLP gate 5120 -> 27392): the
-  // backward, and the forward with NF4 (a bf16 forward takes the one-launch
-  // skinny kernel)
-  if (!bwd && !nf4) return F;
+  // paths: the backward; the forward with NF4; the forward with a bf16 W up
+  // to 64 tokens wherever the one-launch skinny kernel (one block per 16
+  // output columns, each forming the whole rank panel) underfills the chip or
+  // re-reads much of A: RoPE (4 skinny blocks per head), more than 16 tokens,
+  // a rank above 16, or W of 2^25 elements or more.  Small plain problems keep
+  // skinny's single launch (4096 x 4096, r = 16, 1 token: 16.6 us against 20.7).
+  if (!bwd && !nf4 && !(M <= 64 && (rope || M > 16 || r > 16 || d_in * d_out >= (int64_t(1) << 25)))) return F;
   F.MB = M <= 16 ? 1 : (M <= 32 ? 2 : (M <= 64 ? 4 : 8));
   F.Mp = 16 * F.MB;
   const int64_t ncols = bwd ? d_in : d_out, K = bwd ? d_out : d_in;

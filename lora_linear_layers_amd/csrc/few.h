@@ -1,5 +1,6 @@
 // few.h - the fused LoRA layer for few tokens (M <= 128, bf16 activations):
-// the NF4 forward in two launches, the backward in three.
+// the forward in two launches (NF4 W, or bf16 W where the dispatch takes it),
+// the backward in three or two.
 //
 //     forward   Y  = X W^T + bf16(s X A^T) B^T           (page "UnSloth加速微调
 //     backward  dX = G W + bf16(s G B) A,                  体验…", sections 算子融合
@@ -19,10 +20,11 @@
 //     stream sums the panels itself, P_s = bf16(s P) and Q_s = bf16(s Q),
 //     while its first stages fly when the partials are few enough (fold);
 //     else a launch between sums them once (few_reduce_kernel).
-//   the W stream (few_fwd_nf4_kernel / few_bwd_kernel): column tiles of 128
-//     outputs, each a sequence of contraction stages; the tiles' stages in
-//     sequence are cut into 256 equal contiguous ranges, one block (one CU)
-//     each, so every CU streams the same share of W in one round.  W stages
+//   the W stream (few_fwd_nf4_kernel, few_fwd_bf16_kernel, few_bwd_kernel):
+//     column tiles of 128 outputs, each a sequence of contraction stages; the
+//     tiles' stages in sequence are cut into 256 equal contiguous ranges,
+//     one block (one CU) each, so every CU streams the same share of W in
+//     one round.  W stages
 //     land in a ring of LDS slots by DMA (buffer_load ... lds), the stage's
 //     resource based at its tile so rows past the end read zero.  A block
 //     leaves one fp32 partial per tile it touches (at most two); the LAST
@@ -884,6 +886,188 @@ few_fwd_nf4_kernel(const FewArgs p) {
     const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
     few_finish<BNF, NT4>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
                          p.rope != 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launch 2, forward with a bf16 W: the same tiles, ranges, partials, rank term
+// and finish as the NF4 form, with 64-deep stages of W (128 rows of 128 bytes,
+// NT layout) and of the activations landing by DMA; 4 waves of 32 columns.
+// ---------------------------------------------------------------------------
+template <int MB>
+__global__ void __launch_bounds__(few::NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+few_fwd_bf16_kernel(const FewArgs p) {
+  using namespace few;
+  constexpr int BNF = 128, NJ = 2;
+  using R = FewRing<MB, false, BNF, BNF * 128>;
+  constexpr int NS = R::NS;
+  constexpr int WI = BNF / 32;  // W DMAs per wave per stage (8 rows each)
+  constexpr int PER = WI + R::XI;
+  static_assert(R::STAGE >= R::MP * 128, "P_s fits a ring slot");
+  __shared__ __attribute__((aligned(1024))) char smem[R::LDS];
+  char* ring = smem + R::FIXED;
+  auto wslot = [&](int slot) { return ring + slot * R::STAGE; };
+  auto xslot = [&](int slot) { return ring + slot * R::STAGE + R::WSLOT; };
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  const FewSpan sp = few_span(p, blockIdx.x);
+  const int nk = sp.nk;
+  const bool two = sp.te < nk - 1;
+
+  const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
+  // W of the block's two tiles, each resource based at the tile's first row:
+  // rows past d_out lie past its end and read zero
+  const int64_t r0 = (int64_t)sp.a0 * BNF, r1 = (int64_t)min(sp.a0 + 1, p.n_tiles - 1) * BNF;
+  const __amdgpu_buffer_rsrc_t rw0 = few_rsrc(p.W + r0 * p.d_in, (p.d_out - r0) * p.d_in * 2);
+  const __amdgpu_buffer_rsrc_t rw1 = few_rsrc(p.W + r1 * p.d_in, (p.d_out - r1) * p.d_in * 2);
+  // DMA lane mapping of an NT tile: 8 rows x 128 bytes per instruction, the
+  // lane lands at physical chunk lane & 7 of row lane / 8 and so fetches
+  // logical chunk (lane & 7) ^ (row & 7).  Offsets at the tile's stage 0
+  // (stage st adds a scalar offset).
+  const int drow = lane >> 3, dpc = lane & 7;
+  uint32_t vw[WI], vx[R::XI];
+#pragma unroll
+  for (int i = 0; i < WI; ++i) {
+    const int row = 8 * (WI * wave + i) + drow;
+    vw[i] = (uint32_t)((row * p.d_in + 8 * (dpc ^ (row & 7))) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < R::XI; ++i) {
+    const int row = 8 * (wave + 4 * i) + drow;
+    vx[i] = row < p.M ? (uint32_t)((row * p.d_in + 8 * (dpc ^ (row & 7))) * 2) : OOB;
+  }
+  auto issue = [&](int t, int slot) {
+    const bool second = t > sp.te;
+    const int st = second ? t - sp.te - 1 : sp.s0 + t;
+    const __amdgpu_buffer_rsrc_t rw = second ? rw1 : rw0;
+#pragma unroll
+    for (int i = 0; i < WI; ++i) few_dma(rw, wslot(slot) + (WI * wave + i) * 1024, vw[i], st * (BK * 2));
+#pragma unroll
+    for (int i = 0; i < R::XI; ++i) few_dma(rx, xslot(slot) + (wave + 4 * i) * 1024, vx[i], st * (BK * 2));
+  };
+
+  // acc0: tile a0's sum once the range has moved on; accr: tile a0 + 1's
+  // starting value (its rank term)
+  f32x4 acc[MB][NJ], acc0[MB][NJ], accr[MB][NJ];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[mb][j] = acc0[mb][j] = accr[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot) {
+    const char* xs = xslot(slot);
+    const char* wt = wslot(slot);
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep) {
+      bf16x8 bfr[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bfr[j] = nt_frag(wt, 32 * wave + 16 * j, sstep, lane);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(xs, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[mb][j] = mfma16(af, bfr[j], acc[mb][j]);
+      }
+    }
+  };
+  auto tile_done = [&](int t) {
+    if (t == sp.te && two) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          acc0[mb][j] = acc[mb][j];
+          acc[mb][j] = accr[mb][j];
+        }
+    }
+  };
+
+  // The rank term P_s B^T of a tile goes into the partial of the block that
+  // streams the tile's first stage (tile a0 when s0 = 0, tile a0 + 1 when the
+  // range reaches it).  Its B fragments (rows = the wave's columns, r8
+  // contiguous) are loaded ahead of the DMAs; P_s is summed from the panel
+  // partials into LDS no stage uses yet (the last ring slot) while the first
+  // stages fly.
+  const bool rk0 = sp.s0 == 0;
+  const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
+  bf16x8 bq[2][2][NJ];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int q = 32 * sstep + 8 * g, col = (sp.a0 + u) * BNF + 32 * wave + 16 * j + l16;
+        const bool ok = (u ? two : rk0) && col < p.d_out && q < p.r8;
+        bq[u][sstep][j] = __builtin_bit_cast(bf16x8, few_ld16(rbr, ok ? (uint32_t)((col * p.r8 + q) * 2) : OOB));
+      }
+
+  few_unroll<NS - 1>([&](auto sc) {
+    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
+  });
+  if (rk0 || two) {
+    char* ps = wslot(NS - 1);
+    few_panel_sum<R::MP>(p.Pp, p.Sp, p, ps);
+    __syncthreads();
+#pragma unroll
+    for (int sstep = 0; sstep < 2; ++sstep)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8 af = nt_frag(ps, 16 * mb, sstep, lane);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (rk0) acc[mb][j] = mfma16(af, bq[0][sstep][j], acc[mb][j]);
+          if (two) accr[mb][j] = mfma16(af, bq[1][sstep][j], accr[mb][j]);
+        }
+      }
+    // (the slot's first DMA, at stage 0, follows the loop's first barrier)
+  }
+  // The stage loop, unrolled so that every ring slot index is a constant.
+  constexpr int U = (NS % 2) ? 2 * NS : NS;
+  for (int t0 = 0; t0 < nk; t0 += U) {
+    few_unroll<U>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const int t = t0 + j;
+      if (t >= nk) return;
+      few_wait_stages<PER>(min(NS - 2, nk - 1 - t));
+      lds_barrier();
+      if (t + NS - 1 < nk) issue(t + NS - 1, (j + NS - 1) % NS);
+      compute(j % NS);
+      tile_done(t);
+    });
+  }
+
+  // ---- one partial per covered tile, then the last block of a tile sums ----
+  const int b = blockIdx.x, na = two ? 2 : 1;
+  auto store_part = [&](const f32x4 (&v)[MB][NJ], int a) {
+    float* cp = p.Cp + (int64_t)(b + a) * p.Mp * BNF;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int vv = 0; vv < 4; ++vv) {
+          const int row = 16 * mb + 4 * g + vv;
+          if (row < p.M) few_st_dev(cp + row * BNF + 32 * wave + 16 * j + l16, v[mb][j][vv]);
+        }
+  };
+  if (two) store_part(acc0, sp.a0);
+  store_part(acc, sp.a0 + na - 1);
+  int* flag = reinterpret_cast<int*>(smem + R::LDS - 16);
+  few_arrive(p.cnt + sp.a0, na,
+             [&](int i) {
+               const int a = sp.a0 + i;
+               return few_blk_of(p, (a + 1) * p.nkt - 1) - few_blk_of(p, a * p.nkt) + 1;
+             },
+             flag);
+  const int fin0 = flag[0], fin1 = na > 1 ? flag[1] : 0;
+  for (int i = 0; i < na; ++i) {
+    if (!(i ? fin1 : fin0)) continue;
+    const int a = sp.a0 + i;
+    const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
+    few_finish<BNF>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
+                    p.rope != 0);
   }
 }
 

@@ -1060,10 +1060,10 @@ hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
   if (what == 0) {
     hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
   } else if (what == 1) {
-    // the forward's few-token launch exists for NF4 W only (a bf16 W takes the
-    // one-launch skinny kernel, measured faster)
-    if (!nf4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((few_fwd_nf4_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT4), 0, st, a);
+    if (nf4)
+      hipLaunchKernelGGL((few_fwd_nf4_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT4), 0, st, a);
+    else
+      hipLaunchKernelGGL((few_fwd_bf16_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT), 0, st, a);
   } else {
     const dim3 grid((unsigned)a.nblk);
     if (nf4)
@@ -1079,6 +1079,13 @@ hipError_t few_dispatch(const FewArgs& a, int MB, int what, bool nf4, hipStream_
   if (a.Sp < 1 || a.n_tiles < 1 || a.n_tiles > a.nblk || a.nkt < 1 || a.T != a.n_tiles * a.nkt || a.nblk < 1 ||
       a.nblk > few::GRID || a.nblk > a.T)
     return hipErrorInvalidValue;
+  // the W stream's tiles and stages cover its output columns and contraction
+  // exactly (stages 128 deep in the NF4 forward, 64 otherwise)
+  if (what > 0) {
+    const int64_t ncols = what == 1 ? a.d_out : a.d_in, K = what == 1 ? a.d_in : a.d_out;
+    if ((ncols + few::BN - 1) / few::BN != a.n_tiles || (int64_t)a.nkt * (what == 1 && nf4 ? 128 : 64) != K)
+      return hipErrorInvalidValue;
+  }
   switch (MB) {
     case 1: return few_launch<1>(a, what, nf4, st);
     case 2: return few_launch<2>(a, what, nf4, st);

@@ -190,8 +190,8 @@ hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t
 
 // Few-token path (few.h), MB = 16-row blocks of tokens (1, 2, 4 or 8): the
 // panel partials (Sp + Sq blocks); the backward's panel sums when the stream
-// does not fold them; the W stream of the NF4 forward or of the backward
-// (nblk <= 256 blocks, each a contiguous range of the tiles' stages).
+// does not fold them; the W stream of the forward (NF4 or bf16 W) or of the
+// backward (nblk <= 256 blocks, each a contiguous range of the tiles' stages).
 struct FewArgs;
 hipError_t launch_few_panel(const FewArgs& a, int MB, hipStream_t st);
 hipError_t launch_few_reduce(const FewArgs& a, hipStream_t st);  // backward: P_s, Q_s between the launches

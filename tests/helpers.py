@@ -64,12 +64,25 @@ def few_path(bwd, nf4, M, d_in, d_out, r, rope=False):
     """Whether the library takes the few-token path (its dispatch rule): bf16
     activations, 1 <= M <= 128, r a multiple of 8 up to 64, d_in and d_out
     multiples of 64 (d_out of 128 with RoPE, d_in of 128 in the backward and
-    with NF4), at
-    most 256 column tiles of 128; the backward, and the forward with NF4."""
+    with NF4), at most 256 column tiles of 128; the backward, the forward with
+    NF4, and the forward with a bf16 W up to 64 tokens with RoPE, more than 16
+    tokens, a rank above 16 or W of 2^25 elements or more."""
     if not (1 <= M <= 128 and r % 8 == 0 and r <= 64 and d_in % 64 == 0 and d_out % 64 == 0):
         return False
     if (rope and d_out % 128) or ((bwd or nf4) and d_in % 128):
         return False
     if -(-(d_in if bwd else d_out) // 128) > 256:
         return False
-    return bwd or nf4
+    return bwd or nf4 or (M <= 64 and (rope or M > 16 or r > 16 or d_in * d_out >= 1 << 25))
+
+
+def fwd_kind(M, d_in, d_out, r, rope=False):
+    """The launch that computes a bf16 forward's product at few tokens: the
+    few-token stream, else the one-launch skinny kernel (up to 64 tokens, r a
+    multiple of 8 up to 64, d_in a multiple of 8, d_out of 128 with RoPE), else
+    the split GEMM."""
+    if few_path(False, False, M, d_in, d_out, r, rope):
+        return "few_fwd"
+    if 1 <= M <= 64 and r % 8 == 0 and r <= 64 and d_in % 8 == 0 and not (rope and d_out % 128):
+        return "skinny_fwd"
+    return "gemm_bf16_128x128_nt_split"

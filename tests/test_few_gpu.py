@@ -1,8 +1,8 @@
 """GPU parity of the few-token path (1 to 128 tokens, bf16 activations, r a
-multiple of 8 up to 64; the backward, and the NF4 forward): a panel-partials
-launch (the backward then sums the
-panels), then one launch that streams W (bf16, or NF4 codes expanded on the
-fly) in 256 equal ranges of the column tiles' contraction stages; the last
+multiple of 8 up to 64; the backward, the NF4 forward and the bf16 forward
+where the dispatch rule takes it): a panel-partials launch (the backward
+then sums the panels), then one launch that streams W (bf16, or NF4 codes
+expanded on the fly) in 256 equal ranges of the column tiles' contraction stages; the last
 block to arrive at a tile sums its partials in block order, adds the rank term
 and stores (or rotates, RoPE).  Against the float64 oracle at the bf16 bar;
 repeats are bitwise equal (the arrival order of blocks must not change a bit);
@@ -34,6 +34,8 @@ def _check_path(kinds, nf4, M, d_in, d_out, r, rope=False):
     """The few-token launches ran exactly where the dispatch rule takes them."""
     fwd, bwd = few_path(False, nf4, M, d_in, d_out, r, rope), few_path(True, nf4, M, d_in, d_out, r, rope)
     assert ("few_fwd" in kinds) == fwd and ("few_bwd" in kinds) == bwd, kinds
+    if not nf4 and not fwd:
+        assert ("skinny_fwd" in kinds) == (M <= 64), kinds
     assert ("few_panel" in kinds) == (fwd or bwd), kinds
     assert fwd or bwd, "a case outside the few-token path"
 

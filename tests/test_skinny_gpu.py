@@ -3,7 +3,9 @@ tokens, rank a multiple of 8 up to 64, bf16 W) against the float64 oracle:
 ragged token counts, outputs that are not a multiple of 16 wide,
 contractions that are not a multiple of 32, both rank widths and both strip
 widths (4 strips from 12288 outputs on), RoPE.  Integer inputs make the
-plain case exact."""
+plain case exact.  Skinny keeps the shapes the few-token stream does not
+take (small plain problems, d_in or d_out off a multiple of 64), so the cases
+with RoPE, more than 16 tokens or a rank above 16 have such a dimension."""
 import math
 
 import numpy as np
@@ -27,8 +29,8 @@ def _kinds(fn):
 
 
 # (M, d_in, d_out, r)
-PLAIN = [(1, 4096, 4096, 16), (5, 2048, 520, 8), (16, 4104, 1024, 24), (17, 1024, 2048, 64),
-         (33, 2056, 776, 16), (64, 4096, 1024, 64), (12, 1024, 12288, 16), (64, 512, 12296, 64)]
+PLAIN = [(1, 4096, 4096, 16), (5, 2048, 520, 8), (16, 4104, 1024, 24), (17, 1032, 2048, 64),
+         (33, 2056, 776, 16), (64, 4104, 1024, 64), (12, 1024, 12288, 16), (64, 512, 12296, 64)]
 
 
 @pytest.mark.parametrize("shape", PLAIN, ids=[f"{m}x{i}x{o}r{r}" for m, i, o, r in PLAIN])
@@ -43,7 +45,7 @@ def test_skinny_plain_parity(lib, shape):
     assert err <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("M,d_in,d_out,r", [(16, 2048, 1024, 8), (64, 1024, 512, 64)])
+@pytest.mark.parametrize("M,d_in,d_out,r", [(16, 2048, 1024, 8), (64, 1032, 512, 64)])
 def test_skinny_integer_exact(lib, M, d_in, d_out, r):
     # sparse {-1, 0, 1} inputs: every product, panel entry and sum is a small
     # integer, so the fused forward must equal the oracle exactly
@@ -60,8 +62,8 @@ def test_skinny_integer_exact(lib, M, d_in, d_out, r):
     assert np.array_equal(cpu64(Y), Yr)
 
 
-@pytest.mark.parametrize("M,d_in,d_out,r,seq", [(1, 4096, 4096, 16, 2048), (40, 2048, 1024, 64, 40),
-                                                (64, 1024, 512, 8, 8192)])
+@pytest.mark.parametrize("M,d_in,d_out,r,seq", [(1, 4104, 4096, 16, 2048), (40, 2056, 1024, 64, 40),
+                                                (64, 1032, 512, 8, 8192)])
 def test_skinny_rope_parity(lib, M, d_in, d_out, r, seq):
     X, W, A, B, _ = lora_inputs(70 + M, M, d_in, d_out, r, "bf16")
     pos = torch.from_numpy(gen.positions_mod(M, seq)).cuda()

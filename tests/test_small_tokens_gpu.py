@@ -3,7 +3,8 @@ tests cover it) the dX GEMM (and the forward beyond 64 tokens, or with a rank
 that is not a multiple of 8 or above 64) splits its contraction into fp32
 partials (the 128x128 tiles alone would leave most CUs idle) and a
 fixed-order sum finishes them (with the RoPE rotation for q/k); up to 64
-tokens the bf16 forward is one fused launch (skinny_fwd).  The profiler
+tokens the bf16 forward is one fused launch (skinny_fwd) where the few-token
+stream does not take it.  The profiler
 confirms which path ran; the oracle is the float64 reference as everywhere
 else."""
 import math
@@ -15,7 +16,7 @@ import torch
 import oracle as O
 from lora_linear_layers_amd import _lib
 from synth import gen
-from tests.helpers import TOL, cpu64, few_path, lora_inputs, rel
+from tests.helpers import TOL, cpu64, few_path, fwd_kind, lora_inputs, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -26,11 +27,6 @@ def _kinds(lib, fn):
     torch.cuda.synchronize()
     _lib.profile_end()
     return out, set(_lib.profile_report())
-
-
-def fused_fwd(M, r):
-    """Whether the forward takes the one-launch few-token kernel."""
-    return 1 <= M <= 64 and r % 8 == 0 and r <= 64
 
 
 # (M, d_in, d_out, r): contraction splits of 2..16, ragged splits and ranks
@@ -49,7 +45,7 @@ def test_small_token_parity(lib, shape):
         assert "few_bwd" in kinds, kinds
     else:
         assert {"gemm_bf16_128x128_nn_split", "split_finish"} <= kinds, kinds
-    assert ("skinny_fwd" if fused_fwd(M, r) else "gemm_bf16_128x128_nt_split") in kinds, kinds
+    assert fwd_kind(M, d_in, d_out, r) in kinds, kinds
     Yr = O.lora_forward(X, W, A, B, s)
     dXr, dAr, dBr = O.lora_backward(X, W, A, B, s, dY)
     errs = dict(Y=rel(Y, Yr), dX=rel(dX, dXr), dA=rel(dA, dAr), dB=rel(dB, dBr))
@@ -73,7 +69,7 @@ def test_small_token_rope_parity(lib, M, d_in, d_out, r, seq):
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (lib.lora_qk_rope_fwd(X, W, A, B, s, pos, cos, sin),
                                                    lib.lora_qk_rope_bwd(X, W, A, B, s, pos, cos, sin, dY)))
     assert ("few_bwd" if few_path(True, False, M, d_in, d_out, r, rope=True) else "split_finish") in kinds, kinds
-    assert ("skinny_fwd" if fused_fwd(M, r) else "gemm_bf16_128x128_nt_split") in kinds, kinds
+    assert fwd_kind(M, d_in, d_out, r, rope=True) in kinds, kinds
     p = pos.cpu().numpy()
     Yr = O.qk_rope_forward(X, W, A, B, s, p)
     dXr, dAr, dBr = O.qk_rope_backward(X, W, A, B, s, p, dY)
@@ -105,7 +101,7 @@ def test_small_token_nf4_parity(lib, M, d_in, d_out, r):
 
 def test_small_token_integer_exact(lib):
     # Sparse {-1, 0, 1} inputs: every partial, panel and output is a small
-    # integer, so the split path must equal the oracle exactly.
+    # integer, so the fixed-order sums must equal the oracle exactly.
     M, d_in, d_out, r, s = 64, 2048, 1024, 16, 1.0
     g = torch.Generator().manual_seed(91)
 
@@ -117,7 +113,7 @@ def test_small_token_integer_exact(lib):
         sp((M, d_out), 1 / 8)
     (Y, (dX, dA, dB)), kinds = _kinds(lib, lambda: (lib.lora_linear_fwd(X, W, A, B, s),
                                                    lib.lora_linear_bwd(X, W, A, B, s, dY)))
-    assert {"skinny_fwd", "few_bwd"} <= kinds, kinds
+    assert {fwd_kind(M, d_in, d_out, r), "few_bwd"} <= kinds, kinds
     Yr = O.lora_forward(X, W, A, B, s)
     dXr, dAr, dBr = O.lora_backward(X, W, A, B, s, dY)
     assert np.abs(O.lora_panel(X, A)).max() <= 256 and np.abs(cpu64(dY) @ cpu64(B)).max() <= 256

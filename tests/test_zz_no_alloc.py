@@ -4,7 +4,8 @@ ABI it must give exactly what lora_linear_fwd gives (same kernels, so bit for
 bit) and meet the oracle's bar, on calls in a row that reuse the array with
 shrinking problems (a later call must not see an earlier call's data), over
 every forward path: whole 256 x 256 tiles, generic tiles, the few-token split
-and one-launch paths, a ragged rank and fp32."""
+and one-launch paths, the few-token W stream (its arrival counters and
+partials live in the array), a ragged rank and fp32."""
 import ctypes
 
 import numpy as np
@@ -19,6 +20,7 @@ SEQUENCES = [
     [("bf16", 8192, 4096, 4096, 64), ("bf16", 300, 512, 768, 16)],
     [("bf16", 2100, 1024, 4096, 40), ("bf16", 100, 1024, 2048, 5), ("bf16", 16, 512, 512, 8)],
     [("f32", 1000, 520, 392, 24), ("f32", 128, 256, 256, 8)],
+    [("bf16", 64, 2048, 4096, 32), ("bf16", 24, 1024, 1024, 8)],
 ]
 
 
