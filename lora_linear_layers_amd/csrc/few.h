@@ -194,19 +194,24 @@ __device__ __forceinline__ void few_cs4(const FewArgs& p, int t, int f, float4& 
 // ---------------------------------------------------------------------------
 // launch 1: panel partials.  Blocks [0, Sp): P chunk b of d_in; blocks
 // [Sp, Sp + Sq): Q chunk of d_out.  A block's 4 waves take the chunk's 32-wide
-// steps in turn (Q with RoPE: a wave takes a whole head, its pairs (i, i+64)
-// in one lane), then the waves' sums meet in LDS.
+// steps in turn (Q: a wave takes a whole head, so that with RoPE its pairs
+// (i, i+64) meet in one lane), then the waves' sums meet in LDS.
 // ---------------------------------------------------------------------------
 template <int MB>
 __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
   using namespace few;
   constexpr int RB = MAXR / 16;
-  // Q: each wave's 128 rows of B (an NN tile of 64 rank columns, 16 KB);
-  // afterwards the waves' partial sums [4][MB * 16][MAXR] fp32
-  constexpr int BT = 128 * 128;
-  constexpr int RED = 4 * MB * 16 * MAXR * 4;
-  __shared__ __attribute__((aligned(16))) char smem[RED > 4 * BT ? RED : 4 * BT];
-  float(*red)[MB * 16][MAXR] = reinterpret_cast<float(*)[MB * 16][MAXR]>(smem);
+  constexpr int MP = MB * 16;
+  // LDS: Q's per-wave B tiles (128 rows of B, an NN tile of 64 rank columns,
+  // 16 KB each), then with RoPE the cos | sin rows of the tokens' positions
+  // (128 floats a row, padded to CSW); afterwards, over both, the waves'
+  // partial sums [4][MP][RW] fp32 (rows padded so that the 4 row groups of a
+  // fragment's store fall in different banks)
+  constexpr int BT = 128 * 128, CSW = 132, RW = MAXR + 4;
+  constexpr int TOP = 4 * BT + MP * CSW * 4, RED = 4 * MP * RW * 4;
+  __shared__ __attribute__((aligned(16))) char smem[RED > TOP ? RED : TOP];
+  float(*red)[MP][RW] = reinterpret_cast<float(*)[MP][RW]>(smem);
+  float* cst = reinterpret_cast<float*>(smem + 4 * BT);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
@@ -228,9 +233,10 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
     const int k1 = min(p.d_in, k0 + p.Kp);
     const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
     const __amdgpu_buffer_rsrc_t ra = few_rsrc(p.A, (int64_t)p.r8 * p.d_in * 2);
-    // UP of the wave's 32-wide steps at a time: all their loads in flight
-    // before the first product (steps past k1 load zeros and are skipped)
-    constexpr int UP = MB <= 2 ? 4 : (MB == 4 ? 2 : 1);
+    // UP of the wave's 32-wide steps at a time (a chunk of up to 512 is 4 a
+    // wave): all their loads in flight before the first product (steps past
+    // k1 load zeros and are skipped)
+    constexpr int UP = MB <= 4 ? 4 : 2;
     for (int kb = k0 + 32 * wave; kb < k1; kb += 128 * UP) {
       bf16x8 xf[UP][MB], af[UP][RB];
 #pragma unroll
@@ -270,11 +276,13 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
     const __amdgpu_buffer_rsrc_t ry = few_rsrc(p.dY, (int64_t)p.M * p.d_out * 2);
     const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
     char* bt = smem + wave * BT;
-    for (int h = i0 + 128 * wave; h < i1; h += 512) {
-      // G fragments: 4 steps of 32 rows of the head; with RoPE the lane's
-      // elements of steps 0 / 1 pair with those of steps 2 / 3 (loaded first,
-      // in flight with the B rows)
-      bf16x8 gf[4][MB];
+    // a head's loads: dY fragments (4 steps of 32 rows of the head; with RoPE
+    // the lane's elements of steps 0 / 1 pair with those of steps 2 / 3) and
+    // B rows h .. h + 127 (fewer at the end: zeros), 8 rank columns per
+    // 16-byte chunk: lane -> row h + lane + 64 j, chunks 0 .. 7
+    bf16x8 gf[4][MB];
+    u32x4 bv[2][8];
+    auto load_g = [&](int h) {
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -284,9 +292,8 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
           gf[st][mb] = __builtin_bit_cast(
               bf16x8, few_ld16(ry, row < p.M && ii < i1 ? (uint32_t)((row * p.d_out + ii) * 2) : OOB));
         }
-      // B rows h .. h + 127 (fewer at the end: zeros), 8 rank columns per
-      // 16-byte chunk: lane -> row h + lane + 64 j, chunks 0 .. 7
-      u32x4 bv[2][8];
+    };
+    auto load_b = [&](int h) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int row = lane + 64 * j;
@@ -296,6 +303,52 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
           bv[j][cc] = few_ld16(rbr, ok ? (uint32_t)(((h + row) * p.r8 + 8 * cc) * 2) : OOB);
         }
       }
+    };
+    // With RoPE, the cos | sin rows of each token's position (zeros for a
+    // position outside the cache) go to LDS in 16-byte pieces, item e ->
+    // token e / 16, piece e % 16 of cos and of sin.  The positions are loaded
+    // first and the first head's loads after them (128 tokens: B only, for
+    // registers), so that the wait for the positions does not wait for those
+    // (loads complete in issue order) and they fly while the rows land.  The
+    // loads take no branch (rows past M read token 0's position, an invalid
+    // position reads row 0 and is zeroed), so that all of them are in flight
+    // at once.
+    constexpr int IT = MP * 16 / NT;
+    constexpr bool PRE_G = MB <= 4;
+    int32_t pq[IT];
+    if (p.rope) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int t = (tid + NT * i) >> 4;
+        pq[i] = p.pos[t < p.M ? t : 0];
+      }
+    }
+    // (a wave without a head loads zeros: its offsets lie past the resources)
+    const int hw = i0 + 128 * wave;
+    load_b(hw);
+    if (PRE_G) load_g(hw);
+    if (p.rope) {
+      f32x4 cv[IT], sv[IT];
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int pc = (tid + NT * i) & 15;
+        const int64_t off = (int64_t)(rope_pos_ok(pq[i], p.max_pos) ? pq[i] : 0) * 64 + 4 * pc;
+        cv[i] = *reinterpret_cast<const f32x4*>(p.cosc + off);
+        sv[i] = *reinterpret_cast<const f32x4*>(p.sinc + off);
+      }
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int e = tid + NT * i, t = e >> 4, pc = e & 15;
+        const bool ok = rope_pos_ok(pq[i], p.max_pos);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(cst + t * CSW + 4 * pc) = ok ? cv[i] : z;
+        *reinterpret_cast<f32x4*>(cst + t * CSW + 64 + 4 * pc) = ok ? sv[i] : z;
+      }
+      __syncthreads();
+    }
+    for (int h = hw; h < i1; h += 512) {
+      if (h != hw) load_b(h);
+      if (h != hw || !PRE_G) load_g(h);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -309,11 +362,11 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             const int f = 32 * st + 8 * g;  // frequency of the lane's first pair
-            float4 c0, s0, c1, s1;
-            few_cs4(p, row, f, c0, s0);
-            few_cs4(p, row, f + 4, c1, s1);
-            const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const float* cr = cst + row * CSW + f;
+            const f32x4 c0 = *reinterpret_cast<const f32x4*>(cr), c1 = *reinterpret_cast<const f32x4*>(cr + 4);
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(cr + 64), s1 = *reinterpret_cast<const f32x4*>(cr + 68);
+            const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+            const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
             const u32x4 y1 = __builtin_bit_cast(u32x4, gf[st][mb]);
             const u32x4 y2 = __builtin_bit_cast(u32x4, gf[st + 2][mb]);
             u32x4 g1, g2;
@@ -346,7 +399,8 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
       }
     }
   }
-  // the waves' sums meet in LDS (over the B tiles: every wave is done with them)
+  // the waves' sums meet in LDS (over the B tiles and RoPE rows: every wave
+  // is done with them)
   __syncthreads();
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -355,11 +409,15 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) red[wave][16 * mb + 4 * g + v][16 * rb + l16] = acc[mb][rb][v];
   __syncthreads();
+  // a thread stores 4 rank columns of a token row: 16 threads a row
   float* out = isq ? p.Qp + (int64_t)(blockIdx.x - p.Sp) * p.Mp * p.r8 : p.Pp + (int64_t)blockIdx.x * p.Mp * p.r8;
-  for (int e = tid; e < p.Mp * p.r8; e += NT) {
-    const int t = e / p.r8, q = e - t * p.r8;
-    out[e] = ((red[0][t][q] + red[1][t][q]) + red[2][t][q]) + red[3][t][q];
-  }
+  const int q = 4 * (tid & 15);
+  if (q < p.r8)
+    for (int t = tid >> 4; t < p.Mp; t += NT / 16) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(&red[0][t][q]), s1 = *reinterpret_cast<const f32x4*>(&red[1][t][q]);
+      const f32x4 s2 = *reinterpret_cast<const f32x4*>(&red[2][t][q]), s3 = *reinterpret_cast<const f32x4*>(&red[3][t][q]);
+      *reinterpret_cast<f32x4*>(out + t * p.r8 + q) = ((s0 + s1) + s2) + s3;
+    }
 }
 
 // ---------------------------------------------------------------------------
