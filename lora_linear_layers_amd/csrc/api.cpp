@@ -70,8 +70,11 @@ struct FewPlan {
 // cut into few::GRID equal contiguous ranges, one block each (at most as
 // many tiles as blocks, so a range covers one tile or two).  P in at most 16
 // chunks of d_in (the forward's finishing blocks sum them with every load in
-// flight); Q in at most 32 chunks of d_out of whole 128-row heads (summed with
-// P between the backward's launches, every slab's load in flight).
+// flight); Q in chunks of d_out of whole 128-row heads, about 32 of them but
+// at most 512 rows each, one head per wave (measured: a wave with two heads
+// in turn, on d_out = 27392, cost 3-7 us; fewer blocks with every wave busy,
+// on d_out = 4096, cost 3 us more than 32 blocks with one); summed with P
+// between the backward's launches, 32 slabs' loads in flight.
 FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t d_out, int64_t r) {
   FewPlan F;
   if (M < 1 || M > 16 * few::MAXMB || r % 8 || r > few::MAXR || d_in % 64 || d_out % 64) return F;
@@ -104,7 +107,8 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, F.fold ? 8 : 16), 128));
   F.Sp = (int)cdiv(d_in, F.Kp);
   if (bwd) {
-    F.Kq = (int)std::max<int64_t>(128, rup(cdiv(d_out, F.fold ? 8 : 32), 128));
+    F.Kq = (int)(F.fold ? std::max<int64_t>(128, rup(cdiv(d_out, 8), 128))
+                        : std::min<int64_t>(512, std::max<int64_t>(128, rup(cdiv(d_out, 32), 128))));
     F.Sq = (int)cdiv(d_out, F.Kq);
   }
   size_t off = 0;

@@ -24,9 +24,9 @@
 //     column tiles of 128 outputs, each a sequence of contraction stages; the
 //     tiles' stages in sequence are cut into 256 equal contiguous ranges,
 //     one block (one CU) each, so every CU streams the same share of W in
-//     one round.  W stages
-//     land in a ring of LDS slots by DMA (buffer_load ... lds), the stage's
-//     resource based at its tile so rows past the end read zero.  A block
+//     one round.  W stages land in a ring of LDS slots by DMA (buffer_load
+//     ... lds), the stage's resource based at its tile so rows past the end
+//     read zero.  A block
 //     leaves one fp32 partial per tile it touches (at most two); the LAST
 //     block of a tile to arrive (an atomic counter; partials written and
 //     read with device-scope loads and stores) sums the tile's partials in
