@@ -179,16 +179,16 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ float bf2f(uint32_t h) { return __builtin_bit_cast(float, h << 16); }
 
 // cos / sin of the row's position at frequencies f .. f + 3 (zeros for a
-// position outside the cache)
-__device__ __forceinline__ void few_cs4(const FewArgs& p, int t, int f, float4& c, float4& s) {
+// position outside the cache: row 0 is read and the values dropped, so that
+// no branch holds the loads back)
+__device__ __forceinline__ void few_cs4(const FewArgs& p, int t, int f, f32x4& c, f32x4& s) {
   const int32_t q = p.pos[t];
-  if (rope_pos_ok(q, p.max_pos)) {
-    c = *reinterpret_cast<const float4*>(p.cosc + (int64_t)q * 64 + f);
-    s = *reinterpret_cast<const float4*>(p.sinc + (int64_t)q * 64 + f);
-  } else {
-    c = make_float4(0.f, 0.f, 0.f, 0.f);
-    s = c;
-  }
+  const bool ok = rope_pos_ok(q, p.max_pos);
+  const int64_t o = (int64_t)(ok ? q : 0) * 64 + f;
+  const f32x4 cv = *reinterpret_cast<const f32x4*>(p.cosc + o), sv = *reinterpret_cast<const f32x4*>(p.sinc + o);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  c = ok ? cv : z;
+  s = ok ? sv : z;
 }
 
 // ---------------------------------------------------------------------------
@@ -429,10 +429,10 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 // copy measured about 2x more bank-conflict cycles than LDS cycles).
 constexpr int NF4_TAB_BYTES = 256 * 16 * 8;
 
-__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float* table, int nth = few::NT) {
+__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float (&table)[16], int nth = few::NT) {
   for (int t = threadIdx.x; t < 256 * 16; t += nth) {
     const int b = t >> 4;
-    tab[t] = f32x2{table[b >> 4], table[b & 15]};
+    tab[t] = f32x2{tab16(table, b >> 4), tab16(table, b & 15)};
   }
 }
 
@@ -669,9 +669,16 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, co
     }
     return;
   }
-  // RoPE: item = (row t, frequencies f .. f + 3); both halves summed
+  // RoPE: item = (row t, frequencies f .. f + 3); both halves summed.  The
+  // positions and their cos / sin are loaded ahead of the partials.
   const int items = p.M * 16;
   for (int i0 = threadIdx.x; i0 < items; i0 += 2 * NTH) {
+    f32x4 cv[2], sv[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int it = min(i0 + i * NTH, items - 1);
+      few_cs4(p, it >> 4, 4 * (it & 15), cv[i], sv[i]);
+    }
     int64_t off[4];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -685,9 +692,7 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, co
     for (int i = 0; i < 2; ++i) {
       const int it = i0 + i * NTH, t = it >> 4, f = 4 * (it & 15);
       if (it >= items) continue;
-      float4 c, sn;
-      few_cs4(p, t, f, c, sn);
-      const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {sn.x, sn.y, sn.z, sn.w};
+      const f32x4 cc = cv[i], ss = sv[i];
       const float z1[4] = {a[2 * i].x, a[2 * i].y, a[2 * i].z, a[2 * i].w};
       const float z2[4] = {a[2 * i + 1].x, a[2 * i + 1].y, a[2 * i + 1].z, a[2 * i + 1].w};
       float y1[4], y2[4];
@@ -1167,36 +1172,43 @@ few_bwd_kernel(const FewArgs p) {
   const FewSpan sp = few_span(p, blockIdx.x);
   const int nk = sp.nk;
   const bool two = sp.te < nk - 1;  // the range reaches tile a0 + 1
-  if constexpr (NF4) few_fill_tab(tab2, p.nf4_table);
+  // Every load of the prologue takes no branch (offsets past a resource read
+  // zero) and those used after the stream's first DMAs are issued before
+  // them: a load issued after the DMAs completes only after all of them, and
+  // a load in a branch makes the compiler wait for every load in flight,
+  // DMAs included, before its first use.
+  // NF4: the byte -> pair table entries this thread writes (entry tid + NT i:
+  // {table[i], table[(tid / 16) % 16]}; the table is in the kernel's
+  // arguments), written to LDS once the DMAs are out
+  static_assert(!NF4 || NT == 256, "the table entries of a thread");
+  const float tlo = NF4 ? tab16(p.nf4_table, (tid >> 4) & 15) : 0.f;
   // The P_s and Q_s tiles start as zeros (rows past Mp, columns past r8)
   for (int e = tid; e < 2 * R::MP * 8; e += NT) *reinterpret_cast<u32x4*>(smem + 16 * e) = u32x4{0u, 0u, 0u, 0u};
-  // Their values are loaded ahead of the stream's DMAs (a load issued after
-  // them would complete only after every one of them): with fold, the panel
-  // partials of up to two 4-column items per thread (P items, then Q items;
-  // at most 8 slabs each), else the bf16 panels, 8 columns per item, up to 8
-  // items per thread.
-  const int nP4 = p.Mp * p.r8 / 4;
+  // Their values: with fold, the panel partials of one 4-column item of P and
+  // one of Q per thread (Mp r8 / 4 <= NT items each; at most 8 slabs each),
+  // else the bf16 panels, 8 columns per item, up to 4 items of each.
+  const int nP4 = p.Mp * p.r8 / 4, n8 = p.Mp * p.r8 / 8;
   f32x4 pv[2][8];
-  u32x4 bv[8];
+  u32x4 bv[2][4];
   if (p.fold) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int it = tid + NT * k;
-      const bool q = it >= nP4;
-      const int off = 4 * (q ? it - nP4 : it), S = q ? p.Sq : p.Sp;
-      const float* src = q ? p.Qp : p.Pp;
+      const int S = k ? p.Sq : p.Sp;
+      const __amdgpu_buffer_rsrc_t rp = few_rsrc(k ? p.Qp : p.Pp, (int64_t)S * p.Mp * p.r8 * 4);
 #pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        pv[k][z] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (it < 2 * nP4 && z < S) pv[k][z] = *reinterpret_cast<const f32x4*>(src + (int64_t)z * p.Mp * p.r8 + off);
-      }
+      for (int z = 0; z < 8; ++z)
+        pv[k][z] = __builtin_bit_cast(
+            f32x4, few_ld16(rp, tid < nP4 && z < S ? (uint32_t)(((int64_t)z * p.Mp * p.r8 + 4 * tid) * 4) : OOB));
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int it = tid + NT * k, n8 = p.Mp * p.r8 / 8;
-      bv[k] = u32x4{0u, 0u, 0u, 0u};
-      if (it < 2 * n8) bv[k] = *reinterpret_cast<const u32x4*>((it < n8 ? p.Ps : p.Qs) + 8 * (it % n8));
+    for (int k = 0; k < 2; ++k) {
+      const __amdgpu_buffer_rsrc_t rs = few_rsrc(k ? p.Qs : p.Ps, (int64_t)n8 * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int it = tid + NT * e;
+        bv[k][e] = few_ld16(rs, it < n8 ? (uint32_t)(16 * it) : OOB);
+      }
     }
   }
   __syncthreads();  // the zeros are written
@@ -1370,6 +1382,7 @@ few_bwd_kernel(const FewArgs p) {
   // tile's 128 columns) are loaded here, ahead of the DMAs, and used once Q_s
   // is in LDS.
   const bool rk0 = sp.s0 == 0;
+  const __amdgpu_buffer_rsrc_t rar = few_rsrc(p.A, (int64_t)p.r8 * p.d_in * 2);
   u32x4 av[2][4];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -1377,41 +1390,43 @@ few_bwd_kernel(const FewArgs p) {
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + NT * e, q = idx >> 4, cc = idx & 15;
       const int col = (sp.a0 + u) * 128 + 8 * cc;
-      av[u][e] = u32x4{0u, 0u, 0u, 0u};
-      if ((u ? two : rk0) && q < p.r8 && col < p.d_in)
-        av[u][e] = *reinterpret_cast<const u32x4*>(p.A + (int64_t)q * p.d_in + col);
+      const bool ok = (u ? two : rk0) && q < p.r8 && col < p.d_in;
+      av[u][e] = few_ld16(rar, ok ? (uint32_t)((q * p.d_in + col) * 2) : OOB);
     }
 
-  // prologue: stages 0 .. NS - 2 in flight
-  few_unroll<NS - 1>([&](auto sc) {
-    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
-  });
+  // prologue: stages 0 .. NS - 2 in flight, with no branch (a range of fewer
+  // stages loads its last stage again into the slots it does not use; the
+  // waits below count them, and the last wait, for none in flight, sees them
+  // land before the ring is reused)
+  few_unroll<NS - 1>([&](auto sc) { issue(min((int)decltype(sc)::value, nk - 1), decltype(sc)::value); });
+  if constexpr (NF4) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tab2[tid + NT * i] = f32x2{p.nf4_table[i], tlo};
+  }
   // P_s and Q_s into their NT tiles while the first stages fly: with fold
   // summed here (slabs in order) from launch 1's partials, else the bf16
   // panels of few_reduce_kernel
   if (p.fold) {
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int it = tid + NT * k;
-      if (it >= 2 * nP4) continue;
-      const bool q = it >= nP4;
-      const int off = 4 * (q ? it - nP4 : it), S = q ? p.Sq : p.Sp;
+      const int S = k ? p.Sq : p.Sp;
       f32x4 a = pv[k][0];
 #pragma unroll
       for (int z = 1; z < 8; ++z)
         if (z < S) a += pv[k][z];
-      const int t = off / p.r8, c = off % p.r8;
-      *reinterpret_cast<u32x2*>((q ? qst : pst) + nt_off(t, c >> 3) + 2 * (c & 7)) =
-          u32x2{pack_bf16x2(p.s * a[0], p.s * a[1]), pack_bf16x2(p.s * a[2], p.s * a[3])};
+      const int off = 4 * tid, t = off / p.r8, c = off % p.r8;
+      if (tid < nP4)
+        *reinterpret_cast<u32x2*>((k ? qst : pst) + nt_off(t, c >> 3) + 2 * (c & 7)) =
+            u32x2{pack_bf16x2(p.s * a[0], p.s * a[1]), pack_bf16x2(p.s * a[2], p.s * a[3])};
     }
   } else {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int it = tid + NT * k, n8 = p.Mp * p.r8 / 8;
-      if (it >= 2 * n8) continue;
-      const int e = 8 * (it % n8);
-      *reinterpret_cast<u32x4*>((it < n8 ? pst : qst) + nt_off(e / p.r8, (e % p.r8) >> 3)) = bv[k];
-    }
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int it = tid + NT * e, x = 8 * it;
+        if (it < n8) *reinterpret_cast<u32x4*>((k ? qst : pst) + nt_off(x / p.r8, (x % p.r8) >> 3)) = bv[k][e];
+      }
   }
   lds_barrier();  // the P_s and Q_s tiles are written
   load_pfr();

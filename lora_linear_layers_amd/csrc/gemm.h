@@ -215,8 +215,19 @@ __device__ __forceinline__ uint32_t nf4_byte_to_bf16x2(const float2* tab2, uint3
   return pack_bf16x2(t.x * am, t.y * am);
 }
 
-__device__ __forceinline__ void nf4_fill_tab2(float2* tab2, const float* table, int tid, int nt) {
-  for (int t = tid; t < 256; t += nt) tab2[t] = make_float2(table[t >> 4], table[t & 15]);
+// t[i] of a 16-entry table held in the kernel's arguments, for a lane's own
+// i, by selects over the 16 values: indexing the argument's array with a
+// lane value (or taking its address) would copy the whole argument block to
+// scratch memory and read every argument from there.
+__device__ __forceinline__ float tab16(const float (&t)[16], int i) {
+  float v = t[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) v = i == k ? t[k] : v;
+  return v;
+}
+
+__device__ __forceinline__ void nf4_fill_tab2(float2* tab2, const float (&table)[16], int tid, int nt) {
+  for (int t = tid; t < 256; t += nt) tab2[t] = make_float2(tab16(table, t >> 4), tab16(table, t & 15));
 }
 
 template <typename T, int BM, int BN, int WM, int WN, bool B_NN, int EPI, int BL>
