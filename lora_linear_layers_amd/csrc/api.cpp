@@ -57,7 +57,7 @@ int check_device() {
 // ---------------------------------------------------------------------------
 struct FewPlan {
   bool ok = false;
-  int MB = 0, Mp = 0, Sp = 0, Kp = 0, Sq = 0, Kq = 0, n_tiles = 0, nkt = 0, T = 0, nblk = 0;
+  int MB = 0, Mp = 0, Sp = 0, Kp = 0, pg = 1, Sq = 0, Kq = 0, n_tiles = 0, nkt = 0, T = 0, nblk = 0;
   bool fold = false;  // backward in two launches: the W stream sums the panels
   size_t pp = 0, qp = 0, cp = 0, cnt = 0, g = 0, ps = 0, qs = 0, total = 0;
 };
@@ -104,8 +104,14 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
   // (Mp + r8): taken while those stay within 64K elements (128 KB)
   auto chunk8 = [](int64_t K) { return std::max<int64_t>(128, rup(cdiv(K, 8), 128)); };
   F.fold = bwd && F.Mp * r <= 1024 && std::max(chunk8(d_in), chunk8(d_out)) * (F.Mp + r) <= 65536;
-  F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, F.fold ? 8 : 16), 128));
+  // the forward's stream blocks each load every P slab for their items (16
+  // tokens x 4 columns each, ahead of their DMAs): at most 16 loads a thread,
+  // so fewer slabs as the tokens grow, and launch 1 then takes each slab in
+  // 16-row groups of tokens, a block each
+  const int64_t fwd_slabs = 16 / cdiv(F.Mp * 16, nf4 ? few::NT4 : few::NT);
+  F.Kp = (int)std::max<int64_t>(128, rup(cdiv(d_in, bwd ? (F.fold ? 8 : 16) : fwd_slabs), 128));
   F.Sp = (int)cdiv(d_in, F.Kp);
+  F.pg = bwd ? 1 : F.MB;
   if (bwd) {
     F.Kq = (int)(F.fold ? std::max<int64_t>(128, rup(cdiv(d_out, 8), 128))
                         : std::min<int64_t>(512, std::max<int64_t>(128, rup(cdiv(d_out, 32), 128))));
@@ -503,7 +509,7 @@ FewArgs few_args(const FewPlan& F, int64_t M, int64_t d_in, int64_t d_out, int64
   a.Qp = reinterpret_cast<float*>(w + F.qp);
   a.Cp = reinterpret_cast<float*>(w + F.cp);
   a.cnt = reinterpret_cast<int*>(w + F.cnt);
-  a.Sp = F.Sp; a.Kp = F.Kp; a.Sq = F.Sq; a.Kq = F.Kq;
+  a.Sp = F.Sp; a.Kp = F.Kp; a.pg = F.pg; a.Sq = F.Sq; a.Kq = F.Kq;
   a.n_tiles = F.n_tiles; a.nkt = F.nkt; a.T = F.T; a.nblk = F.nblk; a.fold = F.fold ? 1 : 0;
   return a;
 }

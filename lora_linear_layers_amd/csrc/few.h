@@ -64,6 +64,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t few_rsrc(const void* p, int64_
 __device__ __forceinline__ u32x4 few_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// An ordering point for the compiler only (no instruction, no wait): memory
+// operations written before it are issued before those written after it.  A W
+// stream puts one between the loads it issues ahead of its DMAs and the DMAs:
+// the compiler would otherwise sink such a load into the branch that uses it,
+// past the DMAs, and a load issued after them completes only after all of them.
+__device__ __forceinline__ void few_issue_order() { asm volatile("" ::: "memory"); }
 
 // One DMA instruction (SIZE bytes per lane) into LDS at lds_base + SIZE lane.
 // voff: the lane's byte offset (a loop-invariant register: a register that a
@@ -192,10 +198,11 @@ __device__ __forceinline__ void few_cs4(const FewArgs& p, int t, int f, f32x4& c
 }
 
 // ---------------------------------------------------------------------------
-// launch 1: panel partials.  Blocks [0, Sp): P chunk b of d_in; blocks
-// [Sp, Sp + Sq): Q chunk of d_out.  A block's 4 waves take the chunk's 32-wide
-// steps in turn (Q: a wave takes a whole head, so that with RoPE its pairs
-// (i, i+64) meet in one lane), then the waves' sums meet in LDS.
+// launch 1: panel partials.  Blocks [0, Sp pg): P, chunk b % Sp of d_in and
+// (pg > 1, the forward, MB = 1) rows 16 (b / Sp) .. + 15; blocks
+// [Sp pg, Sp pg + Sq): Q chunk of d_out.  A block's 4 waves take the chunk's
+// 32-wide steps in turn (Q: a wave takes a whole head, so that with RoPE its
+// pairs (i, i+64) meet in one lane), then the waves' sums meet in LDS.
 // ---------------------------------------------------------------------------
 template <int MB>
 __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
@@ -226,10 +233,13 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[mb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool isq = (int)blockIdx.x >= p.Sp;
+  const int np = p.Sp * p.pg;  // P blocks
+  const bool isq = (int)blockIdx.x >= np;
+  const int chunk = isq ? (int)blockIdx.x - np : (int)blockIdx.x % p.Sp;
+  const int row0 = isq ? 0 : MP * ((int)blockIdx.x / p.Sp);  // the block's first token row
   if (!isq) {
     // P chunk: [X rows] x [A rows]^T over k in [k0, k1)
-    const int k0 = blockIdx.x * p.Kp;
+    const int k0 = chunk * p.Kp;
     const int k1 = min(p.d_in, k0 + p.Kp);
     const __amdgpu_buffer_rsrc_t rx = few_rsrc(p.X, (int64_t)p.M * p.d_in * 2);
     const __amdgpu_buffer_rsrc_t ra = few_rsrc(p.A, (int64_t)p.r8 * p.d_in * 2);
@@ -245,7 +255,7 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
         const int kk = k + 8 * g;  // the lane's first element (k1 - k0 is a multiple of 32)
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const int row = 16 * mb + l16;
+          const int row = row0 + 16 * mb + l16;
           xf[u][mb] = __builtin_bit_cast(
               bf16x8, few_ld16(rx, row < p.M && k < k1 ? (uint32_t)((row * p.d_in + kk) * 2) : OOB));
         }
@@ -270,8 +280,7 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
     // Q chunk: [G rows] x B over i in [i0, i1), a head (128 rows of B) per
     // wave at a time; B's rows go to the wave's NN tile (rows of 64 rank
     // columns, zero past r8), read back with the transposing LDS read
-    const int c = blockIdx.x - p.Sp;
-    const int i0 = c * p.Kq;
+    const int i0 = chunk * p.Kq;
     const int i1 = min(p.d_out, i0 + p.Kq);
     const __amdgpu_buffer_rsrc_t ry = few_rsrc(p.dY, (int64_t)p.M * p.d_out * 2);
     const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
@@ -410,10 +419,10 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
       for (int v = 0; v < 4; ++v) red[wave][16 * mb + 4 * g + v][16 * rb + l16] = acc[mb][rb][v];
   __syncthreads();
   // a thread stores 4 rank columns of a token row: 16 threads a row
-  float* out = isq ? p.Qp + (int64_t)(blockIdx.x - p.Sp) * p.Mp * p.r8 : p.Pp + (int64_t)blockIdx.x * p.Mp * p.r8;
+  float* out = (isq ? p.Qp : p.Pp) + (int64_t)chunk * p.Mp * p.r8 + (int64_t)row0 * p.r8;
   const int q = 4 * (tid & 15);
   if (q < p.r8)
-    for (int t = tid >> 4; t < p.Mp; t += NT / 16) {
+    for (int t = tid >> 4; t < MP; t += NT / 16) {
       const f32x4 s0 = *reinterpret_cast<const f32x4*>(&red[0][t][q]), s1 = *reinterpret_cast<const f32x4*>(&red[1][t][q]);
       const f32x4 s2 = *reinterpret_cast<const f32x4*>(&red[2][t][q]), s3 = *reinterpret_cast<const f32x4*>(&red[3][t][q]);
       *reinterpret_cast<f32x4*>(out + t * p.r8 + q) = ((s0 + s1) + s2) + s3;
@@ -429,10 +438,19 @@ __global__ void __launch_bounds__(few::NT) few_panel_kernel(const FewArgs p) {
 // copy measured about 2x more bank-conflict cycles than LDS cycles).
 constexpr int NF4_TAB_BYTES = 256 * 16 * 8;
 
-__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float (&table)[16], int nth = few::NT) {
-  for (int t = threadIdx.x; t < 256 * 16; t += nth) {
-    const int b = t >> 4;
-    tab[t] = f32x2{tab16(table, b >> 4), tab16(table, b & 15)};
+// A thread writes entries tid + NTH i: byte b = tid / 16 + (NTH / 16) i, so
+// its low nibble's value is the same in all of them and the high nibble is
+// i (NTH = 256) or 2 i + tid / 256 (NTH = 512).
+template <int NTH>
+__device__ __forceinline__ void few_fill_tab(f32x2* tab, const float (&table)[16]) {
+  static_assert(NTH == 256 || NTH == 512, "the table entries of a thread");
+  auto u = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x))); };
+  const int tid = threadIdx.x;
+  const float lo = tab16(table, (tid >> 4) & 15);
+#pragma unroll
+  for (int i = 0; i < 4096 / NTH; ++i) {
+    const float hi = NTH == 256 ? u(table[i]) : ((tid >> 8) ? u(table[2 * i + 1]) : u(table[2 * i]));
+    tab[tid + NTH * i] = f32x2{hi, lo};
   }
 }
 
@@ -574,30 +592,44 @@ __device__ __forceinline__ void few_sum4(const float* src, int S, int64_t zstrid
   }
 }
 
-// bf16(s * sum over z < S of part[z][t][q]) into an NT tile of MP rows and 64
-// columns (zeros past M and r8): four columns per item, up to four items of
-// a thread summed together
-template <int MP, int NTH = few::NT>
-__device__ __forceinline__ void few_panel_sum(const float* part, int S, const FewArgs& p, char* tile) {
-  constexpr int ITEMS = MP * 16;
-  for (int i0 = threadIdx.x; i0 < ITEMS; i0 += 4 * NTH) {
-    int64_t off[4];
+// The forward's rank panel P_s = bf16(s P), P the sum of launch 1's Sp slabs
+// in slab order, into an NT tile of Mp rows and 64 columns (zeros past M and
+// r8).  Item it: token it / 16, columns 4 (it % 16) .. + 3, IPT items a
+// thread.  load() issues every slab load of the thread's items, to go ahead
+// of the stream's DMAs (a load issued after them completes only after all of
+// them); store() sums once they have landed.  The plan keeps Sp <= SMAX.
+template <int MB, int NTH>
+struct FewPanelPre {
+  static constexpr int ITEMS = MB * 16 * 16;
+  static constexpr int IPT = (ITEMS + NTH - 1) / NTH;
+  static constexpr int SMAX = 16 / IPT;
+  f32x4 v[IPT][SMAX];
+  __device__ __forceinline__ void load(const FewArgs& p) {
+    const __amdgpu_buffer_rsrc_t r = few_rsrc(p.Pp, (int64_t)p.Sp * p.Mp * p.r8 * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = i0 + i * NTH, t = it >> 4, q = 4 * (it & 15);
-      off[i] = (it < ITEMS && t < p.M && q < p.r8) ? (int64_t)t * p.r8 + q : -1;
-    }
-    float4 a[4];
-    few_sum4<4>(part, S, (int64_t)p.Mp * p.r8, off, a);
+    for (int i = 0; i < IPT; ++i) {
+      const int it = threadIdx.x + NTH * i, t = it >> 4, q = 4 * (it & 15);
+      const bool ok = it < ITEMS && t < p.M && q < p.r8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int it = i0 + i * NTH, t = it >> 4, q = 4 * (it & 15);
-      if (it >= ITEMS) continue;
-      const uint2 v = make_uint2(pack_bf16x2(p.s * a[i].x, p.s * a[i].y), pack_bf16x2(p.s * a[i].z, p.s * a[i].w));
-      *reinterpret_cast<uint2*>(tile + nt_off(t, q >> 3) + 2 * (q & 7)) = v;
+      for (int z = 0; z < SMAX; ++z)
+        v[i][z] = __builtin_bit_cast(
+            f32x4, few_ld16(r, ok && z < p.Sp ? (uint32_t)(((z * p.Mp + t) * p.r8 + q) * 4) : few::OOB));
     }
   }
-}
+  __device__ __forceinline__ void store(const FewArgs& p, char* tile) const {
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int it = threadIdx.x + NTH * i, t = it >> 4, q = 4 * (it & 15);
+      if (it >= ITEMS) continue;
+      f32x4 a = v[i][0];
+#pragma unroll
+      for (int z = 1; z < SMAX; ++z)
+        if (z < p.Sp) a += v[i][z];
+      *reinterpret_cast<u32x2*>(tile + nt_off(t, q >> 3) + 2 * (q & 7)) =
+          u32x2{pack_bf16x2(p.s * a[0], p.s * a[1]), pack_bf16x2(p.s * a[2], p.s * a[3])};
+    }
+  }
+};
 
 // few_sum4 over partials written by other blocks of the same launch:
 // device-scope loads, 8 slabs of every item in flight.
@@ -743,11 +775,6 @@ __global__ void __launch_bounds__(few::NT) few_reduce_kernel(const FewArgs p) {
 // same share of W; one partial per (block, tile) and the last block to arrive
 // at a tile sums them (few_finish).
 // ---------------------------------------------------------------------------
-namespace few {
-constexpr int NW4 = 8;           // waves of the NF4 forward block
-constexpr int NT4 = 64 * NW4;    // its threads
-}  // namespace few
-
 template <int MB>
 struct FewNf4Ring {
   static constexpr int MP = MB <= 2 ? 32 : (MB <= 4 ? 64 : 128);  // activation rows in LDS
@@ -784,7 +811,6 @@ few_fwd_nf4_kernel(const FewArgs p) {
   const FewSpan sp = few_span(p, blockIdx.x);
   const int nk = sp.nk;
   const bool two = sp.te < nk - 1;
-  few_fill_tab(tab2, p.nf4_table, NT4);  // read after the first stage barrier
   // the lane's copy of the pair table: byte b's entry at 128 b + 8 (lane % 16)
   const uint32_t rep = 8 * l16;
 
@@ -874,11 +900,15 @@ few_fwd_nf4_kernel(const FewArgs p) {
   // The rank term P_s B^T of a tile goes into the partial of the block that
   // streams the tile's first stage (tile a0 when s0 = 0, tile a0 + 1 when the
   // range reaches it).  Its B fragments (rows = the wave's 16 columns, r8
-  // contiguous) are loaded ahead of the DMAs; P_s is summed from the panel
-  // partials into LDS no stage uses yet (the last ring slot) while the first
-  // stages fly.
+  // contiguous) and the panel partials are loaded ahead of the DMAs, with no
+  // branch (offsets past a resource read zero: a load in a branch makes the
+  // compiler wait for every load in flight, DMAs included, before its first
+  // use); P_s goes to LDS no stage uses yet (the last ring slot) while the
+  // first stages fly.
   const bool rk0 = sp.s0 == 0;
   const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
+  FewPanelPre<MB, NT4> pre;
+  pre.load(p);
   bf16x8 bq[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -889,13 +919,15 @@ few_fwd_nf4_kernel(const FewArgs p) {
       bq[u][sstep] = __builtin_bit_cast(bf16x8, few_ld16(rbr, ok ? (uint32_t)((col * p.r8 + q) * 2) : OOB));
     }
 
-  few_unroll<NS - 1>([&](auto sc) {
-    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
-  });
+  // stages 0 .. NS - 2 in flight, with no branch (a range of fewer stages
+  // loads its last stage again into slots it does not use; the loop's waits
+  // count them, and its last wait, for none in flight, sees them land)
+  few_issue_order();
+  few_unroll<NS - 1>([&](auto sc) { issue(min((int)decltype(sc)::value, nk - 1), decltype(sc)::value); });
   if (rk0 || two) {
     char* ps = cslot(NS - 1);
-    few_panel_sum<R::MP, NT4>(p.Pp, p.Sp, p, ps);
-    __syncthreads();
+    pre.store(p, ps);
+    lds_barrier();  // (LDS only: a __syncthreads would also wait for every DMA in flight)
 #pragma unroll
     for (int sstep = 0; sstep < 2; ++sstep)
 #pragma unroll
@@ -906,6 +938,9 @@ few_fwd_nf4_kernel(const FewArgs p) {
       }
     // (the slot's first DMA, at stage 0, follows the loop's first barrier)
   }
+  // the pair table, read after the loop's first barrier (filled once the
+  // loads and DMAs are out)
+  few_fill_tab<NT4>(tab2, p.nf4_table);
   constexpr int U = (NS % 2) ? 2 * NS : NS;
   for (int t0 = 0; t0 < nk; t0 += U) {
     few_unroll<U>([&](auto jc) {
@@ -1049,11 +1084,13 @@ few_fwd_bf16_kernel(const FewArgs p) {
   // The rank term P_s B^T of a tile goes into the partial of the block that
   // streams the tile's first stage (tile a0 when s0 = 0, tile a0 + 1 when the
   // range reaches it).  Its B fragments (rows = the wave's columns, r8
-  // contiguous) are loaded ahead of the DMAs; P_s is summed from the panel
-  // partials into LDS no stage uses yet (the last ring slot) while the first
-  // stages fly.
+  // contiguous) and the panel partials are loaded ahead of the DMAs, with no
+  // branch; P_s goes to LDS no stage uses yet (the last ring slot) while the
+  // first stages fly.
   const bool rk0 = sp.s0 == 0;
   const __amdgpu_buffer_rsrc_t rbr = few_rsrc(p.B, (int64_t)p.d_out * p.r8 * 2);
+  FewPanelPre<MB, NT> pre;
+  pre.load(p);
   bf16x8 bq[2][2][NJ];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -1066,13 +1103,13 @@ few_fwd_bf16_kernel(const FewArgs p) {
         bq[u][sstep][j] = __builtin_bit_cast(bf16x8, few_ld16(rbr, ok ? (uint32_t)((col * p.r8 + q) * 2) : OOB));
       }
 
-  few_unroll<NS - 1>([&](auto sc) {
-    if (decltype(sc)::value < nk) issue(decltype(sc)::value, decltype(sc)::value);
-  });
+  // stages 0 .. NS - 2 in flight, with no branch (as in the NF4 form)
+  few_issue_order();
+  few_unroll<NS - 1>([&](auto sc) { issue(min((int)decltype(sc)::value, nk - 1), decltype(sc)::value); });
   if (rk0 || two) {
     char* ps = wslot(NS - 1);
-    few_panel_sum<R::MP>(p.Pp, p.Sp, p, ps);
-    __syncthreads();
+    pre.store(p, ps);
+    lds_barrier();  // (LDS only: a __syncthreads would also wait for every DMA in flight)
 #pragma unroll
     for (int sstep = 0; sstep < 2; ++sstep)
 #pragma unroll
@@ -1172,16 +1209,16 @@ few_bwd_kernel(const FewArgs p) {
   const FewSpan sp = few_span(p, blockIdx.x);
   const int nk = sp.nk;
   const bool two = sp.te < nk - 1;  // the range reaches tile a0 + 1
-  // Every load of the prologue takes no branch (offsets past a resource read
-  // zero) and those used after the stream's first DMAs are issued before
-  // them: a load issued after the DMAs completes only after all of them, and
-  // a load in a branch makes the compiler wait for every load in flight,
-  // DMAs included, before its first use.
   // NF4: the byte -> pair table entries this thread writes (entry tid + NT i:
   // {table[i], table[(tid / 16) % 16]}; the table is in the kernel's
   // arguments), written to LDS once the DMAs are out
   static_assert(!NF4 || NT == 256, "the table entries of a thread");
   const float tlo = NF4 ? tab16(p.nf4_table, (tid >> 4) & 15) : 0.f;
+  // Every load of the prologue takes no branch (offsets past a resource read
+  // zero) and those used after the stream's first DMAs are issued before
+  // them: a load issued after the DMAs completes only after all of them, and
+  // a load in a branch makes the compiler wait for every load in flight,
+  // DMAs included, before its first use.
   // The P_s and Q_s tiles start as zeros (rows past Mp, columns past r8)
   for (int e = tid; e < 2 * R::MP * 8; e += NT) *reinterpret_cast<u32x4*>(smem + 16 * e) = u32x4{0u, 0u, 0u, 0u};
   // Their values: with fold, the panel partials of one 4-column item of P and
@@ -1398,6 +1435,7 @@ few_bwd_kernel(const FewArgs p) {
   // stages loads its last stage again into the slots it does not use; the
   // waits below count them, and the last wait, for none in flight, sees them
   // land before the ring is reused)
+  few_issue_order();
   few_unroll<NS - 1>([&](auto sc) { issue(min((int)decltype(sc)::value, nk - 1), decltype(sc)::value); });
   if constexpr (NF4) {
 #pragma unroll
@@ -1437,13 +1475,14 @@ few_bwd_kernel(const FewArgs p) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     if (!(u ? two : rk0)) continue;
-    if (u && rk0) __syncthreads();  // every wave is done with tile a0's A
+    // (LDS-only barriers: a __syncthreads would also wait for every DMA in flight)
+    if (u && rk0) lds_barrier();  // every wave is done with tile a0's A
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + NT * e;
       *reinterpret_cast<u32x4*>(at + nn_off<256>(idx >> 4, idx & 15)) = av[u][e];
     }
-    __syncthreads();
+    lds_barrier();
     bf16x8 bfr[2 * NJ];
     u32x2 ad[2 * NJ];
 #pragma unroll

@@ -8,6 +8,8 @@ namespace lora {
 
 namespace few {
 constexpr int NT = 256;                // threads per block
+constexpr int NW4 = 8;                 // waves of the NF4 forward's W-streaming block
+constexpr int NT4 = 64 * NW4;          // its threads
 constexpr int BN = 128;                // output columns per block (one RoPE head)
 constexpr int BK = 64;                 // contraction per stage
 constexpr int MAXMB = 8;               // 16-row blocks of tokens (M <= 128)
@@ -46,6 +48,7 @@ struct FewArgs {
   uint16_t* Ps;  // backward: bf16(s P) [Mp, r8] (few_reduce_kernel)
   uint16_t* Qs;  // backward: bf16(s Q) [Mp, r8]
   int Sp, Kp;  // P: chunks of d_in of Kp (a multiple of 32)
+  int pg;      // P: 16-row groups of tokens per chunk, a block each (1: one block takes every row)
   int Sq, Kq;  // Q: chunks of d_out of Kq (a multiple of 128)
   // launch 2: n_tiles column tiles of BN, nkt stages of BK each; block b of
   // nblk takes the stages [b T / nblk, (b + 1) T / nblk) of the T = n_tiles nkt

@@ -218,11 +218,15 @@ __device__ __forceinline__ uint32_t nf4_byte_to_bf16x2(const float2* tab2, uint3
 // t[i] of a 16-entry table held in the kernel's arguments, for a lane's own
 // i, by selects over the 16 values: indexing the argument's array with a
 // lane value (or taking its address) would copy the whole argument block to
-// scratch memory and read every argument from there.
+// scratch memory and read every argument from there.  Each value passes
+// through readfirstlane (free on a uniform value), which keeps the compiler
+// from turning the selects of loaded values into a select of addresses and
+// one per-lane load from the argument segment, a memory round trip each call.
 __device__ __forceinline__ float tab16(const float (&t)[16], int i) {
-  float v = t[0];
+  auto u = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x))); };
+  float v = u(t[0]);
 #pragma unroll
-  for (int k = 1; k < 16; ++k) v = i == k ? t[k] : v;
+  for (int k = 1; k < 16; ++k) v = i == k ? u(t[k]) : v;
   return v;
 }
 

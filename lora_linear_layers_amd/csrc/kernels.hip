@@ -1058,8 +1058,14 @@ hipError_t run_skinny_mode(const SkinnyArgs& a, int mode, hipStream_t st) {
 template <int MB>
 hipError_t few_launch(const FewArgs& a, int what, bool nf4, hipStream_t st) {
   if (what == 0) {
-    hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
+    // (row groups: one 16-row block of tokens per launch-1 block)
+    if (a.pg > 1)
+      hipLaunchKernelGGL(few_panel_kernel<1>, dim3(a.Sp * a.pg + a.Sq), dim3(few::NT), 0, st, a);
+    else
+      hipLaunchKernelGGL(few_panel_kernel<MB>, dim3(a.Sp + a.Sq), dim3(few::NT), 0, st, a);
   } else if (what == 1) {
+    // the stream sums at most SMAX panel slabs
+    if (a.Sp > (nf4 ? FewPanelPre<MB, few::NT4>::SMAX : FewPanelPre<MB, few::NT>::SMAX)) return hipErrorInvalidValue;
     if (nf4)
       hipLaunchKernelGGL((few_fwd_nf4_kernel<MB>), dim3((unsigned)a.nblk), dim3(few::NT4), 0, st, a);
     else
@@ -1079,6 +1085,8 @@ hipError_t few_dispatch(const FewArgs& a, int MB, int what, bool nf4, hipStream_
   if (a.Sp < 1 || a.n_tiles < 1 || a.n_tiles > a.nblk || a.nkt < 1 || a.T != a.n_tiles * a.nkt || a.nblk < 1 ||
       a.nblk > few::GRID || a.nblk > a.T)
     return hipErrorInvalidValue;
+  // launch 1's row groups: all rows per block, or one 16-row block each (P only)
+  if (!(a.pg == 1 || (a.pg == MB && a.Sq == 0))) return hipErrorInvalidValue;
   // the W stream's tiles and stages cover its output columns and contraction
   // exactly (stages 128 deep in the NF4 forward, 64 otherwise)
   if (what > 0) {
