@@ -665,63 +665,63 @@ __device__ __forceinline__ void few_sum4_dev(const float* src, int S, int64_t zs
   }
 }
 
-// The finishing block's output pass: y = (sum over chunks of the partials) +
-// rank term (an fp32 tile [MP][BNT] in LDS, in the same columns; none when tl
-// is null, the term being in a partial already), then bf16
-// stores of four columns per item, or, with RoPE (BNT = 128, one head), the
-// rotation of the pairs (f, f + 64) of each row.
+// The finishing block's output pass: y = the sum over the tile's partials (the
+// rank term is in the partial of the tile's first block), then bf16 stores of
+// four columns per item, or, with RoPE (BNT = 128, one head), the rotation of
+// the pairs (f, f + 64) of each row.
 // part: the tile's first partial slab ([Mp][BNT] each, S of them, summed in
 // slab order).
 template <int BNT, int NTH = few::NT>
-__device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, const float* part, int S, int n0,
-                                           int N, uint16_t* out, bool rope) {
+__device__ __forceinline__ void few_finish(const FewArgs& p, const float* part, int S, int n0, int N, uint16_t* out,
+                                           bool rope) {
+  // NI items (16 bytes of 4 columns) of every slab in flight per thread (8
+  // measured slower: the kernel's register allocation grows to all 256 and
+  // its stream slows down)
+  constexpr int NI = 4;
   const int64_t zs = (int64_t)p.Mp * BNT;
   if (!rope) {
     const int items = p.M * (BNT / 4);
-    for (int i0 = threadIdx.x; i0 < items; i0 += 4 * NTH) {
-      int64_t off[4];
+    for (int i0 = threadIdx.x; i0 < items; i0 += NI * NTH) {
+      int64_t off[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const int it = i0 + i * NTH, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
         off[i] = (it < items && n0 + c < N) ? (int64_t)t * BNT + c : -1;
       }
-      float4 a[4];
-      few_sum4_dev<4>(part, S, zs, off, a);
+      float4 a[NI];
+      few_sum4_dev<NI>(part, S, zs, off, a);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NI; ++i) {
         if (off[i] < 0) continue;
         const int it = i0 + i * NTH, t = it / (BNT / 4), c = 4 * (it % (BNT / 4));
-        float r[4] = {0.f, 0.f, 0.f, 0.f};
-        if (tl)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = tl[t * BNT + c + e];
         *reinterpret_cast<uint2*>(out + (int64_t)t * N + n0 + c) =
-            make_uint2(pack_bf16x2(a[i].x + r[0], a[i].y + r[1]), pack_bf16x2(a[i].z + r[2], a[i].w + r[3]));
+            make_uint2(pack_bf16x2(a[i].x, a[i].y), pack_bf16x2(a[i].z, a[i].w));
       }
     }
     return;
   }
   // RoPE: item = (row t, frequencies f .. f + 3); both halves summed.  The
   // positions and their cos / sin are loaded ahead of the partials.
+  constexpr int IP = NI / 2;
   const int items = p.M * 16;
-  for (int i0 = threadIdx.x; i0 < items; i0 += 2 * NTH) {
-    f32x4 cv[2], sv[2];
+  for (int i0 = threadIdx.x; i0 < items; i0 += IP * NTH) {
+    f32x4 cv[IP], sv[IP];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < IP; ++i) {
       const int it = min(i0 + i * NTH, items - 1);
       few_cs4(p, it >> 4, 4 * (it & 15), cv[i], sv[i]);
     }
-    int64_t off[4];
+    int64_t off[NI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < IP; ++i) {
       const int it = i0 + i * NTH, t = it >> 4, f = 4 * (it & 15);
       off[2 * i] = it < items ? (int64_t)t * BNT + f : -1;
       off[2 * i + 1] = it < items ? (int64_t)t * BNT + f + 64 : -1;
     }
-    float4 a[4];
-    few_sum4_dev<4>(part, S, zs, off, a);
+    float4 a[NI];
+    few_sum4_dev<NI>(part, S, zs, off, a);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < IP; ++i) {
       const int it = i0 + i * NTH, t = it >> 4, f = 4 * (it & 15);
       if (it >= items) continue;
       const f32x4 cc = cv[i], ss = sv[i];
@@ -730,9 +730,8 @@ __device__ __forceinline__ void few_finish(const FewArgs& p, const float* tl, co
       float y1[4], y2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float u = z1[e] + (tl ? tl[t * BNT + f + e] : 0.f), w = z2[e] + (tl ? tl[t * BNT + 64 + f + e] : 0.f);
-        y1[e] = u * cc[e] - w * ss[e];
-        y2[e] = w * cc[e] + u * ss[e];
+        y1[e] = z1[e] * cc[e] - z2[e] * ss[e];
+        y2[e] = z2[e] * cc[e] + z1[e] * ss[e];
       }
       uint16_t* o = out + (int64_t)t * N + n0 + f;
       *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(y1[0], y1[1]), pack_bf16x2(y1[2], y1[3]));
@@ -982,7 +981,7 @@ few_fwd_nf4_kernel(const FewArgs p) {
     // (the rank term is in the partial of the tile's first block)
     const int a = sp.a0 + i;
     const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
-    few_finish<BNF, NT4>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
+    few_finish<BNF, NT4>(p, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
                          p.rope != 0);
   }
 }
@@ -1166,7 +1165,7 @@ few_fwd_bf16_kernel(const FewArgs p) {
     if (!(i ? fin1 : fin0)) continue;
     const int a = sp.a0 + i;
     const int lo = few_blk_of(p, a * p.nkt), hi = few_blk_of(p, (a + 1) * p.nkt - 1);
-    few_finish<BNF>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
+    few_finish<BNF>(p, p.Cp + (int64_t)(lo + a) * p.Mp * BNF, hi - lo + 1, a * BNF, p.d_out, p.Y,
                     p.rope != 0);
   }
 }
@@ -1605,7 +1604,7 @@ few_bwd_kernel(const FewArgs p) {
     // (the rank term is in the partial of the tile's first block)
     __syncthreads();
     const int lo = blo(a);
-    few_finish<128>(p, nullptr, p.Cp + (int64_t)(lo + a) * p.Mp * 128, bhi(a) - lo + 1, n0, N, p.dX, false);
+    few_finish<128>(p, p.Cp + (int64_t)(lo + a) * p.Mp * 128, bhi(a) - lo + 1, n0, N, p.dX, false);
   }
 }
 
