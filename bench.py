@@ -75,6 +75,7 @@ KIND_OF = {
     "gemm_w4_nt_kernel<6>": "gemm_bf16_256x256_swiglu",
     "gemm_w4_nt_kernel<8>": "gemm_bf16_256x256_nt_group",
     "gemm_w4_nn_kernel<2>": "gemm_bf16_256x256_nn_store",
+    "gemm_w4_nf4_kernel": "gemm_nf4_256x256_nt_whole",
     "gemm_kernel<unsigned short, 256, 64, 4, 1, false, 4, 0>": "panel_bf16_split",
     "panel_dma_kernel": "panel_bf16_split",
     "splitnn_dma_kernel": "split_bf16_nn_partial",
@@ -506,6 +507,59 @@ def small_token_sweep(device, reps=10):
     return res
 
 
+def nf4_paths(device, reps=10):
+    """The two NF4 forward paths on the Qwen1.5-32B MLP shapes (gate
+    5120->27392, down 27392->5120, r 64): the whole-tile GEMM expanding the
+    codes in its load stage against the one-pass dequantisation followed by
+    the bf16 GEMM, timed round-robin, at 512, 2048 and 8192 tokens (the
+    library's automatic choice takes the load stage only for 128-255 whole
+    tiles)."""
+    import math
+
+    import torch
+
+    import lora_linear_layers_amd as L
+    from lora_linear_layers_amd import _lib
+    from synth import gen
+
+    tab = gen.nf4_table()
+    res = {}
+    r = 64
+    prev = _lib.set_nf4_fwd_path("auto")
+    try:
+        for name, k, d in (("gate_proj", 5120, 27392), ("down_proj", 27392, 5120)):
+            seed = 9500 + d
+            codes = gen.nf4_random_codes(seed + 1, d * k, device=device)
+            absmax = gen.nf4_random_absmax(seed + 4, d * k // 64, 1.0 / math.sqrt(k), device=device)
+            A = gen.to_storage(gen.uniform_sym(seed + 2, r * k, 1.0 / math.sqrt(k), device=device), (r, k), "bf16")
+            B = gen.to_storage(gen.normal(seed + 3, d * r, math.sqrt(0.02), device=device), (d, r), "bf16")
+            for M in (512, 2048, 8192):
+                X = gen.to_storage(gen.normal(seed + 5, M * k, 1.0, device=device), (M, k), "bf16")
+                Y = torch.empty(M, d, dtype=torch.bfloat16, device=device)
+                ws = {}
+                for mode in ("load_stage", "dequant"):
+                    _lib.set_nf4_fwd_path(mode)
+                    ws[mode] = torch.empty(max(L.workspace_bytes(L.OP_NF4_FWD, L.LORA_BF16, M, k, d, r), 256),
+                                           dtype=torch.uint8, device=device)
+
+                def call(mode):
+                    _lib.set_nf4_fwd_path(mode)
+                    L.nf4_lora_linear_fwd(X, codes, absmax, tab, A, B, 0.25, d, Y=Y, ws=ws[mode])
+
+                t = _time_interleaved({"load_stage_ms": lambda: call("load_stage"),
+                                       "dequant_ms": lambda: call("dequant")}, reps)
+                fl = 2.0 * M * d * (k + r)
+                for key in ("load_stage_ms", "dequant_ms"):
+                    t[key.replace("_ms", "_tflops")] = round(fl / (t[key]["median"] * 1e-3) / 1e12, 1)
+                t["tiles_256"] = (M // 256) * (d // 256)
+                res[f"{name} {k}->{d} M={M}"] = t
+                del X, Y, ws
+            del codes, absmax
+    finally:
+        _lib.set_nf4_fwd_path(prev)
+    return res
+
+
 def _rope_bwd(L, it, w, s, ws, out):
     from lora_linear_layers_amd import _lib
 
@@ -825,6 +879,7 @@ def main():
         out["small_token"] = small_token_sweep(dev)
     if args.call_reps > 0:
         out["next_rows"] = next_rows(work, args.call_reps)
+        out["nf4_paths"] = nf4_paths(dev, args.call_reps)
     if not args.no_configs:
         if cfg.dtype == "bf16" and not cfg.nf4 and not args.no_wt:
             out["config"]["without_w_t"] = without_wt(args, dev, cfg)

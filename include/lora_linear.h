@@ -185,14 +185,32 @@ int lora_qk_rope_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
  *     W[e] = bf16_rne(fp32_rne(table16[code_e] * absmax[e / blocksize])).
  * Below LORA_NF4_DEQUANT_MIN_TOKENS tokens (M) it is formed inside the GEMM's
  * load stage and never written to memory: there the GEMM is bound by reading
- * W, and the codes are a quarter of its bf16 bytes.  From that M on, the same
- * routine writes W once per call into the workspace (2 * d_out * d_in bytes,
- * included in lora_workspace_bytes) and the bf16 GEMMs read it: there the GEMM
- * is bound by the matrix cores, and the load stage would repeat the lookup
- * once per 256-row tile of X.  Both give the same W bit for bit.
+ * W, and the codes are a quarter of its bf16 bytes.  From that M on, either
+ * the whole-tile GEMM expands W in its load stage (M and d_out multiples of
+ * 256), or the same routine writes W once per call into the workspace
+ * (2 * d_out * d_in bytes, included in lora_workspace_bytes) and the bf16
+ * GEMMs read it; lora_set_nf4_fwd_path picks between them.  Every path gives
+ * the same W bit for bit.
  * blocksize must be 64 and d_in a multiple of 64.  X, A, B, Y are bf16.
  */
 #define LORA_NF4_DEQUANT_MIN_TOKENS 512
+
+/*
+ * Which NF4 forward path runs from LORA_NF4_DEQUANT_MIN_TOKENS tokens on, for
+ * every later call in the process (a measurement and test control):
+ *   LORA_NF4_PATH_AUTO        the library's choice by shape (the default);
+ *   LORA_NF4_PATH_DEQUANT     W dequantised once per call, then the bf16 GEMM;
+ *   LORA_NF4_PATH_LOAD_STAGE  the whole-tile GEMM expanding W in its load
+ *                             stage wherever M and d_out are multiples of 256.
+ * lora_workspace_bytes depends on it: size the workspace after setting it,
+ * and do not change it while a call that was sized under another mode is
+ * pending.  Returns the previous mode, or LORA_ERR_SHAPE for another value
+ * (no change).  No HIP call.
+ */
+#define LORA_NF4_PATH_AUTO 0
+#define LORA_NF4_PATH_DEQUANT 1
+#define LORA_NF4_PATH_LOAD_STAGE 2
+int lora_set_nf4_fwd_path(int mode);
 int nf4_lora_linear_fwd(int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale,
                         const void* X, const uint8_t* W_nf4, const float* absmax, int blocksize,
                         const float* table16, const void* A, const void* B, void* Y, void* ws,

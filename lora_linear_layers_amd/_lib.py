@@ -71,6 +71,7 @@ _SIGS = {
     "lora_profile_end": ([], _int),
     "lora_profile_only": ([_int], _int),
     "lora_profile_kinds": ([], _int),
+    "lora_set_nf4_fwd_path": ([_int], _int),
     "lora_profile_kind_name": ([_int], ctypes.c_char_p),
     "lora_profile_query": ([_int, ctypes.POINTER(_dbl), ctypes.POINTER(_int), ctypes.POINTER(_dbl),
                             ctypes.POINTER(_dbl)], _int),
@@ -164,6 +165,18 @@ def profile_only(kind_name=None):
         names = [lib().lora_profile_kind_name(i).decode() for i in range(lib().lora_profile_kinds())]
         k = names.index(kind_name)
     _check("lora_profile_only", lib().lora_profile_only(k))
+
+
+NF4_PATH = {"auto": 0, "dequant": 1, "load_stage": 2}
+
+
+def set_nf4_fwd_path(mode: str) -> str:
+    """Pick the NF4 forward path for later calls ("auto", "dequant" or
+    "load_stage", lora_set_nf4_fwd_path); returns the previous one."""
+    prev = lib().lora_set_nf4_fwd_path(NF4_PATH[mode])
+    if prev < 0:
+        _check("lora_set_nf4_fwd_path", prev)
+    return {v: k for k, v in NF4_PATH.items()}[prev]
 
 
 def mfma_rate(iters: int = 4096, blocks: int = 1024, device=None) -> float:

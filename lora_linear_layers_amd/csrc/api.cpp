@@ -147,6 +147,7 @@ struct Layout {
   int splits_main = 1;  // contraction splits of the Y (forward) or dX (backward) GEMM
   int64_t ksplit_main = 0;
   bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
+  bool nf4_whole = false;  // NF4 forward: whole-tile GEMM expanding W in its load stage
   // dX on whole tiles: W^T [d_in, d_out] and A^T [d_in, r8] in the workspace,
   // and the input gradient runs through the forward-orientation kernel
   bool dx_nt = false;
@@ -225,6 +226,30 @@ void main_split(int64_t M, int64_t N, int64_t K, int* splits, int64_t* ksplit) {
   *splits = (int)cdiv(K, ks);
 }
 
+// NF4 forward from LORA_NF4_DEQUANT_MIN_TOKENS tokens on: W expanded in the
+// whole-tile GEMM's load stage, or dequantised once per call into the
+// workspace for the bf16 GEMM (lora_set_nf4_fwd_path).  Automatic: the load
+// stage only for 128 to 255 whole 256 x 256 tiles.  Measured on MI355X
+// (r = 64, Qwen1.5-32B shapes): with 256 tiles or more the dequantised W runs
+// the bf16 whole-tile kernel and wins (gate 5120 -> 27392 at 8192 tokens:
+// 1.81 against 2.82 ms; the expansion's permutes, products and LDS writes
+// slow every stage); below 256 the bf16 path falls back to 128 x 128 tiles
+// and the load stage wins down to about 128 tiles (gate at 512 tokens, 214
+// tiles: 0.25 against 0.40 ms; down 27392 -> 5120 at 2048, 160 tiles: 1.03
+// against 1.34 ms); with fewer tiles its stages wait on the codes' latency
+// (80 tiles: 1.01 against 0.76 ms).
+std::atomic<int> g_nf4_fwd_path{LORA_NF4_PATH_AUTO};
+
+bool nf4_fwd_whole(int64_t M, int64_t d_in, int64_t d_out) {
+  const int mode = g_nf4_fwd_path.load();
+  if (mode == LORA_NF4_PATH_DEQUANT) return false;
+  const bool fits = M >= LORA_NF4_DEQUANT_MIN_TOKENS && M % 256 == 0 && d_out % 256 == 0 && d_in % 64 == 0 &&
+                    whole_ld_fits(d_in);
+  if (mode == LORA_NF4_PATH_LOAD_STAGE) return fits;
+  const int64_t tiles = (M / 256) * (d_out / 256);
+  return fits && tiles >= 128 && tiles < 256;
+}
+
 // have_wt: the caller supplies W^T, so the backward needs no room for it.
 Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, bool have_wt = false) {
   Layout L;
@@ -244,7 +269,9 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
   }
   const bool drop = op == LORA_OP_DROPOUT_FWD || op == LORA_OP_DROPOUT_BWD;
   const bool bwd = op == LORA_OP_BWD || op == LORA_OP_ROPE_BWD || op == LORA_OP_NF4_BWD || op == LORA_OP_DROPOUT_BWD;
-  if ((op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD) && M >= LORA_NF4_DEQUANT_MIN_TOKENS) {
+  if (op == LORA_OP_NF4_FWD && nf4_fwd_whole(M, d_in, d_out)) {
+    L.nf4_whole = true;
+  } else if ((op == LORA_OP_NF4_FWD || op == LORA_OP_NF4_BWD) && M >= LORA_NF4_DEQUANT_MIN_TOKENS) {
     L.dequant = true;
     L.wdq = take(size_t(d_out) * d_in * 2);
   }
@@ -375,7 +402,8 @@ const char* kind_name(int k) {
       "panel_bf16_split",           "gemm_bf16_128x128_nt_split", "gemm_bf16_128x128_nn_split",
       "gemm_nf4_128x128_nt_split",  "gemm_nf4_128x128_nn_split",  "merge_bf16_128x128",
       "merge_f32_64x128",           "gemm_bf16_256x256_swiglu",   "dropout_dx_bf16_128x128",
-      "dropout_dx_f32_64x128",      "gemm_bf16_256x256_nt_group", "pad_cols",
+      "dropout_dx_f32_64x128",      "gemm_bf16_256x256_nt_group", "gemm_nf4_256x256_nt_whole",
+      "pad_cols",
       "rope_inverse",
       "reduce_splits",              "fill_zero",                  "rope_cache",
       "nf4_dequant",                "panel_reduce",               "transpose_ab",
@@ -619,6 +647,15 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   a.c = Y; a.ldc = d_out;
   GemmKind k;
   const bool big = use_big(M, d_out);
+  if (nf4 && L.nf4_whole) {
+    // whole tiles, W expanded from its codes in the load stage
+    a.codes = nf4->codes; a.absmax = nf4->absmax; a.codes_ld = d_in / 2; a.blocks_per_row = d_in / 64;
+    for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
+    const double flop = 2 * Md * ko * (ki + rr);
+    const double bytes = (Md * ki + Md * rr + ko * rr + Md * ko) * e + ko * ki * (0.5 + 1.0 / 16);
+    HIPTRY(gemm(G_NF4_WHOLE_NT_STORE, a, 1, st, flop, bytes));
+    return LORA_OK;
+  }
   if (nf4) {
     a.codes = nf4->codes; a.absmax = nf4->absmax; a.codes_ld = d_in / 2; a.blocks_per_row = d_in / 64;
     for (int i = 0; i < 16; ++i) a.nf4_table[i] = nf4->table[i];
@@ -1730,6 +1767,12 @@ int lora_profile_only(int kind) {
 }
 
 int lora_profile_kinds(void) { return K_PROF_COUNT; }
+
+int lora_set_nf4_fwd_path(int mode) {
+  if (mode != LORA_NF4_PATH_AUTO && mode != LORA_NF4_PATH_DEQUANT && mode != LORA_NF4_PATH_LOAD_STAGE)
+    return LORA_ERR_SHAPE;
+  return g_nf4_fwd_path.exchange(mode);
+}
 
 const char* lora_profile_kind_name(int kind) { return kind_name(kind); }
 

@@ -10,6 +10,7 @@
 #include "gemm.h"
 #include "gemm_w4.h"
 #include "gemm_w4_nt.h"
+#include "gemm_w4_nf4.h"
 #include "gemm_panel.h"
 #include "skinny.h"
 #include "few.h"
@@ -139,6 +140,7 @@ TileShape gemm_tile(GemmKind k) {
       return {64, 256};
     case G_BF16_WHOLE_SWIGLU:
     case G_BF16_WHOLE_GROUP:
+    case G_NF4_WHOLE_NT_STORE:
       return {256, 256};
     case G_BF16_PANEL_SPLIT_NT:
       return {256, 64};
@@ -199,6 +201,20 @@ hipError_t launch_gemm(GemmKind k, GemmArgs a, int splits, hipStream_t st) {
           (int64_t)a.mem_tile0[a.n_mem] != (a.m_store / w4::BM) * (a.n_store / w4::BN))
         return hipErrorInvalidValue;
       return run_whole<false, EPI_GROUP>(a, st);
+    case G_NF4_WHOLE_NT_STORE: {
+      // whole tiles, codes and absmax present, every lane offset of a tile's
+      // codes and absmax below the buffer-resource range
+      if (!whole_tiles(a, splits) || !a.codes || !a.absmax || a.K1 < w4::BK || a.codes_ld * 2 != a.K1 ||
+          a.blocks_per_row * w4::BK != a.K1 || a.codes_ld * (w4::BN + 1) >= (int64_t)w4::BIG)
+        return hipErrorInvalidValue;
+      const int64_t tiles_m = a.m_store / w4::BM;
+      const int64_t nblocks = tiles_m * (a.n_store / w4::BN);
+      if (nblocks <= 0) return hipSuccess;
+      if (nblocks > INT32_MAX) return hipErrorInvalidValue;
+      a.tiles_m = (int)tiles_m;
+      hipLaunchKernelGGL(gemm_w4_nf4_kernel, dim3((unsigned)nblocks), dim3(w4::NT), 0, st, a);
+      return hipGetLastError();
+    }
     case G_F32_NN_ADD: return run<float, 64, 128, 4, 1, true, EPI_ADD, BL_PLAIN>(a, splits, st);
     case G_BF16_MED_NN_ADD_MASKED: return run<bf, 128, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);
     case G_F32_NN_ADD_MASKED: return run<float, 64, 128, 4, 1, true, EPI_ADD_MASKED, BL_PLAIN>(a, splits, st);

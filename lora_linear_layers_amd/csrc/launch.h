@@ -55,6 +55,7 @@ enum GemmKind : int {
   G_BF16_MED_NN_ADD_MASKED,
   G_F32_NN_ADD_MASKED,
   G_BF16_WHOLE_GROUP,  // several projections' forward GEMMs in one whole-tile launch (GemmArgs::n_mem)
+  G_NF4_WHOLE_NT_STORE,  // whole-tile forward GEMM, NF4 W expanded in the load stage (gemm_w4_nf4_kernel)
   G_KIND_COUNT
 };
 

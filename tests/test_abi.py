@@ -213,6 +213,29 @@ def test_profile_only_validation(lib):
     assert lib.lora_profile_only(-1) == 0
 
 
+def test_nf4_fwd_path_switch(lib):
+    # the NF4 forward path switch: previous mode back, bad modes rejected, and
+    # the workspace follows it (the load stage needs no dequantised W)
+    f = lib.lora_workspace_bytes
+    prev = lib.lora_set_nf4_fwd_path(1)
+    try:
+        assert lib.lora_set_nf4_fwd_path(3) == ESHAPE
+        assert lib.lora_set_nf4_fwd_path(-1) == ESHAPE
+        deq = f(_lib.OP_NF4_FWD, 1, 1024, 1024, 2048, 16)
+        assert lib.lora_set_nf4_fwd_path(2) == 1
+        whole = f(_lib.OP_NF4_FWD, 1, 1024, 1024, 2048, 16)
+        assert deq - whole >= 2048 * 1024 * 2
+        # below LORA_NF4_DEQUANT_MIN_TOKENS, or with tiles that are not whole,
+        # nothing changes
+        assert f(_lib.OP_NF4_FWD, 1, 256, 1024, 2048, 16) == f(_lib.OP_NF4_FWD, 1, 256, 1024, 2048, 16)
+        lib.lora_set_nf4_fwd_path(1)
+        ragged = f(_lib.OP_NF4_FWD, 1, 1000, 1024, 2048, 16)
+        lib.lora_set_nf4_fwd_path(2)
+        assert f(_lib.OP_NF4_FWD, 1, 1000, 1024, 2048, 16) == ragged
+    finally:
+        lib.lora_set_nf4_fwd_path(prev)
+
+
 def test_merge_validation(lib):
     def call(dtype=1, d_out=64, d_in=64, r=8, W=P, A=P, B=P, out=P, ws=P, wsb=1 << 20):
         return lib.lora_merge(dtype, d_out, d_in, r, 1.0, W, A, B, out, ws, wsb, None)

@@ -335,6 +335,43 @@ def test_nf4_fwd_bwd_parity(lib, M, d_in, d_out, r):
     assert torch.equal(Y, Yb)
 
 
+@pytest.mark.parametrize("M,d_in,d_out,r", [(512, 1024, 1024, 16), (768, 640, 512, 64), (512, 128, 768, 8),
+                                             (512, 64, 256, 3), (1024, 320, 512, 200), (4096, 1024, 4096, 16)])
+def test_nf4_load_stage_forward(lib, M, d_in, d_out, r):
+    # the whole-tile GEMM that expands NF4 codes in its load stage (one and
+    # two stages of W, several rank stages, a ragged rank): within the bar of
+    # the oracle; and where the dequantise-once path also runs whole 256 x 256
+    # tiles (at least 256 of them), bit-equal to it: the same tile, stage and
+    # MFMA order on the same W values
+    from lora_linear_layers_amd import _lib
+    tab = gen.nf4_table()
+    X, _, A, B, _ = lora_inputs(61 + M + r, M, d_in, d_out, r, "bf16")
+    codes, absmax = _nf4_weight(63 + d_in, d_out, d_in)
+    s = 16.0 / r
+    prev = _lib.set_nf4_fwd_path("load_stage")
+    try:
+        _lib.profile_only(None)
+        _lib.profile_begin(64)
+        Y = lib.nf4_lora_linear_fwd(X, codes, absmax, tab, A, B, s, d_out)
+        torch.cuda.synchronize()
+        _lib.profile_end()
+        kinds = set(_lib.profile_report())
+        _lib.set_nf4_fwd_path("dequant")
+        Yd = lib.nf4_lora_linear_fwd(X, codes, absmax, tab, A, B, s, d_out)
+        torch.cuda.synchronize()
+    finally:
+        _lib.set_nf4_fwd_path(prev)
+    assert "gemm_nf4_256x256_nt_whole" in kinds, kinds
+    Yr = O.nf4_lora_forward(X, codes.cpu().numpy(), absmax.cpu().numpy(), tab, A, B, s, d_out, d_in)
+    e = rel(Y, Yr)
+    print("nf4 load stage", M, d_in, d_out, r, e)
+    assert e <= 2e-2
+    if (M // 256) * (d_out // 256) >= 256:
+        assert torch.equal(Y, Yd)
+    else:
+        assert rel(Yd, Yr) <= 2e-2
+
+
 def test_nf4_whole_tile_backward_equals_bf16_on_dequantised(lib):
     # from 512 tokens on whole tiles the NF4 backward dequantises straight
     # into W^T; the result must equal, bit for bit, the bf16 backward on the
