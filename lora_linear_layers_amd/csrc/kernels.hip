@@ -363,6 +363,10 @@ __device__ __forceinline__ float ld_as_f32(const T* p, int64_t i) {
 // One thread per (row t, head h, group of 8 frequencies): rotates the pairs
 // (h*128 + f, h*128 + f + 64) for f in [8q, 8q+8) by the negated angle:
 //   g1 = y1 cos + y2 sin,   g2 = y2 cos - y1 sin.
+// Every access is a 16-byte vector: the 8 values of each half of the pair
+// group (bf16: one vector, fp32: two), their 8 cos and 8 sin; the 8 lanes of
+// a (row, head) read and write whole 128-byte pieces.  (Scalar 2-byte
+// accesses, one frequency per instruction, ran this pass at 1.5 TB/s.)
 template <typename T>
 __global__ void rope_inverse_kernel(const T* __restrict__ dY, T* __restrict__ G, int64_t M, int64_t d_out,
                                     const int32_t* __restrict__ pos, const float* __restrict__ cosc,
@@ -375,20 +379,61 @@ __global__ void rope_inverse_kernel(const T* __restrict__ dY, T* __restrict__ G,
     const int64_t t = th / heads, h = th - t * heads;
     const int32_t ps = pos[t];
     const bool ok = rope_pos_ok(ps, max_pos);
-    const int64_t prow = ok ? (int64_t)ps * 64 : 0;
-    const int64_t base = t * d_out + h * 128;
+    const int64_t prow = (ok ? (int64_t)ps * 64 : 0) + 8 * q;
+    const int64_t i1 = t * d_out + h * 128 + 8 * q, i2 = i1 + 64;
+    float c[8], sn[8], y1[8], y2[8];
+    {
+      const float4 c0 = *reinterpret_cast<const float4*>(cosc + prow);
+      const float4 c1 = *reinterpret_cast<const float4*>(cosc + prow + 4);
+      const float4 s0 = *reinterpret_cast<const float4*>(sinc + prow);
+      const float4 s1 = *reinterpret_cast<const float4*>(sinc + prow + 4);
+      const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        c[u] = ok ? cv[u] : 0.f;
+        sn[u] = ok ? sv[u] : 0.f;
+      }
+    }
+    if constexpr (sizeof(T) == 2) {
+      const uint4 a = *reinterpret_cast<const uint4*>(dY + i1);
+      const uint4 b = *reinterpret_cast<const uint4*>(dY + i2);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y1[2 * k] = __builtin_bit_cast(float, av[k] << 16);
+        y1[2 * k + 1] = __builtin_bit_cast(float, av[k] & 0xffff0000u);
+        y2[2 * k] = __builtin_bit_cast(float, bv[k] << 16);
+        y2[2 * k + 1] = __builtin_bit_cast(float, bv[k] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float4 a = *reinterpret_cast<const float4*>(dY + i1 + 4 * k);
+        const float4 b = *reinterpret_cast<const float4*>(dY + i2 + 4 * k);
+        y1[4 * k] = a.x; y1[4 * k + 1] = a.y; y1[4 * k + 2] = a.z; y1[4 * k + 3] = a.w;
+        y2[4 * k] = b.x; y2[4 * k + 1] = b.y; y2[4 * k + 2] = b.z; y2[4 * k + 3] = b.w;
+      }
+    }
+    float g1[8], g2[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int64_t f = q * 8 + u;
-      const float c = ok ? cosc[prow + f] : 0.f, s = ok ? sinc[prow + f] : 0.f;
-      const float y1 = ld_as_f32(dY, base + f), y2 = ld_as_f32(dY, base + f + 64);
-      const float g1 = y1 * c + y2 * s, g2 = y2 * c - y1 * s;
-      if constexpr (sizeof(T) == 2) {
-        G[base + f] = f2bf(g1);
-        G[base + f + 64] = f2bf(g2);
-      } else {
-        G[base + f] = g1;
-        G[base + f + 64] = g2;
+      g1[u] = y1[u] * c[u] + y2[u] * sn[u];
+      g2[u] = y2[u] * c[u] - y1[u] * sn[u];
+    }
+    if constexpr (sizeof(T) == 2) {
+      uint4 o1, o2;
+      o1.x = pack_bf16x2(g1[0], g1[1]); o1.y = pack_bf16x2(g1[2], g1[3]);
+      o1.z = pack_bf16x2(g1[4], g1[5]); o1.w = pack_bf16x2(g1[6], g1[7]);
+      o2.x = pack_bf16x2(g2[0], g2[1]); o2.y = pack_bf16x2(g2[2], g2[3]);
+      o2.z = pack_bf16x2(g2[4], g2[5]); o2.w = pack_bf16x2(g2[6], g2[7]);
+      *reinterpret_cast<uint4*>(G + i1) = o1;
+      *reinterpret_cast<uint4*>(G + i2) = o2;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        *reinterpret_cast<float4*>(G + i1 + 4 * k) = make_float4(g1[4 * k], g1[4 * k + 1], g1[4 * k + 2], g1[4 * k + 3]);
+        *reinterpret_cast<float4*>(G + i2 + 4 * k) = make_float4(g2[4 * k], g2[4 * k + 1], g2[4 * k + 2], g2[4 * k + 3]);
       }
     }
   }
