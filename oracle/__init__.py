@@ -23,6 +23,11 @@ from .lora_oracle import (  # noqa: F401
     nf4_lora_backward,
     merged_weight,
     dropout_keep,
+    philox4x32_10,
+    dropout_threshold,
+    dropout_mask_philox,
+    dropout_mask_philox_np,
+    dropout_pack,
     lora_dropout_forward,
     lora_dropout_backward,
     silu,

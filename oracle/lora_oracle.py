@@ -43,7 +43,8 @@ notes):
   * LoRA dropout (a rate on the pages, not a definition): inverted dropout on
     the adapter's input only, D(x) = x * keep / (1 - p) with keep ~ Bernoulli(1 - p)
     per element of X; the base path W x sees x unchanged.  The keep mask is an
-    input (bit-packed, bit b of byte [i, j] keeps element (i, 8 j + b));
+    input (bit-packed, bit b of byte [i, j] keeps element (i, 8 j + b)), or is
+    drawn from a Philox4x32-10 stream keyed by a seed (dropout_mask_philox);
   * SwiGLU (named, not defined, on the pages): the Llama MLP's gated unit
     h = silu(g) * u elementwise, g and u the gate and up projections of the
     same x, silu(z) = z / (1 + e^-z).
@@ -238,6 +239,82 @@ def dropout_keep(bits, M: int, d_in: int) -> np.ndarray:
     for bit in range(8):
         out[:, bit::8] = (b >> bit) & 1
     return out
+
+
+# Philox4x32-10 (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel
+# random numbers: as easy as 1, 2, 3", SC'11, section 4): a counter-based
+# generator whose output block is a keyed bijection of a 128-bit counter.  The
+# dropout mask is drawn from it so that the backward regenerates the forward's
+# mask from (seed, offset) instead of storing it.
+
+PHILOX_M0, PHILOX_M1 = 0xD2511F53, 0xCD9E8D57  # round multipliers
+PHILOX_W0, PHILOX_W1 = 0x9E3779B9, 0xBB67AE85  # key schedule increments (Weyl)
+_U32 = 0xFFFFFFFF
+
+
+def philox4x32_10(counter, key):
+    """One output block: four 32-bit words from four counter words and two key
+    words, ten rounds.  A round multiplies words 0 and 2 by the two constants
+    (full 64-bit products), then the new words are (hi of product 1) xor word 1
+    xor key 0, (lo of product 1), (hi of product 0) xor word 3 xor key 1,
+    (lo of product 0); the key advances by the increments between rounds."""
+    x = [int(c) & _U32 for c in counter]
+    k0, k1 = int(key[0]) & _U32, int(key[1]) & _U32
+    for rnd in range(10):
+        if rnd:
+            k0, k1 = (k0 + PHILOX_W0) & _U32, (k1 + PHILOX_W1) & _U32
+        p0, p1 = PHILOX_M0 * x[0], PHILOX_M1 * x[2]
+        x = [(p1 >> 32) ^ x[1] ^ k0, p1 & _U32, (p0 >> 32) ^ x[3] ^ k1, p0 & _U32]
+    return x
+
+
+def dropout_threshold(p: float) -> int:
+    """A word w keeps its element iff w >= floor(p 2^32), with p taken as the
+    float32 the C interface receives (so P(keep) = 1 - p up to 2^-32)."""
+    return int(np.floor(float(np.float32(p)) * 4294967296.0))
+
+
+def dropout_mask_philox(n: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """bool keep mask of n elements (the row-major flattening of X [M, d_in]).
+    Element e takes word e mod 4 of the block whose counter is
+    (lo32(e // 4), hi32(e // 4), lo32(offset), hi32(offset)) under the key
+    (lo32(seed), hi32(seed)).  Plain loop over blocks: small n only."""
+    thr = dropout_threshold(p)
+    key = (seed & _U32, (seed >> 32) & _U32)
+    keep = np.zeros(n, dtype=bool)
+    for g in range((n + 3) // 4):
+        w = philox4x32_10((g & _U32, g >> 32, offset & _U32, (offset >> 32) & _U32), key)
+        for j in range(4):
+            if 4 * g + j < n:
+                keep[4 * g + j] = w[j] >= thr
+    return keep
+
+
+def dropout_mask_philox_np(n: int, p: float, seed: int, offset: int) -> np.ndarray:
+    """The same mask as dropout_mask_philox, the ten rounds evaluated on every
+    block at once in uint64 numpy arithmetic (for sizes where the loop is slow)."""
+    thr = dropout_threshold(p)
+    nb = (n + 3) // 4
+    g = np.arange(nb, dtype=np.uint64)
+    m32 = np.uint64(_U32)
+    x0, x1 = g & m32, g >> np.uint64(32)
+    x2 = np.full(nb, offset & _U32, dtype=np.uint64)
+    x3 = np.full(nb, (offset >> 32) & _U32, dtype=np.uint64)
+    k0, k1 = seed & _U32, (seed >> 32) & _U32
+    for rnd in range(10):
+        if rnd:
+            k0, k1 = (k0 + PHILOX_W0) & _U32, (k1 + PHILOX_W1) & _U32
+        p0, p1 = x0 * np.uint64(PHILOX_M0), x2 * np.uint64(PHILOX_M1)
+        x0, x1, x2, x3 = ((p1 >> np.uint64(32)) ^ x1 ^ np.uint64(k0), p1 & m32,
+                          (p0 >> np.uint64(32)) ^ x3 ^ np.uint64(k1), p0 & m32)
+    words = np.stack([x0, x1, x2, x3], axis=1).reshape(-1)[:n]
+    return words >= np.uint64(thr)
+
+
+def dropout_pack(keep) -> np.ndarray:
+    """Packed bytes of a bool mask with 8 | n: bit b of byte j is element 8 j + b."""
+    k = np.asarray(keep, dtype=bool).reshape(-1, 8).astype(np.uint8)
+    return (k << np.arange(8, dtype=np.uint8)).sum(axis=1).astype(np.uint8)
 
 
 def lora_dropout_forward(X, W, A, B, s: float, p: float, keep) -> np.ndarray:

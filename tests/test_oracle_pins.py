@@ -503,3 +503,63 @@ def test_dropout_is_unbiased_over_masks():
     ys = np.stack([O.lora_dropout_forward(X, W, A, B, 1.0, p, rng.random((M, k)) >= p) for _ in range(20000)])
     se = ys.std(axis=0) / np.sqrt(len(ys))
     assert np.all(np.abs(ys.mean(axis=0) - O.lora_forward(X, W, A, B, 1.0)) <= 5 * se + 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Philox4x32-10 dropout mask
+# ---------------------------------------------------------------------------
+
+def _philox_kat():
+    path = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    rows = []
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            w = [int(t, 16) for t in line.split()]
+            rows.append((w[0:4], w[4:6], w[6:10]))
+    return rows
+
+
+def test_philox_known_answers():
+    # the published known-answer vectors: a wrong multiplier, key increment,
+    # word order or round count changes every output word
+    rows = _philox_kat()
+    assert len(rows) == 3
+    for ctr, key, out in rows:
+        assert O.philox4x32_10(ctr, key) == out
+
+
+def test_philox_mask_word_mapping():
+    # element e takes word e mod 4 of block e // 4, the block's counter is
+    # (e // 4, 0, offset lo, offset hi) and the key (seed lo, seed hi)
+    seed, offset, p = 0x0123456789ABCDEF, 0x0000000500000007, 0.25
+    thr = O.dropout_threshold(p)
+    assert thr == 1 << 30
+    keep = O.dropout_mask_philox(24, p, seed, offset)
+    for e in range(24):
+        w = O.philox4x32_10((e // 4, 0, 7, 5), (0x89ABCDEF, 0x01234567))[e % 4]
+        assert keep[e] == (w >= thr)
+
+
+def test_philox_mask_vectorised_equals_loop():
+    for n, p, seed, off in ((40, 0.1, 3407, 0), (1000, 0.5, 2**40 + 9, 2**33 + 1), (8, 0.0, 1, 2)):
+        assert np.array_equal(O.dropout_mask_philox(n, p, seed, off), O.dropout_mask_philox_np(n, p, seed, off))
+
+
+def test_philox_mask_rate_and_limits():
+    # p = 0 keeps everything (every word >= 0); the kept share of 2^18 draws
+    # lies within 5 standard deviations of 1 - p; another seed or offset
+    # gives another mask
+    assert O.dropout_mask_philox_np(4096, 0.0, 5, 0).all()
+    n = 1 << 18
+    for p in (0.05, 0.1, 0.5):
+        k = O.dropout_mask_philox_np(n, p, 3407, 0)
+        sd = math.sqrt(n * p * (1 - p))
+        assert abs(int(k.sum()) - n * (1 - p)) < 5 * sd
+    a = O.dropout_mask_philox_np(4096, 0.5, 1, 0)
+    assert not np.array_equal(a, O.dropout_mask_philox_np(4096, 0.5, 2, 0))
+    assert not np.array_equal(a, O.dropout_mask_philox_np(4096, 0.5, 1, 1))
+
+
+def test_dropout_pack_matches_bit_order():
+    keep = O.dropout_mask_philox_np(64, 0.5, 77, 3)
+    assert np.array_equal(O.dropout_keep(O.dropout_pack(keep), 1, 64)[0], keep)
