@@ -416,9 +416,14 @@ def next_rows(work, reps=10):
             "plain_fwd_ms": lambda: L.lora_linear_fwd(X, it["W"], it["A"], it["B"], s, Y=it["Y"], ws=dws),
             "bwd_ms": lambda: L.lora_dropout_bwd(X, it["W"], it["A"], it["B"], s, p, keep, it["dY"], ws=dws),
             "plain_bwd_ms": lambda: L.lora_linear_bwd(X, it["W"], it["A"], it["B"], s, it["dY"], ws=dws,
-                                                      out=(it["dX"], it["dA"], it["dB"]))}, reps))
+                                                      out=(it["dX"], it["dA"], it["dB"])),
+            # the mask drawn on the device from Philox4x32-10 (seed 3407), again in the backward
+            "philox_fwd_ms": lambda: L.lora_dropout_philox_fwd(X, it["W"], it["A"], it["B"], s, p, 3407, 0,
+                                                               Y=it["Y"], ws=dws),
+            "philox_bwd_ms": lambda: L.lora_dropout_philox_bwd(X, it["W"], it["A"], it["B"], s, p, 3407, it["dY"],
+                                                               0, ws=dws)}, reps))
         for key, fl in (("fwd_ms", one_fwd), ("bwd_ms", one_bwd), ("plain_fwd_ms", one_fwd),
-                        ("plain_bwd_ms", one_bwd)):
+                        ("plain_bwd_ms", one_bwd), ("philox_fwd_ms", one_fwd), ("philox_bwd_ms", one_bwd)):
             dr[key.replace("_ms", "_tflops")] = round(fl / (dr[key]["median"] * 1e-3) / 1e12, 1)
         out["dropout"] = dr
         del dws, keep

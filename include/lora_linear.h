@@ -253,6 +253,36 @@ int lora_dropout_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
                      const void* dY, void* dX, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * The dropout keep mask drawn on the device from the counter-based generator
+ * Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+ * as 1, 2, 3", SC'11, section 4), so that a backward regenerates its forward's
+ * mask from the same (seed, offset) instead of keeping it.  Element e of the
+ * row-major [M, d_in] input takes word e mod 4 of the generator's block for
+ * the counter (lo32(e / 4), hi32(e / 4), lo32(offset), hi32(offset)) under the
+ * key (lo32(seed), hi32(seed)), and is kept iff that word >= floor(p 2^32).
+ * keep: device output [M, d_in / 8] bytes in lora_dropout_fwd's bit order.
+ * Needs d_in % 8 == 0 and 0 <= p < 1 (else LORA_ERR_SHAPE); asynchronous.
+ */
+int lora_dropout_mask(int64_t M, int64_t d_in, float p, uint64_t seed, uint64_t offset, uint8_t* keep,
+                      void* stream);
+
+/*
+ * lora_dropout_fwd / _bwd with the mask drawn on the device as
+ * lora_dropout_mask(M, d_in, p, seed, offset) draws it (one pass over X
+ * writes the masked copy and, in the backward, the bits); the same
+ * (seed, offset) in the forward and the backward gives the same mask.
+ * Results equal lora_dropout_fwd / _bwd given that mask.  Workspace: ops
+ * LORA_OP_DROPOUT_FWD / _BWD; errors as there.
+ */
+int lora_dropout_philox_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                            uint64_t seed, uint64_t offset, const void* X, const void* W, const void* A,
+                            const void* B, void* Y, void* ws, size_t ws_bytes, void* stream);
+int lora_dropout_philox_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                            uint64_t seed, uint64_t offset, const void* X, const void* W, const void* A,
+                            const void* B, const void* dY, void* dX, float* dA, float* dB, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * Merge for inference: W_out = W + scale * B A, one GEMM over the rank (fp32
  * accumulation) whose epilogue adds W and rounds once to the output type.
  * Page "微调太慢？试试Unsloth：实测训练速度翻倍，显存占用减半", section 5.1: for

@@ -32,6 +32,9 @@ from .functional import (  # noqa: F401
     LoraLinearFunction,
     lora_dropout_bwd,
     lora_dropout_fwd,
+    lora_dropout_mask,
+    lora_dropout_philox_bwd,
+    lora_dropout_philox_fwd,
     lora_group_bwd,
     lora_group_fwd,
     lora_linear_bwd,

@@ -22,6 +22,7 @@ _lib = None
 
 _i64, _f32, _vp, _sz, _int, _dbl = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t,
                                     ctypes.c_int, ctypes.c_double)
+_u64 = ctypes.c_uint64
 _fp = ctypes.POINTER(ctypes.c_float)
 
 GROUP_MAX = 8
@@ -65,6 +66,11 @@ _SIGS = {
                          _int),
     "lora_dropout_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                           _vp, _sz, _vp], _int),
+    "lora_dropout_mask": ([_i64, _i64, _f32, _u64, _u64, _vp, _vp], _int),
+    "lora_dropout_philox_fwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _sz, _vp], _int),
+    "lora_dropout_philox_bwd": ([_int, _i64, _i64, _i64, _i64, _f32, _f32, _u64, _u64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _vp, _vp, _vp, _sz, _vp], _int),
     "lora_mfma_rate": ([_int, _int, _vp, _vp], _int),
     "lora_transpose": ([_vp, _i64, _i64, _vp, _vp], _int),
     "lora_profile_begin": ([_int], _int),

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 #include <vector>
@@ -143,7 +144,7 @@ FewPlan few_plan(bool bwd, bool nf4, bool rope, int64_t M, int64_t d_in, int64_t
 struct Layout {
   int64_t r8 = 0, M8 = 0;
   size_t bpad = 0, bt = 0, p = 0, g = 0, pt = 0, qs = 0, qt = 0, part = 0, ppart = 0, wdq = 0, spart = 0, xm = 0,
-         total = 0;
+         keep = 0, total = 0;
   int splits_main = 1;  // contraction splits of the Y (forward) or dX (backward) GEMM
   int64_t ksplit_main = 0;
   bool dequant = false;  // NF4: W dequantised once into wdq, then the bf16 GEMMs
@@ -322,6 +323,8 @@ Layout make_layout(int op, int dtype, int64_t M, int64_t d_in, int64_t d_out, in
     L.spart = L.part;
   }
   if (drop) L.xm = take(size_t(M) * d_in * eb);
+  // the backward's keep bits when it draws them itself (Philox entry point)
+  if (op == LORA_OP_DROPOUT_BWD) L.keep = take(size_t(M) * d_in / 8);
   L.total = off;
   if (eb == 2 && !drop) {
     const bool rope = op == LORA_OP_ROPE_FWD || op == LORA_OP_ROPE_BWD;
@@ -1653,6 +1656,68 @@ int lora_dropout_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t 
   if (M > 0)
     HIPTRY(timed(K_MASK, 0, (2.0 * elem_bytes(dtype) + 0.125) * M * d_in, st,
                  [&] { return launch_mask_copy(elem_bytes(dtype), X, keep, Xm, M * d_in, st); }));
+  return backward_impl(dtype, M, d_in, d_out, r, scale / (1.f - p), X, W, nullptr, A, B, nullptr, dY, dX, dA, dB,
+                       ws, L, st, nullptr, Xm, keep);
+}
+
+static uint32_t dropout_threshold(float p) { return (uint32_t)std::floor(double(p) * 4294967296.0); }
+
+int lora_dropout_mask(int64_t M, int64_t d_in, float p, uint64_t seed, uint64_t offset, uint8_t* keep,
+                      void* stream) {
+  if (M < 0 || d_in <= 0 || d_in % 8) return LORA_ERR_SHAPE;
+  if (!(p >= 0.f && p < 1.f)) return LORA_ERR_SHAPE;
+  if (M == 0) return LORA_OK;
+  TRY(check_ptrs({keep}));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIPTRY(timed(K_MASK, 0, 0.125 * M * d_in, st, [&] {
+    return launch_dropout_philox(2, nullptr, nullptr, keep, M * d_in, dropout_threshold(p), seed, offset, st);
+  }));
+  return LORA_OK;
+}
+
+int lora_dropout_philox_fwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                            uint64_t seed, uint64_t offset, const void* X, const void* W, const void* A,
+                            const void* B, void* Y, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  if (!(p >= 0.f && p < 1.f)) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({W, A, B}));
+  if (M > 0) TRY(check_ptrs({X, Y}));
+  const Layout L = make_layout(LORA_OP_DROPOUT_FWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* Xm = static_cast<char*>(ws) + L.xm;
+  HIPTRY(timed(K_MASK, 0, 2.0 * elem_bytes(dtype) * M * d_in, st, [&] {
+    return launch_dropout_philox(elem_bytes(dtype), X, Xm, nullptr, M * d_in, dropout_threshold(p), seed, offset,
+                                 st);
+  }));
+  return forward_impl(dtype, M, d_in, d_out, r, scale / (1.f - p), X, W, nullptr, A, B, nullptr, Y, ws, L, st,
+                      nullptr, 0, Xm);
+}
+
+int lora_dropout_philox_bwd(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, float scale, float p,
+                            uint64_t seed, uint64_t offset, const void* X, const void* W, const void* A,
+                            const void* B, const void* dY, void* dX, float* dA, float* dB, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (dtype != LORA_F32 && dtype != LORA_BF16) return LORA_ERR_DTYPE;
+  TRY(check_sizes(M, d_in, d_out, r));
+  if (!(p >= 0.f && p < 1.f)) return LORA_ERR_SHAPE;
+  TRY(check_ptrs({W, A, B, dA, dB}));
+  if (M > 0) TRY(check_ptrs({X, dY}));
+  if (dX && !aligned16(dX)) return LORA_ERR_ALIGN;
+  const Layout L = make_layout(LORA_OP_DROPOUT_BWD, dtype, M, d_in, d_out, r);
+  TRY(check_ws(L, ws, ws_bytes));
+  TRY(check_device());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  void* Xm = static_cast<char*>(ws) + L.xm;
+  uint8_t* keep = reinterpret_cast<uint8_t*>(static_cast<char*>(ws) + L.keep);
+  if (M > 0)
+    HIPTRY(timed(K_MASK, 0, (2.0 * elem_bytes(dtype) + 0.125) * M * d_in, st, [&] {
+      return launch_dropout_philox(elem_bytes(dtype), X, Xm, keep, M * d_in, dropout_threshold(p), seed, offset,
+                                   st);
+    }));
   return backward_impl(dtype, M, d_in, d_out, r, scale / (1.f - p), X, W, nullptr, A, B, nullptr, dY, dX, dA, dB,
                        ws, L, st, nullptr, Xm, keep);
 }

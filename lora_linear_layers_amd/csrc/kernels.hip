@@ -870,6 +870,85 @@ hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, 
   return hipGetLastError();
 }
 
+// The dropout keep mask drawn on the device from Philox4x32-10 (J. K. Salmon
+// et al., "Parallel random numbers: as easy as 1, 2, 3", SC'11, section 4),
+// so the backward regenerates the forward's mask from (seed, offset) instead
+// of reading a stored one.  Element e of the flattened input takes word e & 3
+// of the block with counter (lo32(e >> 2), hi32(e >> 2), o0, o1) under the key
+// (k0, k1) and is kept iff that word >= thr (thr = floor(p 2^32)).
+__device__ __forceinline__ void philox4x32_10(uint32_t& x0, uint32_t& x1, uint32_t& x2, uint32_t& x3, uint32_t k0,
+                                              uint32_t k1) {
+#pragma unroll
+  for (int rnd = 0; rnd < 10; ++rnd) {
+    const uint64_t a = (uint64_t)0xD2511F53u * x0, b = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t y0 = (uint32_t)(b >> 32) ^ x1 ^ k0, y2 = (uint32_t)(a >> 32) ^ x3 ^ k1;
+    x0 = y0;
+    x1 = (uint32_t)b;
+    x2 = y2;
+    x3 = (uint32_t)a;
+    k0 += 0x9E3779B9u;  // the key after the last round is unused
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// One mask byte (8 elements, two Philox blocks) per thread and iteration:
+// writes the packed byte (bit b keeps element 8 e + b) if keep is set and the
+// masked copy of X (kept elements exact, the rest 0) if out is set.
+template <int EB>
+__global__ void dropout_philox_kernel(const void* __restrict__ X, void* __restrict__ out,
+                                      uint8_t* __restrict__ keep, int64_t n8, uint32_t thr, uint32_t k0,
+                                      uint32_t k1, uint32_t o0, uint32_t o1) {
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n8; e += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint64_t g = 2 * (uint64_t)e + h;
+      uint32_t x0 = (uint32_t)g, x1 = (uint32_t)(g >> 32), x2 = o0, x3 = o1;
+      philox4x32_10(x0, x1, x2, x3, k0, k1);
+      bits |= ((x0 >= thr ? 1u : 0u) | (x1 >= thr ? 2u : 0u) | (x2 >= thr ? 4u : 0u) | (x3 >= thr ? 8u : 0u))
+              << (4 * h);
+    }
+    if (keep) keep[e] = (uint8_t)bits;
+    if (!out) continue;
+    if constexpr (EB == 2) {
+      u32x4 v = static_cast<const u32x4*>(X)[e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[q] &= (((bits >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u) | (((bits >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u);
+      static_cast<u32x4*>(out)[e] = v;
+    } else {
+      const float4* x = static_cast<const float4*>(X);
+      float4 a = x[2 * e], b = x[2 * e + 1];
+      a.x = (bits & 1u) ? a.x : 0.f;
+      a.y = (bits & 2u) ? a.y : 0.f;
+      a.z = (bits & 4u) ? a.z : 0.f;
+      a.w = (bits & 8u) ? a.w : 0.f;
+      b.x = (bits & 16u) ? b.x : 0.f;
+      b.y = (bits & 32u) ? b.y : 0.f;
+      b.z = (bits & 64u) ? b.z : 0.f;
+      b.w = (bits & 128u) ? b.w : 0.f;
+      static_cast<float4*>(out)[2 * e] = a;
+      static_cast<float4*>(out)[2 * e + 1] = b;
+    }
+  }
+}
+
+hipError_t launch_dropout_philox(int elem_bytes, const void* X, void* out, uint8_t* keep, int64_t n, uint32_t thr,
+                                 uint64_t seed, uint64_t offset, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8 || (out && !X)) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32), o0 = (uint32_t)offset,
+                 o1 = (uint32_t)(offset >> 32);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(dropout_philox_kernel<2>, dim3(grid_for(n8, 256)), dim3(256), 0, st, X, out, keep, n8, thr,
+                       k0, k1, o0, o1);
+  else
+    hipLaunchKernelGGL(dropout_philox_kernel<4>, dim3(grid_for(n8, 256)), dim3(256), 0, st, X, out, keep, n8, thr,
+                       k0, k1, o0, o1);
+  return hipGetLastError();
+}
+
 constexpr int kMaxPanelSplits = 32;
 
 // One 16-row x 64-column tile of the panel per workgroup: the fixed-order

@@ -169,6 +169,10 @@ hipError_t launch_add_into(int elem_bytes, void* dst, const void* src, int64_t n
 // n % 8 == 0, bit b of keep[e] is element 8 e + b).
 hipError_t launch_mask_copy(int elem_bytes, const void* X, const uint8_t* keep, void* out, int64_t n,
                             hipStream_t st);
+// Philox4x32-10 keep mask of n elements (8 | n): packed bits into keep and/or
+// the masked copy of X into out (either may be null; out needs X).
+hipError_t launch_dropout_philox(int elem_bytes, const void* X, void* out, uint8_t* keep, int64_t n, uint32_t thr,
+                                 uint64_t seed, uint64_t offset, hipStream_t st);
 
 // blocks x 256 threads of the MFMA-rate kernel (iters rounds of 8 MFMAs per
 // wave); out [blocks * 256] receives one float per thread.

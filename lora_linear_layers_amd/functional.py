@@ -190,6 +190,47 @@ def lora_dropout_bwd(X, W, A, B, scale: float, p: float, keep, dY, need_dX: bool
     return dX, dA, dB
 
 
+def lora_dropout_mask(M: int, d_in: int, p: float, seed: int, offset: int = 0, device="cuda"):
+    """The packed keep mask [M, d_in / 8] (uint8) that the Philox dropout entry
+    points draw for (seed, offset), generated on the device."""
+    keep = torch.empty(M, d_in // 8, dtype=torch.uint8, device=device)
+    L._check("lora_dropout_mask", L.lib().lora_dropout_mask(M, d_in, float(p), int(seed), int(offset),
+                                                            L._ptr(keep), L._stream(keep.device)))
+    return keep
+
+
+def lora_dropout_philox_fwd(X, W, A, B, scale: float, p: float, seed: int, offset: int = 0, Y=None, ws=None):
+    """lora_dropout_fwd with the keep mask drawn on the device from Philox4x32-10
+    (seed, offset), as lora_dropout_mask draws it."""
+    L._contig(X, W, A, B, Y)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    if Y is None:
+        Y = torch.empty(M, d_out, dtype=X.dtype, device=X.device)
+    ws = L._workspace(L.OP_DROPOUT_FWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_dropout_philox_fwd", L.lib().lora_dropout_philox_fwd(
+        dt, M, d_in, d_out, r, float(scale), float(p), int(seed), int(offset), L._ptr(X), L._ptr(W), L._ptr(A),
+        L._ptr(B), L._ptr(Y), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return Y
+
+
+def lora_dropout_philox_bwd(X, W, A, B, scale: float, p: float, seed: int, dY, offset: int = 0,
+                            need_dX: bool = True, ws=None):
+    """(dX or None, dA fp32, dB fp32) of lora_dropout_philox_fwd with the same
+    (seed, offset): the mask is drawn again, not stored."""
+    L._contig(X, W, A, B, dY)
+    M, d_in, d_out, r = _dims(X, W.shape[0], W.shape[1], A, B)
+    dt = L._dtype_code(X)
+    dX = torch.empty(M, d_in, dtype=X.dtype, device=X.device) if need_dX else None
+    dA = torch.empty(r, d_in, dtype=torch.float32, device=X.device)
+    dB = torch.empty(d_out, r, dtype=torch.float32, device=X.device)
+    ws = L._workspace(L.OP_DROPOUT_BWD, dt, M, d_in, d_out, r, X.device, ws)
+    L._check("lora_dropout_philox_bwd", L.lib().lora_dropout_philox_bwd(
+        dt, M, d_in, d_out, r, float(scale), float(p), int(seed), int(offset), L._ptr(X), L._ptr(W), L._ptr(A),
+        L._ptr(B), L._ptr(dY), L._ptr(dX), L._ptr(dA), L._ptr(dB), L._ptr(ws), ws.numel(), L._stream(X.device)))
+    return dX, dA, dB
+
+
 def _check_keep(keep, M, d_in):
     if keep.dtype != torch.uint8 or keep.numel() != M * d_in // 8:
         raise ValueError("keep must be a uint8 bit mask of M * d_in / 8 bytes")

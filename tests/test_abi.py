@@ -314,3 +314,21 @@ def test_transpose_and_wt_validation(lib):
     mt = _members(1, d_out=4096, r=16, W_t=P)
     f = lib.lora_group_workspace_bytes
     assert f(1, 1, 8192, 4096, 1, m) - f(1, 1, 8192, 4096, 1, mt) >= 4096 * 4096 * 2 - 256
+
+
+def test_dropout_mask_validation(lib):
+    f = lib.lora_dropout_mask
+    assert f(16, 12, 0.1, 1, 0, P, None) == ESHAPE  # d_in % 8
+    assert f(16, 16, 1.0, 1, 0, P, None) == ESHAPE  # p outside [0, 1)
+    assert f(16, 16, -0.1, 1, 0, P, None) == ESHAPE
+    assert f(-1, 16, 0.1, 1, 0, P, None) == ESHAPE
+    assert f(16, 16, 0.1, 1, 0, None, None) == ENULL
+    assert f(0, 16, 0.1, 1, 0, None, None) == OK  # nothing to draw
+    # the Philox layer entry points validate like the mask-taking ones
+    fw = lib.lora_dropout_philox_fwd
+    assert fw(1, 16, 64, 64, 8, 1.0, 1.0, 1, 0, P, P, P, P, P, P, 1 << 30, None) == ESHAPE
+    assert fw(1, 16, 64, 64, 8, 1.0, 0.1, 1, 0, P, P, P, P, None, P, 1 << 30, None) == ENULL
+    assert fw(1, 16, 64, 64, 8, 1.0, 0.1, 1, 0, P, P, P, P, P, P, 10, None) == EWS
+    bw = lib.lora_dropout_philox_bwd
+    assert bw(1, 16, 64, 64, 8, 1.0, 0.1, 1, 0, P, P, P, P, P, P, None, P, P, 1 << 30, None) == ENULL
+    assert bw(1, 16, 64, 64, 8, 1.0, 0.1, 1, 0, P, P, P, P, P, P + 2, P, P, P, 1 << 30, None) == EALIGN
