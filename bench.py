@@ -106,6 +106,8 @@ KIND_OF = {
     "few_bwd_kernel": "few_bwd",
     "nf4_dequant_t_kernel": "nf4_dequant",
     "nf4_dequant_kernel": "nf4_dequant",
+    "tiny_fwd_f32_kernel": "tiny_f32",
+    "tiny_bwd_f32_kernel": "tiny_f32",
 }
 
 

@@ -391,6 +391,7 @@ enum ProfKind : int {
   K_FEW_PANEL,
   K_FEW_FWD,
   K_FEW_BWD,
+  K_TINY,
   K_PROF_COUNT
 };
 
@@ -412,7 +413,8 @@ const char* kind_name(int k) {
       "nf4_dequant",                "panel_reduce",               "transpose_ab",
       "split_finish",               "swiglu_elementwise",
       "dropout_mask_copy",          "transpose_w",                "skinny_fwd",
-      "few_panel",                  "few_fwd",                    "few_bwd"};
+      "few_panel",                  "few_fwd",                    "few_bwd",
+      "tiny_f32"};
   static_assert(sizeof(names) / sizeof(names[0]) == K_PROF_COUNT, "one name per launch kind");
   return (k >= 0 && k < K_PROF_COUNT) ? names[k] : "unknown";
 }
@@ -597,6 +599,18 @@ int forward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, f
   char* w = static_cast<char*>(ws);
   if (!f32 && L.few.ok && !Pext && !Xa)
     return few_forward(L.few, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, Y, w, st);
+  // tiny fp32 problems: the whole forward in one launch
+  if (f32 && !rope && !Pext && !Xa && tiny_fits(M, d_in, d_out, r)) {
+    const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
+    HIPTRY(timed(K_TINY, 2 * Md * ko * ki + 2 * Md * rr * (ki + ko),
+                 4 * (Md * ki + ko * ki + rr * ki + ko * rr + Md * ko), st, [&] {
+                   return launch_tiny(false, static_cast<const float*>(X), static_cast<const float*>(W),
+                                      static_cast<const float*>(A), static_cast<const float*>(B), nullptr,
+                                      static_cast<float*>(Y), nullptr, nullptr, nullptr, nullptr, nullptr, M, d_in,
+                                      d_out, r, scale, st);
+                 }));
+    return LORA_OK;
+  }
   // few tokens: panel, GEMM, rank term and epilogue in one launch
   // (bf16 W; an NF4 W keeps the split path's load-stage dequantisation)
   const int smode = rope ? sk::ROPE : sk::PLAIN;
@@ -726,6 +740,20 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
   const bool f32 = dtype == LORA_F32;
   const int eb = elem_bytes(dtype);
   char* w = static_cast<char*>(ws);
+  if (f32 && !rope && !ov && !Xa && !keep && !nf4 && tiny_fits(M, d_in, d_out, r)) {
+    // tiny fp32 problems: the rank rows of every token (into the panel
+    // workspace: Pt holds r8 M8 >= M r floats, Qs M8 r8), then dX, dA, dB
+    const double Md = double(M), ki = double(d_in), ko = double(d_out), rr = double(r);
+    HIPTRY(timed(K_TINY, (dX ? 2 * Md * ki * ko : 0) + 6 * Md * rr * (ki + ko),
+                 4 * (Md * ki + ko * ki + rr * ki + ko * rr + Md * ko + (dX ? Md * ki : 0)), st, [&] {
+                   return launch_tiny(true, static_cast<const float*>(X), static_cast<const float*>(W),
+                                      static_cast<const float*>(A), static_cast<const float*>(B),
+                                      static_cast<const float*>(dY), nullptr, static_cast<float*>(dX), dA, dB,
+                                      reinterpret_cast<float*>(w + L.pt), reinterpret_cast<float*>(w + L.qs), M,
+                                      d_in, d_out, r, scale, st);
+                 }));
+    return LORA_OK;
+  }
   if (!f32 && L.few.ok && dX && !ov && !Xa && !keep)
     return few_backward(L.few, M, d_in, d_out, r, scale, X, W, nf4, A, B, rope, dY, dX, dA, dB, w, st);
   if (nf4 && L.dequant && L.dx_nt && dX && !Wt_in) {

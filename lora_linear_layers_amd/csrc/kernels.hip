@@ -13,6 +13,7 @@
 #include "gemm_w4_nf4.h"
 #include "gemm_panel.h"
 #include "skinny.h"
+#include "tiny.h"
 #include "few.h"
 #include "launch.h"
 
@@ -1161,6 +1162,41 @@ mfma_rate_kernel(int iters, float* __restrict__ out) {
 
 hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st) {
   hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)blocks), dim3(256), 0, st, iters, out);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// tiny fp32 problems: one launch per direction (tiny.h)
+// ---------------------------------------------------------------------------
+bool tiny_fits(int64_t M, int64_t K, int64_t N, int64_t r) {
+  const int64_t mx = K > N ? K : N;
+  return M >= 1 && r >= 1 && r <= tiny::MAX_R && M * r <= tiny::MAX_MR && K >= 1 && N >= 1 && mx <= 4096 &&
+         M * r * mx <= (int64_t(1) << 21) && M * K * N <= (int64_t(1) << 25);
+}
+
+hipError_t launch_tiny(bool bwd, const float* X, const float* W, const float* A, const float* B, const float* G,
+                       float* Y, float* dX, float* dA, float* dB, float* Ps, float* Qs, int64_t M, int64_t K,
+                       int64_t N, int64_t r, float s, hipStream_t st) {
+  if (!tiny_fits(M, K, N, r)) return hipErrorInvalidValue;
+  if (bwd && (!Ps || !Qs)) return hipErrorInvalidValue;
+  TinyArgs a;
+  a.X = X; a.W = W; a.A = A; a.B = B; a.G = G;
+  a.Y = Y; a.dX = dX; a.dA = dA; a.dB = dB; a.Ps = Ps; a.Qs = Qs;
+  a.M = (int)M; a.K = (int)K; a.N = (int)N; a.r = (int)r; a.s = s;
+  a.tiles_m = (int)((M + tiny::T - 1) / tiny::T);
+  const int tk = (int)((K + tiny::T - 1) / tiny::T), tn = (int)((N + tiny::T - 1) / tiny::T);
+  if (!bwd) {
+    a.blocks_x = a.tiles_m * tn;
+    a.blocks_a = 0;
+    hipLaunchKernelGGL(tiny_fwd_f32_kernel, dim3((unsigned)a.blocks_x), dim3(tiny::NT), 0, st, a);
+  } else {
+    a.blocks_x = dX ? a.tiles_m * tk : 0;
+    a.blocks_a = tk;
+    hipLaunchKernelGGL(tiny_rank_f32_kernel, dim3((unsigned)(2 * a.tiles_m)), dim3(tiny::NT), 0, st, a);
+    const hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+    hipLaunchKernelGGL(tiny_bwd_f32_kernel, dim3((unsigned)(a.blocks_x + tk + tn)), dim3(tiny::NT), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -178,6 +178,15 @@ hipError_t launch_dropout_philox(int elem_bytes, const void* X, void* out, uint8
 // wave); out [blocks * 256] receives one float per thread.
 hipError_t launch_mfma_rate(int iters, int blocks, float* out, hipStream_t st);
 
+// Tiny fp32 problems (tiny.h): forward (bwd false) Y = X W^T + s (X A^T) B^T
+// in one launch; backward dX (nullable), dA, dB of it for G in two launches,
+// the rank rows s X A^T and s G B going through Ps and Qs (M r floats each).
+// Only where tiny_fits holds (else hipErrorInvalidValue).
+bool tiny_fits(int64_t M, int64_t K, int64_t N, int64_t r);
+hipError_t launch_tiny(bool bwd, const float* X, const float* W, const float* A, const float* B, const float* G,
+                       float* Y, float* dX, float* dA, float* dB, float* Ps, float* Qs, int64_t M, int64_t K,
+                       int64_t N, int64_t r, float s, hipStream_t st);
+
 // Few-token forward in one launch (skinny.h): Y = X W^T + bf16(s X A^T) B^T,
 // mode 0 plain, 1 RoPE (pos / cosc / sinc, N % 128 == 0), bf16 W.  Requires
 // 1 <= M <= 64, r % 8 == 0, r <= 64 (skinny_fits).
