@@ -81,26 +81,32 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
   uint16_t* out = reinterpret_cast<uint16_t*>(c_out);
   if constexpr (EPI == EPI_ROPE) {
     // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
-    // first: 16-byte loads, all in flight together.  Row q's 64 values sit
-    // rotated by 32 when (q >> 2) & 1, so the reads below (rows q and q + 4,
-    // 32 consecutive frequencies each) hit distinct banks.
+    // first: the tile's positions (one per thread) through LDS, then each
+    // thread's 32 16-byte cache loads all in flight together (two round trips
+    // to memory; loading the positions per half of the rows had made four).
+    // Row q's 64 values sit rotated by 32 when (q >> 2) & 1, so the reads
+    // below (rows q and q + 4, 32 consecutive frequencies each) hit distinct
+    // banks.
     __syncthreads();
     float* cs_l = reinterpret_cast<float*>(smem);
     float* sn_l = cs_l + BM * 64;
+    int32_t* pos_l = reinterpret_cast<int32_t*>(sn_l + BM * 64);
+    static_assert(NT == BM, "one position per thread");
+    pos_l[te] = p.pos[m0 + te];
+    __syncthreads();
+    {
+      float4 buf[32];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float4 buf[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int c = te + NT * (16 * half + k);
-        const int q = c >> 5, part = c & 31;
-        const int32_t ps = p.pos[m0 + q];
+      for (int k = 0; k < 32; ++k) {
+        const int c = te + NT * k;
+        const int32_t ps = pos_l[c >> 5];
+        const int part = c & 31;
         const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)ps * 64 + 4 * (part & 15);
         buf[k] = rope_pos_ok(ps, p.max_pos) ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int c = te + NT * (16 * half + k);
+      for (int k = 0; k < 32; ++k) {
+        const int c = te + NT * k;
         const int q = c >> 5, part = c & 31;
         float* dst = (part < 16 ? cs_l : sn_l) + q * 64 + ((4 * (part & 15) + 32 * ((q >> 2) & 1)) & 63);
         *reinterpret_cast<float4*>(dst) = buf[k];
