@@ -33,14 +33,18 @@ namespace tiny {
 constexpr int T = 32;         // output tile edge
 constexpr int NT = 256;       // threads per block
 constexpr int MAX_R = 32;     // rank limit
-constexpr int KC = 128;       // contraction steps per LDS stage
+constexpr int KC = 128;       // contraction steps per LDS stage (32 per wave)
+constexpr int LP = T + 4;     // L row pitch: rows stay 16-byte aligned, column writes spread over banks
 constexpr int MAX_MR = 4096;  // M r limit (bounds the dA / dB blocks' contraction over the tokens)
-// a stage's operand tiles: L [32 rows][KC] (padded rows), R and R2 [KC][32]
+// a stage's operand tiles, contraction-major: L [KC][32 rows] (padded), R and
+// R2 [KC][32 columns]; R also holds the waves' partial tiles at the end
 struct Tiles {
-  float L[T][KC + 1];
+  __attribute__((aligned(16))) float L[KC][LP];
   __attribute__((aligned(16))) float R[KC][T];
   __attribute__((aligned(16))) float R2[KC][T];
 };
+static_assert(KC * T >= 4 * T * T, "R holds the four waves' partial tiles");
+static_assert(KC == 4 * 32, "a wave takes 32 steps of a stage");
 }  // namespace tiny
 
 struct TinyArgs {
@@ -62,17 +66,26 @@ __device__ inline float tiny_ld(const float* p, int64_t i) {
 
 // One 32 x 32 tile of a product over a contraction of length kn, staged
 // through LDS KC contraction steps at a time, the next stage's operands loaded
-// into registers while this one is multiplied: acc[c] += L(ti, k) R(k, tj + c)
-// for thread t (ti = t / 8, tj = 4 (t % 8)), and, when TWO, acc2[c] +=
-// L(ti, k) R2(k, tj + c) from the same L tile (the rank-r panel that shares
-// the main product's left operand).  lf(u, k) / rf(k, v) / rf2(k, v) return
-// the operands (zero outside their matrices); LT: L is read along u
-// (consecutive threads take consecutive u, for a transposed source).
+// into registers while this one is multiplied.  Result for thread t
+// (ti = t / 8, tj = 4 (t % 8)): acc[c] += sum_k L(ti, k) R(k, tj + c), and,
+// when TWO, acc2[c] += sum_k L(ti, k) R2(k, tj + c) from the same L tiles (the
+// rank-r panel that shares the main product's left operand).  lf(u, k) /
+// rf(k, v) / rf2(k, v) return the operands (zero outside their matrices); LT:
+// L is read along u (consecutive threads take consecutive u, for a
+// transposed source).
+//
+// Inside a stage, wave w takes the steps 32 w .. 32 w + 31 over the whole
+// tile, lane l the 4 x 4 outputs of rows 4 (l / 8) .. + 3 and columns
+// 4 (l % 8) .. + 3, one 16-byte read of L (stored k-major) and one of R per
+// step for 16 FMAs; the four waves' sums then meet in LDS, added in wave
+// order.  Every sum has one fixed order.
 template <bool TWO, bool LT, class LF, class RF, class RF2>
 __device__ inline void tiny_mm(int kn, LF lf, RF rf, RF2 rf2, tiny::Tiles& sm, float (&acc)[4], float (&acc2)[4]) {
   using tiny::KC;
+  using tiny::LP;
   constexpr int PER = tiny::T * KC / tiny::NT;
-  const int ti = threadIdx.x >> 3, tj = (threadIdx.x & 7) * 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ri = 4 * (lane >> 3), cj = 4 * (lane & 7);
   float lv[PER], rv[PER], r2v[PER];
   auto fetch = [&](int k0) {
 #pragma unroll
@@ -90,6 +103,7 @@ __device__ inline void tiny_mm(int kn, LF lf, RF rf, RF2 rf2, tiny::Tiles& sm, f
       if (TWO) r2v[i] = k0 + k < kn ? rf2(k0 + k, v) : 0.f;
     }
   };
+  float pa[4][4] = {}, pb[4][4] = {};
   fetch(0);
   for (int k0 = 0; k0 < kn; k0 += KC) {
     __syncthreads();  // every wave done with the previous stage's tiles
@@ -97,41 +111,65 @@ __device__ inline void tiny_mm(int kn, LF lf, RF rf, RF2 rf2, tiny::Tiles& sm, f
     for (int i = 0; i < PER; ++i) {
       const int e = (int)threadIdx.x + i * tiny::NT;
       if (LT)
-        sm.L[e & 31][e >> 5] = lv[i];
+        sm.L[e >> 5][e & 31] = lv[i];
       else
-        sm.L[e / KC][e % KC] = lv[i];
+        sm.L[e % KC][e / KC] = lv[i];
       sm.R[e >> 5][e & 31] = rv[i];
       if (TWO) sm.R2[e >> 5][e & 31] = r2v[i];
     }
     __syncthreads();
     if (k0 + KC < kn) fetch(k0 + KC);
     const int steps = kn - k0 < KC ? kn - k0 : KC;
-    // 8 contraction steps' LDS reads issued together, then their products
-    // (one wave per SIMD: nothing else would hide a wait per read)
-    for (int k8 = 0; k8 < steps; k8 += 8) {
-      float l[8];
-      float4 rr[8], r2[8];
+    const int kb = 32 * wave, ke = kb + 32 < steps ? kb + 32 : steps;
+    // 4 steps' 16-byte reads issued together, then their 64 (or 128) FMAs
+    for (int k4 = kb; k4 < ke; k4 += 4) {
+      float4 l[4], rr[4], r2[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        l[u] = sm.L[ti][k8 + u];
-        rr[u] = *reinterpret_cast<const float4*>(&sm.R[k8 + u][tj]);
-        if (TWO) r2[u] = *reinterpret_cast<const float4*>(&sm.R2[k8 + u][tj]);
+      for (int u = 0; u < 4; ++u) {
+        l[u] = *reinterpret_cast<const float4*>(&sm.L[k4 + u][ri]);
+        rr[u] = *reinterpret_cast<const float4*>(&sm.R[k4 + u][cj]);
+        if (TWO) r2[u] = *reinterpret_cast<const float4*>(&sm.R2[k4 + u][cj]);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc[0] = __builtin_fmaf(l[u], rr[u].x, acc[0]);
-        acc[1] = __builtin_fmaf(l[u], rr[u].y, acc[1]);
-        acc[2] = __builtin_fmaf(l[u], rr[u].z, acc[2]);
-        acc[3] = __builtin_fmaf(l[u], rr[u].w, acc[3]);
+      for (int u = 0; u < 4; ++u) {
+        const float lx[4] = {l[u].x, l[u].y, l[u].z, l[u].w};
+        const float rx[4] = {rr[u].x, rr[u].y, rr[u].z, rr[u].w};
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) pa[a][b] = __builtin_fmaf(lx[a], rx[b], pa[a][b]);
         if (TWO) {
-          acc2[0] = __builtin_fmaf(l[u], r2[u].x, acc2[0]);
-          acc2[1] = __builtin_fmaf(l[u], r2[u].y, acc2[1]);
-          acc2[2] = __builtin_fmaf(l[u], r2[u].z, acc2[2]);
-          acc2[3] = __builtin_fmaf(l[u], r2[u].w, acc2[3]);
+          const float r2x[4] = {r2[u].x, r2[u].y, r2[u].z, r2[u].w};
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) pb[a][b] = __builtin_fmaf(lx[a], r2x[b], pb[a][b]);
         }
       }
     }
   }
+  // the waves' partial tiles meet in LDS (the stage tiles are free after the
+  // barrier); thread t adds its 4 outputs over the waves in order
+  const int ti = threadIdx.x >> 3, tj = (threadIdx.x & 7) * 4;
+  auto reduce = [&](float (&part)[4][4], float (&out)[4]) {
+    __syncthreads();  // every wave done reading the stage tiles
+    float* red = &sm.R[0][0];  // [4 waves][32][32]
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+      *reinterpret_cast<float4*>(red + (wave * 32 + ri + a) * 32 + cj) =
+          make_float4(part[a][0], part[a][1], part[a][2], part[a][3]);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(red + (w * 32 + ti) * 32 + tj);
+      out[0] += v.x;
+      out[1] += v.y;
+      out[2] += v.z;
+      out[3] += v.w;
+    }
+  };
+  reduce(pa, acc);
+  if (TWO) reduce(pb, acc2);
 }
 
 __global__ void __launch_bounds__(tiny::NT) tiny_fwd_f32_kernel(const TinyArgs a) {
