@@ -144,9 +144,11 @@ def workspace_bytes(op: int, dtype: int, M: int, d_in: int, d_out: int, r: int) 
 
 
 def _workspace(op, dtype, M, d_in, d_out, r, device, ws=None):
-    n = workspace_bytes(op, dtype, M, d_in, d_out, r)
+    # a caller's workspace is passed through as it is: the library checks its
+    # size against the layout itself (LORA_ERR_WORKSPACE)
     if ws is not None:
         return ws
+    n = workspace_bytes(op, dtype, M, d_in, d_out, r)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 

@@ -292,9 +292,9 @@ def _group_members(X, members):
 
 
 def _group_ws(backward, dt, M, d_in, arr, device, ws):
-    n = int(L.lib().lora_group_workspace_bytes(int(backward), dt, M, d_in, len(arr), arr))
     if ws is not None:
-        return ws
+        return ws  # the library checks its size
+    n = int(L.lib().lora_group_workspace_bytes(int(backward), dt, M, d_in, len(arr), arr))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
@@ -367,9 +367,9 @@ def lora_group_bwd(X, members, dYs, positions=None, cos=None, sin=None, table16=
 
 
 def _swiglu_ws(backward, dt, M, d_in, arr, device, ws):
-    n = int(L.lib().lora_swiglu_workspace_bytes(int(backward), dt, M, d_in, arr))
     if ws is not None:
-        return ws
+        return ws  # the library checks its size
+    n = int(L.lib().lora_swiglu_workspace_bytes(int(backward), dt, M, d_in, arr))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
