@@ -15,13 +15,14 @@
 // the dX, dA and dB tiles in one launch.  All products go through LDS
 // stages of 128 contraction steps with fp32 fused multiply-adds, the next
 // stage's operands in flight while the current one is multiplied.  Every sum
-// runs in one fixed order (the contraction index ascending, the rank term
-// after the base term), so results do not depend on the grid and repeat bit
-// for bit.  Rows and columns past the ends load as zeros and are not stored.
-// No MFMA: at these sizes the work is a few thousand FMAs per thread and the
-// launches are the cost (the 128-token, 256 -> 256, r 8 layer: 37 us of kernel
-// time per forward + backward against 100 us in the ten launches of the
-// generic fp32 GEMMs).
+// runs in one fixed order (each wave its quarter of every stage in ascending
+// order, the four waves' sums added in wave order, the rank term after the
+// base term), so results do not depend on the grid and repeat bit for bit.
+// Rows and columns past the ends load as zeros and are not stored.  No MFMA:
+// at these sizes the work is a few thousand FMAs per thread and the launches
+// are the cost (the 128-token, 256 -> 256, r 8 layer: 34 us of kernel time
+// per forward + backward against 100 us in the ten launches of the generic
+// fp32 GEMMs).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -82,7 +83,6 @@ __device__ inline float tiny_ld(const float* p, int64_t i) {
 template <bool TWO, bool LT, class LF, class RF, class RF2>
 __device__ inline void tiny_mm(int kn, LF lf, RF rf, RF2 rf2, tiny::Tiles& sm, float (&acc)[4], float (&acc2)[4]) {
   using tiny::KC;
-  using tiny::LP;
   constexpr int PER = tiny::T * KC / tiny::NT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ri = 4 * (lane >> 3), cj = 4 * (lane & 7);
