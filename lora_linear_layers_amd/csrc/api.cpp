@@ -951,7 +951,8 @@ int backward_impl(int dtype, int64_t M, int64_t d_in, int64_t d_out, int64_t r, 
 int check_rope(int head_dim, int64_t d_out, int64_t M, const int32_t* pos, const float* c, const float* s,
                int64_t max_pos) {
   if (head_dim != 128 || d_out % 128) return LORA_ERR_SHAPE;
-  if (max_pos < 1) return LORA_ERR_SHAPE;
+  // cache rows are addressed with 32-bit byte offsets (256 bytes a row)
+  if (max_pos < 1 || max_pos > LORA_ROPE_MAX_POS) return LORA_ERR_SHAPE;
   TRY(check_ptrs({c, s}));
   return M > 0 ? check_ptrs({pos}) : LORA_OK;
 }

@@ -82,8 +82,9 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
   if constexpr (EPI == EPI_ROPE) {
     // The tile's 256 rows of the cos/sin cache (64 frequencies each) go to LDS
     // first: the tile's positions (one per thread) through LDS, then each
-    // thread's 32 16-byte cache loads all in flight together (two round trips
-    // to memory; loading the positions per half of the rows had made four).
+    // thread's 32 16-byte cache loads all in flight together.  (A load per
+    // position read and branch had cost the launch 20 us more at the
+    // Llama-3-8B attention shapes.)
     // Row q's 64 values sit rotated by 32 when (q >> 2) & 1, so the reads
     // below (rows q and q + 4, 32 consecutive frequencies each) hit distinct
     // banks.
@@ -95,21 +96,36 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
     pos_l[te] = p.pos[m0 + te];
     __syncthreads();
     {
-      float4 buf[32];
+      // thread t takes the 16-byte chunks (q, ch) = ((t + 256 k) / 16,
+      // (t + 256 k) % 16), k < 16, of both the cos and the sin row of tile row
+      // q: the 16 positions first (one wait), then 32 buffer loads with no
+      // branch, cos and sin through two wave-uniform resources sharing one
+      // 32-bit offset; a position outside the cache gets an offset past the
+      // resource, which reads zeros
+      const int nrec = (int)(p.max_pos * 256 < 0x7fffffff ? p.max_pos * 256 : 0x7fffffff);
+      const __amdgpu_buffer_rsrc_t rc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.cosc), (short)0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.sinc), (short)0, nrec, 0x00020000);
+      const int ch = te & 15;
+      uint32_t off[16];
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int c = te + NT * k;
-        const int32_t ps = pos_l[c >> 5];
-        const int part = c & 31;
-        const float* src = (part < 16 ? p.cosc : p.sinc) + (int64_t)ps * 64 + 4 * (part & 15);
-        buf[k] = rope_pos_ok(ps, p.max_pos) ? *reinterpret_cast<const float4*>(src) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < 16; ++k) {
+        const int32_t ps = pos_l[(te + NT * k) >> 4];
+        off[k] = rope_pos_ok(ps, p.max_pos) ? (uint32_t)ps * 256u + 16u * ch : OOB;
+      }
+      u32x4 bc[16], bs[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        bc[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, (int)off[k], 0, 0));
+        bs[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off[k], 0, 0));
       }
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        const int c = te + NT * k;
-        const int q = c >> 5, part = c & 31;
-        float* dst = (part < 16 ? cs_l : sn_l) + q * 64 + ((4 * (part & 15) + 32 * ((q >> 2) & 1)) & 63);
-        *reinterpret_cast<float4*>(dst) = buf[k];
+      for (int k = 0; k < 16; ++k) {
+        const int q = (te + NT * k) >> 4;
+        const int o = q * 64 + ((4 * ch + 32 * ((q >> 2) & 1)) & 63);
+        *reinterpret_cast<u32x4*>(cs_l + o) = bc[k];
+        *reinterpret_cast<u32x4*>(sn_l + o) = bs[k];
       }
     }
     __syncthreads();
