@@ -54,8 +54,9 @@ extern "C" {
 
 #define LORA_ABI_VERSION 1
 
-/* Largest RoPE cache (rows) the q/k projections accept. */
-#define LORA_ROPE_MAX_POS (1 << 23)
+/* Largest RoPE cache (rows) the q/k projections accept: 2^23 - 1, so that a
+ * row's byte offset (256 bytes a row) stays below 2^31. */
+#define LORA_ROPE_MAX_POS ((1 << 23) - 1)
 
 /* element types of X, W, A, B, Y, dY, dX */
 enum { LORA_F32 = 0, LORA_BF16 = 1 };
@@ -155,8 +156,8 @@ int lora_rope_cache(int64_t max_pos, int head_dim, double theta, float* cos_cach
  * multiple of it), element i pairs with i + 64 and rotates by the angle whose
  * cos/sin sit in row positions[t] of the caches (rotate-half pairing):
  *     y_i = z_i cos - z_{i+64} sin,   y_{i+64} = z_{i+64} cos + z_i sin,
- * where z is the fused LoRA output.  1 <= max_pos <= LORA_ROPE_MAX_POS (2^23;
- * else LORA_ERR_SHAPE).  positions: device int32 [M], each meant to lie in
+ * where z is the fused LoRA output.  1 <= max_pos <= LORA_ROPE_MAX_POS
+ * (2^23 - 1; else LORA_ERR_SHAPE).  positions: device int32 [M], each meant to lie in
  * [0, max_pos).  The host cannot read them before the launch;
  * the kernels check each one against max_pos and read no cache row for a
  * position outside that range: such a row of y comes out as zeros (and in

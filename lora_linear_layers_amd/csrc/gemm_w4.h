@@ -102,7 +102,10 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
       // branch, cos and sin through two wave-uniform resources sharing one
       // 32-bit offset; a position outside the cache gets an offset past the
       // resource, which reads zeros
-      const int nrec = (int)(p.max_pos * 256 < 0x7fffffff ? p.max_pos * 256 : 0x7fffffff);
+      // max_pos < 2^23 (validated on the host): every row ends below 2^31 and
+      // 2^31 lies past the resource for any cache size
+      const int nrec = (int)(p.max_pos * 256);
+      constexpr uint32_t PAST = 0x80000000u;
       const __amdgpu_buffer_rsrc_t rc =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.cosc), (short)0, nrec, 0x00020000);
       const __amdgpu_buffer_rsrc_t rs =
@@ -112,7 +115,7 @@ __device__ __forceinline__ void w4_epilogue(const GemmArgs& p, f32x16 (&acc)[w4:
 #pragma unroll
       for (int k = 0; k < 16; ++k) {
         const int32_t ps = pos_l[(te + NT * k) >> 4];
-        off[k] = rope_pos_ok(ps, p.max_pos) ? (uint32_t)ps * 256u + 16u * ch : OOB;
+        off[k] = rope_pos_ok(ps, p.max_pos) ? (uint32_t)ps * 256u + 16u * ch : PAST;
       }
       u32x4 bc[16], bs[16];
 #pragma unroll

@@ -110,8 +110,8 @@ def test_rope_validation(lib):
     assert call(pos=None) == ENULL
     assert call(cs=P + 4) == EALIGN
     assert call(max_pos=0) == ESHAPE
-    assert call(max_pos=(1 << 23) + 1) == ESHAPE  # rows past 32-bit byte offsets
-    assert call(max_pos=1 << 23) != ESHAPE
+    assert call(max_pos=1 << 23) == ESHAPE  # rows at 2^31 bytes and past
+    assert call(max_pos=(1 << 23) - 1) != ESHAPE
     assert lib.lora_rope_cache(0, 128, 5e5, P, P, None) == ESHAPE
     assert lib.lora_rope_cache(16, 128, -1.0, P, P, None) == ESHAPE
     assert lib.lora_rope_cache(16, 128, 5e5, None, P, None) == ENULL

@@ -284,6 +284,43 @@ def test_rope_out_of_range_positions_give_zero_rows(lib, M, d_out):
     assert all(e <= TOL["bf16"] for e in errs.values()), errs
 
 
+def test_rope_largest_cache_top_rows(lib):
+    # the largest cache the q/k projections accept (2^23 - 1 rows, more than
+    # 1 GiB each for cos and sin): positions in its top rows, where the
+    # whole-tile epilogue's 32-bit byte offsets into the cache are largest,
+    # one position on the last row, one just past it and one negative (zero
+    # rows), one at 0
+    from lora_linear_layers_amd import _lib
+
+    M, d_in, d_out, r = 4096, 256, 4096, 16
+    max_pos = (1 << 23) - 1
+    X, W, A, B, dY = lora_inputs(41, M, d_in, d_out, r, "bf16")
+    p = (max_pos - 1 - (np.arange(M) % 97)).astype(np.int32)
+    p[5], p[M // 3], p[M // 2], p[M - 2] = max_pos - 1, max_pos, -7, 0
+    pos = torch.from_numpy(p).cuda()
+    cos, sin = lib.rope_cache(max_pos, 128, 500000.0)
+    _lib.profile_begin(64)
+    Y = lib.lora_qk_rope_fwd(X, W, A, B, 1.0, pos, cos, sin)
+    torch.cuda.synchronize()
+    _lib.profile_end()
+    assert "gemm_bf16_256x256_nt_rope" in _lib.profile_report()
+    dX, dA, dB = lib.lora_qk_rope_bwd(X, W, A, B, 1.0, pos, cos, sin, dY)
+    torch.cuda.synchronize()
+    del cos, sin
+    bad = np.array([M // 3, M // 2])
+    good = np.setdiff1d(np.arange(M), bad)
+    pc = np.where((p >= 0) & (p < max_pos), p, 0)
+    assert np.all(cpu64(Y)[bad] == 0.0)
+    gi = torch.from_numpy(good).cuda()
+    assert rel(Y[gi], O.qk_rope_forward(X[gi], W, A, B, 1.0, pc[good])) <= TOL["bf16"]
+    dY0 = cpu64(dY)
+    dY0[bad] = 0.0
+    dXr, dAr, dBr = O.qk_rope_backward(X, W, A, B, 1.0, pc, dY0)
+    errs = dict(dX=rel(dX, dXr), dA=rel(dA, dAr), dB=rel(dB, dBr))
+    print(errs)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
+
+
 # ---------------------------------------------------------------------------
 # NF4
 # ---------------------------------------------------------------------------
