@@ -1030,25 +1030,40 @@ struct Table16 {
   float v[16];
 };
 
-// The same byte -> bf16x2 routine as the NF4 GEMM load stage.  Per thread and
-// iteration: 16 code bytes (32 elements, half of one 64-element absmax block)
-// in one 16-byte load, four 16-byte stores of bf16.
+// W bf16 from NF4 codes with the NF4 GEMM load stage's own byte -> bf16x2
+// routine: code dword d (8 elements, absmax block d / 8) to the 16-byte
+// output chunk d.  Each wave takes 256 consecutive dwords, lane l
+// the dwords l, l + 64, l + 128, l + 192 of them, so every load and every
+// 16-byte store instruction covers one contiguous KB of its wave's range
+// (one thread per four consecutive dwords had spread each store instruction
+// over 4 KB, 32 cache lines).
 __global__ void __launch_bounds__(256) nf4_dequant_kernel(const uint8_t* __restrict__ codes,
-                                                          const float* __restrict__ absmax, int64_t nchunks,
+                                                          const float* __restrict__ absmax, int64_t ndw,
                                                           Table16 tab, u32x4* __restrict__ out) {
   __shared__ float2 tab2[256];
   nf4_fill_tab2(tab2, tab.v, threadIdx.x, blockDim.x);
   __syncthreads();
-  const u32x4* src = reinterpret_cast<const u32x4*>(codes);
-  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < nchunks; j += (int64_t)gridDim.x * blockDim.x) {
-    const u32x4 c = src[j];
-    const float am = absmax[j >> 1];
+  const uint32_t* src = reinterpret_cast<const uint32_t*>(codes);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int64_t waves = ((int64_t)gridDim.x * blockDim.x) >> 6;
+  for (int64_t d0 = wave * 256; d0 < ndw; d0 += waves * 256) {
+    uint32_t c[4];
+    float am[4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int k = 0; k < 4; ++k) {
+      const int64_t d = d0 + lane + 64 * k;
+      c[k] = d < ndw ? src[d] : 0u;
+      am[k] = d < ndw ? absmax[d >> 3] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t d = d0 + lane + 64 * k;
+      if (d >= ndw) break;
       u32x4 o;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) o[b] = nf4_byte_to_bf16x2(tab2, c[w] >> (8 * b), am);
-      out[4 * j + w] = o;
+      for (int b = 0; b < 4; ++b) o[b] = nf4_byte_to_bf16x2(tab2, c[k] >> (8 * b), am[k]);
+      out[d] = o;
     }
   }
 }
@@ -1111,8 +1126,8 @@ hipError_t launch_nf4_dequant(const uint8_t* codes, const float* absmax, int64_t
   if (n % 64) return hipErrorInvalidValue;
   Table16 t;
   for (int i = 0; i < 16; ++i) t.v[i] = table16[i];
-  const int64_t nchunks = n / 32;
-  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for(nchunks, 256)), dim3(256), 0, st, codes, absmax, nchunks, t,
+  const int64_t ndw = n / 8;  // code dwords; one thread per four of them
+  hipLaunchKernelGGL(nf4_dequant_kernel, dim3(grid_for((ndw + 3) / 4, 256)), dim3(256), 0, st, codes, absmax, ndw, t,
                      reinterpret_cast<u32x4*>(out));
   return hipGetLastError();
 }
